@@ -1,0 +1,183 @@
+"""Plain CPU oracle for the MSA forward pass -- TEST INFRASTRUCTURE ONLY.
+
+Only the test-suite, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import this package.  The product path (the HIP library and
+its Python binding) never imports, links or calls it, and the two share no
+code: this side decodes raw bf16 / fp8 storage itself and computes every step
+from the definitions on the pages:
+
+* block scores and top-k with the forced local block --
+  "MiniMax Sparse Attention (MSA)", Deep Dive > Index Branch Architecture and
+  Training Stability Mechanisms; "Flash-MSA", Forward > Proxy attention;
+* sparse main attention -- "MiniMax Sparse Attention", sec. 2.1 and 2.2;
+* split-K log-sum-exp combine -- "MiniMax Sparse Attention (MSA)", Deep Dive >
+  KV-Outer Sparse Attention (two-phase forward);
+* block-index inversion -- "Flash-MSA", Backward.
+
+The arithmetic lives in ``msa_oracle.c`` (plain C, OpenMP over rows); this
+module builds it with gcc and marshals numpy arrays through ctypes.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "msa_oracle.c")
+_LIB = os.path.join(_HERE, "libmsa_oracle.so")
+
+BF16, FP8 = 0, 1
+
+
+def build() -> str:
+    """Compile the oracle with gcc (no fast-math, no FP contraction)."""
+    cmd = ["gcc", "-O2", "-fopenmp", "-ffp-contract=off", "-fno-fast-math",
+           "-std=c99", "-fPIC", "-shared", _SRC, "-o", _LIB + ".tmp", "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(_LIB + ".tmp", _LIB)
+    return _LIB
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+            build()
+        L = ctypes.CDLL(_LIB)
+        P = ctypes.c_void_p
+        i64, i32, f64 = ctypes.c_int64, ctypes.c_int, ctypes.c_double
+        L.oracle_block_scores.argtypes = [i64, i32, i32, i32, i64, P, P, P, i64, P]
+        L.oracle_block_scores.restype = None
+        L.oracle_select.argtypes = [i64, i32, i64, i32, i32, P, P, P, P]
+        L.oracle_select.restype = None
+        L.oracle_attention.argtypes = [i64, i32, i32, i32, i32, i32, i64, P, P, P, P,
+                                       i32, f64, f64, f64, P, f64, P, P]
+        L.oracle_attention.restype = None
+        L.oracle_combine.argtypes = [i32, i32, i32, i32, i64, P, P, P, P, P]
+        L.oracle_combine.restype = None
+        L.oracle_invert.argtypes = [i64, i64, i32, i64, P, P, P]
+        L.oracle_invert.restype = None
+        L.oracle_decode_bf16.argtypes = [ctypes.c_uint16]
+        L.oracle_decode_bf16.restype = ctypes.c_float
+        L.oracle_decode_e4m3.argtypes = [ctypes.c_uint8]
+        L.oracle_decode_e4m3.restype = ctypes.c_double
+        L.oracle_num_threads.argtypes = []
+        L.oracle_num_threads.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _c(a, dtype):
+    a = np.ascontiguousarray(a, dtype=dtype)
+    return a, a.ctypes.data_as(ctypes.c_void_p)
+
+
+def block_scores(N, B_k, pos, q_idx_rows, k_idx):
+    """Block scores M [n_rows, H_kv, B] (fp32, unscaled; +inf at the local block,
+    -inf past it).  ``q_idx_rows`` [n_rows, H_kv, d_idx] and ``k_idx``
+    [N, d_idx] hold raw bf16 bit patterns (uint16)."""
+    pos, pp = _c(pos, np.int64)
+    q, qp = _c(q_idx_rows, np.uint16)
+    kk, kp = _c(k_idx, np.uint16)
+    n_rows, H_kv, d_idx = q.shape
+    assert kk.shape[1] == d_idx and kk.shape[0] >= N
+    B = -(-N // B_k)
+    M = np.empty((n_rows, H_kv, B), np.float32)
+    lib().oracle_block_scores(N, H_kv, d_idx, B_k, n_rows, pp, qp, kp, B,
+                              M.ctypes.data_as(ctypes.c_void_p))
+    return M
+
+
+def select(M, pos, B_k, k):
+    """TopK with the forced local block.  Returns (block_idx [H_kv, n_rows, k]
+    int32 ascending / -1 padded, rel_margin [H_kv, n_rows])."""
+    M, mp = _c(M, np.float32)
+    pos, pp = _c(pos, np.int64)
+    n_rows, H_kv, B = M.shape
+    out = np.empty((H_kv, n_rows, k), np.int32)
+    marg = np.empty((H_kv, n_rows), np.float64)
+    lib().oracle_select(n_rows, H_kv, B, B_k, k, pp, mp,
+                        out.ctypes.data_as(ctypes.c_void_p),
+                        marg.ctypes.data_as(ctypes.c_void_p))
+    return out, marg
+
+
+def index_topk(N, B_k, k, pos, q_idx_rows, k_idx):
+    """Index branch for the given query rows: (block_idx, rel_margin, M)."""
+    M = block_scores(N, B_k, pos, q_idx_rows, k_idx)
+    bi, marg = select(M, pos, B_k, k)
+    return bi, marg, M
+
+
+def attention(N, B_k, pos, q_rows, K, V, block_idx, softmax_scale=None,
+              dtype=BF16, q_scale=1.0, k_scale=1.0, v_scale=1.0):
+    """Sparse main attention for the given query rows, fp64.
+
+    q_rows [n_rows, H_q, d_h]; K, V [N, H_kv, d_h] as raw uint16 (bf16) or
+    uint8 (fp8 e4m3) codes; block_idx [H_kv, n_rows, k].
+    Returns (O [n_rows, H_q, d_h], lse [n_rows, H_q]) in float64."""
+    st = np.uint16 if dtype == BF16 else np.uint8
+    pos, pp = _c(pos, np.int64)
+    q, qp = _c(q_rows, st)
+    Kc, kp = _c(K, st)
+    Vc, vp = _c(V, st)
+    bi, bp = _c(block_idx, np.int32)
+    n_rows, H_q, d_h = q.shape
+    H_kv = Kc.shape[1]
+    k = bi.shape[2]
+    assert bi.shape == (H_kv, n_rows, k)
+    if softmax_scale is None:
+        softmax_scale = 1.0 / np.sqrt(d_h)
+    O = np.empty((n_rows, H_q, d_h), np.float64)
+    lse = np.empty((n_rows, H_q), np.float64)
+    lib().oracle_attention(N, H_q, H_kv, d_h, B_k, k, n_rows, pp, qp, kp, vp, dtype,
+                           float(q_scale), float(k_scale), float(v_scale), bp,
+                           float(softmax_scale), O.ctypes.data_as(ctypes.c_void_p),
+                           lse.ctypes.data_as(ctypes.c_void_p))
+    return O, lse
+
+
+def combine(block_idx, o_part, lse_part):
+    """LSE merge.  block_idx [H_kv, n, k]; o_part [H_kv, n, k, G, d_h] bf16 bits;
+    lse_part [H_kv, n, k, G] float32.  Returns (O [n, H_q, d_h], lse [n, H_q])."""
+    bi, bp = _c(block_idx, np.int32)
+    op_, opp = _c(o_part, np.uint16)
+    lp, lpp = _c(lse_part, np.float32)
+    H_kv, n, k, G, d_h = op_.shape
+    O = np.empty((n, H_kv * G, d_h), np.float64)
+    lse = np.empty((n, H_kv * G), np.float64)
+    lib().oracle_combine(H_kv, G, d_h, k, n, bp, opp, lpp,
+                         O.ctypes.data_as(ctypes.c_void_p),
+                         lse.ctypes.data_as(ctypes.c_void_p))
+    return O, lse
+
+
+def invert(block_idx, B):
+    """Stable counting-sort inversion.  block_idx [n_seq, n_rows, k] ->
+    (offsets [n_seq, B + 1], entries [total]) with entry = row * k + slot."""
+    bi, bp = _c(block_idx, np.int32)
+    n_seq, n_rows, k = bi.shape
+    offsets = np.empty((n_seq, B + 1), np.int32)
+    entries = np.empty(max(int((bi >= 0).sum()), 1), np.int32)
+    lib().oracle_invert(n_seq, n_rows, k, B, bp,
+                        offsets.ctypes.data_as(ctypes.c_void_p),
+                        entries.ctypes.data_as(ctypes.c_void_p))
+    return offsets, entries[: int(offsets[-1, -1]) if n_seq else 0]
+
+
+def decode_bf16(h: int) -> float:
+    return float(lib().oracle_decode_bf16(h))
+
+
+def decode_e4m3(c: int) -> float:
+    return float(lib().oracle_decode_e4m3(c))
+
+
+def num_threads() -> int:
+    return int(lib().oracle_num_threads())

@@ -1,0 +1,56 @@
+"""The accounting model reproduces the numbers the pages print."""
+import json
+import os
+
+import numpy as np
+import pytest
+
+from block_sparse_attention_idx_amd import accounting as acc
+
+GOLD = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "pages_numbers.json")))
+
+
+def _near(got, ent):
+    return abs(got - ent["value"]) <= ent["rounding"] + 1e-12
+
+
+def test_flops_reduction_at_1m():
+    e = GOLD["flops_reduction_1M"]
+    assert _near(acc.flops_reduction(**e["config"]), e)
+    # with a smaller index head the printed figure is not reproduced
+    c = dict(e["config"], d_idx=64)
+    assert not _near(acc.flops_reduction(**c), e)
+
+
+def test_attended_context_reductions():
+    for key in ("attended_reduction_128K", "attended_reduction_1M"):
+        e = GOLD[key]
+        assert _near(acc.attended_context_reduction(**e["config"]), e)
+    e = GOLD["budget_tokens"]
+    assert e["config"]["k"] * e["config"]["B_k"] == e["value"]
+
+
+def test_intensities():
+    kv = acc.kv_outer_intensity(**GOLD["kv_outer_intensity"]["config"])
+    qo = acc.q_outer_intensity(**GOLD["q_outer_intensity"]["config"])
+    assert _near(kv, GOLD["kv_outer_intensity"])
+    assert _near(qo, GOLD["q_outer_intensity"])
+    assert _near(kv / qo, GOLD["intensity_ratio"])
+
+
+def test_io_crossover_model():
+    e = GOLD["io_model"]
+    m = acc.io_model(**e["config"])
+    for key in ("hbm_per_token", "hbm_per_block", "l2_per_token", "l2_per_block", "q_outer_l2_token"):
+        assert m[key] == pytest.approx(e[key], abs=0.5), key
+    for key in ("hbm_latency_token", "hbm_latency_block", "l2_latency_token", "l2_latency_block"):
+        assert m[key] == pytest.approx(e[key], abs=0.5), key
+    assert m["crossover"] == pytest.approx(e["crossover"], abs=0.005)
+
+
+def test_exact_counts_small():
+    # one sequence, B_k = 4, N = 10: rows 0..9, L = 0,0,0,0,1,1,1,1,2,2
+    assert acc.index_flops(0, 10, 1, 2, 4) == 2 * 2 * 1 * 4 * (0 * 4 + 1 * 4 + 2 * 2)
+    bi = np.array([[[0, -1], [0, -1], [0, 1], [1, 2]]], np.int32)   # rows 4..7
+    vis = acc.visible_keys(bi, 4, 10, 4)
+    assert vis.tolist() == [[4, 4, 4 + 3, 4 + 0]]  # row 6 sees 4..6 of block 1; row 7 none of block 2
