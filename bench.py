@@ -1,0 +1,207 @@
+#!/usr/bin/env python3
+"""Benchmark of the MSA forward pass on one MI355X.
+
+One step = one msa_forward over the whole workload (index branch, inversion,
+KV-outer sparse attention, combine) with every input already resident in HBM.
+Default workload: the 128K prefill with 64 planted hot blocks (N = 131,072,
+H_q = 64, H_kv = 4, d_h = d_idx = 128, B_k = 128, k = 16, bf16), synthetic
+seeded inputs.
+
+Prints one JSON line: whole-job tokens/s, the sparse-counted TFLOP/s, per-kernel
+times measured with HIP events on the launch stream, each kernel's roofline
+fraction, and the CPU oracle timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="prefill_n131072_hq64_hkv4_k16_hot64")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=768,
+                    help="query rows of the oracle sample (all heads and groups)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the MSA forward path here is a single-GPU "
+              "build (no collectives); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import block_sparse_attention_idx_amd as msa
+    from block_sparse_attention_idx_amd import accounting as acc
+    import synth
+
+    w = synth.WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    log(f"workload {w.name}: generating inputs on the device")
+    t = {x: synth.device_tensor(w, x, dev) for x in ("q", "k", "v", "q_idx", "k_idx")}
+    d = msa.make_dims(w.batch, w.N, w.H_q, w.H_kv, w.d_h, w.d_idx, w.B_k, w.k)
+    if w.dtype == "fp8":
+        s = synth.fp8_scale()
+        o = msa.make_opts("fp8", q_scale=s, k_scale=s, v_scale=s, q_chunk=w.q_chunk)
+    else:
+        o = msa.make_opts("bf16", q_chunk=w.q_chunk)
+    out = torch.empty((w.batch, w.N, w.H_q, w.d_h), dtype=torch.bfloat16, device=dev)
+    bi = torch.empty((w.batch, w.H_kv, w.N, w.k), dtype=torch.int32, device=dev)
+    ws = torch.empty((msa.msa_workspace_size(d, o),), dtype=torch.uint8, device=dev)
+    args_f = (d, o, t["q"], t["k"], t["v"], t["q_idx"], t["k_idx"])
+    stream = torch.cuda.current_stream(dev)
+
+    # ---- whole-step timing: msa_forward
+    log(f"warmup {args.warmup}, timed steps {args.steps}")
+    for _ in range(args.warmup):
+        msa.msa_forward(*args_f, o=out, block_idx_out=bi, workspace=ws)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        msa.msa_forward(*args_f, o=out, block_idx_out=bi, workspace=ws)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = ev0.elapsed_time(ev1) / args.steps
+    log(f"msa_forward: {ms_step:.3f} ms/step (host wall {1e3 * wall / args.steps:.3f} ms/step)")
+
+    # ---- per-kernel timing: the same pass through the four entry points, with
+    # HIP events between the calls on the launch stream (single-chunk workloads)
+    kern = {}
+    if w.q_chunk == 0 or w.q_chunk >= w.N:
+        sb = msa.msa_invert_workspace_size(d, 0, w.N)
+        sched = torch.empty(((sb + 3) // 4,), dtype=torch.int32, device=dev)
+        offs = torch.empty((w.batch, w.H_kv, w.B + 1), dtype=torch.int32, device=dev)
+        ents = torch.empty((w.batch * w.H_kv * w.N * w.k,), dtype=torch.int32, device=dev)
+        opart = torch.empty((w.batch, w.H_kv, w.N, w.k, w.G, w.d_h), dtype=torch.bfloat16, device=dev)
+        lpart = torch.empty((w.batch, w.H_kv, w.N, w.k, w.G), dtype=torch.float32, device=dev)
+        del ws
+        torch.cuda.empty_cache()
+        names = ("index_topk", "invert_blocks", "sparse_attn_fwd", "combine")
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps + 1)]
+        for it in range(args.steps + 1):       # iteration 0 is a warmup
+            e = evs[it]
+            e[0].record(stream)
+            msa.msa_index_topk(d, t["q_idx"], t["k_idx"], block_idx=bi)
+            e[1].record(stream)
+            msa.msa_invert_blocks(d, bi, blk_offsets=offs, blk_entries=ents, sched=sched)
+            e[2].record(stream)
+            msa.msa_sparse_attn_fwd(d, o, t["q"], t["k"], t["v"], offs, ents, sched,
+                                    o_part=opart, lse_part=lpart)
+            e[3].record(stream)
+            msa.msa_combine(d, bi, opart, lpart, o=out)
+            e[4].record(stream)
+        torch.cuda.synchronize()
+        for j, name in enumerate(names):
+            kern[name] = float(np.mean([evs[it][j].elapsed_time(evs[it][j + 1])
+                                        for it in range(1, args.steps + 1)]))
+        log("per call ms: " + ", ".join(f"{k} {v:.3f}" for k, v in kern.items()))
+
+    # ---- work accounting from the selection actually made
+    sel = bi.cpu().numpy().reshape(w.batch * w.H_kv, w.N, w.k)
+    f_idx = acc.index_flops(0, w.N, w.H_kv, w.d_idx, w.B_k, batch=w.batch)
+    f_main = acc.main_flops(sel, 0, w.N, w.B_k, w.G, w.d_h)
+    valid_slots = int((sel >= 0).sum())
+    bins = len(np.unique((np.arange(sel.shape[0])[:, None, None] * (w.B + 1) + sel)[sel >= 0]))
+    eb = 1 if w.dtype == "fp8" else 2
+    part = acc.partial_bytes(valid_slots, w.G, w.d_h)
+    bytes_attn = (part + 4 * valid_slots                       # partials out, entries in
+                  + w.batch * w.N * w.H_q * w.d_h * eb         # Q once
+                  + bins * 2 * w.B_k * w.d_h * eb)             # K, V once per selected block
+    bytes_comb = part + 4 * w.batch * w.H_kv * w.N * w.k + w.batch * w.N * w.H_q * w.d_h * 2
+    bytes_inv = 4 * w.batch * w.H_kv * w.N * w.k + 4 * valid_slots
+    tokens_s = w.batch * w.N / (ms_step * 1e-3)
+    tflops = (f_idx + f_main) / (ms_step * 1e-3) / 1e12
+
+    kernels = {}
+    if kern:
+        kernels = {
+            "index_topk": {"ms": kern["index_topk"], "bound": "mfma", "flops": f_idx,
+                           "achieved": f_idx / kern["index_topk"] / 1e9, "peak": PEAK_BF16_TFLOPS,
+                           "unit": "TFLOP/s"},
+            "invert_blocks": {"ms": kern["invert_blocks"], "bound": "hbm", "bytes": bytes_inv,
+                              "achieved": bytes_inv / kern["invert_blocks"] / 1e6,
+                              "peak": PEAK_HBM_GBS, "unit": "GB/s"},
+            "sparse_attn_fwd": {"ms": kern["sparse_attn_fwd"], "bound": "hbm", "bytes": bytes_attn,
+                                "achieved": bytes_attn / kern["sparse_attn_fwd"] / 1e6,
+                                "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                                "mfma_tflops": f_main / kern["sparse_attn_fwd"] / 1e9},
+            "combine": {"ms": kern["combine"], "bound": "hbm", "bytes": bytes_comb,
+                        "achieved": bytes_comb / kern["combine"] / 1e6, "peak": PEAK_HBM_GBS,
+                        "unit": "GB/s"},
+        }
+        for v in kernels.values():
+            v["frac"] = v["achieved"] / v["peak"]
+        dom = max(kernels, key=lambda n: kernels[n]["ms"])
+        dk = kernels[dom]
+        roofline = {"kernel": dom, "bound": dk["bound"], "achieved": dk["achieved"],
+                    "peak": dk["peak"], "unit": dk["unit"], "frac": dk["frac"], "traffic": None}
+    else:
+        roofline = None
+
+    # ---- the CPU oracle on a bounded sample of the same workload
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        rng = np.random.default_rng(12345)
+        rows = np.sort(rng.choice(w.N, size=min(args.cpu_rows, w.N), replace=False))
+        log(f"cpu baseline: host inputs for {len(rows)} sampled rows")
+        qi = synth.host_rows(w, "q_idx", rows)
+        ki = synth.host_all(w, "k_idx")
+        qr = synth.host_rows(w, "q", rows)
+        K = synth.host_all(w, "k")
+        V = synth.host_all(w, "v")
+        code = oracle.FP8 if w.dtype == "fp8" else oracle.BF16
+        sc = synth.fp8_scale() if w.dtype == "fp8" else 1.0
+        oracle.lib()
+        log("cpu baseline: timing the oracle")
+        c0 = time.perf_counter()
+        obi, _, _ = oracle.index_topk(w.N, w.B_k, w.k, rows, qi, ki)
+        oracle.attention(w.N, w.B_k, rows, qr, K, V, obi, dtype=code, q_scale=sc, k_scale=sc,
+                         v_scale=sc)
+        csec = time.perf_counter() - c0
+        sample_flops = (float((rows // w.B_k).sum()) * 2 * w.d_idx * w.H_kv * w.B_k
+                        + acc.main_flops(obi, 0, w.N, w.B_k, w.G, w.d_h) / 1.0)
+        cpu = {"value": len(rows) / csec, "unit": "tokens/s", "cores": oracle.num_threads(),
+               "kind": "oracle", "seconds": csec, "gflops": sample_flops / csec / 1e9,
+               "sample": f"{len(rows)} seeded random query rows of {w.name}, all {w.H_kv} groups "
+                         f"and {w.H_q} heads: index branch (fp32) + sparse attention (fp64)"}
+        log(f"cpu baseline: {csec:.1f} s -> {cpu['value']:.1f} tokens/s on {cpu['cores']} threads")
+
+    line = {
+        "metric": "MSA fwd sparse TFLOP/s + tokens/s at N=128K (Hq64/Hkv4/d128/k16); % MFMA/HBM peak",
+        "value": tokens_s, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "N": w.N, "H_q": w.H_q, "H_kv": w.H_kv,
+                   "d_h": w.d_h, "d_idx": w.d_idx, "B_k": w.B_k, "k": w.k,
+                   "q_chunk": w.q_chunk, "hot_blocks": w.plant},
+        "sparse_tflops": tflops, "index_flops": f_idx, "main_flops": f_main,
+        "roofline": roofline, "kernels": kernels, "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,287 @@
+// Host side of the C ABI declared in include/msa.h: argument validation,
+// scratch/workspace sizing, the chunk loop of the whole forward pass and the
+// kernel launches.  Validation makes no HIP call, so every error path returns
+// before anything is enqueued.
+#include <math.h>
+#include <string.h>
+
+#include "msa.h"
+#include "msa_internal.h"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+int hip_fail(hipError_t e) {
+  g_last_hip_error = static_cast<int>(e);
+  return MSA_ERR_HIP;
+}
+
+bool misaligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
+
+int check_dims(const msa_dims* d) {
+  if (!d) return MSA_ERR_NULL;
+  if (d->batch < 1 || d->N < 1 || d->H_kv < 1 || d->G < 1 || d->H_q < 1 || d->k < 1 ||
+      d->d_h < 1 || d->d_idx < 1 || d->B_k < 1)
+    return MSA_ERR_SHAPE;
+  if (static_cast<int64_t>(d->G) * d->H_kv != d->H_q) return MSA_ERR_SHAPE;
+  if (d->d_h != msa::kDh || d->B_k != msa::kBk) return MSA_ERR_UNSUPPORTED;
+  if (d->d_idx != 64 && d->d_idx != 128) return MSA_ERR_UNSUPPORTED;
+  if (d->G != 1 && d->G != 2 && d->G != 4 && d->G != 8 && d->G != 16) return MSA_ERR_UNSUPPORTED;
+  if (d->k > 32) return MSA_ERR_UNSUPPORTED;
+  if ((d->N + d->B_k - 1) / d->B_k > 16384) return MSA_ERR_UNSUPPORTED;
+  return MSA_OK;
+}
+
+int check_range(const msa_dims* d, int64_t q_begin, int64_t q_count) {
+  if (q_begin < 0 || q_count < 1 || q_begin > d->N || q_count > d->N - q_begin) return MSA_ERR_SHAPE;
+  if (q_begin % d->B_k != 0) return MSA_ERR_SHAPE;
+  const int64_t slots = static_cast<int64_t>(d->batch) * d->H_kv * q_count * d->k;
+  if (slots >= (int64_t(1) << 31)) return MSA_ERR_UNSUPPORTED;
+  return MSA_OK;
+}
+
+int check_opts(const msa_dims* d, const msa_opts* o) {
+  if (!o) return MSA_ERR_NULL;
+  if (o->qkv_dtype != MSA_DTYPE_BF16 && o->qkv_dtype != MSA_DTYPE_FP8_E4M3) return MSA_ERR_UNSUPPORTED;
+  if (o->reserved != 0) return MSA_ERR_SHAPE;
+  if (!isfinite(o->softmax_scale)) return MSA_ERR_SHAPE;
+  if (o->qkv_dtype == MSA_DTYPE_FP8_E4M3) {
+    if (!(o->q_scale > 0.f) || !(o->k_scale > 0.f) || !(o->v_scale > 0.f) ||
+        !isfinite(o->q_scale) || !isfinite(o->k_scale) || !isfinite(o->v_scale))
+      return MSA_ERR_SHAPE;
+  }
+  if (o->q_chunk < 0 || (o->q_chunk > 0 && o->q_chunk % d->B_k != 0)) return MSA_ERR_SHAPE;
+  return MSA_OK;
+}
+
+// Softmax multiplier in log2 units and the output multiplier of the attention
+// kernel.  fp8 operands are widened as value * 2^-8 each, which the scales undo.
+void attn_scales(const msa_dims* d, const msa_opts* o, float* scale_log2, float* out_scale) {
+  double s = o->softmax_scale > 0.f ? o->softmax_scale : 1.0 / sqrt(static_cast<double>(d->d_h));
+  double out = 1.0;
+  if (o->qkv_dtype == MSA_DTYPE_FP8_E4M3) {
+    s *= static_cast<double>(o->q_scale) * o->k_scale * 65536.0;
+    out = static_cast<double>(o->v_scale) * 256.0;
+  }
+  *scale_log2 = static_cast<float>(s * 1.4426950408889634);
+  *out_scale = static_cast<float>(out);
+}
+
+size_t align256(size_t b) { return (b + 255) / 256 * 256; }
+
+struct ForwardLayout {
+  int64_t qc;  // rows per chunk
+  size_t off_bi, off_off, off_ent, off_sched, off_opart, off_lpart, total;
+};
+
+ForwardLayout forward_layout(const msa_dims* d, const msa_opts* o) {
+  ForwardLayout L{};
+  L.qc = o->q_chunk > 0 ? (o->q_chunk < d->N ? o->q_chunk : d->N) : d->N;
+  const int64_t seqs = static_cast<int64_t>(d->batch) * d->H_kv;
+  const int64_t B = (d->N + d->B_k - 1) / d->B_k;
+  const size_t slots = static_cast<size_t>(seqs) * L.qc * d->k;
+  // the largest scratch is needed by the last (or the only) full-size chunk
+  int64_t words = 0;
+  const int64_t nchunks = (d->N + L.qc - 1) / L.qc;
+  for (int64_t c = (nchunks > 2 ? nchunks - 2 : 0); c < nchunks; ++c) {
+    const int64_t qb = c * L.qc, qn = (d->N - qb) < L.qc ? (d->N - qb) : L.qc;
+    const msa::SchedLayout s = msa::sched_layout(d->batch, d->H_kv, d->G, qb, qn);
+    words = s.words > words ? s.words : words;
+  }
+  size_t off = 0;
+  L.off_bi = off;
+  off += align256(slots * 4);
+  L.off_off = off;
+  off += align256(static_cast<size_t>(seqs) * (B + 1) * 4);
+  L.off_ent = off;
+  off += align256(slots * 4);
+  L.off_sched = off;
+  off += align256(static_cast<size_t>(words) * 4);
+  L.off_opart = off;
+  off += align256(slots * d->G * d->d_h * 2);
+  L.off_lpart = off;
+  off += align256(slots * d->G * 4);
+  L.total = off;
+  return L;
+}
+
+}  // namespace
+
+extern "C" {
+
+int msa_abi_version(void) { return MSA_ABI_VERSION; }
+
+const char* msa_status_string(int status) {
+  switch (status) {
+    case MSA_OK: return "ok";
+    case MSA_ERR_NULL: return "a required pointer is NULL";
+    case MSA_ERR_SHAPE: return "inconsistent sizes or range";
+    case MSA_ERR_UNSUPPORTED: return "shape outside the supported set";
+    case MSA_ERR_ALIGN: return "device pointer not 16-byte aligned";
+    case MSA_ERR_WORKSPACE: return "workspace too small";
+    case MSA_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+int msa_last_hip_error(void) { return g_last_hip_error; }
+
+int msa_index_topk(const msa_dims* dims, const void* q_idx, const void* k_idx, int64_t q_begin,
+                   int64_t q_count, int32_t* block_idx, void* stream) {
+  int st = check_dims(dims);
+  if (st) return st;
+  if ((st = check_range(dims, q_begin, q_count))) return st;
+  if (!q_idx || !k_idx || !block_idx) return MSA_ERR_NULL;
+  if (misaligned(q_idx) || misaligned(k_idx) || misaligned(block_idx)) return MSA_ERR_ALIGN;
+  hipError_t e = msa::launch_index_topk(static_cast<const uint16_t*>(q_idx),
+                                        static_cast<const uint16_t*>(k_idx), dims->batch, dims->N,
+                                        dims->H_kv, dims->d_idx, dims->k, q_begin, q_count,
+                                        block_idx, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MSA_OK : hip_fail(e);
+}
+
+int msa_invert_workspace_size(const msa_dims* dims, int64_t q_begin, int64_t q_count,
+                              size_t* bytes) {
+  int st = check_dims(dims);
+  if (st) return st;
+  if ((st = check_range(dims, q_begin, q_count))) return st;
+  if (!bytes) return MSA_ERR_NULL;
+  const msa::SchedLayout s = msa::sched_layout(dims->batch, dims->H_kv, dims->G, q_begin, q_count);
+  *bytes = static_cast<size_t>(s.words) * 4;
+  return MSA_OK;
+}
+
+int msa_invert_blocks(const msa_dims* dims, const int32_t* block_idx, int64_t q_begin,
+                      int64_t q_count, int32_t* blk_offsets, int32_t* blk_entries, void* sched,
+                      size_t sched_bytes, void* stream) {
+  int st = check_dims(dims);
+  if (st) return st;
+  if ((st = check_range(dims, q_begin, q_count))) return st;
+  if (!block_idx || !blk_offsets || !blk_entries || !sched) return MSA_ERR_NULL;
+  if (misaligned(block_idx) || misaligned(blk_offsets) || misaligned(blk_entries) ||
+      misaligned(sched))
+    return MSA_ERR_ALIGN;
+  const msa::SchedLayout s = msa::sched_layout(dims->batch, dims->H_kv, dims->G, q_begin, q_count);
+  if (sched_bytes < static_cast<size_t>(s.words) * 4) return MSA_ERR_WORKSPACE;
+  hipError_t e = msa::launch_invert(block_idx, dims->batch, dims->H_kv, dims->G, dims->k, q_begin,
+                                    q_count, blk_offsets, blk_entries, static_cast<int32_t*>(sched),
+                                    static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MSA_OK : hip_fail(e);
+}
+
+int msa_invert_status(const void* sched, int32_t* bad_ids, void* stream) {
+  if (!sched || !bad_ids) return MSA_ERR_NULL;
+  if (misaligned(sched)) return MSA_ERR_ALIGN;
+  hipError_t e = hipStreamSynchronize(static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e);
+  e = hipMemcpy(bad_ids, static_cast<const int32_t*>(sched) + msa::kHdrBad, sizeof(int32_t),
+                hipMemcpyDeviceToHost);
+  return e == hipSuccess ? MSA_OK : hip_fail(e);
+}
+
+int msa_sparse_attn_fwd(const msa_dims* dims, const msa_opts* opts, const void* q, const void* k,
+                        const void* v, const int32_t* blk_offsets, const int32_t* blk_entries,
+                        const void* sched, int64_t q_begin, int64_t q_count, void* o_part,
+                        float* lse_part, void* stream) {
+  int st = check_dims(dims);
+  if (st) return st;
+  if ((st = check_range(dims, q_begin, q_count))) return st;
+  if ((st = check_opts(dims, opts))) return st;
+  if (!q || !k || !v || !blk_offsets || !blk_entries || !sched || !o_part || !lse_part)
+    return MSA_ERR_NULL;
+  if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(blk_offsets) ||
+      misaligned(blk_entries) || misaligned(sched) || misaligned(o_part) || misaligned(lse_part))
+    return MSA_ERR_ALIGN;
+  float sl2, osc;
+  attn_scales(dims, opts, &sl2, &osc);
+  hipError_t e = msa::launch_sparse_attn(
+      q, k, v, opts->qkv_dtype == MSA_DTYPE_FP8_E4M3, dims->batch, dims->N, dims->H_kv, dims->G,
+      dims->k, sl2, osc, blk_offsets, blk_entries, static_cast<const int32_t*>(sched), q_begin,
+      q_count, static_cast<uint16_t*>(o_part), lse_part, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MSA_OK : hip_fail(e);
+}
+
+int msa_combine(const msa_dims* dims, const int32_t* block_idx, const void* o_part,
+                const float* lse_part, int64_t q_begin, int64_t q_count, void* o, float* lse,
+                void* stream) {
+  int st = check_dims(dims);
+  if (st) return st;
+  if ((st = check_range(dims, q_begin, q_count))) return st;
+  if (!block_idx || !o_part || !lse_part || !o) return MSA_ERR_NULL;
+  if (misaligned(block_idx) || misaligned(o_part) || misaligned(lse_part) || misaligned(o) ||
+      (lse && misaligned(lse)))
+    return MSA_ERR_ALIGN;
+  hipError_t e = msa::launch_combine(block_idx, static_cast<const uint16_t*>(o_part), lse_part,
+                                     dims->batch, dims->N, dims->H_kv, dims->G, dims->k, q_begin,
+                                     q_count, static_cast<uint16_t*>(o), lse,
+                                     static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MSA_OK : hip_fail(e);
+}
+
+int msa_workspace_size(const msa_dims* dims, const msa_opts* opts, size_t* bytes) {
+  int st = check_dims(dims);
+  if (st) return st;
+  if ((st = check_opts(dims, opts))) return st;
+  if (!bytes) return MSA_ERR_NULL;
+  const ForwardLayout L = forward_layout(dims, opts);
+  if ((st = check_range(dims, 0, L.qc))) return st;
+  *bytes = L.total;
+  return MSA_OK;
+}
+
+int msa_forward(const msa_dims* dims, const msa_opts* opts, const void* q, const void* k,
+                const void* v, const void* q_idx, const void* k_idx, void* o, float* lse,
+                int32_t* block_idx_out, void* workspace, size_t ws_bytes, void* stream) {
+  int st = check_dims(dims);
+  if (st) return st;
+  if ((st = check_opts(dims, opts))) return st;
+  if (!q || !k || !v || !q_idx || !k_idx || !o || !workspace) return MSA_ERR_NULL;
+  if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(q_idx) || misaligned(k_idx) ||
+      misaligned(o) || (lse && misaligned(lse)) || (block_idx_out && misaligned(block_idx_out)) ||
+      (reinterpret_cast<uintptr_t>(workspace) & 255u))
+    return MSA_ERR_ALIGN;
+  const ForwardLayout L = forward_layout(dims, opts);
+  if ((st = check_range(dims, 0, L.qc))) return st;
+  if (ws_bytes < L.total) return MSA_ERR_WORKSPACE;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  int32_t* bi_chunk = reinterpret_cast<int32_t*>(ws + L.off_bi);
+  int32_t* offs = reinterpret_cast<int32_t*>(ws + L.off_off);
+  int32_t* ents = reinterpret_cast<int32_t*>(ws + L.off_ent);
+  int32_t* sched = reinterpret_cast<int32_t*>(ws + L.off_sched);
+  uint16_t* opart = reinterpret_cast<uint16_t*>(ws + L.off_opart);
+  float* lpart = reinterpret_cast<float*>(ws + L.off_lpart);
+  float sl2, osc;
+  attn_scales(dims, opts, &sl2, &osc);
+  const bool fp8 = opts->qkv_dtype == MSA_DTYPE_FP8_E4M3;
+  const bool one_chunk = L.qc >= dims->N;
+  const int64_t seqs = static_cast<int64_t>(dims->batch) * dims->H_kv;
+
+  for (int64_t qb = 0; qb < dims->N; qb += L.qc) {
+    const int64_t qn = (dims->N - qb) < L.qc ? (dims->N - qb) : L.qc;
+    int32_t* bi = (one_chunk && block_idx_out) ? block_idx_out : bi_chunk;
+    hipError_t e = msa::launch_index_topk(static_cast<const uint16_t*>(q_idx),
+                                          static_cast<const uint16_t*>(k_idx), dims->batch, dims->N,
+                                          dims->H_kv, dims->d_idx, dims->k, qb, qn, bi, s);
+    if (e != hipSuccess) return hip_fail(e);
+    e = msa::launch_invert(bi, dims->batch, dims->H_kv, dims->G, dims->k, qb, qn, offs, ents, sched, s);
+    if (e != hipSuccess) return hip_fail(e);
+    e = msa::launch_sparse_attn(q, k, v, fp8, dims->batch, dims->N, dims->H_kv, dims->G, dims->k,
+                                sl2, osc, offs, ents, sched, qb, qn, opart, lpart, s);
+    if (e != hipSuccess) return hip_fail(e);
+    e = msa::launch_combine(bi, opart, lpart, dims->batch, dims->N, dims->H_kv, dims->G, dims->k,
+                            qb, qn, static_cast<uint16_t*>(o), lse, s);
+    if (e != hipSuccess) return hip_fail(e);
+    if (block_idx_out && !one_chunk) {
+      const size_t w = static_cast<size_t>(qn) * dims->k * sizeof(int32_t);
+      e = hipMemcpy2DAsync(block_idx_out + qb * dims->k, static_cast<size_t>(dims->N) * dims->k * 4,
+                           bi, w, w, static_cast<size_t>(seqs), hipMemcpyDeviceToDevice, s);
+      if (e != hipSuccess) return hip_fail(e);
+    }
+  }
+  return MSA_OK;
+}
+
+}  // extern "C"

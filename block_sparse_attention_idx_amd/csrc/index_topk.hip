@@ -1,0 +1,254 @@
+// Index branch of MSA: block scores, causal block max-pool and a streaming
+// top-k with the forced local block, fused in one kernel.
+//
+// What is computed ("MiniMax Sparse Attention (MSA)", Deep Dive > Index Branch
+// Architecture; "Flash-MSA", Forward > Proxy attention): for query i and group
+// r, every earlier key block b < L = floor(i / B_k) scores
+//     M[i, r, b] = max_{j in block b} Q^idx[i, r] . K^idx[j]
+// and the k - 1 best blocks are kept next to the local block L.  Softmax is
+// order preserving, so selection works on raw scores with no exponentials
+// ("MiniMax Sparse Attention (MSA)", Exp-Free TopK Kernel); the 1/sqrt(d_idx)
+// factor is a positive constant and is left out.  Every token of an earlier
+// block is visible to the query, so the causal mask never has to be applied:
+// the only partially visible block is the local one, which is forced.
+//
+// gfx950 design:
+//  * One workgroup = 8 waves = 512 (query, group) rows; rows are consecutive
+//    in Q^idx memory ([N][H_kv][d_idx]), so all groups of a query tile share
+//    each staged K^idx block (there is a single index key head).
+//  * Scores are computed transposed, S^T = K^idx_b * Q^idx^T, with
+//    v_mfma_f32_32x32x16_bf16: keys on the MFMA row dimension, queries on the
+//    column dimension.  Each lane then holds 16 keys of one query column per
+//    32-key tile, so the block max-pool is an in-lane max plus one exchange
+//    between the two half-waves.  No score ever leaves the VGPRs.
+//  * Q^idx fragments stay in VGPRs for the whole scan; K^idx blocks stream
+//    through double-buffered, XOR-swizzled LDS with one barrier per block.
+//  * After the exchange, each lane owns exactly one row and keeps that row's
+//    top-(k-1) (score, block) list sorted in VGPRs.  A new block can only
+//    enter when it beats the row's current k-1-th score; the insertion runs
+//    only when some lane of the wave needs it (wave vote).  Blocks arrive in
+//    ascending id order, so "ties keep the earlier block" is a strict compare.
+//  * Workgroups are issued heaviest (latest queries, most blocks) first.
+#include <limits.h>
+
+#include "msa_internal.h"
+
+namespace msa {
+namespace {
+
+constexpr int kIdxThreads = 512;
+constexpr int kIdxRows = 512;  // rows per workgroup, 64 per wave
+
+template <int DIDX>
+__device__ __forceinline__ int kidx_lds_off(int key, int c) {
+  constexpr int NCH = DIDX / 8;  // 16-byte chunks per key row
+  return key * (DIDX * 2) + ((c ^ (key & (NCH - 1))) << 4);
+}
+
+__device__ __forceinline__ float max16(const f32x16& a) {
+  float m0 = fmaxf(fmaxf(a[0], a[1]), a[2]);
+  float m1 = fmaxf(fmaxf(a[3], a[4]), a[5]);
+  float m2 = fmaxf(fmaxf(a[6], a[7]), a[8]);
+  float m3 = fmaxf(fmaxf(a[9], a[10]), a[11]);
+  float m4 = fmaxf(fmaxf(a[12], a[13]), a[14]);
+  return fmaxf(fmaxf(fmaxf(m0, m1), fmaxf(m2, m3)), fmaxf(m4, a[15]));
+}
+
+// Ascending compare-exchange network (bitonic) over KP (power of two) ints.
+template <int KP>
+__device__ __forceinline__ void sort_ascending(int (&v)[KP]) {
+#pragma unroll
+  for (int size = 2; size <= KP; size <<= 1) {
+#pragma unroll
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+#pragma unroll
+      for (int i = 0; i < KP; ++i) {
+        const int j = i ^ stride;
+        if (j > i) {
+          const bool up = (i & size) == 0;
+          const int a = v[i], b = v[j];
+          const int lo = min(a, b), hi = max(a, b);
+          v[i] = up ? lo : hi;
+          v[j] = up ? hi : lo;
+        }
+      }
+    }
+  }
+}
+
+// KP = capacity rounded up to a power of two; the list holds KP - 1 entries of
+// which the first KP - k are +inf sentinels, so the last entry is always the
+// row's (k-1)-th best score.
+template <int DIDX, int KP>
+__global__ __launch_bounds__(kIdxThreads, 1) void index_topk_kernel(
+    const uint16_t* __restrict__ q_idx, const uint16_t* __restrict__ k_idx, int64_t N, int H_kv,
+    int k, int64_t q_begin, int64_t q_count, int32_t* __restrict__ block_idx) {
+  constexpr int KM = KP - 1;
+  constexpr int NCH = DIDX / 8;
+  constexpr int STEPS = DIDX / 16;
+  constexpr int TILE = kBk * DIDX * 2;
+  constexpr int PER = kBk * NCH / kIdxThreads;  // 16-byte chunks staged per thread
+  __shared__ __attribute__((aligned(16))) uint8_t lds[KM > 0 ? 2 * TILE : 16];
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int n = lane & 31, h = lane >> 5;
+  const int64_t rows_total = q_count * H_kv;
+  const int64_t nwg = (rows_total + kIdxRows - 1) / kIdxRows;
+  const int64_t wg = nwg - 1 - static_cast<int64_t>(blockIdx.x);
+  const int64_t bat = blockIdx.y;
+  const int64_t f0 = wg * kIdxRows;
+
+  // The row whose top-k this lane keeps: column tile h of this wave, column n.
+  const int64_t f_mine = f0 + wave * 64 + h * 32 + n;
+  const bool mine_ok = f_mine < rows_total;
+  const int64_t il_mine = mine_ok ? f_mine / H_kv : 0;
+  const int r_mine = mine_ok ? static_cast<int>(f_mine % H_kv) : 0;
+  const int L_mine = static_cast<int>((q_begin + il_mine) / kBk);
+  const int64_t f_last = min(f0 + kIdxRows, rows_total) - 1;
+  const int Lmax = static_cast<int>((q_begin + f_last / H_kv) / kBk);
+
+  int ids[KM > 0 ? KM : 1];
+  if constexpr (KM > 0) {
+    float ts[KM];
+#pragma unroll
+    for (int j = 0; j < KM; ++j) {
+      const bool sentinel = j < KP - k;
+      ts[j] = sentinel ? __builtin_huge_valf() : -__builtin_huge_valf();
+      ids[j] = sentinel ? INT_MAX : -1;
+    }
+
+    // Q^idx fragments of the wave's two 32-row column tiles (B operand).
+    bf16x8 qf[2][STEPS];
+    const uint16_t* qbase = q_idx + (bat * N + q_begin) * H_kv * DIDX;
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      int64_t f = f0 + wave * 64 + nt * 32 + n;
+      f = f < rows_total ? f : rows_total - 1;
+      const uint16_t* qrow = qbase + f * DIDX;
+#pragma unroll
+      for (int ks = 0; ks < STEPS; ++ks)
+        qf[nt][ks] = as_bf16x8(*reinterpret_cast<const u32x4*>(qrow + 16 * ks + 8 * h));
+    }
+
+    const uint16_t* kbase = k_idx + bat * N * DIDX;
+    u32x4 st[PER];
+    auto load_block = [&](int blk) {
+#pragma unroll
+      for (int p = 0; p < PER; ++p) {
+        const int cid = tid + p * kIdxThreads;
+        const int key = cid / NCH, c = cid % NCH;
+        st[p] = *reinterpret_cast<const u32x4*>(kbase + (static_cast<int64_t>(blk) * kBk + key) * DIDX + c * 8);
+      }
+    };
+    auto store_block = [&](int buf) {
+#pragma unroll
+      for (int p = 0; p < PER; ++p) {
+        const int cid = tid + p * kIdxThreads;
+        const int key = cid / NCH, c = cid % NCH;
+        *reinterpret_cast<u32x4*>(lds + buf * TILE + kidx_lds_off<DIDX>(key, c)) = st[p];
+      }
+    };
+
+    if (Lmax > 0) {
+      load_block(0);
+      store_block(0);
+      __syncthreads();
+    }
+    for (int b = 0; b < Lmax; ++b) {
+      const int cur = b & 1;
+      if (b + 1 < Lmax) load_block(b + 1);
+      const uint8_t* tile = lds + cur * TILE;
+      float mx0 = -__builtin_huge_valf(), mx1 = -__builtin_huge_valf();
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        f32x16 a0 = {}, a1 = {};
+#pragma unroll
+        for (int ks = 0; ks < STEPS; ++ks) {
+          const bf16x8 kf = as_bf16x8(*reinterpret_cast<const u32x4*>(tile + kidx_lds_off<DIDX>(32 * mt + n, 2 * ks + h)));
+          a0 = mfma32x32x16(kf, qf[0][ks], a0);
+          a1 = mfma32x32x16(kf, qf[1][ks], a1);
+        }
+        mx0 = fmaxf(mx0, max16(a0));
+        mx1 = fmaxf(mx1, max16(a1));
+      }
+      // Lane half 0 holds keys 4h.. of every 8 for column tile 0 and 1; swap so
+      // that half 0 finishes column tile 0 and half 1 column tile 1.
+      const float send = h ? mx0 : mx1;
+      const float recv = __shfl_xor(send, 32);
+      const float score = fmaxf(h ? mx1 : mx0, recv);
+      const bool need = (b < L_mine) && (score > ts[KM - 1]);
+      if (__any(need)) {
+        float x = score;
+        int xi = b;
+        bool moved = false;
+#pragma unroll
+        for (int j = 0; j < KM; ++j) {
+          const bool sw = need && (moved || x > ts[j]);
+          const float t = ts[j];
+          const int ti = ids[j];
+          ts[j] = sw ? x : t;
+          ids[j] = sw ? xi : ti;
+          x = sw ? t : x;
+          xi = sw ? ti : xi;
+          moved = moved || sw;
+        }
+      }
+      if (b + 1 < Lmax) store_block(cur ^ 1);
+      __syncthreads();
+    }
+  }
+
+  if (!mine_ok) return;
+  int32_t* dst = block_idx + ((bat * H_kv + r_mine) * q_count + il_mine) * k;
+  if constexpr (KM == 0) {
+    dst[0] = L_mine;
+  } else {
+    int v[KP];
+#pragma unroll
+    for (int j = 0; j < KM; ++j) v[j] = ids[j] < 0 ? INT_MAX : ids[j];
+    v[KM] = INT_MAX;
+    sort_ascending<KP>(v);
+    int nv = 0;
+#pragma unroll
+    for (int j = 0; j < KP; ++j) nv += v[j] != INT_MAX ? 1 : 0;
+#pragma unroll
+    for (int j = 0; j < KP; ++j)
+      if (j < k) dst[j] = j < nv ? v[j] : (j == nv ? L_mine : -1);
+  }
+}
+
+template <int DIDX, int KP>
+hipError_t launch_t(const uint16_t* q_idx, const uint16_t* k_idx, int batch, int64_t N, int H_kv,
+                    int k, int64_t q_begin, int64_t q_count, int32_t* block_idx,
+                    hipStream_t stream) {
+  const int64_t nwg = (q_count * H_kv + kIdxRows - 1) / kIdxRows;
+  hipLaunchKernelGGL((index_topk_kernel<DIDX, KP>), dim3(static_cast<unsigned>(nwg), batch),
+                     dim3(kIdxThreads), 0, stream, q_idx, k_idx, N, H_kv, k, q_begin, q_count,
+                     block_idx);
+  return hipGetLastError();
+}
+
+template <int DIDX>
+hipError_t launch_d(const uint16_t* q_idx, const uint16_t* k_idx, int batch, int64_t N, int H_kv,
+                    int k, int64_t q_begin, int64_t q_count, int32_t* block_idx,
+                    hipStream_t stream) {
+  if (k <= 1) return launch_t<DIDX, 1>(q_idx, k_idx, batch, N, H_kv, k, q_begin, q_count, block_idx, stream);
+  if (k <= 2) return launch_t<DIDX, 2>(q_idx, k_idx, batch, N, H_kv, k, q_begin, q_count, block_idx, stream);
+  if (k <= 4) return launch_t<DIDX, 4>(q_idx, k_idx, batch, N, H_kv, k, q_begin, q_count, block_idx, stream);
+  if (k <= 8) return launch_t<DIDX, 8>(q_idx, k_idx, batch, N, H_kv, k, q_begin, q_count, block_idx, stream);
+  if (k <= 16) return launch_t<DIDX, 16>(q_idx, k_idx, batch, N, H_kv, k, q_begin, q_count, block_idx, stream);
+  return launch_t<DIDX, 32>(q_idx, k_idx, batch, N, H_kv, k, q_begin, q_count, block_idx, stream);
+}
+
+}  // namespace
+
+hipError_t launch_index_topk(const uint16_t* q_idx, const uint16_t* k_idx, int batch, int64_t N,
+                             int H_kv, int d_idx, int k, int64_t q_begin, int64_t q_count,
+                             int32_t* block_idx, hipStream_t stream) {
+  if (d_idx == 64)
+    return launch_d<64>(q_idx, k_idx, batch, N, H_kv, k, q_begin, q_count, block_idx, stream);
+  return launch_d<128>(q_idx, k_idx, batch, N, H_kv, k, q_begin, q_count, block_idx, stream);
+}
+
+}  // namespace msa

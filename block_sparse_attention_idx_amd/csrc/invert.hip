@@ -1,0 +1,253 @@
+// Block-index inversion and work-list construction for the KV-outer pass.
+//
+// The selection B[seq, query, slot] -> block (seq = batch * H_kv + group) is
+// inverted into B*[seq, block] -> the queries that selected it ("Flash-MSA",
+// Backward; "MiniMax Sparse Attention (MSA)", Deep Dive > KV-Outer Sparse
+// Attention, step 1: reverse index).  The result is a CSR whose entries are
+// ascending in query inside every bin, i.e. a stable counting sort, computed
+// deterministically without global atomics:
+//
+//  1. count:    one workgroup per (seq, 64-row query tile) builds, in LDS, a
+//               64-bit mask per block of which tile rows selected it (LDS
+//               atomic OR is order independent) and writes the popcounts,
+//               cnt[seq][tile][block].
+//  2. colscan:  exclusive prefix of cnt down each block column (over tiles),
+//               in place; column totals tot[seq][block].
+//  3. binscan:  one workgroup scans the totals over all (seq, block) bins into
+//               absolute CSR offsets, and the per-bin work-item counts
+//               ceil(tot / items) into the work-list prefix.
+//  4. scatter:  the count workgroup's masks are rebuilt and every entry lands at
+//               offset[bin] + colprefix[tile][bin] + popcount(mask below row).
+//
+// Pre-scheduled chunking ("MiniMax Sparse Attention (MSA)", KV-Outer Sparse
+// Attention, step 5): every bin is cut into work items of at most
+// queries_per_item(G) queries with preassigned output slots, so a block that
+// many queries picked is spread over many workgroups.  The attention kernel
+// finds its item by binary search in the work-list prefix.
+#include "msa_internal.h"
+
+namespace msa {
+
+SchedLayout sched_layout(int batch, int H_kv, int G, int64_t q_begin, int64_t q_count) {
+  SchedLayout s{};
+  auto al = [](int64_t w) { return (w + 63) / 64 * 64; };  // 256-byte alignment
+  s.B_c = (q_begin + q_count + kBk - 1) / kBk;
+  s.T64 = (q_count + 63) / 64;
+  s.nbins = static_cast<int64_t>(batch) * H_kv * s.B_c;
+  s.qpi = queries_per_item(G);
+  int64_t w = kHdrWords;
+  s.off_items = w;
+  w = al(w + s.nbins + 1);
+  s.off_tot = w;
+  w = al(w + s.nbins);
+  s.off_bad = w;
+  w = al(w + static_cast<int64_t>(batch) * H_kv * s.T64);
+  s.off_cnt = w;
+  w = al(w + static_cast<int64_t>(batch) * H_kv * s.T64 * s.B_c);
+  s.words = w;
+  return s;
+}
+
+int64_t attn_max_items(int batch, int H_kv, int G, int k, int64_t q_begin, int64_t q_count) {
+  const SchedLayout s = sched_layout(batch, H_kv, G, q_begin, q_count);
+  const int64_t entries = static_cast<int64_t>(batch) * H_kv * q_count * k;
+  return entries / s.qpi + s.nbins + 1;
+}
+
+namespace {
+
+constexpr int kInvThreads = 256;
+
+// Build the LDS row masks of one (seq, tile).  Returns the number of bins used.
+__device__ __forceinline__ int build_masks(const int32_t* __restrict__ rows, int k, int64_t q_begin,
+                                           int64_t q0, int nrows, unsigned long long* mask,
+                                           int* bad) {
+  const int tmax = static_cast<int>((q_begin + q0 + nrows - 1) / kBk);
+  const int nb = tmax + 1;
+  for (int b = threadIdx.x; b < nb; b += blockDim.x) mask[b] = 0ull;
+  __syncthreads();
+  int nbad = 0;
+  for (int e = threadIdx.x; e < nrows * k; e += blockDim.x) {
+    const int row = e / k;
+    const int v = rows[e];
+    const int L = static_cast<int>((q_begin + q0 + row) / kBk);
+    if (v >= 0 && v <= L)
+      atomicOr(&mask[v], 1ull << row);
+    else if (v != -1)
+      ++nbad;
+  }
+  *bad = nbad;
+  __syncthreads();
+  return nb;
+}
+
+__global__ __launch_bounds__(kInvThreads) void inv_count_kernel(
+    const int32_t* __restrict__ block_idx, int k, int64_t q_begin, int64_t q_count, int64_t B_c,
+    int64_t T64, int32_t* __restrict__ cnt, int32_t* __restrict__ bad_out) {
+  extern __shared__ unsigned long long mask[];
+  __shared__ int bad_sum;
+  const int64_t tq = blockIdx.x, seq = blockIdx.y;
+  const int64_t q0 = tq * 64;
+  const int nrows = static_cast<int>(min<int64_t>(64, q_count - q0));
+  if (threadIdx.x == 0) bad_sum = 0;
+  int nbad;
+  const int nb = build_masks(block_idx + (seq * q_count + q0) * k, k, q_begin, q0, nrows, mask, &nbad);
+  if (nbad) atomicAdd(&bad_sum, nbad);
+  int32_t* out = cnt + (seq * T64 + tq) * B_c;
+  for (int64_t b = threadIdx.x; b < B_c; b += blockDim.x)
+    out[b] = b < nb ? __popcll(mask[b]) : 0;
+  __syncthreads();
+  if (threadIdx.x == 0) bad_out[seq * T64 + tq] = bad_sum;
+}
+
+// 16 waves per workgroup walk the tiles of 64 block columns.
+constexpr int kScanWaves = 16;
+
+__global__ __launch_bounds__(kScanWaves * 64) void inv_colscan_kernel(
+    int32_t* __restrict__ cnt, int64_t B_c, int64_t T64, int32_t* __restrict__ tot) {
+  __shared__ int part[kScanWaves][64];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int64_t seq = blockIdx.y;
+  const int64_t col = static_cast<int64_t>(blockIdx.x) * 64 + lane;
+  const int64_t per = (T64 + kScanWaves - 1) / kScanWaves;
+  const int64_t t0 = min<int64_t>(T64, wave * per), t1 = min<int64_t>(T64, t0 + per);
+  int32_t* base = cnt + seq * T64 * B_c + col;
+  int s = 0;
+  if (col < B_c)
+    for (int64_t t = t0; t < t1; ++t) s += base[t * B_c];
+  part[wave][lane] = s;
+  __syncthreads();
+  int run = 0, all = 0;
+#pragma unroll
+  for (int w = 0; w < kScanWaves; ++w) {
+    run += w < wave ? part[w][lane] : 0;
+    all += part[w][lane];
+  }
+  if (col < B_c) {
+    for (int64_t t = t0; t < t1; ++t) {
+      const int c = base[t * B_c];
+      base[t * B_c] = run;
+      run += c;
+    }
+    if (wave == 0) tot[seq * B_c + col] = all;
+  }
+}
+
+// Single workgroup: exclusive scans over all bins of entry counts (CSR
+// offsets) and of work-item counts (work-list prefix); sums the bad-id counts.
+constexpr int kBinThreads = 1024;
+
+__global__ __launch_bounds__(kBinThreads) void inv_binscan_kernel(
+    const int32_t* __restrict__ tot, int64_t nbins, int64_t B_c, int qpi,
+    const int32_t* __restrict__ bad, int64_t nbad_slots, int32_t* __restrict__ blk_offsets,
+    int32_t* __restrict__ items, int32_t* __restrict__ hdr) {
+  __shared__ int se[kBinThreads], si[kBinThreads];
+  __shared__ int sbad;
+  const int t = threadIdx.x;
+  const int64_t per = (nbins + kBinThreads - 1) / kBinThreads;
+  const int64_t b0 = min<int64_t>(nbins, t * per), b1 = min<int64_t>(nbins, b0 + per);
+  int e = 0, it = 0;
+  for (int64_t b = b0; b < b1; ++b) {
+    const int c = tot[b];
+    e += c;
+    it += (c + qpi - 1) / qpi;
+  }
+  se[t] = e;
+  si[t] = it;
+  if (t == 0) sbad = 0;
+  __syncthreads();
+  // Hillis-Steele inclusive scan over the per-thread sums.
+  for (int d = 1; d < kBinThreads; d <<= 1) {
+    const int ae = t >= d ? se[t - d] : 0, ai = t >= d ? si[t - d] : 0;
+    __syncthreads();
+    se[t] += ae;
+    si[t] += ai;
+    __syncthreads();
+  }
+  int re = se[t] - e, ri = si[t] - it;  // exclusive starts of this thread's range
+  for (int64_t b = b0; b < b1; ++b) {
+    const int64_t seq = b / B_c, blk = b % B_c;
+    const int c = tot[b];
+    blk_offsets[seq * (B_c + 1) + blk] = re;
+    items[b] = ri;
+    re += c;
+    ri += (c + qpi - 1) / qpi;
+    if (blk == B_c - 1) blk_offsets[seq * (B_c + 1) + B_c] = re;
+  }
+  int nb = 0;
+  for (int64_t j = t; j < nbad_slots; j += kBinThreads) nb += bad[j];
+  if (nb) atomicAdd(&sbad, nb);
+  __syncthreads();
+  if (t == kBinThreads - 1) {
+    items[nbins] = si[t];
+    hdr[kHdrItems] = si[t];
+  }
+  if (t == 0) hdr[kHdrBad] = sbad;
+}
+
+__global__ __launch_bounds__(kInvThreads) void inv_scatter_kernel(
+    const int32_t* __restrict__ block_idx, int k, int64_t q_begin, int64_t q_count, int64_t B_c,
+    int64_t T64, const int32_t* __restrict__ colpre, const int32_t* __restrict__ blk_offsets,
+    int32_t* __restrict__ entries) {
+  extern __shared__ unsigned long long mask[];
+  const int64_t tq = blockIdx.x, seq = blockIdx.y;
+  const int64_t q0 = tq * 64;
+  const int nrows = static_cast<int>(min<int64_t>(64, q_count - q0));
+  const int32_t* rows = block_idx + (seq * q_count + q0) * k;
+  int nbad;
+  build_masks(rows, k, q_begin, q0, nrows, mask, &nbad);
+  const int32_t* pre = colpre + (seq * T64 + tq) * B_c;
+  const int32_t* off = blk_offsets + seq * (B_c + 1);
+  for (int e = threadIdx.x; e < nrows * k; e += blockDim.x) {
+    const int row = e / k, slot = e % k;
+    const int v = rows[e];
+    const int L = static_cast<int>((q_begin + q0 + row) / kBk);
+    if (v < 0 || v > L) continue;
+    const int rank = __popcll(mask[v] & ((1ull << row) - 1ull));
+    entries[off[v] + pre[v] + rank] = static_cast<int32_t>((q0 + row) * k + slot);
+  }
+}
+
+bool g_lds_attr_set = false;
+
+}  // namespace
+
+hipError_t launch_invert(const int32_t* block_idx, int batch, int H_kv, int G, int k,
+                         int64_t q_begin, int64_t q_count, int32_t* blk_offsets,
+                         int32_t* blk_entries, int32_t* sched, hipStream_t stream) {
+  const SchedLayout s = sched_layout(batch, H_kv, G, q_begin, q_count);
+  const int64_t nseq = static_cast<int64_t>(batch) * H_kv;
+  const size_t lds = static_cast<size_t>(s.B_c) * sizeof(unsigned long long);
+  if (!g_lds_attr_set) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(inv_count_kernel),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024 - 1024);
+    if (e != hipSuccess) return e;
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(inv_scatter_kernel),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024 - 1024);
+    if (e != hipSuccess) return e;
+    g_lds_attr_set = true;
+  }
+  int32_t* hdr = sched;
+  int32_t* items = sched + s.off_items;
+  int32_t* tot = sched + s.off_tot;
+  int32_t* bad = sched + s.off_bad;
+  int32_t* cnt = sched + s.off_cnt;
+  const dim3 tiles(static_cast<unsigned>(s.T64), static_cast<unsigned>(nseq));
+  hipLaunchKernelGGL(inv_count_kernel, tiles, dim3(kInvThreads), lds, stream, block_idx, k, q_begin,
+                     q_count, s.B_c, s.T64, cnt, bad);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(inv_colscan_kernel, dim3(static_cast<unsigned>((s.B_c + 63) / 64), nseq),
+                     dim3(kScanWaves * 64), 0, stream, cnt, s.B_c, s.T64, tot);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(inv_binscan_kernel, dim3(1), dim3(kBinThreads), 0, stream, tot, s.nbins, s.B_c,
+                     static_cast<int>(s.qpi), bad, nseq * s.T64, blk_offsets, items, hdr);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(inv_scatter_kernel, tiles, dim3(kInvThreads), lds, stream, block_idx, k, q_begin,
+                     q_count, s.B_c, s.T64, cnt, blk_offsets, blk_entries);
+  return hipGetLastError();
+}
+
+}  // namespace msa

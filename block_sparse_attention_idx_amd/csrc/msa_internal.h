@@ -1,0 +1,105 @@
+// Internal declarations shared by the MSA HIP sources (not part of the ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace msa {
+
+// ---------------------------------------------------------------- vector types
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+constexpr int kBk = 128;   // tokens per key block
+constexpr int kDh = 128;   // head dimension of Q, K, V
+constexpr int kXcds = 8;   // MI355X: workgroups are dealt round-robin to 8 XCDs
+
+// Queries per attention work item: 1024 (query, head) rows = 8 MFMA row tiles.
+__host__ __device__ constexpr int queries_per_item(int G) { return 1024 / G; }
+
+// ---------------------------------------------------------------- device helpers
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+// D[32x32] += A[32x16] * B[16x32] in bf16 with fp32 accumulation.
+// Lane l supplies A row (l % 32) and B column (l % 32), reduction slots
+// 8 * (l / 32) .. + 7; it receives D column (l % 32), rows
+// 8 * (e / 4) + 4 * (l / 32) + (e % 4) for accumulator element e.
+__device__ __forceinline__ f32x16 mfma32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// Pack two fp32 into two bf16 (round to nearest even) in one u32.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  bf16x2 v;
+  v[0] = static_cast<__bf16>(lo);
+  v[1] = static_cast<__bf16>(hi);
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// OCP e4m3fn code -> bf16 bits of (value * 2^-8), exact.  The code's bits are
+// placed into an fp16 (exponent bias 15 instead of 7, so the value is scaled
+// by 2^-8; fp16 subnormals carry the e4m3 subnormals), widened to fp32 and
+// truncated to bf16 (at most 4 significant bits, so no rounding happens).
+__device__ __forceinline__ uint32_t e4m3_to_bf16_scaled(uint32_t c) {
+  uint16_t h = static_cast<uint16_t>(((c & 0x80u) << 8) | ((c & 0x7Fu) << 7));
+  float f = static_cast<float>(__builtin_bit_cast(_Float16, h));
+  return __float_as_uint(f) >> 16;
+}
+
+// 4 e4m3 codes (one u32) -> 4 bf16 (two u32), each scaled by 2^-8.
+__device__ __forceinline__ u32x2 e4m3x4_to_bf16x4(uint32_t w) {
+  u32x2 r;
+  r[0] = e4m3_to_bf16_scaled(w & 0xFF) | (e4m3_to_bf16_scaled((w >> 8) & 0xFF) << 16);
+  r[1] = e4m3_to_bf16_scaled((w >> 16) & 0xFF) | (e4m3_to_bf16_scaled(w >> 24) << 16);
+  return r;
+}
+
+// ---------------------------------------------------------------- launchers
+// Each returns hipSuccess or the HIP error of the launch.
+
+// Index branch.  block_idx rows: [batch][H_kv][q_count][k].
+hipError_t launch_index_topk(const uint16_t* q_idx, const uint16_t* k_idx, int batch, int64_t N,
+                             int H_kv, int d_idx, int k, int64_t q_begin, int64_t q_count,
+                             int32_t* block_idx, hipStream_t stream);
+
+// Inversion scratch layout (all offsets in 4-byte words, 256-byte aligned).
+struct SchedLayout {
+  int64_t nbins;       // batch * H_kv * B_c
+  int64_t B_c;         // key blocks visible to the range
+  int64_t T64;         // 64-row query tiles of the range
+  int64_t qpi;         // queries per attention work item
+  int64_t off_items;   // item_prefix [nbins + 1]
+  int64_t off_tot;     // per-bin totals [nbins]
+  int64_t off_bad;     // per-tile out-of-range counts [batch * H_kv * T64]
+  int64_t off_cnt;     // per-(seq, tile, bin) counts / column prefixes
+  int64_t words;       // total size in words
+};
+// Header words at the start of the scratch buffer.
+enum { kHdrItems = 0, kHdrBad = 1, kHdrWords = 64 };
+
+SchedLayout sched_layout(int batch, int H_kv, int G, int64_t q_begin, int64_t q_count);
+
+hipError_t launch_invert(const int32_t* block_idx, int batch, int H_kv, int G, int k,
+                         int64_t q_begin, int64_t q_count, int32_t* blk_offsets,
+                         int32_t* blk_entries, int32_t* sched, hipStream_t stream);
+
+// Upper bound on the attention work items of a range (grid size).
+int64_t attn_max_items(int batch, int H_kv, int G, int k, int64_t q_begin, int64_t q_count);
+
+hipError_t launch_sparse_attn(const void* q, const void* k, const void* v, bool fp8, int batch,
+                              int64_t N, int H_kv, int G, int kslots, float scale_log2,
+                              float out_scale, const int32_t* blk_offsets,
+                              const int32_t* blk_entries, const int32_t* sched, int64_t q_begin,
+                              int64_t q_count, uint16_t* o_part, float* lse_part,
+                              hipStream_t stream);
+
+hipError_t launch_combine(const int32_t* block_idx, const uint16_t* o_part, const float* lse_part,
+                          int batch, int64_t N, int H_kv, int G, int k, int64_t q_begin,
+                          int64_t q_count, uint16_t* o, float* lse, hipStream_t stream);
+
+}  // namespace msa

@@ -1,0 +1,217 @@
+/*
+ * msa.h -- C ABI of the MiniMax Sparse Attention (MSA) forward pass for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * What the library computes (notation of the pages):
+ *   N tokens, H_q query heads, H_kv key/value heads, G = H_q / H_kv query heads
+ *   per GQA group (adjacent heads: head h belongs to group r = h / G), head
+ *   dimension d_h, index head dimension d_idx, key blocks of B_k tokens,
+ *   k selected blocks per (query, group).
+ *   - Index branch: for query i and group r, block b < L = floor(i / B_k) scores
+ *     max_{j in block b} Q^idx[i, r] . K^idx[j]; the k - 1 best blocks are kept
+ *     together with the local block L ("MiniMax Sparse Attention (MSA)",
+ *     Deep Dive > Index Branch Architecture; Training Stability Mechanisms).
+ *   - Main branch: each query head attends, with exact softmax, to the causally
+ *     visible tokens of the selected blocks of its group, using the group's
+ *     K/V head ("MiniMax Sparse Attention", sec. 2.1-2.2).
+ *   - Execution: the selection is inverted into per-(group, block) query lists,
+ *     each selected K/V block is loaded once and attended by all queries that
+ *     picked it (KV-outer), one partial output per (query, block) is written,
+ *     and a combine step merges the partials by log-sum-exp ("MiniMax Sparse
+ *     Attention", sec. 4.2; "MiniMax Sparse Attention (MSA)", Deep Dive >
+ *     KV-Outer Sparse Attention; "Optimizing MiniMax M3 Sparse Attention on
+ *     NVIDIA Blackwell", sec. 1).
+ *
+ * Conventions for every entry point:
+ *   - Tensor arguments are DEVICE pointers owned by the caller.  The library
+ *     never allocates, frees or synchronises, except msa_invert_status, which
+ *     synchronises the given stream.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     All work is enqueued asynchronously on it.
+ *   - Every call validates its arguments on the host first.  On any error it
+ *     returns a nonzero status, enqueues nothing and writes nothing.  No call
+ *     throws or aborts across the ABI.
+ *   - All device pointers must be 16-byte aligned (MSA_ERR_ALIGN otherwise).
+ *   - bf16 is bfloat16 (upper half of IEEE binary32); fp8 is OCP FP8 E4M3
+ *     ("e4m3fn", max 448).
+ *   - Query rows are processed in a range [q_begin, q_begin + q_count); the
+ *     keys visible to that range are [0, q_begin + q_count).  q_begin must be
+ *     a multiple of B_k.  B_c = ceil((q_begin + q_count) / B_k) is the number
+ *     of key blocks of the range.
+ *
+ * Supported shapes (MSA_ERR_UNSUPPORTED otherwise): d_h = 128, B_k = 128,
+ * d_idx in {64, 128}, G in {1, 2, 4, 8, 16}, 1 <= k <= 32, B_c <= 16384
+ * (N <= 2,097,152), batch * H_kv * q_count * k < 2^31.
+ */
+#ifndef MSA_H
+#define MSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MSA_ABI_VERSION 1
+
+enum msa_status_code {
+    MSA_OK = 0,
+    MSA_ERR_NULL = 1,        /* a required pointer is NULL */
+    MSA_ERR_SHAPE = 2,       /* inconsistent sizes (e.g. H_q != G * H_kv) or range */
+    MSA_ERR_UNSUPPORTED = 3, /* valid but outside the supported shapes above */
+    MSA_ERR_ALIGN = 4,       /* a device pointer is not 16-byte aligned */
+    MSA_ERR_WORKSPACE = 5,   /* workspace smaller than the size query returned */
+    MSA_ERR_HIP = 6          /* a HIP runtime call failed (see msa_last_hip_error) */
+};
+
+enum msa_dtype_code {
+    MSA_DTYPE_BF16 = 0,
+    MSA_DTYPE_FP8_E4M3 = 1
+};
+
+/* Problem sizes, in the pages' notation. */
+typedef struct msa_dims {
+    int32_t batch; /* independent sequences */
+    int32_t H_q;   /* query heads */
+    int32_t H_kv;  /* key/value heads = GQA groups = index query heads */
+    int32_t G;     /* query heads per group; must equal H_q / H_kv */
+    int32_t d_h;   /* head dimension of Q, K, V */
+    int32_t d_idx; /* head dimension of Q^idx, K^idx */
+    int32_t B_k;   /* tokens per key block */
+    int32_t k;     /* blocks selected per (query, group), local block included */
+    int64_t N;     /* sequence length (queries = keys) */
+} msa_dims;
+
+/* Options of the main branch. */
+typedef struct msa_opts {
+    int32_t qkv_dtype;   /* MSA_DTYPE_BF16 or MSA_DTYPE_FP8_E4M3 for Q, K, V */
+    float softmax_scale; /* <= 0 selects 1 / sqrt(d_h) */
+    float q_scale;       /* fp8 only: real value = code * scale; ignored for bf16 */
+    float k_scale;
+    float v_scale;
+    int32_t reserved;    /* must be 0 */
+    int64_t q_chunk;     /* msa_forward only: 0 = all N rows at once; else a
+                            positive multiple of B_k, rows processed per pass */
+} msa_opts;
+
+/* Library identity and diagnostics. */
+int msa_abi_version(void);
+const char *msa_status_string(int status);
+/* hipError_t of the last failed HIP call on this thread (0 if none). */
+int msa_last_hip_error(void);
+
+/*
+ * msa_index_topk -- index branch: block scores, causal block max-pool and
+ * top-k with the forced local block.
+ * ("MiniMax Sparse Attention (MSA)", Deep Dive > Index Branch Architecture and
+ *  Exp-Free TopK Kernel; "Flash-MSA", Forward > Proxy attention.)
+ *
+ *   q_idx      bf16 [batch][N][H_kv][d_idx]   index queries (one head per group)
+ *   k_idx      bf16 [batch][N][d_idx]         the single shared index key head
+ *   block_idx  int32 [batch][H_kv][q_count][k] output: row i - q_begin of group r
+ *              lists the selected block ids in ascending order, padded with -1.
+ *              The local block L = floor(i / B_k) is always present and is the
+ *              last valid entry; when L < k all blocks 0..L are selected.
+ * Selection is on the unscaled fp32 dot products (the 1/sqrt(d_idx) factor
+ * does not change the order); equal scores rank the smaller block id first.
+ */
+int msa_index_topk(const msa_dims *dims, const void *q_idx, const void *k_idx,
+                   int64_t q_begin, int64_t q_count, int32_t *block_idx, void *stream);
+
+/*
+ * msa_invert_workspace_size -- bytes of the device scratch buffer `sched` used by
+ * msa_invert_blocks and read by msa_sparse_attn_fwd for the same range.
+ */
+int msa_invert_workspace_size(const msa_dims *dims, int64_t q_begin, int64_t q_count,
+                              size_t *bytes);
+
+/*
+ * msa_invert_blocks -- invert the selection B[batch, group, query, slot] -> block
+ * into B*[batch, group, block] -> queries, and build the pre-scheduled work
+ * list of the KV-outer attention ("Flash-MSA", Backward; "MiniMax Sparse
+ * Attention (MSA)", Deep Dive > KV-Outer Sparse Attention, steps 1 and 5).
+ *
+ *   block_idx    int32 [batch][H_kv][q_count][k] as written by msa_index_topk
+ *                (any valid selection: ids in [0, floor(i / B_k)], no repeats
+ *                within a row, -1 for empty slots).
+ *   blk_offsets  int32 [batch][H_kv][B_c + 1] output: bin (bh, b) owns entries
+ *                [blk_offsets[bh][b], blk_offsets[bh][b + 1]); the offsets are
+ *                absolute positions in blk_entries (bins are laid out in
+ *                (bh, b) order, so blk_offsets[bh][B_c] == blk_offsets[bh+1][0]).
+ *   blk_entries  int32 [batch * H_kv * q_count * k] output (capacity): entry
+ *                value (i - q_begin) * k + slot, ascending in i within a bin.
+ *   sched        device scratch of msa_invert_workspace_size bytes; on return it
+ *                holds the work list for msa_sparse_attn_fwd.
+ * Ids outside [0, floor(i / B_k)] are skipped and counted (msa_invert_status).
+ */
+int msa_invert_blocks(const msa_dims *dims, const int32_t *block_idx, int64_t q_begin,
+                      int64_t q_count, int32_t *blk_offsets, int32_t *blk_entries, void *sched,
+                      size_t sched_bytes, void *stream);
+
+/*
+ * msa_invert_status -- synchronises `stream`, then reports how many block ids
+ * the last msa_invert_blocks call on `sched` skipped as out of range.
+ */
+int msa_invert_status(const void *sched, int32_t *bad_ids, void *stream);
+
+/*
+ * msa_sparse_attn_fwd -- KV-outer block-sparse attention: for every (group,
+ * selected block), the K/V block is staged once and every query that selected
+ * it is attended with exact softmax over the block's causally visible tokens.
+ * ("MiniMax Sparse Attention", sec. 4.2; "MiniMax Sparse Attention (MSA)",
+ *  Deep Dive > KV-Outer Sparse Attention, steps 2-6.)
+ *
+ *   q         [batch][N][H_q][d_h]   bf16 or fp8 codes (opts->qkv_dtype)
+ *   k, v      [batch][N][H_kv][d_h]  same dtype
+ *   blk_offsets, blk_entries, sched  as produced by msa_invert_blocks for the
+ *             same (q_begin, q_count)
+ *   o_part    bf16 [batch][H_kv][q_count][k][G][d_h] output: per (query, slot,
+ *             head) the block's normalised partial output
+ *             sum_j softmax_j V[j] over the block's visible tokens j
+ *   lse_part  fp32 [batch][H_kv][q_count][k][G] output: natural-log
+ *             log-sum-exp of the scaled scores over the same tokens
+ * Only slots that hold a block are written.
+ */
+int msa_sparse_attn_fwd(const msa_dims *dims, const msa_opts *opts, const void *q,
+                        const void *k, const void *v, const int32_t *blk_offsets,
+                        const int32_t *blk_entries, const void *sched, int64_t q_begin,
+                        int64_t q_count, void *o_part, float *lse_part, void *stream);
+
+/*
+ * msa_combine -- split-K log-sum-exp merge of the partials of each query
+ * ("MiniMax Sparse Attention (MSA)", Deep Dive > KV-Outer Sparse Attention,
+ *  step 6): LSE = ln sum_s exp(lse_s), O = sum_s exp(lse_s - LSE) * Obar_s over
+ *  the slots s whose block_idx entry is >= 0.
+ *
+ *   block_idx  int32 [batch][H_kv][q_count][k]
+ *   o_part, lse_part  as written by msa_sparse_attn_fwd
+ *   o          bf16 [batch][N][H_q][d_h] output, rows [q_begin, q_begin + q_count)
+ *   lse        fp32 [batch][N][H_q] output (may be NULL): the main-branch LSE
+ */
+int msa_combine(const msa_dims *dims, const int32_t *block_idx, const void *o_part,
+                const float *lse_part, int64_t q_begin, int64_t q_count, void *o, float *lse,
+                void *stream);
+
+/*
+ * msa_workspace_size / msa_forward -- the whole forward pass: for each chunk of
+ * opts->q_chunk query rows (all N at once when 0): index_topk, invert_blocks,
+ * sparse_attn_fwd, combine.  The workspace (device memory, at least
+ * msa_workspace_size bytes, 256-byte aligned) holds the per-chunk selection,
+ * inverted index, work list and partial outputs.
+ *
+ *   q, k, v        as for msa_sparse_attn_fwd
+ *   q_idx, k_idx   as for msa_index_topk
+ *   o, lse         as for msa_combine (all N rows); lse may be NULL
+ *   block_idx_out  int32 [batch][H_kv][N][k] (may be NULL): the selection
+ */
+int msa_workspace_size(const msa_dims *dims, const msa_opts *opts, size_t *bytes);
+int msa_forward(const msa_dims *dims, const msa_opts *opts, const void *q, const void *k,
+                const void *v, const void *q_idx, const void *k_idx, void *o, float *lse,
+                int32_t *block_idx_out, void *workspace, size_t ws_bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MSA_H */

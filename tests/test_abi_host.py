@@ -1,0 +1,124 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports
+every entry point the header declares, and rejects bad arguments before any
+HIP call."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import block_sparse_attention_idx_amd as msa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "msa.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(msa_[a-z_0-9]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(msa.LIB_PATH):
+        import __graft_entry__
+        __graft_entry__.build()
+    return msa.lib()
+
+
+def test_exports_every_declared_symbol(L):
+    names = declared_functions()
+    assert len(names) >= 11
+    out = subprocess.run(["nm", "-D", "--defined-only", msa.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (msa_[a-z_0-9]+)", out))
+    missing = [n for n in names if n not in exported]
+    assert not missing, missing
+    for n in names:
+        assert hasattr(L, n)
+    assert set(msa.EXPORTS) <= set(names)
+
+
+def test_identity(L):
+    assert L.msa_abi_version() == 1
+    assert L.msa_status_string(0) == b"ok"
+    assert L.msa_status_string(5) == b"workspace too small"
+
+
+FAKE = ctypes.c_void_p(0x10000)       # never dereferenced: every call below fails validation
+ODD = ctypes.c_void_p(0x10008)
+
+
+def dims(**kw):
+    base = dict(batch=1, N=2048, H_q=8, H_kv=2, d_h=128, d_idx=64, B_k=128, k=4)
+    G = kw.pop("G", None)
+    base.update(kw)
+    d = msa.make_dims(**base)
+    if G is not None:
+        d.G = G
+    return d
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(H_q=9), 2), (dict(G=3), 2), (dict(N=0), 2), (dict(k=0), 2), (dict(batch=0), 2),
+    (dict(d_h=64), 3), (dict(B_k=64), 3), (dict(d_idx=96), 3), (dict(k=33), 3),
+    (dict(H_q=6, H_kv=2), 3), (dict(N=16384 * 128 + 1), 3),
+])
+def test_index_topk_rejects_bad_dims(L, kw, status):
+    d = dims(**kw)
+    assert L.msa_index_topk(ctypes.byref(d), FAKE, FAKE, 0, 16, FAKE, None) == status
+
+
+@pytest.mark.parametrize("qb,qn,status", [(-128, 16, 2), (0, 0, 2), (64, 16, 2), (0, 2049, 2),
+                                          (1920, 200, 2)])
+def test_ranges(L, qb, qn, status):
+    d = dims()
+    assert L.msa_index_topk(ctypes.byref(d), FAKE, FAKE, qb, qn, FAKE, None) == status
+    assert L.msa_combine(ctypes.byref(d), FAKE, FAKE, FAKE, qb, qn, FAKE, None, None) == status
+
+
+def test_null_and_alignment(L):
+    d = dims()
+    assert L.msa_index_topk(ctypes.byref(d), None, FAKE, 0, 16, FAKE, None) == 1
+    assert L.msa_index_topk(ctypes.byref(d), FAKE, ODD, 0, 16, FAKE, None) == 4
+    assert L.msa_index_topk(None, FAKE, FAKE, 0, 16, FAKE, None) == 1
+    assert L.msa_combine(ctypes.byref(d), FAKE, FAKE, FAKE, 0, 16, FAKE, ODD, None) == 4
+    o = msa.make_opts()
+    assert L.msa_sparse_attn_fwd(ctypes.byref(d), ctypes.byref(o), FAKE, FAKE, FAKE, FAKE, FAKE,
+                                 None, 0, 16, FAKE, FAKE, None) == 1
+
+
+def test_workspace_and_opts(L):
+    d = dims()
+    n = ctypes.c_size_t(0)
+    assert L.msa_invert_workspace_size(ctypes.byref(d), 0, 2048, ctypes.byref(n)) == 0
+    assert n.value > 0
+    assert L.msa_invert_blocks(ctypes.byref(d), FAKE, 0, 2048, FAKE, FAKE, FAKE, n.value - 4,
+                               None) == 5
+    o = msa.make_opts()
+    assert L.msa_workspace_size(ctypes.byref(d), ctypes.byref(o), ctypes.byref(n)) == 0
+    ws = n.value
+    # partial buffers dominate: k * G * (2 d_h + 4) bytes per (query, group)
+    assert ws >= 2048 * 2 * 4 * 4 * (2 * 128 + 4)
+    assert L.msa_forward(ctypes.byref(d), ctypes.byref(o), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                         None, None, FAKE, ws - 256, None) == 5
+    bad = msa.make_opts(q_chunk=100)
+    assert L.msa_workspace_size(ctypes.byref(d), ctypes.byref(bad), ctypes.byref(n)) == 2
+    bad = msa.make_opts(dtype="fp8", q_scale=0.0)
+    assert L.msa_workspace_size(ctypes.byref(d), ctypes.byref(bad), ctypes.byref(n)) == 2
+    bad = msa.make_opts()
+    bad.qkv_dtype = 7
+    assert L.msa_workspace_size(ctypes.byref(d), ctypes.byref(bad), ctypes.byref(n)) == 3
+    # chunking shrinks the workspace
+    c = msa.make_opts(q_chunk=512)
+    assert L.msa_workspace_size(ctypes.byref(d), ctypes.byref(c), ctypes.byref(n)) == 0
+    assert n.value < ws
+
+
+def test_binding_raises_when_library_missing(monkeypatch):
+    monkeypatch.setattr(msa, "_lib", None)
+    monkeypatch.setattr(msa, "LIB_PATH", "/nonexistent/libmsa.so")
+    with pytest.raises(msa.MSAError):
+        msa.lib()

@@ -1,0 +1,321 @@
+"""Parity of the HIP path (called through the C ABI) with the CPU oracle.
+
+Small cases compare every row; the full-size workloads compare sampled rows in
+the same launch configuration the benchmark times (msa_forward over the whole
+sequence, or over 32,768-row chunks for the 1M case).
+"""
+import numpy as np
+import pytest
+import torch
+
+import block_sparse_attention_idx_amd as msa
+import oracle
+import synth
+from gpu_util import (admissible, check_selection, compact_attention_rows, device_inputs,
+                      dims_of, err_stats, log, opts_of, oracle_index_rows, sample_rows)
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0")
+TINY = synth.TINY
+
+
+@pytest.fixture(autouse=True)
+def _gpu_cleanup():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    if not msa.LIB_PATH or not __import__("os").path.exists(msa.LIB_PATH):
+        pytest.fail("libmsa.so is not built")
+    yield
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+# --------------------------------------------------------------------------- inputs
+
+def test_device_generator_matches_host():
+    for w in (TINY.with_(N=1000, plant=4), TINY.with_(N=640, dtype="fp8")):
+        log(f"generator {w.name} N={w.N} dtype={w.dtype} plant={w.plant}")
+        t = device_inputs(w, DEV)
+        rows = np.array([0, 5, 127, 128, 300, w.N - 1])
+        for x in ("q", "k", "v", "q_idx", "k_idx"):
+            dv = t[x]
+            dv = dv.view(torch.int16) if dv.dtype == torch.bfloat16 else dv
+            got = dv.cpu().numpy().reshape(w.N, -1)[rows]
+            want = synth.host_rows(w, x, rows).reshape(len(rows), -1)
+            assert np.array_equal(got.view(want.dtype), want), x
+
+
+# --------------------------------------------------------------------------- index branch
+
+INDEX_CASES = [
+    TINY,
+    TINY.with_(N=1000),                                   # ragged last block
+    TINY.with_(N=1),
+    TINY.with_(N=100),
+    TINY.with_(k=1),
+    TINY.with_(k=2, d_idx=128),
+    TINY.with_(k=16),                                     # k * B_k >= N: all causal blocks
+    TINY.with_(N=5000, k=32, d_idx=128),
+    TINY.with_(N=3000, k=7, H_q=4, H_kv=1),
+    TINY.with_(N=2500, k=5, H_q=64, H_kv=4, d_idx=128),
+    TINY.with_(batch=2, N=1300),
+]
+
+
+@pytest.mark.parametrize("w", INDEX_CASES, ids=lambda w: f"N{w.N}_hkv{w.H_kv}_d{w.d_idx}_k{w.k}_b{w.batch}")
+def test_index_topk_parity(w):
+    log(f"index_topk N={w.N} H_kv={w.H_kv} d_idx={w.d_idx} k={w.k} batch={w.batch}")
+    t = device_inputs(w, DEV)
+    d = dims_of(w)
+    bi = msa.msa_index_topk(d, t["q_idx"], t["k_idx"]).cpu().numpy()
+    rows = np.arange(w.N)
+    for b in range(w.batch):
+        ob, marg, M = oracle_index_rows(w, rows, bat=b)
+        st = check_selection(bi[b], ob, marg, M, w.k, what=f"batch {b}")
+        log(f"  batch {b}: {st}")
+
+
+def test_index_topk_chunk_offsets():
+    """A range [q_begin, q_begin + q_count) gives the rows of the full call."""
+    w = TINY.with_(N=3000, k=6)
+    t = device_inputs(w, DEV)
+    d = dims_of(w)
+    full = msa.msa_index_topk(d, t["q_idx"], t["k_idx"]).cpu().numpy()
+    for qb, qn in ((0, 640), (640, 1000), (2048, 952), (2944, 56)):
+        log(f"index_topk range {qb}+{qn}")
+        part = msa.msa_index_topk(d, t["q_idx"], t["k_idx"], qb, qn).cpu().numpy()
+        assert np.array_equal(part, full[:, :, qb:qb + qn])
+
+
+# --------------------------------------------------------------------------- inversion
+
+def _random_selection(rng, H, n, q_begin, B_k, k, hot=None):
+    out = np.full((H, n, k), -1, np.int32)
+    for r in range(H):
+        for j in range(n):
+            L = (q_begin + j) // B_k
+            if L == 0:
+                out[r, j, 0] = 0
+                continue
+            p = np.ones(L)
+            if hot is not None:
+                p[hot[hot < L]] *= 20.0
+            p /= p.sum()
+            others = rng.choice(L, size=min(k - 1, L), replace=False, p=p)
+            v = np.sort(np.concatenate([others, [L]]))
+            out[r, j, :len(v)] = v
+    return out
+
+
+@pytest.mark.parametrize("batch,H,N,q_begin,q_count,k,G", [
+    (1, 2, 2048, 0, 2048, 4, 4), (1, 4, 3000, 0, 3000, 16, 16), (2, 2, 1500, 512, 988, 5, 2),
+    (1, 1, 9000, 8192, 808, 8, 1), (1, 3, 700, 0, 700, 32, 8),
+])
+def test_invert_parity(batch, H, N, q_begin, q_count, k, G):
+    log(f"invert batch={batch} H_kv={H} N={N} range={q_begin}+{q_count} k={k} G={G}")
+    rng = np.random.default_rng(N + k)
+    B_c = -(-(q_begin + q_count) // 128)
+    hot = rng.choice(B_c, size=min(4, B_c), replace=False)
+    sel = np.stack([_random_selection(rng, H, q_count, q_begin, 128, k, hot) for _ in range(batch)])
+    d = msa.make_dims(batch, N, H * G, H, 128, 64, 128, k)
+    bi = torch.from_numpy(sel).to(DEV)
+    off, ent, sched = msa.msa_invert_blocks(d, bi, q_begin, q_count)
+    assert msa.msa_invert_status(sched) == 0
+    ooff, oent = oracle.invert(sel.reshape(batch * H, q_count, k), B_c)
+    assert np.array_equal(off.cpu().numpy().reshape(batch * H, B_c + 1), ooff)
+    assert np.array_equal(ent.cpu().numpy()[: len(oent)], oent)
+
+
+def test_invert_counts_out_of_range_ids():
+    w = TINY.with_(N=1024, k=4)
+    rng = np.random.default_rng(3)
+    sel = _random_selection(rng, 2, 1024, 0, 128, 4)
+    sel[0, 500, 0] = 9          # beyond the row's local block
+    sel[1, 7, 1] = -5           # negative, not the -1 padding
+    d = dims_of(w)
+    off, ent, sched = msa.msa_invert_blocks(d, torch.from_numpy(sel[None]).to(DEV))
+    assert msa.msa_invert_status(sched) == 2
+    keep = sel.copy()
+    keep[0, 500, 0] = -1
+    keep[1, 7, 1] = -1
+    ooff, oent = oracle.invert(keep, 8)
+    assert np.array_equal(off.cpu().numpy().reshape(2, 9), ooff)
+    assert np.array_equal(ent.cpu().numpy()[: len(oent)], oent)
+
+
+# --------------------------------------------------------------------------- attention + combine
+
+ATTN_CASES = [
+    TINY,
+    TINY.with_(N=1000, k=3),
+    TINY.with_(N=700, k=2, H_q=2, H_kv=2),               # G = 1
+    TINY.with_(N=900, k=5, H_q=4, H_kv=2),               # G = 2
+    TINY.with_(N=1200, k=4, H_q=16, H_kv=2),             # G = 8
+    TINY.with_(N=1536, k=16, H_q=32, H_kv=2),            # G = 16, all causal blocks
+    TINY.with_(N=777, k=4, dtype="fp8"),
+    TINY.with_(N=1300, k=4, batch=2, H_q=16, H_kv=4),
+]
+
+
+def _oracle_partials(w, sel, rows):
+    """Oracle partial (Obar, lse) of every (row, slot): attention over that one block."""
+    H = w.H_kv
+    code = oracle.FP8 if w.dtype == "fp8" else oracle.BF16
+    sc = synth.fp8_scale() if w.dtype == "fp8" else 1.0
+    q = synth.host_rows(w, "q", rows)
+    K = synth.host_all(w, "k")[: w.N]
+    V = synth.host_all(w, "v")[: w.N]
+    parts = []
+    for s in range(w.k):
+        one = np.full((H, len(rows), w.k), -1, np.int32)
+        one[:, :, 0] = sel[:, :, s]
+        valid = sel[:, :, s] >= 0
+        one[:, :, 0] = np.where(valid, sel[:, :, s], sel[:, :, 0])
+        O, lse = oracle.attention(w.N, w.B_k, rows, q, K, V, one, dtype=code, q_scale=sc,
+                                  k_scale=sc, v_scale=sc)
+        parts.append((O, lse, valid))
+    return parts
+
+
+@pytest.mark.parametrize("w", ATTN_CASES, ids=lambda w: f"N{w.N}_G{w.G}_k{w.k}_{w.dtype}_b{w.batch}")
+def test_attention_and_combine_parity(w):
+    """Feed the oracle's selection to the GPU inversion, attention and combine."""
+    log(f"attention N={w.N} H_q={w.H_q} H_kv={w.H_kv} k={w.k} dtype={w.dtype} batch={w.batch}")
+    t = device_inputs(w, DEV)
+    d, o = dims_of(w), opts_of(w)
+    tol_max = 6e-2 if w.dtype == "fp8" else 2e-2
+    rows = np.arange(w.N)
+    sels = []
+    for b in range(w.batch):
+        ob, _, _ = oracle_index_rows(w, rows, bat=b)
+        sels.append(ob)
+    sel = np.stack(sels)
+    bi = torch.from_numpy(sel).to(DEV)
+    off, ent, sched = msa.msa_invert_blocks(d, bi)
+    q, k, v = t["q"], t["k"], t["v"]
+    opart, lpart = msa.msa_sparse_attn_fwd(d, o, q, k, v, off, ent, sched)
+    out, lse = msa.msa_combine(d, bi, opart, lpart, want_lse=True)
+    torch.cuda.synchronize()
+    opart = opart.float().cpu().numpy()
+    lpart = lpart.cpu().numpy()
+    out = out.float().cpu().numpy()
+    lse = lse.cpu().numpy()
+    G = w.G
+    for b in range(w.batch):
+        # partials per slot (batch 0 only: the oracle helper reads batch-0 rows)
+        if b == 0:
+            for s, (Os, ls, valid) in enumerate(_oracle_partials(w, sel[0], rows)):
+                for r in range(w.H_kv):
+                    m = valid[r]
+                    got = opart[0, r, m, s]                       # [n, G, d_h]
+                    ref = Os[m][:, r * G:(r + 1) * G]
+                    mx, mn = err_stats(got, ref)
+                    assert mx <= tol_max and mn <= 2e-3, (s, r, mx, mn)
+                    lmx, _ = err_stats(lpart[0, r, m, s], ls[m][:, r * G:(r + 1) * G])
+                    assert lmx <= 1e-3, (s, r, lmx)
+        code = oracle.FP8 if w.dtype == "fp8" else oracle.BF16
+        sc = synth.fp8_scale() if w.dtype == "fp8" else 1.0
+        flat = b * w.N + rows
+        O, L = oracle.attention(w.N, w.B_k, rows, synth.host_rows(w, "q", flat),
+                                synth.host_rows(w, "k", b * w.N + np.arange(w.N)),
+                                synth.host_rows(w, "v", b * w.N + np.arange(w.N)), sel[b],
+                                dtype=code, q_scale=sc, k_scale=sc, v_scale=sc)
+        mx, mn = err_stats(out[b], O)
+        log(f"  batch {b}: output max abs {mx:.3g} mean abs {mn:.3g}")
+        assert mx <= tol_max and mn <= 2e-3
+        lmx, _ = err_stats(lse[b], L)
+        assert lmx <= 1e-3
+
+
+def test_combine_parity_random_partials():
+    rng = np.random.default_rng(21)
+    H, n, k, G = 2, 300, 6, 4
+    w = TINY.with_(N=n, k=k, H_q=H * G, H_kv=H)
+    sel = _random_selection(rng, H, n, 0, 128, k)
+    op = synth.f32_to_bf16_bits(rng.standard_normal((H, n, k, G, 128)).astype(np.float32))
+    lp = (3.0 * rng.standard_normal((H, n, k, G))).astype(np.float32)
+    d = dims_of(w)
+    bi = torch.from_numpy(sel[None]).to(DEV)
+    opt = torch.from_numpy(op.view(np.int16)[None].copy()).to(DEV).view(torch.bfloat16)
+    lpt = torch.from_numpy(lp[None]).to(DEV)
+    out, lse = msa.msa_combine(d, bi, opt, lpt, want_lse=True)
+    O, L = oracle.combine(sel, op, lp)
+    mx, mn = err_stats(out.float().cpu().numpy()[0], O)
+    assert mx <= 2e-2 and mn <= 2e-3
+    lmx, _ = err_stats(lse.cpu().numpy()[0], L)
+    assert lmx <= 1e-5
+
+
+# --------------------------------------------------------------------------- whole forward
+
+FWD_CASES = [TINY, TINY.with_(N=1000, k=5), TINY.with_(N=2304, k=4, q_chunk=512),
+             TINY.with_(N=3000, H_q=32, H_kv=2, k=8, d_idx=128, dtype="fp8")]
+
+
+@pytest.mark.parametrize("w", FWD_CASES, ids=lambda w: f"N{w.N}_k{w.k}_{w.dtype}_chunk{w.q_chunk}")
+def test_forward_parity(w):
+    log(f"forward N={w.N} k={w.k} dtype={w.dtype} q_chunk={w.q_chunk}")
+    t = device_inputs(w, DEV)
+    d, o = dims_of(w), opts_of(w)
+    bi = torch.empty((w.batch, w.H_kv, w.N, w.k), dtype=torch.int32, device=DEV)
+    out, lse, _ = msa.msa_forward(d, o, t["q"], t["k"], t["v"], t["q_idx"], t["k_idx"],
+                                  block_idx_out=bi, want_lse=True)
+    torch.cuda.synchronize()
+    gsel = bi.cpu().numpy()[0]
+    rows = np.arange(w.N)
+    ob, marg, M = oracle_index_rows(w, rows)
+    st = check_selection(gsel, ob, marg, M, w.k, what="forward")
+    log(f"  selection: {st}")
+    code = oracle.FP8 if w.dtype == "fp8" else oracle.BF16
+    sc = synth.fp8_scale() if w.dtype == "fp8" else 1.0
+    O, L = oracle.attention(w.N, w.B_k, rows, synth.host_all(w, "q"), synth.host_all(w, "k"),
+                            synth.host_all(w, "v"), gsel, dtype=code, q_scale=sc, k_scale=sc,
+                            v_scale=sc)
+    mx, mn = err_stats(out.float().cpu().numpy()[0], O)
+    log(f"  output max abs {mx:.3g} mean abs {mn:.3g}")
+    assert mx <= (6e-2 if w.dtype == "fp8" else 2e-2) and mn <= 2e-3
+    lmx, _ = err_stats(lse.cpu().numpy()[0], L)
+    assert lmx <= 1e-3
+
+
+def test_forward_chunked_equals_whole_and_deterministic():
+    w = TINY.with_(N=2560, k=6)
+    t = device_inputs(w, DEV)
+    d = dims_of(w)
+    args = (t["q"], t["k"], t["v"], t["q_idx"], t["k_idx"])
+    a, _, _ = msa.msa_forward(d, msa.make_opts(), *args)
+    b, _, _ = msa.msa_forward(d, msa.make_opts(), *args)
+    c, _, _ = msa.msa_forward(d, msa.make_opts(q_chunk=768), *args)
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    assert torch.equal(a.view(torch.int16), c.view(torch.int16))
+
+
+# --------------------------------------------------------------------------- full-size workloads
+
+BIG = [(synth.P16K, 160), (synth.P128K_HOT, 48), (synth.P128K_FP8, 40), (synth.P1M, 32)]
+
+
+@pytest.mark.parametrize("w,nrows", BIG, ids=lambda x: x.name if hasattr(x, "name") else str(x))
+def test_full_size_sampled_parity(w, nrows):
+    log(f"full-size {w.name}: generating inputs")
+    t = device_inputs(w, DEV)
+    d, o = dims_of(w), opts_of(w)
+    bi = torch.empty((w.batch, w.H_kv, w.N, w.k), dtype=torch.int32, device=DEV)
+    log(f"full-size {w.name}: msa_forward q_chunk={w.q_chunk}")
+    out, _, _ = msa.msa_forward(d, o, t["q"], t["k"], t["v"], t["q_idx"], t["k_idx"],
+                                block_idx_out=bi)
+    torch.cuda.synchronize()
+    rows = sample_rows(w.N, w.B_k, nrows, seed=w.seed)
+    gsel = np.ascontiguousarray(bi[0][:, torch.from_numpy(rows).to(DEV)].cpu().numpy())
+    gout = out[0][torch.from_numpy(rows).to(DEV)].float().cpu().numpy()
+    del t, out, bi
+    torch.cuda.empty_cache()
+    log(f"full-size {w.name}: oracle index on {len(rows)} rows")
+    ob, marg, M = oracle_index_rows(w, rows)
+    st = check_selection(gsel, ob, marg, M, w.k, what=w.name)
+    log(f"  selection: {st}")
+    log(f"full-size {w.name}: oracle attention on {len(rows)} rows")
+    O, _ = compact_attention_rows(w, rows, gsel)
+    mx, mn = err_stats(gout, O)
+    log(f"  output max abs {mx:.3g} mean abs {mn:.3g}")
+    assert mx <= (6e-2 if w.dtype == "fp8" else 2e-2) and mn <= 2e-3
