@@ -41,6 +41,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=768,
                     help="query rows of the oracle sample (all heads and groups)")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="first run one plain device-to-device copy of this many MiB (a kernel "
+                         "of known traffic, to calibrate hardware byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the MSA forward path here is a single-GPU "
@@ -56,6 +59,13 @@ def main():
     w = synth.WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.calib_copy_mib > 0:
+        src = torch.ones(args.calib_copy_mib << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"calibration copy: {args.calib_copy_mib} MiB read + {args.calib_copy_mib} MiB written")
+        del src, dst
     log(f"workload {w.name}: generating inputs on the device")
     t = {x: synth.device_tensor(w, x, dev) for x in ("q", "k", "v", "q_idx", "k_idx")}
     d = msa.make_dims(w.batch, w.N, w.H_q, w.H_kv, w.d_h, w.d_idx, w.B_k, w.k)

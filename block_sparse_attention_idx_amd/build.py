@@ -16,31 +16,34 @@ FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
          "-I", os.path.join(ROOT, "include"), "-I", CSRC]
 
 
-def build(verbose: bool = False) -> str:
-    objdir = os.path.join(HERE, "_build")
+def build(verbose: bool = False, defines=None, out: str = OUT) -> str:
+    """Compile every source and link ``out``.  ``defines`` (name -> value)
+    override the build-time tunables of the kernels."""
+    defs = [f"-D{k}={v}" for k, v in (defines or {}).items()]
+    objdir = os.path.join(os.path.dirname(os.path.abspath(out)), "_build")
     os.makedirs(objdir, exist_ok=True)
 
     def compile_one(src):
         obj = os.path.join(objdir, src + ".o")
-        cmd = ["hipcc", "-c", *FLAGS, os.path.join(CSRC, src), "-o", obj]
+        cmd = ["hipcc", "-c", *FLAGS, *defs, os.path.join(CSRC, src), "-o", obj]
         r = subprocess.run(cmd, capture_output=True, text=True)
-        out = "\n".join(l for l in (r.stdout + r.stderr).splitlines()
+        log = "\n".join(l for l in (r.stdout + r.stderr).splitlines()
                         if "packed-fp32-ops" not in l)
         if r.returncode != 0:
-            raise RuntimeError(f"hipcc failed for {src}:\n{out}")
-        if verbose and out.strip():
-            print(out, file=sys.stderr)
+            raise RuntimeError(f"hipcc failed for {src}:\n{log}")
+        if verbose and log.strip():
+            print(log, file=sys.stderr)
         return obj
 
     with ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
         objs = list(ex.map(compile_one, SOURCES))
-    tmp = OUT + ".tmp"
+    tmp = out + ".tmp"
     cmd = ["hipcc", "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}{r.stderr}")
-    os.replace(tmp, OUT)
-    return OUT
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":

@@ -5,10 +5,14 @@
 // whose block id is valid:
 //     LSE = ln sum_s exp(lse_s),   O = sum_s exp(lse_s - LSE) * Obar_s.
 //
-// A pure streaming kernel: the partials of one (query, group) are one
-// contiguous k * G * d_h bf16 slab, read once with 16-byte loads; each thread
-// owns 8 output dimensions of one head.  Output rows (a query's G heads of
-// group r) are contiguous 16-byte stores.
+// A pure streaming kernel.  The partials of one (query, group) are one
+// contiguous k * G * d_h bf16 slab; a workgroup of 256 threads owns
+// 4096 / (G * d_h) (query, group) pairs at a time and every thread 8 output
+// dimensions of one head.  The slot loop is unrolled at compile time so all
+// of a thread's slab loads (16 bytes each, non-temporal: the partials are
+// read exactly once) are in flight together; the selection row and the lse
+// values are read first, the weights computed once per (query, head).
+// Output rows (a query's G heads of group r) are contiguous 16-byte stores.
 #include "msa_internal.h"
 
 namespace msa {
@@ -16,41 +20,59 @@ namespace {
 
 constexpr int kCombThreads = 256;
 
-template <int G>
+template <int G, int KMAX>
 __global__ __launch_bounds__(kCombThreads) void combine_kernel(
     const int32_t* __restrict__ block_idx, const uint16_t* __restrict__ o_part,
     const float* __restrict__ lse_part, int64_t N, int H_kv, int k, int64_t q_begin,
-    int64_t q_count, uint16_t* __restrict__ o, float* __restrict__ lse) {
+    int64_t q_count, int64_t rows_total, uint16_t* __restrict__ o, float* __restrict__ lse) {
   constexpr int TPQ = 16 * G;              // threads per (query, group)
-  constexpr int QPW = kCombThreads / TPQ;  // queries per workgroup
+  constexpr int QPW = kCombThreads / TPQ;  // (query, group) pairs per workgroup
   const int t = threadIdx.x;
-  const int64_t seq = blockIdx.y;
-  const int64_t row = static_cast<int64_t>(blockIdx.x) * QPW + t / TPQ;
-  if (row >= q_count) return;
+  // flat (query, group) index: f = seq * q_count + row, seq = batch * H_kv + r
+  const int64_t f = static_cast<int64_t>(blockIdx.x) * QPW + t / TPQ;
+  if (f >= rows_total) return;
+  const int64_t seq = f / q_count, row = f % q_count;
   const int g = (t % TPQ) >> 4, dc = t & 15;
   const int64_t bat = seq / H_kv;
   const int r = static_cast<int>(seq % H_kv);
-  const int32_t* sel = block_idx + (seq * q_count + row) * k;
-  const int64_t base = (seq * q_count + row) * k;  // slot 0 of this (query, group)
+  const int32_t* sel = block_idx + f * k;
+  const int64_t base = f * k;  // slot 0 of this (query, group)
 
-  float mx = -__builtin_huge_valf();
-  for (int s = 0; s < k; ++s)
-    if (sel[s] >= 0) mx = fmaxf(mx, lse_part[(base + s) * G + g]);
+  bool valid[KMAX];
+  float l[KMAX];
+  u32x4 v[KMAX];
+#pragma unroll
+  for (int s = 0; s < KMAX; ++s) valid[s] = s < k && sel[s] >= 0;
+#pragma unroll
+  for (int s = 0; s < KMAX; ++s) {
+    v[s] = u32x4{0u, 0u, 0u, 0u};
+    if (valid[s])
+      v[s] = __builtin_nontemporal_load(
+          reinterpret_cast<const u32x4*>(o_part + ((base + s) * G + g) * kDh + dc * 8));
+  }
+#pragma unroll
+  for (int s = 0; s < KMAX; ++s) l[s] = valid[s] ? lse_part[(base + s) * G + g] : -__builtin_huge_valf();
+
   constexpr float kLog2e = 1.4426950408889634f;
+  float mx = -__builtin_huge_valf();
+#pragma unroll
+  for (int s = 0; s < KMAX; ++s) mx = fmaxf(mx, l[s]);
   float sum = 0.f;
-  for (int s = 0; s < k; ++s)
-    if (sel[s] >= 0) sum += __builtin_amdgcn_exp2f((lse_part[(base + s) * G + g] - mx) * kLog2e);
+#pragma unroll
+  for (int s = 0; s < KMAX; ++s) {
+    l[s] = valid[s] ? __builtin_amdgcn_exp2f((l[s] - mx) * kLog2e) : 0.f;
+    sum += l[s];
+  }
   const float inv = 1.f / sum;
 
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  for (int s = 0; s < k; ++s) {
-    if (sel[s] < 0) continue;
-    const float w = __builtin_amdgcn_exp2f((lse_part[(base + s) * G + g] - mx) * kLog2e) * inv;
-    const u32x4 v = *reinterpret_cast<const u32x4*>(o_part + ((base + s) * G + g) * kDh + dc * 8);
+#pragma unroll
+  for (int s = 0; s < KMAX; ++s) {
+    const float w = l[s] * inv;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      acc[2 * j] += w * __uint_as_float(v[j] << 16);
-      acc[2 * j + 1] += w * __uint_as_float(v[j] & 0xFFFF0000u);
+      acc[2 * j] += w * __uint_as_float(v[s][j] << 16);
+      acc[2 * j + 1] += w * __uint_as_float(v[s][j] & 0xFFFF0000u);
     }
   }
   const int64_t orow = (bat * N + q_begin + row) * (static_cast<int64_t>(H_kv) * G) + r * G + g;
@@ -60,16 +82,30 @@ __global__ __launch_bounds__(kCombThreads) void combine_kernel(
   if (lse && dc == 0) lse[orow] = mx + __builtin_amdgcn_logf(sum) * 0.69314718055994531f;
 }
 
+template <int G, int KMAX>
+hipError_t launch_gk(const int32_t* block_idx, const uint16_t* o_part, const float* lse_part,
+                     int batch, int64_t N, int H_kv, int k, int64_t q_begin, int64_t q_count,
+                     uint16_t* o, float* lse, hipStream_t stream) {
+  constexpr int QPW = kCombThreads / (16 * G);
+  const int64_t rows_total = static_cast<int64_t>(batch) * H_kv * q_count;
+  const int64_t nx = (rows_total + QPW - 1) / QPW;
+  hipLaunchKernelGGL((combine_kernel<G, KMAX>), dim3(static_cast<unsigned>(nx)),
+                     dim3(kCombThreads), 0, stream, block_idx, o_part, lse_part, N, H_kv, k,
+                     q_begin, q_count, rows_total, o, lse);
+  return hipGetLastError();
+}
+
 template <int G>
 hipError_t launch_g(const int32_t* block_idx, const uint16_t* o_part, const float* lse_part,
                     int batch, int64_t N, int H_kv, int k, int64_t q_begin, int64_t q_count,
                     uint16_t* o, float* lse, hipStream_t stream) {
-  constexpr int QPW = kCombThreads / (16 * G);
-  const int64_t nx = (q_count + QPW - 1) / QPW;
-  hipLaunchKernelGGL(combine_kernel<G>, dim3(static_cast<unsigned>(nx), batch * H_kv),
-                     dim3(kCombThreads), 0, stream, block_idx, o_part, lse_part, N, H_kv, k,
-                     q_begin, q_count, o, lse);
-  return hipGetLastError();
+  if (k <= 4)
+    return launch_gk<G, 4>(block_idx, o_part, lse_part, batch, N, H_kv, k, q_begin, q_count, o, lse, stream);
+  if (k <= 8)
+    return launch_gk<G, 8>(block_idx, o_part, lse_part, batch, N, H_kv, k, q_begin, q_count, o, lse, stream);
+  if (k <= 16)
+    return launch_gk<G, 16>(block_idx, o_part, lse_part, batch, N, H_kv, k, q_begin, q_count, o, lse, stream);
+  return launch_gk<G, 32>(block_idx, o_part, lse_part, batch, N, H_kv, k, q_begin, q_count, o, lse, stream);
 }
 
 }  // namespace

@@ -14,44 +14,46 @@
 //  2. colscan:  exclusive prefix of cnt down each block column (over tiles),
 //               in place; column totals tot[seq][block].
 //  3. binscan:  one workgroup scans the totals over all (seq, block) bins into
-//               absolute CSR offsets, and the per-bin work-item counts
-//               ceil(tot / items) into the work-list prefix.
+//               absolute CSR offsets; then it lists the non-empty segments --
+//               a bin restricted to one query window, in (seq, window, block)
+//               order -- with their start positions in that order.
 //  4. scatter:  the count workgroup's masks are rebuilt and every entry lands at
 //               offset[bin] + colprefix[tile][bin] + popcount(mask below row).
 //
 // Pre-scheduled chunking ("MiniMax Sparse Attention (MSA)", KV-Outer Sparse
-// Attention, step 5): every bin is cut into work items of at most
-// queries_per_item(G) queries with preassigned output slots, so a block that
-// many queries picked is spread over many workgroups.  The attention kernel
-// finds its item by binary search in the work-list prefix.
+// Attention, step 5): the attention pass walks the entries in segment order
+// and splits that sequence evenly over its workgroups, so a block that many
+// queries picked is spread over as many workgroups as its share of the work
+// asks for, and every (query, slot) keeps its own preassigned output slot.
+// The window order keeps the gathered queries of a window in cache while all
+// blocks they picked are processed.
 #include "msa_internal.h"
 
 namespace msa {
 
-SchedLayout sched_layout(int batch, int H_kv, int G, int64_t q_begin, int64_t q_count) {
+SchedLayout sched_layout(int batch, int H_kv, int64_t q_begin, int64_t q_count) {
   SchedLayout s{};
   auto al = [](int64_t w) { return (w + 63) / 64 * 64; };  // 256-byte alignment
+  const int64_t nseq = static_cast<int64_t>(batch) * H_kv;
   s.B_c = (q_begin + q_count + kBk - 1) / kBk;
   s.T64 = (q_count + 63) / 64;
-  s.nbins = static_cast<int64_t>(batch) * H_kv * s.B_c;
-  s.qpi = queries_per_item(G);
+  s.TW = kAttnWindowRows / 64;
+  s.nW = (s.T64 + s.TW - 1) / s.TW;
+  s.nbins = nseq * s.B_c;
+  s.nseg = nseq * s.nW * s.B_c;
   int64_t w = kHdrWords;
-  s.off_items = w;
-  w = al(w + s.nbins + 1);
   s.off_tot = w;
   w = al(w + s.nbins);
   s.off_bad = w;
-  w = al(w + static_cast<int64_t>(batch) * H_kv * s.T64);
+  w = al(w + nseq * s.T64);
+  s.off_ckey = w;
+  w = al(w + s.nseg);
+  s.off_cpre = w;
+  w = al(w + s.nseg + 1);
   s.off_cnt = w;
-  w = al(w + static_cast<int64_t>(batch) * H_kv * s.T64 * s.B_c);
+  w = al(w + nseq * s.T64 * s.B_c);
   s.words = w;
   return s;
-}
-
-int64_t attn_max_items(int batch, int H_kv, int G, int k, int64_t q_begin, int64_t q_count) {
-  const SchedLayout s = sched_layout(batch, H_kv, G, q_begin, q_count);
-  const int64_t entries = static_cast<int64_t>(batch) * H_kv * q_count * k;
-  return entries / s.qpi + s.nbins + 1;
 }
 
 namespace {
@@ -133,28 +135,28 @@ __global__ __launch_bounds__(kScanWaves * 64) void inv_colscan_kernel(
   }
 }
 
-// Single workgroup: exclusive scans over all bins of entry counts (CSR
-// offsets) and of work-item counts (work-list prefix); sums the bad-id counts.
+// Single workgroup.  Part 1: exclusive scan of the entry counts over all bins
+// (CSR offsets) and the sum of the bad-id counts.  Part 2: lengths of the
+// segments (seq, window, block) from the column prefixes, and the compact list
+// of the non-empty ones with their start positions in segment order.  Part 2
+// reads only what earlier kernels wrote.
 constexpr int kBinThreads = 1024;
 
-__global__ __launch_bounds__(kBinThreads) void inv_binscan_kernel(
-    const int32_t* __restrict__ tot, int64_t nbins, int64_t B_c, int qpi,
-    const int32_t* __restrict__ bad, int64_t nbad_slots, int32_t* __restrict__ blk_offsets,
-    int32_t* __restrict__ items, int32_t* __restrict__ hdr) {
-  __shared__ int se[kBinThreads], si[kBinThreads];
-  __shared__ int sbad;
+__device__ __forceinline__ int seg_len(const int32_t* __restrict__ tot, const int32_t* __restrict__ cnt,
+                                       int64_t sgi, int64_t B_c, int64_t T64, int64_t TW,
+                                       int64_t nW) {
+  const int64_t blk = sgi % B_c, sw = sgi / B_c;
+  const int64_t seq = sw / nW, w = sw % nW;
+  const int64_t t0 = w * TW, t1 = t0 + TW;
+  const int lo = cnt[(seq * T64 + t0) * B_c + blk];
+  const int hi = t1 < T64 ? cnt[(seq * T64 + t1) * B_c + blk] : tot[seq * B_c + blk];
+  return hi - lo;
+}
+
+__device__ __forceinline__ void block_exclusive_scan2(int* se, int* si, int& e, int& it) {
   const int t = threadIdx.x;
-  const int64_t per = (nbins + kBinThreads - 1) / kBinThreads;
-  const int64_t b0 = min<int64_t>(nbins, t * per), b1 = min<int64_t>(nbins, b0 + per);
-  int e = 0, it = 0;
-  for (int64_t b = b0; b < b1; ++b) {
-    const int c = tot[b];
-    e += c;
-    it += (c + qpi - 1) / qpi;
-  }
   se[t] = e;
   si[t] = it;
-  if (t == 0) sbad = 0;
   __syncthreads();
   // Hillis-Steele inclusive scan over the per-thread sums.
   for (int d = 1; d < kBinThreads; d <<= 1) {
@@ -164,23 +166,64 @@ __global__ __launch_bounds__(kBinThreads) void inv_binscan_kernel(
     si[t] += ai;
     __syncthreads();
   }
-  int re = se[t] - e, ri = si[t] - it;  // exclusive starts of this thread's range
-  for (int64_t b = b0; b < b1; ++b) {
-    const int64_t seq = b / B_c, blk = b % B_c;
-    const int c = tot[b];
-    blk_offsets[seq * (B_c + 1) + blk] = re;
-    items[b] = ri;
-    re += c;
-    ri += (c + qpi - 1) / qpi;
-    if (blk == B_c - 1) blk_offsets[seq * (B_c + 1) + B_c] = re;
+  e = se[t] - e;  // exclusive starts of this thread's range
+  it = si[t] - it;
+}
+
+__global__ __launch_bounds__(kBinThreads) void inv_binscan_kernel(
+    const int32_t* __restrict__ tot, const int32_t* __restrict__ cnt, int64_t nbins, int64_t B_c,
+    int64_t T64, int64_t TW, int64_t nW, int64_t nseg, const int32_t* __restrict__ bad,
+    int64_t nbad_slots, int32_t* __restrict__ blk_offsets, int32_t* __restrict__ ckey,
+    int32_t* __restrict__ cpre, int32_t* __restrict__ hdr) {
+  __shared__ int se[kBinThreads], si[kBinThreads];
+  __shared__ int sbad;
+  const int t = threadIdx.x;
+  if (t == 0) sbad = 0;
+
+  // ---- part 1: CSR offsets
+  {
+    const int64_t per = (nbins + kBinThreads - 1) / kBinThreads;
+    const int64_t b0 = min<int64_t>(nbins, t * per), b1 = min<int64_t>(nbins, b0 + per);
+    int e = 0, dummy = 0;
+    for (int64_t b = b0; b < b1; ++b) e += tot[b];
+    block_exclusive_scan2(se, si, e, dummy);
+    for (int64_t b = b0; b < b1; ++b) {
+      const int64_t seq = b / B_c, blk = b % B_c;
+      blk_offsets[seq * (B_c + 1) + blk] = e;
+      e += tot[b];
+      if (blk == B_c - 1) blk_offsets[seq * (B_c + 1) + B_c] = e;
+    }
+    int nb = 0;
+    for (int64_t j = t; j < nbad_slots; j += kBinThreads) nb += bad[j];
+    if (nb) atomicAdd(&sbad, nb);
   }
-  int nb = 0;
-  for (int64_t j = t; j < nbad_slots; j += kBinThreads) nb += bad[j];
-  if (nb) atomicAdd(&sbad, nb);
   __syncthreads();
-  if (t == kBinThreads - 1) {
-    items[nbins] = si[t];
-    hdr[kHdrItems] = si[t];
+
+  // ---- part 2: non-empty segments in (seq, window, block) order
+  {
+    const int64_t per = (nseg + kBinThreads - 1) / kBinThreads;
+    const int64_t s0 = min<int64_t>(nseg, t * per), s1 = min<int64_t>(nseg, s0 + per);
+    int pos = 0, nz = 0;
+    for (int64_t g = s0; g < s1; ++g) {
+      const int len = seg_len(tot, cnt, g, B_c, T64, TW, nW);
+      pos += len;
+      nz += len > 0 ? 1 : 0;
+    }
+    block_exclusive_scan2(se, si, pos, nz);
+    for (int64_t g = s0; g < s1; ++g) {
+      const int len = seg_len(tot, cnt, g, B_c, T64, TW, nW);
+      if (len > 0) {
+        ckey[nz] = static_cast<int32_t>(g);
+        cpre[nz] = pos;
+        ++nz;
+        pos += len;
+      }
+    }
+    if (t == kBinThreads - 1) {
+      cpre[nz] = pos;  // total number of entries
+      hdr[kHdrEntries] = pos;
+      hdr[kHdrSegs] = nz;
+    }
   }
   if (t == 0) hdr[kHdrBad] = sbad;
 }
@@ -212,10 +255,10 @@ bool g_lds_attr_set = false;
 
 }  // namespace
 
-hipError_t launch_invert(const int32_t* block_idx, int batch, int H_kv, int G, int k,
+hipError_t launch_invert(const int32_t* block_idx, int batch, int H_kv, int k,
                          int64_t q_begin, int64_t q_count, int32_t* blk_offsets,
                          int32_t* blk_entries, int32_t* sched, hipStream_t stream) {
-  const SchedLayout s = sched_layout(batch, H_kv, G, q_begin, q_count);
+  const SchedLayout s = sched_layout(batch, H_kv, q_begin, q_count);
   const int64_t nseq = static_cast<int64_t>(batch) * H_kv;
   const size_t lds = static_cast<size_t>(s.B_c) * sizeof(unsigned long long);
   if (!g_lds_attr_set) {
@@ -228,7 +271,6 @@ hipError_t launch_invert(const int32_t* block_idx, int batch, int H_kv, int G, i
     g_lds_attr_set = true;
   }
   int32_t* hdr = sched;
-  int32_t* items = sched + s.off_items;
   int32_t* tot = sched + s.off_tot;
   int32_t* bad = sched + s.off_bad;
   int32_t* cnt = sched + s.off_cnt;
@@ -241,8 +283,9 @@ hipError_t launch_invert(const int32_t* block_idx, int batch, int H_kv, int G, i
                      dim3(kScanWaves * 64), 0, stream, cnt, s.B_c, s.T64, tot);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(inv_binscan_kernel, dim3(1), dim3(kBinThreads), 0, stream, tot, s.nbins, s.B_c,
-                     static_cast<int>(s.qpi), bad, nseq * s.T64, blk_offsets, items, hdr);
+  hipLaunchKernelGGL(inv_binscan_kernel, dim3(1), dim3(kBinThreads), 0, stream, tot, cnt, s.nbins,
+                     s.B_c, s.T64, s.TW, s.nW, s.nseg, bad, nseq * s.T64, blk_offsets,
+                     sched + s.off_ckey, sched + s.off_cpre, hdr);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(inv_scatter_kernel, tiles, dim3(kInvThreads), lds, stream, block_idx, k, q_begin,

@@ -18,8 +18,15 @@ constexpr int kBk = 128;   // tokens per key block
 constexpr int kDh = 128;   // head dimension of Q, K, V
 constexpr int kXcds = 8;   // MI355X: workgroups are dealt round-robin to 8 XCDs
 
-// Queries per attention work item: 1024 (query, head) rows = 8 MFMA row tiles.
-__host__ __device__ constexpr int queries_per_item(int G) { return 1024 / G; }
+// Query rows per scheduling window of the attention pass: the (query, slot)
+// entries of a window are processed, block by block, before the next window
+// starts, so the gathered Q rows of a window are re-read while still cached.
+// A multiple of 64; build-time tunable.
+#ifndef MSA_ATTN_WINDOW_ROWS
+#define MSA_ATTN_WINDOW_ROWS 16384
+#endif
+constexpr int64_t kAttnWindowRows = MSA_ATTN_WINDOW_ROWS;
+static_assert(kAttnWindowRows % 64 == 0 && kAttnWindowRows > 0, "window must be whole 64-row tiles");
 
 // ---------------------------------------------------------------- device helpers
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
@@ -68,28 +75,35 @@ hipError_t launch_index_topk(const uint16_t* q_idx, const uint16_t* k_idx, int b
                              int32_t* block_idx, hipStream_t stream);
 
 // Inversion scratch layout (all offsets in 4-byte words, 256-byte aligned).
+// Segments: bin (seq, block) restricted to query window w, ordered
+// (seq, w, block); only the non-empty ones are listed, with their start
+// position in that order.
 struct SchedLayout {
   int64_t nbins;       // batch * H_kv * B_c
   int64_t B_c;         // key blocks visible to the range
   int64_t T64;         // 64-row query tiles of the range
-  int64_t qpi;         // queries per attention work item
-  int64_t off_items;   // item_prefix [nbins + 1]
+  int64_t TW;          // 64-row tiles per scheduling window
+  int64_t nW;          // scheduling windows of the range
+  int64_t nseg;        // batch * H_kv * nW * B_c
   int64_t off_tot;     // per-bin totals [nbins]
   int64_t off_bad;     // per-tile out-of-range counts [batch * H_kv * T64]
-  int64_t off_cnt;     // per-(seq, tile, bin) counts / column prefixes
+  int64_t off_ckey;    // non-empty segment ids [nseg]
+  int64_t off_cpre;    // their start positions [nseg + 1]
+  int64_t off_cnt;     // per-(seq, tile, bin) counts, then column prefixes
   int64_t words;       // total size in words
 };
 // Header words at the start of the scratch buffer.
-enum { kHdrItems = 0, kHdrBad = 1, kHdrWords = 64 };
+enum { kHdrEntries = 0, kHdrBad = 1, kHdrSegs = 2, kHdrWords = 64 };
 
-SchedLayout sched_layout(int batch, int H_kv, int G, int64_t q_begin, int64_t q_count);
+SchedLayout sched_layout(int batch, int H_kv, int64_t q_begin, int64_t q_count);
 
-hipError_t launch_invert(const int32_t* block_idx, int batch, int H_kv, int G, int k,
+hipError_t launch_invert(const int32_t* block_idx, int batch, int H_kv, int k,
                          int64_t q_begin, int64_t q_count, int32_t* blk_offsets,
                          int32_t* blk_entries, int32_t* sched, hipStream_t stream);
 
-// Upper bound on the attention work items of a range (grid size).
-int64_t attn_max_items(int batch, int H_kv, int G, int k, int64_t q_begin, int64_t q_count);
+// Multiply-high reciprocal of a slot count d <= 32 (exact for 31-bit
+// dividends): n / d == umulhi(n, magic) >> shift for d >= 2.
+void kdiv_params(int d, uint32_t* magic, int* shift);
 
 hipError_t launch_sparse_attn(const void* q, const void* k, const void* v, bool fp8, int batch,
                               int64_t N, int H_kv, int G, int kslots, float scale_log2,

@@ -2,11 +2,10 @@
 //
 // What is computed ("MiniMax Sparse Attention", sec. 2.2 and 4.2;
 // "MiniMax Sparse Attention (MSA)", Deep Dive > KV-Outer Sparse Attention):
-// for every work item -- a (sequence, group r, key block b) bin of the
-// inverted index, cut into pieces of at most queries_per_item(G) queries --
-// the K and V rows of block b (head r) are staged in LDS once, and every
-// (query i, head g of group r) that selected the block gets the block's
-// partial softmax attention over its causally visible tokens:
+// for every (sequence, group r, key block b) bin of the inverted index, the K
+// and V rows of block b (head r) are staged in LDS once, and every (query i,
+// head g of group r) that selected the block gets the block's partial softmax
+// attention over its causally visible tokens:
 //     Obar = sum_j softmax(s)_j V_j,  lse = ln sum_j exp(s_j),
 //     s_j = scale * Q[i, rG+g] . K[j, r],  j in block b, j <= i.
 // The causal mask only bites when b is the query's own block.  One (Obar, lse)
@@ -14,23 +13,30 @@
 // by the combine kernel.
 //
 // gfx950 design:
-//  * 4 waves per workgroup, one 128-row MFMA tile at a time: 128 / G queries x
-//    G heads (a query's G heads are contiguous in Q, 256 B each); each wave
-//    owns 32 rows.  K (row-major) and V (transposed) live in XOR-swizzled LDS,
-//    64 KB per workgroup, two workgroups per CU.
-//  * S^T = K_b * Q^T with v_mfma_f32_32x32x16_bf16 (keys on the row dimension).
-//    The accumulator layout then gives every lane 64 of the 128 keys of one
-//    (query, head) row, so the row max and row sum need one half-wave exchange,
-//    and the probabilities feed O^T = V^T * P^T directly as the MFMA B operand
-//    with no shuffle: the reduction slots of each P^T step are exactly the keys
-//    that lane already holds.  The V^T operand rows are permuted so that every
-//    lane ends up with 64 contiguous output dimensions of its row, stored as
-//    eight 16-byte writes.
+//  * Persistent grid of two workgroups per CU.  The (query, slot) entries are
+//    taken in segment order -- (sequence, query window, block), see invert.hip
+//    -- and that sequence is cut into one equal contiguous share per
+//    workgroup: every workgroup gets the same number of entries whatever the
+//    block popularity, and stages a K/V block only when its share moves to the
+//    next segment.
+//  * 4 waves, 256 (query, head) rows per pass: 256 / G entries x G heads (a
+//    query's G heads are contiguous in Q, 256 B each); each wave owns 64 rows
+//    as two 32-row MFMA column tiles, so every K or V^T fragment read from LDS
+//    feeds two MFMAs.  K (row-major) and V (transposed) live in XOR-swizzled
+//    LDS, 64 KB per workgroup.
+//  * S^T = K_b * Q^T with v_mfma_f32_32x32x16_bf16 (keys on the row
+//    dimension): every lane holds 64 of the 128 keys of one (query, head) row,
+//    so the row max and row sum need one half-wave exchange, and the
+//    probabilities feed O^T = V^T * P^T directly as the MFMA B operand with no
+//    shuffle (the reduction slots of each P^T step are exactly the keys that
+//    lane already holds).  The V^T operand rows are permuted so that every
+//    lane ends up with 64 contiguous output dimensions of its row.
+//  * Software pipeline over passes: the Q rows of the next pass are gathered
+//    into registers and the entries of the pass after it are read while the
+//    current pass computes, so a whole pass covers the gather latency.
 //  * Softmax in base 2 (v_exp_f32) with the scale folded in; fp8 (OCP e4m3)
 //    inputs are widened exactly to bf16 while loading and the per-tensor
 //    scales are folded into the softmax scale and the output scale.
-//  * Work items are mapped XCD-aware: consecutive items (same K/V block) run on
-//    the same XCD, so the block is fetched into one L2 instead of eight.
 #include "msa_internal.h"
 
 namespace msa {
@@ -38,16 +44,36 @@ namespace {
 
 constexpr int kAttnThreads = 256;
 
+// Rows per wave: RT column tiles of 32 (query, head) rows.  RT = 2 shares each
+// LDS fragment between two MFMAs but needs ~450 registers (one wave per SIMD);
+// RT = 1 fits two waves per SIMD.  Build-time tunable.
+#ifndef MSA_ATTN_RT
+#define MSA_ATTN_RT 1
+#endif
+constexpr int kRT = MSA_ATTN_RT;
+static_assert(kRT == 1 || kRT == 2, "one or two row tiles per wave");
+constexpr int kWavesPerSimd = kRT == 2 ? 1 : 2;
+constexpr int kPassRows = 4 * 32 * kRT;  // (query, head) rows per pass
+
+// LDS layouts.  Rows are padded rather than swizzled so that every fragment
+// read of a lane is one base address plus a compile-time offset (no per-read
+// address registers):
+//  * K row-major, 272 B per key row: a 16-lane phase of 16-byte reads of rows
+//    n .. n + 15 starts at banks 4n + const, all distinct.
+//  * V^T, 264 B per output-dimension row, row d stored at position
+//    2 (d mod 64) + d / 64: the 32 rows one 8-byte read touches
+//    (d in 0..15 and 64..79, plus 16 dt) land on 32 distinct even banks.
+constexpr int kKStride = 272;
+constexpr int kVStride = 264;
+
 __device__ __forceinline__ int k_lds_off(int key, int c) {  // 16-byte chunk c of key row
-  return key * 256 + ((c ^ (key & 15)) << 4);
+  return key * kKStride + c * 16;
 }
 
-__device__ __forceinline__ int vt_swz(int d) {
-  return (d & 7) | ((d >> 3) & 8) | ((d << 1) & 16);
-}
+__device__ __forceinline__ int vt_row(int d) { return ((d & 63) << 1) | (d >> 6); }
 
 __device__ __forceinline__ int vt_lds_off(int d, int kc) {  // 8-byte chunk kc (4 keys) of row d
-  return d * 256 + ((kc ^ vt_swz(d)) << 3);
+  return vt_row(d) * kVStride + kc * 8;
 }
 
 __device__ __forceinline__ uint32_t half_of(const u32x4& w, int dd) {
@@ -55,237 +81,446 @@ __device__ __forceinline__ uint32_t half_of(const u32x4& w, int dd) {
   return (dd & 1) ? (x >> 16) : (x & 0xFFFFu);
 }
 
+// Stage K (row-major) and V (transposed) of one block of one head into LDS.
+template <bool FP8>
+__device__ __forceinline__ void stage_kv(const uint8_t* __restrict__ kb, const uint8_t* __restrict__ vb,
+                                         int64_t rstride, int nvalid, uint8_t* k_lds,
+                                         uint8_t* vt_lds) {
+  // Staging is rare (once per segment); an opaque copy of the thread id keeps
+  // the compiler from hoisting its ~50 per-lane addresses out of the caller's
+  // loop, where they would stay live across every pass.
+  int tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));
+  // Rows past the end of the sequence (a partial last block) are read from the
+  // last valid row and replaced by zeros, so every load is issued at once.
+  if constexpr (!FP8) {
+    u32x4 w[8];
+#pragma unroll
+    for (int p = 0; p < 8; ++p) {
+      const int key = (tid >> 4) + 16 * p, c = tid & 15;
+      w[p] = *reinterpret_cast<const u32x4*>(kb + min(key, nvalid - 1) * rstride + c * 16);
+    }
+#pragma unroll
+    for (int p = 0; p < 8; ++p) {
+      const int key = (tid >> 4) + 16 * p, c = tid & 15;
+      if (key >= nvalid) w[p] = u32x4{0u, 0u, 0u, 0u};
+      *reinterpret_cast<u32x4*>(k_lds + k_lds_off(key, c)) = w[p];
+    }
+  } else {
+    u32x4 wk[4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const int key = (tid >> 3) + 32 * p, cc = tid & 7;
+      wk[p] = *reinterpret_cast<const u32x4*>(kb + min(key, nvalid - 1) * rstride + cc * 16);
+    }
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const int key = (tid >> 3) + 32 * p, cc = tid & 7;
+      u32x4 w = key < nvalid ? wk[p] : u32x4{0u, 0u, 0u, 0u};
+      const u32x2 a = e4m3x4_to_bf16x4(w[0]), b = e4m3x4_to_bf16x4(w[1]);
+      const u32x2 c2 = e4m3x4_to_bf16x4(w[2]), d2 = e4m3x4_to_bf16x4(w[3]);
+      *reinterpret_cast<u32x4*>(k_lds + k_lds_off(key, 2 * cc)) = u32x4{a[0], a[1], b[0], b[1]};
+      *reinterpret_cast<u32x4*>(k_lds + k_lds_off(key, 2 * cc + 1)) = u32x4{c2[0], c2[1], d2[0], d2[1]};
+    }
+  }
+  const int kc = tid & 31;
+  u32x4 rows[2][4];
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    const int dg = (tid >> 5) + 8 * p;  // 8 output dims d = 8 dg .. 8 dg + 7
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int key = min(4 * kc + j, nvalid - 1);
+      if constexpr (!FP8) {
+        rows[p][j] = *reinterpret_cast<const u32x4*>(vb + key * rstride + dg * 16);
+      } else {
+        const u32x2 w = *reinterpret_cast<const u32x2*>(vb + key * rstride + dg * 8);
+        rows[p][j] = u32x4{w[0], w[1], 0u, 0u};
+      }
+    }
+  }
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    const int dg = (tid >> 5) + 8 * p;
+    u32x4 row[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (4 * kc + j >= nvalid) {
+        row[j] = u32x4{0u, 0u, 0u, 0u};
+      } else if constexpr (!FP8) {
+        row[j] = rows[p][j];
+      } else {
+        const u32x2 a = e4m3x4_to_bf16x4(rows[p][j][0]), b = e4m3x4_to_bf16x4(rows[p][j][1]);
+        row[j] = u32x4{a[0], a[1], b[0], b[1]};
+      }
+    }
+#pragma unroll
+    for (int dd = 0; dd < 8; ++dd) {
+      const int d = 8 * dg + dd;
+      const u32x2 v = {half_of(row[0], dd) | (half_of(row[1], dd) << 16),
+                       half_of(row[2], dd) | (half_of(row[3], dd) << 16)};
+      *reinterpret_cast<u32x2*>(vt_lds + vt_lds_off(d, kc)) = v;
+    }
+  }
+}
+
+// Q fragments (B operand of S^T) of one row: dims 16 ks + 8 h .. + 8.
+template <bool FP8>
+__device__ __forceinline__ void load_q(const uint8_t* __restrict__ qr, int h, bf16x8 (&qf)[8]) {
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) {
+    if constexpr (!FP8) {
+      qf[ks] = as_bf16x8(*reinterpret_cast<const u32x4*>(qr + (16 * ks + 8 * h) * 2));
+    } else {
+      const u32x2 w = *reinterpret_cast<const u32x2*>(qr + 16 * ks + 8 * h);
+      const u32x2 a = e4m3x4_to_bf16x4(w[0]), b = e4m3x4_to_bf16x4(w[1]);
+      qf[ks] = as_bf16x8(u32x4{a[0], a[1], b[0], b[1]});
+    }
+  }
+}
+
+struct AttnSched {
+  int64_t B_c, T64, TW, nW;
+  int64_t off_ckey, off_cpre, off_cnt;
+};
+
 template <int G, bool FP8>
-__global__ __launch_bounds__(kAttnThreads, 2) void sparse_attn_kernel(
+__global__ __launch_bounds__(kAttnThreads, kWavesPerSimd) void sparse_attn_kernel(
     const void* __restrict__ qp, const void* __restrict__ kp, const void* __restrict__ vp,
-    int64_t N, int H_kv, int kslots, float scale_log2, float out_scale,
-    const int32_t* __restrict__ blk_offsets, const int32_t* __restrict__ entries,
-    const int32_t* __restrict__ items, const int32_t* __restrict__ hdr, int64_t nbins, int64_t B_c,
-    int64_t q_begin, int64_t q_count, uint16_t* __restrict__ o_part, float* __restrict__ lse_part) {
-  constexpr int QT = 128 / G;  // queries per 128-row tile
-  constexpr int QPI = queries_per_item(G);
-  constexpr int EB = FP8 ? 1 : 2;  // bytes per Q/K/V element
-  __shared__ __attribute__((aligned(16))) uint8_t k_lds[kBk * kDh * 2];
-  __shared__ __attribute__((aligned(16))) uint8_t vt_lds[kBk * kDh * 2];
-  __shared__ int64_t s_item[4];
+    int64_t N, int H_kv, int kslots, uint32_t kdiv_magic, int kdiv_shift, float scale_log2,
+    float out_scale, const int32_t* __restrict__ blk_offsets, const int32_t* __restrict__ entries,
+    const int32_t* __restrict__ sched, AttnSched sv, int64_t q_begin, int64_t q_count,
+    uint16_t* __restrict__ o_part, float* __restrict__ lse_part) {
+  constexpr int EPP = kPassRows / G;  // entries per pass
+  constexpr int EB = FP8 ? 1 : 2;     // bytes per Q/K/V element
+  __shared__ __attribute__((aligned(16))) uint8_t k_lds[kBk * kKStride];
+  __shared__ __attribute__((aligned(16))) uint8_t vt_lds[kDh * kVStride];
+  __shared__ int s_seg;
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   const int n = lane & 31, h = lane >> 5;
   const int H_q = H_kv * G;
+  const int32_t* ckey = sched + sv.off_ckey;
+  const int32_t* cpre = sched + sv.off_cpre;
+  const int32_t* ccnt = sched + sv.off_cnt;
 
-  if (tid == 0) {
-    const int64_t n_items = hdr[kHdrItems];
-    const int64_t per = (n_items + kXcds - 1) / kXcds;
-    const int64_t x = blockIdx.x % kXcds, j = blockIdx.x / kXcds;
-    const int64_t logical = x * per + j;
-    int64_t ok = 0, bin = 0, e0 = 0, e1 = 0;
-    if (j < per && logical < n_items) {
-      int64_t lo = 0, hi = nbins - 1;  // largest bin with items[bin] <= logical
-      while (lo < hi) {
-        const int64_t mid = (lo + hi + 1) >> 1;
-        if (items[mid] <= logical) lo = mid; else hi = mid - 1;
-      }
-      bin = lo;
-      const int64_t seq = bin / B_c, blk = bin % B_c;
-      const int64_t beg = blk_offsets[seq * (B_c + 1) + blk];
-      const int64_t end = blk_offsets[seq * (B_c + 1) + blk + 1];
-      e0 = beg + (logical - items[bin]) * QPI;
-      e1 = min(end, e0 + QPI);
-      ok = e1 > e0;
+  // This workgroup's share [p0, p1) of the entries in segment order.
+  const int64_t T = sched[kHdrEntries];
+  const int64_t nsegc = sched[kHdrSegs];
+  const int64_t p0 = T * blockIdx.x / gridDim.x;
+  const int64_t p1 = T * (blockIdx.x + 1) / gridDim.x;
+  if (p0 >= p1) return;
+  if (tid == 0) {  // last non-empty segment starting at or before p0
+    int64_t lo = 0, hi = nsegc - 1;
+    while (lo < hi) {
+      const int64_t mid = (lo + hi + 1) >> 1;
+      if (cpre[mid] <= p0) lo = mid; else hi = mid - 1;
     }
-    s_item[0] = ok;
-    s_item[1] = bin;
-    s_item[2] = e0;
-    s_item[3] = e1;
+    s_seg = static_cast<int>(lo);
   }
   __syncthreads();
-  if (!s_item[0]) return;
-  const int64_t bin = s_item[1], e0 = s_item[2];
-  const int n_ent = static_cast<int>(s_item[3] - e0);
-  const int64_t seq = bin / B_c, blk = bin % B_c;
-  const int64_t bat = seq / H_kv;
-  const int r = static_cast<int>(seq % H_kv);
-  const int64_t key0 = blk * kBk;
 
-  // ---- stage K (row-major) and V (transposed) of block blk, head r
-  {
-    const uint8_t* kb = static_cast<const uint8_t*>(kp) + ((bat * N + key0) * H_kv + r) * kDh * EB;
-    const uint8_t* vb = static_cast<const uint8_t*>(vp) + ((bat * N + key0) * H_kv + r) * kDh * EB;
-    const int64_t rstride = static_cast<int64_t>(H_kv) * kDh * EB;  // bytes between token rows
-    if constexpr (!FP8) {
+  // Segment state (uniform across the workgroup).
+  int64_t c = s_seg;
+  int64_t seg_end = 0, eoff = 0, seq_q = 0;
+  int seq = 0, blk = 0;
+  const uint8_t* seg_q = nullptr;  // Q rows of this segment's (batch, group)
+  auto open_segment = [&](int64_t cc) {
+    const int key = ckey[cc];
+    const int B_c = static_cast<int>(sv.B_c), nW = static_cast<int>(sv.nW);
+    blk = key % B_c;
+    const int sw = key / B_c;
+    seq = sw / nW;
+    const int64_t t0 = static_cast<int64_t>(sw % nW) * sv.TW;
+    // entry index = position + eoff
+    eoff = static_cast<int64_t>(blk_offsets[static_cast<int64_t>(seq) * (B_c + 1) + blk]) +
+           ccnt[(seq * sv.T64 + t0) * sv.B_c + blk] - cpre[cc];
+    seg_end = cpre[cc + 1];
+    seq_q = static_cast<int64_t>(seq) * q_count;
+    const int bat = seq / H_kv, r = seq % H_kv;
+    seg_q = static_cast<const uint8_t*>(qp) +
+            (static_cast<int64_t>(bat) * N * H_q + r * G) * static_cast<int64_t>(kDh) * EB;
+  };
+  open_segment(c);
+
+  // Output dimension of V^T operand row n in d-tile 0 (d-tile dt adds 16 dt;
+  // see the store below), and the lane's fragment base addresses.
+  const int dsel = 64 * ((n >> 2) & 1) + 4 * (n >> 3) + (n & 3);
+  const uint8_t* k_base = k_lds + n * kKStride + h * 16;
+  const uint8_t* v_base = vt_lds + vt_row(dsel) * kVStride + h * 8;
+  const int rho0 = 32 * kRT * wave + n;  // this lane's row in column tile 0; tile t is rho0 + 32 t
+
+  // Per-lane row descriptor of a pass.  An entry holds qrow * k + slot; the
+  // division by k is a multiply-high by the host's round-up reciprocal.
+  struct RowRef {
+    const uint8_t* q;  // the row's Q vector
+    int64_t orow;      // partial-output row (seq, qrow, slot, g)
+    int64_t i;         // query position
+    bool ok;
+  };
+  auto row_ent = [&](int64_t pos, int cnt, int rho) {  // raw entry word of a row
+    const int e = rho / G;
+    return static_cast<uint32_t>(entries[pos + eoff + (e < cnt ? e : 0)]);
+  };
+  // Decode with the segment cursor at the pass's segment.
+  auto row_dec = [&](uint32_t ent, int cnt, int rho) {
+    RowRef rr;
+    const int e = rho / G, g = rho % G;
+    rr.ok = e < cnt;
+    const uint32_t qrow = kslots == 1 ? ent : (__umulhi(ent, kdiv_magic) >> kdiv_shift);
+    const uint32_t slot = ent - qrow * static_cast<uint32_t>(kslots);
+    rr.i = q_begin + qrow;
+    rr.orow = ((seq_q + qrow) * kslots + slot) * G + g;
+    rr.q = seg_q + (rr.i * H_q + g) * static_cast<int64_t>(kDh) * EB;
+    return rr;
+  };
+  auto row_ref = [&](int64_t pos, int cnt, int rho) { return row_dec(row_ent(pos, cnt, rho), cnt, rho); };
+
+  // ---- software pipeline over passes: while pass p computes, the Q rows of
+  // pass p+1 are in flight and the entries (row descriptors) of pass p+2 are
+  // being read.  A pass never spans two segments; the segment cursor always
+  // sits at the furthest pass looked up.
+  struct Pass {
+    int64_t pos;  // first position (segment order)
+    int cnt;      // entries
+    int seq, blk;
+  };
+  auto next_pass = [&](int64_t at, Pass& P) -> bool {
+    if (at >= p1) return false;
+    if (at >= seg_end) {
+      // (with a consistent work list the next segment starts exactly here)
+      if (c + 1 >= nsegc) return false;
+      open_segment(++c);
+    }
+    P.pos = at;
+    P.cnt = static_cast<int>(min<int64_t>(EPP, min(seg_end, p1) - at));
+    P.seq = seq;
+    P.blk = blk;
+    return P.cnt > 0;
+  };
+
+  Pass P0, P1{}, P2{};
+  RowRef rr0[kRT], rr1[kRT];
+  uint32_t raw2[kRT];  // pass p+2's entry words, decoded one iteration later
+  bf16x8 qf[kRT][8], qn[kRT][8];
+  if (!next_pass(p0, P0)) return;  // uniform
 #pragma unroll
-      for (int p = 0; p < 8; ++p) {
-        const int cid = tid + p * kAttnThreads;
-        const int key = cid >> 4, c = cid & 15;
-        u32x4 w = {0u, 0u, 0u, 0u};
-        if (key0 + key < N) w = *reinterpret_cast<const u32x4*>(kb + key * rstride + c * 16);
-        *reinterpret_cast<u32x4*>(k_lds + k_lds_off(key, c)) = w;
-      }
-    } else {
+  for (int nt = 0; nt < kRT; ++nt) rr0[nt] = row_ref(P0.pos, P0.cnt, rho0 + 32 * nt);
+  bool have1 = next_pass(P0.pos + P0.cnt, P1);
+  if (have1) {
 #pragma unroll
-      for (int p = 0; p < 4; ++p) {
-        const int cid = tid + p * kAttnThreads;
-        const int key = cid >> 3, cc = cid & 7;
-        u32x4 w = {0u, 0u, 0u, 0u};
-        if (key0 + key < N) w = *reinterpret_cast<const u32x4*>(kb + key * rstride + cc * 16);
-        const u32x2 a = e4m3x4_to_bf16x4(w[0]), b = e4m3x4_to_bf16x4(w[1]);
-        const u32x2 c2 = e4m3x4_to_bf16x4(w[2]), d2 = e4m3x4_to_bf16x4(w[3]);
-        *reinterpret_cast<u32x4*>(k_lds + k_lds_off(key, 2 * cc)) = u32x4{a[0], a[1], b[0], b[1]};
-        *reinterpret_cast<u32x4*>(k_lds + k_lds_off(key, 2 * cc + 1)) = u32x4{c2[0], c2[1], d2[0], d2[1]};
+    for (int nt = 0; nt < kRT; ++nt) rr1[nt] = row_ref(P1.pos, P1.cnt, rho0 + 32 * nt);
+  }
+#pragma unroll
+  for (int nt = 0; nt < kRT; ++nt) load_q<FP8>(rr0[nt].q, h, qf[nt]);
+  // Settle the first pass's gather here, once: inside the loop qf is always a
+  // copy of an already-waited prefetch, so no wait there has to cover the
+  // loads issued in the same iteration.
+#pragma unroll
+  for (int nt = 0; nt < kRT; ++nt)
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) asm volatile("" ::"v"(qf[nt][ks]));
+  int64_t staged = -1;
+
+  while (true) {
+    // ---- stage K and V of this pass's block if not resident
+    const int64_t bin = static_cast<int64_t>(P0.seq) * sv.B_c + P0.blk;
+    const int64_t key0 = static_cast<int64_t>(P0.blk) * kBk;
+    if (bin != staged) {
+      __syncthreads();
+      const int64_t bat = P0.seq / H_kv;
+      const int r = P0.seq % H_kv;
+      const int64_t rstride = static_cast<int64_t>(H_kv) * kDh * EB;
+      const uint8_t* kb = static_cast<const uint8_t*>(kp) + ((bat * N + key0) * H_kv + r) * kDh * EB;
+      const uint8_t* vb = static_cast<const uint8_t*>(vp) + ((bat * N + key0) * H_kv + r) * kDh * EB;
+      stage_kv<FP8>(kb, vb, rstride, static_cast<int>(min<int64_t>(kBk, N - key0)), k_lds, vt_lds);
+      __syncthreads();
+      staged = bin;
+    }
+
+    // ---- read pass p+2's entries and gather pass p+1's Q rows.  Every
+    // memory operation of an iteration is issued unconditionally (a missing
+    // pass reads entry 0 / this pass's rows and ignores them): with a fixed
+    // count per iteration the compiler's in-order vmcnt waits only ever cover
+    // what is really needed, never the stores or the loads just issued.
+    const bool have2 = have1 && next_pass(P1.pos + P1.cnt, P2);
+#pragma unroll
+    for (int nt = 0; nt < kRT; ++nt) {
+      const int e = (rho0 + 32 * nt) / G;
+      const int64_t at = have2 ? P2.pos + eoff + (e < P2.cnt ? e : 0) : 0;
+      raw2[nt] = static_cast<uint32_t>(entries[at]);
+    }
+#pragma unroll
+    for (int nt = 0; nt < kRT; ++nt) load_q<FP8>(have1 ? rr1[nt].q : rr0[nt].q, h, qn[nt]);
+
+    // ---- S^T = K_b Q^T: acc[nt][mt] holds keys 32mt + 8(e/4) + 4h + (e%4) of row rho0 + 32nt
+    f32x16 acc[kRT][4];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+#pragma unroll
+      for (int nt = 0; nt < kRT; ++nt) acc[nt][mt] = f32x16{};
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) {
+        // row 32 mt + n, 16-byte chunk 2 ks + h
+        const bf16x8 kf = as_bf16x8(*reinterpret_cast<const u32x4*>(k_base + 32 * mt * kKStride + 32 * ks));
+#pragma unroll
+        for (int nt = 0; nt < kRT; ++nt) acc[nt][mt] = mfma32x32x16(kf, qf[nt][ks], acc[nt][mt]);
       }
     }
-    const int kc = tid & 31;
+    const int cur_blk = P0.blk;
+    const RowRef* cur = rr0;
+
+    // ---- softmax per row.  The causal mask only bites in a query's own
+    // block, so it runs on a wave-uniform branch taken by the few passes that
+    // hold such a row.  The maximum is taken on the raw scores and the scale
+    // is folded into one FMA before exp2; the row sum adds the fp32
+    // probabilities, so lse is the exact log-sum-exp up to fp32 rounding.
+    bool own = false;
 #pragma unroll
-    for (int p = 0; p < 2; ++p) {
-      const int dg = (tid >> 5) + 8 * p;  // 8 output dims d = 8 dg .. 8 dg + 7
-      u32x4 row[4];
+    for (int nt = 0; nt < kRT; ++nt) own = own || (cur_blk == (cur[nt].i >> 7));
+    if (__any(own)) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int key = 4 * kc + j;
-        row[j] = u32x4{0u, 0u, 0u, 0u};
-        if (key0 + key < N) {
-          if constexpr (!FP8) {
-            row[j] = *reinterpret_cast<const u32x4*>(vb + key * rstride + dg * 16);
-          } else {
-            const u32x2 w = *reinterpret_cast<const u32x2*>(vb + key * rstride + dg * 8);
-            const u32x2 a = e4m3x4_to_bf16x4(w[0]), b = e4m3x4_to_bf16x4(w[1]);
-            row[j] = u32x4{a[0], a[1], b[0], b[1]};
+      for (int nt = 0; nt < kRT; ++nt) {
+        const int limit = (cur_blk == cur[nt].i >> 7) ? static_cast<int>(cur[nt].i - static_cast<int64_t>(cur_blk) * kBk) : kBk - 1;
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+#pragma unroll
+          for (int el = 0; el < 16; ++el) {
+            const int key = 32 * mt + 8 * (el >> 2) + 4 * h + (el & 3);
+            if (key > limit) acc[nt][mt][el] = -__builtin_huge_valf();
           }
         }
       }
-#pragma unroll
-      for (int dd = 0; dd < 8; ++dd) {
-        const int d = 8 * dg + dd;
-        const u32x2 v = {half_of(row[0], dd) | (half_of(row[1], dd) << 16),
-                         half_of(row[2], dd) | (half_of(row[3], dd) << 16)};
-        *reinterpret_cast<u32x2*>(vt_lds + vt_lds_off(d, kc)) = v;
-      }
     }
-  }
-  __syncthreads();
-
-  // Output dimension of V^T operand row n in d-tile nt (see the store below).
-  const int dsel = 64 * ((n >> 2) & 1) + 4 * (n >> 3) + (n & 3);
-  const int rho = 32 * wave + n;  // this lane's row in the 128-row tile
-  const int qs = rho / G, g = rho % G;
-
-  for (int t0 = 0; t0 < n_ent; t0 += QT) {
-    // The LDS tiles do not change across row tiles; an opaque zero added to
-    // their addresses keeps the compiler from hoisting all 96 fragment reads
-    // (256 VGPRs) out of the loop.
-    int salt = 0;
-    asm volatile("" : "+s"(salt));
-    const uint8_t* kl = k_lds + salt;
-    const uint8_t* vl = vt_lds + salt;
-    const int e = t0 + qs;
-    const bool row_ok = e < n_ent;
-    const int ent = entries[e0 + (row_ok ? e : n_ent - 1)];
-    const int64_t qrow = ent / kslots;
-    const int slot = ent % kslots;
-    const int64_t i = q_begin + qrow;
-
-    // ---- Q fragments (B operand of S^T): row (i, rG+g), dims 16ks + 8h .. +8
-    bf16x8 qf[8];
-    {
-      const uint8_t* qr = static_cast<const uint8_t*>(qp) + ((bat * N + i) * H_q + r * G + g) * kDh * EB;
+    bf16x8 pf[kRT][8];
+    float inv[kRT], lse2[kRT];
 #pragma unroll
-      for (int ks = 0; ks < 8; ++ks) {
-        if constexpr (!FP8) {
-          qf[ks] = as_bf16x8(*reinterpret_cast<const u32x4*>(qr + (16 * ks + 8 * h) * 2));
-        } else {
-          const u32x2 w = *reinterpret_cast<const u32x2*>(qr + 16 * ks + 8 * h);
-          const u32x2 a = e4m3x4_to_bf16x4(w[0]), b = e4m3x4_to_bf16x4(w[1]);
-          qf[ks] = as_bf16x8(u32x4{a[0], a[1], b[0], b[1]});
+    for (int nt = 0; nt < kRT; ++nt) {
+      float m = -__builtin_huge_valf();
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+#pragma unroll
+        for (int el = 0; el < 16; el += 2) m = fmaxf(m, fmaxf(acc[nt][mt][el], acc[nt][mt][el + 1]));
+      }
+      m = fmaxf(m, __shfl_xor(m, 32));
+      const float mb = m * scale_log2;  // scale_log2 > 0: the max commutes with it
+      float l = 0.f;
+      // P^T fragments (B operand of O^T = V^T P^T): step st = 2 mt + e2 covers
+      // keys 32mt + 16e2 + 8(j/4) + 4h + (j%4), accumulator elements 8e2 .. +7.
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+#pragma unroll
+        for (int e2 = 0; e2 < 2; ++e2) {
+          uint32_t w[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(acc[nt][mt][8 * e2 + 2 * j], scale_log2, -mb));
+            const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(acc[nt][mt][8 * e2 + 2 * j + 1], scale_log2, -mb));
+            w[j] = pack_bf16x2(p0, p1);
+            l += p0 + p1;
+          }
+          pf[nt][2 * mt + e2] = as_bf16x8(u32x4{w[0], w[1], w[2], w[3]});
         }
       }
+      l += __shfl_xor(l, 32);
+      inv[nt] = out_scale / l;
+      lse2[nt] = mb + __builtin_amdgcn_logf(l);
     }
-
-    // ---- S^T = K_b Q^T: acc[mt] holds keys 32mt + 8(e/4) + 4h + (e%4) of row rho
-    f32x16 acc[4];
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-      acc[mt] = f32x16{};
-#pragma unroll
-      for (int ks = 0; ks < 8; ++ks) {
-        const bf16x8 kf = as_bf16x8(*reinterpret_cast<const u32x4*>(kl + k_lds_off(32 * mt + n, 2 * ks + h)));
-        acc[mt] = mfma32x32x16(kf, qf[ks], acc[mt]);
-      }
-    }
-
-    // ---- causal limit (only the query's own block is partially visible)
-    const int limit = (blk == i / kBk) ? static_cast<int>(i - key0) : kBk - 1;
-    float m = -__builtin_huge_valf();
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-#pragma unroll
-      for (int el = 0; el < 16; ++el) {
-        const int key = 32 * mt + 8 * (el >> 2) + 4 * h + (el & 3);
-        const float t = key <= limit ? acc[mt][el] * scale_log2 : -__builtin_huge_valf();
-        acc[mt][el] = t;
-        m = fmaxf(m, t);
-      }
-    }
-    m = fmaxf(m, __shfl_xor(m, 32));
-    float l = 0.f;
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-#pragma unroll
-      for (int el = 0; el < 16; ++el) {
-        const float p = __builtin_amdgcn_exp2f(acc[mt][el] - m);
-        acc[mt][el] = p;
-        l += p;
-      }
-    }
-    l += __shfl_xor(l, 32);
-
-    // ---- P^T fragments (B operand of O^T = V^T P^T): step (mt, e2) covers
-    // keys 32mt + 16e2 + 8(j/4) + 4h + (j%4), exactly accumulator elements
-    // 8e2 .. 8e2 + 7 of acc[mt].
-    bf16x8 pf[8];
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-#pragma unroll
-      for (int e2 = 0; e2 < 2; ++e2) {
-        pf[2 * mt + e2] = as_bf16x8(u32x4{
-            pack_bf16x2(acc[mt][8 * e2 + 0], acc[mt][8 * e2 + 1]),
-            pack_bf16x2(acc[mt][8 * e2 + 2], acc[mt][8 * e2 + 3]),
-            pack_bf16x2(acc[mt][8 * e2 + 4], acc[mt][8 * e2 + 5]),
-            pack_bf16x2(acc[mt][8 * e2 + 6], acc[mt][8 * e2 + 7])});
-      }
-    }
-    const float inv = out_scale / l;
-    const int64_t orow = ((seq * q_count + qrow) * kslots + slot) * G + g;
-    uint16_t* dst = o_part + orow * kDh + 64 * h;
 
     // ---- O^T = V^T P^T, one 32-dim tile at a time; lane (n, h) receives dims
-    // 64h + 16nt + el of its row and stores them straight away.
+    // 64h + 16dt + el of its row and stores them straight away.
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-      const int d = dsel + 16 * nt;
-      f32x16 oacc = {};
+    for (int dt = 0; dt < 4; ++dt) {
+      f32x16 oa[kRT];
+#pragma unroll
+      for (int nt = 0; nt < kRT; ++nt) oa[nt] = f32x16{};
 #pragma unroll
       for (int st = 0; st < 8; ++st) {
-        const int c1 = 4 * st + h;  // = 8 mt + 4 e2 + h
-        const u32x2 lo = *reinterpret_cast<const u32x2*>(vl + vt_lds_off(d, c1));
-        const u32x2 hi = *reinterpret_cast<const u32x2*>(vl + vt_lds_off(d, c1 + 2));
-        oacc = mfma32x32x16(as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]}), pf[st], oacc);
-      }
-      if (row_ok) {
+        // row dsel + 16 dt (stored at vt_row(dsel) + 32 dt), 8-byte chunks
+        // c1 = 4 st + h = 8 mt + 4 e2 + h and c1 + 2
+        const uint8_t* vp8 = v_base + 32 * dt * kVStride + 32 * st;
+        const u32x2 lo = *reinterpret_cast<const u32x2*>(vp8);
+        const u32x2 hi = *reinterpret_cast<const u32x2*>(vp8 + 16);
+        const bf16x8 vf = as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
 #pragma unroll
-        for (int hf = 0; hf < 2; ++hf) {
-          const int b8 = 8 * hf;
-          *reinterpret_cast<u32x4*>(dst + 16 * nt + b8) = u32x4{
-              pack_bf16x2(oacc[b8 + 0] * inv, oacc[b8 + 1] * inv),
-              pack_bf16x2(oacc[b8 + 2] * inv, oacc[b8 + 3] * inv),
-              pack_bf16x2(oacc[b8 + 4] * inv, oacc[b8 + 5] * inv),
-              pack_bf16x2(oacc[b8 + 6] * inv, oacc[b8 + 7] * inv)};
+        for (int nt = 0; nt < kRT; ++nt) oa[nt] = mfma32x32x16(vf, pf[nt][st], oa[nt]);
+      }
+      // A row past the pass's entries recomputed entry 0 of the pass with the
+      // same head, bit for bit, so its store repeats that row's store.
+#pragma unroll
+      for (int nt = 0; nt < kRT; ++nt) {
+        {
+          uint16_t* dst = o_part + cur[nt].orow * kDh + 64 * h + 16 * dt;
+#pragma unroll
+          for (int hf = 0; hf < 2; ++hf) {
+            const int b8 = 8 * hf;
+            const float iv = inv[nt];
+            *reinterpret_cast<u32x4*>(dst + b8) =
+                u32x4{pack_bf16x2(oa[nt][b8 + 0] * iv, oa[nt][b8 + 1] * iv),
+                      pack_bf16x2(oa[nt][b8 + 2] * iv, oa[nt][b8 + 3] * iv),
+                      pack_bf16x2(oa[nt][b8 + 4] * iv, oa[nt][b8 + 5] * iv),
+                      pack_bf16x2(oa[nt][b8 + 6] * iv, oa[nt][b8 + 7] * iv)};
+          }
         }
       }
     }
-    if (row_ok && h == 0) lse_part[orow] = (m + __builtin_amdgcn_logf(l)) * 0.69314718055994531f;
+    // (both half-waves hold the same m and l; their stores coincide)
+#pragma unroll
+    for (int nt = 0; nt < kRT; ++nt) lse_part[cur[nt].orow] = lse2[nt] * 0.69314718055994531f;
+    if (!have1) break;
+
+    // ---- rotate the pipeline (the cursor still sits at pass p+2's segment)
+    P0 = P1;
+    P1 = P2;
+#pragma unroll
+    for (int nt = 0; nt < kRT; ++nt) {
+      rr0[nt] = rr1[nt];
+      if (have2) rr1[nt] = row_dec(raw2[nt], P2.cnt, rho0 + 32 * nt);
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) qf[nt][ks] = qn[nt][ks];
+    }
+    have1 = have2;
   }
 }
+
+// Persistent workgroups per CU: one per wave slot of each SIMD (67 KB of LDS
+// each).
+constexpr int kAttnWgPerCu = kWavesPerSimd;
+
+int device_cus() {
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cus[dev] == 0) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0)
+      v = 256;
+    cus[dev] = v;
+  }
+  return cus[dev];
+}
+
+}  // namespace
+
+// Round-up reciprocal of d in [2, 32] for 31-bit dividends (Granlund and
+// Montgomery, "Division by invariant integers using multiplication", PLDI 1994,
+// Thm. 4.2 with N = 31): with l = ceil(log2 d) and m = floor(2^(31+l) / d) + 1,
+// 2^(31+l) < m d <= 2^(31+l) + 2^l, so n / d = (m n) >> (31 + l), i.e.
+// umulhi(n, m) >> (l - 1), for every 0 <= n < 2^31; m < 2^32 for d >= 2.
+void kdiv_params(int d, uint32_t* magic, int* shift) {
+  if (d <= 1) {
+    *magic = 0;
+    *shift = 0;
+    return;
+  }
+  int l = 0;
+  while ((1 << l) < d) ++l;
+  *magic = static_cast<uint32_t>(((uint64_t(1) << (31 + l)) / static_cast<uint64_t>(d)) + 1);
+  *shift = l - 1;
+}
+
+namespace {
 
 template <int G>
 hipError_t launch_g(const void* q, const void* k, const void* v, bool fp8, int batch, int64_t N,
@@ -293,14 +528,22 @@ hipError_t launch_g(const void* q, const void* k, const void* v, bool fp8, int b
                     const int32_t* blk_offsets, const int32_t* blk_entries, const int32_t* sched,
                     int64_t q_begin, int64_t q_count, uint16_t* o_part, float* lse_part,
                     hipStream_t stream) {
-  const SchedLayout s = sched_layout(batch, H_kv, G, q_begin, q_count);
-  int64_t grid = attn_max_items(batch, H_kv, G, kslots, q_begin, q_count) + kXcds;
-  grid = (grid + kXcds - 1) / kXcds * kXcds;
+  const SchedLayout s = sched_layout(batch, H_kv, q_begin, q_count);
+  const AttnSched sv{s.B_c, s.T64, s.TW, s.nW, s.off_ckey, s.off_cpre, s.off_cnt};
+  // Never more workgroups than passes, so every workgroup has work when the
+  // range is small.
+  const int64_t entries_max = static_cast<int64_t>(batch) * H_kv * q_count * kslots;
+  const int64_t passes = (entries_max + (kPassRows / G) - 1) / (kPassRows / G);
+  int64_t grid = static_cast<int64_t>(device_cus()) * kAttnWgPerCu;
+  if (passes < grid) grid = passes;
+  if (grid < 1) grid = 1;
+  uint32_t magic = 0;
+  int shift = 0;
+  kdiv_params(kslots, &magic, &shift);
   auto kern = fp8 ? sparse_attn_kernel<G, true> : sparse_attn_kernel<G, false>;
   hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(grid)), dim3(kAttnThreads), 0, stream, q, k,
-                     v, N, H_kv, kslots, scale_log2, out_scale, blk_offsets, blk_entries,
-                     sched + s.off_items, sched, s.nbins, s.B_c, q_begin, q_count, o_part,
-                     lse_part);
+                     v, N, H_kv, kslots, magic, shift, scale_log2, out_scale, blk_offsets,
+                     blk_entries, sched, sv, q_begin, q_count, o_part, lse_part);
   return hipGetLastError();
 }
 
