@@ -13,17 +13,16 @@
 // by the combine kernel.
 //
 // gfx950 design:
-//  * Persistent grid of two workgroups per CU.  The (query, slot) entries are
-//    taken in segment order -- (sequence, query window, block), see invert.hip
-//    -- and that sequence is cut into one equal contiguous share per
-//    workgroup: every workgroup gets the same number of entries whatever the
-//    block popularity, and stages a K/V block only when its share moves to the
-//    next segment.
-//  * 4 waves, 256 (query, head) rows per pass: 256 / G entries x G heads (a
-//    query's G heads are contiguous in Q, 256 B each); each wave owns 64 rows
-//    as two 32-row MFMA column tiles, so every K or V^T fragment read from LDS
-//    feeds two MFMAs.  K (row-major) and V (transposed) live in XOR-swizzled
-//    LDS, 64 KB per workgroup.
+//  * Persistent grid, one workgroup of 8 waves per CU (two waves per SIMD).
+//    The (query, slot) entries are taken in segment order -- (sequence, query
+//    window, block), see invert.hip -- and that sequence is cut into one equal
+//    contiguous share per workgroup: every workgroup gets the same number of
+//    entries whatever the block popularity, and stages a K/V block only when
+//    its share moves to the next segment.
+//  * A pass is 256 (query, head) rows: 256 / G entries x G heads (a query's G
+//    heads are contiguous in Q, 256 B each); each wave owns one 32-row MFMA
+//    column tile.  K (row-major) and V (transposed) live in padded LDS
+//    (67 KB), shared by the 8 waves.
 //  * S^T = K_b * Q^T with v_mfma_f32_32x32x16_bf16 (keys on the row
 //    dimension): every lane holds 64 of the 128 keys of one (query, head) row,
 //    so the row max and row sum need one half-wave exchange, and the
@@ -31,29 +30,26 @@
 //    shuffle (the reduction slots of each P^T step are exactly the keys that
 //    lane already holds).  The V^T operand rows are permuted so that every
 //    lane ends up with 64 contiguous output dimensions of its row.
+//  * The partial outputs go through an 8.5 KB LDS tile per wave: written in
+//    the MFMA layout (lane = row), read back row-contiguous, and stored 1 KB
+//    contiguous per instruction, so L2 receives whole 128-byte lines rather
+//    than 16-byte pieces of 64 different rows.
 //  * Software pipeline over passes: the Q rows of the next pass are gathered
 //    into registers and the entries of the pass after it are read while the
-//    current pass computes, so a whole pass covers the gather latency.
-//  * Softmax in base 2 (v_exp_f32) with the scale folded in; fp8 (OCP e4m3)
-//    inputs are widened exactly to bf16 while loading and the per-tensor
-//    scales are folded into the softmax scale and the output scale.
+//    current pass computes.  Every memory operation of the loop is issued
+//    unconditionally, so the compiler's in-order vmcnt waits never have to
+//    cover the stores or the loads just issued.
+//  * Softmax in base 2 (v_exp_f32) with the scale folded into one FMA; fp8
+//    (OCP e4m3) inputs are widened exactly to bf16 when used and the
+//    per-tensor scales are folded into the softmax scale and the output scale.
 #include "msa_internal.h"
 
 namespace msa {
 namespace {
 
-constexpr int kAttnThreads = 256;
-
-// Rows per wave: RT column tiles of 32 (query, head) rows.  RT = 2 shares each
-// LDS fragment between two MFMAs but needs ~450 registers (one wave per SIMD);
-// RT = 1 fits two waves per SIMD.  Build-time tunable.
-#ifndef MSA_ATTN_RT
-#define MSA_ATTN_RT 1
-#endif
-constexpr int kRT = MSA_ATTN_RT;
-static_assert(kRT == 1 || kRT == 2, "one or two row tiles per wave");
-constexpr int kWavesPerSimd = kRT == 2 ? 1 : 2;
-constexpr int kPassRows = 4 * 32 * kRT;  // (query, head) rows per pass
+constexpr int kThreads = 512;
+constexpr int kWaves = kThreads / 64;
+constexpr int kPassRows = 32 * kWaves;  // (query, head) rows per pass
 
 // LDS layouts.  Rows are padded rather than swizzled so that every fragment
 // read of a lane is one base address plus a compile-time offset (no per-read
@@ -63,8 +59,11 @@ constexpr int kPassRows = 4 * 32 * kRT;  // (query, head) rows per pass
 //  * V^T, 264 B per output-dimension row, row d stored at position
 //    2 (d mod 64) + d / 64: the 32 rows one 8-byte read touches
 //    (d in 0..15 and 64..79, plus 16 dt) land on 32 distinct even banks.
+//  * Output tile, 272 B per row: 16-byte writes of rows n .. n + 15 and
+//    16-byte reads of the 16 chunks of one row are both conflict free.
 constexpr int kKStride = 272;
 constexpr int kVStride = 264;
+constexpr int kOStride = 272;
 
 __device__ __forceinline__ int k_lds_off(int key, int c) {  // 16-byte chunk c of key row
   return key * kKStride + c * 16;
@@ -87,97 +86,103 @@ __device__ __forceinline__ void stage_kv(const uint8_t* __restrict__ kb, const u
                                          int64_t rstride, int nvalid, uint8_t* k_lds,
                                          uint8_t* vt_lds) {
   // Staging is rare (once per segment); an opaque copy of the thread id keeps
-  // the compiler from hoisting its ~50 per-lane addresses out of the caller's
+  // the compiler from hoisting its per-lane addresses out of the caller's
   // loop, where they would stay live across every pass.
   int tid = threadIdx.x;
   asm volatile("" : "+v"(tid));
   // Rows past the end of the sequence (a partial last block) are read from the
   // last valid row and replaced by zeros, so every load is issued at once.
   if constexpr (!FP8) {
-    u32x4 w[8];
+    u32x4 w[4];
 #pragma unroll
-    for (int p = 0; p < 8; ++p) {
-      const int key = (tid >> 4) + 16 * p, c = tid & 15;
+    for (int p = 0; p < 4; ++p) {
+      const int key = (tid >> 4) + 32 * p, c = tid & 15;
       w[p] = *reinterpret_cast<const u32x4*>(kb + min(key, nvalid - 1) * rstride + c * 16);
     }
 #pragma unroll
-    for (int p = 0; p < 8; ++p) {
-      const int key = (tid >> 4) + 16 * p, c = tid & 15;
+    for (int p = 0; p < 4; ++p) {
+      const int key = (tid >> 4) + 32 * p, c = tid & 15;
       if (key >= nvalid) w[p] = u32x4{0u, 0u, 0u, 0u};
       *reinterpret_cast<u32x4*>(k_lds + k_lds_off(key, c)) = w[p];
     }
   } else {
-    u32x4 wk[4];
+    u32x4 wk[2];
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      const int key = (tid >> 3) + 32 * p, cc = tid & 7;
+    for (int p = 0; p < 2; ++p) {
+      const int key = (tid >> 3) + 64 * p, cc = tid & 7;
       wk[p] = *reinterpret_cast<const u32x4*>(kb + min(key, nvalid - 1) * rstride + cc * 16);
     }
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      const int key = (tid >> 3) + 32 * p, cc = tid & 7;
-      u32x4 w = key < nvalid ? wk[p] : u32x4{0u, 0u, 0u, 0u};
+    for (int p = 0; p < 2; ++p) {
+      const int key = (tid >> 3) + 64 * p, cc = tid & 7;
+      const u32x4 w = key < nvalid ? wk[p] : u32x4{0u, 0u, 0u, 0u};
       const u32x2 a = e4m3x4_to_bf16x4(w[0]), b = e4m3x4_to_bf16x4(w[1]);
       const u32x2 c2 = e4m3x4_to_bf16x4(w[2]), d2 = e4m3x4_to_bf16x4(w[3]);
       *reinterpret_cast<u32x4*>(k_lds + k_lds_off(key, 2 * cc)) = u32x4{a[0], a[1], b[0], b[1]};
       *reinterpret_cast<u32x4*>(k_lds + k_lds_off(key, 2 * cc + 1)) = u32x4{c2[0], c2[1], d2[0], d2[1]};
     }
   }
-  const int kc = tid & 31;
-  u32x4 rows[2][4];
+  // V: thread (dg, kc) transposes the 8 dims 8 dg .. 8 dg + 7 of keys
+  // 4 kc .. 4 kc + 3 into four-key chunks of V^T rows.
+  const int kc = tid & 31, dg = tid >> 5;
+  u32x4 rows[4];
 #pragma unroll
-  for (int p = 0; p < 2; ++p) {
-    const int dg = (tid >> 5) + 8 * p;  // 8 output dims d = 8 dg .. 8 dg + 7
+  for (int j = 0; j < 4; ++j) {
+    const int key = min(4 * kc + j, nvalid - 1);
+    if constexpr (!FP8) {
+      rows[j] = *reinterpret_cast<const u32x4*>(vb + key * rstride + dg * 16);
+    } else {
+      const u32x2 w = *reinterpret_cast<const u32x2*>(vb + key * rstride + dg * 8);
+      rows[j] = u32x4{w[0], w[1], 0u, 0u};
+    }
+  }
+  u32x4 row[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int key = min(4 * kc + j, nvalid - 1);
-      if constexpr (!FP8) {
-        rows[p][j] = *reinterpret_cast<const u32x4*>(vb + key * rstride + dg * 16);
-      } else {
-        const u32x2 w = *reinterpret_cast<const u32x2*>(vb + key * rstride + dg * 8);
-        rows[p][j] = u32x4{w[0], w[1], 0u, 0u};
-      }
+  for (int j = 0; j < 4; ++j) {
+    if (4 * kc + j >= nvalid) {
+      row[j] = u32x4{0u, 0u, 0u, 0u};
+    } else if constexpr (!FP8) {
+      row[j] = rows[j];
+    } else {
+      const u32x2 a = e4m3x4_to_bf16x4(rows[j][0]), b = e4m3x4_to_bf16x4(rows[j][1]);
+      row[j] = u32x4{a[0], a[1], b[0], b[1]};
     }
   }
 #pragma unroll
-  for (int p = 0; p < 2; ++p) {
-    const int dg = (tid >> 5) + 8 * p;
-    u32x4 row[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      if (4 * kc + j >= nvalid) {
-        row[j] = u32x4{0u, 0u, 0u, 0u};
-      } else if constexpr (!FP8) {
-        row[j] = rows[p][j];
-      } else {
-        const u32x2 a = e4m3x4_to_bf16x4(rows[p][j][0]), b = e4m3x4_to_bf16x4(rows[p][j][1]);
-        row[j] = u32x4{a[0], a[1], b[0], b[1]};
-      }
-    }
-#pragma unroll
-    for (int dd = 0; dd < 8; ++dd) {
-      const int d = 8 * dg + dd;
-      const u32x2 v = {half_of(row[0], dd) | (half_of(row[1], dd) << 16),
-                       half_of(row[2], dd) | (half_of(row[3], dd) << 16)};
-      *reinterpret_cast<u32x2*>(vt_lds + vt_lds_off(d, kc)) = v;
-    }
+  for (int dd = 0; dd < 8; ++dd) {
+    const int d = 8 * dg + dd;
+    const u32x2 v = {half_of(row[0], dd) | (half_of(row[1], dd) << 16),
+                     half_of(row[2], dd) | (half_of(row[3], dd) << 16)};
+    *reinterpret_cast<u32x2*>(vt_lds + vt_lds_off(d, kc)) = v;
   }
 }
 
-// Q fragments (B operand of S^T) of one row: dims 16 ks + 8 h .. + 8.
+// Q fragments (B operand of S^T) of one row, dims 16 ks + 8 h .. + 8, kept as
+// loaded (bf16: 8 x 16 B; fp8: 8 x 8 B of codes) and widened when used, so a
+// prefetch is never waited on before its pass.
 template <bool FP8>
-__device__ __forceinline__ void load_q(const uint8_t* __restrict__ qr, int h, bf16x8 (&qf)[8]) {
+struct QFrag;
+template <>
+struct QFrag<false> {
+  u32x4 w[8];
+  __device__ __forceinline__ void load(const uint8_t* __restrict__ qr, int h) {
 #pragma unroll
-  for (int ks = 0; ks < 8; ++ks) {
-    if constexpr (!FP8) {
-      qf[ks] = as_bf16x8(*reinterpret_cast<const u32x4*>(qr + (16 * ks + 8 * h) * 2));
-    } else {
-      const u32x2 w = *reinterpret_cast<const u32x2*>(qr + 16 * ks + 8 * h);
-      const u32x2 a = e4m3x4_to_bf16x4(w[0]), b = e4m3x4_to_bf16x4(w[1]);
-      qf[ks] = as_bf16x8(u32x4{a[0], a[1], b[0], b[1]});
-    }
+    for (int ks = 0; ks < 8; ++ks) w[ks] = *reinterpret_cast<const u32x4*>(qr + (16 * ks + 8 * h) * 2);
   }
-}
+  __device__ __forceinline__ bf16x8 get(int ks) const { return as_bf16x8(w[ks]); }
+};
+template <>
+struct QFrag<true> {
+  u32x2 w[8];
+  __device__ __forceinline__ void load(const uint8_t* __restrict__ qr, int h) {
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) w[ks] = *reinterpret_cast<const u32x2*>(qr + 16 * ks + 8 * h);
+  }
+  __device__ __forceinline__ bf16x8 get(int ks) const {
+    const u32x2 a = e4m3x4_to_bf16x4(w[ks][0]), b = e4m3x4_to_bf16x4(w[ks][1]);
+    return as_bf16x8(u32x4{a[0], a[1], b[0], b[1]});
+  }
+};
 
 struct AttnSched {
   int64_t B_c, T64, TW, nW;
@@ -185,7 +190,7 @@ struct AttnSched {
 };
 
 template <int G, bool FP8>
-__global__ __launch_bounds__(kAttnThreads, kWavesPerSimd) void sparse_attn_kernel(
+__global__ __launch_bounds__(kThreads, 2) void sparse_attn_kernel(
     const void* __restrict__ qp, const void* __restrict__ kp, const void* __restrict__ vp,
     int64_t N, int H_kv, int kslots, uint32_t kdiv_magic, int kdiv_shift, float scale_log2,
     float out_scale, const int32_t* __restrict__ blk_offsets, const int32_t* __restrict__ entries,
@@ -195,6 +200,8 @@ __global__ __launch_bounds__(kAttnThreads, kWavesPerSimd) void sparse_attn_kerne
   constexpr int EB = FP8 ? 1 : 2;     // bytes per Q/K/V element
   __shared__ __attribute__((aligned(16))) uint8_t k_lds[kBk * kKStride];
   __shared__ __attribute__((aligned(16))) uint8_t vt_lds[kDh * kVStride];
+  __shared__ __attribute__((aligned(16))) uint8_t o_lds[kWaves * 32 * kOStride];
+  __shared__ __attribute__((aligned(8))) int64_t orow_lds[kWaves * 32];
   __shared__ int s_seg;
 
   const int tid = threadIdx.x;
@@ -221,7 +228,7 @@ __global__ __launch_bounds__(kAttnThreads, kWavesPerSimd) void sparse_attn_kerne
   }
   __syncthreads();
 
-  // Segment state (uniform across the workgroup).
+  // Segment cursor (uniform across the workgroup).
   int64_t c = s_seg;
   int64_t seg_end = 0, eoff = 0, seq_q = 0;
   int seq = 0, blk = 0;
@@ -245,42 +252,41 @@ __global__ __launch_bounds__(kAttnThreads, kWavesPerSimd) void sparse_attn_kerne
   open_segment(c);
 
   // Output dimension of V^T operand row n in d-tile 0 (d-tile dt adds 16 dt;
-  // see the store below), and the lane's fragment base addresses.
+  // see the output step below), and the lane's fragment base addresses.
   const int dsel = 64 * ((n >> 2) & 1) + 4 * (n >> 3) + (n & 3);
   const uint8_t* k_base = k_lds + n * kKStride + h * 16;
   const uint8_t* v_base = vt_lds + vt_row(dsel) * kVStride + h * 8;
-  const int rho0 = 32 * kRT * wave + n;  // this lane's row in column tile 0; tile t is rho0 + 32 t
+  uint8_t* o_tile = o_lds + wave * 32 * kOStride;
+  int64_t* orow_tile = orow_lds + wave * 32;
+  const int rho = 32 * wave + n;     // this lane's row of the pass
+  const int e_row = rho / G, g_row = rho % G;
 
   // Per-lane row descriptor of a pass.  An entry holds qrow * k + slot; the
-  // division by k is a multiply-high by the host's round-up reciprocal.
+  // division by k is a multiply-high by the host's round-up reciprocal.  A row
+  // past the pass's entries takes the pass's first entry (same head): it
+  // recomputes that row bit for bit, so its stores repeat that row's stores.
   struct RowRef {
     const uint8_t* q;  // the row's Q vector
     int64_t orow;      // partial-output row (seq, qrow, slot, g)
     int64_t i;         // query position
-    bool ok;
   };
-  auto row_ent = [&](int64_t pos, int cnt, int rho) {  // raw entry word of a row
-    const int e = rho / G;
-    return static_cast<uint32_t>(entries[pos + eoff + (e < cnt ? e : 0)]);
+  auto row_ent = [&](int64_t pos, int cnt) {  // raw entry word
+    return static_cast<uint32_t>(entries[pos + eoff + (e_row < cnt ? e_row : 0)]);
   };
-  // Decode with the segment cursor at the pass's segment.
-  auto row_dec = [&](uint32_t ent, int cnt, int rho) {
+  auto row_dec = [&](uint32_t ent) {  // with the cursor at the pass's segment
     RowRef rr;
-    const int e = rho / G, g = rho % G;
-    rr.ok = e < cnt;
     const uint32_t qrow = kslots == 1 ? ent : (__umulhi(ent, kdiv_magic) >> kdiv_shift);
     const uint32_t slot = ent - qrow * static_cast<uint32_t>(kslots);
     rr.i = q_begin + qrow;
-    rr.orow = ((seq_q + qrow) * kslots + slot) * G + g;
-    rr.q = seg_q + (rr.i * H_q + g) * static_cast<int64_t>(kDh) * EB;
+    rr.orow = ((seq_q + qrow) * kslots + slot) * G + g_row;
+    rr.q = seg_q + (rr.i * H_q + g_row) * static_cast<int64_t>(kDh) * EB;
     return rr;
   };
-  auto row_ref = [&](int64_t pos, int cnt, int rho) { return row_dec(row_ent(pos, cnt, rho), cnt, rho); };
 
   // ---- software pipeline over passes: while pass p computes, the Q rows of
-  // pass p+1 are in flight and the entries (row descriptors) of pass p+2 are
-  // being read.  A pass never spans two segments; the segment cursor always
-  // sits at the furthest pass looked up.
+  // pass p+1 are in flight and the entries of pass p+2 are being read.  A pass
+  // never spans two segments; the segment cursor always sits at the furthest
+  // pass looked up.
   struct Pass {
     int64_t pos;  // first position (segment order)
     int cnt;      // entries
@@ -301,26 +307,18 @@ __global__ __launch_bounds__(kAttnThreads, kWavesPerSimd) void sparse_attn_kerne
   };
 
   Pass P0, P1{}, P2{};
-  RowRef rr0[kRT], rr1[kRT];
-  uint32_t raw2[kRT];  // pass p+2's entry words, decoded one iteration later
-  bf16x8 qf[kRT][8], qn[kRT][8];
+  RowRef rr0, rr1;
+  uint32_t raw2 = 0;  // pass p+2's entry word, decoded one iteration later
+  QFrag<FP8> qf, qn;
   if (!next_pass(p0, P0)) return;  // uniform
-#pragma unroll
-  for (int nt = 0; nt < kRT; ++nt) rr0[nt] = row_ref(P0.pos, P0.cnt, rho0 + 32 * nt);
+  rr0 = row_dec(row_ent(P0.pos, P0.cnt));
   bool have1 = next_pass(P0.pos + P0.cnt, P1);
-  if (have1) {
-#pragma unroll
-    for (int nt = 0; nt < kRT; ++nt) rr1[nt] = row_ref(P1.pos, P1.cnt, rho0 + 32 * nt);
-  }
-#pragma unroll
-  for (int nt = 0; nt < kRT; ++nt) load_q<FP8>(rr0[nt].q, h, qf[nt]);
+  if (have1) rr1 = row_dec(row_ent(P1.pos, P1.cnt));
+  qf.load(rr0.q, h);
   // Settle the first pass's gather here, once: inside the loop qf is always a
-  // copy of an already-waited prefetch, so no wait there has to cover the
-  // loads issued in the same iteration.
+  // copy of an already-waited prefetch.
 #pragma unroll
-  for (int nt = 0; nt < kRT; ++nt)
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks) asm volatile("" ::"v"(qf[nt][ks]));
+  for (int ks = 0; ks < 8; ++ks) asm volatile("" ::"v"(qf.w[ks]));
   int64_t staged = -1;
 
   while (true) {
@@ -339,102 +337,79 @@ __global__ __launch_bounds__(kAttnThreads, kWavesPerSimd) void sparse_attn_kerne
       staged = bin;
     }
 
-    // ---- read pass p+2's entries and gather pass p+1's Q rows.  Every
-    // memory operation of an iteration is issued unconditionally (a missing
-    // pass reads entry 0 / this pass's rows and ignores them): with a fixed
-    // count per iteration the compiler's in-order vmcnt waits only ever cover
-    // what is really needed, never the stores or the loads just issued.
+    // ---- read pass p+2's entry and gather pass p+1's Q row (unconditionally:
+    // a missing pass reads entry 0 / this pass's row and ignores it)
     const bool have2 = have1 && next_pass(P1.pos + P1.cnt, P2);
-#pragma unroll
-    for (int nt = 0; nt < kRT; ++nt) {
-      const int e = (rho0 + 32 * nt) / G;
-      const int64_t at = have2 ? P2.pos + eoff + (e < P2.cnt ? e : 0) : 0;
-      raw2[nt] = static_cast<uint32_t>(entries[at]);
-    }
-#pragma unroll
-    for (int nt = 0; nt < kRT; ++nt) load_q<FP8>(have1 ? rr1[nt].q : rr0[nt].q, h, qn[nt]);
+    raw2 = static_cast<uint32_t>(entries[have2 ? P2.pos + eoff + (e_row < P2.cnt ? e_row : 0) : 0]);
+    qn.load(have1 ? rr1.q : rr0.q, h);
 
-    // ---- S^T = K_b Q^T: acc[nt][mt] holds keys 32mt + 8(e/4) + 4h + (e%4) of row rho0 + 32nt
-    f32x16 acc[kRT][4];
+    // ---- S^T = K_b Q^T: acc[mt] holds keys 32mt + 8(e/4) + 4h + (e%4) of this row
+    f32x16 acc[4];
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
-#pragma unroll
-      for (int nt = 0; nt < kRT; ++nt) acc[nt][mt] = f32x16{};
+      acc[mt] = f32x16{};
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks) {
         // row 32 mt + n, 16-byte chunk 2 ks + h
         const bf16x8 kf = as_bf16x8(*reinterpret_cast<const u32x4*>(k_base + 32 * mt * kKStride + 32 * ks));
-#pragma unroll
-        for (int nt = 0; nt < kRT; ++nt) acc[nt][mt] = mfma32x32x16(kf, qf[nt][ks], acc[nt][mt]);
+        acc[mt] = mfma32x32x16(kf, qf.get(ks), acc[mt]);
       }
     }
-    const int cur_blk = P0.blk;
-    const RowRef* cur = rr0;
 
-    // ---- softmax per row.  The causal mask only bites in a query's own
-    // block, so it runs on a wave-uniform branch taken by the few passes that
-    // hold such a row.  The maximum is taken on the raw scores and the scale
-    // is folded into one FMA before exp2; the row sum adds the fp32
-    // probabilities, so lse is the exact log-sum-exp up to fp32 rounding.
-    bool own = false;
-#pragma unroll
-    for (int nt = 0; nt < kRT; ++nt) own = own || (cur_blk == (cur[nt].i >> 7));
+    // ---- softmax.  The causal mask only bites in a query's own block, so it
+    // runs on a wave-uniform branch taken by the few passes that hold such a
+    // row.  The maximum is taken on the raw scores and the scale is folded
+    // into one FMA before exp2; the row sum adds the fp32 probabilities, so
+    // lse is the exact log-sum-exp up to fp32 rounding.
+    const bool own = P0.blk == (rr0.i >> 7);
     if (__any(own)) {
-#pragma unroll
-      for (int nt = 0; nt < kRT; ++nt) {
-        const int limit = (cur_blk == cur[nt].i >> 7) ? static_cast<int>(cur[nt].i - static_cast<int64_t>(cur_blk) * kBk) : kBk - 1;
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt) {
-#pragma unroll
-          for (int el = 0; el < 16; ++el) {
-            const int key = 32 * mt + 8 * (el >> 2) + 4 * h + (el & 3);
-            if (key > limit) acc[nt][mt][el] = -__builtin_huge_valf();
-          }
-        }
-      }
-    }
-    bf16x8 pf[kRT][8];
-    float inv[kRT], lse2[kRT];
-#pragma unroll
-    for (int nt = 0; nt < kRT; ++nt) {
-      float m = -__builtin_huge_valf();
+      const int limit = own ? static_cast<int>(rr0.i - key0) : kBk - 1;
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
 #pragma unroll
-        for (int el = 0; el < 16; el += 2) m = fmaxf(m, fmaxf(acc[nt][mt][el], acc[nt][mt][el + 1]));
-      }
-      m = fmaxf(m, __shfl_xor(m, 32));
-      const float mb = m * scale_log2;  // scale_log2 > 0: the max commutes with it
-      float l = 0.f;
-      // P^T fragments (B operand of O^T = V^T P^T): step st = 2 mt + e2 covers
-      // keys 32mt + 16e2 + 8(j/4) + 4h + (j%4), accumulator elements 8e2 .. +7.
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
-#pragma unroll
-        for (int e2 = 0; e2 < 2; ++e2) {
-          uint32_t w[4];
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(acc[nt][mt][8 * e2 + 2 * j], scale_log2, -mb));
-            const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(acc[nt][mt][8 * e2 + 2 * j + 1], scale_log2, -mb));
-            w[j] = pack_bf16x2(p0, p1);
-            l += p0 + p1;
-          }
-          pf[nt][2 * mt + e2] = as_bf16x8(u32x4{w[0], w[1], w[2], w[3]});
+        for (int el = 0; el < 16; ++el) {
+          const int key = 32 * mt + 8 * (el >> 2) + 4 * h + (el & 3);
+          if (key > limit) acc[mt][el] = -__builtin_huge_valf();
         }
       }
-      l += __shfl_xor(l, 32);
-      inv[nt] = out_scale / l;
-      lse2[nt] = mb + __builtin_amdgcn_logf(l);
     }
+    float m = -__builtin_huge_valf();
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+#pragma unroll
+      for (int el = 0; el < 16; el += 2) m = fmaxf(m, fmaxf(acc[mt][el], acc[mt][el + 1]));
+    }
+    m = fmaxf(m, __shfl_xor(m, 32));
+    const float mb = m * scale_log2;  // scale_log2 > 0: the max commutes with it
+    float l = 0.f;
+    // P^T fragments (B operand of O^T = V^T P^T): step st = 2 mt + e2 covers
+    // keys 32mt + 16e2 + 8(j/4) + 4h + (j%4), accumulator elements 8e2 .. +7.
+    bf16x8 pf[8];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+#pragma unroll
+      for (int e2 = 0; e2 < 2; ++e2) {
+        uint32_t w[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float pa = __builtin_amdgcn_exp2f(__builtin_fmaf(acc[mt][8 * e2 + 2 * j], scale_log2, -mb));
+          const float pb = __builtin_amdgcn_exp2f(__builtin_fmaf(acc[mt][8 * e2 + 2 * j + 1], scale_log2, -mb));
+          w[j] = pack_bf16x2(pa, pb);
+          l += pa + pb;
+        }
+        pf[2 * mt + e2] = as_bf16x8(u32x4{w[0], w[1], w[2], w[3]});
+      }
+    }
+    l += __shfl_xor(l, 32);
+    const float inv = out_scale / l;
+    const float lse2 = mb + __builtin_amdgcn_logf(l);
 
     // ---- O^T = V^T P^T, one 32-dim tile at a time; lane (n, h) receives dims
-    // 64h + 16dt + el of its row and stores them straight away.
+    // 64h + 16dt + el of its row and writes them to the wave's output tile.
+    if (h == 0) orow_tile[n] = rr0.orow;
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) {
-      f32x16 oa[kRT];
-#pragma unroll
-      for (int nt = 0; nt < kRT; ++nt) oa[nt] = f32x16{};
+      f32x16 oa = {};
 #pragma unroll
       for (int st = 0; st < 8; ++st) {
         // row dsel + 16 dt (stored at vt_row(dsel) + 32 dt), 8-byte chunks
@@ -442,51 +417,46 @@ __global__ __launch_bounds__(kAttnThreads, kWavesPerSimd) void sparse_attn_kerne
         const uint8_t* vp8 = v_base + 32 * dt * kVStride + 32 * st;
         const u32x2 lo = *reinterpret_cast<const u32x2*>(vp8);
         const u32x2 hi = *reinterpret_cast<const u32x2*>(vp8 + 16);
-        const bf16x8 vf = as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
-#pragma unroll
-        for (int nt = 0; nt < kRT; ++nt) oa[nt] = mfma32x32x16(vf, pf[nt][st], oa[nt]);
+        oa = mfma32x32x16(as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]}), pf[st], oa);
       }
-      // A row past the pass's entries recomputed entry 0 of the pass with the
-      // same head, bit for bit, so its store repeats that row's store.
+      uint8_t* dst = o_tile + n * kOStride + 128 * h + 32 * dt;
 #pragma unroll
-      for (int nt = 0; nt < kRT; ++nt) {
-        {
-          uint16_t* dst = o_part + cur[nt].orow * kDh + 64 * h + 16 * dt;
-#pragma unroll
-          for (int hf = 0; hf < 2; ++hf) {
-            const int b8 = 8 * hf;
-            const float iv = inv[nt];
-            *reinterpret_cast<u32x4*>(dst + b8) =
-                u32x4{pack_bf16x2(oa[nt][b8 + 0] * iv, oa[nt][b8 + 1] * iv),
-                      pack_bf16x2(oa[nt][b8 + 2] * iv, oa[nt][b8 + 3] * iv),
-                      pack_bf16x2(oa[nt][b8 + 4] * iv, oa[nt][b8 + 5] * iv),
-                      pack_bf16x2(oa[nt][b8 + 6] * iv, oa[nt][b8 + 7] * iv)};
-          }
-        }
+      for (int hf = 0; hf < 2; ++hf) {
+        const int b8 = 8 * hf;
+        *reinterpret_cast<u32x4*>(dst + 16 * hf) =
+            u32x4{pack_bf16x2(oa[b8 + 0] * inv, oa[b8 + 1] * inv),
+                  pack_bf16x2(oa[b8 + 2] * inv, oa[b8 + 3] * inv),
+                  pack_bf16x2(oa[b8 + 4] * inv, oa[b8 + 5] * inv),
+                  pack_bf16x2(oa[b8 + 6] * inv, oa[b8 + 7] * inv)};
       }
     }
     // (both half-waves hold the same m and l; their stores coincide)
+    lse_part[rr0.orow] = lse2 * 0.69314718055994531f;
+    // ---- the wave's 32 rows leave row-contiguous: instruction j stores rows
+    // 4j .. 4j + 3, lane L the 16-byte chunk L % 16 of row 4j + L / 16.  LDS
+    // operations of a wave complete in order, so the tile is read back after
+    // it was written, and rewritten only after this readback.
 #pragma unroll
-    for (int nt = 0; nt < kRT; ++nt) lse_part[cur[nt].orow] = lse2[nt] * 0.69314718055994531f;
+    for (int j = 0; j < 8; ++j) {
+      const int row = 4 * j + (lane >> 4), chunk = lane & 15;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(o_tile + row * kOStride + chunk * 16);
+      const int64_t orow = orow_tile[row];
+      *reinterpret_cast<u32x4*>(o_part + orow * kDh + chunk * 8) = v;
+    }
     if (!have1) break;
 
     // ---- rotate the pipeline (the cursor still sits at pass p+2's segment)
     P0 = P1;
     P1 = P2;
-#pragma unroll
-    for (int nt = 0; nt < kRT; ++nt) {
-      rr0[nt] = rr1[nt];
-      if (have2) rr1[nt] = row_dec(raw2[nt], P2.cnt, rho0 + 32 * nt);
-#pragma unroll
-      for (int ks = 0; ks < 8; ++ks) qf[nt][ks] = qn[nt][ks];
-    }
+    rr0 = rr1;
+    if (have2) rr1 = row_dec(raw2);
+    qf = qn;
     have1 = have2;
   }
 }
 
-// Persistent workgroups per CU: one per wave slot of each SIMD (67 KB of LDS
-// each).
-constexpr int kAttnWgPerCu = kWavesPerSimd;
+// Persistent workgroups per CU (135 KB of LDS each).
+constexpr int kAttnWgPerCu = 1;
 
 int device_cus() {
   static int cus[64] = {0};
@@ -541,8 +511,8 @@ hipError_t launch_g(const void* q, const void* k, const void* v, bool fp8, int b
   int shift = 0;
   kdiv_params(kslots, &magic, &shift);
   auto kern = fp8 ? sparse_attn_kernel<G, true> : sparse_attn_kernel<G, false>;
-  hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(grid)), dim3(kAttnThreads), 0, stream, q, k,
-                     v, N, H_kv, kslots, magic, shift, scale_log2, out_scale, blk_offsets,
+  hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(grid)), dim3(kThreads), 0, stream, q, k, v,
+                     N, H_kv, kslots, magic, shift, scale_log2, out_scale, blk_offsets,
                      blk_entries, sched, sv, q_begin, q_count, o_part, lse_part);
   return hipGetLastError();
 }
