@@ -22,7 +22,9 @@
 //    32-key tile, so the block max-pool is an in-lane max plus one exchange
 //    between the two half-waves.  No score ever leaves the VGPRs.
 //  * Q^idx fragments stay in VGPRs for the whole scan; K^idx blocks stream
-//    through double-buffered, XOR-swizzled LDS with one barrier per block.
+//    through double-buffered, row-padded LDS with one barrier per block, and
+//    the K^idx fragments of the next 32-key tile are read while the MFMAs of
+//    the current one run.
 //  * After the exchange, each lane owns exactly one row and keeps that row's
 //    top-(k-1) (score, block) list sorted in VGPRs.  A new block can only
 //    enter when it beats the row's current k-1-th score; the insertion runs
@@ -39,10 +41,16 @@ namespace {
 constexpr int kIdxThreads = 512;
 constexpr int kIdxRows = 512;  // rows per workgroup, 64 per wave
 
+// K^idx rows in LDS are padded by 16 bytes (272 B for d_idx = 128, 144 B for
+// 64): a 16-lane phase of 16-byte reads of rows n .. n + 15 starts at distinct
+// 4-bank groups, and every fragment read of a lane is one base address plus a
+// compile-time offset.
+template <int DIDX>
+constexpr int kidx_stride() { return DIDX * 2 + 16; }
+
 template <int DIDX>
 __device__ __forceinline__ int kidx_lds_off(int key, int c) {
-  constexpr int NCH = DIDX / 8;  // 16-byte chunks per key row
-  return key * (DIDX * 2) + ((c ^ (key & (NCH - 1))) << 4);
+  return key * kidx_stride<DIDX>() + c * 16;
 }
 
 __device__ __forceinline__ float max16(const f32x16& a) {
@@ -86,7 +94,8 @@ __global__ __launch_bounds__(kIdxThreads, 1) void index_topk_kernel(
   constexpr int KM = KP - 1;
   constexpr int NCH = DIDX / 8;
   constexpr int STEPS = DIDX / 16;
-  constexpr int TILE = kBk * DIDX * 2;
+  constexpr int KSTR = kidx_stride<DIDX>();
+  constexpr int TILE = kBk * KSTR;
   constexpr int PER = kBk * NCH / kIdxThreads;  // 16-byte chunks staged per thread
   __shared__ __attribute__((aligned(16))) uint8_t lds[KM > 0 ? 2 * TILE : 16];
 
@@ -131,9 +140,15 @@ __global__ __launch_bounds__(kIdxThreads, 1) void index_topk_kernel(
         qf[nt][ks] = as_bf16x8(*reinterpret_cast<const u32x4*>(qrow + 16 * ks + 8 * h));
     }
 
+    // K^idx blocks are staged through registers two blocks ahead: while block
+    // b is scored, block b + 2 is in flight and block b + 1 (loaded one step
+    // earlier) is written to the other LDS buffer at the end of the step.  The
+    // loads are issued unconditionally (a block index past the last is clamped
+    // to it) so the in-order vmcnt waits never cover the loads just issued.
     const uint16_t* kbase = k_idx + bat * N * DIDX;
-    u32x4 st[PER];
-    auto load_block = [&](int blk) {
+    u32x4 stA[PER], stB[PER];
+    auto load_block = [&](int blk, u32x4(&st)[PER]) {
+      blk = min(blk, Lmax - 1);
 #pragma unroll
       for (int p = 0; p < PER; ++p) {
         const int cid = tid + p * kIdxThreads;
@@ -141,7 +156,7 @@ __global__ __launch_bounds__(kIdxThreads, 1) void index_topk_kernel(
         st[p] = *reinterpret_cast<const u32x4*>(kbase + (static_cast<int64_t>(blk) * kBk + key) * DIDX + c * 8);
       }
     };
-    auto store_block = [&](int buf) {
+    auto store_block = [&](int buf, const u32x4(&st)[PER]) {
 #pragma unroll
       for (int p = 0; p < PER; ++p) {
         const int cid = tid + p * kIdxThreads;
@@ -150,24 +165,33 @@ __global__ __launch_bounds__(kIdxThreads, 1) void index_topk_kernel(
       }
     };
 
-    if (Lmax > 0) {
-      load_block(0);
-      store_block(0);
-      __syncthreads();
-    }
-    for (int b = 0; b < Lmax; ++b) {
-      const int cur = b & 1;
-      if (b + 1 < Lmax) load_block(b + 1);
-      const uint8_t* tile = lds + cur * TILE;
+    // Score block b from LDS buffer b & 1 and update the row's top list.
+    auto score_block = [&](int b) {
+      // Fragment (mt, ks) of this lane: key row 32 mt + n, 16-byte chunk
+      // 2 ks + h.  The fragments of key tile mt + 1 are read while the 2 x
+      // STEPS MFMAs of tile mt run.
+      const uint8_t* tile = lds + (b & 1) * TILE + n * KSTR + h * 16;
       float mx0 = -__builtin_huge_valf(), mx1 = -__builtin_huge_valf();
+      bf16x8 kf[2][STEPS];
+#pragma unroll
+      for (int ks = 0; ks < STEPS; ++ks)
+        kf[0][ks] = as_bf16x8(*reinterpret_cast<const u32x4*>(tile + 32 * ks));
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
+        if (mt + 1 < 4) {
+#pragma unroll
+          for (int ks = 0; ks < STEPS; ++ks)
+            kf[(mt + 1) & 1][ks] = as_bf16x8(
+                *reinterpret_cast<const u32x4*>(tile + 32 * (mt + 1) * KSTR + 32 * ks));
+        }
+        // keep those reads ahead of this tile's MFMAs (the scheduler would
+        // otherwise sink each read next to its use and expose its latency)
+        __builtin_amdgcn_sched_barrier(0);
         f32x16 a0 = {}, a1 = {};
 #pragma unroll
         for (int ks = 0; ks < STEPS; ++ks) {
-          const bf16x8 kf = as_bf16x8(*reinterpret_cast<const u32x4*>(tile + kidx_lds_off<DIDX>(32 * mt + n, 2 * ks + h)));
-          a0 = mfma32x32x16(kf, qf[0][ks], a0);
-          a1 = mfma32x32x16(kf, qf[1][ks], a1);
+          a0 = mfma32x32x16(kf[mt & 1][ks], qf[0][ks], a0);
+          a1 = mfma32x32x16(kf[mt & 1][ks], qf[1][ks], a1);
         }
         mx0 = fmaxf(mx0, max16(a0));
         mx1 = fmaxf(mx1, max16(a1));
@@ -194,8 +218,27 @@ __global__ __launch_bounds__(kIdxThreads, 1) void index_topk_kernel(
           moved = moved || sw;
         }
       }
-      if (b + 1 < Lmax) store_block(cur ^ 1);
+    };
+
+    if (Lmax > 0) {
+      load_block(0, stA);
+      store_block(0, stA);
+      load_block(1, stB);
       __syncthreads();
+    }
+    // Two blocks per iteration so that the staging registers alternate
+    // statically: even steps load into stA and store stB, odd steps the reverse.
+    for (int b = 0; b < Lmax; b += 2) {
+      load_block(b + 2, stA);
+      score_block(b);
+      if (b + 1 < Lmax) store_block(1, stB);
+      __syncthreads();
+      if (b + 1 < Lmax) {
+        load_block(b + 3, stB);
+        score_block(b + 1);
+        if (b + 2 < Lmax) store_block(0, stA);
+        __syncthreads();
+      }
     }
   }
 
