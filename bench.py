@@ -27,9 +27,43 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 
+# Sources whose change invalidates a recorded hardware-counter traffic figure
+# of the attention kernel (its own code and the schedule it walks).
+TRAFFIC_SOURCES = ("sparse_attn.hip", "msa_internal.h", "invert.hip")
+
 
 def log(msg):
     print(msg, file=sys.stderr, flush=True)
+
+
+def sources_sha256() -> str:
+    import hashlib
+    hsh = hashlib.sha256()
+    for name in TRAFFIC_SOURCES:
+        with open(os.path.join(ROOT, "block_sparse_attention_idx_amd", "csrc", name), "rb") as f:
+            hsh.update(f.read())
+    return hsh.hexdigest()
+
+
+def recorded_traffic(workload: str):
+    """HBM bytes per attention launch from the committed rocprofv3 counter
+    summary for this workload (FETCH_SIZE and WRITE_SIZE scaled by a plain
+    copy of known size), or None when there is none or the kernel sources
+    changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", f"sparse_attn_fwd_{workload}_hbm_traffic.md")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path):
+        if line.startswith("- ") and ":" in line:
+            key, val = line[2:].split(":", 1)
+            fields[key.strip()] = val.strip().strip("`")
+    if fields.get("source_sha256") != sources_sha256():
+        return None
+    try:
+        return float(fields["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 def main():
@@ -39,7 +73,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="prefill_n131072_hq64_hkv4_k16_hot64")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=768,
+    ap.add_argument("--cpu-rows", type=int, default=3072,
                     help="query rows of the oracle sample (all heads and groups)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="first run one plain device-to-device copy of this many MiB (a kernel "
@@ -165,8 +199,10 @@ def main():
             v["frac"] = v["achieved"] / v["peak"]
         dom = max(kernels, key=lambda n: kernels[n]["ms"])
         dk = kernels[dom]
+        traffic = recorded_traffic(w.name) if dom == "sparse_attn_fwd" else None
         roofline = {"kernel": dom, "bound": dk["bound"], "achieved": dk["achieved"],
-                    "peak": dk["peak"], "unit": dk["unit"], "frac": dk["frac"], "traffic": None}
+                    "peak": dk["peak"], "unit": dk["unit"], "frac": dk["frac"],
+                    "traffic": traffic}
     else:
         roofline = None
 
