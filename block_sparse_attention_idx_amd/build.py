@@ -11,7 +11,10 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libmsa.so")
 SOURCES = ["api.hip", "index_topk.hip", "invert.hip", "sparse_attn.hip", "combine.hip"]
-FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
+# -fno-honor-nans: no NaN reaches a kernel from valid inputs (scores are finite
+# or -inf, and every row and (query, group) has a visible key), so fmaxf needs
+# no canonicalising copies of MFMA results; infinities are still honoured.
+FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-fno-honor-nans",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-I", os.path.join(ROOT, "include"), "-I", CSRC]
 

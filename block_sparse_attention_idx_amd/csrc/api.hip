@@ -86,7 +86,7 @@ ForwardLayout forward_layout(const msa_dims* d, const msa_opts* o) {
   const int64_t nchunks = (d->N + L.qc - 1) / L.qc;
   for (int64_t c = (nchunks > 2 ? nchunks - 2 : 0); c < nchunks; ++c) {
     const int64_t qb = c * L.qc, qn = (d->N - qb) < L.qc ? (d->N - qb) : L.qc;
-    const msa::SchedLayout s = msa::sched_layout(d->batch, d->H_kv, qb, qn);
+    const msa::SchedLayout s = msa::sched_layout(d->batch, d->H_kv, d->G, d->k, qb, qn);
     words = s.words > words ? s.words : words;
   }
   size_t off = 0;
@@ -147,7 +147,7 @@ int msa_invert_workspace_size(const msa_dims* dims, int64_t q_begin, int64_t q_c
   if (st) return st;
   if ((st = check_range(dims, q_begin, q_count))) return st;
   if (!bytes) return MSA_ERR_NULL;
-  const msa::SchedLayout s = msa::sched_layout(dims->batch, dims->H_kv, q_begin, q_count);
+  const msa::SchedLayout s = msa::sched_layout(dims->batch, dims->H_kv, dims->G, dims->k, q_begin, q_count);
   *bytes = static_cast<size_t>(s.words) * 4;
   return MSA_OK;
 }
@@ -162,9 +162,9 @@ int msa_invert_blocks(const msa_dims* dims, const int32_t* block_idx, int64_t q_
   if (misaligned(block_idx) || misaligned(blk_offsets) || misaligned(blk_entries) ||
       misaligned(sched))
     return MSA_ERR_ALIGN;
-  const msa::SchedLayout s = msa::sched_layout(dims->batch, dims->H_kv, q_begin, q_count);
+  const msa::SchedLayout s = msa::sched_layout(dims->batch, dims->H_kv, dims->G, dims->k, q_begin, q_count);
   if (sched_bytes < static_cast<size_t>(s.words) * 4) return MSA_ERR_WORKSPACE;
-  hipError_t e = msa::launch_invert(block_idx, dims->batch, dims->H_kv, dims->k, q_begin,
+  hipError_t e = msa::launch_invert(block_idx, dims->batch, dims->H_kv, dims->G, dims->k, q_begin,
                                     q_count, blk_offsets, blk_entries, static_cast<int32_t*>(sched),
                                     static_cast<hipStream_t>(stream));
   return e == hipSuccess ? MSA_OK : hip_fail(e);
@@ -266,7 +266,7 @@ int msa_forward(const msa_dims* dims, const msa_opts* opts, const void* q, const
                                           static_cast<const uint16_t*>(k_idx), dims->batch, dims->N,
                                           dims->H_kv, dims->d_idx, dims->k, qb, qn, bi, s);
     if (e != hipSuccess) return hip_fail(e);
-    e = msa::launch_invert(bi, dims->batch, dims->H_kv, dims->k, qb, qn, offs, ents, sched, s);
+    e = msa::launch_invert(bi, dims->batch, dims->H_kv, dims->G, dims->k, qb, qn, offs, ents, sched, s);
     if (e != hipSuccess) return hip_fail(e);
     e = msa::launch_sparse_attn(q, k, v, fp8, dims->batch, dims->N, dims->H_kv, dims->G, dims->k,
                                 sl2, osc, offs, ents, sched, qb, qn, opart, lpart, s);

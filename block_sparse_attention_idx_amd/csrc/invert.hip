@@ -14,24 +14,28 @@
 //  2. colscan:  exclusive prefix of cnt down each block column (over tiles),
 //               in place; column totals tot[seq][block].
 //  3. binscan:  one workgroup scans the totals over all (seq, block) bins into
-//               absolute CSR offsets; then it lists the non-empty segments --
-//               a bin restricted to one query window, in (seq, window, block)
-//               order -- with their start positions in that order.
+//               absolute CSR offsets, then the pass counts ceil(len / EPP),
+//               EPP = kPassRows / G, of the segments -- a bin restricted to
+//               one query window, in (seq, window, block) order -- into the
+//               first pass of every segment.
 //  4. scatter:  the count workgroup's masks are rebuilt and every entry lands at
 //               offset[bin] + colprefix[tile][bin] + popcount(mask below row).
+//  5. passes:   the work list: one descriptor per pass of EPP consecutive
+//               entries of a segment (the last one partial).
 //
 // Pre-scheduled chunking ("MiniMax Sparse Attention (MSA)", KV-Outer Sparse
-// Attention, step 5): the attention pass walks the entries in segment order
-// and splits that sequence evenly over its workgroups, so a block that many
-// queries picked is spread over as many workgroups as its share of the work
-// asks for, and every (query, slot) keeps its own preassigned output slot.
-// The window order keeps the gathered queries of a window in cache while all
-// blocks they picked are processed.
+// Attention, step 5): the attention kernel takes the (seq, window) pairs one
+// after another and splits each pair's passes into one contiguous, equal
+// share per workgroup, so a block that many queries picked is spread over as
+// many workgroups as its share of the work asks for, all workgroups gather
+// the Q rows of one window at a time (they stay in the memory-side cache while
+// every block they picked is processed), and every (query, slot) keeps its own
+// preassigned output slot.
 #include "msa_internal.h"
 
 namespace msa {
 
-SchedLayout sched_layout(int batch, int H_kv, int64_t q_begin, int64_t q_count) {
+SchedLayout sched_layout(int batch, int H_kv, int G, int k, int64_t q_begin, int64_t q_count) {
   SchedLayout s{};
   auto al = [](int64_t w) { return (w + 63) / 64 * 64; };  // 256-byte alignment
   const int64_t nseq = static_cast<int64_t>(batch) * H_kv;
@@ -41,15 +45,20 @@ SchedLayout sched_layout(int batch, int H_kv, int64_t q_begin, int64_t q_count) 
   s.nW = (s.T64 + s.TW - 1) / s.TW;
   s.nbins = nseq * s.B_c;
   s.nseg = nseq * s.nW * s.B_c;
+  s.EPP = kPassRows / (G > 0 ? G : 1);
+  // sum_g ceil(t_g / EPP) <= (sum_g t_g) / EPP + (non-empty segments), and a
+  // window of TW tiles holds at most min(B_c, blocks the window's rows see)
+  // non-empty segments per seq; nseg bounds that.
+  s.max_passes = (nseq * q_count * k + s.EPP - 1) / s.EPP + s.nseg;
   int64_t w = kHdrWords;
   s.off_tot = w;
   w = al(w + s.nbins);
   s.off_bad = w;
   w = al(w + nseq * s.T64);
-  s.off_ckey = w;
-  w = al(w + s.nseg);
-  s.off_cpre = w;
+  s.off_segp = w;
   w = al(w + s.nseg + 1);
+  s.off_pass = w;
+  w = al(w + s.max_passes * 4);
   s.off_cnt = w;
   w = al(w + nseq * s.T64 * s.B_c);
   s.words = w;
@@ -136,16 +145,16 @@ __global__ __launch_bounds__(kScanWaves * 64) void inv_colscan_kernel(
 }
 
 // Single workgroup.  Part 1: exclusive scan of the entry counts over all bins
-// (CSR offsets) and the sum of the bad-id counts.  Part 2: lengths of the
-// segments (seq, window, block) from the column prefixes, and the compact list
-// of the non-empty ones with their start positions in segment order.  Part 2
-// reads only what earlier kernels wrote.
+// (CSR offsets) and the sum of the bad-id counts.  Part 2: exclusive scan of
+// the pass counts of the segments (seq, window, block).  Both read only what
+// earlier kernels wrote.
 constexpr int kBinThreads = 1024;
 
+// Entries of segment g = ((seq * nW) + w) * B_c + blk: the rows of tiles
+// [w TW, (w + 1) TW) in the bin's column prefix.
 __device__ __forceinline__ int seg_len(const int32_t* __restrict__ tot, const int32_t* __restrict__ cnt,
-                                       int64_t sgi, int64_t B_c, int64_t T64, int64_t TW,
-                                       int64_t nW) {
-  const int64_t blk = sgi % B_c, sw = sgi / B_c;
+                                       int64_t g, int64_t B_c, int64_t T64, int64_t TW, int64_t nW) {
+  const int64_t blk = g % B_c, sw = g / B_c;
   const int64_t seq = sw / nW, w = sw % nW;
   const int64_t t0 = w * TW, t1 = t0 + TW;
   const int lo = cnt[(seq * T64 + t0) * B_c + blk];
@@ -153,29 +162,26 @@ __device__ __forceinline__ int seg_len(const int32_t* __restrict__ tot, const in
   return hi - lo;
 }
 
-__device__ __forceinline__ void block_exclusive_scan2(int* se, int* si, int& e, int& it) {
+__device__ __forceinline__ void block_exclusive_scan(int* se, int& e) {
   const int t = threadIdx.x;
   se[t] = e;
-  si[t] = it;
   __syncthreads();
   // Hillis-Steele inclusive scan over the per-thread sums.
   for (int d = 1; d < kBinThreads; d <<= 1) {
-    const int ae = t >= d ? se[t - d] : 0, ai = t >= d ? si[t - d] : 0;
+    const int a = t >= d ? se[t - d] : 0;
     __syncthreads();
-    se[t] += ae;
-    si[t] += ai;
+    se[t] += a;
     __syncthreads();
   }
-  e = se[t] - e;  // exclusive starts of this thread's range
-  it = si[t] - it;
+  e = se[t] - e;  // exclusive start of this thread's range
 }
 
 __global__ __launch_bounds__(kBinThreads) void inv_binscan_kernel(
     const int32_t* __restrict__ tot, const int32_t* __restrict__ cnt, int64_t nbins, int64_t B_c,
-    int64_t T64, int64_t TW, int64_t nW, int64_t nseg, const int32_t* __restrict__ bad,
-    int64_t nbad_slots, int32_t* __restrict__ blk_offsets, int32_t* __restrict__ ckey,
-    int32_t* __restrict__ cpre, int32_t* __restrict__ hdr) {
-  __shared__ int se[kBinThreads], si[kBinThreads];
+    int64_t T64, int64_t TW, int64_t nW, int64_t nseg, int epp, const int32_t* __restrict__ bad,
+    int64_t nbad_slots, int32_t* __restrict__ blk_offsets, int32_t* __restrict__ segp,
+    int32_t* __restrict__ hdr) {
+  __shared__ int se[kBinThreads];
   __shared__ int sbad;
   const int t = threadIdx.x;
   if (t == 0) sbad = 0;
@@ -184,48 +190,63 @@ __global__ __launch_bounds__(kBinThreads) void inv_binscan_kernel(
   {
     const int64_t per = (nbins + kBinThreads - 1) / kBinThreads;
     const int64_t b0 = min<int64_t>(nbins, t * per), b1 = min<int64_t>(nbins, b0 + per);
-    int e = 0, dummy = 0;
+    int e = 0;
     for (int64_t b = b0; b < b1; ++b) e += tot[b];
-    block_exclusive_scan2(se, si, e, dummy);
+    block_exclusive_scan(se, e);
     for (int64_t b = b0; b < b1; ++b) {
       const int64_t seq = b / B_c, blk = b % B_c;
       blk_offsets[seq * (B_c + 1) + blk] = e;
       e += tot[b];
       if (blk == B_c - 1) blk_offsets[seq * (B_c + 1) + B_c] = e;
     }
+    if (t == kBinThreads - 1) hdr[kHdrEntries] = e;
     int nb = 0;
     for (int64_t j = t; j < nbad_slots; j += kBinThreads) nb += bad[j];
     if (nb) atomicAdd(&sbad, nb);
   }
   __syncthreads();
 
-  // ---- part 2: non-empty segments in (seq, window, block) order
+  // ---- part 2: first pass of every segment
   {
     const int64_t per = (nseg + kBinThreads - 1) / kBinThreads;
     const int64_t s0 = min<int64_t>(nseg, t * per), s1 = min<int64_t>(nseg, s0 + per);
-    int pos = 0, nz = 0;
+    int np = 0;
+    for (int64_t g = s0; g < s1; ++g) np += (seg_len(tot, cnt, g, B_c, T64, TW, nW) + epp - 1) / epp;
+    block_exclusive_scan(se, np);
     for (int64_t g = s0; g < s1; ++g) {
-      const int len = seg_len(tot, cnt, g, B_c, T64, TW, nW);
-      pos += len;
-      nz += len > 0 ? 1 : 0;
-    }
-    block_exclusive_scan2(se, si, pos, nz);
-    for (int64_t g = s0; g < s1; ++g) {
-      const int len = seg_len(tot, cnt, g, B_c, T64, TW, nW);
-      if (len > 0) {
-        ckey[nz] = static_cast<int32_t>(g);
-        cpre[nz] = pos;
-        ++nz;
-        pos += len;
-      }
+      segp[g] = np;
+      np += (seg_len(tot, cnt, g, B_c, T64, TW, nW) + epp - 1) / epp;
     }
     if (t == kBinThreads - 1) {
-      cpre[nz] = pos;  // total number of entries
-      hdr[kHdrEntries] = pos;
-      hdr[kHdrSegs] = nz;
+      segp[nseg] = np;
+      hdr[kHdrPasses] = np;
     }
   }
   if (t == 0) hdr[kHdrBad] = sbad;
+}
+
+// Pass descriptors: workgroups stride over the segments, threads over a
+// segment's passes.
+__global__ __launch_bounds__(kInvThreads) void inv_passes_kernel(
+    const int32_t* __restrict__ tot, const int32_t* __restrict__ cnt,
+    const int32_t* __restrict__ segp, const int32_t* __restrict__ blk_offsets, int64_t B_c,
+    int64_t T64, int64_t TW, int64_t nW, int64_t nseg, int epp, PassDesc* __restrict__ passes) {
+  for (int64_t g = blockIdx.x; g < nseg; g += gridDim.x) {
+    const int p0 = segp[g], np = segp[g + 1] - p0;
+    if (np == 0) continue;
+    const int64_t blk = g % B_c, sw = g / B_c;
+    const int64_t seq = sw / nW, w = sw % nW;
+    const int len = seg_len(tot, cnt, g, B_c, T64, TW, nW);
+    const int off = blk_offsets[seq * (B_c + 1) + blk] + cnt[(seq * T64 + w * TW) * B_c + blk];
+    for (int j = threadIdx.x; j < np; j += blockDim.x) {
+      PassDesc d;
+      d.start = off + j * epp;
+      d.cnt = min(epp, len - j * epp);
+      d.seq = static_cast<int32_t>(seq);
+      d.blk = static_cast<int32_t>(blk);
+      passes[p0 + j] = d;
+    }
+  }
 }
 
 __global__ __launch_bounds__(kInvThreads) void inv_scatter_kernel(
@@ -255,10 +276,10 @@ bool g_lds_attr_set = false;
 
 }  // namespace
 
-hipError_t launch_invert(const int32_t* block_idx, int batch, int H_kv, int k,
+hipError_t launch_invert(const int32_t* block_idx, int batch, int H_kv, int G, int k,
                          int64_t q_begin, int64_t q_count, int32_t* blk_offsets,
                          int32_t* blk_entries, int32_t* sched, hipStream_t stream) {
-  const SchedLayout s = sched_layout(batch, H_kv, q_begin, q_count);
+  const SchedLayout s = sched_layout(batch, H_kv, G, k, q_begin, q_count);
   const int64_t nseq = static_cast<int64_t>(batch) * H_kv;
   const size_t lds = static_cast<size_t>(s.B_c) * sizeof(unsigned long long);
   if (!g_lds_attr_set) {
@@ -274,6 +295,8 @@ hipError_t launch_invert(const int32_t* block_idx, int batch, int H_kv, int k,
   int32_t* tot = sched + s.off_tot;
   int32_t* bad = sched + s.off_bad;
   int32_t* cnt = sched + s.off_cnt;
+  int32_t* segp = sched + s.off_segp;
+  const int epp = static_cast<int>(s.EPP);
   const dim3 tiles(static_cast<unsigned>(s.T64), static_cast<unsigned>(nseq));
   hipLaunchKernelGGL(inv_count_kernel, tiles, dim3(kInvThreads), lds, stream, block_idx, k, q_begin,
                      q_count, s.B_c, s.T64, cnt, bad);
@@ -284,12 +307,18 @@ hipError_t launch_invert(const int32_t* block_idx, int batch, int H_kv, int k,
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(inv_binscan_kernel, dim3(1), dim3(kBinThreads), 0, stream, tot, cnt, s.nbins,
-                     s.B_c, s.T64, s.TW, s.nW, s.nseg, bad, nseq * s.T64, blk_offsets,
-                     sched + s.off_ckey, sched + s.off_cpre, hdr);
+                     s.B_c, s.T64, s.TW, s.nW, s.nseg, epp, bad, nseq * s.T64, blk_offsets, segp,
+                     hdr);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(inv_scatter_kernel, tiles, dim3(kInvThreads), lds, stream, block_idx, k, q_begin,
                      q_count, s.B_c, s.T64, cnt, blk_offsets, blk_entries);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t pgrid = s.nseg < 8192 ? s.nseg : 8192;
+  hipLaunchKernelGGL(inv_passes_kernel, dim3(static_cast<unsigned>(pgrid > 0 ? pgrid : 1)),
+                     dim3(kInvThreads), 0, stream, tot, cnt, segp, blk_offsets, s.B_c, s.T64, s.TW,
+                     s.nW, s.nseg, epp, reinterpret_cast<PassDesc*>(sched + s.off_pass));
   return hipGetLastError();
 }
 

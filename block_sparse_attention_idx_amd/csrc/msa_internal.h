@@ -18,12 +18,22 @@ constexpr int kBk = 128;   // tokens per key block
 constexpr int kDh = 128;   // head dimension of Q, K, V
 constexpr int kXcds = 8;   // MI355X: workgroups are dealt round-robin to 8 XCDs
 
-// Query rows per scheduling window of the attention pass: the (query, slot)
-// entries of a window are processed, block by block, before the next window
-// starts, so the gathered Q rows of a window are re-read while still cached.
-// A multiple of 64; build-time tunable.
+// Attention workgroup: kAttnWaves waves, one 32-row MFMA tile each, so a pass
+// is kPassRows (query, head) rows = kPassRows / G entries.  Build-time
+// tunable: 8 waves (two per SIMD) or 4 waves (one per SIMD, all 512 registers).
+#ifndef MSA_ATTN_WAVES
+#define MSA_ATTN_WAVES 8
+#endif
+constexpr int kAttnWaves = MSA_ATTN_WAVES;
+static_assert(kAttnWaves == 4 || kAttnWaves == 8, "4 or 8 attention waves");
+constexpr int kPassRows = 32 * kAttnWaves;
+
+// Query rows per scheduling window of the attention pass: the passes of one
+// (seq, window) pair are shared out over all workgroups before the next pair
+// starts, so the Q rows one window gathers are re-read while the memory-side
+// cache still holds them.  A multiple of 64; build-time tunable.
 #ifndef MSA_ATTN_WINDOW_ROWS
-#define MSA_ATTN_WINDOW_ROWS 16384
+#define MSA_ATTN_WINDOW_ROWS 32768
 #endif
 constexpr int64_t kAttnWindowRows = MSA_ATTN_WINDOW_ROWS;
 static_assert(kAttnWindowRows % 64 == 0 && kAttnWindowRows > 0, "window must be whole 64-row tiles");
@@ -75,9 +85,11 @@ hipError_t launch_index_topk(const uint16_t* q_idx, const uint16_t* k_idx, int b
                              int32_t* block_idx, hipStream_t stream);
 
 // Inversion scratch layout (all offsets in 4-byte words, 256-byte aligned).
-// Segments: bin (seq, block) restricted to query window w, ordered
-// (seq, w, block); only the non-empty ones are listed, with their start
-// position in that order.
+// A segment is a (seq, block) bin restricted to one query window; segments are
+// ordered (seq, window, block), and (seq, window) pairs own B_c consecutive
+// segments.  The attention work list is a flat array of passes in segment
+// order: each holds up to EPP = kPassRows / G consecutive entries of one
+// segment, so no pass spans two segments (or two bins).
 struct SchedLayout {
   int64_t nbins;       // batch * H_kv * B_c
   int64_t B_c;         // key blocks visible to the range
@@ -85,19 +97,27 @@ struct SchedLayout {
   int64_t TW;          // 64-row tiles per scheduling window
   int64_t nW;          // scheduling windows of the range
   int64_t nseg;        // batch * H_kv * nW * B_c
+  int64_t EPP;         // entries per pass
+  int64_t max_passes;  // capacity of the pass list
   int64_t off_tot;     // per-bin totals [nbins]
   int64_t off_bad;     // per-tile out-of-range counts [batch * H_kv * T64]
-  int64_t off_ckey;    // non-empty segment ids [nseg]
-  int64_t off_cpre;    // their start positions [nseg + 1]
+  int64_t off_segp;    // first pass of each segment [nseg + 1]
+  int64_t off_pass;    // pass descriptors [max_passes]
   int64_t off_cnt;     // per-(seq, tile, bin) counts, then column prefixes
   int64_t words;       // total size in words
 };
 // Header words at the start of the scratch buffer.
-enum { kHdrEntries = 0, kHdrBad = 1, kHdrSegs = 2, kHdrWords = 64 };
+enum { kHdrEntries = 0, kHdrBad = 1, kHdrPasses = 2, kHdrWords = 64 };
 
-SchedLayout sched_layout(int batch, int H_kv, int64_t q_begin, int64_t q_count);
+// One attention pass: entries [start, start + cnt) of blk_entries, all in
+// bin (seq, blk).
+struct PassDesc {
+  int32_t start, cnt, seq, blk;
+};
 
-hipError_t launch_invert(const int32_t* block_idx, int batch, int H_kv, int k,
+SchedLayout sched_layout(int batch, int H_kv, int G, int k, int64_t q_begin, int64_t q_count);
+
+hipError_t launch_invert(const int32_t* block_idx, int batch, int H_kv, int G, int k,
                          int64_t q_begin, int64_t q_count, int32_t* blk_offsets,
                          int32_t* blk_entries, int32_t* sched, hipStream_t stream);
 

@@ -15,10 +15,12 @@
 // gfx950 design:
 //  * Persistent grid, one workgroup of 8 waves per CU (two waves per SIMD).
 //    The (query, slot) entries are taken in segment order -- (sequence, query
-//    window, block), see invert.hip -- and that sequence is cut into one equal
-//    contiguous share per workgroup: every workgroup gets the same number of
-//    entries whatever the block popularity, and stages a K/V block only when
-//    its share moves to the next segment.
+//    window, block), see invert.hip -- one (sequence, window) pair at a time,
+//    and each pair's entries are cut into one equal contiguous share per
+//    workgroup: every workgroup gets the same number of entries whatever the
+//    block popularity, all workgroups gather from the same query window at a
+//    time (it stays in the memory-side cache), and a K/V block is staged only
+//    when a share moves to the next segment.
 //  * A pass is 256 (query, head) rows: 256 / G entries x G heads (a query's G
 //    heads are contiguous in Q, 256 B each); each wave owns one 32-row MFMA
 //    column tile.  K (row-major) and V (transposed) live in padded LDS
@@ -47,22 +49,31 @@
 namespace msa {
 namespace {
 
-constexpr int kThreads = 512;
-constexpr int kWaves = kThreads / 64;
-constexpr int kPassRows = 32 * kWaves;  // (query, head) rows per pass
+constexpr int kWaves = kAttnWaves;
+constexpr int kThreads = 64 * kWaves;
+// Scores of the next pass computed while the softmax of this one runs (needs
+// the registers of one wave per SIMD), or after this pass's P V.
+#ifndef MSA_ATTN_OVERLAP
+#define MSA_ATTN_OVERLAP (MSA_ATTN_WAVES == 4)
+#endif
+constexpr bool kOverlap = MSA_ATTN_OVERLAP;
 
 // LDS layouts.  Rows are padded rather than swizzled so that every fragment
 // read of a lane is one base address plus a compile-time offset (no per-read
 // address registers):
 //  * K row-major, 272 B per key row: a 16-lane phase of 16-byte reads of rows
 //    n .. n + 15 starts at banks 4n + const, all distinct.
-//  * V^T, 264 B per output-dimension row, row d stored at position
-//    2 (d mod 64) + d / 64: the 32 rows one 8-byte read touches
-//    (d in 0..15 and 64..79, plus 16 dt) land on 32 distinct even banks.
+//  * V^T, 272 B per output-dimension row, row d stored at position
+//    2 (d mod 64) + d / 64, so that the 32 rows one operand read touches
+//    (d in 0..15 and 64..79, plus 16 dt) are 32 consecutive rows.  Within a
+//    row, bits 2 and 3 of the key index are swapped: the 8 keys
+//    16 s + 8 h' + 4 a + b (h', a, b: lane half, chunk, key in chunk) that
+//    one lane feeds to P^T step s, keys 16 s + 8 a + 4 h' + b, lie in one
+//    16-byte chunk.
 //  * Output tile, 272 B per row: 16-byte writes of rows n .. n + 15 and
 //    16-byte reads of the 16 chunks of one row are both conflict free.
 constexpr int kKStride = 272;
-constexpr int kVStride = 264;
+constexpr int kVStride = 272;
 constexpr int kOStride = 272;
 
 __device__ __forceinline__ int k_lds_off(int key, int c) {  // 16-byte chunk c of key row
@@ -71,8 +82,10 @@ __device__ __forceinline__ int k_lds_off(int key, int c) {  // 16-byte chunk c o
 
 __device__ __forceinline__ int vt_row(int d) { return ((d & 63) << 1) | (d >> 6); }
 
-__device__ __forceinline__ int vt_lds_off(int d, int kc) {  // 8-byte chunk kc (4 keys) of row d
-  return vt_row(d) * kVStride + kc * 8;
+// 8-byte chunk of keys 4 kc .. 4 kc + 3 in V^T row d (bits 0 and 1 of kc swapped).
+__device__ __forceinline__ int vt_lds_off(int d, int kc) {
+  const int kcp = (kc & ~3) | ((kc & 1) << 1) | ((kc & 2) >> 1);
+  return vt_row(d) * kVStride + kcp * 8;
 }
 
 __device__ __forceinline__ uint32_t half_of(const u32x4& w, int dd) {
@@ -80,41 +93,58 @@ __device__ __forceinline__ uint32_t half_of(const u32x4& w, int dd) {
   return (dd & 1) ? (x >> 16) : (x & 0xFFFFu);
 }
 
-// Stage K (row-major) and V (transposed) of one block of one head into LDS.
+// Lanes n and n + 32 hold the two halves of one row: v_permlane32_swap
+// exchanges the half-waves, and combining both results gives each lane the
+// full-row value.
+__device__ __forceinline__ float both_halves_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float both_halves_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Stage K (row-major) and V (transposed) of one block of one head into LDS,
+// with the kThreads threads of the workgroup.
 template <bool FP8>
 __device__ __forceinline__ void stage_kv(const uint8_t* __restrict__ kb, const uint8_t* __restrict__ vb,
                                          int64_t rstride, int nvalid, uint8_t* k_lds,
                                          uint8_t* vt_lds) {
-  // Staging is rare (once per segment); an opaque copy of the thread id keeps
-  // the compiler from hoisting its per-lane addresses out of the caller's
-  // loop, where they would stay live across every pass.
+  // Staging is rare (once per run of passes on a block); an opaque copy of the
+  // thread id keeps the compiler from hoisting its per-lane addresses out of
+  // the caller's loop, where they would stay live across every pass.
   int tid = threadIdx.x;
   asm volatile("" : "+v"(tid));
   // Rows past the end of the sequence (a partial last block) are read from the
   // last valid row and replaced by zeros, so every load is issued at once.
   if constexpr (!FP8) {
-    u32x4 w[4];
+    // 128 keys x 16 chunks of 16 bytes
+    constexpr int R = kBk * 16 / kThreads;
+    u32x4 w[R];
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      const int key = (tid >> 4) + 32 * p, c = tid & 15;
+    for (int p = 0; p < R; ++p) {
+      const int key = (tid >> 4) + (kThreads / 16) * p, c = tid & 15;
       w[p] = *reinterpret_cast<const u32x4*>(kb + min(key, nvalid - 1) * rstride + c * 16);
     }
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      const int key = (tid >> 4) + 32 * p, c = tid & 15;
+    for (int p = 0; p < R; ++p) {
+      const int key = (tid >> 4) + (kThreads / 16) * p, c = tid & 15;
       if (key >= nvalid) w[p] = u32x4{0u, 0u, 0u, 0u};
       *reinterpret_cast<u32x4*>(k_lds + k_lds_off(key, c)) = w[p];
     }
   } else {
-    u32x4 wk[2];
+    // 128 keys x 8 chunks of 16 codes
+    constexpr int R = kBk * 8 / kThreads;
+    u32x4 wk[R];
 #pragma unroll
-    for (int p = 0; p < 2; ++p) {
-      const int key = (tid >> 3) + 64 * p, cc = tid & 7;
+    for (int p = 0; p < R; ++p) {
+      const int key = (tid >> 3) + (kThreads / 8) * p, cc = tid & 7;
       wk[p] = *reinterpret_cast<const u32x4*>(kb + min(key, nvalid - 1) * rstride + cc * 16);
     }
 #pragma unroll
-    for (int p = 0; p < 2; ++p) {
-      const int key = (tid >> 3) + 64 * p, cc = tid & 7;
+    for (int p = 0; p < R; ++p) {
+      const int key = (tid >> 3) + (kThreads / 8) * p, cc = tid & 7;
       const u32x4 w = key < nvalid ? wk[p] : u32x4{0u, 0u, 0u, 0u};
       const u32x2 a = e4m3x4_to_bf16x4(w[0]), b = e4m3x4_to_bf16x4(w[1]);
       const u32x2 c2 = e4m3x4_to_bf16x4(w[2]), d2 = e4m3x4_to_bf16x4(w[3]);
@@ -122,38 +152,42 @@ __device__ __forceinline__ void stage_kv(const uint8_t* __restrict__ kb, const u
       *reinterpret_cast<u32x4*>(k_lds + k_lds_off(key, 2 * cc + 1)) = u32x4{c2[0], c2[1], d2[0], d2[1]};
     }
   }
-  // V: thread (dg, kc) transposes the 8 dims 8 dg .. 8 dg + 7 of keys
-  // 4 kc .. 4 kc + 3 into four-key chunks of V^T rows.
-  const int kc = tid & 31, dg = tid >> 5;
-  u32x4 rows[4];
+  // V: item (dg, kc) transposes the 8 dims 8 dg .. 8 dg + 7 of keys
+  // 4 kc .. 4 kc + 3 into four-key chunks of V^T rows; 16 x 32 items.
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int key = min(4 * kc + j, nvalid - 1);
-    if constexpr (!FP8) {
-      rows[j] = *reinterpret_cast<const u32x4*>(vb + key * rstride + dg * 16);
-    } else {
-      const u32x2 w = *reinterpret_cast<const u32x2*>(vb + key * rstride + dg * 8);
-      rows[j] = u32x4{w[0], w[1], 0u, 0u};
+  for (int it = 0; it < 512 / kThreads; ++it) {
+    const int item = tid + kThreads * it;
+    const int kc = item & 31, dg = item >> 5;
+    u32x4 rows[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int key = min(4 * kc + j, nvalid - 1);
+      if constexpr (!FP8) {
+        rows[j] = *reinterpret_cast<const u32x4*>(vb + key * rstride + dg * 16);
+      } else {
+        const u32x2 w = *reinterpret_cast<const u32x2*>(vb + key * rstride + dg * 8);
+        rows[j] = u32x4{w[0], w[1], 0u, 0u};
+      }
     }
-  }
-  u32x4 row[4];
+    u32x4 row[4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    if (4 * kc + j >= nvalid) {
-      row[j] = u32x4{0u, 0u, 0u, 0u};
-    } else if constexpr (!FP8) {
-      row[j] = rows[j];
-    } else {
-      const u32x2 a = e4m3x4_to_bf16x4(rows[j][0]), b = e4m3x4_to_bf16x4(rows[j][1]);
-      row[j] = u32x4{a[0], a[1], b[0], b[1]};
+    for (int j = 0; j < 4; ++j) {
+      if (4 * kc + j >= nvalid) {
+        row[j] = u32x4{0u, 0u, 0u, 0u};
+      } else if constexpr (!FP8) {
+        row[j] = rows[j];
+      } else {
+        const u32x2 a = e4m3x4_to_bf16x4(rows[j][0]), b = e4m3x4_to_bf16x4(rows[j][1]);
+        row[j] = u32x4{a[0], a[1], b[0], b[1]};
+      }
     }
-  }
 #pragma unroll
-  for (int dd = 0; dd < 8; ++dd) {
-    const int d = 8 * dg + dd;
-    const u32x2 v = {half_of(row[0], dd) | (half_of(row[1], dd) << 16),
-                     half_of(row[2], dd) | (half_of(row[3], dd) << 16)};
-    *reinterpret_cast<u32x2*>(vt_lds + vt_lds_off(d, kc)) = v;
+    for (int dd = 0; dd < 8; ++dd) {
+      const int d = 8 * dg + dd;
+      const u32x2 v = {half_of(row[0], dd) | (half_of(row[1], dd) << 16),
+                       half_of(row[2], dd) | (half_of(row[3], dd) << 16)};
+      *reinterpret_cast<u32x2*>(vt_lds + vt_lds_off(d, kc)) = v;
+    }
   }
 }
 
@@ -184,167 +218,93 @@ struct QFrag<true> {
   }
 };
 
-struct AttnSched {
-  int64_t B_c, T64, TW, nW;
-  int64_t off_ckey, off_cpre, off_cnt;
-};
-
 template <int G, bool FP8>
-__global__ __launch_bounds__(kThreads, 2) void sparse_attn_kernel(
+__global__ __launch_bounds__(kThreads, 8 / kWaves) void sparse_attn_kernel(
     const void* __restrict__ qp, const void* __restrict__ kp, const void* __restrict__ vp,
     int64_t N, int H_kv, int kslots, uint32_t kdiv_magic, int kdiv_shift, float scale_log2,
-    float out_scale, const int32_t* __restrict__ blk_offsets, const int32_t* __restrict__ entries,
-    const int32_t* __restrict__ sched, AttnSched sv, int64_t q_begin, int64_t q_count,
+    float out_scale, const int32_t* __restrict__ entries, const int32_t* __restrict__ segp,
+    const PassDesc* __restrict__ passes, int B_c, int npairs, int q_begin, int q_count,
     uint16_t* __restrict__ o_part, float* __restrict__ lse_part) {
-  constexpr int EPP = kPassRows / G;  // entries per pass
-  constexpr int EB = FP8 ? 1 : 2;     // bytes per Q/K/V element
+  constexpr int EB = FP8 ? 1 : 2;  // bytes per Q/K/V element
   __shared__ __attribute__((aligned(16))) uint8_t k_lds[kBk * kKStride];
   __shared__ __attribute__((aligned(16))) uint8_t vt_lds[kDh * kVStride];
   __shared__ __attribute__((aligned(16))) uint8_t o_lds[kWaves * 32 * kOStride];
   __shared__ __attribute__((aligned(8))) int64_t orow_lds[kWaves * 32];
-  __shared__ int s_seg;
+
+  // This workgroup's passes: the (seq, window) pairs in order, and in each
+  // pair one contiguous, equal share of its passes.  next_pass() returns the
+  // next pass index, or -1 when the shares are exhausted (and from then on).
+  int it_pair = -1, it_p = 0, it_end = 0;
+  auto next_pass = [&]() -> int {
+    if (++it_p < it_end) return it_p;
+    while (++it_pair < npairs) {
+      const int a = segp[it_pair * B_c];
+      const int64_t np = segp[(it_pair + 1) * B_c] - a;
+      const int s0 = a + static_cast<int>(np * blockIdx.x / gridDim.x);
+      const int s1 = a + static_cast<int>(np * (blockIdx.x + 1) / gridDim.x);
+      if (s0 < s1) {
+        it_p = s0;
+        it_end = s1;
+        return s0;
+      }
+    }
+    return -1;
+  };
+  const int i0 = next_pass();
+  if (i0 < 0) return;  // uniform
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   const int n = lane & 31, h = lane >> 5;
   const int H_q = H_kv * G;
-  const int32_t* ckey = sched + sv.off_ckey;
-  const int32_t* cpre = sched + sv.off_cpre;
-  const int32_t* ccnt = sched + sv.off_cnt;
-
-  // This workgroup's share [p0, p1) of the entries in segment order.
-  const int64_t T = sched[kHdrEntries];
-  const int64_t nsegc = sched[kHdrSegs];
-  const int64_t p0 = T * blockIdx.x / gridDim.x;
-  const int64_t p1 = T * (blockIdx.x + 1) / gridDim.x;
-  if (p0 >= p1) return;
-  if (tid == 0) {  // last non-empty segment starting at or before p0
-    int64_t lo = 0, hi = nsegc - 1;
-    while (lo < hi) {
-      const int64_t mid = (lo + hi + 1) >> 1;
-      if (cpre[mid] <= p0) lo = mid; else hi = mid - 1;
-    }
-    s_seg = static_cast<int>(lo);
-  }
-  __syncthreads();
-
-  // Segment cursor (uniform across the workgroup).
-  int64_t c = s_seg;
-  int64_t seg_end = 0, eoff = 0, seq_q = 0;
-  int seq = 0, blk = 0;
-  const uint8_t* seg_q = nullptr;  // Q rows of this segment's (batch, group)
-  auto open_segment = [&](int64_t cc) {
-    const int key = ckey[cc];
-    const int B_c = static_cast<int>(sv.B_c), nW = static_cast<int>(sv.nW);
-    blk = key % B_c;
-    const int sw = key / B_c;
-    seq = sw / nW;
-    const int64_t t0 = static_cast<int64_t>(sw % nW) * sv.TW;
-    // entry index = position + eoff
-    eoff = static_cast<int64_t>(blk_offsets[static_cast<int64_t>(seq) * (B_c + 1) + blk]) +
-           ccnt[(seq * sv.T64 + t0) * sv.B_c + blk] - cpre[cc];
-    seg_end = cpre[cc + 1];
-    seq_q = static_cast<int64_t>(seq) * q_count;
-    const int bat = seq / H_kv, r = seq % H_kv;
-    seg_q = static_cast<const uint8_t*>(qp) +
-            (static_cast<int64_t>(bat) * N * H_q + r * G) * static_cast<int64_t>(kDh) * EB;
-  };
-  open_segment(c);
 
   // Output dimension of V^T operand row n in d-tile 0 (d-tile dt adds 16 dt;
   // see the output step below), and the lane's fragment base addresses.
   const int dsel = 64 * ((n >> 2) & 1) + 4 * (n >> 3) + (n & 3);
   const uint8_t* k_base = k_lds + n * kKStride + h * 16;
-  const uint8_t* v_base = vt_lds + vt_row(dsel) * kVStride + h * 8;
+  const uint8_t* v_base = vt_lds + vt_row(dsel) * kVStride + h * 16;
   uint8_t* o_tile = o_lds + wave * 32 * kOStride;
   int64_t* orow_tile = orow_lds + wave * 32;
   const int rho = 32 * wave + n;     // this lane's row of the pass
   const int e_row = rho / G, g_row = rho % G;
 
-  // Per-lane row descriptor of a pass.  An entry holds qrow * k + slot; the
-  // division by k is a multiply-high by the host's round-up reciprocal.  A row
-  // past the pass's entries takes the pass's first entry (same head): it
-  // recomputes that row bit for bit, so its stores repeat that row's stores.
+  // Per-lane row of a pass.  An entry holds qrow * k + slot; the division by
+  // k is a multiply-high by the host's round-up reciprocal.  A row past the
+  // pass's entries takes the pass's first entry (same head): it recomputes
+  // that row bit for bit, so its stores repeat that row's stores.
   struct RowRef {
     const uint8_t* q;  // the row's Q vector
     int64_t orow;      // partial-output row (seq, qrow, slot, g)
-    int64_t i;         // query position
+    int i;             // query position
   };
-  auto row_ent = [&](int64_t pos, int cnt) {  // raw entry word
-    return static_cast<uint32_t>(entries[pos + eoff + (e_row < cnt ? e_row : 0)]);
+  auto row_ent = [&](const PassDesc& D) {  // raw entry word
+    return static_cast<uint32_t>(entries[D.start + (e_row < D.cnt ? e_row : 0)]);
   };
-  auto row_dec = [&](uint32_t ent) {  // with the cursor at the pass's segment
+  auto row_dec = [&](uint32_t ent, int seq) {
     RowRef rr;
     const uint32_t qrow = kslots == 1 ? ent : (__umulhi(ent, kdiv_magic) >> kdiv_shift);
     const uint32_t slot = ent - qrow * static_cast<uint32_t>(kslots);
-    rr.i = q_begin + qrow;
-    rr.orow = ((seq_q + qrow) * kslots + slot) * G + g_row;
-    rr.q = seg_q + (rr.i * H_q + g_row) * static_cast<int64_t>(kDh) * EB;
+    rr.i = q_begin + static_cast<int>(qrow);
+    rr.orow = ((static_cast<int64_t>(seq) * q_count + qrow) * kslots + slot) * G + g_row;
+    const int bat = seq / H_kv, r = seq - bat * H_kv;
+    rr.q = static_cast<const uint8_t*>(qp) +
+           ((static_cast<int64_t>(bat) * N + rr.i) * H_q + r * G + g_row) * static_cast<int64_t>(kDh) * EB;
     return rr;
   };
 
-  // ---- software pipeline over passes: while pass p computes, the Q rows of
-  // pass p+1 are in flight and the entries of pass p+2 are being read.  A pass
-  // never spans two segments; the segment cursor always sits at the furthest
-  // pass looked up.
-  struct Pass {
-    int64_t pos;  // first position (segment order)
-    int cnt;      // entries
-    int seq, blk;
-  };
-  auto next_pass = [&](int64_t at, Pass& P) -> bool {
-    if (at >= p1) return false;
-    if (at >= seg_end) {
-      // (with a consistent work list the next segment starts exactly here)
-      if (c + 1 >= nsegc) return false;
-      open_segment(++c);
-    }
-    P.pos = at;
-    P.cnt = static_cast<int>(min<int64_t>(EPP, min(seg_end, p1) - at));
-    P.seq = seq;
-    P.blk = blk;
-    return P.cnt > 0;
+  auto stage = [&](const PassDesc& D) {
+    const int64_t key0 = static_cast<int64_t>(D.blk) * kBk;
+    const int bat = D.seq / H_kv, r = D.seq - bat * H_kv;
+    const int64_t rstride = static_cast<int64_t>(H_kv) * kDh * EB;
+    const int64_t row0 = (static_cast<int64_t>(bat) * N + key0) * H_kv + r;
+    stage_kv<FP8>(static_cast<const uint8_t*>(kp) + row0 * kDh * EB,
+                  static_cast<const uint8_t*>(vp) + row0 * kDh * EB, rstride,
+                  static_cast<int>(min<int64_t>(kBk, N - key0)), k_lds, vt_lds);
   };
 
-  Pass P0, P1{}, P2{};
-  RowRef rr0, rr1;
-  uint32_t raw2 = 0;  // pass p+2's entry word, decoded one iteration later
-  QFrag<FP8> qf, qn;
-  if (!next_pass(p0, P0)) return;  // uniform
-  rr0 = row_dec(row_ent(P0.pos, P0.cnt));
-  bool have1 = next_pass(P0.pos + P0.cnt, P1);
-  if (have1) rr1 = row_dec(row_ent(P1.pos, P1.cnt));
-  qf.load(rr0.q, h);
-  // Settle the first pass's gather here, once: inside the loop qf is always a
-  // copy of an already-waited prefetch.
-#pragma unroll
-  for (int ks = 0; ks < 8; ++ks) asm volatile("" ::"v"(qf.w[ks]));
-  int64_t staged = -1;
-
-  while (true) {
-    // ---- stage K and V of this pass's block if not resident
-    const int64_t bin = static_cast<int64_t>(P0.seq) * sv.B_c + P0.blk;
-    const int64_t key0 = static_cast<int64_t>(P0.blk) * kBk;
-    if (bin != staged) {
-      __syncthreads();
-      const int64_t bat = P0.seq / H_kv;
-      const int r = P0.seq % H_kv;
-      const int64_t rstride = static_cast<int64_t>(H_kv) * kDh * EB;
-      const uint8_t* kb = static_cast<const uint8_t*>(kp) + ((bat * N + key0) * H_kv + r) * kDh * EB;
-      const uint8_t* vb = static_cast<const uint8_t*>(vp) + ((bat * N + key0) * H_kv + r) * kDh * EB;
-      stage_kv<FP8>(kb, vb, rstride, static_cast<int>(min<int64_t>(kBk, N - key0)), k_lds, vt_lds);
-      __syncthreads();
-      staged = bin;
-    }
-
-    // ---- read pass p+2's entry and gather pass p+1's Q row (unconditionally:
-    // a missing pass reads entry 0 / this pass's row and ignores it)
-    const bool have2 = have1 && next_pass(P1.pos + P1.cnt, P2);
-    raw2 = static_cast<uint32_t>(entries[have2 ? P2.pos + eoff + (e_row < P2.cnt ? e_row : 0) : 0]);
-    qn.load(have1 ? rr1.q : rr0.q, h);
-
-    // ---- S^T = K_b Q^T: acc[mt] holds keys 32mt + 8(e/4) + 4h + (e%4) of this row
-    f32x16 acc[4];
+  // S^T = K_b Q^T of one pass: acc[mt] holds keys 32mt + 8(e/4) + 4h + (e%4)
+  // of this lane's row.
+  auto scores = [&](const QFrag<FP8>& q, f32x16(&acc)[4]) {
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
       acc[mt] = f32x16{};
@@ -352,39 +312,52 @@ __global__ __launch_bounds__(kThreads, 2) void sparse_attn_kernel(
       for (int ks = 0; ks < 8; ++ks) {
         // row 32 mt + n, 16-byte chunk 2 ks + h
         const bf16x8 kf = as_bf16x8(*reinterpret_cast<const u32x4*>(k_base + 32 * mt * kKStride + 32 * ks));
-        acc[mt] = mfma32x32x16(kf, qf.get(ks), acc[mt]);
+        acc[mt] = mfma32x32x16(kf, q.get(ks), acc[mt]);
       }
     }
+  };
 
-    // ---- softmax.  The causal mask only bites in a query's own block, so it
-    // runs on a wave-uniform branch taken by the few passes that hold such a
-    // row.  The maximum is taken on the raw scores and the scale is folded
-    // into one FMA before exp2; the row sum adds the fp32 probabilities, so
-    // lse is the exact log-sum-exp up to fp32 rounding.
-    const bool own = P0.blk == (rr0.i >> 7);
+  // The causal mask only bites in a query's own block, so it runs on a
+  // wave-uniform branch taken by the few passes that hold such a row.  Key
+  // 32mt + 8(e/4) + 4h + (e%4) is hidden when it lies past the query; the
+  // lane part 4h moves to the limit so that the comparisons take constants.
+  // The opaque statement keeps the branch a branch (not a select executed by
+  // every pass), and the mask is a bit select on the sign of lim - key, which
+  // needs no scalar condition registers.
+  auto mask_own = [&](f32x16(&acc)[4], const RowRef& rr, int blk) {
+    const bool own = blk == (rr.i >> 7);
     if (__any(own)) {
-      const int limit = own ? static_cast<int>(rr0.i - key0) : kBk - 1;
+      asm volatile("" ::: "memory");
+      const int lim = (own ? rr.i - blk * kBk : kBk - 1) - 4 * h;
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
 #pragma unroll
         for (int el = 0; el < 16; ++el) {
-          const int key = 32 * mt + 8 * (el >> 2) + 4 * h + (el & 3);
-          if (key > limit) acc[mt][el] = -__builtin_huge_valf();
+          const uint32_t hide = static_cast<uint32_t>((lim - (32 * mt + 8 * (el >> 2) + (el & 3))) >> 31);
+          acc[mt][el] = __uint_as_float((__float_as_uint(acc[mt][el]) & ~hide) | (0xFF800000u & hide));
         }
       }
     }
-    float m = -__builtin_huge_valf();
+  };
+
+  // Row maximum on the raw scores, then the scale folded into one FMA before
+  // exp2; the row sum adds the fp32 probabilities, so lse is the exact
+  // log-sum-exp up to fp32 rounding.  The two half-waves hold the two halves
+  // of every row and swap partial results with one v_permlane32_swap.
+  // P^T fragments (B operand of O^T = V^T P^T): step st = 2 mt + e2 covers
+  // keys 32mt + 16e2 + 8(j/4) + 4h + (j%4), accumulator elements 8e2 .. +7.
+  auto softmax = [&](const f32x16(&acc)[4], bf16x8(&pf)[8], float& inv, float& lse2) {
+    float m0 = -__builtin_huge_valf(), m1 = -__builtin_huge_valf();
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
 #pragma unroll
-      for (int el = 0; el < 16; el += 2) m = fmaxf(m, fmaxf(acc[mt][el], acc[mt][el + 1]));
+      for (int el = 0; el < 16; el += 4) {
+        m0 = fmaxf(m0, fmaxf(acc[mt][el], acc[mt][el + 1]));
+        m1 = fmaxf(m1, fmaxf(acc[mt][el + 2], acc[mt][el + 3]));
+      }
     }
-    m = fmaxf(m, __shfl_xor(m, 32));
-    const float mb = m * scale_log2;  // scale_log2 > 0: the max commutes with it
-    float l = 0.f;
-    // P^T fragments (B operand of O^T = V^T P^T): step st = 2 mt + e2 covers
-    // keys 32mt + 16e2 + 8(j/4) + 4h + (j%4), accumulator elements 8e2 .. +7.
-    bf16x8 pf[8];
+    const float mb = both_halves_max(fmaxf(m0, m1)) * scale_log2;  // scale_log2 > 0
+    float l0 = 0.f, l1 = 0.f;
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
 #pragma unroll
@@ -395,29 +368,29 @@ __global__ __launch_bounds__(kThreads, 2) void sparse_attn_kernel(
           const float pa = __builtin_amdgcn_exp2f(__builtin_fmaf(acc[mt][8 * e2 + 2 * j], scale_log2, -mb));
           const float pb = __builtin_amdgcn_exp2f(__builtin_fmaf(acc[mt][8 * e2 + 2 * j + 1], scale_log2, -mb));
           w[j] = pack_bf16x2(pa, pb);
-          l += pa + pb;
+          l0 += pa;
+          l1 += pb;
         }
         pf[2 * mt + e2] = as_bf16x8(u32x4{w[0], w[1], w[2], w[3]});
       }
     }
-    l += __shfl_xor(l, 32);
-    const float inv = out_scale / l;
-    const float lse2 = mb + __builtin_amdgcn_logf(l);
+    const float l = both_halves_sum(l0 + l1);
+    inv = out_scale * __builtin_amdgcn_rcpf(l);
+    lse2 = mb + __builtin_amdgcn_logf(l);
+  };
 
-    // ---- O^T = V^T P^T, one 32-dim tile at a time; lane (n, h) receives dims
-    // 64h + 16dt + el of its row and writes them to the wave's output tile.
-    if (h == 0) orow_tile[n] = rr0.orow;
+  // O^T = V^T P^T, one 32-dim tile at a time; lane (n, h) receives dims
+  // 64h + 16dt + el of its row and writes them, scaled, to the wave's tile.
+  auto pv_out = [&](const bf16x8(&pf)[8], float inv) {
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) {
       f32x16 oa = {};
 #pragma unroll
       for (int st = 0; st < 8; ++st) {
-        // row dsel + 16 dt (stored at vt_row(dsel) + 32 dt), 8-byte chunks
-        // c1 = 4 st + h = 8 mt + 4 e2 + h and c1 + 2
-        const uint8_t* vp8 = v_base + 32 * dt * kVStride + 32 * st;
-        const u32x2 lo = *reinterpret_cast<const u32x2*>(vp8);
-        const u32x2 hi = *reinterpret_cast<const u32x2*>(vp8 + 16);
-        oa = mfma32x32x16(as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]}), pf[st], oa);
+        // row dsel + 16 dt (stored at vt_row(dsel) + 32 dt); keys
+        // 16 st + 8 h .. + 7, one 16-byte chunk in the permuted key order
+        const u32x4 vf = *reinterpret_cast<const u32x4*>(v_base + 32 * dt * kVStride + 32 * st);
+        oa = mfma32x32x16(as_bf16x8(vf), pf[st], oa);
       }
       uint8_t* dst = o_tile + n * kOStride + 128 * h + 32 * dt;
 #pragma unroll
@@ -430,9 +403,87 @@ __global__ __launch_bounds__(kThreads, 2) void sparse_attn_kernel(
                   pack_bf16x2(oa[b8 + 6] * inv, oa[b8 + 7] * inv)};
       }
     }
+  };
+
+  // ---- software pipeline over passes p, p+1, p+2, p+3: pass p runs its
+  // softmax and P V while the scores of pass p+1 go through the matrix cores
+  // (when p+1 uses the same K/V block), the Q rows of pass p+2 are in flight
+  // and the entry of pass p+3 is being read.  Past the end of the work the
+  // last pass stands in (its loads are valid and their results unused).
+  const int i1 = next_pass();
+  const bool have1_0 = i1 >= 0;
+  const int j1 = have1_0 ? i1 : i0;
+  const int i2 = have1_0 ? next_pass() : -1;
+  const bool have2_0 = i2 >= 0;
+  int j_last = have2_0 ? i2 : j1;  // furthest pass looked up (a valid index)
+  PassDesc D0 = passes[i0];
+  PassDesc D1 = passes[j1];
+  PassDesc D2 = passes[j_last];
+  bool have1 = have1_0, have2 = have2_0;
+  RowRef rr0 = row_dec(row_ent(D0), D0.seq);
+  RowRef rr1 = row_dec(row_ent(D1), D1.seq);
+  RowRef rr2 = row_dec(row_ent(D2), D2.seq);
+  QFrag<FP8> qa, qb;
+  f32x16 acca[4], accb[4];
+  {
+    QFrag<FP8> q0;
+    q0.load(rr0.q, h);
+    qa.load(rr1.q, h);
+    // Settle the first gathers here, once: inside the loop every Q fragment is
+    // a prefetch issued one pass earlier.
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) asm volatile("" ::"v"(q0.w[ks]), "v"(qa.w[ks]));
+    stage(D0);
+    __syncthreads();
+    scores(q0, acca);
+  }
+
+  // One pass.  acc holds its scores, qc the Q rows of pass p+1; the scores of
+  // pass p+1 go to accn and the Q rows of pass p+2 to qn.  The loop below
+  // alternates the two register sets, so nothing is copied between passes.
+  auto step = [&](f32x16(&acc)[4], f32x16(&accn)[4], const QFrag<FP8>& qc, QFrag<FP8>& qn) -> bool {
+    // ---- entry of pass p+3 and the Q rows of pass p+2 (unconditionally)
+    const int i3 = have2 ? next_pass() : -1;
+    const bool have3 = i3 >= 0;
+    if (have3) j_last = i3;
+    const PassDesc D3 = passes[j_last];
+    const uint32_t raw3 = row_ent(D3);
+    qn.load(rr2.q, h);
+
+    mask_own(acc, rr0, D0.blk);
+
+    // ---- softmax of pass p; the scores of pass p+1 overlap it when that pass
+    // uses the staged block (the MFMAs run while the VALU does the softmax).
+    const bool same = have1 && D1.seq == D0.seq && D1.blk == D0.blk;
+    bf16x8 pf[8];
+    float inv, lse2;
+    if (kOverlap && same) {
+      scores(qc, accn);
+      softmax(acc, pf, inv, lse2);
+      // Interleave: each MFMA with about nine VALU operations, the K fragment
+      // reads two MFMAs ahead.
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+      for (int i = 0; i < 30; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x402, 9, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x402, 9, 0);
+      }
+    } else {
+      softmax(acc, pf, inv, lse2);
+    }
+
+    // ---- O^T = V^T P^T into the wave's tile, then out
+    if (h == 0) orow_tile[n] = rr0.orow;
+    pv_out(pf, inv);
     // (both half-waves hold the same m and l; their stores coincide)
     lse_part[rr0.orow] = lse2 * 0.69314718055994531f;
-    // ---- the wave's 32 rows leave row-contiguous: instruction j stores rows
+    // The wave's 32 rows leave row-contiguous: instruction j stores rows
     // 4j .. 4j + 3, lane L the 16-byte chunk L % 16 of row 4j + L / 16.  LDS
     // operations of a wave complete in order, so the tile is read back after
     // it was written, and rewritten only after this readback.
@@ -443,15 +494,30 @@ __global__ __launch_bounds__(kThreads, 2) void sparse_attn_kernel(
       const int64_t orow = orow_tile[row];
       *reinterpret_cast<u32x4*>(o_part + orow * kDh + chunk * 8) = v;
     }
-    if (!have1) break;
+    if (!have1) return false;
 
-    // ---- rotate the pipeline (the cursor still sits at pass p+2's segment)
-    P0 = P1;
-    P1 = P2;
+    // ---- pass p+1 on another block: stage it, then its scores
+    if (!same) {
+      __syncthreads();
+      stage(D1);
+      __syncthreads();
+      scores(qc, accn);
+    } else if (!kOverlap) {
+      scores(qc, accn);
+    }
+
+    // ---- advance the pass descriptors and row references
+    D0 = D1;
+    D1 = D2;
+    D2 = D3;
     rr0 = rr1;
-    if (have2) rr1 = row_dec(raw2);
-    qf = qn;
+    rr1 = rr2;
+    rr2 = row_dec(raw3, D3.seq);
     have1 = have2;
+    have2 = have3;
+    return true;
+  };
+  while (step(acca, accb, qa, qb) && step(accb, acca, qb, qa)) {
   }
 }
 
@@ -495,25 +561,24 @@ namespace {
 template <int G>
 hipError_t launch_g(const void* q, const void* k, const void* v, bool fp8, int batch, int64_t N,
                     int H_kv, int kslots, float scale_log2, float out_scale,
-                    const int32_t* blk_offsets, const int32_t* blk_entries, const int32_t* sched,
-                    int64_t q_begin, int64_t q_count, uint16_t* o_part, float* lse_part,
-                    hipStream_t stream) {
-  const SchedLayout s = sched_layout(batch, H_kv, q_begin, q_count);
-  const AttnSched sv{s.B_c, s.T64, s.TW, s.nW, s.off_ckey, s.off_cpre, s.off_cnt};
+                    const int32_t* blk_entries, const int32_t* sched, int64_t q_begin,
+                    int64_t q_count, uint16_t* o_part, float* lse_part, hipStream_t stream) {
+  const SchedLayout s = sched_layout(batch, H_kv, G, kslots, q_begin, q_count);
   // Never more workgroups than passes, so every workgroup has work when the
   // range is small.
-  const int64_t entries_max = static_cast<int64_t>(batch) * H_kv * q_count * kslots;
-  const int64_t passes = (entries_max + (kPassRows / G) - 1) / (kPassRows / G);
   int64_t grid = static_cast<int64_t>(device_cus()) * kAttnWgPerCu;
-  if (passes < grid) grid = passes;
+  const int64_t min_passes = (static_cast<int64_t>(batch) * H_kv * q_count * kslots + s.EPP - 1) / s.EPP;
+  if (min_passes < grid) grid = min_passes;
   if (grid < 1) grid = 1;
   uint32_t magic = 0;
   int shift = 0;
   kdiv_params(kslots, &magic, &shift);
   auto kern = fp8 ? sparse_attn_kernel<G, true> : sparse_attn_kernel<G, false>;
   hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(grid)), dim3(kThreads), 0, stream, q, k, v,
-                     N, H_kv, kslots, magic, shift, scale_log2, out_scale, blk_offsets,
-                     blk_entries, sched, sv, q_begin, q_count, o_part, lse_part);
+                     N, H_kv, kslots, magic, shift, scale_log2, out_scale, blk_entries,
+                     sched + s.off_segp, reinterpret_cast<const PassDesc*>(sched + s.off_pass),
+                     static_cast<int>(s.B_c), static_cast<int>(batch * H_kv * s.nW),
+                     static_cast<int>(q_begin), static_cast<int>(q_count), o_part, lse_part);
   return hipGetLastError();
 }
 
@@ -528,8 +593,7 @@ hipError_t launch_sparse_attn(const void* q, const void* k, const void* v, bool 
 #define MSA_ATTN_CASE(GG)                                                                      \
   case GG:                                                                                     \
     return launch_g<GG>(q, k, v, fp8, batch, N, H_kv, kslots, scale_log2, out_scale,           \
-                        blk_offsets, blk_entries, sched, q_begin, q_count, o_part, lse_part,   \
-                        stream);
+                        blk_entries, sched, q_begin, q_count, o_part, lse_part, stream);
   switch (G) {
     MSA_ATTN_CASE(1)
     MSA_ATTN_CASE(2)
