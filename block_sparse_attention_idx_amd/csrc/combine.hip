@@ -13,6 +13,7 @@
 // read exactly once) are in flight together; the selection row and the lse
 // values are read first, the weights computed once per (query, head).
 // Output rows (a query's G heads of group r) are contiguous 16-byte stores.
+// Each XCD streams one contiguous share of the partial buffer.
 #include "msa_internal.h"
 
 namespace msa {
@@ -28,8 +29,14 @@ __global__ __launch_bounds__(kCombThreads) void combine_kernel(
   constexpr int TPQ = 16 * G;              // threads per (query, group)
   constexpr int QPW = kCombThreads / TPQ;  // (query, group) pairs per workgroup
   const int t = threadIdx.x;
+  // Workgroups are dealt round-robin to the kXcds XCDs; the grid is a
+  // multiple of kXcds and XCD x takes the x-th contiguous share of the
+  // (query, group) slabs, so each XCD streams its own region of the partial
+  // buffer (measured: steadier and faster than interleaving the XCDs).
+  const int64_t per = gridDim.x / kXcds;
+  const int64_t wgi = (blockIdx.x % kXcds) * per + blockIdx.x / kXcds;
   // flat (query, group) index: f = seq * q_count + row, seq = batch * H_kv + r
-  const int64_t f = static_cast<int64_t>(blockIdx.x) * QPW + t / TPQ;
+  const int64_t f = wgi * QPW + t / TPQ;
   if (f >= rows_total) return;
   const int64_t seq = f / q_count, row = f % q_count;
   const int g = (t % TPQ) >> 4, dc = t & 15;
@@ -89,7 +96,8 @@ hipError_t launch_gk(const int32_t* block_idx, const uint16_t* o_part, const flo
   constexpr int QPW = kCombThreads / (16 * G);
   const int64_t rows_total = static_cast<int64_t>(batch) * H_kv * q_count;
   const int64_t nx = (rows_total + QPW - 1) / QPW;
-  hipLaunchKernelGGL((combine_kernel<G, KMAX>), dim3(static_cast<unsigned>(nx)),
+  const int64_t grid = (nx + kXcds - 1) / kXcds * kXcds;  // see the kernel
+  hipLaunchKernelGGL((combine_kernel<G, KMAX>), dim3(static_cast<unsigned>(grid)),
                      dim3(kCombThreads), 0, stream, block_idx, o_part, lse_part, N, H_kv, k,
                      q_begin, q_count, rows_total, o, lse);
   return hipGetLastError();
