@@ -14,17 +14,16 @@
 //
 // gfx950 design:
 //  * Persistent grid, one workgroup of 8 waves per CU (two waves per SIMD).
-//    The (query, slot) entries are taken in segment order -- (sequence, query
-//    window, block), see invert.hip -- one (sequence, window) pair at a time,
-//    and each pair's entries are cut into one equal contiguous share per
-//    workgroup: every workgroup gets the same number of entries whatever the
-//    block popularity, all workgroups gather from the same query window at a
-//    time (it stays in the memory-side cache), and a K/V block is staged only
-//    when a share moves to the next segment.
+//    The work list is a flat array of pass descriptors (entry start, count,
+//    group, block) built by the inversion, ordered (sequence, query window,
+//    block); the workgroups take the (sequence, window) pairs in order and
+//    each takes an equal contiguous share of every pair's passes: every
+//    workgroup gets the same work whatever the block popularity, and a K/V
+//    block is staged only when consecutive passes change block.
 //  * A pass is 256 (query, head) rows: 256 / G entries x G heads (a query's G
 //    heads are contiguous in Q, 256 B each); each wave owns one 32-row MFMA
 //    column tile.  K (row-major) and V (transposed) live in padded LDS
-//    (67 KB), shared by the 8 waves.
+//    (68 KB), shared by the 8 waves.
 //  * S^T = K_b * Q^T with v_mfma_f32_32x32x16_bf16 (keys on the row
 //    dimension): every lane holds 64 of the 128 keys of one (query, head) row,
 //    so the row max and row sum need one half-wave exchange, and the
@@ -34,13 +33,14 @@
 //    lane ends up with 64 contiguous output dimensions of its row.
 //  * The partial outputs go through an 8.5 KB LDS tile per wave: written in
 //    the MFMA layout (lane = row), read back row-contiguous, and stored 1 KB
-//    contiguous per instruction, so L2 receives whole 128-byte lines rather
-//    than 16-byte pieces of 64 different rows.
-//  * Software pipeline over passes: the Q rows of the next pass are gathered
-//    into registers and the entries of the pass after it are read while the
-//    current pass computes.  Every memory operation of the loop is issued
-//    unconditionally, so the compiler's in-order vmcnt waits never have to
-//    cover the stores or the loads just issued.
+//    contiguous per instruction (non-temporal), so L2 receives whole 128-byte
+//    lines rather than 16-byte pieces of 64 different rows.
+//  * Software pipeline over passes: while pass p computes, the Q rows of pass
+//    p+2 are gathered into registers and the entry of pass p+3 is read; the
+//    scores of pass p+1 follow pass p's P V.  The loop is unrolled twice so
+//    the score and Q registers alternate by name.  Every memory operation of
+//    the loop is issued unconditionally, so the compiler's in-order vmcnt
+//    waits never have to cover the stores or the loads just issued.
 //  * Softmax in base 2 (v_exp_f32) with the scale folded into one FMA; fp8
 //    (OCP e4m3) inputs are widened exactly to bf16 when used and the
 //    per-tensor scales are folded into the softmax scale and the output scale.
@@ -486,13 +486,14 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void sparse_attn_kernel(
     // The wave's 32 rows leave row-contiguous: instruction j stores rows
     // 4j .. 4j + 3, lane L the 16-byte chunk L % 16 of row 4j + L / 16.  LDS
     // operations of a wave complete in order, so the tile is read back after
-    // it was written, and rewritten only after this readback.
+    // it was written, and rewritten only after this readback.  The partials
+    // are read once, much later, by the combine: the stores are non-temporal.
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int row = 4 * j + (lane >> 4), chunk = lane & 15;
       const u32x4 v = *reinterpret_cast<const u32x4*>(o_tile + row * kOStride + chunk * 16);
       const int64_t orow = orow_tile[row];
-      *reinterpret_cast<u32x4*>(o_part + orow * kDh + chunk * 8) = v;
+      __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(o_part + orow * kDh + chunk * 8));
     }
     if (!have1) return false;
 
