@@ -39,6 +39,7 @@ namespace msa {
 namespace {
 
 constexpr int kIdxThreads = 512;
+constexpr int kIdxWaves = kIdxThreads / 64;
 constexpr int kIdxRows = 512;  // rows per workgroup, 64 per wave
 
 // K^idx rows in LDS are padded by 16 bytes (272 B for d_idx = 128, 144 B for
@@ -51,6 +52,12 @@ constexpr int kidx_stride() { return DIDX * 2 + 16; }
 template <int DIDX>
 __device__ __forceinline__ int kidx_lds_off(int key, int c) {
   return key * kidx_stride<DIDX>() + c * 16;
+}
+
+// 16 bytes per lane from global memory straight into LDS: the wave writes
+// 1 KB at lds_base (wave-uniform), lane i at lds_base + 16 i.
+__device__ __forceinline__ void lds_dma16(const void* g, void* lds_base) {
+  __builtin_amdgcn_global_load_lds(g, lds_base, 16, 0, 0);
 }
 
 __device__ __forceinline__ float max16(const f32x16& a) {
@@ -96,8 +103,8 @@ __global__ __launch_bounds__(kIdxThreads, 1) void index_topk_kernel(
   constexpr int STEPS = DIDX / 16;
   constexpr int KSTR = kidx_stride<DIDX>();
   constexpr int TILE = kBk * KSTR;
-  constexpr int PER = kBk * NCH / kIdxThreads;  // 16-byte chunks staged per thread
-  __shared__ __attribute__((aligned(16))) uint8_t lds[KM > 0 ? 2 * TILE : 16];
+  constexpr int NBUF = 4;  // LDS ring: two blocks scored, two in flight
+  __shared__ __attribute__((aligned(16))) uint8_t lds[KM > 0 ? NBUF * TILE : 16];
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
@@ -140,28 +147,34 @@ __global__ __launch_bounds__(kIdxThreads, 1) void index_topk_kernel(
         qf[nt][ks] = as_bf16x8(*reinterpret_cast<const u32x4*>(qrow + 16 * ks + 8 * h));
     }
 
-    // K^idx blocks are staged through registers two blocks ahead: while block
-    // b is scored, block b + 2 is in flight and block b + 1 (loaded one step
-    // earlier) is written to the other LDS buffer at the end of the step.  The
-    // loads are issued unconditionally (a block index past the last is clamped
-    // to it) so the in-order vmcnt waits never cover the loads just issued.
+    // K^idx blocks go straight from global memory into a 4-buffer LDS ring
+    // (global_load_lds, no registers): while blocks b and b + 1 are scored,
+    // blocks b + 2 and b + 3 are in flight into the other two buffers, and one
+    // barrier per two blocks makes them visible.  The padded tile is
+    // NSLOT = 128 x (NCH + 1) 16-byte slots; wave instruction j fills slots
+    // 64 j .. 64 j + 63, lane i slot 64 j + i = (key row) (NCH + 1) + chunk,
+    // where the padding chunk NCH loads the row's last chunk again.  A block
+    // index past the last is clamped to it (its data is never used).
     const uint16_t* kbase = k_idx + bat * N * DIDX;
-    u32x4 stA[PER], stB[PER];
-    auto load_block = [&](int blk, u32x4(&st)[PER]) {
+    constexpr int NSLOT = kBk * (NCH + 1);
+    constexpr int NJ = (NSLOT + 63) / 64;          // wave instructions per block
+    constexpr int JW = (NJ + kIdxWaves - 1) / kIdxWaves;  // per wave (some do one less)
+    int src_off[JW];  // element offset of this lane's slot within a block
+#pragma unroll
+    for (int q = 0; q < JW; ++q) {
+      const int j = wave + kIdxWaves * q;
+      const int sl = min(64 * j + lane, NSLOT - 1);
+      const int key = sl / (NCH + 1), c = min(sl % (NCH + 1), NCH - 1);
+      src_off[q] = key * DIDX + c * 8;
+    }
+    auto stage_block = [&](int blk, int buf) {
       blk = min(blk, Lmax - 1);
+      const uint16_t* src = kbase + static_cast<int64_t>(blk) * kBk * DIDX;
 #pragma unroll
-      for (int p = 0; p < PER; ++p) {
-        const int cid = tid + p * kIdxThreads;
-        const int key = cid / NCH, c = cid % NCH;
-        st[p] = *reinterpret_cast<const u32x4*>(kbase + (static_cast<int64_t>(blk) * kBk + key) * DIDX + c * 8);
-      }
-    };
-    auto store_block = [&](int buf, const u32x4(&st)[PER]) {
-#pragma unroll
-      for (int p = 0; p < PER; ++p) {
-        const int cid = tid + p * kIdxThreads;
-        const int key = cid / NCH, c = cid % NCH;
-        *reinterpret_cast<u32x4*>(lds + buf * TILE + kidx_lds_off<DIDX>(key, c)) = st[p];
+      for (int q = 0; q < JW; ++q) {
+        const int j = wave + kIdxWaves * q;
+        if (j < NJ)  // wave-uniform
+          lds_dma16(src + src_off[q], lds + buf * TILE + 1024 * j);
       }
     };
 
@@ -170,7 +183,7 @@ __global__ __launch_bounds__(kIdxThreads, 1) void index_topk_kernel(
       // Fragment (mt, ks) of this lane: key row 32 mt + n, 16-byte chunk
       // 2 ks + h.  The fragments of key tile mt + 1 are read while the 2 x
       // STEPS MFMAs of tile mt run.
-      const uint8_t* tile = lds + (b & 1) * TILE + n * KSTR + h * 16;
+      const uint8_t* tile = lds + (b % NBUF) * TILE + n * KSTR + h * 16;
       float mx0 = -__builtin_huge_valf(), mx1 = -__builtin_huge_valf();
       bf16x8 kf[2][STEPS];
 #pragma unroll
@@ -221,24 +234,22 @@ __global__ __launch_bounds__(kIdxThreads, 1) void index_topk_kernel(
     };
 
     if (Lmax > 0) {
-      load_block(0, stA);
-      store_block(0, stA);
-      load_block(1, stB);
+      stage_block(0, 0);
+      stage_block(1, 1);
+      __builtin_amdgcn_s_waitcnt(0);  // (all counters: only the ring loads are out)
       __syncthreads();
     }
-    // Two blocks per iteration so that the staging registers alternate
-    // statically: even steps load into stA and store stB, odd steps the reverse.
     for (int b = 0; b < Lmax; b += 2) {
-      load_block(b + 2, stA);
-      score_block(b);
-      if (b + 1 < Lmax) store_block(1, stB);
-      __syncthreads();
-      if (b + 1 < Lmax) {
-        load_block(b + 3, stB);
-        score_block(b + 1);
-        if (b + 2 < Lmax) store_block(0, stA);
-        __syncthreads();
+      if (b + 2 < Lmax) {
+        stage_block(b + 2, (b + 2) % NBUF);
+        stage_block(b + 3, (b + 3) % NBUF);
       }
+      score_block(b);
+      if (b + 1 < Lmax) score_block(b + 1);
+      // this wave's ring loads have landed; the barrier makes every wave's
+      // visible and frees the two buffers just scored
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
     }
   }
 
