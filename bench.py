@@ -9,7 +9,9 @@ seeded inputs.
 
 Prints one JSON line: whole-job tokens/s, the sparse-counted TFLOP/s, per-kernel
 times measured with HIP events on the launch stream, each kernel's roofline
-fraction, and the CPU oracle timed on a bounded sample of the same workload.
+fraction against the published peaks and against peaks measured on this GPU by
+a probe for the same access patterns, and the CPU oracle timed on a bounded
+sample of the same workload.
 """
 from __future__ import annotations
 
@@ -66,6 +68,38 @@ def recorded_traffic(workload: str):
         return None
 
 
+def measured_peaks():
+    """Run the measured-peaks probe (a separate program built next to the
+    library) and return its figures, or None when it is not built or fails."""
+    import subprocess
+    exe = os.path.join(ROOT, "block_sparse_attention_idx_amd", "msa_peaks")
+    if not os.path.exists(exe):
+        log("measured peaks: probe not built (block_sparse_attention_idx_amd.build.build_peaks)")
+        return None
+    log("measured peaks: running the probe")
+    try:
+        r = subprocess.run([exe], capture_output=True, text=True, timeout=180)
+    except subprocess.TimeoutExpired:
+        log("measured peaks: probe timed out")
+        return None
+    if r.returncode != 0:
+        log(f"measured peaks: probe failed ({r.returncode}): {r.stderr.strip()[-300:]}")
+        return None
+    try:
+        return json.loads(r.stdout.strip().splitlines()[-1])
+    except (ValueError, IndexError):
+        log("measured peaks: unreadable probe output")
+        return None
+
+
+# The measured peak each kernel is compared with: the indexer with sustained
+# MFMA throughput, the attention kernel with the random 4 KB read/write mix
+# (its Q gathers and partial-output stores), the combine with sequential reads
+# (its partial slabs), the inversion with a plain copy.
+MEASURED_PEAK_OF = {"index_topk": "mfma_bf16_TFLOPs", "invert_blocks": "hbm_copy_GBs",
+                    "sparse_attn_fwd": "hbm_rand4k_mixed_GBs", "combine": "hbm_seq_read_GBs"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -75,6 +109,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=3072,
                     help="query rows of the oracle sample (all heads and groups)")
+    ap.add_argument("--no-peaks", action="store_true",
+                    help="skip the measured-peaks probe (HBM patterns and MFMA throughput)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="first run one plain device-to-device copy of this many MiB (a kernel "
                          "of known traffic, to calibrate hardware byte counters)")
@@ -203,8 +239,26 @@ def main():
         roofline = {"kernel": dom, "bound": dk["bound"], "achieved": dk["achieved"],
                     "peak": dk["peak"], "unit": dk["unit"], "frac": dk["frac"],
                     "traffic": traffic}
+        if traffic:
+            # the counted HBM bytes over the same launch time (GB/s)
+            roofline["traffic_achieved"] = traffic / dk["ms"] / 1e6
     else:
         roofline = None
+
+    # ---- measured peaks of this GPU for the patterns the kernels use
+    peaks = None if args.no_peaks else measured_peaks()
+    if peaks:
+        log("measured peaks: " + ", ".join(f"{k} {v}" for k, v in peaks.items()))
+        for name, v in kernels.items():
+            key = MEASURED_PEAK_OF.get(name)
+            if key in peaks and peaks[key] > 0:
+                v["measured_peak"] = peaks[key]
+                v["measured_peak_kind"] = key
+                v["frac_measured"] = v["achieved"] / peaks[key]
+        if roofline and roofline.get("traffic_achieved") and roofline["kernel"] in kernels:
+            mp = kernels[roofline["kernel"]].get("measured_peak")
+            if mp:
+                roofline["traffic_frac_measured"] = roofline["traffic_achieved"] / mp
 
     # ---- the CPU oracle on a bounded sample of the same workload
     cpu = None
@@ -244,7 +298,7 @@ def main():
                    "d_h": w.d_h, "d_idx": w.d_idx, "B_k": w.B_k, "k": w.k,
                    "q_chunk": w.q_chunk, "hot_blocks": w.plant},
         "sparse_tflops": tflops, "index_flops": f_idx, "main_flops": f_main,
-        "roofline": roofline, "kernels": kernels, "cpu_baseline": cpu,
+        "roofline": roofline, "kernels": kernels, "measured_peaks": peaks, "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
 

@@ -49,5 +49,22 @@ def build(verbose: bool = False, defines=None, out: str = OUT) -> str:
     return out
 
 
+PEAKS_SRC = os.path.join(HERE, "probes", "peaks.hip")
+PEAKS_BIN = os.path.join(HERE, "msa_peaks")
+
+
+def build_peaks(out: str = PEAKS_BIN) -> str:
+    """Compile the measured-peaks probe that bench.py runs as a child process."""
+    tmp = out + ".tmp"
+    cmd = ["hipcc", "--offload-arch=gfx950", "-O3", "-std=c++17",
+           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", PEAKS_SRC, "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed for the peaks probe:\n{r.stdout}{r.stderr}")
+    os.replace(tmp, out)
+    return out
+
+
 if __name__ == "__main__":
     print(build(verbose=True))
+    print(build_peaks())
