@@ -38,6 +38,9 @@
 namespace msa {
 namespace {
 
+#ifndef IX_DEFER
+#define IX_DEFER 1
+#endif
 constexpr int kIdxThreads = 512;
 constexpr int kIdxWaves = kIdxThreads / 64;
 constexpr int kIdxRows = 512;  // rows per workgroup, 64 per wave
@@ -178,7 +181,37 @@ __global__ __launch_bounds__(kIdxThreads, 1) void index_topk_kernel(
       }
     };
 
-    // Score block b from LDS buffer b & 1 and update the row's top list.
+    // Insertion of a candidate (score, block) into the row's sorted list: the
+    // candidate moves down the list, swapping with every smaller entry.  For
+    // lists of up to 15 entries the candidate of block b is inserted,
+    // branch-free, in the same scheduling region as the MFMAs of block b + 1's
+    // first key tile, so its VALU work runs between those MFMAs instead of
+    // stalling the matrix cores; block b + 1's threshold test comes after it,
+    // so the order of insertions is unchanged.  (Longer lists would not fit
+    // the registers that way; they insert at once, when a lane needs it.)
+    constexpr bool kDefer = IX_DEFER && KP <= 16;
+    float pend_x = 0.f;
+    int pend_b = 0;
+    bool pend_need = false;
+    auto insert_pending = [&]() {
+      float x = pend_x;
+      int xi = pend_b;
+      bool moved = false;
+#pragma unroll
+      for (int j = 0; j < KM; ++j) {
+        const bool sw = pend_need && (moved || x > ts[j]);
+        const float t = ts[j];
+        const int ti = ids[j];
+        ts[j] = sw ? x : t;
+        ids[j] = sw ? xi : ti;
+        x = sw ? t : x;
+        xi = sw ? ti : xi;
+        moved = moved || sw;
+      }
+      pend_need = false;
+    };
+
+    // Score block b from LDS buffer b % NBUF and update the row's top list.
     auto score_block = [&](int b) {
       // Fragment (mt, ks) of this lane: key row 32 mt + n, 16-byte chunk
       // 2 ks + h.  The fragments of key tile mt + 1 are read while the 2 x
@@ -206,6 +239,7 @@ __global__ __launch_bounds__(kIdxThreads, 1) void index_topk_kernel(
           a0 = mfma32x32x16(kf[mt & 1][ks], qf[0][ks], a0);
           a1 = mfma32x32x16(kf[mt & 1][ks], qf[1][ks], a1);
         }
+        if (kDefer && mt == 0) insert_pending();
         mx0 = fmaxf(mx0, max16(a0));
         mx1 = fmaxf(mx1, max16(a1));
       }
@@ -215,21 +249,15 @@ __global__ __launch_bounds__(kIdxThreads, 1) void index_topk_kernel(
       const float recv = __shfl_xor(send, 32);
       const float score = fmaxf(h ? mx1 : mx0, recv);
       const bool need = (b < L_mine) && (score > ts[KM - 1]);
-      if (__any(need)) {
-        float x = score;
-        int xi = b;
-        bool moved = false;
-#pragma unroll
-        for (int j = 0; j < KM; ++j) {
-          const bool sw = need && (moved || x > ts[j]);
-          const float t = ts[j];
-          const int ti = ids[j];
-          ts[j] = sw ? x : t;
-          ids[j] = sw ? xi : ti;
-          x = sw ? t : x;
-          xi = sw ? ti : xi;
-          moved = moved || sw;
-        }
+      if constexpr (kDefer) {
+        pend_x = score;
+        pend_b = b;
+        pend_need = need;
+      } else if (__any(need)) {
+        pend_x = score;
+        pend_b = b;
+        pend_need = need;
+        insert_pending();
       }
     };
 
@@ -251,6 +279,7 @@ __global__ __launch_bounds__(kIdxThreads, 1) void index_topk_kernel(
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
     }
+    if constexpr (kDefer) insert_pending();  // the last block's candidate
   }
 
   if (!mine_ok) return;
