@@ -30,10 +30,12 @@ constexpr int kPassRows = 32 * kAttnWaves;
 
 // Query rows per scheduling window of the attention pass: the passes of one
 // (seq, window) pair are shared out over all workgroups before the next pair
-// starts, so the Q rows one window gathers are re-read while the memory-side
-// cache still holds them.  A multiple of 64; build-time tunable.
+// starts, so the Q rows one window gathers can be re-read while a cache still
+// holds them.  A multiple of 64; build-time tunable.  The default, 2^21 rows,
+// is one window for every supported N: with non-temporal partial-output
+// stores, windows of 4K-32K rows measured slower than none.
 #ifndef MSA_ATTN_WINDOW_ROWS
-#define MSA_ATTN_WINDOW_ROWS 32768
+#define MSA_ATTN_WINDOW_ROWS 2097152
 #endif
 constexpr int64_t kAttnWindowRows = MSA_ATTN_WINDOW_ROWS;
 static_assert(kAttnWindowRows % 64 == 0 && kAttnWindowRows > 0, "window must be whole 64-row tiles");
