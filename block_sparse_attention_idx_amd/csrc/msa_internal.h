@@ -60,21 +60,34 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
-// OCP e4m3fn code -> bf16 bits of (value * 2^-8), exact.  The code's bits are
-// placed into an fp16 (exponent bias 15 instead of 7, so the value is scaled
-// by 2^-8; fp16 subnormals carry the e4m3 subnormals), widened to fp32 and
-// truncated to bf16 (at most 4 significant bits, so no rounding happens).
+// OCP e4m3fn code -> bf16 bits of (value * 2^-8), exact, in integer
+// arithmetic.  The code's bits are placed into an fp16 (exponent bias 15
+// instead of 7, so the value is scaled by 2^-8; fp16 subnormals carry the e4m3
+// subnormals), widened to fp32 and truncated to bf16 (at most 4 significant
+// bits, so no rounding happens).
 __device__ __forceinline__ uint32_t e4m3_to_bf16_scaled(uint32_t c) {
   uint16_t h = static_cast<uint16_t>(((c & 0x80u) << 8) | ((c & 0x7Fu) << 7));
   float f = static_cast<float>(__builtin_bit_cast(_Float16, h));
   return __float_as_uint(f) >> 16;
 }
 
-// 4 e4m3 codes (one u32) -> 4 bf16 (two u32), each scaled by 2^-8.
-__device__ __forceinline__ u32x2 e4m3x4_to_bf16x4(uint32_t w) {
+// The same for 4 codes (one u32) -> 4 bf16 (two u32), in integer arithmetic.
+__device__ __forceinline__ u32x2 e4m3x4_to_bf16x4_int(uint32_t w) {
   u32x2 r;
   r[0] = e4m3_to_bf16_scaled(w & 0xFF) | (e4m3_to_bf16_scaled((w >> 8) & 0xFF) << 16);
   r[1] = e4m3_to_bf16_scaled((w >> 16) & 0xFF) | (e4m3_to_bf16_scaled(w >> 24) << 16);
+  return r;
+}
+
+// 4 OCP e4m3fn codes (one u32) -> 4 bf16 (two u32), each value times 2^-8,
+// exactly: v_cvt_scalef32_pk_bf16_fp8 converts two codes (bytes 0-1, or 2-3
+// with the word select) per instruction.  Every e4m3 value, subnormals
+// included, is a bf16 value, and so is its product with 2^-8; the NaN codes
+// (0x7F, 0xFF) do not occur in saturating quantised inputs.
+__device__ __forceinline__ u32x2 e4m3x4_to_bf16x4(uint32_t w) {
+  u32x2 r;
+  r[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 0x1p-8f, false));
+  r[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 0x1p-8f, true));
   return r;
 }
 

@@ -146,8 +146,8 @@ __device__ __forceinline__ void stage_kv(const uint8_t* __restrict__ kb, const u
     for (int p = 0; p < R; ++p) {
       const int key = (tid >> 3) + (kThreads / 8) * p, cc = tid & 7;
       const u32x4 w = key < nvalid ? wk[p] : u32x4{0u, 0u, 0u, 0u};
-      const u32x2 a = e4m3x4_to_bf16x4(w[0]), b = e4m3x4_to_bf16x4(w[1]);
-      const u32x2 c2 = e4m3x4_to_bf16x4(w[2]), d2 = e4m3x4_to_bf16x4(w[3]);
+      const u32x2 a = e4m3x4_to_bf16x4_int(w[0]), b = e4m3x4_to_bf16x4_int(w[1]);
+      const u32x2 c2 = e4m3x4_to_bf16x4_int(w[2]), d2 = e4m3x4_to_bf16x4_int(w[3]);
       *reinterpret_cast<u32x4*>(k_lds + k_lds_off(key, 2 * cc)) = u32x4{a[0], a[1], b[0], b[1]};
       *reinterpret_cast<u32x4*>(k_lds + k_lds_off(key, 2 * cc + 1)) = u32x4{c2[0], c2[1], d2[0], d2[1]};
     }
@@ -177,7 +177,7 @@ __device__ __forceinline__ void stage_kv(const uint8_t* __restrict__ kb, const u
       } else if constexpr (!FP8) {
         row[j] = rows[j];
       } else {
-        const u32x2 a = e4m3x4_to_bf16x4(rows[j][0]), b = e4m3x4_to_bf16x4(rows[j][1]);
+        const u32x2 a = e4m3x4_to_bf16x4_int(rows[j][0]), b = e4m3x4_to_bf16x4_int(rows[j][1]);
         row[j] = u32x4{a[0], a[1], b[0], b[1]};
       }
     }
@@ -192,8 +192,10 @@ __device__ __forceinline__ void stage_kv(const uint8_t* __restrict__ kb, const u
 }
 
 // Q fragments (B operand of S^T) of one row, dims 16 ks + 8 h .. + 8, kept as
-// loaded (bf16: 8 x 16 B; fp8: 8 x 8 B of codes) and widened when used, so a
-// prefetch is never waited on before its pass.
+// loaded (bf16: 8 x 16 B; fp8: 8 x 8 B of codes) and widened when used (two
+// v_cvt_scalef32_pk_bf16_fp8 per 4 codes), so a prefetch is never waited on
+// before its pass.  K and V are widened once per staging with integer
+// arithmetic (the conversion instruction there made the compiler spill).
 template <bool FP8>
 struct QFrag;
 template <>
@@ -304,15 +306,28 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void sparse_attn_kernel(
 
   // S^T = K_b Q^T of one pass: acc[mt] holds keys 32mt + 8(e/4) + 4h + (e%4)
   // of this lane's row.
+  // For fp8 the reduction step is the outer loop, so each widened Q fragment
+  // is used by its four MFMAs and dies; for bf16 (no widening) the key tile.
   auto scores = [&](const QFrag<FP8>& q, f32x16(&acc)[4]) {
+    // row 32 mt + n, 16-byte chunk 2 ks + h
+    auto kfrag = [&](int mt, int ks) {
+      return as_bf16x8(*reinterpret_cast<const u32x4*>(k_base + 32 * mt * kKStride + 32 * ks));
+    };
+    if constexpr (FP8) {
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-      acc[mt] = f32x16{};
+      for (int mt = 0; mt < 4; ++mt) acc[mt] = f32x16{};
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks) {
-        // row 32 mt + n, 16-byte chunk 2 ks + h
-        const bf16x8 kf = as_bf16x8(*reinterpret_cast<const u32x4*>(k_base + 32 * mt * kKStride + 32 * ks));
-        acc[mt] = mfma32x32x16(kf, q.get(ks), acc[mt]);
+        const bf16x8 qk = q.get(ks);
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) acc[mt] = mfma32x32x16(kfrag(mt, ks), qk, acc[mt]);
+      }
+    } else {
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        acc[mt] = f32x16{};
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) acc[mt] = mfma32x32x16(kfrag(mt, ks), q.get(ks), acc[mt]);
       }
     }
   };
