@@ -27,6 +27,7 @@ EXPORTS = (
     "msa_abi_version", "msa_status_string", "msa_last_hip_error", "msa_index_topk",
     "msa_invert_workspace_size", "msa_invert_blocks", "msa_invert_status",
     "msa_sparse_attn_fwd", "msa_combine", "msa_workspace_size", "msa_forward",
+    "msa_dense_attn_fwd",
 )
 
 
@@ -91,6 +92,7 @@ def lib():
             "msa_combine": ([D, P, P, P, I64, I64, P, P, P], ctypes.c_int),
             "msa_workspace_size": ([D, O, ctypes.POINTER(SZ)], ctypes.c_int),
             "msa_forward": ([D, O, P, P, P, P, P, P, P, P, P, SZ, P], ctypes.c_int),
+            "msa_dense_attn_fwd": ([D, O, P, P, P, I64, I64, P, P, P], ctypes.c_int),
         }
         for name, (args, res) in sig.items():
             f = getattr(L, name)
@@ -243,6 +245,24 @@ def msa_forward(dims: msa_dims, opts: msa_opts, q, k, v, q_idx, k_idx, o=None, l
                                  _p(workspace), workspace.numel() * workspace.element_size(),
                                  _stream(q)), "msa_forward")
     return o, lse, block_idx_out
+
+
+def msa_dense_attn_fwd(dims: msa_dims, opts: msa_opts, q, k, v, q_begin: int = 0,
+                       q_count: Optional[int] = None, o=None, lse=None, want_lse: bool = False):
+    """Dense causal GQA attention (the baseline).  Returns (o bf16 [batch, N, H_q, d_h],
+    lse fp32 [batch, N, H_q] or None); rows outside [q_begin, q_begin + q_count) of a
+    freshly allocated o are uninitialised."""
+    import torch
+    q_count = dims.N - q_begin if q_count is None else q_count
+    if o is None:
+        o = _empty((dims.batch, dims.N, dims.H_q, dims.d_h), torch.bfloat16, q)
+    if lse is None and want_lse:
+        lse = _empty((dims.batch, dims.N, dims.H_q), torch.float32, q)
+    with _dev(q):
+        _check(lib().msa_dense_attn_fwd(ctypes.byref(dims), ctypes.byref(opts), _p(q), _p(k), _p(v),
+                                        q_begin, q_count, _p(o), _p(lse), _stream(q)),
+               "msa_dense_attn_fwd")
+    return o, lse
 
 
 def default_softmax_scale(d_h: int) -> float:

@@ -219,6 +219,34 @@ int msa_combine(const msa_dims* dims, const int32_t* block_idx, const void* o_pa
   return e == hipSuccess ? MSA_OK : hip_fail(e);
 }
 
+int msa_dense_attn_fwd(const msa_dims* dims, const msa_opts* opts, const void* q, const void* k,
+                       const void* v, int64_t q_begin, int64_t q_count, void* o, float* lse,
+                       void* stream) {
+  if (!dims || !opts) return MSA_ERR_NULL;
+  if (dims->batch < 1 || dims->N < 1 || dims->H_kv < 1 || dims->G < 1 || dims->H_q < 1 ||
+      dims->d_h < 1)
+    return MSA_ERR_SHAPE;
+  if (static_cast<int64_t>(dims->G) * dims->H_kv != dims->H_q) return MSA_ERR_SHAPE;
+  if (dims->d_h != msa::kDh) return MSA_ERR_UNSUPPORTED;
+  if (dims->G != 1 && dims->G != 2 && dims->G != 4 && dims->G != 8 && dims->G != 16)
+    return MSA_ERR_UNSUPPORTED;
+  if (q_begin < 0 || q_count < 1 || q_begin > dims->N || q_count > dims->N - q_begin)
+    return MSA_ERR_SHAPE;
+  if (static_cast<int64_t>(dims->batch) * dims->H_kv > (int64_t(1) << 20)) return MSA_ERR_UNSUPPORTED;
+  if (opts->reserved != 0 || !isfinite(opts->softmax_scale)) return MSA_ERR_SHAPE;
+  if (opts->qkv_dtype != MSA_DTYPE_BF16) return MSA_ERR_UNSUPPORTED;
+  if (!q || !k || !v || !o) return MSA_ERR_NULL;
+  if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(o) || (lse && misaligned(lse)))
+    return MSA_ERR_ALIGN;
+  float sl2, osc;
+  attn_scales(dims, opts, &sl2, &osc);
+  hipError_t e = msa::launch_dense_attn(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                                        static_cast<const uint16_t*>(v), dims->batch, dims->N,
+                                        dims->H_kv, dims->G, q_begin, q_count, sl2,
+                                        static_cast<uint16_t*>(o), lse, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MSA_OK : hip_fail(e);
+}
+
 int msa_workspace_size(const msa_dims* dims, const msa_opts* opts, size_t* bytes) {
   int st = check_dims(dims);
   if (st) return st;

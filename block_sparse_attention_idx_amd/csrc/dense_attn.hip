@@ -1,0 +1,316 @@
+// Dense causal GQA attention forward: the baseline that the sparse path is
+// measured against.
+//
+// What is computed ("MiniMax Sparse Attention", sec. 2.1: causal scaled
+// dot-product attention in which G adjacent query heads share one K/V head;
+// the pages quote MSA's prefill speed against this dense form):
+//     O[i, h]   = sum_{j <= i} softmax_j(s_j) V[j, r],
+//     lse[i, h] = ln sum_{j <= i} exp(s_j),
+//     s_j = scale * Q[i, h] . K[j, r],   r = h / G.
+//
+// gfx950 design (query-outer, online softmax):
+//  * One workgroup = 8 waves = 256 (token, head) rows: 256 / G consecutive
+//    tokens times the G heads of one group (a token's G heads are contiguous
+//    in Q and O), one 32-row MFMA column tile per wave.  Q stays in VGPRs.
+//  * The group's key blocks 0 .. (last token) / 128 stream through two LDS
+//    buffers (K row-major, V transposed, rows padded to 272 B as in the
+//    sparse kernel): block b + 1 is loaded into registers while block b is
+//    computed and written to the other buffer after it, one barrier per block.
+//  * Per block and wave: S^T = K_b Q^T (32 v_mfma_f32_32x32x16_bf16, keys on
+//    the row dimension, so each lane holds 64 keys of its own row), the
+//    running max and sum update in base 2, and O^T += V^T P^T (32 MFMAs) with
+//    P^T straight from the score registers.  Every output element a lane
+//    accumulates belongs to the lane's own row, so the rescale by
+//    exp2(m_old - m_new) is a per-lane multiply.  The lanes keep their partial
+//    row sums; the two half-waves add them once, at the end.
+//  * A wave skips the blocks that lie wholly after its last token, and masks
+//    only the blocks that reach past its first token.
+//  * Workgroups are issued heaviest (latest tokens) first; consecutive
+//    workgroups take the same token tile of consecutive groups, so the
+//    workgroups of one XCD (dealt round-robin) share a K/V head in its L2.
+//  * The output leaves through an LDS tile, row-contiguous, 1 KB per store
+//    instruction.
+#include "msa_internal.h"
+
+namespace msa {
+namespace {
+
+constexpr int kDWaves = 8;
+constexpr int kDThreads = 64 * kDWaves;
+constexpr int kDRows = 32 * kDWaves;             // (token, head) rows per workgroup
+constexpr int kStr = 272;                        // padded LDS row of K, V^T and the output tile
+constexpr int kVtOff = kBk * kStr;               // V^T after K in a buffer
+constexpr int kBufBytes = kVtOff + kDh * kStr;   // one block: 69,632 B
+
+// V^T row d is stored at position 2 (d mod 64) + d / 64, and bits 0 and 1 of
+// the 8-byte key-chunk index kc (four keys) are swapped, so that the eight
+// keys one lane feeds to a P^T step lie in one 16-byte chunk and the 32 rows
+// one operand read touches are consecutive.
+__device__ __forceinline__ int dvt_row(int d) { return ((d & 63) << 1) | (d >> 6); }
+__device__ __forceinline__ int dvt_off(int d, int kc) {
+  const int kcp = (kc & ~3) | ((kc & 1) << 1) | ((kc & 2) >> 1);
+  return dvt_row(d) * kStr + kcp * 8;
+}
+
+__device__ __forceinline__ uint32_t bf16_of(const u32x4& w, int dd) {
+  const uint32_t x = w[dd >> 1];
+  return (dd & 1) ? (x >> 16) : (x & 0xFFFFu);
+}
+
+// Lanes n and n + 32 hold the two halves of one row; v_permlane32_swap
+// exchanges the half-waves.
+__device__ __forceinline__ float halves_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float halves_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// One K/V block of one head in flight through registers: thread t holds
+// 16-byte chunks t % 16 of keys t / 16 + 32 p (K) and the 8 dims 8 (t / 32) ..
+// + 7 of keys 4 (t % 32) .. + 3 (V, transposed when written).
+struct KVRegs {
+  u32x4 k[4];
+  u32x4 v[4];
+};
+
+__device__ __forceinline__ void kv_load(KVRegs& R, const uint8_t* __restrict__ kb,
+                                        const uint8_t* __restrict__ vb, int64_t rstride, int nvalid,
+                                        int tid) {
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const int key = (tid >> 4) + 32 * p, c = tid & 15;
+    R.k[p] = *reinterpret_cast<const u32x4*>(kb + min(key, nvalid - 1) * rstride + c * 16);
+  }
+  const int kc = tid & 31, dg = tid >> 5;
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    R.v[j] = *reinterpret_cast<const u32x4*>(vb + min(4 * kc + j, nvalid - 1) * rstride + dg * 16);
+}
+
+// Keys past the end of the sequence become zeros (they are also masked).
+__device__ __forceinline__ void kv_store(const KVRegs& R, uint8_t* buf, int nvalid, int tid) {
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const int key = (tid >> 4) + 32 * p, c = tid & 15;
+    const u32x4 w = key < nvalid ? R.k[p] : u32x4{0u, 0u, 0u, 0u};
+    *reinterpret_cast<u32x4*>(buf + key * kStr + c * 16) = w;
+  }
+  const int kc = tid & 31, dg = tid >> 5;
+  u32x4 row[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) row[j] = 4 * kc + j < nvalid ? R.v[j] : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int dd = 0; dd < 8; ++dd) {
+    const int d = 8 * dg + dd;
+    const u32x2 w = {bf16_of(row[0], dd) | (bf16_of(row[1], dd) << 16),
+                     bf16_of(row[2], dd) | (bf16_of(row[3], dd) << 16)};
+    *reinterpret_cast<u32x2*>(buf + kVtOff + dvt_off(d, kc)) = w;
+  }
+}
+
+template <int G>
+__global__ __launch_bounds__(kDThreads, 1) void dense_attn_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    int64_t N, int H_kv, int nseq, int64_t q_begin, int64_t q_count, int64_t ntile,
+    float scale_log2, uint16_t* __restrict__ o, float* __restrict__ lse) {
+  constexpr int T = kDRows / G;  // tokens per workgroup
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kBufBytes];
+
+  const int64_t wg = blockIdx.x;
+  const int seq = static_cast<int>(wg % nseq);
+  const int64_t tile = ntile - 1 - wg / nseq;
+  const int bat = seq / H_kv, r = seq - bat * H_kv;
+  const int H_q = H_kv * G;
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int n = lane & 31, h = lane >> 5;
+
+  const int64_t q_end = q_begin + q_count;
+  const int64_t t0 = q_begin + tile * T;
+  const int64_t t_last = min(t0 + T, q_end) - 1;
+  const int nb = static_cast<int>(t_last / kBk) + 1;
+
+  // This lane's row (rows past the range repeat the last token; not stored).
+  const int rho = 32 * wave + n;
+  const int64_t t_raw = t0 + rho / G;
+  const int64_t t_row = min(t_raw, t_last);
+  const int g = rho % G;
+  const int64_t orow = (static_cast<int64_t>(bat) * N + t_row) * H_q + r * G + g;
+  // The wave's first and last tokens.
+  const int64_t tw_lo = min(t0 + (32 * wave) / G, t_last);
+  const int64_t tw_hi = min(t0 + (32 * wave + 31) / G, t_last);
+
+  u32x4 qf[8];
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks)
+    qf[ks] = *reinterpret_cast<const u32x4*>(q + orow * kDh + 16 * ks + 8 * h);
+
+  const int64_t rstride = static_cast<int64_t>(H_kv) * kDh * 2;
+  const uint8_t* kseq = reinterpret_cast<const uint8_t*>(k) + (static_cast<int64_t>(bat) * N * H_kv + r) * kDh * 2;
+  const uint8_t* vseq = reinterpret_cast<const uint8_t*>(v) + (static_cast<int64_t>(bat) * N * H_kv + r) * kDh * 2;
+  auto nvalid_of = [&](int b) { return static_cast<int>(min<int64_t>(kBk, N - static_cast<int64_t>(b) * kBk)); };
+
+  const int dsel = 64 * ((n >> 2) & 1) + 4 * (n >> 3) + (n & 3);
+  f32x16 oacc[4];
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt) oacc[dt] = f32x16{};
+  float m_run = -__builtin_huge_valf(), l_run = 0.f;
+
+  KVRegs R;
+  kv_load(R, kseq, vseq, rstride, nvalid_of(0), tid);
+  kv_store(R, lds, nvalid_of(0), tid);
+  __syncthreads();
+
+  for (int b = 0; b < nb; ++b) {
+    // Block b + 1 (the last block again at the end: its loads stay in
+    // bounds, and the copy lands in the buffer nobody reads any more).
+    const int bn = min(b + 1, nb - 1);
+    kv_load(R, kseq + static_cast<int64_t>(bn) * kBk * rstride,
+            vseq + static_cast<int64_t>(bn) * kBk * rstride, rstride, nvalid_of(bn), tid);
+
+    const uint8_t* buf = lds + (b & 1) * kBufBytes;
+    const int64_t key0 = static_cast<int64_t>(b) * kBk;
+    if (key0 <= tw_hi) {  // wave-uniform
+      // S^T = K_b Q^T: acc[mt] holds keys 32 mt + 8 (e / 4) + 4 h + (e % 4).
+      const uint8_t* kfr = buf + n * kStr + h * 16;
+      f32x16 acc[4];
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        acc[mt] = f32x16{};
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks)
+          acc[mt] = mfma32x32x16(as_bf16x8(*reinterpret_cast<const u32x4*>(kfr + 32 * mt * kStr + 32 * ks)),
+                                 as_bf16x8(qf[ks]), acc[mt]);
+      }
+      if (key0 + kBk - 1 > tw_lo) {  // some key of the block lies past some row's token
+        const int lim = static_cast<int>(t_row - key0) - 4 * h;
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+#pragma unroll
+          for (int el = 0; el < 16; ++el) {
+            const uint32_t hide = static_cast<uint32_t>((lim - (32 * mt + 8 * (el >> 2) + (el & 3))) >> 31);
+            acc[mt][el] = __uint_as_float((__float_as_uint(acc[mt][el]) & ~hide) | (0xFF800000u & hide));
+          }
+        }
+      }
+      // Running max in base-2 units (scale_log2 > 0).  Every row sees key 0,
+      // so m_run is finite from block 0 on and a fully hidden row of a later
+      // block gets alpha = 1 and p = 0.
+      float m0 = -__builtin_huge_valf(), m1 = -__builtin_huge_valf();
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+#pragma unroll
+        for (int el = 0; el < 16; el += 4) {
+          m0 = fmaxf(m0, fmaxf(acc[mt][el], acc[mt][el + 1]));
+          m1 = fmaxf(m1, fmaxf(acc[mt][el + 2], acc[mt][el + 3]));
+        }
+      }
+      const float m_new = fmaxf(m_run, halves_max(fmaxf(m0, m1)) * scale_log2);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      m_run = m_new;
+      bf16x8 pf[8];
+      float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+#pragma unroll
+        for (int e2 = 0; e2 < 2; ++e2) {
+          uint32_t w[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const float pa = __builtin_amdgcn_exp2f(__builtin_fmaf(acc[mt][8 * e2 + 2 * j], scale_log2, -m_new));
+            const float pb = __builtin_amdgcn_exp2f(__builtin_fmaf(acc[mt][8 * e2 + 2 * j + 1], scale_log2, -m_new));
+            w[j] = pack_bf16x2(pa, pb);
+            s0 += pa;
+            s1 += pb;
+          }
+          pf[2 * mt + e2] = as_bf16x8(u32x4{w[0], w[1], w[2], w[3]});
+        }
+      }
+      l_run = l_run * alpha + (s0 + s1);
+      // O^T = alpha O^T + V^T P^T; lane (n, h) holds dims 64 h + 16 dt + e of
+      // its row (V^T operand row dsel + 16 dt, stored at dvt_row(dsel) + 32 dt).
+      const uint8_t* vfr = buf + kVtOff + dvt_row(dsel) * kStr + h * 16;
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) {
+        f32x16 a = oacc[dt] * alpha;
+#pragma unroll
+        for (int st = 0; st < 8; ++st)
+          a = mfma32x32x16(as_bf16x8(*reinterpret_cast<const u32x4*>(vfr + 32 * dt * kStr + 32 * st)), pf[st], a);
+        oacc[dt] = a;
+      }
+    }
+
+    // The other buffer was last read in block b - 1, before the previous
+    // barrier.
+    kv_store(R, lds + ((b + 1) & 1) * kBufBytes, nvalid_of(bn), tid);
+    __syncthreads();
+  }
+
+  // ---- normalise and write out (the buffers are free after the last barrier)
+  const float l = halves_sum(l_run);
+  const float inv = __builtin_amdgcn_rcpf(l);
+  if (h == 0 && t_raw < q_end && lse != nullptr)
+    lse[orow] = (m_run + __builtin_amdgcn_logf(l)) * 0.69314718055994531f;
+  uint8_t* o_tile = lds + wave * 32 * kStr;
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt) {
+    uint8_t* dst = o_tile + n * kStr + 128 * h + 32 * dt;
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      const int b8 = 8 * hf;
+      *reinterpret_cast<u32x4*>(dst + 16 * hf) =
+          u32x4{pack_bf16x2(oacc[dt][b8 + 0] * inv, oacc[dt][b8 + 1] * inv),
+                pack_bf16x2(oacc[dt][b8 + 2] * inv, oacc[dt][b8 + 3] * inv),
+                pack_bf16x2(oacc[dt][b8 + 4] * inv, oacc[dt][b8 + 5] * inv),
+                pack_bf16x2(oacc[dt][b8 + 6] * inv, oacc[dt][b8 + 7] * inv)};
+    }
+  }
+  // LDS operations of a wave complete in order: the tile is read back after it
+  // was written.  Instruction j stores rows 4 j .. 4 j + 3, lane L the 16-byte
+  // chunk L % 16 of row 4 j + L / 16.
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int row = 4 * j + (lane >> 4), chunk = lane & 15;
+    const int rr = 32 * wave + row;
+    const int64_t t = t0 + rr / G;
+    const u32x4 val = *reinterpret_cast<const u32x4*>(o_tile + row * kStr + chunk * 16);
+    if (t < q_end) {
+      const int64_t orr = (static_cast<int64_t>(bat) * N + t) * H_q + r * G + rr % G;
+      *reinterpret_cast<u32x4*>(o + orr * kDh + chunk * 8) = val;
+    }
+  }
+}
+
+template <int G>
+hipError_t launch_dense_g(const uint16_t* q, const uint16_t* k, const uint16_t* v, int batch, int64_t N,
+                          int H_kv, int64_t q_begin, int64_t q_count, float scale_log2, uint16_t* o,
+                          float* lse, hipStream_t stream) {
+  constexpr int T = kDRows / G;
+  const int nseq = batch * H_kv;
+  const int64_t ntile = (q_count + T - 1) / T;
+  const int64_t grid = ntile * nseq;
+  if (grid > 0x7FFFFFFFLL) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(dense_attn_kernel<G>, dim3(static_cast<unsigned>(grid)), dim3(kDThreads), 0,
+                     stream, q, k, v, N, H_kv, nseq, q_begin, q_count, ntile, scale_log2, o, lse);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_dense_attn(const uint16_t* q, const uint16_t* k, const uint16_t* v, int batch,
+                             int64_t N, int H_kv, int G, int64_t q_begin, int64_t q_count,
+                             float scale_log2, uint16_t* o, float* lse, hipStream_t stream) {
+  switch (G) {
+    case 1: return launch_dense_g<1>(q, k, v, batch, N, H_kv, q_begin, q_count, scale_log2, o, lse, stream);
+    case 2: return launch_dense_g<2>(q, k, v, batch, N, H_kv, q_begin, q_count, scale_log2, o, lse, stream);
+    case 4: return launch_dense_g<4>(q, k, v, batch, N, H_kv, q_begin, q_count, scale_log2, o, lse, stream);
+    case 8: return launch_dense_g<8>(q, k, v, batch, N, H_kv, q_begin, q_count, scale_log2, o, lse, stream);
+    case 16: return launch_dense_g<16>(q, k, v, batch, N, H_kv, q_begin, q_count, scale_log2, o, lse, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace msa

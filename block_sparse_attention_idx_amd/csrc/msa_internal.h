@@ -151,4 +151,10 @@ hipError_t launch_combine(const int32_t* block_idx, const uint16_t* o_part, cons
                           int batch, int64_t N, int H_kv, int G, int k, int64_t q_begin,
                           int64_t q_count, uint16_t* o, float* lse, hipStream_t stream);
 
+// Dense causal GQA attention (bf16), query rows [q_begin, q_begin + q_count):
+// o [batch][N][H_q][d_h], lse [batch][N][H_q] (natural log; may be null).
+hipError_t launch_dense_attn(const uint16_t* q, const uint16_t* k, const uint16_t* v, int batch,
+                             int64_t N, int H_kv, int G, int64_t q_begin, int64_t q_count,
+                             float scale_log2, uint16_t* o, float* lse, hipStream_t stream);
+
 }  // namespace msa

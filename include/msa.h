@@ -210,6 +210,26 @@ int msa_forward(const msa_dims *dims, const msa_opts *opts, const void *q, const
                 const void *v, const void *q_idx, const void *k_idx, void *o, float *lse,
                 int32_t *block_idx_out, void *workspace, size_t ws_bytes, void *stream);
 
+/*
+ * msa_dense_attn_fwd -- dense causal GQA attention, the baseline MSA is
+ * measured against: every query head attends, with exact softmax, to all
+ * tokens j <= i of its group's K/V head ("MiniMax Sparse Attention", sec. 2.1;
+ * the pages compare MSA's prefill speed with this dense form).
+ *
+ *   q     bf16 [batch][N][H_q][d_h]
+ *   k, v  bf16 [batch][N][H_kv][d_h]
+ *   o     bf16 [batch][N][H_q][d_h] output, rows [q_begin, q_begin + q_count)
+ *         (other rows untouched)
+ *   lse   fp32 [batch][N][H_q] output (may be NULL): natural-log log-sum-exp
+ *         of the scaled scores of each row
+ * Uses dims->batch, N, H_q, H_kv, G and d_h (d_idx, B_k and k are ignored)
+ * and opts->softmax_scale; q_begin needs no alignment.  Only bf16 is
+ * supported (MSA_ERR_UNSUPPORTED for fp8), and batch * H_kv <= 2^20.
+ */
+int msa_dense_attn_fwd(const msa_dims *dims, const msa_opts *opts, const void *q,
+                       const void *k, const void *v, int64_t q_begin, int64_t q_count,
+                       void *o, float *lse, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -143,6 +143,21 @@ def attention(N, B_k, pos, q_rows, K, V, block_idx, softmax_scale=None,
     return O, lse
 
 
+def dense_attention(N, B_k, pos, q_rows, K, V, softmax_scale=None):
+    """Dense causal GQA attention ("MiniMax Sparse Attention", sec. 2.1) for the
+    given query rows, fp64: the sparse attention above with every block
+    0 .. floor(i / B_k) selected, whose visible tokens are then exactly the
+    j <= i of the dense causal form.  Returns (O [n_rows, H_q, d_h],
+    lse [n_rows, H_q])."""
+    pos = np.asarray(pos, np.int64)
+    H_kv = np.asarray(K).shape[1]
+    B = -(-N // B_k)
+    L = pos // B_k
+    sel = np.where(np.arange(B)[None, :] <= L[:, None], np.arange(B)[None, :], -1).astype(np.int32)
+    sel = np.ascontiguousarray(np.broadcast_to(sel[None], (H_kv, len(pos), B)))
+    return attention(N, B_k, pos, q_rows, K, V, sel, softmax_scale=softmax_scale)
+
+
 def combine(block_idx, o_part, lse_part):
     """LSE merge.  block_idx [H_kv, n, k]; o_part [H_kv, n, k, G, d_h] bf16 bits;
     lse_part [H_kv, n, k, G] float32.  Returns (O [n, H_q, d_h], lse [n, H_q])."""

@@ -117,6 +117,25 @@ def test_workspace_and_opts(L):
     assert n.value < ws
 
 
+def test_dense_attn_validation(L):
+    o = msa.make_opts()
+    call = lambda d, o, qb, qn, q=FAKE, out=FAKE, lse=None: L.msa_dense_attn_fwd(
+        ctypes.byref(d), ctypes.byref(o), q, FAKE, FAKE, qb, qn, out, lse, None)
+    # d_idx, B_k and k are not used by the dense path
+    assert call(dims(d_idx=96, B_k=64, k=0, N=0), o, 0, 16) == 2
+    assert call(dims(H_q=9), o, 0, 16) == 2
+    assert call(dims(d_h=64), o, 0, 16) == 3
+    assert call(dims(H_q=6, H_kv=2), o, 0, 16) == 3
+    assert call(dims(), o, -1, 16) == 2
+    assert call(dims(), o, 0, 0) == 2
+    assert call(dims(), o, 2000, 49) == 2
+    assert call(dims(), msa.make_opts(dtype="fp8"), 0, 16) == 3
+    assert call(dims(), o, 0, 16, q=None) == 1
+    assert call(dims(), o, 0, 16, out=ODD) == 4
+    assert call(dims(), o, 0, 16, lse=ODD) == 4
+    assert L.msa_dense_attn_fwd(None, ctypes.byref(o), FAKE, FAKE, FAKE, 0, 16, FAKE, None, None) == 1
+
+
 def test_binding_raises_when_library_missing(monkeypatch):
     monkeypatch.setattr(msa, "_lib", None)
     monkeypatch.setattr(msa, "LIB_PATH", "/nonexistent/libmsa.so")

@@ -292,6 +292,92 @@ def test_forward_chunked_equals_whole_and_deterministic():
     assert torch.equal(a.view(torch.int16), c.view(torch.int16))
 
 
+# --------------------------------------------------------------------------- dense baseline
+
+DENSE_CASES = [
+    TINY,                                    # G = 4
+    TINY.with_(N=1000),                      # ragged last block and tile
+    TINY.with_(N=1),
+    TINY.with_(N=300, H_q=64, H_kv=4),       # G = 16
+    TINY.with_(N=700, H_q=2, H_kv=2),        # G = 1: a tile spans two key blocks
+    TINY.with_(N=520, H_q=4, H_kv=2),        # G = 2
+    TINY.with_(N=900, H_q=16, H_kv=2),       # G = 8
+    TINY.with_(N=640, batch=2),
+]
+
+
+def _dense_oracle(w, rows, bat=0):
+    keys = bat * w.N + np.arange(w.N)
+    return oracle.dense_attention(w.N, w.B_k, rows, synth.host_rows(w, "q", bat * w.N + rows),
+                                  synth.host_rows(w, "k", keys), synth.host_rows(w, "v", keys))
+
+
+@pytest.mark.parametrize("w", DENSE_CASES, ids=lambda w: f"N{w.N}_G{w.G}_b{w.batch}")
+def test_dense_attention_parity(w):
+    log(f"dense N={w.N} H_q={w.H_q} H_kv={w.H_kv} batch={w.batch}")
+    t = device_inputs(w, DEV)
+    out, lse = msa.msa_dense_attn_fwd(dims_of(w), msa.make_opts(), t["q"], t["k"], t["v"],
+                                      want_lse=True)
+    torch.cuda.synchronize()
+    out = out.float().cpu().numpy()
+    lse = lse.cpu().numpy()
+    rows = np.arange(w.N)
+    for b in range(w.batch):
+        O, L = _dense_oracle(w, rows, b)
+        mx, mn = err_stats(out[b], O)
+        log(f"  batch {b}: output max abs {mx:.3g} mean abs {mn:.3g}")
+        assert mx <= 2e-2 and mn <= 2e-3
+        lmx, _ = err_stats(lse[b], L)
+        assert lmx <= 1e-3
+
+
+def test_dense_attention_subrange_leaves_other_rows():
+    """Rows [q_begin, q_begin + q_count) (unaligned) are written; the others keep
+    what the caller put there."""
+    w = TINY.with_(N=1500, H_q=32, H_kv=2)
+    qb, qn = 333, 777
+    log(f"dense subrange N={w.N} rows [{qb}, {qb + qn})")
+    t = device_inputs(w, DEV)
+    o = torch.full((1, w.N, w.H_q, w.d_h), 7.0, dtype=torch.bfloat16, device=DEV)
+    lse = torch.full((1, w.N, w.H_q), -5.0, dtype=torch.float32, device=DEV)
+    msa.msa_dense_attn_fwd(dims_of(w), msa.make_opts(), t["q"], t["k"], t["v"], qb, qn, o=o, lse=lse)
+    torch.cuda.synchronize()
+    o = o.float().cpu().numpy()[0]
+    lse = lse.cpu().numpy()[0]
+    outside = np.r_[0:qb, qb + qn:w.N]
+    assert (o[outside] == 7.0).all() and (lse[outside] == -5.0).all()
+    rows = np.arange(qb, qb + qn)
+    O, L = _dense_oracle(w, rows)
+    mx, mn = err_stats(o[rows], O)
+    assert mx <= 2e-2 and mn <= 2e-3
+    lmx, _ = err_stats(lse[rows], L)
+    assert lmx <= 1e-3
+
+
+def test_dense_attention_full_size_sampled():
+    """128K tokens, 64 query heads over 4 K/V heads: sampled rows against the oracle."""
+    w = synth.P128K_HOT
+    log(f"dense full-size {w.name}")
+    t = device_inputs(w, DEV)
+    out, lse = msa.msa_dense_attn_fwd(dims_of(w), msa.make_opts(), t["q"], t["k"], t["v"],
+                                      want_lse=True)
+    torch.cuda.synchronize()
+    rows = sample_rows(w.N, w.B_k, 12, seed=w.seed)
+    ridx = torch.from_numpy(rows).to(DEV)
+    gout = out[0][ridx].float().cpu().numpy()
+    glse = lse[0][ridx].cpu().numpy()
+    del t, out, lse
+    torch.cuda.empty_cache()
+    log(f"dense full-size {w.name}: oracle on {len(rows)} rows")
+    O, L = oracle.dense_attention(w.N, w.B_k, rows, synth.host_rows(w, "q", rows),
+                                  synth.host_all(w, "k"), synth.host_all(w, "v"))
+    mx, mn = err_stats(gout, O)
+    log(f"  output max abs {mx:.3g} mean abs {mn:.3g}")
+    assert mx <= 2e-2 and mn <= 2e-3
+    lmx, _ = err_stats(glse, L)
+    assert lmx <= 1e-3
+
+
 # --------------------------------------------------------------------------- full-size workloads
 
 BIG = [(synth.P16K, 160), (synth.P128K_HOT, 48), (synth.P128K_FP8, 40), (synth.P1M, 32)]

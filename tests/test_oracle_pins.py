@@ -224,6 +224,24 @@ def test_attention_full_budget_is_dense_causal_gqa():
     np.testing.assert_allclose(O, ref[0].permute(1, 0, 2).numpy(), rtol=0, atol=1e-12)
 
 
+@pytest.mark.parametrize("N,Hq,Hkv,rows", [(300, 4, 2, None), (261, 8, 1, [0, 1, 127, 128, 200, 260]),
+                                           (129, 2, 2, [128])])
+def test_dense_attention_is_library_causal_gqa(N, Hq, Hkv, rows):
+    """The dense baseline's oracle equals library causal attention with K/V
+    repeated over each group's heads, for all rows or a subset (ragged N)."""
+    rng = np.random.default_rng(N + Hq)
+    d, B_k = 32, 128
+    G = Hq // Hkv
+    q, K, V = _make_attn_inputs(rng, N, Hq, Hkv, d)
+    pos = np.arange(N) if rows is None else np.array(rows)
+    O, lse = oracle.dense_attention(N, B_k, pos, q[pos], K, V, softmax_scale=0.2)
+    mask = np.tril(np.ones((N, N), bool))[None].repeat(Hq, axis=0)
+    ref, ref_lse = _sdpa_masked(_f32(q), np.repeat(_f32(K), G, axis=1),
+                                np.repeat(_f32(V), G, axis=1), mask, 0.2)
+    np.testing.assert_allclose(O, ref[pos], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse, ref_lse[pos], rtol=0, atol=1e-12)
+
+
 @pytest.mark.parametrize("N,Hq,Hkv,k,seed", [(900, 4, 2, 3, 11), (1024, 6, 3, 2, 12),
                                             (513, 2, 1, 4, 13)])
 def test_attention_matches_masked_library_attention(N, Hq, Hkv, k, seed):
