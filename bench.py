@@ -10,8 +10,9 @@ seeded inputs.
 Prints one JSON line: whole-job tokens/s, the sparse-counted TFLOP/s, per-kernel
 times measured with HIP events on the launch stream, each kernel's roofline
 fraction against the published peaks and against peaks measured on this GPU by
-a probe for the same access patterns, and the CPU oracle timed on a bounded
-sample of the same workload.
+a probe for the same access patterns, the dense causal GQA kernel on the same
+Q, K, V (the baseline MSA's speedup is quoted against), and the CPU oracle
+timed on a bounded sample of the same workload.
 """
 from __future__ import annotations
 
@@ -111,6 +112,8 @@ def main():
                     help="query rows of the oracle sample (all heads and groups)")
     ap.add_argument("--no-peaks", action="store_true",
                     help="skip the measured-peaks probe (HBM patterns and MFMA throughput)")
+    ap.add_argument("--no-dense", action="store_true",
+                    help="skip the dense causal GQA baseline on the same Q, K, V")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="first run one plain device-to-device copy of this many MiB (a kernel "
                          "of known traffic, to calibrate hardware byte counters)")
@@ -198,6 +201,27 @@ def main():
                                         for it in range(1, args.steps + 1)]))
         log("per call ms: " + ", ".join(f"{k} {v:.3f}" for k, v in kern.items()))
 
+    # ---- the dense causal GQA baseline on the same Q, K, V (bf16 workloads up
+    # to 128K tokens: it grows quadratically, 0.3 s per call at 128K)
+    dense = None
+    if not args.no_dense and w.dtype == "bf16" and w.batch * w.N <= 131072:
+        log("dense baseline: 1 warmup, 3 timed calls")
+        msa.msa_dense_attn_fwd(d, o, t["q"], t["k"], t["v"], o=out)
+        ed0, ed1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ed0.record(stream)
+        for _ in range(3):
+            msa.msa_dense_attn_fwd(d, o, t["q"], t["k"], t["v"], o=out)
+        ed1.record(stream)
+        torch.cuda.synchronize()
+        dms = ed0.elapsed_time(ed1) / 3
+        f_dense = acc.dense_flops(0, w.N, w.H_q, w.d_h, batch=w.batch)
+        dense = {"kernel": "dense_attn_fwd", "ms": dms, "bound": "mfma", "flops": f_dense,
+                 "achieved": f_dense / dms / 1e9, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                 "frac": f_dense / dms / 1e9 / PEAK_BF16_TFLOPS,
+                 "tokens_s": w.batch * w.N / (dms * 1e-3), "msa_speedup": dms / ms_step}
+        log(f"dense baseline: {dms:.2f} ms, {dense['achieved']:.0f} TFLOP/s; "
+            f"msa_forward is {dense['msa_speedup']:.2f}x faster")
+
     # ---- work accounting from the selection actually made
     sel = bi.cpu().numpy().reshape(w.batch * w.H_kv, w.N, w.k)
     f_idx = acc.index_flops(0, w.N, w.H_kv, w.d_idx, w.B_k, batch=w.batch)
@@ -255,6 +279,10 @@ def main():
                 v["measured_peak"] = peaks[key]
                 v["measured_peak_kind"] = key
                 v["frac_measured"] = v["achieved"] / peaks[key]
+        if dense and peaks.get("mfma_bf16_TFLOPs", 0) > 0:
+            dense["measured_peak"] = peaks["mfma_bf16_TFLOPs"]
+            dense["measured_peak_kind"] = "mfma_bf16_TFLOPs"
+            dense["frac_measured"] = dense["achieved"] / peaks["mfma_bf16_TFLOPs"]
         if roofline and roofline.get("traffic_achieved") and roofline["kernel"] in kernels:
             mp = kernels[roofline["kernel"]].get("measured_peak")
             if mp:
@@ -298,7 +326,8 @@ def main():
                    "d_h": w.d_h, "d_idx": w.d_idx, "B_k": w.B_k, "k": w.k,
                    "q_chunk": w.q_chunk, "hot_blocks": w.plant},
         "sparse_tflops": tflops, "index_flops": f_idx, "main_flops": f_main,
-        "roofline": roofline, "kernels": kernels, "measured_peaks": peaks, "cpu_baseline": cpu,
+        "roofline": roofline, "kernels": kernels, "dense_baseline": dense,
+        "measured_peaks": peaks, "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
 

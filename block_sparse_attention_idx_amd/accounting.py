@@ -96,6 +96,12 @@ def main_flops(block_idx: np.ndarray, q_begin: int, N: int, B_k: int, G: int, d_
     return 4.0 * d_h * G * float(visible_keys(block_idx, q_begin, N, B_k).sum())
 
 
+def dense_flops(q_begin: int, q_count: int, H_q: int, d_h: int, batch: int = 1) -> float:
+    """Dense causal attention: 4 d_h FLOPs per (query head, key j <= i)."""
+    i = np.arange(q_begin, q_begin + q_count, dtype=np.float64)
+    return float(batch) * 4.0 * d_h * H_q * float((i + 1.0).sum())
+
+
 def partial_bytes(n_valid_slots: int, G: int, d_h: int) -> int:
     """Bytes of one partial output set: bf16 O-bar (2 d_h) + fp32 lse per head."""
     return n_valid_slots * G * (2 * d_h + 4)

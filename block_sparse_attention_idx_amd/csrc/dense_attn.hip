@@ -21,8 +21,10 @@
 //    running max and sum update in base 2, and O^T += V^T P^T (32 MFMAs) with
 //    P^T straight from the score registers.  Every output element a lane
 //    accumulates belongs to the lane's own row, so the rescale by
-//    exp2(m_old - m_new) is a per-lane multiply.  The lanes keep their partial
-//    row sums; the two half-waves add them once, at the end.
+//    exp2(m_old - m_new) is a per-lane multiply, and the reference max only
+//    moves when a block exceeds it by more than 2^8 (probabilities stay
+//    below 256), so almost every block skips the rescale.  The lanes keep
+//    their partial row sums; the two half-waves add them once, at the end.
 //  * A wave skips the blocks that lie wholly after its last token, and masks
 //    only the blocks that reach past its first token.
 //  * Workgroups are issued heaviest (latest tokens) first; consecutive
@@ -41,6 +43,7 @@ constexpr int kDRows = 32 * kDWaves;             // (token, head) rows per workg
 constexpr int kStr = 272;                        // padded LDS row of K, V^T and the output tile
 constexpr int kVtOff = kBk * kStr;               // V^T after K in a buffer
 constexpr int kBufBytes = kVtOff + kDh * kStr;   // one block: 69,632 B
+constexpr float kLazy = 8.f;                     // log2 of the largest unnormalised probability
 
 // V^T row d is stored at position 2 (d mod 64) + d / 64, and bits 0 and 1 of
 // the 8-byte key-chunk index kc (four keys) are swapped, so that the eight
@@ -159,93 +162,149 @@ __global__ __launch_bounds__(kDThreads, 1) void dense_attn_kernel(
   for (int dt = 0; dt < 4; ++dt) oacc[dt] = f32x16{};
   float m_run = -__builtin_huge_valf(), l_run = 0.f;
 
+  // ---- software pipeline over half blocks (64 keys).  Step (b, hb) runs the
+  // scores of the next half on the matrix cores while the VALU turns the
+  // scores of half (b, hb) into probabilities, then that half's P V.  The loop
+  // body holds the two steps of block b, so the score registers alternate by
+  // name.  LDS: block b in slot b & 1; block b + 1 is written into the other
+  // slot at the top of iteration b (its previous block was last read before
+  // the barrier that ended iteration b - 1) and published by the barrier
+  // between the two steps, in time for the second step's look-ahead scores.
+  //
+  // Scores of one half: s[mt2] holds keys 64 hb + 32 mt2 + 8 (e / 4) + 4 h +
+  // (e % 4) of this lane's row.
+  auto scores_half = [&](const uint8_t* kbuf, int hb, f32x16(&s)[2]) {
+    const uint8_t* kfr = kbuf + (64 * hb + n) * kStr + h * 16;
+#pragma unroll
+    for (int mt2 = 0; mt2 < 2; ++mt2) {
+      s[mt2] = f32x16{};
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks)
+        s[mt2] = mfma32x32x16(as_bf16x8(*reinterpret_cast<const u32x4*>(kfr + 32 * mt2 * kStr + 32 * ks)),
+                              as_bf16x8(qf[ks]), s[mt2]);
+    }
+  };
+
+  const uint8_t* vlane = lds + kVtOff + dvt_row(dsel) * kStr + h * 16;  // slot 0
+  auto step = [&](f32x16(&s)[2], f32x16(&sn)[2], int slot, int b, int hb, const uint8_t* kbuf_next,
+                  int hb_next) {
+    const int64_t key0 = static_cast<int64_t>(b) * kBk + 64 * hb;
+    if (key0 + 63 > tw_lo) {  // wave-uniform: some key of the half lies past some row's token
+      asm volatile("" ::: "memory");
+      const int lim = static_cast<int>(t_row - key0) - 4 * h;
+#pragma unroll
+      for (int mt2 = 0; mt2 < 2; ++mt2) {
+#pragma unroll
+        for (int el = 0; el < 16; ++el) {
+          const uint32_t hide = static_cast<uint32_t>((lim - (32 * mt2 + 8 * (el >> 2) + (el & 3))) >> 31);
+          s[mt2][el] = __uint_as_float((__float_as_uint(s[mt2][el]) & ~hide) | (0xFF800000u & hide));
+        }
+      }
+    }
+    // Reference max in base-2 units (scale_log2 > 0).  It moves only when
+    // the half's max exceeds it by more than kLazy, so every probability
+    // stays below 2^kLazy and almost no step rescales O; the final O / l and
+    // m + log2 l are exact for any reference.  Every row sees key 0, so m_run
+    // is finite from the first half on, and a fully hidden row of a later
+    // half keeps alpha = 1 and gets p = 0.
+    float m0 = -__builtin_huge_valf(), m1 = -__builtin_huge_valf();
+#pragma unroll
+    for (int mt2 = 0; mt2 < 2; ++mt2) {
+#pragma unroll
+      for (int el = 0; el < 16; el += 4) {
+        m0 = fmaxf(m0, fmaxf(s[mt2][el], s[mt2][el + 1]));
+        m1 = fmaxf(m1, fmaxf(s[mt2][el + 2], s[mt2][el + 3]));
+      }
+    }
+    const float m_blk = halves_max(fmaxf(m0, m1)) * scale_log2;
+    const bool raise = m_blk > m_run + kLazy;
+    const float m_new = raise ? m_blk : m_run;
+    if (__any(raise)) {  // wave-uniform, rare
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) oacc[dt] *= alpha;
+      l_run *= alpha;
+    }
+    m_run = m_new;
+
+    // ---- the next half's scores || this half's probabilities, interleaved by
+    // hand (fenced slots): slot i issues look-ahead MFMA i (key tile i / 8,
+    // reduction step i % 8), reads the K fragment of MFMA i + 2, and turns
+    // score pair i (tile i / 8, elements 2 (i % 8), + 1) into probabilities.
+    const uint8_t* kfr = kbuf_next + (64 * hb_next + n) * kStr + h * 16;
+    auto kread = [&](int i) {
+      return *reinterpret_cast<const u32x4*>(kfr + 32 * (i >> 3) * kStr + 32 * (i & 7));
+    };
+    u32x4 kq[3];
+    kq[0] = kread(0);
+    kq[1] = kread(1);
+    uint32_t w[16];
+    float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      if (i + 2 < 16) kq[(i + 2) % 3] = kread(i + 2);
+      const int mt2 = i >> 3, ks = i & 7;
+      sn[mt2] = mfma32x32x16(as_bf16x8(kq[i % 3]), as_bf16x8(qf[ks]), ks == 0 ? f32x16{} : sn[mt2]);
+      const float pa = __builtin_amdgcn_exp2f(__builtin_fmaf(s[mt2][2 * ks], scale_log2, -m_new));
+      const float pb = __builtin_amdgcn_exp2f(__builtin_fmaf(s[mt2][2 * ks + 1], scale_log2, -m_new));
+      w[i] = pack_bf16x2(pa, pb);
+      s0 += pa;
+      s1 += pb;
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    l_run += s0 + s1;
+    // P^T fragment f = 2 mt2 + e2 holds elements 8 e2 .. 8 e2 + 7 of tile
+    // mt2, i.e. pairs 8 mt2 + 4 e2 .. + 3.
+    bf16x8 pf[4];
+#pragma unroll
+    for (int f = 0; f < 4; ++f)
+      pf[f] = as_bf16x8(u32x4{w[4 * f + 0], w[4 * f + 1], w[4 * f + 2], w[4 * f + 3]});
+
+    // ---- O^T += V^T P^T over this half: P^T steps 4 hb .. 4 hb + 3 of the
+    // block; lane (n, h) holds dims 64 h + 16 dt + e of its row (V^T operand
+    // row dsel + 16 dt, stored at dvt_row(dsel) + 32 dt).  Fragment reads run
+    // two MFMAs ahead.
+    const uint8_t* vfr = vlane + slot * kBufBytes + 32 * 4 * hb;
+    auto vread = [&](int i) {
+      return *reinterpret_cast<const u32x4*>(vfr + 32 * (i >> 2) * kStr + 32 * (i & 3));
+    };
+    u32x4 vq[3];
+    vq[0] = vread(0);
+    vq[1] = vread(1);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      if (i + 2 < 16) vq[(i + 2) % 3] = vread(i + 2);
+      const int dt = i >> 2, st = i & 3;
+      oacc[dt] = mfma32x32x16(as_bf16x8(vq[i % 3]), pf[st], oacc[dt]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  f32x16 sA[2], sB[2];
   KVRegs R;
   kv_load(R, kseq, vseq, rstride, nvalid_of(0), tid);
   kv_store(R, lds, nvalid_of(0), tid);
+  {
+    const int b1 = min(1, nb - 1);
+    kv_load(R, kseq + static_cast<int64_t>(b1) * kBk * rstride, vseq + static_cast<int64_t>(b1) * kBk * rstride,
+            rstride, nvalid_of(b1), tid);
+  }
   __syncthreads();
+  scores_half(lds, 0, sA);
 
   for (int b = 0; b < nb; ++b) {
-    // Block b + 1 (the last block again at the end: its loads stay in
-    // bounds, and the copy lands in the buffer nobody reads any more).
-    const int bn = min(b + 1, nb - 1);
-    kv_load(R, kseq + static_cast<int64_t>(bn) * kBk * rstride,
-            vseq + static_cast<int64_t>(bn) * kBk * rstride, rstride, nvalid_of(bn), tid);
-
-    const uint8_t* buf = lds + (b & 1) * kBufBytes;
-    const int64_t key0 = static_cast<int64_t>(b) * kBk;
-    if (key0 <= tw_hi) {  // wave-uniform
-      // S^T = K_b Q^T: acc[mt] holds keys 32 mt + 8 (e / 4) + 4 h + (e % 4).
-      const uint8_t* kfr = buf + n * kStr + h * 16;
-      f32x16 acc[4];
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
-        acc[mt] = f32x16{};
-#pragma unroll
-        for (int ks = 0; ks < 8; ++ks)
-          acc[mt] = mfma32x32x16(as_bf16x8(*reinterpret_cast<const u32x4*>(kfr + 32 * mt * kStr + 32 * ks)),
-                                 as_bf16x8(qf[ks]), acc[mt]);
-      }
-      if (key0 + kBk - 1 > tw_lo) {  // some key of the block lies past some row's token
-        const int lim = static_cast<int>(t_row - key0) - 4 * h;
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt) {
-#pragma unroll
-          for (int el = 0; el < 16; ++el) {
-            const uint32_t hide = static_cast<uint32_t>((lim - (32 * mt + 8 * (el >> 2) + (el & 3))) >> 31);
-            acc[mt][el] = __uint_as_float((__float_as_uint(acc[mt][el]) & ~hide) | (0xFF800000u & hide));
-          }
-        }
-      }
-      // Running max in base-2 units (scale_log2 > 0).  Every row sees key 0,
-      // so m_run is finite from block 0 on and a fully hidden row of a later
-      // block gets alpha = 1 and p = 0.
-      float m0 = -__builtin_huge_valf(), m1 = -__builtin_huge_valf();
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
-#pragma unroll
-        for (int el = 0; el < 16; el += 4) {
-          m0 = fmaxf(m0, fmaxf(acc[mt][el], acc[mt][el + 1]));
-          m1 = fmaxf(m1, fmaxf(acc[mt][el + 2], acc[mt][el + 3]));
-        }
-      }
-      const float m_new = fmaxf(m_run, halves_max(fmaxf(m0, m1)) * scale_log2);
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-      m_run = m_new;
-      bf16x8 pf[8];
-      float s0 = 0.f, s1 = 0.f;
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
-#pragma unroll
-        for (int e2 = 0; e2 < 2; ++e2) {
-          uint32_t w[4];
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const float pa = __builtin_amdgcn_exp2f(__builtin_fmaf(acc[mt][8 * e2 + 2 * j], scale_log2, -m_new));
-            const float pb = __builtin_amdgcn_exp2f(__builtin_fmaf(acc[mt][8 * e2 + 2 * j + 1], scale_log2, -m_new));
-            w[j] = pack_bf16x2(pa, pb);
-            s0 += pa;
-            s1 += pb;
-          }
-          pf[2 * mt + e2] = as_bf16x8(u32x4{w[0], w[1], w[2], w[3]});
-        }
-      }
-      l_run = l_run * alpha + (s0 + s1);
-      // O^T = alpha O^T + V^T P^T; lane (n, h) holds dims 64 h + 16 dt + e of
-      // its row (V^T operand row dsel + 16 dt, stored at dvt_row(dsel) + 32 dt).
-      const uint8_t* vfr = buf + kVtOff + dvt_row(dsel) * kStr + h * 16;
-#pragma unroll
-      for (int dt = 0; dt < 4; ++dt) {
-        f32x16 a = oacc[dt] * alpha;
-#pragma unroll
-        for (int st = 0; st < 8; ++st)
-          a = mfma32x32x16(as_bf16x8(*reinterpret_cast<const u32x4*>(vfr + 32 * dt * kStr + 32 * st)), pf[st], a);
-        oacc[dt] = a;
-      }
-    }
-
-    // The other buffer was last read in block b - 1, before the previous
-    // barrier.
-    kv_store(R, lds + ((b + 1) & 1) * kBufBytes, nvalid_of(bn), tid);
+    // Past the last block the copies repeat block nb - 1: the loads stay in
+    // bounds and the look-ahead scores from it are never used.
+    const int slot = b & 1;
+    uint8_t* cur = lds + slot * kBufBytes;
+    uint8_t* nxt = lds + (slot ^ 1) * kBufBytes;
+    const int b1 = min(b + 1, nb - 1), b2 = min(b + 2, nb - 1);
+    kv_store(R, nxt, nvalid_of(b1), tid);
+    step(sA, sB, slot, b, 0, cur, 1);
+    kv_load(R, kseq + static_cast<int64_t>(b2) * kBk * rstride, vseq + static_cast<int64_t>(b2) * kBk * rstride,
+            rstride, nvalid_of(b2), tid);
+    __syncthreads();
+    step(sB, sA, slot, b, 1, nxt, 0);
     __syncthreads();
   }
 

@@ -54,3 +54,15 @@ def test_exact_counts_small():
     bi = np.array([[[0, -1], [0, -1], [0, 1], [1, 2]]], np.int32)   # rows 4..7
     vis = acc.visible_keys(bi, 4, 10, 4)
     assert vis.tolist() == [[4, 4, 4 + 3, 4 + 0]]  # row 6 sees 4..6 of block 1; row 7 none of block 2
+
+
+def test_dense_flops_closed_form_and_chunks():
+    """Dense causal FLOPs: 4 d_h H_q N (N + 1) / 2; chunks add up; the per-token
+    GQA figure the pages use (N / 2 keys per query) matches to O(1 / N)."""
+    N, H_q, d_h = 131072, 64, 128
+    full = acc.dense_flops(0, N, H_q, d_h)
+    assert full == 4.0 * d_h * H_q * N * (N + 1) / 2
+    parts = sum(acc.dense_flops(b, 32768, H_q, d_h) for b in range(0, N, 32768))
+    assert parts == full
+    assert abs(full / (N * acc.gqa_flops_per_token(N, H_q, d_h)) - 1.0) < 2.0 / N
+    assert acc.dense_flops(0, 1, 1, 1, batch=3) == 12.0
