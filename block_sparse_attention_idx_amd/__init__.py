@@ -27,7 +27,7 @@ EXPORTS = (
     "msa_abi_version", "msa_status_string", "msa_last_hip_error", "msa_index_topk",
     "msa_invert_workspace_size", "msa_invert_blocks", "msa_invert_status",
     "msa_sparse_attn_fwd", "msa_combine", "msa_workspace_size", "msa_forward",
-    "msa_dense_attn_fwd",
+    "msa_dense_attn_fwd", "msa_decode_workspace_size", "msa_decode",
 )
 
 
@@ -93,6 +93,8 @@ def lib():
             "msa_workspace_size": ([D, O, ctypes.POINTER(SZ)], ctypes.c_int),
             "msa_forward": ([D, O, P, P, P, P, P, P, P, P, P, SZ, P], ctypes.c_int),
             "msa_dense_attn_fwd": ([D, O, P, P, P, I64, I64, P, P, P], ctypes.c_int),
+            "msa_decode_workspace_size": ([D, O, ctypes.POINTER(SZ)], ctypes.c_int),
+            "msa_decode": ([D, O, P, P, P, P, P, P, P, P, P, SZ, P], ctypes.c_int),
         }
         for name, (args, res) in sig.items():
             f = getattr(L, name)
@@ -263,6 +265,34 @@ def msa_dense_attn_fwd(dims: msa_dims, opts: msa_opts, q, k, v, q_begin: int = 0
                                         q_begin, q_count, _p(o), _p(lse), _stream(q)),
                "msa_dense_attn_fwd")
     return o, lse
+
+
+def msa_decode_workspace_size(dims: msa_dims, opts: msa_opts) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().msa_decode_workspace_size(ctypes.byref(dims), ctypes.byref(opts), ctypes.byref(n)),
+           "msa_decode_workspace_size")
+    return n.value
+
+
+def msa_decode(dims: msa_dims, opts: msa_opts, q, q_idx, k, v, k_idx, o=None, lse=None,
+               block_idx_out=None, workspace=None, want_lse: bool = False):
+    """One decode step (the token at position N - 1 of each sequence).
+    q [batch, H_q, d_h], q_idx [batch, H_kv, d_idx]; caches as for msa_forward.
+    Returns (o bf16 [batch, H_q, d_h], lse fp32 [batch, H_q] or None, block_idx_out)."""
+    import torch
+    if o is None:
+        o = _empty((dims.batch, dims.H_q, dims.d_h), torch.bfloat16, q)
+    if lse is None and want_lse:
+        lse = _empty((dims.batch, dims.H_q), torch.float32, q)
+    nbytes = msa_decode_workspace_size(dims, opts)
+    if workspace is None:
+        workspace = _empty((nbytes,), torch.uint8, q)
+    with _dev(q):
+        _check(lib().msa_decode(ctypes.byref(dims), ctypes.byref(opts), _p(q), _p(q_idx), _p(k), _p(v),
+                                _p(k_idx), _p(o), _p(lse), _p(block_idx_out), _p(workspace),
+                                workspace.numel() * workspace.element_size(), _stream(q)),
+               "msa_decode")
+    return o, lse, block_idx_out
 
 
 def default_softmax_scale(d_h: int) -> float:

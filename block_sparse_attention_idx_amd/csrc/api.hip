@@ -247,6 +247,74 @@ int msa_dense_attn_fwd(const msa_dims* dims, const msa_opts* opts, const void* q
   return e == hipSuccess ? MSA_OK : hip_fail(e);
 }
 
+namespace {
+
+struct DecodeLayout {
+  size_t off_scores, off_bi, off_opart, off_lpart, total;
+};
+
+DecodeLayout decode_layout(const msa_dims* d) {
+  DecodeLayout L{};
+  const size_t seqs = static_cast<size_t>(d->batch) * d->H_kv;
+  const size_t B = static_cast<size_t>((d->N + d->B_k - 1) / d->B_k);
+  size_t off = 0;
+  L.off_scores = off;
+  off += align256(seqs * B * 4);
+  L.off_bi = off;
+  off += align256(seqs * d->k * 4);
+  L.off_opart = off;
+  off += align256(seqs * d->k * d->G * d->d_h * 2);
+  L.off_lpart = off;
+  off += align256(seqs * d->k * d->G * 4);
+  L.total = off;
+  return L;
+}
+
+int check_decode(const msa_dims* d, const msa_opts* o) {
+  int st = check_dims(d);
+  if (st) return st;
+  if (!o) return MSA_ERR_NULL;
+  if (o->reserved != 0 || !isfinite(o->softmax_scale)) return MSA_ERR_SHAPE;
+  if (o->qkv_dtype != MSA_DTYPE_BF16) return MSA_ERR_UNSUPPORTED;
+  if (d->H_kv > 32 || d->batch > 65535) return MSA_ERR_UNSUPPORTED;
+  return MSA_OK;
+}
+
+}  // namespace
+
+int msa_decode_workspace_size(const msa_dims* dims, const msa_opts* opts, size_t* bytes) {
+  int st = check_decode(dims, opts);
+  if (st) return st;
+  if (!bytes) return MSA_ERR_NULL;
+  *bytes = decode_layout(dims).total;
+  return MSA_OK;
+}
+
+int msa_decode(const msa_dims* dims, const msa_opts* opts, const void* q, const void* q_idx,
+               const void* k, const void* v, const void* k_idx, void* o, float* lse,
+               int32_t* block_idx_out, void* workspace, size_t ws_bytes, void* stream) {
+  int st = check_decode(dims, opts);
+  if (st) return st;
+  if (!q || !q_idx || !k || !v || !k_idx || !o || !workspace) return MSA_ERR_NULL;
+  if (misaligned(q) || misaligned(q_idx) || misaligned(k) || misaligned(v) || misaligned(k_idx) ||
+      misaligned(o) || (lse && misaligned(lse)) || (block_idx_out && misaligned(block_idx_out)) ||
+      (reinterpret_cast<uintptr_t>(workspace) & 255u))
+    return MSA_ERR_ALIGN;
+  const DecodeLayout L = decode_layout(dims);
+  if (ws_bytes < L.total) return MSA_ERR_WORKSPACE;
+  float sl2, osc;
+  attn_scales(dims, opts, &sl2, &osc);
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  int32_t* bi = block_idx_out ? block_idx_out : reinterpret_cast<int32_t*>(ws + L.off_bi);
+  hipError_t e = msa::launch_decode(
+      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(q_idx), static_cast<const uint16_t*>(k),
+      static_cast<const uint16_t*>(v), static_cast<const uint16_t*>(k_idx), dims->batch, dims->N, dims->H_kv,
+      dims->G, dims->d_idx, dims->k, sl2, reinterpret_cast<float*>(ws + L.off_scores), bi,
+      reinterpret_cast<uint16_t*>(ws + L.off_opart), reinterpret_cast<float*>(ws + L.off_lpart),
+      static_cast<uint16_t*>(o), lse, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MSA_OK : hip_fail(e);
+}
+
 int msa_workspace_size(const msa_dims* dims, const msa_opts* opts, size_t* bytes) {
   int st = check_dims(dims);
   if (st) return st;

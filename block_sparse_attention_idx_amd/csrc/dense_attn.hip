@@ -13,9 +13,8 @@
 //    tokens times the G heads of one group (a token's G heads are contiguous
 //    in Q and O), one 32-row MFMA column tile per wave.  Q stays in VGPRs.
 //  * The group's key blocks 0 .. (last token) / 128 stream through two LDS
-//    buffers (K row-major, V transposed, rows padded to 272 B as in the
-//    sparse kernel): block b + 1 is loaded into registers while block b is
-//    computed and written to the other buffer after it, one barrier per block.
+//    buffers (the shared tile layout: K row-major, V transposed, rows padded
+//    to 272 B), loaded into registers one step ahead.
 //  * Per block and wave: S^T = K_b Q^T (32 v_mfma_f32_32x32x16_bf16, keys on
 //    the row dimension, so each lane holds 64 keys of its own row), the
 //    running max and sum update in base 2, and O^T += V^T P^T (32 MFMAs) with
@@ -32,88 +31,18 @@
 //    workgroups of one XCD (dealt round-robin) share a K/V head in its L2.
 //  * The output leaves through an LDS tile, row-contiguous, 1 KB per store
 //    instruction.
+#include "attn_tile.h"
 #include "msa_internal.h"
 
 namespace msa {
 namespace {
 
+using namespace tile;
+
 constexpr int kDWaves = 8;
 constexpr int kDThreads = 64 * kDWaves;
 constexpr int kDRows = 32 * kDWaves;             // (token, head) rows per workgroup
-constexpr int kStr = 272;                        // padded LDS row of K, V^T and the output tile
-constexpr int kVtOff = kBk * kStr;               // V^T after K in a buffer
-constexpr int kBufBytes = kVtOff + kDh * kStr;   // one block: 69,632 B
 constexpr float kLazy = 8.f;                     // log2 of the largest unnormalised probability
-
-// V^T row d is stored at position 2 (d mod 64) + d / 64, and bits 0 and 1 of
-// the 8-byte key-chunk index kc (four keys) are swapped, so that the eight
-// keys one lane feeds to a P^T step lie in one 16-byte chunk and the 32 rows
-// one operand read touches are consecutive.
-__device__ __forceinline__ int dvt_row(int d) { return ((d & 63) << 1) | (d >> 6); }
-__device__ __forceinline__ int dvt_off(int d, int kc) {
-  const int kcp = (kc & ~3) | ((kc & 1) << 1) | ((kc & 2) >> 1);
-  return dvt_row(d) * kStr + kcp * 8;
-}
-
-__device__ __forceinline__ uint32_t bf16_of(const u32x4& w, int dd) {
-  const uint32_t x = w[dd >> 1];
-  return (dd & 1) ? (x >> 16) : (x & 0xFFFFu);
-}
-
-// Lanes n and n + 32 hold the two halves of one row; v_permlane32_swap
-// exchanges the half-waves.
-__device__ __forceinline__ float halves_max(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float halves_sum(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-
-// One K/V block of one head in flight through registers: thread t holds
-// 16-byte chunks t % 16 of keys t / 16 + 32 p (K) and the 8 dims 8 (t / 32) ..
-// + 7 of keys 4 (t % 32) .. + 3 (V, transposed when written).
-struct KVRegs {
-  u32x4 k[4];
-  u32x4 v[4];
-};
-
-__device__ __forceinline__ void kv_load(KVRegs& R, const uint8_t* __restrict__ kb,
-                                        const uint8_t* __restrict__ vb, int64_t rstride, int nvalid,
-                                        int tid) {
-#pragma unroll
-  for (int p = 0; p < 4; ++p) {
-    const int key = (tid >> 4) + 32 * p, c = tid & 15;
-    R.k[p] = *reinterpret_cast<const u32x4*>(kb + min(key, nvalid - 1) * rstride + c * 16);
-  }
-  const int kc = tid & 31, dg = tid >> 5;
-#pragma unroll
-  for (int j = 0; j < 4; ++j)
-    R.v[j] = *reinterpret_cast<const u32x4*>(vb + min(4 * kc + j, nvalid - 1) * rstride + dg * 16);
-}
-
-// Keys past the end of the sequence become zeros (they are also masked).
-__device__ __forceinline__ void kv_store(const KVRegs& R, uint8_t* buf, int nvalid, int tid) {
-#pragma unroll
-  for (int p = 0; p < 4; ++p) {
-    const int key = (tid >> 4) + 32 * p, c = tid & 15;
-    const u32x4 w = key < nvalid ? R.k[p] : u32x4{0u, 0u, 0u, 0u};
-    *reinterpret_cast<u32x4*>(buf + key * kStr + c * 16) = w;
-  }
-  const int kc = tid & 31, dg = tid >> 5;
-  u32x4 row[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) row[j] = 4 * kc + j < nvalid ? R.v[j] : u32x4{0u, 0u, 0u, 0u};
-#pragma unroll
-  for (int dd = 0; dd < 8; ++dd) {
-    const int d = 8 * dg + dd;
-    const u32x2 w = {bf16_of(row[0], dd) | (bf16_of(row[1], dd) << 16),
-                     bf16_of(row[2], dd) | (bf16_of(row[3], dd) << 16)};
-    *reinterpret_cast<u32x2*>(buf + kVtOff + dvt_off(d, kc)) = w;
-  }
-}
-
 template <int G>
 __global__ __launch_bounds__(kDThreads, 1) void dense_attn_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,

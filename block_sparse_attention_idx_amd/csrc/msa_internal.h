@@ -157,4 +157,15 @@ hipError_t launch_dense_attn(const uint16_t* q, const uint16_t* k, const uint16_
                              int64_t N, int H_kv, int G, int64_t q_begin, int64_t q_count,
                              float scale_log2, uint16_t* o, float* lse, hipStream_t stream);
 
+// Decode: one query (position N - 1) per sequence against cached K, V, K^idx.
+// q [batch][H_q][d_h], q_idx [batch][H_kv][d_idx], caches as for the prefill;
+// scores [batch][H_kv][ceil(N / B_k)] fp32, block_idx [batch][H_kv][k],
+// o_part [batch][H_kv][k][G][d_h], lse_part [batch][H_kv][k][G] are scratch
+// (block_idx is also an output); o [batch][H_q][d_h], lse [batch][H_q] or null.
+hipError_t launch_decode(const uint16_t* q, const uint16_t* q_idx, const uint16_t* k, const uint16_t* v,
+                         const uint16_t* k_idx, int batch, int64_t N, int H_kv, int G, int d_idx,
+                         int kslots, float scale_log2, float* scores, int32_t* block_idx,
+                         uint16_t* o_part, float* lse_part, uint16_t* o, float* lse,
+                         hipStream_t stream);
+
 }  // namespace msa

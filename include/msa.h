@@ -230,6 +230,34 @@ int msa_dense_attn_fwd(const msa_dims *dims, const msa_opts *opts, const void *q
                        const void *k, const void *v, int64_t q_begin, int64_t q_count,
                        void *o, float *lse, void *stream);
 
+/*
+ * msa_decode_workspace_size / msa_decode -- one decode step: the last token
+ * (position N - 1) of each of `batch` sequences attends to the N cached
+ * tokens.  Index branch, top-k with the forced local block, and the main
+ * branch over the selected blocks, exactly as msa_forward computes row N - 1
+ * ("MiniMax Sparse Attention (MSA)", Deep Dive > Index Branch Architecture,
+ * Exp-Free TopK Kernel, KV-Outer Sparse Attention step 6 for the merge;
+ * "MiniMax Sparse Attention", sec. 2.1-2.2; the decode-shaped query-outer
+ * tile: "Optimizing MiniMax M3 Sparse Attention on NVIDIA Blackwell", sec. 1).
+ *
+ *   q              bf16 [batch][H_q][d_h]      the new token's queries
+ *   q_idx          bf16 [batch][H_kv][d_idx]   its index queries
+ *   k, v           bf16 [batch][N][H_kv][d_h]  the cache, token N - 1 included
+ *   k_idx          bf16 [batch][N][d_idx]      the index-key cache
+ *   o              bf16 [batch][H_q][d_h] output
+ *   lse            fp32 [batch][H_q] output (may be NULL): natural-log LSE
+ *   block_idx_out  int32 [batch][H_kv][k] (may be NULL): the selection, as a
+ *                  row of msa_index_topk's output
+ *   workspace      device memory of msa_decode_workspace_size bytes,
+ *                  256-byte aligned: block scores, partial outputs
+ * bf16 Q/K/V only (MSA_ERR_UNSUPPORTED for fp8); H_kv <= 32, batch <= 65535;
+ * opts->q_chunk is ignored.
+ */
+int msa_decode_workspace_size(const msa_dims *dims, const msa_opts *opts, size_t *bytes);
+int msa_decode(const msa_dims *dims, const msa_opts *opts, const void *q, const void *q_idx,
+               const void *k, const void *v, const void *k_idx, void *o, float *lse,
+               int32_t *block_idx_out, void *workspace, size_t ws_bytes, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -278,7 +278,7 @@ def _dlib():
         L = ctypes.CDLL(_LIB)
         P = ctypes.c_void_p
         L.synth_fill.argtypes = [P, ctypes.c_int, ctypes.c_int64, ctypes.c_uint64, ctypes.c_int64,
-                                 P, P, ctypes.c_int, P, ctypes.c_int64, ctypes.c_int, P]
+                                 P, P, ctypes.c_int, P, ctypes.c_int64, ctypes.c_int64, ctypes.c_int, P]
         L.synth_fill.restype = ctypes.c_int
         _lib = L
     return _lib
@@ -317,7 +317,7 @@ def device_tensor(w: Workload, which: str, device="cuda"):
         stream_key(w.seed, tid), 0, ctypes.c_void_p(table.data_ptr()),
         ctypes.c_void_p(vec_t.data_ptr() if vec_t is not None else 0), dim,
         ctypes.c_void_p(mask_t.data_ptr() if mask_t is not None else 0),
-        w.B_k * dim, mode, ctypes.c_void_p(stream))
+        w.B_k * dim, w.N * dim, mode, ctypes.c_void_p(stream))
     if rc != 0:
         raise RuntimeError(f"synth_fill failed with HIP error {rc}")
     # keep table / vector alive until the fill has run

@@ -25,10 +25,12 @@ __device__ __forceinline__ uint16_t add_round_bf16(uint16_t x, float v) {
 }
 
 // mode 0: plain; 1: add vec[col] to every row; 2: add vec[col] to rows whose
-// block (e / rows_per_block_elems) is flagged in block_mask.
+// block within their sequence ((e mod seq_elems) / block_elems) is flagged in
+// block_mask.
 __global__ void fill_kernel(void* out, int elem_bytes, int64_t n, uint64_t key, int64_t offset,
                             const void* table, const float* vec, int dim,
-                            const uint8_t* block_mask, int64_t block_elems, int mode) {
+                            const uint8_t* block_mask, int64_t block_elems, int64_t seq_elems,
+                            int mode) {
   int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
   for (int64_t e = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; e < n; e += stride) {
     uint64_t h = splitmix_at(key, static_cast<uint64_t>(e + offset));
@@ -37,7 +39,7 @@ __global__ void fill_kernel(void* out, int elem_bytes, int64_t n, uint64_t key, 
       static_cast<uint8_t*>(out)[e] = static_cast<const uint8_t*>(table)[u];
     } else {
       uint16_t x = static_cast<const uint16_t*>(table)[u];
-      if (mode == 1 || (mode == 2 && block_mask[(e + offset) / block_elems]))
+      if (mode == 1 || (mode == 2 && block_mask[((e + offset) % seq_elems) / block_elems]))
         x = add_round_bf16(x, vec[(e + offset) % dim]);
       static_cast<uint16_t*>(out)[e] = x;
     }
@@ -46,16 +48,19 @@ __global__ void fill_kernel(void* out, int elem_bytes, int64_t n, uint64_t key, 
 
 }  // namespace
 
+// seq_elems: elements of one sequence (N rows); block_mask holds
+// ceil(seq_elems / block_elems) flags.
 extern "C" int synth_fill(void* out, int elem_bytes, int64_t n, uint64_t key, int64_t offset,
                           const void* table, const float* vec, int dim, const uint8_t* block_mask,
-                          int64_t block_elems, int mode, hipStream_t stream) {
+                          int64_t block_elems, int64_t seq_elems, int mode, hipStream_t stream) {
   if (n <= 0) return 0;
   if (!out || !table || (elem_bytes != 1 && elem_bytes != 2)) return -1;
   if (mode != 0 && (!vec || dim <= 0 || elem_bytes != 2)) return -1;
-  if (mode == 2 && (!block_mask || block_elems <= 0)) return -1;
+  if (mode == 2 && (!block_mask || block_elems <= 0 || seq_elems <= 0)) return -1;
   int64_t blocks = (n + 255) / 256;
   if (blocks > 65536) blocks = 65536;
   hipLaunchKernelGGL(fill_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream, out,
-                     elem_bytes, n, key, offset, table, vec, dim, block_mask, block_elems, mode);
+                     elem_bytes, n, key, offset, table, vec, dim, block_mask, block_elems, seq_elems,
+                     mode);
   return static_cast<int>(hipGetLastError());
 }

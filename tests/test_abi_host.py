@@ -136,6 +136,27 @@ def test_dense_attn_validation(L):
     assert L.msa_dense_attn_fwd(None, ctypes.byref(o), FAKE, FAKE, FAKE, 0, 16, FAKE, None, None) == 1
 
 
+def test_decode_validation(L):
+    o = msa.make_opts()
+    n = ctypes.c_size_t(0)
+    d = dims()
+    assert L.msa_decode_workspace_size(ctypes.byref(d), ctypes.byref(o), ctypes.byref(n)) == 0
+    ws = n.value
+    # block scores, selection, partial outputs and their lse
+    B = (2048 + 127) // 128
+    assert ws >= 2 * B * 4 + 2 * 4 * 4 + 2 * 4 * 4 * 128 * 2 + 2 * 4 * 4 * 4
+    call = lambda d, o, ws_bytes=ws, q=FAKE, out=FAKE, wsp=FAKE: L.msa_decode(
+        ctypes.byref(d), ctypes.byref(o), q, FAKE, FAKE, FAKE, FAKE, out, None, None, wsp, ws_bytes, None)
+    assert call(d, o, ws - 1) == 5
+    assert call(d, msa.make_opts(dtype="fp8"), ws) == 3
+    assert call(dims(H_q=66, H_kv=33), o) == 3
+    assert call(dims(k=0), o) == 2
+    assert call(d, o, q=None) == 1
+    assert call(d, o, out=ODD) == 4
+    assert call(d, o, wsp=ctypes.c_void_p(0x10010)) == 4     # workspace needs 256-byte alignment
+    assert L.msa_decode_workspace_size(ctypes.byref(d), ctypes.byref(o), None) == 1
+
+
 def test_binding_raises_when_library_missing(monkeypatch):
     monkeypatch.setattr(msa, "_lib", None)
     monkeypatch.setattr(msa, "LIB_PATH", "/nonexistent/libmsa.so")

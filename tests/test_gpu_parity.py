@@ -33,14 +33,16 @@ def _gpu_cleanup():
 # --------------------------------------------------------------------------- inputs
 
 def test_device_generator_matches_host():
-    for w in (TINY.with_(N=1000, plant=4), TINY.with_(N=640, dtype="fp8")):
+    for w in (TINY.with_(N=1000, plant=4), TINY.with_(N=640, dtype="fp8"),
+              TINY.with_(N=768, plant=3, batch=3)):             # planting per sequence
         log(f"generator {w.name} N={w.N} dtype={w.dtype} plant={w.plant}")
         t = device_inputs(w, DEV)
         rows = np.array([0, 5, 127, 128, 300, w.N - 1])
+        rows = np.concatenate([rows + b * w.N for b in range(w.batch)])
         for x in ("q", "k", "v", "q_idx", "k_idx"):
             dv = t[x]
             dv = dv.view(torch.int16) if dv.dtype == torch.bfloat16 else dv
-            got = dv.cpu().numpy().reshape(w.N, -1)[rows]
+            got = dv.cpu().numpy().reshape(w.batch * w.N, -1)[rows]
             want = synth.host_rows(w, x, rows).reshape(len(rows), -1)
             assert np.array_equal(got.view(want.dtype), want), x
 
@@ -376,6 +378,89 @@ def test_dense_attention_full_size_sampled():
     assert mx <= 2e-2 and mn <= 2e-3
     lmx, _ = err_stats(glse, L)
     assert lmx <= 1e-3
+
+
+# --------------------------------------------------------------------------- decode
+
+DECODE_CASES = [
+    TINY,                                          # N = 2048, k = 4, d_idx = 64, G = 4
+    TINY.with_(N=1),                               # no earlier block
+    TINY.with_(N=128),                             # exactly one block
+    TINY.with_(N=129, k=2),                        # local block of one token
+    TINY.with_(N=1000, k=16),                      # k - 1 >= L: all blocks
+    TINY.with_(N=3000, k=1, batch=2),              # local block only
+    TINY.with_(N=2500, k=5, H_q=64, H_kv=4, d_idx=128, batch=3),
+    TINY.with_(N=4000, k=32, H_q=2, H_kv=2, plant=4),   # G = 1, planted hot blocks
+    TINY.with_(N=1500, k=7, H_q=32, H_kv=4, batch=2),   # G = 8
+]
+
+
+def _decode_inputs(w, t):
+    """The last token's Q and Q^idx of every sequence, contiguous."""
+    return t["q"][:, w.N - 1].contiguous(), t["q_idx"][:, w.N - 1].contiguous()
+
+
+def _check_decode(w, t, out, lse, bi, tol_max=2e-2):
+    last = np.array([w.N - 1])
+    for b in range(w.batch):
+        ob, marg, M = oracle_index_rows(w, last, bat=b)
+        gsel = bi[b][:, None, :]                                   # [H_kv, 1, k]
+        st = check_selection(gsel, ob, marg, M, w.k, what=f"decode b{b}")
+        O, L = compact_attention_rows(w, last, gsel, bat=b)
+        mx, mn = err_stats(out[b], O[0])
+        log(f"  batch {b}: {st}; output max abs {mx:.3g} mean abs {mn:.3g}")
+        assert mx <= tol_max and mn <= 2e-3
+        lmx, _ = err_stats(lse[b], L[0])
+        assert lmx <= 1e-3
+
+
+@pytest.mark.parametrize("w", DECODE_CASES, ids=lambda w: f"N{w.N}_k{w.k}_G{w.G}_d{w.d_idx}_b{w.batch}")
+def test_decode_parity(w):
+    log(f"decode N={w.N} k={w.k} H_q={w.H_q} H_kv={w.H_kv} d_idx={w.d_idx} batch={w.batch}")
+    t = device_inputs(w, DEV)
+    q1, qi1 = _decode_inputs(w, t)
+    bi = torch.empty((w.batch, w.H_kv, w.k), dtype=torch.int32, device=DEV)
+    out, lse, _ = msa.msa_decode(dims_of(w), msa.make_opts(), q1, qi1, t["k"], t["v"], t["k_idx"],
+                                 block_idx_out=bi, want_lse=True)
+    torch.cuda.synchronize()
+    _check_decode(w, t, out.float().cpu().numpy(), lse.cpu().numpy(), bi.cpu().numpy())
+
+
+def test_decode_matches_forward_last_row():
+    """Decode of token N - 1 equals the whole forward's row N - 1 (same
+    selection; outputs within the bf16 rounding of two different kernels)."""
+    w = TINY.with_(N=1792, k=5, batch=2)
+    t = device_inputs(w, DEV)
+    d = dims_of(w)
+    bi_f = torch.empty((w.batch, w.H_kv, w.N, w.k), dtype=torch.int32, device=DEV)
+    of, lf, _ = msa.msa_forward(d, msa.make_opts(), t["q"], t["k"], t["v"], t["q_idx"], t["k_idx"],
+                                block_idx_out=bi_f, want_lse=True)
+    q1, qi1 = _decode_inputs(w, t)
+    bi_d = torch.empty((w.batch, w.H_kv, w.k), dtype=torch.int32, device=DEV)
+    od, ld, _ = msa.msa_decode(d, msa.make_opts(), q1, qi1, t["k"], t["v"], t["k_idx"],
+                               block_idx_out=bi_d, want_lse=True)
+    torch.cuda.synchronize()
+    assert torch.equal(bi_d, bi_f[:, :, w.N - 1])
+    mx, _ = err_stats(od.float().cpu().numpy(), of[:, w.N - 1].float().cpu().numpy())
+    assert mx <= 1e-2
+    lmx, _ = err_stats(ld.cpu().numpy(), lf[:, w.N - 1].cpu().numpy())
+    assert lmx <= 1e-4
+
+
+@pytest.mark.parametrize("w", [synth.P128K_HOT.with_(batch=4), synth.P1M],
+                         ids=lambda w: f"{w.name}_b{w.batch}")
+def test_decode_full_size(w):
+    log(f"decode full-size {w.name} batch={w.batch}: generating inputs")
+    t = device_inputs(w, DEV)
+    q1, qi1 = _decode_inputs(w, t)
+    bi = torch.empty((w.batch, w.H_kv, w.k), dtype=torch.int32, device=DEV)
+    out, lse, _ = msa.msa_decode(dims_of(w), msa.make_opts(), q1, qi1, t["k"], t["v"], t["k_idx"],
+                                 block_idx_out=bi, want_lse=True)
+    torch.cuda.synchronize()
+    out, lse, bi = out.float().cpu().numpy(), lse.cpu().numpy(), bi.cpu().numpy()
+    del t
+    torch.cuda.empty_cache()
+    _check_decode(w, None, out, lse, bi)
 
 
 # --------------------------------------------------------------------------- full-size workloads
