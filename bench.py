@@ -11,8 +11,9 @@ Prints one JSON line: whole-job tokens/s, the sparse-counted TFLOP/s, per-kernel
 times measured with HIP events on the launch stream, each kernel's roofline
 fraction against the published peaks and against peaks measured on this GPU by
 a probe for the same access patterns, the dense causal GQA kernel on the same
-Q, K, V (the baseline MSA's speedup is quoted against), and the CPU oracle
-timed on a bounded sample of the same workload.
+Q, K, V (the baseline MSA's speedup is quoted against), one decode step over 8
+caches of the workload's shape, and the CPU oracle timed on a bounded sample of
+the same workload.
 """
 from __future__ import annotations
 
@@ -114,6 +115,8 @@ def main():
                     help="skip the measured-peaks probe (HBM patterns and MFMA throughput)")
     ap.add_argument("--no-dense", action="store_true",
                     help="skip the dense causal GQA baseline on the same Q, K, V")
+    ap.add_argument("--no-decode", action="store_true",
+                    help="skip the decode step (last token of 8 sequences of the workload's length)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="first run one plain device-to-device copy of this many MiB (a kernel "
                          "of known traffic, to calibrate hardware byte counters)")
@@ -222,6 +225,46 @@ def main():
         log(f"dense baseline: {dms:.2f} ms, {dense['achieved']:.0f} TFLOP/s; "
             f"msa_forward is {dense['msa_speedup']:.2f}x faster")
 
+    # ---- decode: one new token per sequence against caches of the workload's
+    # shape (8 sequences up to 128K tokens, else 1), inputs resident in HBM
+    decode = None
+    if not args.no_decode and w.dtype == "bf16":
+        nb_dec = 8 if w.N <= 131072 else 1
+        wd = w.with_(batch=nb_dec, q_chunk=0)
+        log(f"decode: {nb_dec} sequences of {wd.N} tokens: generating caches")
+        last = np.arange(nb_dec) * wd.N + (wd.N - 1)
+        qd = torch.from_numpy(synth.host_rows(wd, "q", last).view(np.int16)).to(dev).view(torch.bfloat16)
+        qid = torch.from_numpy(synth.host_rows(wd, "q_idx", last).view(np.int16)).to(dev).view(torch.bfloat16)
+        kd, vd, kid = (synth.device_tensor(wd, x, dev) for x in ("k", "v", "k_idx"))
+        dd = msa.make_dims(wd.batch, wd.N, wd.H_q, wd.H_kv, wd.d_h, wd.d_idx, wd.B_k, wd.k)
+        od = msa.make_opts("bf16")
+        bid = torch.empty((wd.batch, wd.H_kv, wd.k), dtype=torch.int32, device=dev)
+        wsd = torch.empty((msa.msa_decode_workspace_size(dd, od),), dtype=torch.uint8, device=dev)
+        outd = torch.empty((wd.batch, wd.H_q, wd.d_h), dtype=torch.bfloat16, device=dev)
+        dargs = (dd, od, qd, qid, kd, vd, kid)
+        for _ in range(3):
+            msa.msa_decode(*dargs, o=outd, block_idx_out=bid, workspace=wsd)
+        torch.cuda.synchronize()
+        reps = 50
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            msa.msa_decode(*dargs, o=outd, block_idx_out=bid, workspace=wsd)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        dec_ms = e0.elapsed_time(e1) / reps
+        sel_d = bid.cpu().numpy()
+        valid_d = int((sel_d >= 0).sum())
+        L_d = (wd.N - 1) // wd.B_k
+        b_dec = acc.decode_bytes(wd.batch, wd.N, wd.H_q, wd.H_kv, wd.d_h, wd.d_idx, wd.B_k, wd.k, valid_d)
+        decode = {"batch": wd.batch, "context": wd.N, "ms": dec_ms, "tokens_s": wd.batch / (dec_ms * 1e-3),
+                  "bound": "hbm", "bytes": b_dec, "achieved": b_dec / dec_ms / 1e6,
+                  "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": b_dec / dec_ms / 1e6 / PEAK_HBM_GBS,
+                  "index_scan_bytes": wd.batch * L_d * wd.B_k * wd.d_idx * 2}
+        log(f"decode: {dec_ms * 1e3:.1f} us per step, {decode['achieved']:.0f} GB/s algorithmic")
+        del qd, qid, kd, vd, kid, wsd, outd, bid
+        torch.cuda.empty_cache()
+
     # ---- work accounting from the selection actually made
     sel = bi.cpu().numpy().reshape(w.batch * w.H_kv, w.N, w.k)
     f_idx = acc.index_flops(0, w.N, w.H_kv, w.d_idx, w.B_k, batch=w.batch)
@@ -279,6 +322,10 @@ def main():
                 v["measured_peak"] = peaks[key]
                 v["measured_peak_kind"] = key
                 v["frac_measured"] = v["achieved"] / peaks[key]
+        if decode and peaks.get("hbm_seq_read_GBs", 0) > 0:
+            decode["measured_peak"] = peaks["hbm_seq_read_GBs"]
+            decode["measured_peak_kind"] = "hbm_seq_read_GBs"
+            decode["frac_measured"] = decode["achieved"] / peaks["hbm_seq_read_GBs"]
         if dense and peaks.get("mfma_bf16_TFLOPs", 0) > 0:
             dense["measured_peak"] = peaks["mfma_bf16_TFLOPs"]
             dense["measured_peak_kind"] = "mfma_bf16_TFLOPs"
@@ -326,7 +373,7 @@ def main():
                    "d_h": w.d_h, "d_idx": w.d_idx, "B_k": w.B_k, "k": w.k,
                    "q_chunk": w.q_chunk, "hot_blocks": w.plant},
         "sparse_tflops": tflops, "index_flops": f_idx, "main_flops": f_main,
-        "roofline": roofline, "kernels": kernels, "dense_baseline": dense,
+        "roofline": roofline, "kernels": kernels, "dense_baseline": dense, "decode": decode,
         "measured_peaks": peaks, "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

@@ -102,6 +102,23 @@ def dense_flops(q_begin: int, q_count: int, H_q: int, d_h: int, batch: int = 1) 
     return float(batch) * 4.0 * d_h * H_q * float((i + 1.0).sum())
 
 
+def decode_bytes(batch: int, N: int, H_q: int, H_kv: int, d_h: int, d_idx: int, B_k: int, k: int,
+                 valid_slots: int) -> int:
+    """HBM bytes of one decode step (bf16), each tensor counted once: the
+    K^idx scan of the L = (N - 1) // B_k earlier blocks, Q^idx and Q, the block
+    scores written and read, K and V of every selected block (the last block
+    partial), the partial outputs written and read by the merge, the selection,
+    and O."""
+    L = (N - 1) // B_k
+    B = -(-N // B_k)
+    G = H_q // H_kv
+    scan = batch * L * B_k * d_idx * 2 + batch * H_kv * d_idx * 2
+    scores = 2 * 4 * batch * H_kv * B
+    kv = valid_slots * 2 * B_k * d_h * 2
+    part = 2 * valid_slots * G * (2 * d_h + 4)
+    return int(scan + scores + kv + part + 2 * 4 * batch * H_kv * k + 2 * batch * H_q * d_h * 2)
+
+
 def partial_bytes(n_valid_slots: int, G: int, d_h: int) -> int:
     """Bytes of one partial output set: bf16 O-bar (2 d_h) + fp32 lse per head."""
     return n_valid_slots * G * (2 * d_h + 4)

@@ -21,18 +21,19 @@
 // gfx950 design.  Decode is bound by HBM, and the index scan dominates: it
 // reads the whole K^idx cache (256 B per token at d_idx = 128), while the main
 // branch reads k blocks of K and V per group.
-//  * Scores: one workgroup of 4 waves per 4 key blocks of one sequence; wave w
-//    scores block 4 c + w for all groups at once with
-//    v_mfma_f32_32x32x16_bf16 (keys on the row dimension, the H_kv <= 32
-//    index query heads on the columns), K^idx fragments loaded straight from
-//    memory (each 256-byte row is read by two lanes, 16 bytes per step), and
-//    the block max is an in-lane max plus one half-wave exchange.  Block
-//    scores go to a small fp32 buffer [batch][H_kv][B].
-//  * Top-k: one workgroup per (sequence, group); each thread keeps the k - 1
-//    best (score, block) keys of its strided share in VGPRs, then the lists
-//    are merged pairwise through LDS.  A 64-bit key (order-preserving score
-//    bits, then the complemented block id) makes "higher score, then smaller
-//    id" a plain unsigned comparison.
+//  * Scores: waves stride over the (sequence, block) pairs; a wave scores one
+//    block for all groups at once with v_mfma_f32_32x32x16_bf16 (keys on the
+//    row dimension, the H_kv <= 32 index query heads on the columns), the
+//    block's K^idx fragments loaded straight from memory, all 32 KB requested
+//    before the first MFMA (each 256-byte row is read by two lanes, 16 bytes
+//    per step); the block max is an in-lane max plus one half-wave exchange.
+//    Block scores go to a small fp32 buffer [batch][H_kv][B].
+//  * Top-k: one workgroup per (sequence, group); each thread keeps the best
+//    (score, block) keys of its strided share in VGPRs, then the lists are
+//    merged pairwise (a bitonic merge in registers per round, the partner
+//    list read from LDS).  A 64-bit key (order-preserving score bits, then the
+//    complemented block id) makes "higher score, then smaller id" a plain
+//    unsigned comparison.
 //  * Partials: one 512-thread workgroup per (sequence, group, slot) stages
 //    the selected K/V block into LDS (the shared tile layout) and one wave
 //    computes S^T = K Q^T for the G heads, the softmax and O^T = V^T P^T.
@@ -57,48 +58,59 @@ __device__ __forceinline__ uint32_t ord_score(float x) {
 template <int DIDX>
 __global__ __launch_bounds__(64 * kScoreWaves) void decode_scores_kernel(
     const uint16_t* __restrict__ q_idx, const uint16_t* __restrict__ k_idx, int64_t N, int H_kv,
-    int L, int B, float* __restrict__ scores) {
+    int L, int B, int batch, float* __restrict__ scores) {
   constexpr int STEPS = DIDX / 16;
-  const int bat = blockIdx.y;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int n = lane & 31, h = lane >> 5;
-  const int blk = blockIdx.x * kScoreWaves + wave;
-  if (blk >= L) return;  // wave-uniform; no barrier in this kernel
-
-  // B operand: column n = index query head n (zero past H_kv).
-  bf16x8 qf[STEPS];
-  const uint16_t* qrow = q_idx + (static_cast<int64_t>(bat) * H_kv + min(n, H_kv - 1)) * DIDX;
+  const int64_t items = static_cast<int64_t>(batch) * L;  // (sequence, block) pairs
+  const int64_t nwaves = static_cast<int64_t>(gridDim.x) * kScoreWaves;
+  // Each wave strides over the pairs; consecutive waves take consecutive
+  // blocks of one sequence.  No barrier in this kernel.
+  for (int64_t it = static_cast<int64_t>(blockIdx.x) * kScoreWaves + wave; it < items; it += nwaves) {
+    const int bat = static_cast<int>(it / L), blk = static_cast<int>(it % L);
+    // All 4 key tiles' A fragments (row 32 mt + n, dims 16 ks + 8 h .. + 7)
+    // are requested before any is used.
+    const uint16_t* kb = k_idx + (static_cast<int64_t>(bat) * N + static_cast<int64_t>(blk) * kBk + n) * DIDX + 8 * h;
+    u32x4 kf[4][STEPS];
 #pragma unroll
-  for (int ks = 0; ks < STEPS; ++ks) {
-    const u32x4 w = *reinterpret_cast<const u32x4*>(qrow + 16 * ks + 8 * h);
-    qf[ks] = as_bf16x8(n < H_kv ? w : u32x4{0u, 0u, 0u, 0u});
+    for (int mt = 0; mt < 4; ++mt) {
+#pragma unroll
+      for (int ks = 0; ks < STEPS; ++ks)
+        kf[mt][ks] = *reinterpret_cast<const u32x4*>(kb + 32 * mt * DIDX + 16 * ks);
+    }
+    // B operand: column n = index query head n (zero past H_kv).
+    const uint16_t* qrow = q_idx + (static_cast<int64_t>(bat) * H_kv + min(n, H_kv - 1)) * DIDX;
+    bf16x8 qf[STEPS];
+#pragma unroll
+    for (int ks = 0; ks < STEPS; ++ks) {
+      const u32x4 w = *reinterpret_cast<const u32x4*>(qrow + 16 * ks + 8 * h);
+      qf[ks] = as_bf16x8(n < H_kv ? w : u32x4{0u, 0u, 0u, 0u});
+    }
+    float mx = -__builtin_huge_valf();
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      f32x16 acc = {};
+#pragma unroll
+      for (int ks = 0; ks < STEPS; ++ks) acc = mfma32x32x16(as_bf16x8(kf[mt][ks]), qf[ks], acc);
+#pragma unroll
+      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, acc[e]);
+    }
+    mx = halves_max(mx);
+    if (h == 0 && n < H_kv) scores[(static_cast<int64_t>(bat) * H_kv + n) * B + blk] = mx;
   }
-  // A operand: key row 32 mt + n of the block, dims 16 ks + 8 h .. + 7.
-  const uint16_t* kb = k_idx + (static_cast<int64_t>(bat) * N + static_cast<int64_t>(blk) * kBk + n) * DIDX + 8 * h;
-  float mx = -__builtin_huge_valf();
-#pragma unroll
-  for (int mt = 0; mt < 4; ++mt) {
-    u32x4 kf[STEPS];
-#pragma unroll
-    for (int ks = 0; ks < STEPS; ++ks)
-      kf[ks] = *reinterpret_cast<const u32x4*>(kb + 32 * mt * DIDX + 16 * ks);
-    f32x16 acc = {};
-#pragma unroll
-    for (int ks = 0; ks < STEPS; ++ks) acc = mfma32x32x16(as_bf16x8(kf[ks]), qf[ks], acc);
-#pragma unroll
-    for (int e = 0; e < 16; ++e) mx = fmaxf(mx, acc[e]);
-  }
-  mx = halves_max(mx);
-  if (h == 0 && n < H_kv) scores[(static_cast<int64_t>(bat) * H_kv + n) * B + blk] = mx;
 }
 
-constexpr int kTopkThreads = 256;
+constexpr int kTopkBatch = 8;  // candidates a thread requests before inserting
+// Threads of the top-k workgroup: few merge rounds matter more than short
+// per-thread scans (each round is a 64-bit bitonic merge in every active lane).
+template <int KP>
+constexpr int topk_threads() { return 256; }
 
-// Insert key x into the descending list v[0..KM) (v[KM - 1] the smallest).
-template <int KM>
-__device__ __forceinline__ void insert_desc(uint64_t (&v)[KM], uint64_t x) {
+// Insert key x into the descending list v[0..KP) (v[KP - 1] the smallest).
+template <int KP>
+__device__ __forceinline__ void insert_desc(uint64_t (&v)[KP], uint64_t x) {
 #pragma unroll
-  for (int j = 0; j < KM; ++j) {
+  for (int j = 0; j < KP; ++j) {
     const uint64_t t = v[j];
     const bool sw = x > t;
     v[j] = sw ? x : t;
@@ -106,61 +118,87 @@ __device__ __forceinline__ void insert_desc(uint64_t (&v)[KM], uint64_t x) {
   }
 }
 
-template <int KM>
-__global__ __launch_bounds__(kTopkThreads) void decode_topk_kernel(const float* __restrict__ scores,
-                                                                   int L, int B, int k,
-                                                                   int32_t* __restrict__ block_idx) {
-  __shared__ uint64_t lists[kTopkThreads * KM];
+// KP (a power of two >= k - 1) best keys per thread, then log2(threads) merge
+// rounds: list t takes the best KP of lists t and t + s.  A thread first
+// requests all its candidates (up to kTopkBatch per pass), then inserts them,
+// so the score loads are not serialised behind the insertions.  A merge is
+// compile-time indexed: the elementwise max of one descending list and the
+// other reversed holds the KP largest keys as a bitonic sequence, which a
+// bitonic merge sorts descending.  Partner lists go through LDS entry-major
+// (conflict-free).
+template <int KP>
+__global__ __launch_bounds__(topk_threads<KP>()) void decode_topk_kernel(const float* __restrict__ scores,
+                                                                         int L, int B, int k,
+                                                                         int32_t* __restrict__ block_idx) {
+  constexpr int kTopkThreads = topk_threads<KP>();
+  __shared__ uint64_t lists[KP * kTopkThreads / 2];
   const int seq = blockIdx.x;  // batch * H_kv + r
   const int t = threadIdx.x;
   const float* row = scores + static_cast<int64_t>(seq) * B;
 
-  uint64_t v[KM];
+  uint64_t v[KP];
 #pragma unroll
-  for (int j = 0; j < KM; ++j) v[j] = 0;  // below every real key
-  for (int b = t; b < L; b += kTopkThreads) {
-    const uint64_t key = (static_cast<uint64_t>(ord_score(row[b])) << 32) | (0xFFFFFFFFu - static_cast<uint32_t>(b));
-    if (key > v[KM - 1]) insert_desc<KM>(v, key);
+  for (int j = 0; j < KP; ++j) v[j] = 0;  // below every real key
+  for (int b0 = t; b0 < L; b0 += kTopkThreads * kTopkBatch) {
+    float sc[kTopkBatch];
+#pragma unroll
+    for (int u = 0; u < kTopkBatch; ++u) {
+      const int b = b0 + u * kTopkThreads;
+      sc[u] = row[b < L ? b : 0];
+    }
+#pragma unroll
+    for (int u = 0; u < kTopkBatch; ++u) {
+      const int b = b0 + u * kTopkThreads;
+      const uint64_t key = b < L ? (static_cast<uint64_t>(ord_score(sc[u])) << 32) |
+                                       (0xFFFFFFFFu - static_cast<uint32_t>(b))
+                                 : 0;
+      if (key > v[KP - 1]) insert_desc<KP>(v, key);
+    }
   }
-#pragma unroll
-  for (int j = 0; j < KM; ++j) lists[t * KM + j] = v[j];
-  __syncthreads();
-  // Pairwise merges: list t takes the best KM of lists t and t + s.
   for (int s = kTopkThreads / 2; s > 0; s >>= 1) {
-    if (t < s) {
-      const uint64_t* a = lists + t * KM;
-      const uint64_t* c = lists + (t + s) * KM;
-      uint64_t m[KM];
-      int ia = 0, ic = 0;
+    if (t >= s && t < 2 * s) {
 #pragma unroll
-      for (int j = 0; j < KM; ++j) {
-        const uint64_t x = a[ia], y = c[ic];
-        const bool ta = x >= y;
-        m[j] = ta ? x : y;
-        ia += ta ? 1 : 0;
-        ic += ta ? 0 : 1;
+      for (int j = 0; j < KP; ++j) lists[j * (kTopkThreads / 2) + (t - s)] = v[j];
+    }
+    __syncthreads();
+    if (t < s) {
+      uint64_t m[KP];
+#pragma unroll
+      for (int j = 0; j < KP; ++j) {
+        const uint64_t x = v[j], y = lists[(KP - 1 - j) * (kTopkThreads / 2) + t];
+        m[j] = x > y ? x : y;
       }
 #pragma unroll
-      for (int j = 0; j < KM; ++j) lists[t * KM + j] = m[j];
+      for (int st = KP / 2; st > 0; st >>= 1) {
+#pragma unroll
+        for (int i = 0; i < KP; ++i) {
+          if ((i & st) == 0) {
+            const uint64_t x = m[i], y = m[i + st];
+            m[i] = x > y ? x : y;
+            m[i + st] = x > y ? y : x;
+          }
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < KP; ++j) v[j] = m[j];
     }
     __syncthreads();
   }
   if (t == 0) {
-    // Ascending ids of the kept blocks (at most k - 1 <= KM of them), then L,
-    // then -1.  Odd-even transposition sort over KM entries (all indices
-    // compile-time constants).
-    int ids[KM];
+    // Ascending ids of the k - 1 best (fewer when there are fewer earlier
+    // blocks), then L, then -1.  Odd-even transposition sort, compile-time
+    // indices.
+    int ids[KP];
     int nv = 0;
 #pragma unroll
-    for (int j = 0; j < KM; ++j) {
-      const uint64_t key = lists[j];
-      ids[j] = (key != 0 && j < k - 1) ? static_cast<int>(0xFFFFFFFFu - static_cast<uint32_t>(key)) : INT_MAX;
+    for (int j = 0; j < KP; ++j) {
+      ids[j] = (v[j] != 0 && j < k - 1) ? static_cast<int>(0xFFFFFFFFu - static_cast<uint32_t>(v[j])) : INT_MAX;
       nv += ids[j] != INT_MAX ? 1 : 0;
     }
 #pragma unroll
-    for (int round = 0; round < KM; ++round) {
+    for (int round = 0; round < KP; ++round) {
 #pragma unroll
-      for (int i = round & 1; i + 1 < KM; i += 2) {
+      for (int i = round & 1; i + 1 < KP; i += 2) {
         const int a = ids[i], c = ids[i + 1];
         ids[i] = min(a, c);
         ids[i + 1] = max(a, c);
@@ -168,8 +206,8 @@ __global__ __launch_bounds__(kTopkThreads) void decode_topk_kernel(const float* 
     }
     int32_t* dst = block_idx + static_cast<int64_t>(seq) * k;
 #pragma unroll
-    for (int j = 0; j <= KM; ++j) {
-      if (j < k) dst[j] = j < nv ? ids[j < KM ? j : 0] : (j == nv ? L : -1);
+    for (int j = 0; j <= KP; ++j) {
+      if (j < k) dst[j] = j < nv ? ids[j < KP ? j : 0] : (j == nv ? L : -1);
     }
   }
 }
@@ -279,10 +317,10 @@ __global__ __launch_bounds__(kStageThreads, 1) void decode_partial_kernel(
   if (h == 0 && n < G) lse_part[item * G + n] = (mb + __builtin_amdgcn_logf(l)) * 0.69314718055994531f;
 }
 
-template <int KM>
+template <int KP>
 hipError_t launch_topk(const float* scores, int nseq, int L, int B, int k, int32_t* block_idx,
                        hipStream_t stream) {
-  hipLaunchKernelGGL(decode_topk_kernel<KM>, dim3(static_cast<unsigned>(nseq)), dim3(kTopkThreads), 0,
+  hipLaunchKernelGGL(decode_topk_kernel<KP>, dim3(static_cast<unsigned>(nseq)), dim3(topk_threads<KP>()), 0,
                      stream, scores, L, B, k, block_idx);
   return hipGetLastError();
 }
@@ -309,21 +347,25 @@ hipError_t launch_decode(const uint16_t* q, const uint16_t* q_idx, const uint16_
   const int nseq = batch * H_kv;
   hipError_t e = hipSuccess;
   if (L > 0) {
-    const dim3 grid(static_cast<unsigned>((L + kScoreWaves - 1) / kScoreWaves), static_cast<unsigned>(batch));
+    // A few waves per SIMD, each striding over many blocks.
+    const int64_t items = static_cast<int64_t>(batch) * L;
+    int64_t wgs = (items + kScoreWaves - 1) / kScoreWaves;
+    if (wgs > 1024) wgs = 1024;
     if (d_idx == 64)
-      hipLaunchKernelGGL(decode_scores_kernel<64>, grid, dim3(64 * kScoreWaves), 0, stream, q_idx, k_idx, N,
-                         H_kv, L, B, scores);
+      hipLaunchKernelGGL(decode_scores_kernel<64>, dim3(static_cast<unsigned>(wgs)), dim3(64 * kScoreWaves), 0,
+                         stream, q_idx, k_idx, N, H_kv, L, B, batch, scores);
     else
-      hipLaunchKernelGGL(decode_scores_kernel<128>, grid, dim3(64 * kScoreWaves), 0, stream, q_idx, k_idx, N,
-                         H_kv, L, B, scores);
+      hipLaunchKernelGGL(decode_scores_kernel<128>, dim3(static_cast<unsigned>(wgs)), dim3(64 * kScoreWaves), 0,
+                         stream, q_idx, k_idx, N, H_kv, L, B, batch, scores);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   const int km = kslots - 1;
   if (km <= 1) e = launch_topk<1>(scores, nseq, L, B, kslots, block_idx, stream);
-  else if (km <= 3) e = launch_topk<3>(scores, nseq, L, B, kslots, block_idx, stream);
-  else if (km <= 7) e = launch_topk<7>(scores, nseq, L, B, kslots, block_idx, stream);
-  else if (km <= 15) e = launch_topk<15>(scores, nseq, L, B, kslots, block_idx, stream);
-  else e = launch_topk<31>(scores, nseq, L, B, kslots, block_idx, stream);
+  else if (km <= 2) e = launch_topk<2>(scores, nseq, L, B, kslots, block_idx, stream);
+  else if (km <= 4) e = launch_topk<4>(scores, nseq, L, B, kslots, block_idx, stream);
+  else if (km <= 8) e = launch_topk<8>(scores, nseq, L, B, kslots, block_idx, stream);
+  else if (km <= 16) e = launch_topk<16>(scores, nseq, L, B, kslots, block_idx, stream);
+  else e = launch_topk<32>(scores, nseq, L, B, kslots, block_idx, stream);
   if (e != hipSuccess) return e;
   switch (G) {
     case 1: e = launch_partial<1>(q, k, v, batch, N, H_kv, kslots, scale_log2, block_idx, o_part, lse_part, stream); break;

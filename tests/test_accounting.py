@@ -66,3 +66,15 @@ def test_dense_flops_closed_form_and_chunks():
     assert parts == full
     assert abs(full / (N * acc.gqa_flops_per_token(N, H_q, d_h)) - 1.0) < 2.0 / N
     assert acc.dense_flops(0, 1, 1, 1, batch=3) == 12.0
+
+
+def test_decode_bytes_dominated_by_index_scan():
+    """At 1M tokens the K^idx scan (256 B per earlier token) is almost all of a
+    decode step's traffic; a single-block context reads no K^idx at all."""
+    N = 1 << 20
+    total = acc.decode_bytes(1, N, 64, 4, 128, 128, 128, 16, 4 * 16)
+    scan = (N - 128) * 128 * 2
+    assert scan < total < 1.02 * scan + 5e6
+    small = acc.decode_bytes(2, 100, 8, 2, 128, 64, 128, 4, 2 * 2)
+    assert small == (2 * 2 * 64 * 2 + 2 * 4 * 2 * 2 * 1 + 4 * 2 * 128 * 128 * 2
+                     + 2 * 4 * 4 * (256 + 4) + 2 * 4 * 2 * 2 * 4 + 2 * 2 * 8 * 128 * 2)
