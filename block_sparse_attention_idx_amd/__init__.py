@@ -27,7 +27,8 @@ EXPORTS = (
     "msa_abi_version", "msa_status_string", "msa_last_hip_error", "msa_index_topk",
     "msa_invert_workspace_size", "msa_invert_blocks", "msa_invert_status",
     "msa_sparse_attn_fwd", "msa_combine", "msa_workspace_size", "msa_forward",
-    "msa_dense_attn_fwd", "msa_decode_workspace_size", "msa_decode",
+    "msa_dense_attn_fwd", "msa_decode_workspace_size", "msa_decode", "msa_index_topk_forced",
+    "msa_window_select",
 )
 
 
@@ -95,6 +96,8 @@ def lib():
             "msa_dense_attn_fwd": ([D, O, P, P, P, I64, I64, P, P, P], ctypes.c_int),
             "msa_decode_workspace_size": ([D, O, ctypes.POINTER(SZ)], ctypes.c_int),
             "msa_decode": ([D, O, P, P, P, P, P, P, P, P, P, SZ, P], ctypes.c_int),
+            "msa_index_topk_forced": ([D, P, P, I64, I64, ctypes.c_int, ctypes.c_int, P, P], ctypes.c_int),
+            "msa_window_select": ([D, I64, I64, P, P], ctypes.c_int),
         }
         for name, (args, res) in sig.items():
             f = getattr(L, name)
@@ -148,6 +151,34 @@ def msa_index_topk(dims: msa_dims, q_idx, k_idx, q_begin: int = 0, q_count: Opti
     with _dev(q_idx):
         _check(lib().msa_index_topk(ctypes.byref(dims), _p(q_idx), _p(k_idx), q_begin, q_count,
                                     _p(block_idx), _stream(q_idx)), "msa_index_topk")
+    return block_idx
+
+
+def msa_index_topk_forced(dims: msa_dims, q_idx, k_idx, force_first: bool = True, local_window: int = 1,
+                          q_begin: int = 0, q_count: Optional[int] = None, block_idx=None):
+    """Index branch with forced block 0 and/or a forced local window of blocks."""
+    import torch
+    q_count = dims.N - q_begin if q_count is None else q_count
+    if block_idx is None:
+        block_idx = _empty((dims.batch, dims.H_kv, q_count, dims.k), torch.int32, q_idx)
+    with _dev(q_idx):
+        _check(lib().msa_index_topk_forced(ctypes.byref(dims), _p(q_idx), _p(k_idx), q_begin, q_count,
+                                           int(force_first), int(local_window), _p(block_idx),
+                                           _stream(q_idx)), "msa_index_topk_forced")
+    return block_idx
+
+
+def msa_window_select(dims: msa_dims, q_begin: int = 0, q_count: Optional[int] = None, block_idx=None,
+                      device=None):
+    """FLOP-matched sliding-window selection int32 [batch, H_kv, q_count, k]."""
+    import torch
+    q_count = dims.N - q_begin if q_count is None else q_count
+    if block_idx is None:
+        block_idx = torch.empty((dims.batch, dims.H_kv, q_count, dims.k), dtype=torch.int32,
+                                device=device or "cuda")
+    with _dev(block_idx):
+        _check(lib().msa_window_select(ctypes.byref(dims), q_begin, q_count, _p(block_idx),
+                                       _stream(block_idx)), "msa_window_select")
     return block_idx
 
 

@@ -141,6 +141,36 @@ int msa_index_topk(const msa_dims* dims, const void* q_idx, const void* k_idx, i
   return e == hipSuccess ? MSA_OK : hip_fail(e);
 }
 
+int msa_index_topk_forced(const msa_dims* dims, const void* q_idx, const void* k_idx,
+                          int64_t q_begin, int64_t q_count, int force_first, int local_window,
+                          int32_t* block_idx, void* stream) {
+  int st = check_dims(dims);
+  if (st) return st;
+  if ((st = check_range(dims, q_begin, q_count))) return st;
+  if (force_first != 0 && force_first != 1) return MSA_ERR_SHAPE;
+  if (local_window < 1 || (force_first ? 1 : 0) + (local_window - 1) > dims->k - 1) return MSA_ERR_SHAPE;
+  if (!q_idx || !k_idx || !block_idx) return MSA_ERR_NULL;
+  if (misaligned(q_idx) || misaligned(k_idx) || misaligned(block_idx)) return MSA_ERR_ALIGN;
+  hipError_t e = msa::launch_index_topk(static_cast<const uint16_t*>(q_idx),
+                                        static_cast<const uint16_t*>(k_idx), dims->batch, dims->N,
+                                        dims->H_kv, dims->d_idx, dims->k, q_begin, q_count,
+                                        block_idx, static_cast<hipStream_t>(stream), force_first,
+                                        local_window);
+  return e == hipSuccess ? MSA_OK : hip_fail(e);
+}
+
+int msa_window_select(const msa_dims* dims, int64_t q_begin, int64_t q_count, int32_t* block_idx,
+                      void* stream) {
+  int st = check_dims(dims);
+  if (st) return st;
+  if ((st = check_range(dims, q_begin, q_count))) return st;
+  if (!block_idx) return MSA_ERR_NULL;
+  if (misaligned(block_idx)) return MSA_ERR_ALIGN;
+  hipError_t e = msa::launch_window_select(dims->batch, dims->H_kv, dims->k, q_begin, q_count, block_idx,
+                                           static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MSA_OK : hip_fail(e);
+}
+
 int msa_invert_workspace_size(const msa_dims* dims, int64_t q_begin, int64_t q_count,
                               size_t* bytes) {
   int st = check_dims(dims);

@@ -97,10 +97,16 @@ __device__ __forceinline__ void sort_ascending(int (&v)[KP]) {
 // KP = capacity rounded up to a power of two; the list holds KP - 1 entries of
 // which the first KP - k are +inf sentinels, so the last entry is always the
 // row's (k-1)-th best score.
-template <int DIDX, int KP>
+//
+// FORCED (the early-training variant, "MiniMax Sparse Attention", ablation of
+// forced sink and local blocks): block 0 (force_first) and the window - 1
+// blocks before the local one score +inf, so they always take slots; among
+// equal scores the smaller id still wins.
+template <int DIDX, int KP, bool FORCED>
 __global__ __launch_bounds__(kIdxThreads, 1) void index_topk_kernel(
     const uint16_t* __restrict__ q_idx, const uint16_t* __restrict__ k_idx, int64_t N, int H_kv,
-    int k, int64_t q_begin, int64_t q_count, int32_t* __restrict__ block_idx) {
+    int k, int64_t q_begin, int64_t q_count, int force_first, int window,
+    int32_t* __restrict__ block_idx) {
   constexpr int KM = KP - 1;
   constexpr int NCH = DIDX / 8;
   constexpr int STEPS = DIDX / 16;
@@ -247,7 +253,10 @@ __global__ __launch_bounds__(kIdxThreads, 1) void index_topk_kernel(
       // that half 0 finishes column tile 0 and half 1 column tile 1.
       const float send = h ? mx0 : mx1;
       const float recv = __shfl_xor(send, 32);
-      const float score = fmaxf(h ? mx1 : mx0, recv);
+      float score = fmaxf(h ? mx1 : mx0, recv);
+      if constexpr (FORCED) {
+        if ((force_first && b == 0) || b > L_mine - window) score = __builtin_huge_valf();
+      }
       const bool need = (b < L_mine) && (score > ts[KM - 1]);
       if constexpr (kDefer) {
         pend_x = score;
@@ -301,37 +310,46 @@ __global__ __launch_bounds__(kIdxThreads, 1) void index_topk_kernel(
   }
 }
 
-template <int DIDX, int KP>
-hipError_t launch_t(const uint16_t* q_idx, const uint16_t* k_idx, int batch, int64_t N, int H_kv,
-                    int k, int64_t q_begin, int64_t q_count, int32_t* block_idx,
-                    hipStream_t stream) {
-  const int64_t nwg = (q_count * H_kv + kIdxRows - 1) / kIdxRows;
-  hipLaunchKernelGGL((index_topk_kernel<DIDX, KP>), dim3(static_cast<unsigned>(nwg), batch),
-                     dim3(kIdxThreads), 0, stream, q_idx, k_idx, N, H_kv, k, q_begin, q_count,
-                     block_idx);
+struct IdxArgs {
+  const uint16_t* q_idx;
+  const uint16_t* k_idx;
+  int batch;
+  int64_t N;
+  int H_kv, k;
+  int64_t q_begin, q_count;
+  int force_first, window;
+  int32_t* block_idx;
+  hipStream_t stream;
+};
+
+template <int DIDX, int KP, bool FORCED>
+hipError_t launch_t(const IdxArgs& a) {
+  const int64_t nwg = (a.q_count * a.H_kv + kIdxRows - 1) / kIdxRows;
+  hipLaunchKernelGGL((index_topk_kernel<DIDX, KP, FORCED>), dim3(static_cast<unsigned>(nwg), a.batch),
+                     dim3(kIdxThreads), 0, a.stream, a.q_idx, a.k_idx, a.N, a.H_kv, a.k, a.q_begin,
+                     a.q_count, a.force_first, a.window, a.block_idx);
   return hipGetLastError();
 }
 
-template <int DIDX>
-hipError_t launch_d(const uint16_t* q_idx, const uint16_t* k_idx, int batch, int64_t N, int H_kv,
-                    int k, int64_t q_begin, int64_t q_count, int32_t* block_idx,
-                    hipStream_t stream) {
-  if (k <= 1) return launch_t<DIDX, 1>(q_idx, k_idx, batch, N, H_kv, k, q_begin, q_count, block_idx, stream);
-  if (k <= 2) return launch_t<DIDX, 2>(q_idx, k_idx, batch, N, H_kv, k, q_begin, q_count, block_idx, stream);
-  if (k <= 4) return launch_t<DIDX, 4>(q_idx, k_idx, batch, N, H_kv, k, q_begin, q_count, block_idx, stream);
-  if (k <= 8) return launch_t<DIDX, 8>(q_idx, k_idx, batch, N, H_kv, k, q_begin, q_count, block_idx, stream);
-  if (k <= 16) return launch_t<DIDX, 16>(q_idx, k_idx, batch, N, H_kv, k, q_begin, q_count, block_idx, stream);
-  return launch_t<DIDX, 32>(q_idx, k_idx, batch, N, H_kv, k, q_begin, q_count, block_idx, stream);
+template <int DIDX, bool FORCED>
+hipError_t launch_d(const IdxArgs& a) {
+  if (a.k <= 1) return launch_t<DIDX, 1, FORCED>(a);
+  if (a.k <= 2) return launch_t<DIDX, 2, FORCED>(a);
+  if (a.k <= 4) return launch_t<DIDX, 4, FORCED>(a);
+  if (a.k <= 8) return launch_t<DIDX, 8, FORCED>(a);
+  if (a.k <= 16) return launch_t<DIDX, 16, FORCED>(a);
+  return launch_t<DIDX, 32, FORCED>(a);
 }
 
 }  // namespace
 
 hipError_t launch_index_topk(const uint16_t* q_idx, const uint16_t* k_idx, int batch, int64_t N,
                              int H_kv, int d_idx, int k, int64_t q_begin, int64_t q_count,
-                             int32_t* block_idx, hipStream_t stream) {
-  if (d_idx == 64)
-    return launch_d<64>(q_idx, k_idx, batch, N, H_kv, k, q_begin, q_count, block_idx, stream);
-  return launch_d<128>(q_idx, k_idx, batch, N, H_kv, k, q_begin, q_count, block_idx, stream);
+                             int32_t* block_idx, hipStream_t stream, int force_first, int window) {
+  const IdxArgs a{q_idx, k_idx, batch, N, H_kv, k, q_begin, q_count, force_first, window, block_idx, stream};
+  const bool forced = force_first != 0 || window > 1;
+  if (d_idx == 64) return forced ? launch_d<64, true>(a) : launch_d<64, false>(a);
+  return forced ? launch_d<128, true>(a) : launch_d<128, false>(a);
 }
 
 }  // namespace msa

@@ -94,10 +94,17 @@ __device__ __forceinline__ u32x2 e4m3x4_to_bf16x4(uint32_t w) {
 // ---------------------------------------------------------------- launchers
 // Each returns hipSuccess or the HIP error of the launch.
 
-// Index branch.  block_idx rows: [batch][H_kv][q_count][k].
+// Index branch.  block_idx rows: [batch][H_kv][q_count][k].  force_first /
+// window > 1 also force block 0 and the window - 1 blocks before the local one.
 hipError_t launch_index_topk(const uint16_t* q_idx, const uint16_t* k_idx, int batch, int64_t N,
                              int H_kv, int d_idx, int k, int64_t q_begin, int64_t q_count,
-                             int32_t* block_idx, hipStream_t stream);
+                             int32_t* block_idx, hipStream_t stream, int force_first = 0,
+                             int window = 1);
+
+// FLOP-matched sliding-window selection: block 0 and the k - 1 blocks ending
+// at the local one (all of 0 .. L when L < k), ascending, -1 padded.
+hipError_t launch_window_select(int batch, int H_kv, int k, int64_t q_begin, int64_t q_count,
+                                int32_t* block_idx, hipStream_t stream);
 
 // Inversion scratch layout (all offsets in 4-byte words, 256-byte aligned).
 // A segment is a (seq, block) bin restricted to one query window; segments are

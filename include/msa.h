@@ -120,6 +120,30 @@ int msa_index_topk(const msa_dims *dims, const void *q_idx, const void *k_idx,
                    int64_t q_begin, int64_t q_count, int32_t *block_idx, void *stream);
 
 /*
+ * msa_index_topk_forced -- msa_index_topk with the early-training forced
+ * blocks ("MiniMax Sparse Attention", ablation of the forced first block and
+ * fixed local window): block 0 when force_first = 1, and the local_window - 1
+ * blocks before the local block, always take slots (their scores count as
+ * +inf); the remaining slots go to the best other blocks.  local_window = 1
+ * and force_first = 0 is msa_index_topk.  The forced blocks must fit:
+ * force_first + local_window - 1 <= k - 1 (MSA_ERR_SHAPE otherwise).
+ */
+int msa_index_topk_forced(const msa_dims *dims, const void *q_idx, const void *k_idx,
+                          int64_t q_begin, int64_t q_count, int force_first, int local_window,
+                          int32_t *block_idx, void *stream);
+
+/*
+ * msa_window_select -- the FLOP-matched sliding-window selection ("MiniMax
+ * Sparse Attention", comparison with a fixed sparse pattern): query i takes
+ * block 0 and the k - 1 blocks ending at its local block L = floor(i / B_k)
+ * (every block 0 .. L when L < k), with no index branch.  block_idx as for
+ * msa_index_topk; feed it to msa_invert_blocks, msa_sparse_attn_fwd and
+ * msa_combine like a top-k selection.
+ */
+int msa_window_select(const msa_dims *dims, int64_t q_begin, int64_t q_count, int32_t *block_idx,
+                      void *stream);
+
+/*
  * msa_invert_workspace_size -- bytes of the device scratch buffer `sched` used by
  * msa_invert_blocks and read by msa_sparse_attn_fwd for the same range.
  */

@@ -108,11 +108,40 @@ def select(M, pos, B_k, k):
     return out, marg
 
 
-def index_topk(N, B_k, k, pos, q_idx_rows, k_idx):
-    """Index branch for the given query rows: (block_idx, rel_margin, M)."""
+def index_topk(N, B_k, k, pos, q_idx_rows, k_idx, force_first=False, window=1):
+    """Index branch for the given query rows: (block_idx, rel_margin, M).
+
+    force_first / window > 1: the early-training variant ("MiniMax Sparse
+    Attention", ablation of the forced first block and fixed local window):
+    block 0 and the window - 1 blocks before the local one get score +inf
+    before the selection, so they always take slots.  The returned M holds
+    those +inf scores; a margin undefined because the (k-1)-th choice is
+    itself forced is +inf (the selection is then unique)."""
     M = block_scores(N, B_k, pos, q_idx_rows, k_idx)
+    if force_first or window > 1:
+        pos = np.asarray(pos, np.int64)
+        for n, i in enumerate(pos):
+            L = int(i // B_k)
+            if force_first and L >= 1:
+                M[n, :, 0] = np.inf
+            M[n, :, max(0, L - window + 1):L] = np.inf
     bi, marg = select(M, pos, B_k, k)
+    marg = np.where(np.isnan(marg), np.inf, marg)
     return bi, marg, M
+
+
+def window_selection(pos, B_k, k, H_kv):
+    """FLOP-matched sliding-window selection ("MiniMax Sparse Attention",
+    comparison with a fixed sparse pattern): block 0 and the k - 1 blocks
+    ending at the local block L = i // B_k; every block 0 .. L when L < k.
+    [H_kv, n_rows, k] int32, ascending, -1 padded."""
+    pos = np.asarray(pos, np.int64)
+    out = np.full((len(pos), k), -1, np.int32)
+    for n, i in enumerate(pos):
+        L = int(i // B_k)
+        blocks = list(range(L + 1)) if L < k else [0] + list(range(L - k + 2, L + 1))
+        out[n, :len(blocks)] = blocks
+    return np.ascontiguousarray(np.broadcast_to(out[None], (H_kv, len(pos), k)))
 
 
 def attention(N, B_k, pos, q_rows, K, V, block_idx, softmax_scale=None,

@@ -57,10 +57,13 @@ def admissible(gsel, osel, Mrow, k) -> bool:
     o = set(int(x) for x in osel if x >= 0)
     if len(g) != len(o) or max(o) not in g:
         return False
+    # blocks forced by a +inf score besides the local one leave k - 1 - forced
+    # free choices among the finite scores
+    free = k - 1 - (int(np.sum(Mrow == np.inf)) - 1)
     cand = np.sort(Mrow[np.isfinite(Mrow)])[::-1]
-    if len(cand) < k:
+    if len(cand) <= free or free < 1:
         return g == o
-    ck1, ck = float(cand[k - 2]), float(cand[k - 1])
+    ck1, ck = float(cand[free - 1]), float(cand[free])
     tol = MARGIN * max(abs(ck1), abs(ck), 1e-6)
     return (all(Mrow[b] >= ck1 - tol for b in g - o) and
             all(Mrow[b] <= ck + tol for b in o - g))

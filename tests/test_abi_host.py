@@ -157,6 +157,21 @@ def test_decode_validation(L):
     assert L.msa_decode_workspace_size(ctypes.byref(d), ctypes.byref(o), None) == 1
 
 
+def test_selection_variant_validation(L):
+    d = dims(k=4)
+    f = lambda first, window, d=d: L.msa_index_topk_forced(ctypes.byref(d), FAKE, FAKE, 0, 16, first,
+                                                          window, FAKE, None)
+    assert f(2, 1) == 2                      # force_first is 0 or 1
+    assert f(0, 0) == 2                      # the window includes the local block
+    assert f(1, 4) == 2                      # 1 + 3 forced > k - 1 = 3
+    assert f(0, 5) == 2
+    assert L.msa_index_topk_forced(ctypes.byref(d), FAKE, ODD, 0, 16, 1, 3, FAKE, None) == 4
+    assert L.msa_index_topk_forced(ctypes.byref(d), None, FAKE, 0, 16, 1, 3, FAKE, None) == 1
+    assert L.msa_window_select(ctypes.byref(d), 64, 16, FAKE, None) == 2   # q_begin % B_k
+    assert L.msa_window_select(ctypes.byref(d), 0, 16, None, None) == 1
+    assert L.msa_window_select(ctypes.byref(d), 0, 16, ODD, None) == 4
+
+
 def test_binding_raises_when_library_missing(monkeypatch):
     monkeypatch.setattr(msa, "_lib", None)
     monkeypatch.setattr(msa, "LIB_PATH", "/nonexistent/libmsa.so")

@@ -294,6 +294,73 @@ def test_forward_chunked_equals_whole_and_deterministic():
     assert torch.equal(a.view(torch.int16), c.view(torch.int16))
 
 
+# --------------------------------------------------------------------------- selection variants
+
+FORCED_CASES = [
+    (TINY.with_(N=3000, k=6), True, 1),
+    (TINY.with_(N=3000, k=6, d_idx=128), False, 3),
+    (TINY.with_(N=2500, k=8, H_q=64, H_kv=4, d_idx=128, batch=2), True, 4),
+    (TINY.with_(N=1000, k=4), True, 3),                 # every free slot forced
+]
+
+
+@pytest.mark.parametrize("w,first,window", FORCED_CASES,
+                         ids=lambda x: f"N{x.N}_k{x.k}_b{x.batch}" if hasattr(x, "N") else str(x))
+def test_forced_index_parity(w, first, window):
+    log(f"forced index N={w.N} k={w.k} first={first} window={window} batch={w.batch}")
+    t = device_inputs(w, DEV)
+    bi = msa.msa_index_topk_forced(dims_of(w), t["q_idx"], t["k_idx"], force_first=first,
+                                   local_window=window)
+    torch.cuda.synchronize()
+    gsel = bi.cpu().numpy()
+    rows = np.arange(w.N)
+    for b in range(w.batch):
+        flat = b * w.N + rows
+        ob, marg, M = oracle.index_topk(w.N, w.B_k, w.k, rows, synth.host_rows(w, "q_idx", flat),
+                                        synth.host_rows(w, "k_idx", b * w.N + np.arange(w.N)),
+                                        force_first=first, window=window)
+        st = check_selection(gsel[b], ob, marg, M, w.k, what=f"forced b{b}")
+        log(f"  batch {b}: {st}")
+        L = rows // w.B_k
+        for r in range(w.H_kv):
+            if first:
+                assert (gsel[b, r][L >= 1] == 0).any(axis=1).all()
+            for back in range(1, window):
+                need = L - back >= 0
+                assert (gsel[b, r][need] == (L - back)[need][:, None]).any(axis=1).all()
+
+
+WINDOW_CASES = [TINY.with_(N=3000, k=6), TINY.with_(N=1000, k=4, batch=2, H_q=32, H_kv=2)]
+
+
+@pytest.mark.parametrize("w", WINDOW_CASES, ids=lambda w: f"N{w.N}_k{w.k}_b{w.batch}")
+def test_window_selection_attention_parity(w):
+    """The sliding-window selection is bit-exact, and attention over it through
+    the inversion, the KV-outer kernel and the combine matches the oracle."""
+    log(f"window selection N={w.N} k={w.k} batch={w.batch}")
+    t = device_inputs(w, DEV)
+    d = dims_of(w)
+    bi = msa.msa_window_select(d, device=DEV)
+    off, ent, sched = msa.msa_invert_blocks(d, bi)
+    opart, lpart = msa.msa_sparse_attn_fwd(d, msa.make_opts(), t["q"], t["k"], t["v"], off, ent, sched)
+    out, lse = msa.msa_combine(d, bi, opart, lpart, want_lse=True)
+    torch.cuda.synchronize()
+    rows = np.arange(w.N)
+    want = oracle.window_selection(rows, w.B_k, w.k, w.H_kv)
+    gsel = bi.cpu().numpy()
+    out, lse = out.float().cpu().numpy(), lse.cpu().numpy()
+    for b in range(w.batch):
+        assert np.array_equal(gsel[b], want)
+        keys = b * w.N + np.arange(w.N)
+        O, L = oracle.attention(w.N, w.B_k, rows, synth.host_rows(w, "q", b * w.N + rows),
+                                synth.host_rows(w, "k", keys), synth.host_rows(w, "v", keys), want)
+        mx, mn = err_stats(out[b], O)
+        log(f"  batch {b}: output max abs {mx:.3g} mean abs {mn:.3g}")
+        assert mx <= 2e-2 and mn <= 2e-3
+        lmx, _ = err_stats(lse[b], L)
+        assert lmx <= 1e-3
+
+
 # --------------------------------------------------------------------------- dense baseline
 
 DENSE_CASES = [

@@ -102,6 +102,60 @@ def test_index_matches_brute_force(N, H, d, k, seed):
     assert np.array_equal(bi[sure], bb[sure])
 
 
+@pytest.mark.parametrize("N,H,d,k,first,window,seed", [
+    (2048, 2, 64, 6, True, 1, 20), (2048, 1, 64, 6, False, 3, 21), (1500, 2, 128, 8, True, 4, 22),
+    (1000, 1, 64, 4, True, 3, 23),                      # all k - 1 choices forced
+])
+def test_forced_selection_matches_brute_force(N, H, d, k, first, window, seed):
+    """Forced first block / local window: the forced blocks are always chosen,
+    the remaining slots go to the best others (fp64 brute force with the
+    forced blocks removed from the candidates)."""
+    rng = np.random.default_rng(seed)
+    B_k = 128
+    q = _rand_bf16(rng, (N, H, d))
+    kk = _rand_bf16(rng, (N, d))
+    pos = np.arange(N)
+    bi, marg, _ = oracle.index_topk(N, B_k, k, pos, q, kk, force_first=first, window=window)
+    Mb = brute_scores(N, B_k, q, kk)
+    checked = 0
+    for r in range(H):
+        for i in pos:
+            L = i // B_k
+            forced = ({0} if first and L >= 1 else set()) | set(range(max(0, L - window + 1), L + 1))
+            got = [int(b) for b in bi[r, i] if b >= 0]
+            assert got == sorted(got) and forced <= set(got), (r, i, got, forced)
+            rest = [b for b in range(L) if b not in forced]
+            free = min(k - len(forced), len(rest))
+            order = sorted(rest, key=lambda b: (-Mb[i, r, b], b))
+            cand = [Mb[i, r, b] for b in order]
+            if free < len(cand) and free > 0:
+                a, b2 = cand[free - 1], cand[free]
+                if (a - b2) / max(abs(a), abs(b2), 1e-6) <= 1e-5:
+                    continue                            # near tie: fp32 vs fp64 order may differ
+            assert set(got) == forced | set(order[:free]), (r, i)
+            assert len(got) == min(k, L + 1)
+            checked += 1
+    assert checked > 0.9 * H * N
+    assert np.isfinite(marg).sum() + np.isinf(marg).sum() == marg.size   # no NaN margins
+
+
+def test_window_selection_closed_form():
+    """The sliding-window selection: block 0 plus the k - 1 blocks ending at L,
+    k blocks in all (the top-k budget), or every block when L < k."""
+    B_k, k = 128, 5
+    pos = np.array([0, 127, 128, 600, 639, 640, 5000, 70000])
+    sel = oracle.window_selection(pos, B_k, k, 3)
+    assert sel.shape == (3, len(pos), k)
+    for n, i in enumerate(pos):
+        L = i // B_k
+        row = [int(b) for b in sel[0, n] if b >= 0]
+        assert row[0] == 0 and row[-1] == L and row == sorted(set(row))
+        assert len(row) == min(k, L + 1)
+        if L >= k:
+            assert row[1:] == list(range(L - k + 2, L + 1))
+        assert (sel[1, n] == sel[0, n]).all() and (sel[2, n] == sel[0, n]).all()
+
+
 def test_selection_closed_forms():
     rng = np.random.default_rng(7)
     N, H, d, B_k = 1000, 2, 64, 128
