@@ -44,6 +44,7 @@
 //  * Softmax in base 2 (v_exp_f32) with the scale folded into one FMA; fp8
 //    (OCP e4m3) inputs are widened exactly to bf16 when used and the
 //    per-tensor scales are folded into the softmax scale and the output scale.
+#include "attn_tile.h"
 #include "msa_internal.h"
 
 namespace msa {
@@ -60,7 +61,7 @@ constexpr bool kOverlap = MSA_ATTN_OVERLAP;
 
 // LDS layouts.  Rows are padded rather than swizzled so that every fragment
 // read of a lane is one base address plus a compile-time offset (no per-read
-// address registers):
+// address registers).  K and V^T use the shared tile layout (attn_tile.h):
 //  * K row-major, 272 B per key row: a 16-lane phase of 16-byte reads of rows
 //    n .. n + 15 starts at banks 4n + const, all distinct.
 //  * V^T, 272 B per output-dimension row, row d stored at position
@@ -72,38 +73,19 @@ constexpr bool kOverlap = MSA_ATTN_OVERLAP;
 //    16-byte chunk.
 //  * Output tile, 272 B per row: 16-byte writes of rows n .. n + 15 and
 //    16-byte reads of the 16 chunks of one row are both conflict free.
-constexpr int kKStride = 272;
-constexpr int kVStride = 272;
-constexpr int kOStride = 272;
+constexpr int kKStride = tile::kStr;
+constexpr int kVStride = tile::kStr;
+constexpr int kOStride = tile::kStr;
 
 __device__ __forceinline__ int k_lds_off(int key, int c) {  // 16-byte chunk c of key row
   return key * kKStride + c * 16;
 }
 
-__device__ __forceinline__ int vt_row(int d) { return ((d & 63) << 1) | (d >> 6); }
-
-// 8-byte chunk of keys 4 kc .. 4 kc + 3 in V^T row d (bits 0 and 1 of kc swapped).
-__device__ __forceinline__ int vt_lds_off(int d, int kc) {
-  const int kcp = (kc & ~3) | ((kc & 1) << 1) | ((kc & 2) >> 1);
-  return vt_row(d) * kVStride + kcp * 8;
-}
-
-__device__ __forceinline__ uint32_t half_of(const u32x4& w, int dd) {
-  const uint32_t x = w[dd >> 1];
-  return (dd & 1) ? (x >> 16) : (x & 0xFFFFu);
-}
-
-// Lanes n and n + 32 hold the two halves of one row: v_permlane32_swap
-// exchanges the half-waves, and combining both results gives each lane the
-// full-row value.
-__device__ __forceinline__ float both_halves_max(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float both_halves_sum(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
+using tile::bf16_of;
+using tile::dvt_off;
+using tile::dvt_row;
+using tile::halves_max;
+using tile::halves_sum;
 
 // Stage K (row-major) and V (transposed) of one block of one head into LDS,
 // with the kThreads threads of the workgroup.
@@ -184,9 +166,9 @@ __device__ __forceinline__ void stage_kv(const uint8_t* __restrict__ kb, const u
 #pragma unroll
     for (int dd = 0; dd < 8; ++dd) {
       const int d = 8 * dg + dd;
-      const u32x2 v = {half_of(row[0], dd) | (half_of(row[1], dd) << 16),
-                       half_of(row[2], dd) | (half_of(row[3], dd) << 16)};
-      *reinterpret_cast<u32x2*>(vt_lds + vt_lds_off(d, kc)) = v;
+      const u32x2 v = {bf16_of(row[0], dd) | (bf16_of(row[1], dd) << 16),
+                       bf16_of(row[2], dd) | (bf16_of(row[3], dd) << 16)};
+      *reinterpret_cast<u32x2*>(vt_lds + dvt_off(d, kc)) = v;
     }
   }
 }
@@ -264,7 +246,7 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void sparse_attn_kernel(
   // see the output step below), and the lane's fragment base addresses.
   const int dsel = 64 * ((n >> 2) & 1) + 4 * (n >> 3) + (n & 3);
   const uint8_t* k_base = k_lds + n * kKStride + h * 16;
-  const uint8_t* v_base = vt_lds + vt_row(dsel) * kVStride + h * 16;
+  const uint8_t* v_base = vt_lds + dvt_row(dsel) * kVStride + h * 16;
   uint8_t* o_tile = o_lds + wave * 32 * kOStride;
   int64_t* orow_tile = orow_lds + wave * 32;
   const int rho = 32 * wave + n;     // this lane's row of the pass
@@ -371,7 +353,7 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void sparse_attn_kernel(
         m1 = fmaxf(m1, fmaxf(acc[mt][el + 2], acc[mt][el + 3]));
       }
     }
-    const float mb = both_halves_max(fmaxf(m0, m1)) * scale_log2;  // scale_log2 > 0
+    const float mb = halves_max(fmaxf(m0, m1)) * scale_log2;  // scale_log2 > 0
     float l0 = 0.f, l1 = 0.f;
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
@@ -389,7 +371,7 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void sparse_attn_kernel(
         pf[2 * mt + e2] = as_bf16x8(u32x4{w[0], w[1], w[2], w[3]});
       }
     }
-    const float l = both_halves_sum(l0 + l1);
+    const float l = halves_sum(l0 + l1);
     inv = out_scale * __builtin_amdgcn_rcpf(l);
     lse2 = mb + __builtin_amdgcn_logf(l);
   };
@@ -402,7 +384,7 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void sparse_attn_kernel(
       f32x16 oa = {};
 #pragma unroll
       for (int st = 0; st < 8; ++st) {
-        // row dsel + 16 dt (stored at vt_row(dsel) + 32 dt); keys
+        // row dsel + 16 dt (stored at dvt_row(dsel) + 32 dt); keys
         // 16 st + 8 h .. + 7, one 16-byte chunk in the permuted key order
         const u32x4 vf = *reinterpret_cast<const u32x4*>(v_base + 32 * dt * kVStride + 32 * st);
         oa = mfma32x32x16(as_bf16x8(vf), pf[st], oa);
