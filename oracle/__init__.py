@@ -56,7 +56,7 @@ def lib():
         L.oracle_block_scores.restype = None
         L.oracle_select.argtypes = [i64, i32, i64, i32, i32, P, P, P, P]
         L.oracle_select.restype = None
-        L.oracle_attention.argtypes = [i64, i32, i32, i32, i32, i32, i64, P, P, P, P,
+        L.oracle_attention.argtypes = [i64, i32, i32, i32, i32, i32, i32, i64, P, P, P, P,
                                        i32, f64, f64, f64, P, f64, P, P]
         L.oracle_attention.restype = None
         L.oracle_combine.argtypes = [i32, i32, i32, i32, i64, P, P, P, P, P]
@@ -149,8 +149,10 @@ def attention(N, B_k, pos, q_rows, K, V, block_idx, softmax_scale=None,
     """Sparse main attention for the given query rows, fp64.
 
     q_rows [n_rows, H_q, d_h]; K, V [N, H_kv, d_h] as raw uint16 (bf16) or
-    uint8 (fp8 e4m3) codes; block_idx [H_kv, n_rows, k].
-    Returns (O [n_rows, H_q, d_h], lse [n_rows, H_q]) in float64."""
+    uint8 (fp8 e4m3) codes; block_idx [H_sel, n_rows, k]: one selection per
+    index head, H_sel a multiple of H_kv dividing H_q (H_sel = H_kv: one per
+    GQA group).  Returns (O [n_rows, H_q, d_h], lse [n_rows, H_q]) in
+    float64."""
     st = np.uint16 if dtype == BF16 else np.uint8
     pos, pp = _c(pos, np.int64)
     q, qp = _c(q_rows, st)
@@ -159,13 +161,13 @@ def attention(N, B_k, pos, q_rows, K, V, block_idx, softmax_scale=None,
     bi, bp = _c(block_idx, np.int32)
     n_rows, H_q, d_h = q.shape
     H_kv = Kc.shape[1]
-    k = bi.shape[2]
-    assert bi.shape == (H_kv, n_rows, k)
+    H_sel, k = bi.shape[0], bi.shape[2]
+    assert bi.shape == (H_sel, n_rows, k) and H_sel % H_kv == 0 and H_q % H_sel == 0
     if softmax_scale is None:
         softmax_scale = 1.0 / np.sqrt(d_h)
     O = np.empty((n_rows, H_q, d_h), np.float64)
     lse = np.empty((n_rows, H_q), np.float64)
-    lib().oracle_attention(N, H_q, H_kv, d_h, B_k, k, n_rows, pp, qp, kp, vp, dtype,
+    lib().oracle_attention(N, H_q, H_kv, H_sel, d_h, B_k, k, n_rows, pp, qp, kp, vp, dtype,
                            float(q_scale), float(k_scale), float(v_scale), bp,
                            float(softmax_scale), O.ctypes.data_as(ctypes.c_void_p),
                            lse.ctypes.data_as(ctypes.c_void_p))

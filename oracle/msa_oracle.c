@@ -193,26 +193,31 @@ void oracle_select(int64_t n_rows, int H_kv, int64_t B, int B_k, int k,
 
 /*
  * Exact softmax attention of every query head over the causally visible
- * tokens of the row's selected blocks.  Head h uses KV head r = h / G.
+ * tokens of the row's selected blocks.  Head h uses KV head r = h / G and the
+ * selection of its index head m = h / (H_q / H_sel): H_sel index (proxy)
+ * heads each choose blocks for the adjacent query heads assigned to them
+ * ("Flash-MSA", What's next > Note about scheduler requiring proxy heads >=
+ * KV heads: an MSA group is the set of query heads of one proxy head); with
+ * H_sel = H_kv the groups are the GQA groups.
  * q_rows [n_rows][H_q][d_h]; K, V [N][H_kv][d_h] (bf16 or fp8 codes times the
- * per-tensor scale); block_idx [H_kv][n_rows][k] (-1 = empty slot).
+ * per-tensor scale); block_idx [H_sel][n_rows][k] (-1 = empty slot).
  * Output O [n_rows][H_q][d_h] and natural-log LSE [n_rows][H_q] in fp64.
  */
-void oracle_attention(int64_t N, int H_q, int H_kv, int d_h, int B_k, int k,
+void oracle_attention(int64_t N, int H_q, int H_kv, int H_sel, int d_h, int B_k, int k,
                       int64_t n_rows, const int64_t *pos, const void *q_rows,
                       const void *K, const void *V, int dtype, double q_scale,
                       double k_scale, double v_scale, const int32_t *block_idx,
                       double softmax_scale, double *O, double *lse)
 {
-    int G = H_q / H_kv;
+    int G = H_q / H_kv, Gs = H_q / H_sel;
     int64_t job;
 #pragma omp parallel for schedule(dynamic, 1)
     for (job = 0; job < n_rows * H_q; job++) {
         int64_t row = job / H_q;
         int h = (int)(job % H_q);
-        int r = h / G;
+        int r = h / G, m = h / Gs;
         int64_t i = pos[row];
-        const int32_t *sel = block_idx + ((int64_t)r * n_rows + row) * k;
+        const int32_t *sel = block_idx + ((int64_t)m * n_rows + row) * k;
         int64_t cap = (int64_t)k * B_k, nt = 0, j, t;
         int64_t *tok = malloc(sizeof(int64_t) * (size_t)cap);
         double *sc = malloc(sizeof(double) * (size_t)cap);

@@ -153,10 +153,21 @@ class Workload:
     plant: int = 0               # number of planted hot blocks (0 = none)
     plant_gain: float = 2.0
     q_chunk: int = 0             # 0 = whole sequence in one pass
+    H_idx: int = 0               # index (proxy) heads; 0 = H_kv
 
     @property
     def G(self) -> int:
         return self.H_q // self.H_kv
+
+    @property
+    def H_sel(self) -> int:
+        """Index heads = selection groups."""
+        return self.H_idx or self.H_kv
+
+    @property
+    def G_sel(self) -> int:
+        """Query heads per selection group."""
+        return self.H_q // self.H_sel
 
     @property
     def B(self) -> int:
@@ -225,7 +236,7 @@ def host_rows(w: Workload, which: str, rows) -> np.ndarray:
         "q": (TID_Q, w.H_q, w.d_h, w.dtype == "fp8"),
         "k": (TID_K, w.H_kv, w.d_h, w.dtype == "fp8"),
         "v": (TID_V, w.H_kv, w.d_h, w.dtype == "fp8"),
-        "q_idx": (TID_QIDX, w.H_kv, w.d_idx, False),
+        "q_idx": (TID_QIDX, w.H_sel, w.d_idx, False),
         "k_idx": (TID_KIDX, 1, w.d_idx, False),
     }[which]
     tid, heads, dim, fp8 = spec
@@ -292,7 +303,7 @@ def device_tensor(w: Workload, which: str, device="cuda"):
         "q": (TID_Q, w.H_q, w.d_h, w.dtype == "fp8"),
         "k": (TID_K, w.H_kv, w.d_h, w.dtype == "fp8"),
         "v": (TID_V, w.H_kv, w.d_h, w.dtype == "fp8"),
-        "q_idx": (TID_QIDX, w.H_kv, w.d_idx, False),
+        "q_idx": (TID_QIDX, w.H_sel, w.d_idx, False),
         "k_idx": (TID_KIDX, 1, w.d_idx, False),
     }[which]
     shape = (w.batch, w.N, heads, dim) if which != "k_idx" else (w.batch, w.N, dim)

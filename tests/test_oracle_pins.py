@@ -319,6 +319,32 @@ def test_attention_matches_masked_library_attention(N, Hq, Hkv, k, seed):
     np.testing.assert_allclose(lse, ref_lse, rtol=0, atol=1e-12)
 
 
+@pytest.mark.parametrize("N,Hq,Hkv,Hsel,k,seed", [(700, 8, 2, 4, 3, 31), (520, 8, 1, 8, 2, 32),
+                                                 (900, 16, 4, 8, 4, 33)])
+def test_attention_with_more_index_heads_than_kv_heads(N, Hq, Hkv, Hsel, k, seed):
+    """H_sel index heads > H_kv: head h follows the selection of index head
+    h // (Hq / Hsel) and reads K/V head h // (Hq / Hkv) (library attention with
+    a per-head block mask)."""
+    rng = np.random.default_rng(seed)
+    d, B_k = 32, 128
+    q, K, V = _make_attn_inputs(rng, N, Hq, Hkv, d)
+    bi = _rand_selection(rng, N, Hsel, B_k, k)
+    pos = np.arange(N)
+    O, lse = oracle.attention(N, B_k, pos, q, K, V, bi, softmax_scale=0.3)
+    mask = np.zeros((Hq, N, N), bool)
+    blk = np.arange(N) // B_k
+    for h in range(Hq):
+        m = h // (Hq // Hsel)
+        for i in range(N):
+            sel = bi[m, i][bi[m, i] >= 0]
+            mask[h, i] = np.isin(blk, sel) & (np.arange(N) <= i)
+    G = Hq // Hkv
+    ref, ref_lse = _sdpa_masked(_f32(q), np.repeat(_f32(K), G, axis=1),
+                                np.repeat(_f32(V), G, axis=1), mask, 0.3)
+    np.testing.assert_allclose(O, ref, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse, ref_lse, rtol=0, atol=1e-12)
+
+
 def test_attention_first_query_returns_first_value():
     rng = np.random.default_rng(14)
     N, Hq, Hkv, d, B_k, k = 300, 4, 2, 16, 128, 2
