@@ -43,11 +43,22 @@ class MSAError(RuntimeError):
 class msa_dims(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int32), ("H_q", ctypes.c_int32), ("H_kv", ctypes.c_int32),
                 ("G", ctypes.c_int32), ("d_h", ctypes.c_int32), ("d_idx", ctypes.c_int32),
-                ("B_k", ctypes.c_int32), ("k", ctypes.c_int32), ("N", ctypes.c_int64)]
+                ("B_k", ctypes.c_int32), ("k", ctypes.c_int32), ("N", ctypes.c_int64),
+                ("H_idx", ctypes.c_int32)]
 
     @property
     def B(self) -> int:
         return -(-self.N // self.B_k)
+
+    @property
+    def H_sel(self) -> int:
+        """Selection groups (index heads)."""
+        return self.H_idx or self.H_kv
+
+    @property
+    def G_sel(self) -> int:
+        """Query heads per selection group."""
+        return self.H_q // self.H_sel
 
 
 class msa_opts(ctypes.Structure):
@@ -57,9 +68,9 @@ class msa_opts(ctypes.Structure):
                 ("q_chunk", ctypes.c_int64)]
 
 
-def make_dims(batch, N, H_q, H_kv, d_h, d_idx, B_k, k) -> msa_dims:
+def make_dims(batch, N, H_q, H_kv, d_h, d_idx, B_k, k, H_idx=0) -> msa_dims:
     return msa_dims(batch=batch, H_q=H_q, H_kv=H_kv, G=H_q // H_kv if H_kv else 0, d_h=d_h,
-                    d_idx=d_idx, B_k=B_k, k=k, N=N)
+                    d_idx=d_idx, B_k=B_k, k=k, N=N, H_idx=H_idx)
 
 
 def make_opts(dtype: str = "bf16", softmax_scale: float = 0.0, q_scale: float = 1.0,
@@ -143,11 +154,11 @@ def _empty(shape, dtype, like):
 
 def msa_index_topk(dims: msa_dims, q_idx, k_idx, q_begin: int = 0, q_count: Optional[int] = None,
                    block_idx=None):
-    """Index branch.  Returns block_idx int32 [batch, H_kv, q_count, k]."""
+    """Index branch.  Returns block_idx int32 [batch, H_sel, q_count, k]."""
     import torch
     q_count = dims.N - q_begin if q_count is None else q_count
     if block_idx is None:
-        block_idx = _empty((dims.batch, dims.H_kv, q_count, dims.k), torch.int32, q_idx)
+        block_idx = _empty((dims.batch, dims.H_sel, q_count, dims.k), torch.int32, q_idx)
     with _dev(q_idx):
         _check(lib().msa_index_topk(ctypes.byref(dims), _p(q_idx), _p(k_idx), q_begin, q_count,
                                     _p(block_idx), _stream(q_idx)), "msa_index_topk")
@@ -160,7 +171,7 @@ def msa_index_topk_forced(dims: msa_dims, q_idx, k_idx, force_first: bool = True
     import torch
     q_count = dims.N - q_begin if q_count is None else q_count
     if block_idx is None:
-        block_idx = _empty((dims.batch, dims.H_kv, q_count, dims.k), torch.int32, q_idx)
+        block_idx = _empty((dims.batch, dims.H_sel, q_count, dims.k), torch.int32, q_idx)
     with _dev(q_idx):
         _check(lib().msa_index_topk_forced(ctypes.byref(dims), _p(q_idx), _p(k_idx), q_begin, q_count,
                                            int(force_first), int(local_window), _p(block_idx),
@@ -170,11 +181,11 @@ def msa_index_topk_forced(dims: msa_dims, q_idx, k_idx, force_first: bool = True
 
 def msa_window_select(dims: msa_dims, q_begin: int = 0, q_count: Optional[int] = None, block_idx=None,
                       device=None):
-    """FLOP-matched sliding-window selection int32 [batch, H_kv, q_count, k]."""
+    """FLOP-matched sliding-window selection int32 [batch, H_sel, q_count, k]."""
     import torch
     q_count = dims.N - q_begin if q_count is None else q_count
     if block_idx is None:
-        block_idx = torch.empty((dims.batch, dims.H_kv, q_count, dims.k), dtype=torch.int32,
+        block_idx = torch.empty((dims.batch, dims.H_sel, q_count, dims.k), dtype=torch.int32,
                                 device=device or "cuda")
     with _dev(block_idx):
         _check(lib().msa_window_select(ctypes.byref(dims), q_begin, q_count, _p(block_idx),
@@ -196,9 +207,9 @@ def msa_invert_blocks(dims: msa_dims, block_idx, q_begin: int = 0, q_count: Opti
     q_count = dims.N - q_begin if q_count is None else q_count
     B_c = -(-(q_begin + q_count) // dims.B_k)
     if blk_offsets is None:
-        blk_offsets = _empty((dims.batch, dims.H_kv, B_c + 1), torch.int32, block_idx)
+        blk_offsets = _empty((dims.batch, dims.H_sel, B_c + 1), torch.int32, block_idx)
     if blk_entries is None:
-        blk_entries = _empty((dims.batch * dims.H_kv * q_count * dims.k,), torch.int32, block_idx)
+        blk_entries = _empty((dims.batch * dims.H_sel * q_count * dims.k,), torch.int32, block_idx)
     nbytes = msa_invert_workspace_size(dims, q_begin, q_count)
     if sched is None:
         sched = _empty(((nbytes + 3) // 4,), torch.int32, block_idx)
@@ -222,11 +233,11 @@ def msa_invert_status(sched) -> int:
 def msa_sparse_attn_fwd(dims: msa_dims, opts: msa_opts, q, k, v, blk_offsets, blk_entries, sched,
                         q_begin: int = 0, q_count: Optional[int] = None, o_part=None,
                         lse_part=None):
-    """KV-outer sparse attention.  Returns (o_part bf16 [batch, H_kv, q_count, k, G, d_h],
-    lse_part fp32 [batch, H_kv, q_count, k, G])."""
+    """KV-outer sparse attention.  Returns (o_part bf16 [batch, H_sel, q_count, k, G_sel, d_h],
+    lse_part fp32 [batch, H_sel, q_count, k, G_sel])."""
     import torch
     q_count = dims.N - q_begin if q_count is None else q_count
-    shp = (dims.batch, dims.H_kv, q_count, dims.k, dims.G)
+    shp = (dims.batch, dims.H_sel, q_count, dims.k, dims.G_sel)
     if o_part is None:
         o_part = _empty(shp + (dims.d_h,), torch.bfloat16, q)
     if lse_part is None:
@@ -308,7 +319,7 @@ def msa_decode_workspace_size(dims: msa_dims, opts: msa_opts) -> int:
 def msa_decode(dims: msa_dims, opts: msa_opts, q, q_idx, k, v, k_idx, o=None, lse=None,
                block_idx_out=None, workspace=None, want_lse: bool = False):
     """One decode step (the token at position N - 1 of each sequence).
-    q [batch, H_q, d_h], q_idx [batch, H_kv, d_idx]; caches as for msa_forward.
+    q [batch, H_q, d_h], q_idx [batch, H_sel, d_idx]; caches as for msa_forward.
     Returns (o bf16 [batch, H_q, d_h], lse fp32 [batch, H_q] or None, block_idx_out)."""
     import torch
     if o is None:

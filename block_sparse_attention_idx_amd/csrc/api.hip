@@ -19,6 +19,17 @@ int hip_fail(hipError_t e) {
 
 bool misaligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
 
+// Selection groups: one per index (proxy) head, each the adjacent
+// H_q / H_sel query heads; H_idx = 0 makes them the GQA groups.
+int HS(const msa_dims* d) { return d->H_idx > 0 ? d->H_idx : d->H_kv; }
+int GS(const msa_dims* d) { return d->H_q / HS(d); }
+// log2 of H_sel / H_kv (= G / G_sel, a ratio of powers of two)
+int KVS(const msa_dims* d) {
+  int s = 0;
+  while ((d->H_kv << s) < HS(d)) ++s;
+  return s;
+}
+
 int check_dims(const msa_dims* d) {
   if (!d) return MSA_ERR_NULL;
   if (d->batch < 1 || d->N < 1 || d->H_kv < 1 || d->G < 1 || d->H_q < 1 || d->k < 1 ||
@@ -29,6 +40,12 @@ int check_dims(const msa_dims* d) {
   if (d->d_idx != 64 && d->d_idx != 128) return MSA_ERR_UNSUPPORTED;
   if (d->G != 1 && d->G != 2 && d->G != 4 && d->G != 8 && d->G != 16) return MSA_ERR_UNSUPPORTED;
   if (d->k > 32) return MSA_ERR_UNSUPPORTED;
+  if (d->H_idx < 0) return MSA_ERR_SHAPE;
+  if (d->H_idx > 0) {
+    if (d->H_idx % d->H_kv != 0 || d->H_q % d->H_idx != 0) return MSA_ERR_SHAPE;
+    const int gs = d->H_q / d->H_idx;
+    if (gs != 1 && gs != 2 && gs != 4 && gs != 8 && gs != 16) return MSA_ERR_UNSUPPORTED;
+  }
   if ((d->N + d->B_k - 1) / d->B_k > 16384) return MSA_ERR_UNSUPPORTED;
   return MSA_OK;
 }
@@ -36,7 +53,7 @@ int check_dims(const msa_dims* d) {
 int check_range(const msa_dims* d, int64_t q_begin, int64_t q_count) {
   if (q_begin < 0 || q_count < 1 || q_begin > d->N || q_count > d->N - q_begin) return MSA_ERR_SHAPE;
   if (q_begin % d->B_k != 0) return MSA_ERR_SHAPE;
-  const int64_t slots = static_cast<int64_t>(d->batch) * d->H_kv * q_count * d->k;
+  const int64_t slots = static_cast<int64_t>(d->batch) * HS(d) * q_count * d->k;
   if (slots >= (int64_t(1) << 31)) return MSA_ERR_UNSUPPORTED;
   return MSA_OK;
 }
@@ -78,7 +95,7 @@ struct ForwardLayout {
 ForwardLayout forward_layout(const msa_dims* d, const msa_opts* o) {
   ForwardLayout L{};
   L.qc = o->q_chunk > 0 ? (o->q_chunk < d->N ? o->q_chunk : d->N) : d->N;
-  const int64_t seqs = static_cast<int64_t>(d->batch) * d->H_kv;
+  const int64_t seqs = static_cast<int64_t>(d->batch) * HS(d);
   const int64_t B = (d->N + d->B_k - 1) / d->B_k;
   const size_t slots = static_cast<size_t>(seqs) * L.qc * d->k;
   // the largest scratch is needed by the last (or the only) full-size chunk
@@ -86,7 +103,7 @@ ForwardLayout forward_layout(const msa_dims* d, const msa_opts* o) {
   const int64_t nchunks = (d->N + L.qc - 1) / L.qc;
   for (int64_t c = (nchunks > 2 ? nchunks - 2 : 0); c < nchunks; ++c) {
     const int64_t qb = c * L.qc, qn = (d->N - qb) < L.qc ? (d->N - qb) : L.qc;
-    const msa::SchedLayout s = msa::sched_layout(d->batch, d->H_kv, d->G, d->k, qb, qn);
+    const msa::SchedLayout s = msa::sched_layout(d->batch, HS(d), GS(d), d->k, qb, qn);
     words = s.words > words ? s.words : words;
   }
   size_t off = 0;
@@ -99,9 +116,9 @@ ForwardLayout forward_layout(const msa_dims* d, const msa_opts* o) {
   L.off_sched = off;
   off += align256(static_cast<size_t>(words) * 4);
   L.off_opart = off;
-  off += align256(slots * d->G * d->d_h * 2);
+  off += align256(slots * GS(d) * d->d_h * 2);
   L.off_lpart = off;
-  off += align256(slots * d->G * 4);
+  off += align256(slots * GS(d) * 4);
   L.total = off;
   return L;
 }
@@ -136,7 +153,7 @@ int msa_index_topk(const msa_dims* dims, const void* q_idx, const void* k_idx, i
   if (misaligned(q_idx) || misaligned(k_idx) || misaligned(block_idx)) return MSA_ERR_ALIGN;
   hipError_t e = msa::launch_index_topk(static_cast<const uint16_t*>(q_idx),
                                         static_cast<const uint16_t*>(k_idx), dims->batch, dims->N,
-                                        dims->H_kv, dims->d_idx, dims->k, q_begin, q_count,
+                                        HS(dims), dims->d_idx, dims->k, q_begin, q_count,
                                         block_idx, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? MSA_OK : hip_fail(e);
 }
@@ -153,7 +170,7 @@ int msa_index_topk_forced(const msa_dims* dims, const void* q_idx, const void* k
   if (misaligned(q_idx) || misaligned(k_idx) || misaligned(block_idx)) return MSA_ERR_ALIGN;
   hipError_t e = msa::launch_index_topk(static_cast<const uint16_t*>(q_idx),
                                         static_cast<const uint16_t*>(k_idx), dims->batch, dims->N,
-                                        dims->H_kv, dims->d_idx, dims->k, q_begin, q_count,
+                                        HS(dims), dims->d_idx, dims->k, q_begin, q_count,
                                         block_idx, static_cast<hipStream_t>(stream), force_first,
                                         local_window);
   return e == hipSuccess ? MSA_OK : hip_fail(e);
@@ -166,7 +183,7 @@ int msa_window_select(const msa_dims* dims, int64_t q_begin, int64_t q_count, in
   if ((st = check_range(dims, q_begin, q_count))) return st;
   if (!block_idx) return MSA_ERR_NULL;
   if (misaligned(block_idx)) return MSA_ERR_ALIGN;
-  hipError_t e = msa::launch_window_select(dims->batch, dims->H_kv, dims->k, q_begin, q_count, block_idx,
+  hipError_t e = msa::launch_window_select(dims->batch, HS(dims), dims->k, q_begin, q_count, block_idx,
                                            static_cast<hipStream_t>(stream));
   return e == hipSuccess ? MSA_OK : hip_fail(e);
 }
@@ -177,7 +194,7 @@ int msa_invert_workspace_size(const msa_dims* dims, int64_t q_begin, int64_t q_c
   if (st) return st;
   if ((st = check_range(dims, q_begin, q_count))) return st;
   if (!bytes) return MSA_ERR_NULL;
-  const msa::SchedLayout s = msa::sched_layout(dims->batch, dims->H_kv, dims->G, dims->k, q_begin, q_count);
+  const msa::SchedLayout s = msa::sched_layout(dims->batch, HS(dims), GS(dims), dims->k, q_begin, q_count);
   *bytes = static_cast<size_t>(s.words) * 4;
   return MSA_OK;
 }
@@ -192,9 +209,9 @@ int msa_invert_blocks(const msa_dims* dims, const int32_t* block_idx, int64_t q_
   if (misaligned(block_idx) || misaligned(blk_offsets) || misaligned(blk_entries) ||
       misaligned(sched))
     return MSA_ERR_ALIGN;
-  const msa::SchedLayout s = msa::sched_layout(dims->batch, dims->H_kv, dims->G, dims->k, q_begin, q_count);
+  const msa::SchedLayout s = msa::sched_layout(dims->batch, HS(dims), GS(dims), dims->k, q_begin, q_count);
   if (sched_bytes < static_cast<size_t>(s.words) * 4) return MSA_ERR_WORKSPACE;
-  hipError_t e = msa::launch_invert(block_idx, dims->batch, dims->H_kv, dims->G, dims->k, q_begin,
+  hipError_t e = msa::launch_invert(block_idx, dims->batch, HS(dims), GS(dims), dims->k, q_begin,
                                     q_count, blk_offsets, blk_entries, static_cast<int32_t*>(sched),
                                     static_cast<hipStream_t>(stream));
   return e == hipSuccess ? MSA_OK : hip_fail(e);
@@ -226,8 +243,8 @@ int msa_sparse_attn_fwd(const msa_dims* dims, const msa_opts* opts, const void* 
   float sl2, osc;
   attn_scales(dims, opts, &sl2, &osc);
   hipError_t e = msa::launch_sparse_attn(
-      q, k, v, opts->qkv_dtype == MSA_DTYPE_FP8_E4M3, dims->batch, dims->N, dims->H_kv, dims->G,
-      dims->k, sl2, osc, blk_offsets, blk_entries, static_cast<const int32_t*>(sched), q_begin,
+      q, k, v, opts->qkv_dtype == MSA_DTYPE_FP8_E4M3, dims->batch, dims->N, HS(dims), GS(dims),
+      KVS(dims), dims->k, sl2, osc, blk_offsets, blk_entries, static_cast<const int32_t*>(sched), q_begin,
       q_count, static_cast<uint16_t*>(o_part), lse_part, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? MSA_OK : hip_fail(e);
 }
@@ -243,7 +260,7 @@ int msa_combine(const msa_dims* dims, const int32_t* block_idx, const void* o_pa
       (lse && misaligned(lse)))
     return MSA_ERR_ALIGN;
   hipError_t e = msa::launch_combine(block_idx, static_cast<const uint16_t*>(o_part), lse_part,
-                                     dims->batch, dims->N, dims->H_kv, dims->G, dims->k, q_begin,
+                                     dims->batch, dims->N, HS(dims), GS(dims), dims->k, q_begin,
                                      q_count, static_cast<uint16_t*>(o), lse,
                                      static_cast<hipStream_t>(stream));
   return e == hipSuccess ? MSA_OK : hip_fail(e);
@@ -285,7 +302,7 @@ struct DecodeLayout {
 
 DecodeLayout decode_layout(const msa_dims* d) {
   DecodeLayout L{};
-  const size_t seqs = static_cast<size_t>(d->batch) * d->H_kv;
+  const size_t seqs = static_cast<size_t>(d->batch) * HS(d);
   const size_t B = static_cast<size_t>((d->N + d->B_k - 1) / d->B_k);
   size_t off = 0;
   L.off_scores = off;
@@ -293,9 +310,9 @@ DecodeLayout decode_layout(const msa_dims* d) {
   L.off_bi = off;
   off += align256(seqs * d->k * 4);
   L.off_opart = off;
-  off += align256(seqs * d->k * d->G * d->d_h * 2);
+  off += align256(seqs * d->k * GS(d) * d->d_h * 2);
   L.off_lpart = off;
-  off += align256(seqs * d->k * d->G * 4);
+  off += align256(seqs * d->k * GS(d) * 4);
   L.total = off;
   return L;
 }
@@ -306,7 +323,7 @@ int check_decode(const msa_dims* d, const msa_opts* o) {
   if (!o) return MSA_ERR_NULL;
   if (o->reserved != 0 || !isfinite(o->softmax_scale)) return MSA_ERR_SHAPE;
   if (o->qkv_dtype != MSA_DTYPE_BF16) return MSA_ERR_UNSUPPORTED;
-  if (d->H_kv > 32 || d->batch > 65535) return MSA_ERR_UNSUPPORTED;
+  if (HS(d) > 32 || d->batch > 65535) return MSA_ERR_UNSUPPORTED;
   return MSA_OK;
 }
 
@@ -338,8 +355,8 @@ int msa_decode(const msa_dims* dims, const msa_opts* opts, const void* q, const 
   int32_t* bi = block_idx_out ? block_idx_out : reinterpret_cast<int32_t*>(ws + L.off_bi);
   hipError_t e = msa::launch_decode(
       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(q_idx), static_cast<const uint16_t*>(k),
-      static_cast<const uint16_t*>(v), static_cast<const uint16_t*>(k_idx), dims->batch, dims->N, dims->H_kv,
-      dims->G, dims->d_idx, dims->k, sl2, reinterpret_cast<float*>(ws + L.off_scores), bi,
+      static_cast<const uint16_t*>(v), static_cast<const uint16_t*>(k_idx), dims->batch, dims->N, HS(dims),
+      GS(dims), KVS(dims), dims->d_idx, dims->k, sl2, reinterpret_cast<float*>(ws + L.off_scores), bi,
       reinterpret_cast<uint16_t*>(ws + L.off_opart), reinterpret_cast<float*>(ws + L.off_lpart),
       static_cast<uint16_t*>(o), lse, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? MSA_OK : hip_fail(e);
@@ -383,21 +400,22 @@ int msa_forward(const msa_dims* dims, const msa_opts* opts, const void* q, const
   attn_scales(dims, opts, &sl2, &osc);
   const bool fp8 = opts->qkv_dtype == MSA_DTYPE_FP8_E4M3;
   const bool one_chunk = L.qc >= dims->N;
-  const int64_t seqs = static_cast<int64_t>(dims->batch) * dims->H_kv;
+  const int64_t seqs = static_cast<int64_t>(dims->batch) * HS(dims);
 
   for (int64_t qb = 0; qb < dims->N; qb += L.qc) {
     const int64_t qn = (dims->N - qb) < L.qc ? (dims->N - qb) : L.qc;
     int32_t* bi = (one_chunk && block_idx_out) ? block_idx_out : bi_chunk;
     hipError_t e = msa::launch_index_topk(static_cast<const uint16_t*>(q_idx),
                                           static_cast<const uint16_t*>(k_idx), dims->batch, dims->N,
-                                          dims->H_kv, dims->d_idx, dims->k, qb, qn, bi, s);
+                                          HS(dims), dims->d_idx, dims->k, qb, qn, bi, s);
     if (e != hipSuccess) return hip_fail(e);
-    e = msa::launch_invert(bi, dims->batch, dims->H_kv, dims->G, dims->k, qb, qn, offs, ents, sched, s);
+    e = msa::launch_invert(bi, dims->batch, HS(dims), GS(dims), dims->k, qb, qn, offs, ents, sched, s);
     if (e != hipSuccess) return hip_fail(e);
-    e = msa::launch_sparse_attn(q, k, v, fp8, dims->batch, dims->N, dims->H_kv, dims->G, dims->k,
+    e = msa::launch_sparse_attn(q, k, v, fp8, dims->batch, dims->N, HS(dims), GS(dims),
+                                KVS(dims), dims->k,
                                 sl2, osc, offs, ents, sched, qb, qn, opart, lpart, s);
     if (e != hipSuccess) return hip_fail(e);
-    e = msa::launch_combine(bi, opart, lpart, dims->batch, dims->N, dims->H_kv, dims->G, dims->k,
+    e = msa::launch_combine(bi, opart, lpart, dims->batch, dims->N, HS(dims), GS(dims), dims->k,
                             qb, qn, static_cast<uint16_t*>(o), lse, s);
     if (e != hipSuccess) return hip_fail(e);
     if (block_idx_out && !one_chunk) {

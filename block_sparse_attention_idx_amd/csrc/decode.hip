@@ -23,11 +23,11 @@
 // branch reads k blocks of K and V per group.
 //  * Scores: waves stride over the (sequence, block) pairs; a wave scores one
 //    block for all groups at once with v_mfma_f32_32x32x16_bf16 (keys on the
-//    row dimension, the H_kv <= 32 index query heads on the columns), the
+//    row dimension, the H_sel <= 32 index query heads on the columns), the
 //    block's K^idx fragments loaded straight from memory, all 32 KB requested
 //    before the first MFMA (each 256-byte row is read by two lanes, 16 bytes
 //    per step); the block max is an in-lane max plus one half-wave exchange.
-//    Block scores go to a small fp32 buffer [batch][H_kv][B].
+//    Block scores go to a small fp32 buffer [batch][H_sel][B].
 //  * Top-k: one workgroup per (sequence, group); each thread keeps the best
 //    (score, block) keys of its strided share in VGPRs, then the lists are
 //    merged pairwise (a bitonic merge in registers per round, the partner
@@ -57,7 +57,7 @@ __device__ __forceinline__ uint32_t ord_score(float x) {
 
 template <int DIDX>
 __global__ __launch_bounds__(64 * kScoreWaves) void decode_scores_kernel(
-    const uint16_t* __restrict__ q_idx, const uint16_t* __restrict__ k_idx, int64_t N, int H_kv,
+    const uint16_t* __restrict__ q_idx, const uint16_t* __restrict__ k_idx, int64_t N, int H_sel,
     int L, int B, int batch, float* __restrict__ scores) {
   constexpr int STEPS = DIDX / 16;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -78,13 +78,13 @@ __global__ __launch_bounds__(64 * kScoreWaves) void decode_scores_kernel(
       for (int ks = 0; ks < STEPS; ++ks)
         kf[mt][ks] = *reinterpret_cast<const u32x4*>(kb + 32 * mt * DIDX + 16 * ks);
     }
-    // B operand: column n = index query head n (zero past H_kv).
-    const uint16_t* qrow = q_idx + (static_cast<int64_t>(bat) * H_kv + min(n, H_kv - 1)) * DIDX;
+    // B operand: column n = index query head n (zero past H_sel).
+    const uint16_t* qrow = q_idx + (static_cast<int64_t>(bat) * H_sel + min(n, H_sel - 1)) * DIDX;
     bf16x8 qf[STEPS];
 #pragma unroll
     for (int ks = 0; ks < STEPS; ++ks) {
       const u32x4 w = *reinterpret_cast<const u32x4*>(qrow + 16 * ks + 8 * h);
-      qf[ks] = as_bf16x8(n < H_kv ? w : u32x4{0u, 0u, 0u, 0u});
+      qf[ks] = as_bf16x8(n < H_sel ? w : u32x4{0u, 0u, 0u, 0u});
     }
     float mx = -__builtin_huge_valf();
 #pragma unroll
@@ -96,7 +96,7 @@ __global__ __launch_bounds__(64 * kScoreWaves) void decode_scores_kernel(
       for (int e = 0; e < 16; ++e) mx = fmaxf(mx, acc[e]);
     }
     mx = halves_max(mx);
-    if (h == 0 && n < H_kv) scores[(static_cast<int64_t>(bat) * H_kv + n) * B + blk] = mx;
+    if (h == 0 && n < H_sel) scores[(static_cast<int64_t>(bat) * H_sel + n) * B + blk] = mx;
   }
 }
 
@@ -132,7 +132,7 @@ __global__ __launch_bounds__(topk_threads<KP>()) void decode_topk_kernel(const f
                                                                          int32_t* __restrict__ block_idx) {
   constexpr int kTopkThreads = topk_threads<KP>();
   __shared__ uint64_t lists[KP * kTopkThreads / 2];
-  const int seq = blockIdx.x;  // batch * H_kv + r
+  const int seq = blockIdx.x;  // batch * H_sel + r
   const int t = threadIdx.x;
   const float* row = scores + static_cast<int64_t>(seq) * B;
 
@@ -216,18 +216,19 @@ __global__ __launch_bounds__(topk_threads<KP>()) void decode_topk_kernel(const f
 template <int G>
 __global__ __launch_bounds__(kStageThreads, 1) void decode_partial_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-    int64_t N, int H_kv, int kslots, float scale_log2, const int32_t* __restrict__ block_idx,
+    int64_t N, int H_sel, int kv_shift, int kslots, float scale_log2, const int32_t* __restrict__ block_idx,
     uint16_t* __restrict__ o_part, float* __restrict__ lse_part) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[kBufBytes];
   const int64_t item = blockIdx.x;  // (seq, slot)
   const int64_t seq = item / kslots;
   const int blk = block_idx[item];
   if (blk < 0) return;  // uniform: empty slot, skipped by the combine
-  const int bat = static_cast<int>(seq / H_kv), r = static_cast<int>(seq % H_kv);
+  const int bat = static_cast<int>(seq / H_sel), r = static_cast<int>(seq % H_sel);
+  const int H_kv = H_sel >> kv_shift;  // selection group r reads K/V head r >> kv_shift
   const int tid = threadIdx.x;
   const int nvalid = static_cast<int>(min<int64_t>(kBk, N - static_cast<int64_t>(blk) * kBk));
   const int64_t rstride = static_cast<int64_t>(H_kv) * kDh * 2;
-  const int64_t row0 = (static_cast<int64_t>(bat) * N + static_cast<int64_t>(blk) * kBk) * H_kv + r;
+  const int64_t row0 = (static_cast<int64_t>(bat) * N + static_cast<int64_t>(blk) * kBk) * H_kv + (r >> kv_shift);
   KVRegs R;
   kv_load(R, reinterpret_cast<const uint8_t*>(k) + row0 * kDh * 2,
           reinterpret_cast<const uint8_t*>(v) + row0 * kDh * 2, rstride, nvalid, tid);
@@ -236,7 +237,7 @@ __global__ __launch_bounds__(kStageThreads, 1) void decode_partial_kernel(
   if (tid >= 64) return;  // one wave computes (no barrier follows)
 
   const int lane = tid, n = lane & 31, h = lane >> 5;
-  const int H_q = H_kv * G;
+  const int H_q = H_sel * G;
   // B operand: column n = head r G + n (zero past G).
   const uint16_t* qrow = q + (static_cast<int64_t>(bat) * H_q + r * G + min(n, G - 1)) * kDh;
   u32x4 qf[8];
@@ -327,24 +328,24 @@ hipError_t launch_topk(const float* scores, int nseq, int L, int B, int k, int32
 
 template <int G>
 hipError_t launch_partial(const uint16_t* q, const uint16_t* k, const uint16_t* v, int batch, int64_t N,
-                          int H_kv, int kslots, float scale_log2, const int32_t* block_idx,
+                          int H_sel, int kv_shift, int kslots, float scale_log2, const int32_t* block_idx,
                           uint16_t* o_part, float* lse_part, hipStream_t stream) {
-  const int64_t items = static_cast<int64_t>(batch) * H_kv * kslots;
+  const int64_t items = static_cast<int64_t>(batch) * H_sel * kslots;
   hipLaunchKernelGGL(decode_partial_kernel<G>, dim3(static_cast<unsigned>(items)), dim3(kStageThreads), 0,
-                     stream, q, k, v, N, H_kv, kslots, scale_log2, block_idx, o_part, lse_part);
+                     stream, q, k, v, N, H_sel, kv_shift, kslots, scale_log2, block_idx, o_part, lse_part);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_decode(const uint16_t* q, const uint16_t* q_idx, const uint16_t* k, const uint16_t* v,
-                         const uint16_t* k_idx, int batch, int64_t N, int H_kv, int G, int d_idx,
+                         const uint16_t* k_idx, int batch, int64_t N, int H_sel, int G, int kv_shift, int d_idx,
                          int kslots, float scale_log2, float* scores, int32_t* block_idx,
                          uint16_t* o_part, float* lse_part, uint16_t* o, float* lse,
                          hipStream_t stream) {
   const int B = static_cast<int>((N + kBk - 1) / kBk);
   const int L = static_cast<int>((N - 1) / kBk);  // the local block; blocks 0 .. L - 1 are scored
-  const int nseq = batch * H_kv;
+  const int nseq = batch * H_sel;
   hipError_t e = hipSuccess;
   if (L > 0) {
     // A few waves per SIMD, each striding over many blocks.
@@ -353,10 +354,10 @@ hipError_t launch_decode(const uint16_t* q, const uint16_t* q_idx, const uint16_
     if (wgs > 1024) wgs = 1024;
     if (d_idx == 64)
       hipLaunchKernelGGL(decode_scores_kernel<64>, dim3(static_cast<unsigned>(wgs)), dim3(64 * kScoreWaves), 0,
-                         stream, q_idx, k_idx, N, H_kv, L, B, batch, scores);
+                         stream, q_idx, k_idx, N, H_sel, L, B, batch, scores);
     else
       hipLaunchKernelGGL(decode_scores_kernel<128>, dim3(static_cast<unsigned>(wgs)), dim3(64 * kScoreWaves), 0,
-                         stream, q_idx, k_idx, N, H_kv, L, B, batch, scores);
+                         stream, q_idx, k_idx, N, H_sel, L, B, batch, scores);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   const int km = kslots - 1;
@@ -368,16 +369,16 @@ hipError_t launch_decode(const uint16_t* q, const uint16_t* q_idx, const uint16_
   else e = launch_topk<32>(scores, nseq, L, B, kslots, block_idx, stream);
   if (e != hipSuccess) return e;
   switch (G) {
-    case 1: e = launch_partial<1>(q, k, v, batch, N, H_kv, kslots, scale_log2, block_idx, o_part, lse_part, stream); break;
-    case 2: e = launch_partial<2>(q, k, v, batch, N, H_kv, kslots, scale_log2, block_idx, o_part, lse_part, stream); break;
-    case 4: e = launch_partial<4>(q, k, v, batch, N, H_kv, kslots, scale_log2, block_idx, o_part, lse_part, stream); break;
-    case 8: e = launch_partial<8>(q, k, v, batch, N, H_kv, kslots, scale_log2, block_idx, o_part, lse_part, stream); break;
-    case 16: e = launch_partial<16>(q, k, v, batch, N, H_kv, kslots, scale_log2, block_idx, o_part, lse_part, stream); break;
+    case 1: e = launch_partial<1>(q, k, v, batch, N, H_sel, kv_shift, kslots, scale_log2, block_idx, o_part, lse_part, stream); break;
+    case 2: e = launch_partial<2>(q, k, v, batch, N, H_sel, kv_shift, kslots, scale_log2, block_idx, o_part, lse_part, stream); break;
+    case 4: e = launch_partial<4>(q, k, v, batch, N, H_sel, kv_shift, kslots, scale_log2, block_idx, o_part, lse_part, stream); break;
+    case 8: e = launch_partial<8>(q, k, v, batch, N, H_sel, kv_shift, kslots, scale_log2, block_idx, o_part, lse_part, stream); break;
+    case 16: e = launch_partial<16>(q, k, v, batch, N, H_sel, kv_shift, kslots, scale_log2, block_idx, o_part, lse_part, stream); break;
     default: return hipErrorInvalidValue;
   }
   if (e != hipSuccess) return e;
   // One query row per sequence: the combine's output rows [batch][1][H_q].
-  return launch_combine(block_idx, o_part, lse_part, batch, 1, H_kv, G, kslots, 0, 1, o, lse, stream);
+  return launch_combine(block_idx, o_part, lse_part, batch, 1, H_sel, G, kslots, 0, 1, o, lse, stream);
 }
 
 }  // namespace msa

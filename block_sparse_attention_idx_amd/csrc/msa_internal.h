@@ -147,8 +147,10 @@ hipError_t launch_invert(const int32_t* block_idx, int batch, int H_kv, int G, i
 // dividends): n / d == umulhi(n, magic) >> shift for d >= 2.
 void kdiv_params(int d, uint32_t* magic, int* shift);
 
+// H_sel selection groups of G query heads each; group r reads K/V head
+// r >> kv_shift (H_kv = H_sel >> kv_shift: the ratio is a power of two).
 hipError_t launch_sparse_attn(const void* q, const void* k, const void* v, bool fp8, int batch,
-                              int64_t N, int H_kv, int G, int kslots, float scale_log2,
+                              int64_t N, int H_sel, int G, int kv_shift, int kslots, float scale_log2,
                               float out_scale, const int32_t* blk_offsets,
                               const int32_t* blk_entries, const int32_t* sched, int64_t q_begin,
                               int64_t q_count, uint16_t* o_part, float* lse_part,
@@ -165,12 +167,14 @@ hipError_t launch_dense_attn(const uint16_t* q, const uint16_t* k, const uint16_
                              float scale_log2, uint16_t* o, float* lse, hipStream_t stream);
 
 // Decode: one query (position N - 1) per sequence against cached K, V, K^idx.
-// q [batch][H_q][d_h], q_idx [batch][H_kv][d_idx], caches as for the prefill;
-// scores [batch][H_kv][ceil(N / B_k)] fp32, block_idx [batch][H_kv][k],
-// o_part [batch][H_kv][k][G][d_h], lse_part [batch][H_kv][k][G] are scratch
-// (block_idx is also an output); o [batch][H_q][d_h], lse [batch][H_q] or null.
+// H_sel selection groups (index heads) of G query heads, group r reading K/V
+// head r >> kv_shift.  q [batch][H_q][d_h], q_idx [batch][H_sel][d_idx],
+// caches as for the prefill; scores [batch][H_sel][ceil(N / B_k)] fp32,
+// block_idx [batch][H_sel][k], o_part [batch][H_sel][k][G][d_h],
+// lse_part [batch][H_sel][k][G] are scratch (block_idx is also an output);
+// o [batch][H_q][d_h], lse [batch][H_q] or null.
 hipError_t launch_decode(const uint16_t* q, const uint16_t* q_idx, const uint16_t* k, const uint16_t* v,
-                         const uint16_t* k_idx, int batch, int64_t N, int H_kv, int G, int d_idx,
+                         const uint16_t* k_idx, int batch, int64_t N, int H_sel, int G, int kv_shift, int d_idx,
                          int kslots, float scale_log2, float* scores, int32_t* block_idx,
                          uint16_t* o_part, float* lse_part, uint16_t* o, float* lse,
                          hipStream_t stream);

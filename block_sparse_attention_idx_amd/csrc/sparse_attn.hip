@@ -205,7 +205,7 @@ struct QFrag<true> {
 template <int G, bool FP8>
 __global__ __launch_bounds__(kThreads, 8 / kWaves) void sparse_attn_kernel(
     const void* __restrict__ qp, const void* __restrict__ kp, const void* __restrict__ vp,
-    int64_t N, int H_kv, int kslots, uint32_t kdiv_magic, int kdiv_shift, float scale_log2,
+    int64_t N, int H_sel, int kv_shift, int kslots, uint32_t kdiv_magic, int kdiv_shift, float scale_log2,
     float out_scale, const int32_t* __restrict__ entries, const int32_t* __restrict__ segp,
     const PassDesc* __restrict__ passes, int B_c, int npairs, int q_begin, int q_count,
     uint16_t* __restrict__ o_part, float* __restrict__ lse_part) {
@@ -240,7 +240,7 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void sparse_attn_kernel(
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   const int n = lane & 31, h = lane >> 5;
-  const int H_q = H_kv * G;
+  const int H_q = H_sel * G;
 
   // Output dimension of V^T operand row n in d-tile 0 (d-tile dt adds 16 dt;
   // see the output step below), and the lane's fragment base addresses.
@@ -270,7 +270,7 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void sparse_attn_kernel(
     const uint32_t slot = ent - qrow * static_cast<uint32_t>(kslots);
     rr.i = q_begin + static_cast<int>(qrow);
     rr.orow = ((static_cast<int64_t>(seq) * q_count + qrow) * kslots + slot) * G + g_row;
-    const int bat = seq / H_kv, r = seq - bat * H_kv;
+    const int bat = seq / H_sel, r = seq - bat * H_sel;
     rr.q = static_cast<const uint8_t*>(qp) +
            ((static_cast<int64_t>(bat) * N + rr.i) * H_q + r * G + g_row) * static_cast<int64_t>(kDh) * EB;
     return rr;
@@ -278,9 +278,11 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void sparse_attn_kernel(
 
   auto stage = [&](const PassDesc& D) {
     const int64_t key0 = static_cast<int64_t>(D.blk) * kBk;
-    const int bat = D.seq / H_kv, r = D.seq - bat * H_kv;
+    // selection group r reads K/V head r >> kv_shift of the H_sel >> kv_shift heads
+    const int bat = D.seq / H_sel, r = D.seq - bat * H_sel;
+    const int H_kv = H_sel >> kv_shift;
     const int64_t rstride = static_cast<int64_t>(H_kv) * kDh * EB;
-    const int64_t row0 = (static_cast<int64_t>(bat) * N + key0) * H_kv + r;
+    const int64_t row0 = (static_cast<int64_t>(bat) * N + key0) * H_kv + (r >> kv_shift);
     stage_kv<FP8>(static_cast<const uint8_t*>(kp) + row0 * kDh * EB,
                   static_cast<const uint8_t*>(vp) + row0 * kDh * EB, rstride,
                   static_cast<int>(min<int64_t>(kBk, N - key0)), k_lds, vt_lds);
@@ -558,14 +560,14 @@ namespace {
 
 template <int G>
 hipError_t launch_g(const void* q, const void* k, const void* v, bool fp8, int batch, int64_t N,
-                    int H_kv, int kslots, float scale_log2, float out_scale,
+                    int H_sel, int kv_shift, int kslots, float scale_log2, float out_scale,
                     const int32_t* blk_entries, const int32_t* sched, int64_t q_begin,
                     int64_t q_count, uint16_t* o_part, float* lse_part, hipStream_t stream) {
-  const SchedLayout s = sched_layout(batch, H_kv, G, kslots, q_begin, q_count);
+  const SchedLayout s = sched_layout(batch, H_sel, G, kslots, q_begin, q_count);
   // Never more workgroups than passes, so every workgroup has work when the
   // range is small.
   int64_t grid = static_cast<int64_t>(device_cus()) * kAttnWgPerCu;
-  const int64_t min_passes = (static_cast<int64_t>(batch) * H_kv * q_count * kslots + s.EPP - 1) / s.EPP;
+  const int64_t min_passes = (static_cast<int64_t>(batch) * H_sel * q_count * kslots + s.EPP - 1) / s.EPP;
   if (min_passes < grid) grid = min_passes;
   if (grid < 1) grid = 1;
   uint32_t magic = 0;
@@ -573,9 +575,9 @@ hipError_t launch_g(const void* q, const void* k, const void* v, bool fp8, int b
   kdiv_params(kslots, &magic, &shift);
   auto kern = fp8 ? sparse_attn_kernel<G, true> : sparse_attn_kernel<G, false>;
   hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(grid)), dim3(kThreads), 0, stream, q, k, v,
-                     N, H_kv, kslots, magic, shift, scale_log2, out_scale, blk_entries,
+                     N, H_sel, kv_shift, kslots, magic, shift, scale_log2, out_scale, blk_entries,
                      sched + s.off_segp, reinterpret_cast<const PassDesc*>(sched + s.off_pass),
-                     static_cast<int>(s.B_c), static_cast<int>(batch * H_kv * s.nW),
+                     static_cast<int>(s.B_c), static_cast<int>(batch * H_sel * s.nW),
                      static_cast<int>(q_begin), static_cast<int>(q_count), o_part, lse_part);
   return hipGetLastError();
 }
@@ -583,14 +585,14 @@ hipError_t launch_g(const void* q, const void* k, const void* v, bool fp8, int b
 }  // namespace
 
 hipError_t launch_sparse_attn(const void* q, const void* k, const void* v, bool fp8, int batch,
-                              int64_t N, int H_kv, int G, int kslots, float scale_log2,
+                              int64_t N, int H_sel, int G, int kv_shift, int kslots, float scale_log2,
                               float out_scale, const int32_t* blk_offsets,
                               const int32_t* blk_entries, const int32_t* sched, int64_t q_begin,
                               int64_t q_count, uint16_t* o_part, float* lse_part,
                               hipStream_t stream) {
 #define MSA_ATTN_CASE(GG)                                                                      \
   case GG:                                                                                     \
-    return launch_g<GG>(q, k, v, fp8, batch, N, H_kv, kslots, scale_log2, out_scale,           \
+    return launch_g<GG>(q, k, v, fp8, batch, N, H_sel, kv_shift, kslots, scale_log2, out_scale, \
                         blk_entries, sched, q_begin, q_count, o_part, lse_part, stream);
   switch (G) {
     MSA_ATTN_CASE(1)

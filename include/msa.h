@@ -41,7 +41,13 @@
  *
  * Supported shapes (MSA_ERR_UNSUPPORTED otherwise): d_h = 128, B_k = 128,
  * d_idx in {64, 128}, G in {1, 2, 4, 8, 16}, 1 <= k <= 32, B_c <= 16384
- * (N <= 2,097,152), batch * H_kv * q_count * k < 2^31.
+ * (N <= 2,097,152), batch * H_sel * q_count * k < 2^31.
+ *
+ * Selection groups: H_sel = dims->H_idx when nonzero, else H_kv, index (proxy)
+ * query heads, each choosing blocks for its G_sel = H_q / H_sel adjacent query
+ * heads; group r reads K/V head r / (H_sel / H_kv).  Every selection-indexed
+ * array below is laid out over H_sel groups of G_sel heads (with H_idx = 0
+ * these are the H_kv GQA groups of G heads).
  */
 #ifndef MSA_H
 #define MSA_H
@@ -53,7 +59,7 @@
 extern "C" {
 #endif
 
-#define MSA_ABI_VERSION 1
+#define MSA_ABI_VERSION 2
 
 enum msa_status_code {
     MSA_OK = 0,
@@ -74,13 +80,18 @@ enum msa_dtype_code {
 typedef struct msa_dims {
     int32_t batch; /* independent sequences */
     int32_t H_q;   /* query heads */
-    int32_t H_kv;  /* key/value heads = GQA groups = index query heads */
+    int32_t H_kv;  /* key/value heads = GQA groups (= index heads when H_idx = 0) */
     int32_t G;     /* query heads per group; must equal H_q / H_kv */
     int32_t d_h;   /* head dimension of Q, K, V */
     int32_t d_idx; /* head dimension of Q^idx, K^idx */
     int32_t B_k;   /* tokens per key block */
     int32_t k;     /* blocks selected per (query, group), local block included */
     int64_t N;     /* sequence length (queries = keys) */
+    int32_t H_idx; /* index (proxy) query heads, each selecting blocks for its
+                      H_q / H_idx adjacent query heads ("Flash-MSA", What's
+                      next, note on proxy heads >= KV heads); a multiple of
+                      H_kv dividing H_q, H_q / H_idx in {1, 2, 4, 8, 16};
+                      0 = H_kv (one index head per GQA group) */
 } msa_dims;
 
 /* Options of the main branch. */
@@ -107,9 +118,9 @@ int msa_last_hip_error(void);
  * ("MiniMax Sparse Attention (MSA)", Deep Dive > Index Branch Architecture and
  *  Exp-Free TopK Kernel; "Flash-MSA", Forward > Proxy attention.)
  *
- *   q_idx      bf16 [batch][N][H_kv][d_idx]   index queries (one head per group)
+ *   q_idx      bf16 [batch][N][H_sel][d_idx]  index queries (one head per group)
  *   k_idx      bf16 [batch][N][d_idx]         the single shared index key head
- *   block_idx  int32 [batch][H_kv][q_count][k] output: row i - q_begin of group r
+ *   block_idx  int32 [batch][H_sel][q_count][k] output: row i - q_begin of group r
  *              lists the selected block ids in ascending order, padded with -1.
  *              The local block L = floor(i / B_k) is always present and is the
  *              last valid entry; when L < k all blocks 0..L are selected.
@@ -156,14 +167,14 @@ int msa_invert_workspace_size(const msa_dims *dims, int64_t q_begin, int64_t q_c
  * list of the KV-outer attention ("Flash-MSA", Backward; "MiniMax Sparse
  * Attention (MSA)", Deep Dive > KV-Outer Sparse Attention, steps 1 and 5).
  *
- *   block_idx    int32 [batch][H_kv][q_count][k] as written by msa_index_topk
+ *   block_idx    int32 [batch][H_sel][q_count][k] as written by msa_index_topk
  *                (any valid selection: ids in [0, floor(i / B_k)], no repeats
  *                within a row, -1 for empty slots).
- *   blk_offsets  int32 [batch][H_kv][B_c + 1] output: bin (bh, b) owns entries
+ *   blk_offsets  int32 [batch][H_sel][B_c + 1] output: bin (bh, b) owns entries
  *                [blk_offsets[bh][b], blk_offsets[bh][b + 1]); the offsets are
  *                absolute positions in blk_entries (bins are laid out in
  *                (bh, b) order, so blk_offsets[bh][B_c] == blk_offsets[bh+1][0]).
- *   blk_entries  int32 [batch * H_kv * q_count * k] output (capacity): entry
+ *   blk_entries  int32 [batch * H_sel * q_count * k] output (capacity): entry
  *                value (i - q_begin) * k + slot, ascending in i within a bin.
  *   sched        device scratch of msa_invert_workspace_size bytes; on return it
  *                holds the work list for msa_sparse_attn_fwd.
@@ -190,10 +201,10 @@ int msa_invert_status(const void *sched, int32_t *bad_ids, void *stream);
  *   k, v      [batch][N][H_kv][d_h]  same dtype
  *   blk_offsets, blk_entries, sched  as produced by msa_invert_blocks for the
  *             same (q_begin, q_count)
- *   o_part    bf16 [batch][H_kv][q_count][k][G][d_h] output: per (query, slot,
+ *   o_part    bf16 [batch][H_sel][q_count][k][G_sel][d_h] output: per (query, slot,
  *             head) the block's normalised partial output
  *             sum_j softmax_j V[j] over the block's visible tokens j
- *   lse_part  fp32 [batch][H_kv][q_count][k][G] output: natural-log
+ *   lse_part  fp32 [batch][H_sel][q_count][k][G_sel] output: natural-log
  *             log-sum-exp of the scaled scores over the same tokens
  * Only slots that hold a block are written.
  */
@@ -208,7 +219,7 @@ int msa_sparse_attn_fwd(const msa_dims *dims, const msa_opts *opts, const void *
  *  step 6): LSE = ln sum_s exp(lse_s), O = sum_s exp(lse_s - LSE) * Obar_s over
  *  the slots s whose block_idx entry is >= 0.
  *
- *   block_idx  int32 [batch][H_kv][q_count][k]
+ *   block_idx  int32 [batch][H_sel][q_count][k]
  *   o_part, lse_part  as written by msa_sparse_attn_fwd
  *   o          bf16 [batch][N][H_q][d_h] output, rows [q_begin, q_begin + q_count)
  *   lse        fp32 [batch][N][H_q] output (may be NULL): the main-branch LSE
@@ -227,7 +238,7 @@ int msa_combine(const msa_dims *dims, const int32_t *block_idx, const void *o_pa
  *   q, k, v        as for msa_sparse_attn_fwd
  *   q_idx, k_idx   as for msa_index_topk
  *   o, lse         as for msa_combine (all N rows); lse may be NULL
- *   block_idx_out  int32 [batch][H_kv][N][k] (may be NULL): the selection
+ *   block_idx_out  int32 [batch][H_sel][N][k] (may be NULL): the selection
  */
 int msa_workspace_size(const msa_dims *dims, const msa_opts *opts, size_t *bytes);
 int msa_forward(const msa_dims *dims, const msa_opts *opts, const void *q, const void *k,
@@ -246,7 +257,7 @@ int msa_forward(const msa_dims *dims, const msa_opts *opts, const void *q, const
  *         (other rows untouched)
  *   lse   fp32 [batch][N][H_q] output (may be NULL): natural-log log-sum-exp
  *         of the scaled scores of each row
- * Uses dims->batch, N, H_q, H_kv, G and d_h (d_idx, B_k and k are ignored)
+ * Uses dims->batch, N, H_q, H_kv, G and d_h (d_idx, B_k, k and H_idx are ignored)
  * and opts->softmax_scale; q_begin needs no alignment.  Only bf16 is
  * supported (MSA_ERR_UNSUPPORTED for fp8), and batch * H_kv <= 2^20.
  */
@@ -265,16 +276,16 @@ int msa_dense_attn_fwd(const msa_dims *dims, const msa_opts *opts, const void *q
  * tile: "Optimizing MiniMax M3 Sparse Attention on NVIDIA Blackwell", sec. 1).
  *
  *   q              bf16 [batch][H_q][d_h]      the new token's queries
- *   q_idx          bf16 [batch][H_kv][d_idx]   its index queries
+ *   q_idx          bf16 [batch][H_sel][d_idx]  its index queries
  *   k, v           bf16 [batch][N][H_kv][d_h]  the cache, token N - 1 included
  *   k_idx          bf16 [batch][N][d_idx]      the index-key cache
  *   o              bf16 [batch][H_q][d_h] output
  *   lse            fp32 [batch][H_q] output (may be NULL): natural-log LSE
- *   block_idx_out  int32 [batch][H_kv][k] (may be NULL): the selection, as a
+ *   block_idx_out  int32 [batch][H_sel][k] (may be NULL): the selection, as a
  *                  row of msa_index_topk's output
  *   workspace      device memory of msa_decode_workspace_size bytes,
  *                  256-byte aligned: block scores, partial outputs
- * bf16 Q/K/V only (MSA_ERR_UNSUPPORTED for fp8); H_kv <= 32, batch <= 65535;
+ * bf16 Q/K/V only (MSA_ERR_UNSUPPORTED for fp8); H_sel <= 32, batch <= 65535;
  * opts->q_chunk is ignored.
  */
 int msa_decode_workspace_size(const msa_dims *dims, const msa_opts *opts, size_t *bytes);

@@ -30,7 +30,7 @@ def log(msg: str) -> None:
 
 
 def dims_of(w: synth.Workload):
-    return msa.make_dims(w.batch, w.N, w.H_q, w.H_kv, w.d_h, w.d_idx, w.B_k, w.k)
+    return msa.make_dims(w.batch, w.N, w.H_q, w.H_kv, w.d_h, w.d_idx, w.B_k, w.k, H_idx=w.H_idx)
 
 
 def opts_of(w: synth.Workload, **kw):
@@ -70,7 +70,7 @@ def admissible(gsel, osel, Mrow, k) -> bool:
 
 
 def check_selection(gpu, orc, marg, M, k, what=""):
-    """gpu, orc: [H_kv, n, k]; marg: [H_kv, n]; M: [n, H_kv, B].  Returns stats."""
+    """gpu, orc: [H_sel, n, k]; marg: [H_sel, n]; M: [n, H_sel, B].  Returns stats."""
     sure = marg > MARGIN
     exact_ok = np.array_equal(gpu[sure], orc[sure])
     if not exact_ok:
@@ -103,7 +103,7 @@ def compact_attention_rows(w: synth.Workload, rows: np.ndarray, sel: np.ndarray,
     sequence; block b maps to its rank in U and the query to the same offset in
     the local block's new position.  Every selected block before the local one
     stays fully visible and the local block keeps its causal prefix, so the
-    attention is unchanged.  sel: [H_kv, n, k] (the selection to attend to)."""
+    attention is unchanged.  sel: [H_sel, n, k] (the selection to attend to)."""
     O = np.zeros((len(rows), w.H_q, w.d_h))
     lse = np.zeros((len(rows), w.H_q))
     code = oracle.FP8 if w.dtype == "fp8" else oracle.BF16

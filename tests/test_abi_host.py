@@ -42,7 +42,7 @@ def test_exports_every_declared_symbol(L):
 
 
 def test_identity(L):
-    assert L.msa_abi_version() == 1
+    assert L.msa_abi_version() == 2
     assert L.msa_status_string(0) == b"ok"
     assert L.msa_status_string(5) == b"workspace too small"
 
@@ -155,6 +155,15 @@ def test_decode_validation(L):
     assert call(d, o, out=ODD) == 4
     assert call(d, o, wsp=ctypes.c_void_p(0x10010)) == 4     # workspace needs 256-byte alignment
     assert L.msa_decode_workspace_size(ctypes.byref(d), ctypes.byref(o), None) == 1
+
+
+@pytest.mark.parametrize("H_idx,status", [(-1, 2), (3, 2), (6, 2), (16, 0), (8, 0), (4, 0), (0, 0)])
+def test_index_head_validation(L, H_idx, status):
+    """H_idx: a multiple of H_kv = 2 dividing H_q = 16 (G_sel a power of two
+    <= 16); 0 means H_kv."""
+    d = dims(H_q=16, H_kv=2, H_idx=H_idx)
+    n = ctypes.c_size_t(0)
+    assert L.msa_invert_workspace_size(ctypes.byref(d), 0, 2048, ctypes.byref(n)) == status
 
 
 def test_selection_variant_validation(L):

@@ -60,11 +60,12 @@ INDEX_CASES = [
     TINY.with_(N=5000, k=32, d_idx=128),
     TINY.with_(N=3000, k=7, H_q=4, H_kv=1),
     TINY.with_(N=2500, k=5, H_q=64, H_kv=4, d_idx=128),
+    TINY.with_(N=2000, k=4, H_q=16, H_kv=2, H_idx=8),       # more index heads than K/V heads
     TINY.with_(batch=2, N=1300),
 ]
 
 
-@pytest.mark.parametrize("w", INDEX_CASES, ids=lambda w: f"N{w.N}_hkv{w.H_kv}_d{w.d_idx}_k{w.k}_b{w.batch}")
+@pytest.mark.parametrize("w", INDEX_CASES, ids=lambda w: f"N{w.N}_hsel{w.H_sel}_d{w.d_idx}_k{w.k}_b{w.batch}")
 def test_index_topk_parity(w):
     log(f"index_topk N={w.N} H_kv={w.H_kv} d_idx={w.d_idx} k={w.k} batch={w.batch}")
     t = device_inputs(w, DEV)
@@ -156,12 +157,14 @@ ATTN_CASES = [
     TINY.with_(N=1536, k=16, H_q=32, H_kv=2),            # G = 16, all causal blocks
     TINY.with_(N=777, k=4, dtype="fp8"),
     TINY.with_(N=1300, k=4, batch=2, H_q=16, H_kv=4),
+    TINY.with_(N=1100, k=4, H_q=16, H_kv=2, H_idx=4),     # index heads: 2 per K/V head, G_sel = 4
+    TINY.with_(N=900, k=3, H_q=16, H_kv=2, H_idx=16, batch=2),   # one index head per query head
 ]
 
 
 def _oracle_partials(w, sel, rows):
     """Oracle partial (Obar, lse) of every (row, slot): attention over that one block."""
-    H = w.H_kv
+    H = w.H_sel
     code = oracle.FP8 if w.dtype == "fp8" else oracle.BF16
     sc = synth.fp8_scale() if w.dtype == "fp8" else 1.0
     q = synth.host_rows(w, "q", rows)
@@ -179,7 +182,7 @@ def _oracle_partials(w, sel, rows):
     return parts
 
 
-@pytest.mark.parametrize("w", ATTN_CASES, ids=lambda w: f"N{w.N}_G{w.G}_k{w.k}_{w.dtype}_b{w.batch}")
+@pytest.mark.parametrize("w", ATTN_CASES, ids=lambda w: f"N{w.N}_G{w.G}_Gs{w.G_sel}_k{w.k}_{w.dtype}_b{w.batch}")
 def test_attention_and_combine_parity(w):
     """Feed the oracle's selection to the GPU inversion, attention and combine."""
     log(f"attention N={w.N} H_q={w.H_q} H_kv={w.H_kv} k={w.k} dtype={w.dtype} batch={w.batch}")
@@ -202,12 +205,12 @@ def test_attention_and_combine_parity(w):
     lpart = lpart.cpu().numpy()
     out = out.float().cpu().numpy()
     lse = lse.cpu().numpy()
-    G = w.G
+    G = w.G_sel
     for b in range(w.batch):
         # partials per slot (batch 0 only: the oracle helper reads batch-0 rows)
         if b == 0:
             for s, (Os, ls, valid) in enumerate(_oracle_partials(w, sel[0], rows)):
-                for r in range(w.H_kv):
+                for r in range(w.H_sel):
                     m = valid[r]
                     if not m.any():                               # slot empty in every row
                         continue
@@ -253,7 +256,8 @@ def test_combine_parity_random_partials():
 # --------------------------------------------------------------------------- whole forward
 
 FWD_CASES = [TINY, TINY.with_(N=1000, k=5), TINY.with_(N=2304, k=4, q_chunk=512),
-             TINY.with_(N=3000, H_q=32, H_kv=2, k=8, d_idx=128, dtype="fp8")]
+             TINY.with_(N=3000, H_q=32, H_kv=2, k=8, d_idx=128, dtype="fp8"),
+             TINY.with_(N=1800, H_q=32, H_kv=2, H_idx=8, k=5, q_chunk=768)]
 
 
 @pytest.mark.parametrize("w", FWD_CASES, ids=lambda w: f"N{w.N}_k{w.k}_{w.dtype}_chunk{w.q_chunk}")
@@ -261,7 +265,7 @@ def test_forward_parity(w):
     log(f"forward N={w.N} k={w.k} dtype={w.dtype} q_chunk={w.q_chunk}")
     t = device_inputs(w, DEV)
     d, o = dims_of(w), opts_of(w)
-    bi = torch.empty((w.batch, w.H_kv, w.N, w.k), dtype=torch.int32, device=DEV)
+    bi = torch.empty((w.batch, w.H_sel, w.N, w.k), dtype=torch.int32, device=DEV)
     out, lse, _ = msa.msa_forward(d, o, t["q"], t["k"], t["v"], t["q_idx"], t["k_idx"],
                                   block_idx_out=bi, want_lse=True)
     torch.cuda.synchronize()
@@ -322,7 +326,7 @@ def test_forced_index_parity(w, first, window):
         st = check_selection(gsel[b], ob, marg, M, w.k, what=f"forced b{b}")
         log(f"  batch {b}: {st}")
         L = rows // w.B_k
-        for r in range(w.H_kv):
+        for r in range(w.H_sel):
             if first:
                 assert (gsel[b, r][L >= 1] == 0).any(axis=1).all()
             for back in range(1, window):
@@ -346,7 +350,7 @@ def test_window_selection_attention_parity(w):
     out, lse = msa.msa_combine(d, bi, opart, lpart, want_lse=True)
     torch.cuda.synchronize()
     rows = np.arange(w.N)
-    want = oracle.window_selection(rows, w.B_k, w.k, w.H_kv)
+    want = oracle.window_selection(rows, w.B_k, w.k, w.H_sel)
     gsel = bi.cpu().numpy()
     out, lse = out.float().cpu().numpy(), lse.cpu().numpy()
     for b in range(w.batch):
@@ -459,6 +463,7 @@ DECODE_CASES = [
     TINY.with_(N=2500, k=5, H_q=64, H_kv=4, d_idx=128, batch=3),
     TINY.with_(N=4000, k=32, H_q=2, H_kv=2, plant=4),   # G = 1, planted hot blocks
     TINY.with_(N=1500, k=7, H_q=32, H_kv=4, batch=2),   # G = 8
+    TINY.with_(N=2200, k=6, H_q=32, H_kv=2, H_idx=8, batch=2),   # 4 index heads per K/V head
 ]
 
 
@@ -471,7 +476,7 @@ def _check_decode(w, t, out, lse, bi, tol_max=2e-2):
     last = np.array([w.N - 1])
     for b in range(w.batch):
         ob, marg, M = oracle_index_rows(w, last, bat=b)
-        gsel = bi[b][:, None, :]                                   # [H_kv, 1, k]
+        gsel = bi[b][:, None, :]                                   # [H_sel, 1, k]
         st = check_selection(gsel, ob, marg, M, w.k, what=f"decode b{b}")
         O, L = compact_attention_rows(w, last, gsel, bat=b)
         mx, mn = err_stats(out[b], O[0])
@@ -481,12 +486,12 @@ def _check_decode(w, t, out, lse, bi, tol_max=2e-2):
         assert lmx <= 1e-3
 
 
-@pytest.mark.parametrize("w", DECODE_CASES, ids=lambda w: f"N{w.N}_k{w.k}_G{w.G}_d{w.d_idx}_b{w.batch}")
+@pytest.mark.parametrize("w", DECODE_CASES, ids=lambda w: f"N{w.N}_k{w.k}_G{w.G}_Hs{w.H_sel}_d{w.d_idx}_b{w.batch}")
 def test_decode_parity(w):
     log(f"decode N={w.N} k={w.k} H_q={w.H_q} H_kv={w.H_kv} d_idx={w.d_idx} batch={w.batch}")
     t = device_inputs(w, DEV)
     q1, qi1 = _decode_inputs(w, t)
-    bi = torch.empty((w.batch, w.H_kv, w.k), dtype=torch.int32, device=DEV)
+    bi = torch.empty((w.batch, w.H_sel, w.k), dtype=torch.int32, device=DEV)
     out, lse, _ = msa.msa_decode(dims_of(w), msa.make_opts(), q1, qi1, t["k"], t["v"], t["k_idx"],
                                  block_idx_out=bi, want_lse=True)
     torch.cuda.synchronize()
@@ -499,11 +504,11 @@ def test_decode_matches_forward_last_row():
     w = TINY.with_(N=1792, k=5, batch=2)
     t = device_inputs(w, DEV)
     d = dims_of(w)
-    bi_f = torch.empty((w.batch, w.H_kv, w.N, w.k), dtype=torch.int32, device=DEV)
+    bi_f = torch.empty((w.batch, w.H_sel, w.N, w.k), dtype=torch.int32, device=DEV)
     of, lf, _ = msa.msa_forward(d, msa.make_opts(), t["q"], t["k"], t["v"], t["q_idx"], t["k_idx"],
                                 block_idx_out=bi_f, want_lse=True)
     q1, qi1 = _decode_inputs(w, t)
-    bi_d = torch.empty((w.batch, w.H_kv, w.k), dtype=torch.int32, device=DEV)
+    bi_d = torch.empty((w.batch, w.H_sel, w.k), dtype=torch.int32, device=DEV)
     od, ld, _ = msa.msa_decode(d, msa.make_opts(), q1, qi1, t["k"], t["v"], t["k_idx"],
                                block_idx_out=bi_d, want_lse=True)
     torch.cuda.synchronize()
@@ -520,7 +525,7 @@ def test_decode_full_size(w):
     log(f"decode full-size {w.name} batch={w.batch}: generating inputs")
     t = device_inputs(w, DEV)
     q1, qi1 = _decode_inputs(w, t)
-    bi = torch.empty((w.batch, w.H_kv, w.k), dtype=torch.int32, device=DEV)
+    bi = torch.empty((w.batch, w.H_sel, w.k), dtype=torch.int32, device=DEV)
     out, lse, _ = msa.msa_decode(dims_of(w), msa.make_opts(), q1, qi1, t["k"], t["v"], t["k_idx"],
                                  block_idx_out=bi, want_lse=True)
     torch.cuda.synchronize()
@@ -540,7 +545,7 @@ def test_full_size_sampled_parity(w, nrows):
     log(f"full-size {w.name}: generating inputs")
     t = device_inputs(w, DEV)
     d, o = dims_of(w), opts_of(w)
-    bi = torch.empty((w.batch, w.H_kv, w.N, w.k), dtype=torch.int32, device=DEV)
+    bi = torch.empty((w.batch, w.H_sel, w.N, w.k), dtype=torch.int32, device=DEV)
     log(f"full-size {w.name}: msa_forward q_chunk={w.q_chunk}")
     out, _, _ = msa.msa_forward(d, o, t["q"], t["k"], t["v"], t["q_idx"], t["k_idx"],
                                 block_idx_out=bi)
