@@ -36,7 +36,8 @@ int check_dims(const msa_dims* d) {
       d->d_h < 1 || d->d_idx < 1 || d->B_k < 1)
     return MSA_ERR_SHAPE;
   if (static_cast<int64_t>(d->G) * d->H_kv != d->H_q) return MSA_ERR_SHAPE;
-  if (d->d_h != msa::kDh || d->B_k != msa::kBk) return MSA_ERR_UNSUPPORTED;
+  if (d->d_h != msa::kDh) return MSA_ERR_UNSUPPORTED;
+  if (d->B_k != 32 && d->B_k != 64 && d->B_k != msa::kBk) return MSA_ERR_UNSUPPORTED;
   if (d->d_idx != 64 && d->d_idx != 128) return MSA_ERR_UNSUPPORTED;
   if (d->G != 1 && d->G != 2 && d->G != 4 && d->G != 8 && d->G != 16) return MSA_ERR_UNSUPPORTED;
   if (d->k > 32) return MSA_ERR_UNSUPPORTED;
@@ -69,6 +70,8 @@ int check_opts(const msa_dims* d, const msa_opts* o) {
       return MSA_ERR_SHAPE;
   }
   if (o->q_chunk < 0 || (o->q_chunk > 0 && o->q_chunk % d->B_k != 0)) return MSA_ERR_SHAPE;
+  // fp8 Q/K/V run with 128-token blocks only
+  if (o->qkv_dtype == MSA_DTYPE_FP8_E4M3 && d->B_k != msa::kBk) return MSA_ERR_UNSUPPORTED;
   return MSA_OK;
 }
 
@@ -103,7 +106,7 @@ ForwardLayout forward_layout(const msa_dims* d, const msa_opts* o) {
   const int64_t nchunks = (d->N + L.qc - 1) / L.qc;
   for (int64_t c = (nchunks > 2 ? nchunks - 2 : 0); c < nchunks; ++c) {
     const int64_t qb = c * L.qc, qn = (d->N - qb) < L.qc ? (d->N - qb) : L.qc;
-    const msa::SchedLayout s = msa::sched_layout(d->batch, HS(d), GS(d), d->k, qb, qn);
+    const msa::SchedLayout s = msa::sched_layout(d->batch, HS(d), GS(d), d->k, qb, qn, d->B_k);
     words = s.words > words ? s.words : words;
   }
   size_t off = 0;
@@ -154,7 +157,7 @@ int msa_index_topk(const msa_dims* dims, const void* q_idx, const void* k_idx, i
   hipError_t e = msa::launch_index_topk(static_cast<const uint16_t*>(q_idx),
                                         static_cast<const uint16_t*>(k_idx), dims->batch, dims->N,
                                         HS(dims), dims->d_idx, dims->k, q_begin, q_count,
-                                        block_idx, static_cast<hipStream_t>(stream));
+                                        block_idx, static_cast<hipStream_t>(stream), 0, 1, dims->B_k);
   return e == hipSuccess ? MSA_OK : hip_fail(e);
 }
 
@@ -172,7 +175,7 @@ int msa_index_topk_forced(const msa_dims* dims, const void* q_idx, const void* k
                                         static_cast<const uint16_t*>(k_idx), dims->batch, dims->N,
                                         HS(dims), dims->d_idx, dims->k, q_begin, q_count,
                                         block_idx, static_cast<hipStream_t>(stream), force_first,
-                                        local_window);
+                                        local_window, dims->B_k);
   return e == hipSuccess ? MSA_OK : hip_fail(e);
 }
 
@@ -184,7 +187,7 @@ int msa_window_select(const msa_dims* dims, int64_t q_begin, int64_t q_count, in
   if (!block_idx) return MSA_ERR_NULL;
   if (misaligned(block_idx)) return MSA_ERR_ALIGN;
   hipError_t e = msa::launch_window_select(dims->batch, HS(dims), dims->k, q_begin, q_count, block_idx,
-                                           static_cast<hipStream_t>(stream));
+                                           static_cast<hipStream_t>(stream), dims->B_k);
   return e == hipSuccess ? MSA_OK : hip_fail(e);
 }
 
@@ -194,7 +197,8 @@ int msa_invert_workspace_size(const msa_dims* dims, int64_t q_begin, int64_t q_c
   if (st) return st;
   if ((st = check_range(dims, q_begin, q_count))) return st;
   if (!bytes) return MSA_ERR_NULL;
-  const msa::SchedLayout s = msa::sched_layout(dims->batch, HS(dims), GS(dims), dims->k, q_begin, q_count);
+  const msa::SchedLayout s = msa::sched_layout(dims->batch, HS(dims), GS(dims), dims->k, q_begin, q_count,
+                                               dims->B_k);
   *bytes = static_cast<size_t>(s.words) * 4;
   return MSA_OK;
 }
@@ -209,11 +213,12 @@ int msa_invert_blocks(const msa_dims* dims, const int32_t* block_idx, int64_t q_
   if (misaligned(block_idx) || misaligned(blk_offsets) || misaligned(blk_entries) ||
       misaligned(sched))
     return MSA_ERR_ALIGN;
-  const msa::SchedLayout s = msa::sched_layout(dims->batch, HS(dims), GS(dims), dims->k, q_begin, q_count);
+  const msa::SchedLayout s = msa::sched_layout(dims->batch, HS(dims), GS(dims), dims->k, q_begin, q_count,
+                                               dims->B_k);
   if (sched_bytes < static_cast<size_t>(s.words) * 4) return MSA_ERR_WORKSPACE;
   hipError_t e = msa::launch_invert(block_idx, dims->batch, HS(dims), GS(dims), dims->k, q_begin,
                                     q_count, blk_offsets, blk_entries, static_cast<int32_t*>(sched),
-                                    static_cast<hipStream_t>(stream));
+                                    static_cast<hipStream_t>(stream), dims->B_k);
   return e == hipSuccess ? MSA_OK : hip_fail(e);
 }
 
@@ -245,7 +250,7 @@ int msa_sparse_attn_fwd(const msa_dims* dims, const msa_opts* opts, const void* 
   hipError_t e = msa::launch_sparse_attn(
       q, k, v, opts->qkv_dtype == MSA_DTYPE_FP8_E4M3, dims->batch, dims->N, HS(dims), GS(dims),
       KVS(dims), dims->k, sl2, osc, blk_offsets, blk_entries, static_cast<const int32_t*>(sched), q_begin,
-      q_count, static_cast<uint16_t*>(o_part), lse_part, static_cast<hipStream_t>(stream));
+      q_count, static_cast<uint16_t*>(o_part), lse_part, static_cast<hipStream_t>(stream), dims->B_k);
   return e == hipSuccess ? MSA_OK : hip_fail(e);
 }
 
@@ -358,7 +363,7 @@ int msa_decode(const msa_dims* dims, const msa_opts* opts, const void* q, const 
       static_cast<const uint16_t*>(v), static_cast<const uint16_t*>(k_idx), dims->batch, dims->N, HS(dims),
       GS(dims), KVS(dims), dims->d_idx, dims->k, sl2, reinterpret_cast<float*>(ws + L.off_scores), bi,
       reinterpret_cast<uint16_t*>(ws + L.off_opart), reinterpret_cast<float*>(ws + L.off_lpart),
-      static_cast<uint16_t*>(o), lse, static_cast<hipStream_t>(stream));
+      static_cast<uint16_t*>(o), lse, static_cast<hipStream_t>(stream), dims->B_k);
   return e == hipSuccess ? MSA_OK : hip_fail(e);
 }
 
@@ -407,13 +412,15 @@ int msa_forward(const msa_dims* dims, const msa_opts* opts, const void* q, const
     int32_t* bi = (one_chunk && block_idx_out) ? block_idx_out : bi_chunk;
     hipError_t e = msa::launch_index_topk(static_cast<const uint16_t*>(q_idx),
                                           static_cast<const uint16_t*>(k_idx), dims->batch, dims->N,
-                                          HS(dims), dims->d_idx, dims->k, qb, qn, bi, s);
+                                          HS(dims), dims->d_idx, dims->k, qb, qn, bi, s, 0, 1,
+                                          dims->B_k);
     if (e != hipSuccess) return hip_fail(e);
-    e = msa::launch_invert(bi, dims->batch, HS(dims), GS(dims), dims->k, qb, qn, offs, ents, sched, s);
+    e = msa::launch_invert(bi, dims->batch, HS(dims), GS(dims), dims->k, qb, qn, offs, ents, sched, s,
+                           dims->B_k);
     if (e != hipSuccess) return hip_fail(e);
     e = msa::launch_sparse_attn(q, k, v, fp8, dims->batch, dims->N, HS(dims), GS(dims),
                                 KVS(dims), dims->k,
-                                sl2, osc, offs, ents, sched, qb, qn, opart, lpart, s);
+                                sl2, osc, offs, ents, sched, qb, qn, opart, lpart, s, dims->B_k);
     if (e != hipSuccess) return hip_fail(e);
     e = msa::launch_combine(bi, opart, lpart, dims->batch, dims->N, HS(dims), GS(dims), dims->k,
                             qb, qn, static_cast<uint16_t*>(o), lse, s);

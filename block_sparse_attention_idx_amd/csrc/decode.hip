@@ -55,7 +55,8 @@ __device__ __forceinline__ uint32_t ord_score(float x) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-template <int DIDX>
+// KT: 32-key tiles per key block (blocks of 32 KT tokens).
+template <int DIDX, int KT>
 __global__ __launch_bounds__(64 * kScoreWaves) void decode_scores_kernel(
     const uint16_t* __restrict__ q_idx, const uint16_t* __restrict__ k_idx, int64_t N, int H_sel,
     int L, int B, int batch, float* __restrict__ scores) {
@@ -70,10 +71,10 @@ __global__ __launch_bounds__(64 * kScoreWaves) void decode_scores_kernel(
     const int bat = static_cast<int>(it / L), blk = static_cast<int>(it % L);
     // All 4 key tiles' A fragments (row 32 mt + n, dims 16 ks + 8 h .. + 7)
     // are requested before any is used.
-    const uint16_t* kb = k_idx + (static_cast<int64_t>(bat) * N + static_cast<int64_t>(blk) * kBk + n) * DIDX + 8 * h;
-    u32x4 kf[4][STEPS];
+    const uint16_t* kb = k_idx + (static_cast<int64_t>(bat) * N + static_cast<int64_t>(blk) * (32 * KT) + n) * DIDX + 8 * h;
+    u32x4 kf[KT][STEPS];
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
+    for (int mt = 0; mt < KT; ++mt) {
 #pragma unroll
       for (int ks = 0; ks < STEPS; ++ks)
         kf[mt][ks] = *reinterpret_cast<const u32x4*>(kb + 32 * mt * DIDX + 16 * ks);
@@ -88,7 +89,7 @@ __global__ __launch_bounds__(64 * kScoreWaves) void decode_scores_kernel(
     }
     float mx = -__builtin_huge_valf();
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
+    for (int mt = 0; mt < KT; ++mt) {
       f32x16 acc = {};
 #pragma unroll
       for (int ks = 0; ks < STEPS; ++ks) acc = mfma32x32x16(as_bf16x8(kf[mt][ks]), qf[ks], acc);
@@ -216,7 +217,7 @@ __global__ __launch_bounds__(topk_threads<KP>()) void decode_topk_kernel(const f
 template <int G>
 __global__ __launch_bounds__(kStageThreads, 1) void decode_partial_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-    int64_t N, int H_sel, int kv_shift, int kslots, float scale_log2, const int32_t* __restrict__ block_idx,
+    int64_t N, int H_sel, int kv_shift, int kslots, int bk, float scale_log2, const int32_t* __restrict__ block_idx,
     uint16_t* __restrict__ o_part, float* __restrict__ lse_part) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[kBufBytes];
   const int64_t item = blockIdx.x;  // (seq, slot)
@@ -226,9 +227,11 @@ __global__ __launch_bounds__(kStageThreads, 1) void decode_partial_kernel(
   const int bat = static_cast<int>(seq / H_sel), r = static_cast<int>(seq % H_sel);
   const int H_kv = H_sel >> kv_shift;  // selection group r reads K/V head r >> kv_shift
   const int tid = threadIdx.x;
-  const int nvalid = static_cast<int>(min<int64_t>(kBk, N - static_cast<int64_t>(blk) * kBk));
+  // Blocks of bk <= 128 tokens sit at the start of the 128-key tile; the keys
+  // after them (and past the sequence end) are zero and hidden below.
+  const int nvalid = static_cast<int>(min<int64_t>(bk, N - static_cast<int64_t>(blk) * bk));
   const int64_t rstride = static_cast<int64_t>(H_kv) * kDh * 2;
-  const int64_t row0 = (static_cast<int64_t>(bat) * N + static_cast<int64_t>(blk) * kBk) * H_kv + (r >> kv_shift);
+  const int64_t row0 = (static_cast<int64_t>(bat) * N + static_cast<int64_t>(blk) * bk) * H_kv + (r >> kv_shift);
   KVRegs R;
   kv_load(R, reinterpret_cast<const uint8_t*>(k) + row0 * kDh * 2,
           reinterpret_cast<const uint8_t*>(v) + row0 * kDh * 2, rstride, nvalid, tid);
@@ -328,11 +331,11 @@ hipError_t launch_topk(const float* scores, int nseq, int L, int B, int k, int32
 
 template <int G>
 hipError_t launch_partial(const uint16_t* q, const uint16_t* k, const uint16_t* v, int batch, int64_t N,
-                          int H_sel, int kv_shift, int kslots, float scale_log2, const int32_t* block_idx,
+                          int H_sel, int kv_shift, int kslots, int bk, float scale_log2, const int32_t* block_idx,
                           uint16_t* o_part, float* lse_part, hipStream_t stream) {
   const int64_t items = static_cast<int64_t>(batch) * H_sel * kslots;
   hipLaunchKernelGGL(decode_partial_kernel<G>, dim3(static_cast<unsigned>(items)), dim3(kStageThreads), 0,
-                     stream, q, k, v, N, H_sel, kv_shift, kslots, scale_log2, block_idx, o_part, lse_part);
+                     stream, q, k, v, N, H_sel, kv_shift, kslots, bk, scale_log2, block_idx, o_part, lse_part);
   return hipGetLastError();
 }
 
@@ -342,9 +345,9 @@ hipError_t launch_decode(const uint16_t* q, const uint16_t* q_idx, const uint16_
                          const uint16_t* k_idx, int batch, int64_t N, int H_sel, int G, int kv_shift, int d_idx,
                          int kslots, float scale_log2, float* scores, int32_t* block_idx,
                          uint16_t* o_part, float* lse_part, uint16_t* o, float* lse,
-                         hipStream_t stream) {
-  const int B = static_cast<int>((N + kBk - 1) / kBk);
-  const int L = static_cast<int>((N - 1) / kBk);  // the local block; blocks 0 .. L - 1 are scored
+                         hipStream_t stream, int bk) {
+  const int B = static_cast<int>((N + bk - 1) / bk);
+  const int L = static_cast<int>((N - 1) / bk);  // the local block; blocks 0 .. L - 1 are scored
   const int nseq = batch * H_sel;
   hipError_t e = hipSuccess;
   if (L > 0) {
@@ -352,12 +355,19 @@ hipError_t launch_decode(const uint16_t* q, const uint16_t* q_idx, const uint16_
     const int64_t items = static_cast<int64_t>(batch) * L;
     int64_t wgs = (items + kScoreWaves - 1) / kScoreWaves;
     if (wgs > 1024) wgs = 1024;
-    if (d_idx == 64)
-      hipLaunchKernelGGL(decode_scores_kernel<64>, dim3(static_cast<unsigned>(wgs)), dim3(64 * kScoreWaves), 0,
-                         stream, q_idx, k_idx, N, H_sel, L, B, batch, scores);
-    else
-      hipLaunchKernelGGL(decode_scores_kernel<128>, dim3(static_cast<unsigned>(wgs)), dim3(64 * kScoreWaves), 0,
-                         stream, q_idx, k_idx, N, H_sel, L, B, batch, scores);
+    const dim3 g(static_cast<unsigned>(wgs)), t(64 * kScoreWaves);
+#define MSA_DEC_SCORES(D, KT) \
+  hipLaunchKernelGGL((decode_scores_kernel<D, KT>), g, t, 0, stream, q_idx, k_idx, N, H_sel, L, B, batch, scores)
+    if (d_idx == 64) {
+      if (bk == 32) MSA_DEC_SCORES(64, 1);
+      else if (bk == 64) MSA_DEC_SCORES(64, 2);
+      else MSA_DEC_SCORES(64, 4);
+    } else {
+      if (bk == 32) MSA_DEC_SCORES(128, 1);
+      else if (bk == 64) MSA_DEC_SCORES(128, 2);
+      else MSA_DEC_SCORES(128, 4);
+    }
+#undef MSA_DEC_SCORES
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   const int km = kslots - 1;
@@ -369,11 +379,11 @@ hipError_t launch_decode(const uint16_t* q, const uint16_t* q_idx, const uint16_
   else e = launch_topk<32>(scores, nseq, L, B, kslots, block_idx, stream);
   if (e != hipSuccess) return e;
   switch (G) {
-    case 1: e = launch_partial<1>(q, k, v, batch, N, H_sel, kv_shift, kslots, scale_log2, block_idx, o_part, lse_part, stream); break;
-    case 2: e = launch_partial<2>(q, k, v, batch, N, H_sel, kv_shift, kslots, scale_log2, block_idx, o_part, lse_part, stream); break;
-    case 4: e = launch_partial<4>(q, k, v, batch, N, H_sel, kv_shift, kslots, scale_log2, block_idx, o_part, lse_part, stream); break;
-    case 8: e = launch_partial<8>(q, k, v, batch, N, H_sel, kv_shift, kslots, scale_log2, block_idx, o_part, lse_part, stream); break;
-    case 16: e = launch_partial<16>(q, k, v, batch, N, H_sel, kv_shift, kslots, scale_log2, block_idx, o_part, lse_part, stream); break;
+    case 1: e = launch_partial<1>(q, k, v, batch, N, H_sel, kv_shift, kslots, bk, scale_log2, block_idx, o_part, lse_part, stream); break;
+    case 2: e = launch_partial<2>(q, k, v, batch, N, H_sel, kv_shift, kslots, bk, scale_log2, block_idx, o_part, lse_part, stream); break;
+    case 4: e = launch_partial<4>(q, k, v, batch, N, H_sel, kv_shift, kslots, bk, scale_log2, block_idx, o_part, lse_part, stream); break;
+    case 8: e = launch_partial<8>(q, k, v, batch, N, H_sel, kv_shift, kslots, bk, scale_log2, block_idx, o_part, lse_part, stream); break;
+    case 16: e = launch_partial<16>(q, k, v, batch, N, H_sel, kv_shift, kslots, bk, scale_log2, block_idx, o_part, lse_part, stream); break;
     default: return hipErrorInvalidValue;
   }
   if (e != hipSuccess) return e;

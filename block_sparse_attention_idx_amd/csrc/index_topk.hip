@@ -102,7 +102,11 @@ __device__ __forceinline__ void sort_ascending(int (&v)[KP]) {
 // forced sink and local blocks): block 0 (force_first) and the window - 1
 // blocks before the local one score +inf, so they always take slots; among
 // equal scores the smaller id still wins.
-template <int DIDX, int KP, bool FORCED>
+//
+// KT: 32-key MFMA tiles per key block, so blocks of BK = 32 KT tokens (the
+// block-size variants 32 and 64 of the paper's block-size ablation; 128 is
+// the default).
+template <int DIDX, int KP, bool FORCED, int KT>
 __global__ __launch_bounds__(kIdxThreads, 1) void index_topk_kernel(
     const uint16_t* __restrict__ q_idx, const uint16_t* __restrict__ k_idx, int64_t N, int H_kv,
     int k, int64_t q_begin, int64_t q_count, int force_first, int window,
@@ -111,7 +115,8 @@ __global__ __launch_bounds__(kIdxThreads, 1) void index_topk_kernel(
   constexpr int NCH = DIDX / 8;
   constexpr int STEPS = DIDX / 16;
   constexpr int KSTR = kidx_stride<DIDX>();
-  constexpr int TILE = kBk * KSTR;
+  constexpr int BK = 32 * KT;
+  constexpr int TILE = BK * KSTR;
   constexpr int NBUF = 4;  // LDS ring: two blocks scored, two in flight
   __shared__ __attribute__((aligned(16))) uint8_t lds[KM > 0 ? NBUF * TILE : 16];
 
@@ -129,9 +134,9 @@ __global__ __launch_bounds__(kIdxThreads, 1) void index_topk_kernel(
   const bool mine_ok = f_mine < rows_total;
   const int64_t il_mine = mine_ok ? f_mine / H_kv : 0;
   const int r_mine = mine_ok ? static_cast<int>(f_mine % H_kv) : 0;
-  const int L_mine = static_cast<int>((q_begin + il_mine) / kBk);
+  const int L_mine = static_cast<int>((q_begin + il_mine) / BK);
   const int64_t f_last = min(f0 + kIdxRows, rows_total) - 1;
-  const int Lmax = static_cast<int>((q_begin + f_last / H_kv) / kBk);
+  const int Lmax = static_cast<int>((q_begin + f_last / H_kv) / BK);
 
   int ids[KM > 0 ? KM : 1];
   if constexpr (KM > 0) {
@@ -165,7 +170,7 @@ __global__ __launch_bounds__(kIdxThreads, 1) void index_topk_kernel(
     // where the padding chunk NCH loads the row's last chunk again.  A block
     // index past the last is clamped to it (its data is never used).
     const uint16_t* kbase = k_idx + bat * N * DIDX;
-    constexpr int NSLOT = kBk * (NCH + 1);
+    constexpr int NSLOT = BK * (NCH + 1);
     constexpr int NJ = (NSLOT + 63) / 64;          // wave instructions per block
     constexpr int JW = (NJ + kIdxWaves - 1) / kIdxWaves;  // per wave (some do one less)
     int src_off[JW];  // element offset of this lane's slot within a block
@@ -178,7 +183,7 @@ __global__ __launch_bounds__(kIdxThreads, 1) void index_topk_kernel(
     }
     auto stage_block = [&](int blk, int buf) {
       blk = min(blk, Lmax - 1);
-      const uint16_t* src = kbase + static_cast<int64_t>(blk) * kBk * DIDX;
+      const uint16_t* src = kbase + static_cast<int64_t>(blk) * BK * DIDX;
 #pragma unroll
       for (int q = 0; q < JW; ++q) {
         const int j = wave + kIdxWaves * q;
@@ -229,8 +234,8 @@ __global__ __launch_bounds__(kIdxThreads, 1) void index_topk_kernel(
       for (int ks = 0; ks < STEPS; ++ks)
         kf[0][ks] = as_bf16x8(*reinterpret_cast<const u32x4*>(tile + 32 * ks));
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
-        if (mt + 1 < 4) {
+      for (int mt = 0; mt < KT; ++mt) {
+        if (mt + 1 < KT) {
 #pragma unroll
           for (int ks = 0; ks < STEPS; ++ks)
             kf[(mt + 1) & 1][ks] = as_bf16x8(
@@ -320,33 +325,41 @@ struct IdxArgs {
   int force_first, window;
   int32_t* block_idx;
   hipStream_t stream;
+  int bk;
 };
 
-template <int DIDX, int KP, bool FORCED>
+template <int DIDX, int KP, bool FORCED, int KT>
 hipError_t launch_t(const IdxArgs& a) {
   const int64_t nwg = (a.q_count * a.H_kv + kIdxRows - 1) / kIdxRows;
-  hipLaunchKernelGGL((index_topk_kernel<DIDX, KP, FORCED>), dim3(static_cast<unsigned>(nwg), a.batch),
+  hipLaunchKernelGGL((index_topk_kernel<DIDX, KP, FORCED, KT>), dim3(static_cast<unsigned>(nwg), a.batch),
                      dim3(kIdxThreads), 0, a.stream, a.q_idx, a.k_idx, a.N, a.H_kv, a.k, a.q_begin,
                      a.q_count, a.force_first, a.window, a.block_idx);
   return hipGetLastError();
 }
 
+template <int DIDX, bool FORCED, int KT>
+hipError_t launch_k(const IdxArgs& a) {
+  if (a.k <= 1) return launch_t<DIDX, 1, FORCED, KT>(a);
+  if (a.k <= 2) return launch_t<DIDX, 2, FORCED, KT>(a);
+  if (a.k <= 4) return launch_t<DIDX, 4, FORCED, KT>(a);
+  if (a.k <= 8) return launch_t<DIDX, 8, FORCED, KT>(a);
+  if (a.k <= 16) return launch_t<DIDX, 16, FORCED, KT>(a);
+  return launch_t<DIDX, 32, FORCED, KT>(a);
+}
+
 template <int DIDX, bool FORCED>
 hipError_t launch_d(const IdxArgs& a) {
-  if (a.k <= 1) return launch_t<DIDX, 1, FORCED>(a);
-  if (a.k <= 2) return launch_t<DIDX, 2, FORCED>(a);
-  if (a.k <= 4) return launch_t<DIDX, 4, FORCED>(a);
-  if (a.k <= 8) return launch_t<DIDX, 8, FORCED>(a);
-  if (a.k <= 16) return launch_t<DIDX, 16, FORCED>(a);
-  return launch_t<DIDX, 32, FORCED>(a);
+  if (a.bk == 32) return launch_k<DIDX, FORCED, 1>(a);
+  if (a.bk == 64) return launch_k<DIDX, FORCED, 2>(a);
+  return launch_k<DIDX, FORCED, 4>(a);
 }
 
 }  // namespace
 
 hipError_t launch_index_topk(const uint16_t* q_idx, const uint16_t* k_idx, int batch, int64_t N,
                              int H_kv, int d_idx, int k, int64_t q_begin, int64_t q_count,
-                             int32_t* block_idx, hipStream_t stream, int force_first, int window) {
-  const IdxArgs a{q_idx, k_idx, batch, N, H_kv, k, q_begin, q_count, force_first, window, block_idx, stream};
+                             int32_t* block_idx, hipStream_t stream, int force_first, int window, int bk) {
+  const IdxArgs a{q_idx, k_idx, batch, N, H_kv, k, q_begin, q_count, force_first, window, block_idx, stream, bk};
   const bool forced = force_first != 0 || window > 1;
   if (d_idx == 64) return forced ? launch_d<64, true>(a) : launch_d<64, false>(a);
   return forced ? launch_d<128, true>(a) : launch_d<128, false>(a);

@@ -35,11 +35,11 @@
 
 namespace msa {
 
-SchedLayout sched_layout(int batch, int H_kv, int G, int k, int64_t q_begin, int64_t q_count) {
+SchedLayout sched_layout(int batch, int H_kv, int G, int k, int64_t q_begin, int64_t q_count, int bk) {
   SchedLayout s{};
   auto al = [](int64_t w) { return (w + 63) / 64 * 64; };  // 256-byte alignment
   const int64_t nseq = static_cast<int64_t>(batch) * H_kv;
-  s.B_c = (q_begin + q_count + kBk - 1) / kBk;
+  s.B_c = (q_begin + q_count + bk - 1) / bk;
   s.T64 = (q_count + 63) / 64;
   s.TW = kAttnWindowRows / 64;
   s.nW = (s.T64 + s.TW - 1) / s.TW;
@@ -72,8 +72,8 @@ constexpr int kInvThreads = 256;
 // Build the LDS row masks of one (seq, tile).  Returns the number of bins used.
 __device__ __forceinline__ int build_masks(const int32_t* __restrict__ rows, int k, int64_t q_begin,
                                            int64_t q0, int nrows, unsigned long long* mask,
-                                           int* bad) {
-  const int tmax = static_cast<int>((q_begin + q0 + nrows - 1) / kBk);
+                                           int* bad, int bk) {
+  const int tmax = static_cast<int>((q_begin + q0 + nrows - 1) / bk);
   const int nb = tmax + 1;
   for (int b = threadIdx.x; b < nb; b += blockDim.x) mask[b] = 0ull;
   __syncthreads();
@@ -81,7 +81,7 @@ __device__ __forceinline__ int build_masks(const int32_t* __restrict__ rows, int
   for (int e = threadIdx.x; e < nrows * k; e += blockDim.x) {
     const int row = e / k;
     const int v = rows[e];
-    const int L = static_cast<int>((q_begin + q0 + row) / kBk);
+    const int L = static_cast<int>((q_begin + q0 + row) / bk);
     if (v >= 0 && v <= L)
       atomicOr(&mask[v], 1ull << row);
     else if (v != -1)
@@ -94,7 +94,7 @@ __device__ __forceinline__ int build_masks(const int32_t* __restrict__ rows, int
 
 __global__ __launch_bounds__(kInvThreads) void inv_count_kernel(
     const int32_t* __restrict__ block_idx, int k, int64_t q_begin, int64_t q_count, int64_t B_c,
-    int64_t T64, int32_t* __restrict__ cnt, int32_t* __restrict__ bad_out) {
+    int64_t T64, int32_t* __restrict__ cnt, int32_t* __restrict__ bad_out, int bk) {
   extern __shared__ unsigned long long mask[];
   __shared__ int bad_sum;
   const int64_t tq = blockIdx.x, seq = blockIdx.y;
@@ -102,7 +102,7 @@ __global__ __launch_bounds__(kInvThreads) void inv_count_kernel(
   const int nrows = static_cast<int>(min<int64_t>(64, q_count - q0));
   if (threadIdx.x == 0) bad_sum = 0;
   int nbad;
-  const int nb = build_masks(block_idx + (seq * q_count + q0) * k, k, q_begin, q0, nrows, mask, &nbad);
+  const int nb = build_masks(block_idx + (seq * q_count + q0) * k, k, q_begin, q0, nrows, mask, &nbad, bk);
   if (nbad) atomicAdd(&bad_sum, nbad);
   int32_t* out = cnt + (seq * T64 + tq) * B_c;
   for (int64_t b = threadIdx.x; b < B_c; b += blockDim.x)
@@ -252,20 +252,20 @@ __global__ __launch_bounds__(kInvThreads) void inv_passes_kernel(
 __global__ __launch_bounds__(kInvThreads) void inv_scatter_kernel(
     const int32_t* __restrict__ block_idx, int k, int64_t q_begin, int64_t q_count, int64_t B_c,
     int64_t T64, const int32_t* __restrict__ colpre, const int32_t* __restrict__ blk_offsets,
-    int32_t* __restrict__ entries) {
+    int32_t* __restrict__ entries, int bk) {
   extern __shared__ unsigned long long mask[];
   const int64_t tq = blockIdx.x, seq = blockIdx.y;
   const int64_t q0 = tq * 64;
   const int nrows = static_cast<int>(min<int64_t>(64, q_count - q0));
   const int32_t* rows = block_idx + (seq * q_count + q0) * k;
   int nbad;
-  build_masks(rows, k, q_begin, q0, nrows, mask, &nbad);
+  build_masks(rows, k, q_begin, q0, nrows, mask, &nbad, bk);
   const int32_t* pre = colpre + (seq * T64 + tq) * B_c;
   const int32_t* off = blk_offsets + seq * (B_c + 1);
   for (int e = threadIdx.x; e < nrows * k; e += blockDim.x) {
     const int row = e / k, slot = e % k;
     const int v = rows[e];
-    const int L = static_cast<int>((q_begin + q0 + row) / kBk);
+    const int L = static_cast<int>((q_begin + q0 + row) / bk);
     if (v < 0 || v > L) continue;
     const int rank = __popcll(mask[v] & ((1ull << row) - 1ull));
     entries[off[v] + pre[v] + rank] = static_cast<int32_t>((q0 + row) * k + slot);
@@ -278,8 +278,8 @@ bool g_lds_attr_set = false;
 
 hipError_t launch_invert(const int32_t* block_idx, int batch, int H_kv, int G, int k,
                          int64_t q_begin, int64_t q_count, int32_t* blk_offsets,
-                         int32_t* blk_entries, int32_t* sched, hipStream_t stream) {
-  const SchedLayout s = sched_layout(batch, H_kv, G, k, q_begin, q_count);
+                         int32_t* blk_entries, int32_t* sched, hipStream_t stream, int bk) {
+  const SchedLayout s = sched_layout(batch, H_kv, G, k, q_begin, q_count, bk);
   const int64_t nseq = static_cast<int64_t>(batch) * H_kv;
   const size_t lds = static_cast<size_t>(s.B_c) * sizeof(unsigned long long);
   if (!g_lds_attr_set) {
@@ -299,7 +299,7 @@ hipError_t launch_invert(const int32_t* block_idx, int batch, int H_kv, int G, i
   const int epp = static_cast<int>(s.EPP);
   const dim3 tiles(static_cast<unsigned>(s.T64), static_cast<unsigned>(nseq));
   hipLaunchKernelGGL(inv_count_kernel, tiles, dim3(kInvThreads), lds, stream, block_idx, k, q_begin,
-                     q_count, s.B_c, s.T64, cnt, bad);
+                     q_count, s.B_c, s.T64, cnt, bad, bk);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(inv_colscan_kernel, dim3(static_cast<unsigned>((s.B_c + 63) / 64), nseq),
@@ -312,7 +312,7 @@ hipError_t launch_invert(const int32_t* block_idx, int batch, int H_kv, int G, i
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(inv_scatter_kernel, tiles, dim3(kInvThreads), lds, stream, block_idx, k, q_begin,
-                     q_count, s.B_c, s.T64, cnt, blk_offsets, blk_entries);
+                     q_count, s.B_c, s.T64, cnt, blk_offsets, blk_entries, bk);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t pgrid = s.nseg < 8192 ? s.nseg : 8192;

@@ -99,12 +99,12 @@ __device__ __forceinline__ u32x2 e4m3x4_to_bf16x4(uint32_t w) {
 hipError_t launch_index_topk(const uint16_t* q_idx, const uint16_t* k_idx, int batch, int64_t N,
                              int H_kv, int d_idx, int k, int64_t q_begin, int64_t q_count,
                              int32_t* block_idx, hipStream_t stream, int force_first = 0,
-                             int window = 1);
+                             int window = 1, int bk = kBk);
 
 // FLOP-matched sliding-window selection: block 0 and the k - 1 blocks ending
 // at the local one (all of 0 .. L when L < k), ascending, -1 padded.
 hipError_t launch_window_select(int batch, int H_kv, int k, int64_t q_begin, int64_t q_count,
-                                int32_t* block_idx, hipStream_t stream);
+                                int32_t* block_idx, hipStream_t stream, int bk = kBk);
 
 // Inversion scratch layout (all offsets in 4-byte words, 256-byte aligned).
 // A segment is a (seq, block) bin restricted to one query window; segments are
@@ -137,11 +137,13 @@ struct PassDesc {
   int32_t start, cnt, seq, blk;
 };
 
-SchedLayout sched_layout(int batch, int H_kv, int G, int k, int64_t q_begin, int64_t q_count);
+// bk: tokens per key block (32, 64 or 128).
+SchedLayout sched_layout(int batch, int H_kv, int G, int k, int64_t q_begin, int64_t q_count,
+                         int bk = kBk);
 
 hipError_t launch_invert(const int32_t* block_idx, int batch, int H_kv, int G, int k,
                          int64_t q_begin, int64_t q_count, int32_t* blk_offsets,
-                         int32_t* blk_entries, int32_t* sched, hipStream_t stream);
+                         int32_t* blk_entries, int32_t* sched, hipStream_t stream, int bk = kBk);
 
 // Multiply-high reciprocal of a slot count d <= 32 (exact for 31-bit
 // dividends): n / d == umulhi(n, magic) >> shift for d >= 2.
@@ -154,7 +156,7 @@ hipError_t launch_sparse_attn(const void* q, const void* k, const void* v, bool 
                               float out_scale, const int32_t* blk_offsets,
                               const int32_t* blk_entries, const int32_t* sched, int64_t q_begin,
                               int64_t q_count, uint16_t* o_part, float* lse_part,
-                              hipStream_t stream);
+                              hipStream_t stream, int bk = kBk);
 
 hipError_t launch_combine(const int32_t* block_idx, const uint16_t* o_part, const float* lse_part,
                           int batch, int64_t N, int H_kv, int G, int k, int64_t q_begin,
@@ -177,6 +179,6 @@ hipError_t launch_decode(const uint16_t* q, const uint16_t* q_idx, const uint16_
                          const uint16_t* k_idx, int batch, int64_t N, int H_sel, int G, int kv_shift, int d_idx,
                          int kslots, float scale_log2, float* scores, int32_t* block_idx,
                          uint16_t* o_part, float* lse_part, uint16_t* o, float* lse,
-                         hipStream_t stream);
+                         hipStream_t stream, int bk = kBk);
 
 }  // namespace msa

@@ -202,7 +202,11 @@ struct QFrag<true> {
   }
 };
 
-template <int G, bool FP8>
+// BKS: log2 of the key block size.  Blocks of 32 or 64 tokens (the paper's
+// block-size ablation) stage their tokens into the 128-key tile with zeros
+// after them, and every pass hides the keys past the block: the same kernel
+// at 2x or 4x the MFMA work per visible key.
+template <int G, bool FP8, int BKS>
 __global__ __launch_bounds__(kThreads, 8 / kWaves) void sparse_attn_kernel(
     const void* __restrict__ qp, const void* __restrict__ kp, const void* __restrict__ vp,
     int64_t N, int H_sel, int kv_shift, int kslots, uint32_t kdiv_magic, int kdiv_shift, float scale_log2,
@@ -277,7 +281,7 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void sparse_attn_kernel(
   };
 
   auto stage = [&](const PassDesc& D) {
-    const int64_t key0 = static_cast<int64_t>(D.blk) * kBk;
+    const int64_t key0 = static_cast<int64_t>(D.blk) << BKS;
     // selection group r reads K/V head r >> kv_shift of the H_sel >> kv_shift heads
     const int bat = D.seq / H_sel, r = D.seq - bat * H_sel;
     const int H_kv = H_sel >> kv_shift;
@@ -285,7 +289,7 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void sparse_attn_kernel(
     const int64_t row0 = (static_cast<int64_t>(bat) * N + key0) * H_kv + (r >> kv_shift);
     stage_kv<FP8>(static_cast<const uint8_t*>(kp) + row0 * kDh * EB,
                   static_cast<const uint8_t*>(vp) + row0 * kDh * EB, rstride,
-                  static_cast<int>(min<int64_t>(kBk, N - key0)), k_lds, vt_lds);
+                  static_cast<int>(min<int64_t>(int64_t(1) << BKS, N - key0)), k_lds, vt_lds);
   };
 
   // S^T = K_b Q^T of one pass: acc[mt] holds keys 32mt + 8(e/4) + 4h + (e%4)
@@ -324,12 +328,18 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void sparse_attn_kernel(
   // every pass), and the mask is a bit select on the sign of lim - key, which
   // needs no scalar condition registers.
   auto mask_own = [&](f32x16(&acc)[4], const RowRef& rr, int blk) {
-    const bool own = blk == (rr.i >> 7);
+    constexpr int BK = 1 << BKS;
+    constexpr int MT = BK / 32;  // key tiles that hold the block's tokens
+    // Smaller blocks: the zero keys BK .. 127 after the block are hidden in
+    // every pass (compile-time tiles).
+#pragma unroll
+    for (int mt = MT; mt < 4; ++mt) acc[mt] = f32x16{} - __builtin_huge_valf();
+    const bool own = blk == (rr.i >> BKS);
     if (__any(own)) {
       asm volatile("" ::: "memory");
-      const int lim = (own ? rr.i - blk * kBk : kBk - 1) - 4 * h;
+      const int lim = (own ? rr.i - (blk << BKS) : BK - 1) - 4 * h;
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
+      for (int mt = 0; mt < MT; ++mt) {
 #pragma unroll
         for (int el = 0; el < 16; ++el) {
           const uint32_t hide = static_cast<uint32_t>((lim - (32 * mt + 8 * (el >> 2) + (el & 3))) >> 31);
@@ -558,12 +568,12 @@ void kdiv_params(int d, uint32_t* magic, int* shift) {
 
 namespace {
 
-template <int G>
+template <int G, int BKS>
 hipError_t launch_g(const void* q, const void* k, const void* v, bool fp8, int batch, int64_t N,
                     int H_sel, int kv_shift, int kslots, float scale_log2, float out_scale,
                     const int32_t* blk_entries, const int32_t* sched, int64_t q_begin,
                     int64_t q_count, uint16_t* o_part, float* lse_part, hipStream_t stream) {
-  const SchedLayout s = sched_layout(batch, H_sel, G, kslots, q_begin, q_count);
+  const SchedLayout s = sched_layout(batch, H_sel, G, kslots, q_begin, q_count, 1 << BKS);
   // Never more workgroups than passes, so every workgroup has work when the
   // range is small.
   int64_t grid = static_cast<int64_t>(device_cus()) * kAttnWgPerCu;
@@ -573,7 +583,8 @@ hipError_t launch_g(const void* q, const void* k, const void* v, bool fp8, int b
   uint32_t magic = 0;
   int shift = 0;
   kdiv_params(kslots, &magic, &shift);
-  auto kern = fp8 ? sparse_attn_kernel<G, true> : sparse_attn_kernel<G, false>;
+  // fp8 runs with 128-token blocks only (the entry point rejects the rest)
+  auto kern = (fp8 && BKS == 7) ? sparse_attn_kernel<G, true, 7> : sparse_attn_kernel<G, false, BKS>;
   hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(grid)), dim3(kThreads), 0, stream, q, k, v,
                      N, H_sel, kv_shift, kslots, magic, shift, scale_log2, out_scale, blk_entries,
                      sched + s.off_segp, reinterpret_cast<const PassDesc*>(sched + s.off_pass),
@@ -589,11 +600,17 @@ hipError_t launch_sparse_attn(const void* q, const void* k, const void* v, bool 
                               float out_scale, const int32_t* blk_offsets,
                               const int32_t* blk_entries, const int32_t* sched, int64_t q_begin,
                               int64_t q_count, uint16_t* o_part, float* lse_part,
-                              hipStream_t stream) {
-#define MSA_ATTN_CASE(GG)                                                                      \
-  case GG:                                                                                     \
-    return launch_g<GG>(q, k, v, fp8, batch, N, H_sel, kv_shift, kslots, scale_log2, out_scale, \
-                        blk_entries, sched, q_begin, q_count, o_part, lse_part, stream);
+                              hipStream_t stream, int bk) {
+#define MSA_ATTN_CASE(GG)                                                                           \
+  case GG:                                                                                          \
+    if (bk == 32)                                                                                   \
+      return launch_g<GG, 5>(q, k, v, fp8, batch, N, H_sel, kv_shift, kslots, scale_log2, out_scale, \
+                             blk_entries, sched, q_begin, q_count, o_part, lse_part, stream);       \
+    if (bk == 64)                                                                                   \
+      return launch_g<GG, 6>(q, k, v, fp8, batch, N, H_sel, kv_shift, kslots, scale_log2, out_scale, \
+                             blk_entries, sched, q_begin, q_count, o_part, lse_part, stream);       \
+    return launch_g<GG, 7>(q, k, v, fp8, batch, N, H_sel, kv_shift, kslots, scale_log2, out_scale,   \
+                           blk_entries, sched, q_begin, q_count, o_part, lse_part, stream);
   switch (G) {
     MSA_ATTN_CASE(1)
     MSA_ATTN_CASE(2)

@@ -12,11 +12,12 @@ namespace msa {
 namespace {
 
 __global__ __launch_bounds__(256) void window_select_kernel(int64_t rows, int k, int64_t q_begin,
-                                                            int64_t q_count, int32_t* __restrict__ block_idx) {
+                                                            int64_t q_count, int bk,
+                                                            int32_t* __restrict__ block_idx) {
   const int64_t f = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;  // (seq, row)
   if (f >= rows) return;
   const int64_t i = q_begin + f % q_count;
-  const int L = static_cast<int>(i / kBk);
+  const int L = static_cast<int>(i / bk);
   int32_t* dst = block_idx + f * k;
   if (L < k) {
     for (int s = 0; s < k; ++s) dst[s] = s <= L ? s : -1;
@@ -29,11 +30,11 @@ __global__ __launch_bounds__(256) void window_select_kernel(int64_t rows, int k,
 }  // namespace
 
 hipError_t launch_window_select(int batch, int H_kv, int k, int64_t q_begin, int64_t q_count,
-                                int32_t* block_idx, hipStream_t stream) {
+                                int32_t* block_idx, hipStream_t stream, int bk) {
   const int64_t rows = static_cast<int64_t>(batch) * H_kv * q_count;
   const int64_t grid = (rows + 255) / 256;
   hipLaunchKernelGGL(window_select_kernel, dim3(static_cast<unsigned>(grid)), dim3(256), 0, stream, rows, k,
-                     q_begin, q_count, block_idx);
+                     q_begin, q_count, bk, block_idx);
   return hipGetLastError();
 }
 

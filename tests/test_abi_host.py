@@ -63,7 +63,7 @@ def dims(**kw):
 
 @pytest.mark.parametrize("kw,status", [
     (dict(H_q=9), 2), (dict(G=3), 2), (dict(N=0), 2), (dict(k=0), 2), (dict(batch=0), 2),
-    (dict(d_h=64), 3), (dict(B_k=64), 3), (dict(d_idx=96), 3), (dict(k=33), 3),
+    (dict(d_h=64), 3), (dict(B_k=96), 3), (dict(B_k=256), 3), (dict(d_idx=96), 3), (dict(k=33), 3),
     (dict(H_q=6, H_kv=2), 3), (dict(N=16384 * 128 + 1), 3),
 ])
 def test_index_topk_rejects_bad_dims(L, kw, status):
@@ -108,6 +108,10 @@ def test_workspace_and_opts(L):
     assert L.msa_workspace_size(ctypes.byref(d), ctypes.byref(bad), ctypes.byref(n)) == 2
     bad = msa.make_opts(dtype="fp8", q_scale=0.0)
     assert L.msa_workspace_size(ctypes.byref(d), ctypes.byref(bad), ctypes.byref(n)) == 2
+    d64 = dims(B_k=64)
+    assert L.msa_workspace_size(ctypes.byref(d64), ctypes.byref(o), ctypes.byref(n)) == 0
+    f8 = msa.make_opts(dtype="fp8")
+    assert L.msa_workspace_size(ctypes.byref(d64), ctypes.byref(f8), ctypes.byref(n)) == 3
     bad = msa.make_opts()
     bad.qkv_dtype = 7
     assert L.msa_workspace_size(ctypes.byref(d), ctypes.byref(bad), ctypes.byref(n)) == 3

@@ -61,11 +61,13 @@ INDEX_CASES = [
     TINY.with_(N=3000, k=7, H_q=4, H_kv=1),
     TINY.with_(N=2500, k=5, H_q=64, H_kv=4, d_idx=128),
     TINY.with_(N=2000, k=4, H_q=16, H_kv=2, H_idx=8),       # more index heads than K/V heads
+    TINY.with_(N=1500, k=6, B_k=64),                        # 64-token blocks
+    TINY.with_(N=1000, k=8, B_k=32, d_idx=128),             # 32-token blocks
     TINY.with_(batch=2, N=1300),
 ]
 
 
-@pytest.mark.parametrize("w", INDEX_CASES, ids=lambda w: f"N{w.N}_hsel{w.H_sel}_d{w.d_idx}_k{w.k}_b{w.batch}")
+@pytest.mark.parametrize("w", INDEX_CASES, ids=lambda w: f"N{w.N}_hsel{w.H_sel}_d{w.d_idx}_k{w.k}_bk{w.B_k}_b{w.batch}")
 def test_index_topk_parity(w):
     log(f"index_topk N={w.N} H_kv={w.H_kv} d_idx={w.d_idx} k={w.k} batch={w.batch}")
     t = device_inputs(w, DEV)
@@ -159,6 +161,8 @@ ATTN_CASES = [
     TINY.with_(N=1300, k=4, batch=2, H_q=16, H_kv=4),
     TINY.with_(N=1100, k=4, H_q=16, H_kv=2, H_idx=4),     # index heads: 2 per K/V head, G_sel = 4
     TINY.with_(N=900, k=3, H_q=16, H_kv=2, H_idx=16, batch=2),   # one index head per query head
+    TINY.with_(N=1000, k=6, B_k=64),                      # 64-token blocks
+    TINY.with_(N=700, k=9, B_k=32, H_q=32, H_kv=2),       # 32-token blocks, G = 16
 ]
 
 
@@ -182,7 +186,7 @@ def _oracle_partials(w, sel, rows):
     return parts
 
 
-@pytest.mark.parametrize("w", ATTN_CASES, ids=lambda w: f"N{w.N}_G{w.G}_Gs{w.G_sel}_k{w.k}_{w.dtype}_b{w.batch}")
+@pytest.mark.parametrize("w", ATTN_CASES, ids=lambda w: f"N{w.N}_G{w.G}_Gs{w.G_sel}_k{w.k}_bk{w.B_k}_{w.dtype}_b{w.batch}")
 def test_attention_and_combine_parity(w):
     """Feed the oracle's selection to the GPU inversion, attention and combine."""
     log(f"attention N={w.N} H_q={w.H_q} H_kv={w.H_kv} k={w.k} dtype={w.dtype} batch={w.batch}")
@@ -257,7 +261,9 @@ def test_combine_parity_random_partials():
 
 FWD_CASES = [TINY, TINY.with_(N=1000, k=5), TINY.with_(N=2304, k=4, q_chunk=512),
              TINY.with_(N=3000, H_q=32, H_kv=2, k=8, d_idx=128, dtype="fp8"),
-             TINY.with_(N=1800, H_q=32, H_kv=2, H_idx=8, k=5, q_chunk=768)]
+             TINY.with_(N=1800, H_q=32, H_kv=2, H_idx=8, k=5, q_chunk=768),
+             TINY.with_(N=1300, k=10, B_k=64, q_chunk=512),
+             TINY.with_(N=900, k=12, B_k=32, H_q=64, H_kv=4, d_idx=128)]
 
 
 @pytest.mark.parametrize("w", FWD_CASES, ids=lambda w: f"N{w.N}_k{w.k}_{w.dtype}_chunk{w.q_chunk}")
@@ -334,7 +340,8 @@ def test_forced_index_parity(w, first, window):
                 assert (gsel[b, r][need] == (L - back)[need][:, None]).any(axis=1).all()
 
 
-WINDOW_CASES = [TINY.with_(N=3000, k=6), TINY.with_(N=1000, k=4, batch=2, H_q=32, H_kv=2)]
+WINDOW_CASES = [TINY.with_(N=3000, k=6), TINY.with_(N=1000, k=4, batch=2, H_q=32, H_kv=2),
+                TINY.with_(N=900, k=5, B_k=64)]
 
 
 @pytest.mark.parametrize("w", WINDOW_CASES, ids=lambda w: f"N{w.N}_k{w.k}_b{w.batch}")
@@ -464,6 +471,8 @@ DECODE_CASES = [
     TINY.with_(N=4000, k=32, H_q=2, H_kv=2, plant=4),   # G = 1, planted hot blocks
     TINY.with_(N=1500, k=7, H_q=32, H_kv=4, batch=2),   # G = 8
     TINY.with_(N=2200, k=6, H_q=32, H_kv=2, H_idx=8, batch=2),   # 4 index heads per K/V head
+    TINY.with_(N=1999, k=8, B_k=64, batch=2),
+    TINY.with_(N=1000, k=16, B_k=32, d_idx=128),
 ]
 
 
