@@ -39,9 +39,9 @@
  *     a multiple of B_k.  B_c = ceil((q_begin + q_count) / B_k) is the number
  *     of key blocks of the range.
  *
- * Supported shapes (MSA_ERR_UNSUPPORTED otherwise): d_h = 128, B_k = 128,
- * d_idx in {64, 128}, G in {1, 2, 4, 8, 16}, 1 <= k <= 32, B_c <= 16384
- * (N <= 2,097,152), batch * H_sel * q_count * k < 2^31.
+ * Supported shapes (MSA_ERR_UNSUPPORTED otherwise): d_h = 128, B_k in {32, 64, 128}
+ * (128 for fp8 Q/K/V), d_idx in {64, 128}, G in {1, 2, 4, 8, 16}, 1 <= k <= 32,
+ * B_c <= 16384 (N <= 16384 B_k), batch * H_sel * q_count * k < 2^31.
  *
  * Selection groups: H_sel = dims->H_idx when nonzero, else H_kv, index (proxy)
  * query heads, each choosing blocks for its G_sel = H_q / H_sel adjacent query
