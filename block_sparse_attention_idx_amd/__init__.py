@@ -106,7 +106,7 @@ def lib():
             "msa_forward": ([D, O, P, P, P, P, P, P, P, P, P, SZ, P], ctypes.c_int),
             "msa_dense_attn_fwd": ([D, O, P, P, P, I64, I64, P, P, P], ctypes.c_int),
             "msa_decode_workspace_size": ([D, O, ctypes.POINTER(SZ)], ctypes.c_int),
-            "msa_decode": ([D, O, P, P, P, P, P, P, P, P, P, SZ, P], ctypes.c_int),
+            "msa_decode": ([D, O, P, P, P, P, P, P, P, P, P, P, SZ, P], ctypes.c_int),
             "msa_index_topk_forced": ([D, P, P, I64, I64, ctypes.c_int, ctypes.c_int, P, P], ctypes.c_int),
             "msa_window_select": ([D, I64, I64, P, P], ctypes.c_int),
         }
@@ -317,8 +317,9 @@ def msa_decode_workspace_size(dims: msa_dims, opts: msa_opts) -> int:
 
 
 def msa_decode(dims: msa_dims, opts: msa_opts, q, q_idx, k, v, k_idx, o=None, lse=None,
-               block_idx_out=None, workspace=None, want_lse: bool = False):
-    """One decode step (the token at position N - 1 of each sequence).
+               block_idx_out=None, workspace=None, want_lse: bool = False, seq_lens=None):
+    """One decode step: the last token of each sequence (position seq_lens[b] - 1,
+    or N - 1 when seq_lens is None; seq_lens an int32 device tensor [batch]).
     q [batch, H_q, d_h], q_idx [batch, H_sel, d_idx]; caches as for msa_forward.
     Returns (o bf16 [batch, H_q, d_h], lse fp32 [batch, H_q] or None, block_idx_out)."""
     import torch
@@ -331,7 +332,7 @@ def msa_decode(dims: msa_dims, opts: msa_opts, q, q_idx, k, v, k_idx, o=None, ls
         workspace = _empty((nbytes,), torch.uint8, q)
     with _dev(q):
         _check(lib().msa_decode(ctypes.byref(dims), ctypes.byref(opts), _p(q), _p(q_idx), _p(k), _p(v),
-                                _p(k_idx), _p(o), _p(lse), _p(block_idx_out), _p(workspace),
+                                _p(k_idx), _p(seq_lens), _p(o), _p(lse), _p(block_idx_out), _p(workspace),
                                 workspace.numel() * workspace.element_size(), _stream(q)),
                "msa_decode")
     return o, lse, block_idx_out

@@ -343,13 +343,14 @@ int msa_decode_workspace_size(const msa_dims* dims, const msa_opts* opts, size_t
 }
 
 int msa_decode(const msa_dims* dims, const msa_opts* opts, const void* q, const void* q_idx,
-               const void* k, const void* v, const void* k_idx, void* o, float* lse,
-               int32_t* block_idx_out, void* workspace, size_t ws_bytes, void* stream) {
+               const void* k, const void* v, const void* k_idx, const int32_t* seq_lens, void* o,
+               float* lse, int32_t* block_idx_out, void* workspace, size_t ws_bytes, void* stream) {
   int st = check_decode(dims, opts);
   if (st) return st;
   if (!q || !q_idx || !k || !v || !k_idx || !o || !workspace) return MSA_ERR_NULL;
   if (misaligned(q) || misaligned(q_idx) || misaligned(k) || misaligned(v) || misaligned(k_idx) ||
       misaligned(o) || (lse && misaligned(lse)) || (block_idx_out && misaligned(block_idx_out)) ||
+      (seq_lens && (reinterpret_cast<uintptr_t>(seq_lens) & 3u)) ||
       (reinterpret_cast<uintptr_t>(workspace) & 255u))
     return MSA_ERR_ALIGN;
   const DecodeLayout L = decode_layout(dims);
@@ -363,7 +364,7 @@ int msa_decode(const msa_dims* dims, const msa_opts* opts, const void* q, const 
       static_cast<const uint16_t*>(v), static_cast<const uint16_t*>(k_idx), dims->batch, dims->N, HS(dims),
       GS(dims), KVS(dims), dims->d_idx, dims->k, sl2, reinterpret_cast<float*>(ws + L.off_scores), bi,
       reinterpret_cast<uint16_t*>(ws + L.off_opart), reinterpret_cast<float*>(ws + L.off_lpart),
-      static_cast<uint16_t*>(o), lse, static_cast<hipStream_t>(stream), dims->B_k);
+      static_cast<uint16_t*>(o), lse, static_cast<hipStream_t>(stream), dims->B_k, seq_lens);
   return e == hipSuccess ? MSA_OK : hip_fail(e);
 }
 

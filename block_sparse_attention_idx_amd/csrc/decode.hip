@@ -1,5 +1,6 @@
-// MSA decode: one new query per sequence (the last token, position N - 1)
-// against cached K, V and K^idx of the N tokens.
+// MSA decode: one new query per sequence (its last token, position len - 1)
+// against cached K, V and K^idx of its len tokens (len = N for every
+// sequence, or per-sequence lengths in caches of N slots).
 //
 // What is computed (the same definitions as the prefill, for row i = N - 1):
 //  * index branch ("MiniMax Sparse Attention (MSA)", Deep Dive > Index Branch
@@ -49,6 +50,14 @@ using namespace tile;
 
 constexpr int kScoreWaves = 4;  // key blocks per scoring workgroup
 
+// Tokens of sequence b: its entry of the per-sequence lengths (clamped to
+// [1, N]), or the cache length N for all when there are none.
+__device__ __forceinline__ int64_t seq_len_of(const int32_t* __restrict__ lens, int b, int64_t N) {
+  if (lens == nullptr) return N;
+  const int64_t l = lens[b];
+  return l < 1 ? 1 : (l > N ? N : l);
+}
+
 // Order-preserving map of an fp32 score (no NaN) onto uint32.
 __device__ __forceinline__ uint32_t ord_score(float x) {
   const uint32_t u = __float_as_uint(x);
@@ -59,7 +68,7 @@ __device__ __forceinline__ uint32_t ord_score(float x) {
 template <int DIDX, int KT>
 __global__ __launch_bounds__(64 * kScoreWaves) void decode_scores_kernel(
     const uint16_t* __restrict__ q_idx, const uint16_t* __restrict__ k_idx, int64_t N, int H_sel,
-    int L, int B, int batch, float* __restrict__ scores) {
+    int L, int B, int batch, const int32_t* __restrict__ lens, float* __restrict__ scores) {
   constexpr int STEPS = DIDX / 16;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int n = lane & 31, h = lane >> 5;
@@ -69,6 +78,8 @@ __global__ __launch_bounds__(64 * kScoreWaves) void decode_scores_kernel(
   // blocks of one sequence.  No barrier in this kernel.
   for (int64_t it = static_cast<int64_t>(blockIdx.x) * kScoreWaves + wave; it < items; it += nwaves) {
     const int bat = static_cast<int>(it / L), blk = static_cast<int>(it % L);
+    // blocks from this sequence's own local block on are not candidates
+    if (lens != nullptr && blk >= static_cast<int>((seq_len_of(lens, bat, N) - 1) / (32 * KT))) continue;
     // All 4 key tiles' A fragments (row 32 mt + n, dims 16 ks + 8 h .. + 7)
     // are requested before any is used.
     const uint16_t* kb = k_idx + (static_cast<int64_t>(bat) * N + static_cast<int64_t>(blk) * (32 * KT) + n) * DIDX + 8 * h;
@@ -129,11 +140,15 @@ __device__ __forceinline__ void insert_desc(uint64_t (&v)[KP], uint64_t x) {
 // (conflict-free).
 template <int KP>
 __global__ __launch_bounds__(topk_threads<KP>()) void decode_topk_kernel(const float* __restrict__ scores,
-                                                                         int L, int B, int k,
+                                                                         int L_all, int B, int k,
+                                                                         const int32_t* __restrict__ lens,
+                                                                         int64_t N, int H_sel, int bk,
                                                                          int32_t* __restrict__ block_idx) {
   constexpr int kTopkThreads = topk_threads<KP>();
   __shared__ uint64_t lists[KP * kTopkThreads / 2];
   const int seq = blockIdx.x;  // batch * H_sel + r
+  // this sequence's local block
+  const int L = lens == nullptr ? L_all : static_cast<int>((seq_len_of(lens, seq / H_sel, N) - 1) / bk);
   const int t = threadIdx.x;
   const float* row = scores + static_cast<int64_t>(seq) * B;
 
@@ -217,7 +232,8 @@ __global__ __launch_bounds__(topk_threads<KP>()) void decode_topk_kernel(const f
 template <int G>
 __global__ __launch_bounds__(kStageThreads, 1) void decode_partial_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-    int64_t N, int H_sel, int kv_shift, int kslots, int bk, float scale_log2, const int32_t* __restrict__ block_idx,
+    int64_t N, int H_sel, int kv_shift, int kslots, int bk, const int32_t* __restrict__ lens, float scale_log2,
+    const int32_t* __restrict__ block_idx,
     uint16_t* __restrict__ o_part, float* __restrict__ lse_part) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[kBufBytes];
   const int64_t item = blockIdx.x;  // (seq, slot)
@@ -229,7 +245,7 @@ __global__ __launch_bounds__(kStageThreads, 1) void decode_partial_kernel(
   const int tid = threadIdx.x;
   // Blocks of bk <= 128 tokens sit at the start of the 128-key tile; the keys
   // after them (and past the sequence end) are zero and hidden below.
-  const int nvalid = static_cast<int>(min<int64_t>(bk, N - static_cast<int64_t>(blk) * bk));
+  const int nvalid = static_cast<int>(min<int64_t>(bk, seq_len_of(lens, bat, N) - static_cast<int64_t>(blk) * bk));
   const int64_t rstride = static_cast<int64_t>(H_kv) * kDh * 2;
   const int64_t row0 = (static_cast<int64_t>(bat) * N + static_cast<int64_t>(blk) * bk) * H_kv + (r >> kv_shift);
   KVRegs R;
@@ -322,20 +338,21 @@ __global__ __launch_bounds__(kStageThreads, 1) void decode_partial_kernel(
 }
 
 template <int KP>
-hipError_t launch_topk(const float* scores, int nseq, int L, int B, int k, int32_t* block_idx,
-                       hipStream_t stream) {
+hipError_t launch_topk(const float* scores, int nseq, int L, int B, int k, const int32_t* lens, int64_t N,
+                       int H_sel, int bk, int32_t* block_idx, hipStream_t stream) {
   hipLaunchKernelGGL(decode_topk_kernel<KP>, dim3(static_cast<unsigned>(nseq)), dim3(topk_threads<KP>()), 0,
-                     stream, scores, L, B, k, block_idx);
+                     stream, scores, L, B, k, lens, N, H_sel, bk, block_idx);
   return hipGetLastError();
 }
 
 template <int G>
 hipError_t launch_partial(const uint16_t* q, const uint16_t* k, const uint16_t* v, int batch, int64_t N,
-                          int H_sel, int kv_shift, int kslots, int bk, float scale_log2, const int32_t* block_idx,
+                          int H_sel, int kv_shift, int kslots, int bk, const int32_t* lens, float scale_log2,
+                          const int32_t* block_idx,
                           uint16_t* o_part, float* lse_part, hipStream_t stream) {
   const int64_t items = static_cast<int64_t>(batch) * H_sel * kslots;
   hipLaunchKernelGGL(decode_partial_kernel<G>, dim3(static_cast<unsigned>(items)), dim3(kStageThreads), 0,
-                     stream, q, k, v, N, H_sel, kv_shift, kslots, bk, scale_log2, block_idx, o_part, lse_part);
+                     stream, q, k, v, N, H_sel, kv_shift, kslots, bk, lens, scale_log2, block_idx, o_part, lse_part);
   return hipGetLastError();
 }
 
@@ -345,9 +362,11 @@ hipError_t launch_decode(const uint16_t* q, const uint16_t* q_idx, const uint16_
                          const uint16_t* k_idx, int batch, int64_t N, int H_sel, int G, int kv_shift, int d_idx,
                          int kslots, float scale_log2, float* scores, int32_t* block_idx,
                          uint16_t* o_part, float* lse_part, uint16_t* o, float* lse,
-                         hipStream_t stream, int bk) {
+                         hipStream_t stream, int bk, const int32_t* lens) {
   const int B = static_cast<int>((N + bk - 1) / bk);
-  const int L = static_cast<int>((N - 1) / bk);  // the local block; blocks 0 .. L - 1 are scored
+  // the local block of a full-length sequence; blocks 0 .. L - 1 are scored
+  // (a shorter sequence scores only the blocks before its own local block)
+  const int L = static_cast<int>((N - 1) / bk);
   const int nseq = batch * H_sel;
   hipError_t e = hipSuccess;
   if (L > 0) {
@@ -357,7 +376,7 @@ hipError_t launch_decode(const uint16_t* q, const uint16_t* q_idx, const uint16_
     if (wgs > 1024) wgs = 1024;
     const dim3 g(static_cast<unsigned>(wgs)), t(64 * kScoreWaves);
 #define MSA_DEC_SCORES(D, KT) \
-  hipLaunchKernelGGL((decode_scores_kernel<D, KT>), g, t, 0, stream, q_idx, k_idx, N, H_sel, L, B, batch, scores)
+  hipLaunchKernelGGL((decode_scores_kernel<D, KT>), g, t, 0, stream, q_idx, k_idx, N, H_sel, L, B, batch, lens, scores)
     if (d_idx == 64) {
       if (bk == 32) MSA_DEC_SCORES(64, 1);
       else if (bk == 64) MSA_DEC_SCORES(64, 2);
@@ -371,19 +390,19 @@ hipError_t launch_decode(const uint16_t* q, const uint16_t* q_idx, const uint16_
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   const int km = kslots - 1;
-  if (km <= 1) e = launch_topk<1>(scores, nseq, L, B, kslots, block_idx, stream);
-  else if (km <= 2) e = launch_topk<2>(scores, nseq, L, B, kslots, block_idx, stream);
-  else if (km <= 4) e = launch_topk<4>(scores, nseq, L, B, kslots, block_idx, stream);
-  else if (km <= 8) e = launch_topk<8>(scores, nseq, L, B, kslots, block_idx, stream);
-  else if (km <= 16) e = launch_topk<16>(scores, nseq, L, B, kslots, block_idx, stream);
-  else e = launch_topk<32>(scores, nseq, L, B, kslots, block_idx, stream);
+  if (km <= 1) e = launch_topk<1>(scores, nseq, L, B, kslots, lens, N, H_sel, bk, block_idx, stream);
+  else if (km <= 2) e = launch_topk<2>(scores, nseq, L, B, kslots, lens, N, H_sel, bk, block_idx, stream);
+  else if (km <= 4) e = launch_topk<4>(scores, nseq, L, B, kslots, lens, N, H_sel, bk, block_idx, stream);
+  else if (km <= 8) e = launch_topk<8>(scores, nseq, L, B, kslots, lens, N, H_sel, bk, block_idx, stream);
+  else if (km <= 16) e = launch_topk<16>(scores, nseq, L, B, kslots, lens, N, H_sel, bk, block_idx, stream);
+  else e = launch_topk<32>(scores, nseq, L, B, kslots, lens, N, H_sel, bk, block_idx, stream);
   if (e != hipSuccess) return e;
   switch (G) {
-    case 1: e = launch_partial<1>(q, k, v, batch, N, H_sel, kv_shift, kslots, bk, scale_log2, block_idx, o_part, lse_part, stream); break;
-    case 2: e = launch_partial<2>(q, k, v, batch, N, H_sel, kv_shift, kslots, bk, scale_log2, block_idx, o_part, lse_part, stream); break;
-    case 4: e = launch_partial<4>(q, k, v, batch, N, H_sel, kv_shift, kslots, bk, scale_log2, block_idx, o_part, lse_part, stream); break;
-    case 8: e = launch_partial<8>(q, k, v, batch, N, H_sel, kv_shift, kslots, bk, scale_log2, block_idx, o_part, lse_part, stream); break;
-    case 16: e = launch_partial<16>(q, k, v, batch, N, H_sel, kv_shift, kslots, bk, scale_log2, block_idx, o_part, lse_part, stream); break;
+    case 1: e = launch_partial<1>(q, k, v, batch, N, H_sel, kv_shift, kslots, bk, lens, scale_log2, block_idx, o_part, lse_part, stream); break;
+    case 2: e = launch_partial<2>(q, k, v, batch, N, H_sel, kv_shift, kslots, bk, lens, scale_log2, block_idx, o_part, lse_part, stream); break;
+    case 4: e = launch_partial<4>(q, k, v, batch, N, H_sel, kv_shift, kslots, bk, lens, scale_log2, block_idx, o_part, lse_part, stream); break;
+    case 8: e = launch_partial<8>(q, k, v, batch, N, H_sel, kv_shift, kslots, bk, lens, scale_log2, block_idx, o_part, lse_part, stream); break;
+    case 16: e = launch_partial<16>(q, k, v, batch, N, H_sel, kv_shift, kslots, bk, lens, scale_log2, block_idx, o_part, lse_part, stream); break;
     default: return hipErrorInvalidValue;
   }
   if (e != hipSuccess) return e;

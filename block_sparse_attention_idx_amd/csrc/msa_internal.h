@@ -168,7 +168,9 @@ hipError_t launch_dense_attn(const uint16_t* q, const uint16_t* k, const uint16_
                              int64_t N, int H_kv, int G, int64_t q_begin, int64_t q_count,
                              float scale_log2, uint16_t* o, float* lse, hipStream_t stream);
 
-// Decode: one query (position N - 1) per sequence against cached K, V, K^idx.
+// Decode: one query per sequence (its last token) against cached K, V, K^idx;
+// lens (device, [batch], may be null = N for all) gives each sequence's
+// length within the N cache slots.
 // H_sel selection groups (index heads) of G query heads, group r reading K/V
 // head r >> kv_shift.  q [batch][H_q][d_h], q_idx [batch][H_sel][d_idx],
 // caches as for the prefill; scores [batch][H_sel][ceil(N / B_k)] fp32,
@@ -179,6 +181,6 @@ hipError_t launch_decode(const uint16_t* q, const uint16_t* q_idx, const uint16_
                          const uint16_t* k_idx, int batch, int64_t N, int H_sel, int G, int kv_shift, int d_idx,
                          int kslots, float scale_log2, float* scores, int32_t* block_idx,
                          uint16_t* o_part, float* lse_part, uint16_t* o, float* lse,
-                         hipStream_t stream, int bk = kBk);
+                         hipStream_t stream, int bk = kBk, const int32_t* lens = nullptr);
 
 }  // namespace msa

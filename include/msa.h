@@ -267,9 +267,9 @@ int msa_dense_attn_fwd(const msa_dims *dims, const msa_opts *opts, const void *q
 
 /*
  * msa_decode_workspace_size / msa_decode -- one decode step: the last token
- * (position N - 1) of each of `batch` sequences attends to the N cached
- * tokens.  Index branch, top-k with the forced local block, and the main
- * branch over the selected blocks, exactly as msa_forward computes row N - 1
+ * of each of `batch` sequences attends to its cached tokens.  Index branch,
+ * top-k with the forced local block, and the main branch over the selected
+ * blocks, exactly as msa_forward computes a sequence's last row
  * ("MiniMax Sparse Attention (MSA)", Deep Dive > Index Branch Architecture,
  * Exp-Free TopK Kernel, KV-Outer Sparse Attention step 6 for the merge;
  * "MiniMax Sparse Attention", sec. 2.1-2.2; the decode-shaped query-outer
@@ -277,8 +277,12 @@ int msa_dense_attn_fwd(const msa_dims *dims, const msa_opts *opts, const void *q
  *
  *   q              bf16 [batch][H_q][d_h]      the new token's queries
  *   q_idx          bf16 [batch][H_sel][d_idx]  its index queries
- *   k, v           bf16 [batch][N][H_kv][d_h]  the cache, token N - 1 included
+ *   k, v           bf16 [batch][N][H_kv][d_h]  the cache, the new token included
  *   k_idx          bf16 [batch][N][d_idx]      the index-key cache
+ *   seq_lens       int32 [batch] device array (may be NULL): tokens of each
+ *                  sequence, its new token at position seq_lens[b] - 1 of the
+ *                  N cache slots (values are clamped to [1, N]); NULL means
+ *                  every sequence has N tokens (4-byte aligned)
  *   o              bf16 [batch][H_q][d_h] output
  *   lse            fp32 [batch][H_q] output (may be NULL): natural-log LSE
  *   block_idx_out  int32 [batch][H_sel][k] (may be NULL): the selection, as a
@@ -290,8 +294,8 @@ int msa_dense_attn_fwd(const msa_dims *dims, const msa_opts *opts, const void *q
  */
 int msa_decode_workspace_size(const msa_dims *dims, const msa_opts *opts, size_t *bytes);
 int msa_decode(const msa_dims *dims, const msa_opts *opts, const void *q, const void *q_idx,
-               const void *k, const void *v, const void *k_idx, void *o, float *lse,
-               int32_t *block_idx_out, void *workspace, size_t ws_bytes, void *stream);
+               const void *k, const void *v, const void *k_idx, const int32_t *seq_lens, void *o,
+               float *lse, int32_t *block_idx_out, void *workspace, size_t ws_bytes, void *stream);
 
 #ifdef __cplusplus
 }

@@ -149,8 +149,9 @@ def test_decode_validation(L):
     # block scores, selection, partial outputs and their lse
     B = (2048 + 127) // 128
     assert ws >= 2 * B * 4 + 2 * 4 * 4 + 2 * 4 * 4 * 128 * 2 + 2 * 4 * 4 * 4
-    call = lambda d, o, ws_bytes=ws, q=FAKE, out=FAKE, wsp=FAKE: L.msa_decode(
-        ctypes.byref(d), ctypes.byref(o), q, FAKE, FAKE, FAKE, FAKE, out, None, None, wsp, ws_bytes, None)
+    call = lambda d, o, ws_bytes=ws, q=FAKE, out=FAKE, wsp=FAKE, lens=None: L.msa_decode(
+        ctypes.byref(d), ctypes.byref(o), q, FAKE, FAKE, FAKE, FAKE, lens, out, None, None, wsp, ws_bytes,
+        None)
     assert call(d, o, ws - 1) == 5
     assert call(d, msa.make_opts(dtype="fp8"), ws) == 3
     assert call(dims(H_q=66, H_kv=33), o) == 3
@@ -158,6 +159,7 @@ def test_decode_validation(L):
     assert call(d, o, q=None) == 1
     assert call(d, o, out=ODD) == 4
     assert call(d, o, wsp=ctypes.c_void_p(0x10010)) == 4     # workspace needs 256-byte alignment
+    assert call(d, o, lens=ctypes.c_void_p(0x10002)) == 4    # lengths are int32
     assert L.msa_decode_workspace_size(ctypes.byref(d), ctypes.byref(o), None) == 1
 
 

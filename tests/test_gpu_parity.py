@@ -528,6 +528,44 @@ def test_decode_matches_forward_last_row():
     assert lmx <= 1e-4
 
 
+@pytest.mark.parametrize("w,lens", [
+    (TINY.with_(N=3000, k=5, batch=5), [3000, 1, 128, 129, 2047]),
+    (TINY.with_(N=2200, k=6, H_q=32, H_kv=2, H_idx=8, batch=3), [700, 2200, 1000]),
+    (TINY.with_(N=1500, k=7, B_k=64, batch=2), [1500, 901]),
+], ids=lambda x: f"N{x.N}_b{x.batch}" if hasattr(x, "N") else "lens")
+def test_decode_ragged_lengths(w, lens):
+    """Per-sequence lengths: sequence b decodes its token lens[b] - 1 against
+    its first lens[b] cache slots (the rest of the cache is ignored)."""
+    log(f"decode ragged N={w.N} lens={lens}")
+    t = device_inputs(w, DEV)
+    lens_np = np.array(lens, np.int64)
+    ridx = torch.from_numpy(lens_np - 1).to(DEV)
+    bidx = torch.arange(w.batch, device=DEV)
+    q1 = t["q"][bidx, ridx].contiguous()
+    qi1 = t["q_idx"][bidx, ridx].contiguous()
+    bi = torch.empty((w.batch, w.H_sel, w.k), dtype=torch.int32, device=DEV)
+    out, lse, _ = msa.msa_decode(dims_of(w), msa.make_opts(), q1, qi1, t["k"], t["v"], t["k_idx"],
+                                 block_idx_out=bi, want_lse=True,
+                                 seq_lens=torch.tensor(lens, dtype=torch.int32, device=DEV))
+    torch.cuda.synchronize()
+    out, lse, bi = out.float().cpu().numpy(), lse.cpu().numpy(), bi.cpu().numpy()
+    for b, n in enumerate(lens):
+        row = np.array([n - 1])            # the sequence as a cache of its own length
+        flat = b * w.N + row
+        keys = b * w.N + np.arange(n)
+        ob, marg, M = oracle.index_topk(n, w.B_k, w.k, row, synth.host_rows(w, "q_idx", flat),
+                                        synth.host_rows(w, "k_idx", keys))
+        gsel = bi[b][:, None, :]
+        check_selection(gsel, ob, marg, M, w.k, what=f"ragged b{b}")
+        O, L = oracle.attention(n, w.B_k, row, synth.host_rows(w, "q", flat), synth.host_rows(w, "k", keys),
+                                synth.host_rows(w, "v", keys), gsel)
+        mx, mn = err_stats(out[b], O[0])
+        log(f"  seq {b} (len {n}): output max abs {mx:.3g} mean abs {mn:.3g}")
+        assert mx <= 2e-2 and mn <= 2e-3
+        lmx, _ = err_stats(lse[b], L[0])
+        assert lmx <= 1e-3
+
+
 @pytest.mark.parametrize("w", [synth.P128K_HOT.with_(batch=4), synth.P1M],
                          ids=lambda w: f"{w.name}_b{w.batch}")
 def test_decode_full_size(w):
