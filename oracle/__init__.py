@@ -12,10 +12,15 @@ from the definitions on the pages:
 * sparse main attention -- "MiniMax Sparse Attention", sec. 2.1 and 2.2;
 * split-K log-sum-exp combine -- "MiniMax Sparse Attention (MSA)", Deep Dive >
   KV-Outer Sparse Attention (two-phase forward);
-* block-index inversion -- "Flash-MSA", Backward.
+* block-index inversion -- "Flash-MSA", Backward;
+* the backward pass: gradients of the sparse main attention and the KL
+  alignment gradient of the index branch -- "MiniMax Sparse Attention (MSA)",
+  Deep Dive > KL Alignment Loss; "Flash-MSA", Backward and KL Divergence Loss.
 
-The arithmetic lives in ``msa_oracle.c`` (plain C, OpenMP over rows); this
-module builds it with gcc and marshals numpy arrays through ctypes.
+The forward arithmetic lives in ``msa_oracle.c`` (plain C, OpenMP over rows);
+this module builds it with gcc and marshals numpy arrays through ctypes.  The
+backward (``backward`` below) is plain numpy in float64, one (query, group)
+at a time.
 """
 from __future__ import annotations
 
@@ -227,3 +232,93 @@ def decode_e4m3(c: int) -> float:
 
 def num_threads() -> int:
     return int(lib().oracle_num_threads())
+
+
+def _bf16_f64(h):
+    """Raw bf16 bit patterns -> float64 (the bits are the top half of an IEEE
+    binary32)."""
+    h = np.ascontiguousarray(h, np.uint16)
+    return (h.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def _softmax(x):
+    m = x.max(axis=-1, keepdims=True)
+    e = np.exp(x - m)
+    return e / e.sum(axis=-1, keepdims=True)
+
+
+def backward(N, B_k, pos, q_rows, K, V, q_idx_rows, k_idx, block_idx, dO_rows,
+             softmax_scale=None, kl_weight=1.0):
+    """Backward pass of MSA for the given query rows, float64.
+
+    Inputs are raw bf16 bit patterns (uint16): q_rows [n, H_q, d_h]; K, V
+    [N, H_kv, d_h]; q_idx_rows [n, H_sel, d_idx]; k_idx [N, d_idx]; dO_rows
+    [n, H_q, d_h] (the gradient of the loss with respect to the attention
+    output).  block_idx [H_sel, n, k] is the forward's selection (-1 = empty
+    slot).
+
+    For query i and selection group r the token set T is the tokens of the
+    selected blocks that are visible to i (j <= i) -- "MiniMax Sparse
+    Attention", sec. 2.2.  With p_h = softmax over T of scale * Q_h . K_j for
+    each head h of the group:
+
+    * main branch (loss sum_h dO_h . O_h, O_h = sum_j p_hj V_j): the gradients
+      of exact softmax attention restricted to T;
+    * index branch ("MiniMax Sparse Attention (MSA)", Deep Dive > KL Alignment
+      Loss): teacher P_j = mean over the group's heads of p_hj (held constant),
+      proxy p_px = softmax over T of z_j = q_idx . k_idx_j / sqrt(d_idx), the
+      per-row loss KL(P || p_px), and -- "Flash-MSA", KL Divergence Loss -- the
+      gradient kl_weight * (p_px - P) on z, carried back to q_idx and k_idx.
+
+    Returns a dict of float64 arrays: dq [n, H_q, d_h], dk, dv [N, H_kv, d_h]
+    (contributions of these rows), dq_idx [n, H_sel, d_idx], dk_idx [N, d_idx],
+    kl [H_sel, n] (per-row KL, not weighted), O [n, H_q, d_h], lse [n, H_q]."""
+    q, Kf, Vf = _bf16_f64(q_rows), _bf16_f64(K), _bf16_f64(V)
+    qi, ki, dO = _bf16_f64(q_idx_rows), _bf16_f64(k_idx), _bf16_f64(dO_rows)
+    bi = np.asarray(block_idx)
+    pos = np.asarray(pos, np.int64)
+    n, H_q, d_h = q.shape
+    H_kv = Kf.shape[1]
+    H_sel = bi.shape[0]
+    d_idx = qi.shape[2]
+    G_sel = H_q // H_sel
+    sel_per_kv = H_sel // H_kv
+    scale = 1.0 / np.sqrt(d_h) if softmax_scale is None else float(softmax_scale)
+    idx_scale = 1.0 / np.sqrt(d_idx)
+    out = {
+        "dq": np.zeros((n, H_q, d_h)), "dk": np.zeros((N, H_kv, d_h)),
+        "dv": np.zeros((N, H_kv, d_h)), "dq_idx": np.zeros((n, H_sel, d_idx)),
+        "dk_idx": np.zeros((N, d_idx)), "kl": np.zeros((H_sel, n)),
+        "O": np.zeros((n, H_q, d_h)), "lse": np.zeros((n, H_q)),
+    }
+    for row in range(n):
+        i = int(pos[row])
+        for r in range(H_sel):
+            blocks = [int(b) for b in bi[r, row] if b >= 0]
+            T = np.concatenate([np.arange(b * B_k, min((b + 1) * B_k, N)) for b in blocks])
+            T = T[T <= i]
+            c = r // sel_per_kv                      # K/V head of group r
+            heads = slice(r * G_sel, (r + 1) * G_sel)
+            Kt, Vt, Qh, dOh = Kf[T, c], Vf[T, c], q[row, heads], dO[row, heads]
+            s = scale * (Qh @ Kt.T)                  # [G_sel, |T|]
+            p = _softmax(s)
+            Oh = p @ Vt
+            out["O"][row, heads] = Oh
+            out["lse"][row, heads] = s.max(axis=1) + np.log(np.exp(s - s.max(axis=1, keepdims=True)).sum(axis=1))
+            # main branch: dV = p^T dO, dP = dO V^T, dS = p (dP - rowsum(dO O))
+            out["dv"][T, c] += p.T @ dOh
+            dP = dOh @ Vt.T
+            dS = p * (dP - (dOh * Oh).sum(axis=1, keepdims=True))
+            out["dq"][row, heads] = scale * (dS @ Kt)
+            out["dk"][T, c] += scale * (dS.T @ Qh)
+            # index branch: KL(P || p_px) and its gradient on z
+            z = idx_scale * (ki[T] @ qi[row, r])
+            log_ppx = z - (z.max() + np.log(np.exp(z - z.max()).sum()))
+            ppx = np.exp(log_ppx)
+            P = p.mean(axis=0)
+            nz = P > 0
+            out["kl"][r, row] = np.sum(P[nz] * (np.log(P[nz]) - log_ppx[nz]))
+            g = kl_weight * (ppx - P)
+            out["dq_idx"][row, r] = idx_scale * (g @ ki[T])
+            out["dk_idx"][T] += idx_scale * np.outer(g, qi[row, r])
+    return out
