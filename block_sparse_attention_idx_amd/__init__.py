@@ -28,7 +28,7 @@ EXPORTS = (
     "msa_invert_workspace_size", "msa_invert_blocks", "msa_invert_status",
     "msa_sparse_attn_fwd", "msa_combine", "msa_workspace_size", "msa_forward",
     "msa_dense_attn_fwd", "msa_decode_workspace_size", "msa_decode", "msa_index_topk_forced",
-    "msa_window_select",
+    "msa_window_select", "msa_backward_workspace_size", "msa_backward",
 )
 
 
@@ -109,6 +109,8 @@ def lib():
             "msa_decode": ([D, O, P, P, P, P, P, P, P, P, P, P, SZ, P], ctypes.c_int),
             "msa_index_topk_forced": ([D, P, P, I64, I64, ctypes.c_int, ctypes.c_int, P, P], ctypes.c_int),
             "msa_window_select": ([D, I64, I64, P, P], ctypes.c_int),
+            "msa_backward_workspace_size": ([D, O, ctypes.POINTER(SZ)], ctypes.c_int),
+            "msa_backward": ([D, O, ctypes.c_float] + [P] * 16 + [SZ, P], ctypes.c_int),
         }
         for name, (args, res) in sig.items():
             f = getattr(L, name)
@@ -336,6 +338,43 @@ def msa_decode(dims: msa_dims, opts: msa_opts, q, q_idx, k, v, k_idx, o=None, ls
                                 workspace.numel() * workspace.element_size(), _stream(q)),
                "msa_decode")
     return o, lse, block_idx_out
+
+
+def msa_backward_workspace_size(dims: msa_dims, opts: msa_opts) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().msa_backward_workspace_size(ctypes.byref(dims), ctypes.byref(opts), ctypes.byref(n)),
+           "msa_backward_workspace_size")
+    return n.value
+
+
+def msa_backward(dims: msa_dims, opts: msa_opts, q, k, v, q_idx, k_idx, o, lse, d_o, block_idx,
+                 kl_weight: float = 1.0, index: bool = True, want_kl: bool = True, workspace=None):
+    """Backward pass: gradients of the sparse main attention (dq, dk, dv) and,
+    when ``index``, the KL alignment gradient of the index branch (dq_idx,
+    dk_idx) and the per-row KL [batch, H_sel, N] (when ``want_kl``).
+    Inputs as msa_forward's, plus its output o, lse and block_idx and the
+    output gradient d_o.  Returns a dict of the outputs (None when skipped)."""
+    import torch
+    B, N = dims.batch, dims.N
+    out = {
+        "dq": _empty((B, N, dims.H_q, dims.d_h), torch.bfloat16, q),
+        "dk": _empty((B, N, dims.H_kv, dims.d_h), torch.bfloat16, q),
+        "dv": _empty((B, N, dims.H_kv, dims.d_h), torch.bfloat16, q),
+        "dq_idx": _empty((B, N, dims.H_sel, dims.d_idx), torch.bfloat16, q) if index else None,
+        "dk_idx": _empty((B, N, dims.d_idx), torch.bfloat16, q) if index else None,
+        "kl": _empty((B, dims.H_sel, N), torch.float32, q) if index and want_kl else None,
+    }
+    nbytes = msa_backward_workspace_size(dims, opts)
+    if workspace is None:
+        workspace = _empty((nbytes,), torch.uint8, q)
+    with _dev(q):
+        _check(lib().msa_backward(ctypes.byref(dims), ctypes.byref(opts), float(kl_weight), _p(q), _p(k), _p(v),
+                                  _p(q_idx), _p(k_idx), _p(o), _p(lse), _p(d_o), _p(block_idx),
+                                  _p(out["dq"]), _p(out["dk"]), _p(out["dv"]), _p(out["dq_idx"]),
+                                  _p(out["dk_idx"]), _p(out["kl"]), _p(workspace),
+                                  workspace.numel() * workspace.element_size(), _stream(q)),
+               "msa_backward")
+    return out
 
 
 def default_softmax_scale(d_h: int) -> float:

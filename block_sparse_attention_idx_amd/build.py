@@ -11,7 +11,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libmsa.so")
 SOURCES = ["api.hip", "index_topk.hip", "invert.hip", "sparse_attn.hip", "combine.hip",
-           "dense_attn.hip", "decode.hip", "window_select.hip"]
+           "dense_attn.hip", "decode.hip", "window_select.hip", "backward.hip"]
 # -fno-honor-nans: no NaN reaches a kernel from valid inputs (scores are finite
 # or -inf, and every row and (query, group) has a visible key), so fmaxf needs
 # no canonicalising copies of MFMA results; infinities are still honoured.

@@ -368,6 +368,165 @@ int msa_decode(const msa_dims* dims, const msa_opts* opts, const void* q, const 
   return e == hipSuccess ? MSA_OK : hip_fail(e);
 }
 
+namespace {
+
+struct BackwardLayout {
+  int64_t qc;  // rows per chunk
+  size_t off_dk, off_dv, off_dki, off_dlt, off_bi, off_off, off_ent, off_sched, off_dqp, off_lsp, off_lsi,
+      off_dqip, off_klp, total;
+};
+
+BackwardLayout backward_layout(const msa_dims* d, const msa_opts* o) {
+  BackwardLayout L{};
+  L.qc = o->q_chunk > 0 ? (o->q_chunk < d->N ? o->q_chunk : d->N) : d->N;
+  const int64_t seqs = static_cast<int64_t>(d->batch) * HS(d);
+  const int64_t B = (d->N + d->B_k - 1) / d->B_k;
+  const size_t slots = static_cast<size_t>(seqs) * L.qc * d->k;
+  int64_t words = 0;
+  const int64_t nchunks = (d->N + L.qc - 1) / L.qc;
+  for (int64_t c = (nchunks > 2 ? nchunks - 2 : 0); c < nchunks; ++c) {
+    const int64_t qb = c * L.qc, qn = (d->N - qb) < L.qc ? (d->N - qb) : L.qc;
+    const msa::SchedLayout s = msa::sched_layout(d->batch, HS(d), GS(d), d->k, qb, qn, d->B_k);
+    words = s.words > words ? s.words : words;
+  }
+  const size_t kv = static_cast<size_t>(d->batch) * d->N * d->H_kv * d->d_h * 4;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off += align256(bytes);
+    return at;
+  };
+  L.off_dk = take(kv);
+  L.off_dv = take(kv);
+  L.off_dki = take(static_cast<size_t>(d->batch) * d->N * d->d_idx * 4);
+  L.off_dlt = take(static_cast<size_t>(d->batch) * d->N * d->H_q * 4);
+  L.off_bi = take(slots * 4);
+  L.off_off = take(static_cast<size_t>(seqs) * (B + 1) * 4);
+  L.off_ent = take(slots * 4);
+  L.off_sched = take(static_cast<size_t>(words) * 4);
+  L.off_dqp = take(slots * GS(d) * d->d_h * 2);
+  L.off_lsp = take(slots * 4);
+  L.off_lsi = take(static_cast<size_t>(seqs) * L.qc * 4);
+  L.off_dqip = take(slots * d->d_idx * 4);
+  L.off_klp = take(slots * 4);
+  L.total = off;
+  return L;
+}
+
+int check_backward(const msa_dims* d, const msa_opts* o) {
+  int st = check_dims(d);
+  if (st) return st;
+  if ((st = check_opts(d, o))) return st;
+  if (o->qkv_dtype != MSA_DTYPE_BF16 || d->B_k != msa::kBk) return MSA_ERR_UNSUPPORTED;
+  const BackwardLayout L = backward_layout(d, o);
+  return check_range(d, 0, L.qc);
+}
+
+}  // namespace
+
+int msa_backward_workspace_size(const msa_dims* dims, const msa_opts* opts, size_t* bytes) {
+  int st = check_backward(dims, opts);
+  if (st) return st;
+  if (!bytes) return MSA_ERR_NULL;
+  *bytes = backward_layout(dims, opts).total;
+  return MSA_OK;
+}
+
+int msa_backward(const msa_dims* dims, const msa_opts* opts, float kl_weight, const void* q, const void* k,
+                 const void* v, const void* q_idx, const void* k_idx, const void* o, const float* lse,
+                 const void* d_o, const int32_t* block_idx, void* dq, void* dk, void* dv, void* dq_idx,
+                 void* dk_idx, float* kl, void* workspace, size_t ws_bytes, void* stream) {
+  int st = check_backward(dims, opts);
+  if (st) return st;
+  if (!isfinite(kl_weight)) return MSA_ERR_SHAPE;
+  const bool index = dq_idx != nullptr || dk_idx != nullptr || kl != nullptr;
+  if (!q || !k || !v || !o || !lse || !d_o || !block_idx || !dq || !dk || !dv || !workspace) return MSA_ERR_NULL;
+  if (index && (!q_idx || !k_idx || !dq_idx || !dk_idx)) return MSA_ERR_NULL;
+  if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(o) || misaligned(lse) || misaligned(d_o) ||
+      misaligned(block_idx) || misaligned(dq) || misaligned(dk) || misaligned(dv) ||
+      (index && (misaligned(q_idx) || misaligned(k_idx) || misaligned(dq_idx) || misaligned(dk_idx))) ||
+      (kl && misaligned(kl)) || (reinterpret_cast<uintptr_t>(workspace) & 255u))
+    return MSA_ERR_ALIGN;
+  const BackwardLayout L = backward_layout(dims, opts);
+  if (ws_bytes < L.total) return MSA_ERR_WORKSPACE;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  float* dk_acc = reinterpret_cast<float*>(ws + L.off_dk);
+  float* dv_acc = reinterpret_cast<float*>(ws + L.off_dv);
+  float* dki_acc = reinterpret_cast<float*>(ws + L.off_dki);
+  const int64_t nkv = static_cast<int64_t>(dims->batch) * dims->N * dims->H_kv * dims->d_h;
+  const int64_t nki = static_cast<int64_t>(dims->batch) * dims->N * dims->d_idx;
+  hipError_t e = msa::launch_fill_zero(dk_acc, nkv, s);
+  if (e == hipSuccess) e = msa::launch_fill_zero(dv_acc, nkv, s);
+  if (e == hipSuccess && index) e = msa::launch_fill_zero(dki_acc, nki, s);
+  if (e != hipSuccess) return hip_fail(e);
+
+  msa::BwdArgs a{};
+  a.q = static_cast<const uint16_t*>(q);
+  a.k_ptr = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.dout = static_cast<const uint16_t*>(d_o);
+  a.o = static_cast<const uint16_t*>(o);
+  a.q_idx = static_cast<const uint16_t*>(q_idx);
+  a.k_idx = static_cast<const uint16_t*>(k_idx);
+  a.lse = lse;
+  a.batch = dims->batch;
+  a.N = dims->N;
+  a.H_sel = HS(dims);
+  a.G = GS(dims);
+  a.kv_shift = KVS(dims);
+  a.k = dims->k;
+  a.d_idx = dims->d_idx;
+  a.scale = opts->softmax_scale > 0.f ? opts->softmax_scale : static_cast<float>(1.0 / sqrt(static_cast<double>(dims->d_h)));
+  a.idx_scale = static_cast<float>(1.0 / sqrt(static_cast<double>(dims->d_idx)));
+  a.kl_weight = kl_weight;
+  a.index = index;
+  a.dlt = reinterpret_cast<float*>(ws + L.off_dlt);
+  a.lsei_part = reinterpret_cast<float*>(ws + L.off_lsp);
+  a.lsei2 = reinterpret_cast<float*>(ws + L.off_lsi);
+  a.dqi_part = reinterpret_cast<float*>(ws + L.off_dqip);
+  a.kl_part = reinterpret_cast<float*>(ws + L.off_klp);
+  a.dk_acc = dk_acc;
+  a.dv_acc = dv_acc;
+  a.dki_acc = dki_acc;
+  a.kl = kl;
+  a.dq_part = reinterpret_cast<uint16_t*>(ws + L.off_dqp);
+  a.dq = static_cast<uint16_t*>(dq);
+  a.dq_idx = static_cast<uint16_t*>(dq_idx);
+  int32_t* offs = reinterpret_cast<int32_t*>(ws + L.off_off);
+  int32_t* ents = reinterpret_cast<int32_t*>(ws + L.off_ent);
+  int32_t* sched = reinterpret_cast<int32_t*>(ws + L.off_sched);
+  int32_t* bi_chunk = reinterpret_cast<int32_t*>(ws + L.off_bi);
+  const bool one_chunk = L.qc >= dims->N;
+  const int64_t seqs = static_cast<int64_t>(dims->batch) * HS(dims);
+
+  for (int64_t qb = 0; qb < dims->N; qb += L.qc) {
+    const int64_t qn = (dims->N - qb) < L.qc ? (dims->N - qb) : L.qc;
+    const int32_t* bi = block_idx;
+    if (!one_chunk) {
+      const size_t w = static_cast<size_t>(qn) * dims->k * sizeof(int32_t);
+      e = hipMemcpy2DAsync(bi_chunk, w, block_idx + qb * dims->k, static_cast<size_t>(dims->N) * dims->k * 4, w,
+                           static_cast<size_t>(seqs), hipMemcpyDeviceToDevice, s);
+      if (e != hipSuccess) return hip_fail(e);
+      bi = bi_chunk;
+    }
+    e = msa::launch_invert(bi, dims->batch, HS(dims), GS(dims), dims->k, qb, qn, offs, ents, sched, s, dims->B_k);
+    if (e != hipSuccess) return hip_fail(e);
+    a.block_idx = bi;
+    a.entries = ents;
+    a.sched = sched;
+    a.q_begin = qb;
+    a.q_count = qn;
+    e = msa::launch_backward_chunk(a, s);
+    if (e != hipSuccess) return hip_fail(e);
+  }
+  e = msa::launch_to_bf16(dk_acc, static_cast<uint16_t*>(dk), nkv, s);
+  if (e == hipSuccess) e = msa::launch_to_bf16(dv_acc, static_cast<uint16_t*>(dv), nkv, s);
+  if (e == hipSuccess && index) e = msa::launch_to_bf16(dki_acc, static_cast<uint16_t*>(dk_idx), nki, s);
+  return e == hipSuccess ? MSA_OK : hip_fail(e);
+}
+
 int msa_workspace_size(const msa_dims* dims, const msa_opts* opts, size_t* bytes) {
   int st = check_dims(dims);
   if (st) return st;

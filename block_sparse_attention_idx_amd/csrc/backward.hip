@@ -1,0 +1,888 @@
+// Backward pass of MSA: gradients of the sparse main attention and the KL
+// alignment gradient of the index branch.
+//
+// What is computed ("MiniMax Sparse Attention (MSA)", Deep Dive > KL Alignment
+// Loss; "Flash-MSA", Backward and KL Divergence Loss): for query i, selection
+// group r and its visible selected tokens T (the forward's block selection,
+// tokens j <= i), with p_h = softmax_T(scale Q_h . K_j) for the group's heads h,
+//   main branch:  dV_j += sum_h p_hj dO_h,   dP_hj = dO_h . V_j,
+//                 dS_hj = p_hj (dP_hj - dO_h . O_h),
+//                 dQ_h = scale sum_j dS_hj K_j,   dK_j += scale sum_h dS_hj Q_h;
+//   index branch: teacher P_j = mean_h p_hj (a constant), proxy
+//                 p_px = softmax_T(z_j), z_j = q_idx . k_idx_j / sqrt(d_idx),
+//                 KL_i,r = sum_j P_j ln(P_j / p_px,j), and the gradient
+//                 w (p_px - P) on z carried to q_idx and k_idx.
+//
+// Schedule ("Flash-MSA", Backward: the cached selection is inverted and the
+// inverse drives the work): the forward's inversion and pass list are reused.
+// Each pass is one (sequence, group, key block) bin restricted to up to
+// 256 / G consecutive entries (query, slot); persistent workgroups take equal
+// contiguous shares of the pass list, so every workgroup keeps one key block
+// for a run of passes.  Per workgroup of 4 waves, wave w owns keys
+// 32 w .. 32 w + 31 of the block, keeps their K, V (and K^idx) rows in
+// registers and accumulates their dK^T, dV^T (and dK^idx^T) in MFMA
+// accumulators across the run; when the block changes, the accumulators are
+// added to fp32 gradient buffers with global atomics (a block's passes may be
+// shared by two workgroups, and with more index heads than K/V heads several
+// groups share a K/V head).  dQ (and dq_idx) need a sum over the block's keys,
+// i.e. over the waves: dS goes through LDS and every (query, slot) writes a
+// partial, summed over the slots afterwards as in the forward's combine.
+//
+// Rows of a pass are processed 64 at a time (64 / G queries x G heads).  All
+// products run on v_mfma_f32_32x32x16_bf16:
+//   S  = Q K^T       A = Q rows (LDS),       B = K rows (registers)
+//   dP = dO V^T      A = dO rows (LDS),      B = V rows (registers)
+//   dV^T += dO^T P   A = dO^T (LDS),         B = P straight from the accumulator
+//   dK^T += Q^T dS   A = Q^T (LDS),          B = dS straight from the accumulator
+//   dQ^T = K^T dS^T  A = K^T (LDS),          B = dS rows (LDS)
+// S, P and dS have the keys on the lane (column) index, so the row-reducing
+// products take them as B operands without a shuffle; the transposed A
+// operands store the rows in the order that makes this exact (row bits 2 and 3
+// swapped, so that the 8 rows a lane contributes to one 16-row step are one
+// 16-byte chunk).
+//
+// The proxy softmax needs the proxy LSE over all of a query's selected tokens
+// first: a KV-outer pass over the same work list (one wave per workgroup)
+// writes one partial LSE per (query, slot), merged per query ("Flash-MSA",
+// Backward: a cheap sparse proxy pass recomputes the proxy LSE).
+#include "attn_tile.h"
+#include "msa_internal.h"
+
+namespace msa {
+namespace {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+using tile::bf16_of;
+using tile::halves_max;
+using tile::halves_sum;
+
+constexpr int kBW = 4;           // waves per backward workgroup
+constexpr int kBT = 64 * kBW;    // threads
+constexpr int kRows = 64;        // (query, head) rows per chunk
+constexpr int kStr = 272;        // row-major LDS row: 128 bf16 + 16 B of padding
+constexpr int kTStr = 144;       // transposed LDS row: 64 bf16 + 16 B of padding
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.69314718055994531f;
+
+// Column of chunk row rho in a transposed tile: bits 2 and 3 swapped, so the
+// rows 16 s + 4 h + (0..3) and 16 s + 8 + 4 h + (0..3) that lane half h feeds
+// to 16-row step s are the 8 consecutive columns 16 s + 8 h .. + 7.
+__device__ __forceinline__ int tpos(int rho) { return (rho & ~12) | ((rho & 4) << 1) | ((rho & 8) >> 1); }
+
+// Accumulator element e of a 32x32 tile holds row 8 (e / 4) + 4 h + (e % 4).
+__device__ __forceinline__ int acc_row(int e, int h) { return 8 * (e >> 2) + 4 * h + (e & 3); }
+
+__device__ __forceinline__ uint16_t bf16_bits(float x) {
+  return static_cast<uint16_t>(pack_bf16x2(x, 0.f) & 0xFFFFu);
+}
+
+// Elements 8 s .. 8 s + 7 of a tile accumulator (rows 16 s + 8 a + 4 h + b,
+// slot 4 a + b) as the bf16 B operand of one 16-row step.
+__device__ __forceinline__ bf16x8 pack_step(const f32x16& a, int s) {
+  return as_bf16x8(u32x4{pack_bf16x2(a[8 * s + 0], a[8 * s + 1]), pack_bf16x2(a[8 * s + 2], a[8 * s + 3]),
+                         pack_bf16x2(a[8 * s + 4], a[8 * s + 5]), pack_bf16x2(a[8 * s + 6], a[8 * s + 7])});
+}
+
+__device__ __forceinline__ bf16x8 lds_frag(const uint8_t* p) {
+  return as_bf16x8(*reinterpret_cast<const u32x4*>(p));
+}
+
+// This workgroup's passes: the (seq, window) pairs in order and, in each, one
+// contiguous equal share of its passes (the forward's partition).
+struct PassIter {
+  const int32_t* segp;
+  int B_c, npairs;
+  int pair = -1, p = 0, end = 0;
+  __device__ int next() {
+    if (++p < end) return p;
+    while (++pair < npairs) {
+      const int a = segp[pair * B_c];
+      const int64_t np = segp[(pair + 1) * B_c] - a;
+      const int s0 = a + static_cast<int>(np * blockIdx.x / gridDim.x);
+      const int s1 = a + static_cast<int>(np * (blockIdx.x + 1) / gridDim.x);
+      if (s0 < s1) {
+        p = s0;
+        end = s1;
+        return s0;
+      }
+    }
+    return -1;
+  }
+};
+
+// Where entry word `ent` (query row * k + slot) of group seq points.
+struct EntryRef {
+  int i;          // query position
+  int64_t slot;   // (seq, query row, slot) index
+};
+__device__ __forceinline__ EntryRef entry_ref(uint32_t ent, int seq, int kslots, int q_begin, int q_count) {
+  const uint32_t qrow = ent / static_cast<uint32_t>(kslots);
+  const uint32_t s = ent - qrow * static_cast<uint32_t>(kslots);
+  EntryRef r;
+  r.i = q_begin + static_cast<int>(qrow);
+  r.slot = (static_cast<int64_t>(seq) * q_count + qrow) * kslots + s;
+  return r;
+}
+
+// Stage 64 rows of a [*, d_h = 128] bf16 tensor: row-major into `rm` (may be
+// null) and transposed into `tr` (may be null).  Thread t loads 16-byte chunk
+// t % 16 of rows 4 (t / 16) .. + 3; `row_ptr(rho)` gives the row (null =
+// zeros).
+template <typename RowPtr>
+__device__ __forceinline__ void stage_rows(RowPtr row_ptr, uint8_t* rm, uint8_t* tr) {
+  const int t = threadIdx.x;
+  const int dg = t & 15, rc = t >> 4;
+  u32x4 w[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint16_t* p = row_ptr(4 * rc + j);
+    w[j] = p ? *reinterpret_cast<const u32x4*>(p + 8 * dg) : u32x4{0u, 0u, 0u, 0u};
+  }
+  if (rm) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) *reinterpret_cast<u32x4*>(rm + (4 * rc + j) * kStr + 16 * dg) = w[j];
+  }
+  if (tr) {
+    const int col = tpos(4 * rc);
+#pragma unroll
+    for (int dd = 0; dd < 8; ++dd) {
+      const u32x2 v = {bf16_of(w[0], dd) | (bf16_of(w[1], dd) << 16),
+                       bf16_of(w[2], dd) | (bf16_of(w[3], dd) << 16)};
+      *reinterpret_cast<u32x2*>(tr + (8 * dg + dd) * kTStr + 2 * col) = v;
+    }
+  }
+}
+
+// Write the 32 keys x 128 dims a wave holds in registers (lane n: key n, dims
+// 16 ks + 8 h .. + 7) transposed into `kt` ([dim][key], kStr per dim row),
+// columns 32 wave + n.
+template <int KS>
+__device__ __forceinline__ void store_keys_t(const u32x4 (&f)[KS], uint8_t* kt, int wave, int n, int h) {
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+    for (int dd = 0; dd < 8; ++dd)
+      *reinterpret_cast<uint16_t*>(kt + (16 * ks + 8 * h + dd) * kStr + 2 * (32 * wave + n)) =
+          static_cast<uint16_t>(bf16_of(f[ks], dd));
+}
+
+// ---------------------------------------------------------------- main branch
+template <int G>
+__global__ __launch_bounds__(kBT, 1) void bwd_main_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    const uint16_t* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ dlt,
+    int64_t N, int H_sel, int kv_shift, int kslots, float scale, float scale_log2,
+    const int32_t* __restrict__ entries, const int32_t* __restrict__ segp,
+    const PassDesc* __restrict__ passes, int B_c, int npairs, int q_begin, int q_count,
+    uint16_t* __restrict__ dq_part, float* __restrict__ dk_acc, float* __restrict__ dv_acc) {
+  constexpr int EC = kRows / G;  // queries per chunk
+  __shared__ __attribute__((aligned(16))) uint8_t qr_lds[kRows * kStr];
+  __shared__ __attribute__((aligned(16))) uint8_t dor_lds[kRows * kStr];
+  __shared__ __attribute__((aligned(16))) uint8_t qt_lds[kDh * kTStr];
+  __shared__ __attribute__((aligned(16))) uint8_t dot_lds[kDh * kTStr];
+  __shared__ __attribute__((aligned(16))) uint8_t kt_lds[kDh * kStr];
+  __shared__ __attribute__((aligned(16))) uint8_t ds_lds[kRows * kStr];
+  __shared__ int ri_i[kRows];
+  __shared__ float ri_lse2[kRows], ri_dlt[kRows];
+  __shared__ int64_t ri_orow[kRows];
+
+  PassIter it{segp, B_c, npairs};
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, n = lane & 31, h = lane >> 5;
+  const int H_q = H_sel * G, H_kv = H_sel >> kv_shift;
+  const int key_l = 32 * wave + n;  // this lane's key within the block
+
+  int cur_seq = -1, cur_blk = 0, cur_nvalid = 0;
+  u32x4 kf[8], vf[8];
+  f32x16 dkt[4], dvt[4];
+
+  auto flush = [&]() {
+    if (cur_seq < 0 || key_l >= cur_nvalid) return;
+    const int bat = cur_seq / H_sel, r = cur_seq - bat * H_sel;
+    const int64_t row = (static_cast<int64_t>(bat) * N + static_cast<int64_t>(cur_blk) * kBk + key_l) * H_kv +
+                        (r >> kv_shift);
+    float* dkp = dk_acc + row * kDh;
+    float* dvp = dv_acc + row * kDh;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int d = 32 * dt + acc_row(e, h);
+        unsafeAtomicAdd(dkp + d, dkt[dt][e] * scale);
+        unsafeAtomicAdd(dvp + d, dvt[dt][e]);
+      }
+  };
+
+  for (int pi = it.next(); pi >= 0; pi = it.next()) {
+    const PassDesc D = passes[pi];
+    const int bat = D.seq / H_sel, r = D.seq - bat * H_sel;
+    if (D.seq != cur_seq || D.blk != cur_blk) {
+      flush();
+      cur_seq = D.seq;
+      cur_blk = D.blk;
+      const int64_t key0 = static_cast<int64_t>(D.blk) * kBk;
+      cur_nvalid = static_cast<int>(min<int64_t>(kBk, N - key0));
+      const int64_t rstride = static_cast<int64_t>(H_kv) * kDh;
+      const int64_t base = ((static_cast<int64_t>(bat) * N + key0) * H_kv + (r >> kv_shift)) * kDh +
+                           min(key_l, cur_nvalid - 1) * rstride;
+      const bool kv_ok = key_l < cur_nvalid;
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) {
+        const u32x4 a = *reinterpret_cast<const u32x4*>(k + base + 16 * ks + 8 * h);
+        const u32x4 b = *reinterpret_cast<const u32x4*>(v + base + 16 * ks + 8 * h);
+        kf[ks] = kv_ok ? a : u32x4{0u, 0u, 0u, 0u};
+        vf[ks] = kv_ok ? b : u32x4{0u, 0u, 0u, 0u};
+      }
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) {
+        dkt[dt] = f32x16{};
+        dvt[dt] = f32x16{};
+      }
+      // every wave finished the previous chunk's dQ (trailing barrier), so
+      // K^T can be replaced; the staging barrier below publishes it
+      store_keys_t<8>(kf, kt_lds, wave, n, h);
+    }
+    const int key_abs = D.blk * kBk + key_l;
+
+    for (int cb = 0; cb < D.cnt; cb += EC) {
+      // ---- stage the chunk's Q and dO rows and per-row constants
+      auto row_off = [&](int rho, EntryRef* er) -> int64_t {
+        const int e = cb + rho / G;
+        if (e >= D.cnt) return -1;
+        const EntryRef x = entry_ref(static_cast<uint32_t>(entries[D.start + e]), D.seq, kslots, q_begin, q_count);
+        if (er) *er = x;
+        return (static_cast<int64_t>(bat) * N + x.i) * H_q + r * G + rho % G;
+      };
+      stage_rows([&](int rho) -> const uint16_t* {
+        const int64_t o = row_off(rho, nullptr);
+        return o < 0 ? nullptr : q + o * kDh;
+      }, qr_lds, qt_lds);
+      stage_rows([&](int rho) -> const uint16_t* {
+        const int64_t o = row_off(rho, nullptr);
+        return o < 0 ? nullptr : dout + o * kDh;
+      }, dor_lds, dot_lds);
+      if (tid < kRows) {
+        EntryRef er{};
+        const int64_t o = row_off(tid, &er);
+        ri_i[tid] = o < 0 ? -1 : er.i;
+        ri_lse2[tid] = o < 0 ? 0.f : lse[o] * kLog2e;
+        ri_dlt[tid] = o < 0 ? 0.f : dlt[o];
+        ri_orow[tid] = o < 0 ? 0 : er.slot * G + tid % G;
+      }
+      __syncthreads();
+
+      // ---- S, P, dP, dS for the wave's 32 keys (lane = key, elements = rows)
+      bf16x8 pb[4], db[4];
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt) {
+        f32x16 s = {}, dp = {};
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) {
+          const int off = (32 * rt + n) * kStr + 32 * ks + 16 * h;
+          s = mfma32x32x16(lds_frag(qr_lds + off), as_bf16x8(kf[ks]), s);
+          dp = mfma32x32x16(lds_frag(dor_lds + off), as_bf16x8(vf[ks]), dp);
+        }
+        f32x16 p, ds;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int rho = 32 * rt + acc_row(e, h);
+          const float pe = key_abs <= ri_i[rho]
+                               ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[e], scale_log2, -ri_lse2[rho]))
+                               : 0.f;
+          p[e] = pe;
+          ds[e] = pe * (dp[e] - ri_dlt[rho]);
+          *reinterpret_cast<uint16_t*>(ds_lds + rho * kStr + 2 * key_l) = bf16_bits(ds[e]);
+        }
+        pb[2 * rt] = pack_step(p, 0);
+        pb[2 * rt + 1] = pack_step(p, 1);
+        db[2 * rt] = pack_step(ds, 0);
+        db[2 * rt + 1] = pack_step(ds, 1);
+      }
+
+      // ---- dV^T += dO^T P, dK^T += Q^T dS (reduction over the 64 rows)
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int st = 0; st < 4; ++st) {
+          const int off = (32 * dt + n) * kTStr + 32 * st + 16 * h;
+          dvt[dt] = mfma32x32x16(lds_frag(dot_lds + off), pb[st], dvt[dt]);
+          dkt[dt] = mfma32x32x16(lds_frag(qt_lds + off), db[st], dkt[dt]);
+        }
+      __syncthreads();
+
+      // ---- dQ^T = K^T dS^T over the block's 128 keys: wave w takes rows
+      // 32 (w / 2) .. + 31 and dims 64 (w % 2) .. + 63
+      {
+        const int rt = wave >> 1, dt0 = 2 * (wave & 1);
+        f32x16 qa[2] = {};
+#pragma unroll
+        for (int kk = 0; kk < 8; ++kk) {
+          const bf16x8 b = lds_frag(ds_lds + (32 * rt + n) * kStr + 32 * kk + 16 * h);
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+            qa[j] = mfma32x32x16(lds_frag(kt_lds + (32 * (dt0 + j) + n) * kStr + 32 * kk + 16 * h), b, qa[j]);
+        }
+        const int rho = 32 * rt + n;
+        if (ri_i[rho] >= 0) {
+          uint16_t* dst = dq_part + ri_orow[rho] * kDh;
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int e4 = 0; e4 < 4; ++e4) {
+              const int d0 = 32 * (dt0 + j) + 8 * e4 + 4 * h;
+              *reinterpret_cast<u32x2*>(dst + d0) =
+                  u32x2{pack_bf16x2(qa[j][4 * e4] * scale, qa[j][4 * e4 + 1] * scale),
+                        pack_bf16x2(qa[j][4 * e4 + 2] * scale, qa[j][4 * e4 + 3] * scale)};
+            }
+        }
+      }
+      __syncthreads();
+    }
+  }
+  flush();
+}
+
+// ---------------------------------------------------------------- index branch
+template <int G, int DIDX>
+__global__ __launch_bounds__(kBT, 1) void bwd_idx_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ q_idx,
+    const uint16_t* __restrict__ k_idx, const float* __restrict__ lse, const float* __restrict__ lsei2,
+    int64_t N, int H_sel, int kv_shift, int kslots, float scale_log2, float idx_scale_log2, float gscale,
+    const int32_t* __restrict__ entries, const int32_t* __restrict__ segp,
+    const PassDesc* __restrict__ passes, int B_c, int npairs, int q_begin, int q_count,
+    float* __restrict__ dqi_part, float* __restrict__ kl_part, float* __restrict__ dki_acc) {
+  constexpr int EC = kRows / G;        // queries (index rows) per chunk
+  constexpr int ZT = (EC + 31) / 32;   // 32-row tiles of index rows
+  constexpr int KE = (EC + 15) / 16;   // 16-row steps of index rows
+  constexpr int KSI = DIDX / 16;       // reduction steps of the index dot product
+  constexpr int TT = DIDX / 32;        // 32-dim tiles of dq_idx / dk_idx
+  constexpr float kInvG = 1.f / G;
+  __shared__ __attribute__((aligned(16))) uint8_t qr_lds[kRows * kStr];
+  __shared__ __attribute__((aligned(16))) uint8_t qi_lds[64 * kStr];
+  __shared__ __attribute__((aligned(16))) uint8_t qit_lds[kDh * kTStr];
+  __shared__ __attribute__((aligned(16))) uint8_t kit_lds[kDh * kStr];
+  __shared__ __attribute__((aligned(16))) uint8_t g_lds[64 * kStr];
+  __shared__ float tch[64 * kBk];  // teacher sums, then KL terms, [index row][key]
+  __shared__ int ri_i[kRows], ei_i[64];
+  __shared__ float ri_lse2[kRows], ei_l2[64];
+  __shared__ int64_t ei_slot[64];
+
+  PassIter it{segp, B_c, npairs};
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, n = lane & 31, h = lane >> 5;
+  const int H_q = H_sel * G, H_kv = H_sel >> kv_shift;
+  const int key_l = 32 * wave + n;
+
+  int cur_seq = -1, cur_blk = 0, cur_nvalid = 0;
+  u32x4 kf[8], kif[KSI];
+  f32x16 dkit[TT];
+
+  auto flush = [&]() {
+    if (cur_seq < 0 || key_l >= cur_nvalid) return;
+    const int bat = cur_seq / H_sel;
+    float* dst = dki_acc + (static_cast<int64_t>(bat) * N + static_cast<int64_t>(cur_blk) * kBk + key_l) * DIDX;
+#pragma unroll
+    for (int tt = 0; tt < TT; ++tt)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) unsafeAtomicAdd(dst + 32 * tt + acc_row(e, h), dkit[tt][e]);
+  };
+
+  for (int pi = it.next(); pi >= 0; pi = it.next()) {
+    const PassDesc D = passes[pi];
+    const int bat = D.seq / H_sel, r = D.seq - bat * H_sel;
+    if (D.seq != cur_seq || D.blk != cur_blk) {
+      flush();
+      cur_seq = D.seq;
+      cur_blk = D.blk;
+      const int64_t key0 = static_cast<int64_t>(D.blk) * kBk;
+      cur_nvalid = static_cast<int>(min<int64_t>(kBk, N - key0));
+      const int kr = min(key_l, cur_nvalid - 1);
+      const bool ok = key_l < cur_nvalid;
+      const uint16_t* kb = k + ((static_cast<int64_t>(bat) * N + key0 + kr) * H_kv + (r >> kv_shift)) * kDh;
+      const uint16_t* kib = k_idx + (static_cast<int64_t>(bat) * N + key0 + kr) * DIDX;
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) {
+        const u32x4 a = *reinterpret_cast<const u32x4*>(kb + 16 * ks + 8 * h);
+        kf[ks] = ok ? a : u32x4{0u, 0u, 0u, 0u};
+      }
+#pragma unroll
+      for (int ks = 0; ks < KSI; ++ks) {
+        const u32x4 a = *reinterpret_cast<const u32x4*>(kib + 16 * ks + 8 * h);
+        kif[ks] = ok ? a : u32x4{0u, 0u, 0u, 0u};
+      }
+#pragma unroll
+      for (int tt = 0; tt < TT; ++tt) dkit[tt] = f32x16{};
+      store_keys_t<KSI>(kif, kit_lds, wave, n, h);
+    }
+    const int key_abs = D.blk * kBk + key_l;
+
+    for (int cb = 0; cb < D.cnt; cb += EC) {
+      // ---- stage Q rows, index rows (row-major and transposed), constants
+      auto ent_of = [&](int e, EntryRef* er) -> bool {  // chunk index row e
+        if (e >= EC || cb + e >= D.cnt) return false;
+        *er = entry_ref(static_cast<uint32_t>(entries[D.start + cb + e]), D.seq, kslots, q_begin, q_count);
+        return true;
+      };
+      stage_rows([&](int rho) -> const uint16_t* {
+        EntryRef er;
+        if (!ent_of(rho / G, &er)) return nullptr;
+        return q + ((static_cast<int64_t>(bat) * N + er.i) * H_q + r * G + rho % G) * kDh;
+      }, qr_lds, nullptr);
+      {
+        // index rows: thread t loads 16-byte chunk t % 16 (< DIDX / 8) of rows
+        // 4 (t / 16) .. + 3 (all 64 rows written, zeros past the chunk)
+        const int dg = tid & 15, rc = tid >> 4;
+        if (dg < DIDX / 8) {
+          u32x4 w[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            EntryRef er;
+            w[j] = u32x4{0u, 0u, 0u, 0u};
+            if (ent_of(4 * rc + j, &er))
+              w[j] = *reinterpret_cast<const u32x4*>(
+                  q_idx + ((static_cast<int64_t>(bat) * N + er.i) * H_sel + r) * DIDX + 8 * dg);
+            *reinterpret_cast<u32x4*>(qi_lds + (4 * rc + j) * kStr + 16 * dg) = w[j];
+          }
+          const int col = tpos(4 * rc);
+#pragma unroll
+          for (int dd = 0; dd < 8; ++dd) {
+            const u32x2 v = {bf16_of(w[0], dd) | (bf16_of(w[1], dd) << 16),
+                             bf16_of(w[2], dd) | (bf16_of(w[3], dd) << 16)};
+            *reinterpret_cast<u32x2*>(qit_lds + (8 * dg + dd) * kTStr + 2 * col) = v;
+          }
+        }
+      }
+      if (tid < kRows) {
+        EntryRef er;
+        const bool ok = ent_of(tid / G, &er);
+        ri_i[tid] = ok ? er.i : -1;
+        ri_lse2[tid] = ok ? lse[(static_cast<int64_t>(bat) * N + er.i) * H_q + r * G + tid % G] * kLog2e : 0.f;
+        const bool oke = ent_of(tid, &er);
+        ei_i[tid] = oke ? er.i : -1;
+        ei_l2[tid] = oke ? lsei2[er.slot / kslots] : 0.f;
+        ei_slot[tid] = oke ? er.slot : 0;
+      }
+      for (int x = tid; x < 64 * kBk; x += kBT) tch[x] = 0.f;
+      __syncthreads();
+
+      // ---- teacher: mean over the G heads of the main probabilities
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt) {
+        f32x16 s = {};
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks)
+          s = mfma32x32x16(lds_frag(qr_lds + (32 * rt + n) * kStr + 32 * ks + 16 * h), as_bf16x8(kf[ks]), s);
+        constexpr int RUN = G < 4 ? G : 4;  // consecutive elements of one query
+#pragma unroll
+        for (int e0 = 0; e0 < 16; e0 += RUN) {
+          float acc = 0.f;
+#pragma unroll
+          for (int e = e0; e < e0 + RUN; ++e) {
+            const int rho = 32 * rt + acc_row(e, h);
+            acc += key_abs <= ri_i[rho]
+                       ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[e], scale_log2, -ri_lse2[rho]))
+                       : 0.f;
+          }
+          const int row = (32 * rt + acc_row(e0, h)) / G;
+          atomicAdd(&tch[row * kBk + key_l], acc * kInvG);
+        }
+      }
+
+      // ---- proxy probabilities, KL terms and the gradient g on z
+      bf16x8 gb[2 * ZT];
+#pragma unroll
+      for (int zt = 0; zt < ZT; ++zt) {
+        f32x16 z = {};
+#pragma unroll
+        for (int ks = 0; ks < KSI; ++ks)
+          z = mfma32x32x16(lds_frag(qi_lds + (32 * zt + n) * kStr + 32 * ks + 16 * h), as_bf16x8(kif[ks]), z);
+        f32x16 g;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int row = 32 * zt + acc_row(e, h);
+          float ge = 0.f;
+          if (row < EC) {
+            const bool vis = key_abs <= ei_i[row];
+            const float zl2 = __builtin_fmaf(z[e], idx_scale_log2, -ei_l2[row]);  // log2 p_px
+            const float ppx = vis ? __builtin_amdgcn_exp2f(zl2) : 0.f;
+            float* tp = &tch[row * kBk + key_l];
+            const float T = *tp;
+            *tp = (vis && T > 0.f) ? T * (__builtin_amdgcn_logf(T) - zl2) * kLn2 : 0.f;
+            ge = gscale * (ppx - T);
+            *reinterpret_cast<uint16_t*>(g_lds + row * kStr + 2 * key_l) = bf16_bits(ge);
+          }
+          g[e] = ge;
+        }
+        gb[2 * zt] = pack_step(g, 0);
+        gb[2 * zt + 1] = pack_step(g, 1);
+      }
+
+      // ---- dk_idx^T += q_idx^T g (reduction over the chunk's index rows)
+#pragma unroll
+      for (int tt = 0; tt < TT; ++tt)
+#pragma unroll
+        for (int st = 0; st < KE; ++st)
+          dkit[tt] = mfma32x32x16(lds_frag(qit_lds + (32 * tt + n) * kTStr + 32 * st + 16 * h), gb[st], dkit[tt]);
+      __syncthreads();
+
+      // ---- dq_idx^T = k_idx^T g^T over the block's keys, and the KL sums
+#pragma unroll
+      for (int x = wave; x < TT * ZT; x += kBW) {
+        const int tt = x % TT, zt = x / TT;
+        f32x16 a = {};
+#pragma unroll
+        for (int kk = 0; kk < 8; ++kk)
+          a = mfma32x32x16(lds_frag(kit_lds + (32 * tt + n) * kStr + 32 * kk + 16 * h),
+                           lds_frag(g_lds + (32 * zt + n) * kStr + 32 * kk + 16 * h), a);
+        const int row = 32 * zt + n;
+        if (row < EC && ei_i[row] >= 0) {
+          float* dst = dqi_part + ei_slot[row] * DIDX + 32 * tt + 4 * h;
+#pragma unroll
+          for (int e4 = 0; e4 < 4; ++e4)
+            *reinterpret_cast<f32x4*>(dst + 8 * e4) = f32x4{a[4 * e4], a[4 * e4 + 1], a[4 * e4 + 2], a[4 * e4 + 3]};
+        }
+      }
+      if (tid < EC && ei_i[tid] >= 0) {
+        float s = 0.f;
+        for (int j = 0; j < kBk; ++j) s += tch[tid * kBk + j];
+        kl_part[ei_slot[tid]] = s;
+      }
+      __syncthreads();
+    }
+  }
+  flush();
+}
+
+// ---------------------------------------------------------------- proxy LSE
+// One wave per workgroup: for every entry (query, slot) of a pass, the
+// log2-sum-exp2 of its proxy scores over the block's visible keys.
+// z^T = K^idx Q^idx^T with the keys on the row index, as in the forward.
+constexpr int kLseWgPerCu = 4;
+
+template <int DIDX>
+__global__ __launch_bounds__(64) void proxy_lse_kernel(
+    const uint16_t* __restrict__ q_idx, const uint16_t* __restrict__ k_idx, int64_t N, int H_sel, int kslots,
+    float idx_scale_log2, const int32_t* __restrict__ entries, const int32_t* __restrict__ segp,
+    const PassDesc* __restrict__ passes, int B_c, int npairs, int q_begin, int q_count,
+    float* __restrict__ lsei_part) {
+  constexpr int KSI = DIDX / 16;
+  __shared__ __attribute__((aligned(16))) uint8_t ki_lds[kBk * kStr];
+  PassIter it{segp, B_c, npairs};
+  const int lane = threadIdx.x, n = lane & 31, h = lane >> 5;
+  int cur_seq = -1, cur_blk = 0;
+  for (int pi = it.next(); pi >= 0; pi = it.next()) {
+    const PassDesc D = passes[pi];
+    const int bat = D.seq / H_sel, r = D.seq - bat * H_sel;
+    if (D.seq / H_sel != cur_seq / H_sel || cur_seq < 0 || D.blk != cur_blk) {
+      // K^idx is shared by the groups of a sequence
+      cur_seq = D.seq;
+      cur_blk = D.blk;
+      const int64_t key0 = static_cast<int64_t>(D.blk) * kBk;
+      const int nvalid = static_cast<int>(min<int64_t>(kBk, N - key0));
+      const uint16_t* kb = k_idx + (static_cast<int64_t>(bat) * N + key0) * DIDX;
+      for (int x = lane; x < kBk * (DIDX / 8); x += 64) {
+        const int key = x / (DIDX / 8), c = x % (DIDX / 8);
+        const u32x4 w = *reinterpret_cast<const u32x4*>(kb + min(key, nvalid - 1) * DIDX + 8 * c);
+        *reinterpret_cast<u32x4*>(ki_lds + key * kStr + 16 * c) = key < nvalid ? w : u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+    cur_seq = D.seq;
+    for (int cb = 0; cb < D.cnt; cb += 32) {
+      const int e = cb + n;
+      const EntryRef er =
+          entry_ref(static_cast<uint32_t>(entries[D.start + (e < D.cnt ? e : 0)]), D.seq, kslots, q_begin, q_count);
+      const uint16_t* qr = q_idx + ((static_cast<int64_t>(bat) * N + er.i) * H_sel + r) * DIDX;
+      bf16x8 qf[KSI];
+#pragma unroll
+      for (int ks = 0; ks < KSI; ++ks) qf[ks] = as_bf16x8(*reinterpret_cast<const u32x4*>(qr + 16 * ks + 8 * h));
+      f32x16 z[4];
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        z[mt] = f32x16{};
+#pragma unroll
+        for (int ks = 0; ks < KSI; ++ks)
+          z[mt] = mfma32x32x16(lds_frag(ki_lds + (32 * mt + n) * kStr + 32 * ks + 16 * h), qf[ks], z[mt]);
+      }
+      // keys 32 mt + acc_row(e, h) of the block; hide those past the query
+      const int lim = er.i - D.blk * kBk;
+      float m = -__builtin_huge_valf();
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int el = 0; el < 16; ++el)
+          if (32 * mt + acc_row(el, h) <= lim) m = fmaxf(m, z[mt][el]);
+      m = halves_max(m);
+      float l = 0.f;
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int el = 0; el < 16; ++el)
+          if (32 * mt + acc_row(el, h) <= lim) l += __builtin_amdgcn_exp2f((z[mt][el] - m) * idx_scale_log2);
+      l = halves_sum(l);
+      if (h == 0 && e < D.cnt) lsei_part[er.slot] = m * idx_scale_log2 + __builtin_amdgcn_logf(l);
+    }
+  }
+}
+
+// Merge of the partial proxy LSEs of one (group, query) over its valid slots
+// (log2 units).
+__global__ __launch_bounds__(256) void proxy_lse_merge_kernel(const int32_t* __restrict__ block_idx,
+                                                              const float* __restrict__ lsei_part, int k,
+                                                              int64_t q_begin, int64_t q_count, int64_t rows,
+                                                              float* __restrict__ lsei2) {
+  const int64_t f = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (f >= rows) return;
+  const int64_t L = (q_begin + f % q_count) / kBk;
+  float m = -__builtin_huge_valf();
+  for (int s = 0; s < k; ++s) {
+    const int b = block_idx[f * k + s];
+    if (b >= 0 && b <= L) m = fmaxf(m, lsei_part[f * k + s]);
+  }
+  float l = 0.f;
+  for (int s = 0; s < k; ++s) {
+    const int b = block_idx[f * k + s];
+    if (b >= 0 && b <= L) l += __builtin_amdgcn_exp2f(lsei_part[f * k + s] - m);
+  }
+  lsei2[f] = m + __builtin_amdgcn_logf(l);
+}
+
+// D = rowsum(dO * O) per (query, head), fp32: 16 threads per row.
+__global__ __launch_bounds__(256) void bwd_prep_kernel(const uint16_t* __restrict__ dout,
+                                                       const uint16_t* __restrict__ o, int64_t N, int H_q,
+                                                       int64_t q_begin, int64_t q_count, int64_t rows,
+                                                       float* __restrict__ dlt) {
+  const int64_t x = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  const int64_t row = x >> 4;  // (batch, query in range, head)
+  const int c = static_cast<int>(x & 15);
+  float s = 0.f;
+  int64_t off = 0;
+  if (row < rows) {
+    const int64_t hq = row % H_q, qb = row / H_q;
+    const int64_t bat = qb / q_count, qi = q_begin + qb % q_count;
+    off = (bat * N + qi) * H_q + hq;
+    const u32x4 a = *reinterpret_cast<const u32x4*>(dout + off * kDh + 8 * c);
+    const u32x4 b = *reinterpret_cast<const u32x4*>(o + off * kDh + 8 * c);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      s += __uint_as_float(a[j] << 16) * __uint_as_float(b[j] << 16);
+      s += __uint_as_float(a[j] & 0xFFFF0000u) * __uint_as_float(b[j] & 0xFFFF0000u);
+    }
+  }
+#pragma unroll
+  for (int w = 8; w >= 1; w >>= 1) s += __shfl_xor(s, w, 16);
+  if (row < rows && c == 0) dlt[off] = s;
+}
+
+// Sum of the per-slot partials of one (group, query): dQ of its G heads,
+// dq_idx and the KL value, over the slots with a valid block.
+constexpr int kRedThreads = 320;
+
+template <int G>
+__global__ __launch_bounds__(kRedThreads) void bwd_reduce_kernel(
+    const int32_t* __restrict__ block_idx, const uint16_t* __restrict__ dq_part,
+    const float* __restrict__ dqi_part, const float* __restrict__ kl_part, int64_t N, int H_sel, int k,
+    int d_idx, int64_t q_begin, int64_t q_count, uint16_t* __restrict__ dq, uint16_t* __restrict__ dq_idx,
+    float* __restrict__ kl) {
+  const int64_t f = blockIdx.x;  // seq * q_count + query row
+  const int64_t seq = f / q_count, qrow = f % q_count, i = q_begin + qrow;
+  const int64_t bat = seq / H_sel;
+  const int r = static_cast<int>(seq % H_sel);
+  const int64_t L = i / kBk;
+  const int t = threadIdx.x;
+  const int32_t* sel = block_idx + f * k;
+  if (t < 16 * G) {
+    const int g = t >> 4, c = t & 15;
+    float acc[8] = {};
+    for (int s = 0; s < k; ++s) {
+      const int b = sel[s];
+      if (b < 0 || b > L) continue;
+      const u32x4 w = *reinterpret_cast<const u32x4*>(dq_part + ((f * k + s) * G + g) * kDh + 8 * c);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        acc[2 * j] += __uint_as_float(w[j] << 16);
+        acc[2 * j + 1] += __uint_as_float(w[j] & 0xFFFF0000u);
+      }
+    }
+    *reinterpret_cast<u32x4*>(dq + ((bat * N + i) * (H_sel * G) + r * G + g) * kDh + 8 * c) =
+        u32x4{pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]), pack_bf16x2(acc[4], acc[5]),
+              pack_bf16x2(acc[6], acc[7])};
+  } else if (dq_idx && t < 16 * G + d_idx / 4) {
+    const int c = t - 16 * G;
+    float acc[4] = {};
+    for (int s = 0; s < k; ++s) {
+      const int b = sel[s];
+      if (b < 0 || b > L) continue;
+      const f32x4 w = *reinterpret_cast<const f32x4*>(dqi_part + (f * k + s) * d_idx + 4 * c);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[j] += w[j];
+    }
+    *reinterpret_cast<u32x2*>(dq_idx + ((bat * N + i) * H_sel + r) * d_idx + 4 * c) =
+        u32x2{pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])};
+  } else if (kl && t == 16 * G + d_idx / 4) {
+    float s = 0.f;
+    for (int j = 0; j < k; ++j) {
+      const int b = sel[j];
+      if (b >= 0 && b <= L) s += kl_part[f * k + j];
+    }
+    kl[seq * N + i] = s;
+  }
+}
+
+__global__ __launch_bounds__(256) void fill_zero_kernel(float* __restrict__ p, int64_t n) {
+  for (int64_t x = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; x < n;
+       x += static_cast<int64_t>(gridDim.x) * blockDim.x)
+    p[x] = 0.f;
+}
+
+// fp32 accumulators -> bf16 (round to nearest even), 4 values per thread.
+__global__ __launch_bounds__(256) void to_bf16_kernel(const float* __restrict__ src, uint16_t* __restrict__ dst,
+                                                      int64_t n4) {
+  for (int64_t x = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; x < n4;
+       x += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+    const f32x4 w = *reinterpret_cast<const f32x4*>(src + 4 * x);
+    *reinterpret_cast<u32x2*>(dst + 4 * x) = u32x2{pack_bf16x2(w[0], w[1]), pack_bf16x2(w[2], w[3])};
+  }
+}
+
+// Grid-stride kernels: at most 65536 workgroups.
+unsigned grid_of(int64_t n, int per = 256) {
+  int64_t g = (n + per - 1) / per;
+  if (g > 65536) g = 65536;
+  return static_cast<unsigned>(g < 1 ? 1 : g);
+}
+
+// One thread per item: every item gets a thread.
+unsigned grid_exact(int64_t n, int per = 256) {
+  const int64_t g = (n + per - 1) / per;
+  return static_cast<unsigned>(g < 1 ? 1 : g);
+}
+
+int cus_of_device() {
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cus[dev] == 0) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) v = 256;
+    cus[dev] = v;
+  }
+  return cus[dev];
+}
+
+}  // namespace
+
+hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t stream) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(fill_zero_kernel, dim3(grid_of(n)), dim3(256), 0, stream, p, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_to_bf16(const float* src, uint16_t* dst, int64_t n, hipStream_t stream) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(to_bf16_kernel, dim3(grid_of(n / 4)), dim3(256), 0, stream, src, dst, n / 4);
+  return hipGetLastError();
+}
+
+hipError_t launch_backward_chunk(const BwdArgs& a, hipStream_t stream) {
+  const SchedLayout s = sched_layout(a.batch, a.H_sel, a.G, a.k, a.q_begin, a.q_count, kBk);
+  const int64_t seqs = static_cast<int64_t>(a.batch) * a.H_sel;
+  const int H_q = a.H_sel * a.G;
+  const int npairs = static_cast<int>(seqs * s.nW);
+  const int32_t* segp = a.sched + s.off_segp;
+  const PassDesc* passes = reinterpret_cast<const PassDesc*>(a.sched + s.off_pass);
+  const int64_t min_passes = (seqs * a.q_count * a.k + s.EPP - 1) / s.EPP;
+  auto clamp_grid = [&](int64_t g) { return static_cast<unsigned>(g < min_passes ? (g < 1 ? 1 : g) : min_passes); };
+  const float scale_log2 = a.scale * kLog2e;
+
+  // D = rowsum(dO * O) of the range's rows
+  {
+    const int64_t rows = static_cast<int64_t>(a.batch) * a.q_count * H_q;
+    hipLaunchKernelGGL(bwd_prep_kernel, dim3(grid_exact(rows * 16)), dim3(256), 0, stream, a.dout, a.o, a.N, H_q,
+                       a.q_begin, a.q_count, rows, a.dlt);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+
+  if (a.index) {
+    const float isl2 = a.idx_scale * kLog2e;
+    const unsigned lgrid = clamp_grid(static_cast<int64_t>(cus_of_device()) * kLseWgPerCu);
+    auto lk = a.d_idx == 64 ? proxy_lse_kernel<64> : proxy_lse_kernel<128>;
+    hipLaunchKernelGGL(lk, dim3(lgrid), dim3(64), 0, stream, a.q_idx, a.k_idx, a.N, a.H_sel, a.k, isl2,
+                       a.entries, segp, passes, static_cast<int>(s.B_c), npairs, static_cast<int>(a.q_begin),
+                       static_cast<int>(a.q_count), a.lsei_part);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int64_t rows = seqs * a.q_count;
+    hipLaunchKernelGGL(proxy_lse_merge_kernel, dim3(grid_exact(rows)), dim3(256), 0, stream, a.block_idx,
+                       a.lsei_part, a.k, a.q_begin, a.q_count, rows, a.lsei2);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const unsigned grid = clamp_grid(cus_of_device());
+#define MSA_BWD_IDX(GG, DD)                                                                                    \
+  hipLaunchKernelGGL((bwd_idx_kernel<GG, DD>), dim3(grid), dim3(kBT), 0, stream, a.q, a.k_ptr, a.q_idx, a.k_idx, \
+                     a.lse, a.lsei2, a.N, a.H_sel, a.kv_shift, a.k, scale_log2, isl2,                           \
+                     a.kl_weight * a.idx_scale, a.entries, segp, passes, static_cast<int>(s.B_c), npairs,       \
+                     static_cast<int>(a.q_begin), static_cast<int>(a.q_count), a.dqi_part, a.kl_part, a.dki_acc)
+#define MSA_BWD_IDX_G(GG)          \
+  case GG:                         \
+    if (a.d_idx == 64)             \
+      MSA_BWD_IDX(GG, 64);         \
+    else                           \
+      MSA_BWD_IDX(GG, 128);        \
+    break;
+    switch (a.G) {
+      MSA_BWD_IDX_G(1)
+      MSA_BWD_IDX_G(2)
+      MSA_BWD_IDX_G(4)
+      MSA_BWD_IDX_G(8)
+      MSA_BWD_IDX_G(16)
+      default:
+        return hipErrorInvalidValue;
+    }
+#undef MSA_BWD_IDX_G
+#undef MSA_BWD_IDX
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+
+  {
+    const unsigned grid = clamp_grid(cus_of_device());
+#define MSA_BWD_MAIN(GG)                                                                                        \
+  case GG:                                                                                                      \
+    hipLaunchKernelGGL(bwd_main_kernel<GG>, dim3(grid), dim3(kBT), 0, stream, a.q, a.k_ptr, a.v, a.dout, a.lse,  \
+                       a.dlt, a.N, a.H_sel, a.kv_shift, a.k, a.scale, scale_log2, a.entries, segp, passes,      \
+                       static_cast<int>(s.B_c), npairs, static_cast<int>(a.q_begin), static_cast<int>(a.q_count), \
+                       a.dq_part, a.dk_acc, a.dv_acc);                                                          \
+    break;
+    switch (a.G) {
+      MSA_BWD_MAIN(1)
+      MSA_BWD_MAIN(2)
+      MSA_BWD_MAIN(4)
+      MSA_BWD_MAIN(8)
+      MSA_BWD_MAIN(16)
+      default:
+        return hipErrorInvalidValue;
+    }
+#undef MSA_BWD_MAIN
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+
+  {
+    const int64_t rows = seqs * a.q_count;
+    auto launch = [&](auto kern) {
+      hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(rows)), dim3(kRedThreads), 0, stream, a.block_idx,
+                         a.dq_part, a.dqi_part, a.kl_part, a.N, a.H_sel, a.k, a.d_idx, a.q_begin, a.q_count,
+                         a.dq, a.index ? a.dq_idx : nullptr, a.index ? a.kl : nullptr);
+    };
+    switch (a.G) {
+      case 1: launch(bwd_reduce_kernel<1>); break;
+      case 2: launch(bwd_reduce_kernel<2>); break;
+      case 4: launch(bwd_reduce_kernel<4>); break;
+      case 8: launch(bwd_reduce_kernel<8>); break;
+      case 16: launch(bwd_reduce_kernel<16>); break;
+      default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+  }
+}
+
+}  // namespace msa

@@ -183,4 +183,30 @@ hipError_t launch_decode(const uint16_t* q, const uint16_t* q_idx, const uint16_
                          uint16_t* o_part, float* lse_part, uint16_t* o, float* lse,
                          hipStream_t stream, int bk = kBk, const int32_t* lens = nullptr);
 
+// Backward pass over one query range [q_begin, q_begin + q_count) with 128-token
+// blocks.  block_idx holds the range's selection rows [batch][H_sel][q_count][k]
+// and entries / sched the inversion launch_invert built from them.  dk_acc,
+// dv_acc [batch][N][H_kv][d_h] and dki_acc [batch][N][d_idx] are fp32
+// accumulators (atomically added to); dq [batch][N][H_q][d_h], dq_idx
+// [batch][N][H_sel][d_idx] (bf16) and kl [batch][H_sel][N] receive the range's
+// rows.  The rest is scratch: dlt [batch][N][H_q], lsei_part, kl_part
+// [slots], lsei2 [batch][H_sel][q_count], dq_part [slots][G][d_h] (bf16),
+// dqi_part [slots][d_idx].  index = false skips the index branch.
+struct BwdArgs {
+  const uint16_t *q, *k_ptr, *v, *dout, *o, *q_idx, *k_idx;
+  const float* lse;
+  const int32_t *block_idx, *entries, *sched;
+  int batch;
+  int64_t N;
+  int H_sel, G, kv_shift, k, d_idx;
+  int64_t q_begin, q_count;
+  float scale, idx_scale, kl_weight;
+  bool index;
+  float *dlt, *lsei_part, *lsei2, *dqi_part, *kl_part, *dk_acc, *dv_acc, *dki_acc, *kl;
+  uint16_t *dq_part, *dq, *dq_idx;
+};
+hipError_t launch_backward_chunk(const BwdArgs& a, hipStream_t stream);
+hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t stream);
+hipError_t launch_to_bf16(const float* src, uint16_t* dst, int64_t n, hipStream_t stream);
+
 }  // namespace msa

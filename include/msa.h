@@ -59,7 +59,7 @@
 extern "C" {
 #endif
 
-#define MSA_ABI_VERSION 2
+#define MSA_ABI_VERSION 3
 
 enum msa_status_code {
     MSA_OK = 0,
@@ -296,6 +296,50 @@ int msa_decode_workspace_size(const msa_dims *dims, const msa_opts *opts, size_t
 int msa_decode(const msa_dims *dims, const msa_opts *opts, const void *q, const void *q_idx,
                const void *k, const void *v, const void *k_idx, const int32_t *seq_lens, void *o,
                float *lse, int32_t *block_idx_out, void *workspace, size_t ws_bytes, void *stream);
+
+/*
+ * msa_backward_workspace_size / msa_backward -- the training backward pass:
+ * gradients of the sparse main attention with respect to Q, K, V ("MiniMax
+ * Sparse Attention", sec. 2.2: exact softmax attention over the selected
+ * tokens, differentiated), and the KL alignment gradient of the index branch
+ * with respect to Q^idx and K^idx ("MiniMax Sparse Attention (MSA)", Deep
+ * Dive > KL Alignment Loss; "Flash-MSA", KL Divergence Loss): for query i and
+ * group r, teacher P = the mean over the group's G_sel heads of their softmax
+ * over the visible selected tokens (held constant), proxy p_idx = softmax of
+ * z_j = Q^idx_i,r . K^idx_j / sqrt(d_idx) over the same tokens, per-row loss
+ * KL(P || p_idx), and gradient kl_weight * (p_idx - P) on z.  The selection
+ * is the forward's (a constant); the work is scheduled by its inversion
+ * ("Flash-MSA", Backward).
+ *
+ *   q, k, v, q_idx, k_idx  the forward's inputs (bf16, layouts as msa_forward)
+ *   o          bf16 [batch][N][H_q][d_h]  the forward's output
+ *   lse        fp32 [batch][N][H_q]       the forward's natural-log LSE
+ *   d_o        bf16 [batch][N][H_q][d_h]  gradient of the loss w.r.t. o
+ *   block_idx  int32 [batch][H_sel][N][k] the forward's selection
+ *              (msa_forward's block_idx_out)
+ *   kl_weight  multiplier of the KL gradient (e.g. the loss coefficient
+ *              times 1 / (N * H_sel) for the mean over rows and groups)
+ *   dq         bf16 [batch][N][H_q][d_h]   output
+ *   dk, dv     bf16 [batch][N][H_kv][d_h]  output
+ *   dq_idx     bf16 [batch][N][H_sel][d_idx] output    } NULL together
+ *   dk_idx     bf16 [batch][N][d_idx] output            } with kl: the index
+ *   kl         fp32 [batch][H_sel][N] output (may be NULL): } branch is skipped
+ *              per-row KL(P || p_idx), not weighted
+ *   workspace  device memory of msa_backward_workspace_size bytes, 256-byte
+ *              aligned: fp32 gradient accumulators, the inversion, per-slot
+ *              partials (dQ and dq_idx are sums over a row's slots)
+ * bf16 only and B_k = 128 (MSA_ERR_UNSUPPORTED otherwise); opts->q_chunk
+ * splits the query rows into chunks as in msa_forward (dK, dV and dk_idx
+ * accumulate over all chunks).  Softmax scale: opts->softmax_scale (<= 0:
+ * 1 / sqrt(d_h)).  fp32 atomics order the accumulation of dK, dV and dk_idx,
+ * so those outputs may differ in the last bits between runs.
+ */
+int msa_backward_workspace_size(const msa_dims *dims, const msa_opts *opts, size_t *bytes);
+int msa_backward(const msa_dims *dims, const msa_opts *opts, float kl_weight, const void *q,
+                 const void *k, const void *v, const void *q_idx, const void *k_idx, const void *o,
+                 const float *lse, const void *d_o, const int32_t *block_idx, void *dq, void *dk,
+                 void *dv, void *dq_idx, void *dk_idx, float *kl, void *workspace, size_t ws_bytes,
+                 void *stream);
 
 #ifdef __cplusplus
 }

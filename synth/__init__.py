@@ -42,7 +42,7 @@ GAMMA = 0x9E3779B97F4A7C15
 MUL1 = 0xBF58476D1CE4E5B9
 MUL2 = 0x94D049BB133111EB
 
-TID_Q, TID_K, TID_V, TID_QIDX, TID_KIDX, TID_HOT, TID_DIR = range(7)
+TID_Q, TID_K, TID_V, TID_QIDX, TID_KIDX, TID_HOT, TID_DIR, TID_DO = range(8)
 
 
 def _fin_int(z: int) -> int:
@@ -228,7 +228,8 @@ def _planted(codes_bf16, cols, rows_hot, vec):
 def host_rows(w: Workload, which: str, rows) -> np.ndarray:
     """Regenerate whole token rows of one tensor on the host.
 
-    which in {"q", "k", "v", "q_idx", "k_idx"}; rows are token positions of
+    which in {"q", "k", "v", "q_idx", "k_idx", "d_o"} ("d_o": a bf16 output
+    gradient for the backward pass); rows are token positions of
     batch element 0.. (flattened as batch * N + i).  Returns raw codes with
     shape [len(rows), heads, dim] (k_idx: [len(rows), dim])."""
     rows = np.asarray(rows, dtype=np.int64)
@@ -238,6 +239,7 @@ def host_rows(w: Workload, which: str, rows) -> np.ndarray:
         "v": (TID_V, w.H_kv, w.d_h, w.dtype == "fp8"),
         "q_idx": (TID_QIDX, w.H_sel, w.d_idx, False),
         "k_idx": (TID_KIDX, 1, w.d_idx, False),
+        "d_o": (TID_DO, w.H_q, w.d_h, False),
     }[which]
     tid, heads, dim, fp8 = spec
     per_row = heads * dim
@@ -305,6 +307,7 @@ def device_tensor(w: Workload, which: str, device="cuda"):
         "v": (TID_V, w.H_kv, w.d_h, w.dtype == "fp8"),
         "q_idx": (TID_QIDX, w.H_sel, w.d_idx, False),
         "k_idx": (TID_KIDX, 1, w.d_idx, False),
+        "d_o": (TID_DO, w.H_q, w.d_h, False),
     }[which]
     shape = (w.batch, w.N, heads, dim) if which != "k_idx" else (w.batch, w.N, dim)
     n = int(np.prod(shape))

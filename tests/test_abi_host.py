@@ -42,7 +42,7 @@ def test_exports_every_declared_symbol(L):
 
 
 def test_identity(L):
-    assert L.msa_abi_version() == 2
+    assert L.msa_abi_version() == 3
     assert L.msa_status_string(0) == b"ok"
     assert L.msa_status_string(5) == b"workspace too small"
 
@@ -192,3 +192,35 @@ def test_binding_raises_when_library_missing(monkeypatch):
     monkeypatch.setattr(msa, "LIB_PATH", "/nonexistent/libmsa.so")
     with pytest.raises(msa.MSAError):
         msa.lib()
+
+
+def test_backward_validation(L):
+    """msa_backward: bf16 and B_k = 128 only; required pointers; the index
+    outputs come together; 16-byte alignment; a 256-byte aligned workspace of
+    the queried size."""
+    o = msa.make_opts()
+    n = ctypes.c_size_t(0)
+    d = dims()
+    assert L.msa_backward_workspace_size(ctypes.byref(d), ctypes.byref(o), ctypes.byref(n)) == 0
+    size = n.value
+    assert size > 0
+    assert L.msa_backward_workspace_size(ctypes.byref(dims(B_k=64)), ctypes.byref(o), ctypes.byref(n)) == 3
+    fp8 = msa.make_opts("fp8")
+    assert L.msa_backward_workspace_size(ctypes.byref(d), ctypes.byref(fp8), ctypes.byref(n)) == 3
+    assert L.msa_backward_workspace_size(ctypes.byref(d), ctypes.byref(o), None) == 1
+
+    def call(d=d, o=o, w=1.0, dqi=FAKE, dki=FAKE, kl=None, q=FAKE, wsp=ctypes.c_void_p(0x100000),
+             nbytes=size, lse=FAKE):
+        return L.msa_backward(ctypes.byref(d), ctypes.byref(o), w, q, FAKE, FAKE, FAKE, FAKE, FAKE, lse, FAKE,
+                              FAKE, FAKE, FAKE, FAKE, dqi, dki, kl, wsp, nbytes, None)
+
+    assert call(w=float("nan")) == 2
+    assert call(q=None) == 1
+    assert call(lse=None) == 1
+    assert call(dqi=None) == 1             # dk_idx without dq_idx
+    assert call(dqi=None, dki=None, kl=FAKE) == 1
+    assert call(q=ODD) == 4
+    assert call(kl=ODD) == 4
+    assert call(wsp=ctypes.c_void_p(0x100010)) == 4
+    assert call(nbytes=size - 1) == 5
+    assert call(d=dims(B_k=32)) == 3
