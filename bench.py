@@ -12,8 +12,9 @@ times measured with HIP events on the launch stream, each kernel's roofline
 fraction against the published peaks and against peaks measured on this GPU by
 a probe for the same access patterns, the dense causal GQA kernel on the same
 Q, K, V (the baseline MSA's speedup is quoted against), one decode step over 8
-caches of the workload's shape, and the CPU oracle timed on a bounded sample of
-the same workload.
+caches of the workload's shape, the training backward (msa_backward) on the
+forward just timed, and the CPU oracle timed on a bounded sample of the same
+workload.
 """
 from __future__ import annotations
 
@@ -117,6 +118,8 @@ def main():
                     help="skip the dense causal GQA baseline on the same Q, K, V")
     ap.add_argument("--no-decode", action="store_true",
                     help="skip the decode step (last token of 8 sequences of the workload's length)")
+    ap.add_argument("--no-backward", action="store_true",
+                    help="skip the training backward pass (msa_backward) timing")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="first run one plain device-to-device copy of this many MiB (a kernel "
                          "of known traffic, to calibrate hardware byte counters)")
@@ -184,6 +187,7 @@ def main():
         lpart = torch.empty((w.batch, w.H_kv, w.N, w.k, w.G), dtype=torch.float32, device=dev)
         del ws
         torch.cuda.empty_cache()
+        lse_out = torch.empty((w.batch, w.N, w.H_q), dtype=torch.float32, device=dev)
         names = ("index_topk", "invert_blocks", "sparse_attn_fwd", "combine")
         evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps + 1)]
         for it in range(args.steps + 1):       # iteration 0 is a warmup
@@ -196,13 +200,45 @@ def main():
             msa.msa_sparse_attn_fwd(d, o, t["q"], t["k"], t["v"], offs, ents, sched,
                                     o_part=opart, lse_part=lpart)
             e[3].record(stream)
-            msa.msa_combine(d, bi, opart, lpart, o=out)
+            msa.msa_combine(d, bi, opart, lpart, o=out, lse=lse_out)
             e[4].record(stream)
         torch.cuda.synchronize()
         for j, name in enumerate(names):
             kern[name] = float(np.mean([evs[it][j].elapsed_time(evs[it][j + 1])
                                         for it in range(1, args.steps + 1)]))
         log("per call ms: " + ", ".join(f"{k} {v:.3f}" for k, v in kern.items()))
+
+    # ---- the training backward (msa_backward: main-branch dQ, dK, dV and the
+    # KL alignment gradient of the index branch) on the forward just timed,
+    # for single-chunk bf16 workloads; dO is seeded N(0, 1)
+    backward = None
+    if kern and not args.no_backward and w.dtype == "bf16":
+        del opart, lpart
+        torch.cuda.empty_cache()
+        d_o = synth.device_tensor(w, "d_o", dev)
+        wsb = torch.empty((msa.msa_backward_workspace_size(d, o),), dtype=torch.uint8, device=dev)
+        bargs = (d, o, t["q"], t["k"], t["v"], t["q_idx"], t["k_idx"], out, lse_out, d_o, bi)
+        kw = 1.0 / (w.batch * w.N * w.H_sel)
+        log("backward: 1 warmup, 3 timed calls")
+        msa.msa_backward(*bargs, kl_weight=kw, workspace=wsb)
+        torch.cuda.synchronize()
+        eb0, eb1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        eb0.record(stream)
+        for _ in range(3):
+            msa.msa_backward(*bargs, kl_weight=kw, workspace=wsb)
+        eb1.record(stream)
+        torch.cuda.synchronize()
+        bms = eb0.elapsed_time(eb1) / 3
+        sel_b = bi.cpu().numpy().reshape(w.batch * w.H_sel, w.N, w.k)
+        fb_main, fb_idx = acc.backward_flops(sel_b, 0, w.N, w.B_k, w.G_sel, w.d_h, w.d_idx)
+        backward = {"call": "msa_backward", "ms": bms, "bound": "mfma", "flops_main": fb_main,
+                    "flops_index": fb_idx, "achieved": (fb_main + fb_idx) / bms / 1e9,
+                    "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                    "frac": (fb_main + fb_idx) / bms / 1e9 / PEAK_BF16_TFLOPS,
+                    "tokens_s": w.batch * w.N / (bms * 1e-3), "workspace_bytes": wsb.numel()}
+        log(f"backward: {bms:.2f} ms, {backward['achieved']:.0f} TFLOP/s")
+        del d_o, wsb
+        torch.cuda.empty_cache()
 
     # ---- the dense causal GQA baseline on the same Q, K, V (bf16 workloads up
     # to 128K tokens: it grows quadratically, 0.3 s per call at 128K)
@@ -374,6 +410,7 @@ def main():
                    "q_chunk": w.q_chunk, "hot_blocks": w.plant},
         "sparse_tflops": tflops, "index_flops": f_idx, "main_flops": f_main,
         "roofline": roofline, "kernels": kernels, "dense_baseline": dense, "decode": decode,
+        "backward": backward,
         "measured_peaks": peaks, "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

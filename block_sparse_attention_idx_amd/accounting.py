@@ -96,6 +96,20 @@ def main_flops(block_idx: np.ndarray, q_begin: int, N: int, B_k: int, G: int, d_
     return 4.0 * d_h * G * float(visible_keys(block_idx, q_begin, N, B_k).sum())
 
 
+def backward_flops(block_idx: np.ndarray, q_begin: int, N: int, B_k: int, G: int, d_h: int,
+                   d_idx: int, index: bool = True) -> tuple:
+    """FLOPs of the backward pass as its kernels execute it, per visible
+    (query, selection group, key): the main branch recomputes S and forms dP,
+    dV, dK and dQ, 10 d_h per head (2.5x the forward's 4 d_h); the index branch
+    recomputes the G heads' S for the teacher distribution (2 d_h G), the proxy
+    scores twice (once in the proxy log-sum-exp pass, once beside the gradient)
+    and forms dq_idx and dk_idx (8 d_idx in all).  Returns (main, index)."""
+    vis = float(visible_keys(block_idx, q_begin, N, B_k).sum())
+    main = 10.0 * d_h * G * vis
+    idx = (2.0 * d_h * G + 8.0 * d_idx) * vis if index else 0.0
+    return main, idx
+
+
 def dense_flops(q_begin: int, q_count: int, H_q: int, d_h: int, batch: int = 1) -> float:
     """Dense causal attention: 4 d_h FLOPs per (query head, key j <= i)."""
     i = np.arange(q_begin, q_begin + q_count, dtype=np.float64)
