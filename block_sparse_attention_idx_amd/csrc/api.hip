@@ -404,11 +404,11 @@ BackwardLayout backward_layout(const msa_dims* d, const msa_opts* o) {
   L.off_off = take(static_cast<size_t>(seqs) * (B + 1) * 4);
   L.off_ent = take(slots * 4);
   L.off_sched = take(static_cast<size_t>(words) * 4);
-  L.off_dqp = take(slots * GS(d) * d->d_h * 2);
+  L.off_dqp = take((slots + 1) * GS(d) * d->d_h * 2);  // + a spare row for padding rows
   L.off_lsp = take(slots * 4);
   L.off_lsi = take(static_cast<size_t>(seqs) * L.qc * 4);
-  L.off_dqip = take(slots * d->d_idx * 4);
-  L.off_klp = take(slots * 4);
+  L.off_dqip = take((slots + 1) * d->d_idx * 4);
+  L.off_klp = take((slots + 1) * 4);
   L.total = off;
   return L;
 }

@@ -153,6 +153,66 @@ __device__ __forceinline__ void stage_rows(RowPtr row_ptr, uint8_t* rm, uint8_t*
   }
 }
 
+// The two halves of stage_rows, for software pipelining: load_rows issues
+// this thread's global loads (16-byte chunk t % 16 of rows 4 (t / 16) .. + 3;
+// `row_ptr(rho)` must give a readable row), put_rows writes them row-major
+// into `rm` and transposed into `tr` (either may be null).
+template <typename RowPtr>
+__device__ __forceinline__ void load_rows(RowPtr row_ptr, u32x4 (&w)[4]) {
+  const int dg = threadIdx.x & 15, rc = threadIdx.x >> 4;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) w[j] = *reinterpret_cast<const u32x4*>(row_ptr(4 * rc + j) + 8 * dg);
+}
+
+__device__ __forceinline__ void put_rows(const u32x4 (&w)[4], uint8_t* rm, uint8_t* tr) {
+  const int dg = threadIdx.x & 15, rc = threadIdx.x >> 4;
+  if (rm) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) *reinterpret_cast<u32x4*>(rm + (4 * rc + j) * kStr + 16 * dg) = w[j];
+  }
+  if (tr) {
+    const int col = tpos(4 * rc);
+#pragma unroll
+    for (int dd = 0; dd < 8; ++dd) {
+      const u32x2 v = {bf16_of(w[0], dd) | (bf16_of(w[1], dd) << 16),
+                       bf16_of(w[2], dd) | (bf16_of(w[3], dd) << 16)};
+      *reinterpret_cast<u32x2*>(tr + (8 * dg + dd) * kTStr + 2 * col) = v;
+    }
+  }
+}
+
+// The chunks of a workgroup's passes in order: pass descriptor and first
+// entry.  `after` advances the pass iterator, so it is called once per chunk,
+// in sequence.
+struct Chunk {
+  PassDesc D;
+  int cb;
+  bool ok;
+};
+
+template <int EC>
+__device__ __forceinline__ Chunk first_chunk(PassIter& it, const PassDesc* __restrict__ passes) {
+  Chunk c{};
+  const int pi = it.next();
+  c.ok = pi >= 0;
+  if (c.ok) c.D = passes[pi];
+  c.cb = 0;
+  return c;
+}
+
+template <int EC>
+__device__ __forceinline__ Chunk next_chunk(const Chunk& c, PassIter& it, const PassDesc* __restrict__ passes) {
+  Chunk n = c;
+  n.cb += EC;
+  if (n.cb >= c.D.cnt) {
+    const int pi = it.next();
+    n.ok = pi >= 0;
+    if (n.ok) n.D = passes[pi];
+    n.cb = 0;
+  }
+  return n;
+}
+
 // Write the 32 keys x 128 dims a wave holds in registers (lane n: key n, dims
 // 16 ks + 8 h .. + 7) transposed into `kt` ([dim][key], kStr per dim row),
 // columns 32 wave + n.
@@ -173,7 +233,7 @@ __global__ __launch_bounds__(kBT, 1) void bwd_main_kernel(
     const uint16_t* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ dlt,
     int64_t N, int H_sel, int kv_shift, int kslots, float scale, float scale_log2,
     const int32_t* __restrict__ entries, const int32_t* __restrict__ segp,
-    const PassDesc* __restrict__ passes, int B_c, int npairs, int q_begin, int q_count,
+    const PassDesc* __restrict__ passes, int B_c, int npairs, int q_begin, int q_count, int64_t dummy_slot,
     uint16_t* __restrict__ dq_part, float* __restrict__ dk_acc, float* __restrict__ dv_acc) {
   constexpr int EC = kRows / G;  // queries per chunk
   __shared__ __attribute__((aligned(16))) uint8_t qr_lds[kRows * kStr];
@@ -212,9 +272,65 @@ __global__ __launch_bounds__(kBT, 1) void bwd_main_kernel(
       }
   };
 
-  for (int pi = it.next(); pi >= 0; pi = it.next()) {
-    const PassDesc D = passes[pi];
+  // Software pipeline over the workgroup's chunks: while chunk c computes,
+  // chunk c + 1's entries are loaded (before S) and then its Q and dO rows
+  // and row constants (after S), into registers that go to LDS at the top of
+  // the next iteration.  Every global load and store of the loop is issued
+  // unconditionally (rows past a pass's end read its last entry and store
+  // their zero dQ to a spare row), so the in-order vmcnt waits never drain
+  // the prefetch early.
+  Chunk cur = first_chunk<EC>(it, passes);
+  if (!cur.ok) return;
+  u32x4 wq[4], wdo[4];   // this thread's staging chunks of the next rows
+  int p_i = -1;          // the row constants of row tid (< kRows)
+  float p_lse2 = 0.f, p_dlt = 0.f;
+  int64_t p_orow = 0;
+  const int rc = tid >> 4, crow = tid & (kRows - 1);
+
+  // entry words of chunk c for this thread's staging rows and constant row
+  auto chunk_entries = [&](const Chunk& c, uint32_t (&en)[4], uint32_t& enc) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      en[j] = static_cast<uint32_t>(entries[c.D.start + min(c.cb + (4 * rc + j) / G, c.D.cnt - 1)]);
+    enc = static_cast<uint32_t>(entries[c.D.start + min(c.cb + crow / G, c.D.cnt - 1)]);
+  };
+  // issue the row loads of chunk c from its entry words
+  auto chunk_rows = [&](const Chunk& c, const uint32_t (&en)[4], uint32_t enc) {
+    const int cbat = c.D.seq / H_sel, cr = c.D.seq - cbat * H_sel;
+    auto rowoff = [&](uint32_t ent, int rho) -> int64_t {
+      const EntryRef x = entry_ref(ent, c.D.seq, kslots, q_begin, q_count);
+      return (static_cast<int64_t>(cbat) * N + x.i) * H_q + cr * G + rho % G;
+    };
+    load_rows([&](int rho) { return q + rowoff(en[rho & 3], rho) * kDh; }, wq);
+    load_rows([&](int rho) { return dout + rowoff(en[rho & 3], rho) * kDh; }, wdo);
+    const EntryRef x = entry_ref(enc, c.D.seq, kslots, q_begin, q_count);
+    const int64_t o = (static_cast<int64_t>(cbat) * N + x.i) * H_q + cr * G + crow % G;
+    const bool ok = c.cb + crow / G < c.D.cnt;
+    const float l = lse[o], dl = dlt[o];
+    p_i = ok ? x.i : -1;
+    p_lse2 = ok ? l * kLog2e : 0.f;
+    p_dlt = ok ? dl : 0.f;
+    p_orow = (ok ? x.slot : dummy_slot) * G + crow % G;
+  };
+  {
+    uint32_t en[4], enc;
+    chunk_entries(cur, en, enc);
+    chunk_rows(cur, en, enc);
+  }
+  Chunk nx = next_chunk<EC>(cur, it, passes);
+
+  while (true) {
+    const PassDesc D = cur.D;
     const int bat = D.seq / H_sel, r = D.seq - bat * H_sel;
+    // ---- this chunk's rows and constants into LDS
+    put_rows(wq, qr_lds, qt_lds);
+    put_rows(wdo, dor_lds, dot_lds);
+    if (tid < kRows) {
+      ri_i[tid] = p_i;
+      ri_lse2[tid] = p_lse2;
+      ri_dlt[tid] = p_dlt;
+      ri_orow[tid] = p_orow;
+    }
     if (D.seq != cur_seq || D.blk != cur_blk) {
       flush();
       cur_seq = D.seq;
@@ -238,105 +354,86 @@ __global__ __launch_bounds__(kBT, 1) void bwd_main_kernel(
         dvt[dt] = f32x16{};
       }
       // every wave finished the previous chunk's dQ (trailing barrier), so
-      // K^T can be replaced; the staging barrier below publishes it
+      // K^T can be replaced; the barrier below publishes it
       store_keys_t<8>(kf, kt_lds, wave, n, h);
     }
     const int key_abs = D.blk * kBk + key_l;
+    // ---- the next chunk's entry words (the last chunk reloads its own)
+    const Chunk& src = nx.ok ? nx : cur;
+    uint32_t en[4], enc;
+    chunk_entries(src, en, enc);
+    __syncthreads();
 
-    for (int cb = 0; cb < D.cnt; cb += EC) {
-      // ---- stage the chunk's Q and dO rows and per-row constants
-      auto row_off = [&](int rho, EntryRef* er) -> int64_t {
-        const int e = cb + rho / G;
-        if (e >= D.cnt) return -1;
-        const EntryRef x = entry_ref(static_cast<uint32_t>(entries[D.start + e]), D.seq, kslots, q_begin, q_count);
-        if (er) *er = x;
-        return (static_cast<int64_t>(bat) * N + x.i) * H_q + r * G + rho % G;
-      };
-      stage_rows([&](int rho) -> const uint16_t* {
-        const int64_t o = row_off(rho, nullptr);
-        return o < 0 ? nullptr : q + o * kDh;
-      }, qr_lds, qt_lds);
-      stage_rows([&](int rho) -> const uint16_t* {
-        const int64_t o = row_off(rho, nullptr);
-        return o < 0 ? nullptr : dout + o * kDh;
-      }, dor_lds, dot_lds);
-      if (tid < kRows) {
-        EntryRef er{};
-        const int64_t o = row_off(tid, &er);
-        ri_i[tid] = o < 0 ? -1 : er.i;
-        ri_lse2[tid] = o < 0 ? 0.f : lse[o] * kLog2e;
-        ri_dlt[tid] = o < 0 ? 0.f : dlt[o];
-        ri_orow[tid] = o < 0 ? 0 : er.slot * G + tid % G;
+    // ---- S, P, dP, dS for the wave's 32 keys (lane = key, elements = rows)
+    bf16x8 pb[4], db[4];
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt) {
+      f32x16 s = {}, dp = {};
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) {
+        const int off = (32 * rt + n) * kStr + 32 * ks + 16 * h;
+        s = mfma32x32x16(lds_frag(qr_lds + off), as_bf16x8(kf[ks]), s);
+        dp = mfma32x32x16(lds_frag(dor_lds + off), as_bf16x8(vf[ks]), dp);
       }
-      __syncthreads();
-
-      // ---- S, P, dP, dS for the wave's 32 keys (lane = key, elements = rows)
-      bf16x8 pb[4], db[4];
+      f32x16 p, ds;
 #pragma unroll
-      for (int rt = 0; rt < 2; ++rt) {
-        f32x16 s = {}, dp = {};
-#pragma unroll
-        for (int ks = 0; ks < 8; ++ks) {
-          const int off = (32 * rt + n) * kStr + 32 * ks + 16 * h;
-          s = mfma32x32x16(lds_frag(qr_lds + off), as_bf16x8(kf[ks]), s);
-          dp = mfma32x32x16(lds_frag(dor_lds + off), as_bf16x8(vf[ks]), dp);
-        }
-        f32x16 p, ds;
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int rho = 32 * rt + acc_row(e, h);
-          const float pe = key_abs <= ri_i[rho]
-                               ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[e], scale_log2, -ri_lse2[rho]))
-                               : 0.f;
-          p[e] = pe;
-          ds[e] = pe * (dp[e] - ri_dlt[rho]);
-          *reinterpret_cast<uint16_t*>(ds_lds + rho * kStr + 2 * key_l) = bf16_bits(ds[e]);
-        }
-        pb[2 * rt] = pack_step(p, 0);
-        pb[2 * rt + 1] = pack_step(p, 1);
-        db[2 * rt] = pack_step(ds, 0);
-        db[2 * rt + 1] = pack_step(ds, 1);
+      for (int e = 0; e < 16; ++e) {
+        const int rho = 32 * rt + acc_row(e, h);
+        const float pe = key_abs <= ri_i[rho]
+                             ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[e], scale_log2, -ri_lse2[rho]))
+                             : 0.f;
+        p[e] = pe;
+        ds[e] = pe * (dp[e] - ri_dlt[rho]);
+        *reinterpret_cast<uint16_t*>(ds_lds + rho * kStr + 2 * key_l) = bf16_bits(ds[e]);
       }
-
-      // ---- dV^T += dO^T P, dK^T += Q^T dS (reduction over the 64 rows)
-#pragma unroll
-      for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-        for (int st = 0; st < 4; ++st) {
-          const int off = (32 * dt + n) * kTStr + 32 * st + 16 * h;
-          dvt[dt] = mfma32x32x16(lds_frag(dot_lds + off), pb[st], dvt[dt]);
-          dkt[dt] = mfma32x32x16(lds_frag(qt_lds + off), db[st], dkt[dt]);
-        }
-      __syncthreads();
-
-      // ---- dQ^T = K^T dS^T over the block's 128 keys: wave w takes rows
-      // 32 (w / 2) .. + 31 and dims 64 (w % 2) .. + 63
-      {
-        const int rt = wave >> 1, dt0 = 2 * (wave & 1);
-        f32x16 qa[2] = {};
-#pragma unroll
-        for (int kk = 0; kk < 8; ++kk) {
-          const bf16x8 b = lds_frag(ds_lds + (32 * rt + n) * kStr + 32 * kk + 16 * h);
-#pragma unroll
-          for (int j = 0; j < 2; ++j)
-            qa[j] = mfma32x32x16(lds_frag(kt_lds + (32 * (dt0 + j) + n) * kStr + 32 * kk + 16 * h), b, qa[j]);
-        }
-        const int rho = 32 * rt + n;
-        if (ri_i[rho] >= 0) {
-          uint16_t* dst = dq_part + ri_orow[rho] * kDh;
-#pragma unroll
-          for (int j = 0; j < 2; ++j)
-#pragma unroll
-            for (int e4 = 0; e4 < 4; ++e4) {
-              const int d0 = 32 * (dt0 + j) + 8 * e4 + 4 * h;
-              *reinterpret_cast<u32x2*>(dst + d0) =
-                  u32x2{pack_bf16x2(qa[j][4 * e4] * scale, qa[j][4 * e4 + 1] * scale),
-                        pack_bf16x2(qa[j][4 * e4 + 2] * scale, qa[j][4 * e4 + 3] * scale)};
-            }
-        }
-      }
-      __syncthreads();
+      pb[2 * rt] = pack_step(p, 0);
+      pb[2 * rt + 1] = pack_step(p, 1);
+      db[2 * rt] = pack_step(ds, 0);
+      db[2 * rt + 1] = pack_step(ds, 1);
     }
+
+    // ---- the next chunk's rows go out while this chunk finishes
+    chunk_rows(src, en, enc);
+
+    // ---- dV^T += dO^T P, dK^T += Q^T dS (reduction over the 64 rows)
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int st = 0; st < 4; ++st) {
+        const int off = (32 * dt + n) * kTStr + 32 * st + 16 * h;
+        dvt[dt] = mfma32x32x16(lds_frag(dot_lds + off), pb[st], dvt[dt]);
+        dkt[dt] = mfma32x32x16(lds_frag(qt_lds + off), db[st], dkt[dt]);
+      }
+    __syncthreads();
+
+    // ---- dQ^T = K^T dS^T over the block's 128 keys: wave w takes rows
+    // 32 (w / 2) .. + 31 and dims 64 (w % 2) .. + 63
+    {
+      const int rt = wave >> 1, dt0 = 2 * (wave & 1);
+      f32x16 qa[2] = {};
+#pragma unroll
+      for (int kk = 0; kk < 8; ++kk) {
+        const bf16x8 b = lds_frag(ds_lds + (32 * rt + n) * kStr + 32 * kk + 16 * h);
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          qa[j] = mfma32x32x16(lds_frag(kt_lds + (32 * (dt0 + j) + n) * kStr + 32 * kk + 16 * h), b, qa[j]);
+      }
+      const int rho = 32 * rt + n;
+      uint16_t* dst = dq_part + ri_orow[rho] * kDh;
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int e4 = 0; e4 < 4; ++e4) {
+          const int d0 = 32 * (dt0 + j) + 8 * e4 + 4 * h;
+          *reinterpret_cast<u32x2*>(dst + d0) =
+              u32x2{pack_bf16x2(qa[j][4 * e4] * scale, qa[j][4 * e4 + 1] * scale),
+                    pack_bf16x2(qa[j][4 * e4 + 2] * scale, qa[j][4 * e4 + 3] * scale)};
+        }
+    }
+    __syncthreads();
+    if (!nx.ok) break;
+    cur = nx;
+    nx = next_chunk<EC>(cur, it, passes);
   }
   flush();
 }
@@ -348,7 +445,7 @@ __global__ __launch_bounds__(kBT, 1) void bwd_idx_kernel(
     const uint16_t* __restrict__ k_idx, const float* __restrict__ lse, const float* __restrict__ lsei2,
     int64_t N, int H_sel, int kv_shift, int kslots, float scale_log2, float idx_scale_log2, float gscale,
     const int32_t* __restrict__ entries, const int32_t* __restrict__ segp,
-    const PassDesc* __restrict__ passes, int B_c, int npairs, int q_begin, int q_count,
+    const PassDesc* __restrict__ passes, int B_c, int npairs, int q_begin, int q_count, int64_t dummy_slot,
     float* __restrict__ dqi_part, float* __restrict__ kl_part, float* __restrict__ dki_acc) {
   constexpr int EC = kRows / G;        // queries (index rows) per chunk
   constexpr int ZT = (EC + 31) / 32;   // 32-row tiles of index rows
@@ -385,9 +482,94 @@ __global__ __launch_bounds__(kBT, 1) void bwd_idx_kernel(
       for (int e = 0; e < 16; ++e) unsafeAtomicAdd(dst + 32 * tt + acc_row(e, h), dkit[tt][e]);
   };
 
-  for (int pi = it.next(); pi >= 0; pi = it.next()) {
-    const PassDesc D = passes[pi];
+  // Software pipeline over the workgroup's chunks, as in the main branch:
+  // chunk c + 1's entry words load before the teacher's S, its Q rows, index
+  // rows and row constants after it; every global load and store of the loop
+  // is unconditional (padding rows read the pass's last entry and store to a
+  // spare row).
+  Chunk cur = first_chunk<EC>(it, passes);
+  if (!cur.ok) return;
+  const int rc = tid >> 4, dg = tid & 15, crow = tid & (kRows - 1);
+  constexpr int NCI = DIDX / 8;  // 16-byte chunks per index row
+  u32x4 wq[4], wqi[4];
+  int p_i = -1, pe_i = -1;
+  float p_lse2 = 0.f, pe_l2 = 0.f;
+  int64_t pe_slot = 0;
+
+  // entry words: staging rows 4 rc + j of the main rows (query (4 rc + j) / G)
+  // and of the index rows (query 4 rc + j), then the constant rows
+  auto chunk_entries = [&](const Chunk& c, uint32_t (&en)[4], uint32_t (&eni)[4], uint32_t& enc,
+                           uint32_t& enci) {
+    const int last = c.D.cnt - 1;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      en[j] = static_cast<uint32_t>(entries[c.D.start + min(c.cb + (4 * rc + j) / G, last)]);
+      eni[j] = static_cast<uint32_t>(entries[c.D.start + min(c.cb + min(4 * rc + j, EC - 1), last)]);
+    }
+    enc = static_cast<uint32_t>(entries[c.D.start + min(c.cb + crow / G, last)]);
+    enci = static_cast<uint32_t>(entries[c.D.start + min(c.cb + min(crow, EC - 1), last)]);
+  };
+  auto chunk_rows = [&](const Chunk& c, const uint32_t (&en)[4], const uint32_t (&eni)[4], uint32_t enc,
+                        uint32_t enci) {
+    const int cbat = c.D.seq / H_sel, cr = c.D.seq - cbat * H_sel;
+    load_rows([&](int rho) {
+      const EntryRef x = entry_ref(en[rho & 3], c.D.seq, kslots, q_begin, q_count);
+      return q + ((static_cast<int64_t>(cbat) * N + x.i) * H_q + cr * G + rho % G) * kDh;
+    }, wq);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const EntryRef x = entry_ref(eni[j], c.D.seq, kslots, q_begin, q_count);
+      wqi[j] = *reinterpret_cast<const u32x4*>(
+          q_idx + ((static_cast<int64_t>(cbat) * N + x.i) * H_sel + cr) * DIDX + 8 * min(dg, NCI - 1));
+    }
+    const EntryRef x = entry_ref(enc, c.D.seq, kslots, q_begin, q_count);
+    const float l = lse[(static_cast<int64_t>(cbat) * N + x.i) * H_q + cr * G + crow % G];
+    const bool ok = c.cb + crow / G < c.D.cnt;
+    p_i = ok ? x.i : -1;
+    p_lse2 = ok ? l * kLog2e : 0.f;
+    const EntryRef y = entry_ref(enci, c.D.seq, kslots, q_begin, q_count);
+    const float l2 = lsei2[y.slot / kslots];
+    const bool oke = crow < EC && c.cb + crow < c.D.cnt;
+    pe_i = oke ? y.i : -1;
+    pe_l2 = oke ? l2 : 0.f;
+    pe_slot = oke ? y.slot : dummy_slot;
+  };
+  {
+    uint32_t en[4], eni[4], enc, enci;
+    chunk_entries(cur, en, eni, enc, enci);
+    chunk_rows(cur, en, eni, enc, enci);
+  }
+  Chunk nx = next_chunk<EC>(cur, it, passes);
+
+  while (true) {
+    const PassDesc D = cur.D;
     const int bat = D.seq / H_sel, r = D.seq - bat * H_sel;
+    // ---- this chunk's Q rows, index rows (row-major and transposed; rows
+    // past the chunk are zeros) and row constants into LDS
+    put_rows(wq, qr_lds, nullptr);
+    if (dg < NCI) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const u32x4 w = 4 * rc + j < EC ? wqi[j] : u32x4{0u, 0u, 0u, 0u};
+        wqi[j] = w;
+        *reinterpret_cast<u32x4*>(qi_lds + (4 * rc + j) * kStr + 16 * dg) = w;
+      }
+      const int col = tpos(4 * rc);
+#pragma unroll
+      for (int dd = 0; dd < 8; ++dd) {
+        const u32x2 v = {bf16_of(wqi[0], dd) | (bf16_of(wqi[1], dd) << 16),
+                         bf16_of(wqi[2], dd) | (bf16_of(wqi[3], dd) << 16)};
+        *reinterpret_cast<u32x2*>(qit_lds + (8 * dg + dd) * kTStr + 2 * col) = v;
+      }
+    }
+    if (tid < kRows) {
+      ri_i[tid] = p_i;
+      ri_lse2[tid] = p_lse2;
+      ei_i[tid] = pe_i;
+      ei_l2[tid] = pe_l2;
+      ei_slot[tid] = pe_slot;
+    }
+    for (int x = tid; x < EC * kBk; x += kBT) tch[x] = 0.f;
     if (D.seq != cur_seq || D.blk != cur_blk) {
       flush();
       cur_seq = D.seq;
@@ -413,140 +595,101 @@ __global__ __launch_bounds__(kBT, 1) void bwd_idx_kernel(
       store_keys_t<KSI>(kif, kit_lds, wave, n, h);
     }
     const int key_abs = D.blk * kBk + key_l;
+    const Chunk& src = nx.ok ? nx : cur;
+    uint32_t en[4], eni[4], enc, enci;
+    chunk_entries(src, en, eni, enc, enci);
+    __syncthreads();
 
-    for (int cb = 0; cb < D.cnt; cb += EC) {
-      // ---- stage Q rows, index rows (row-major and transposed), constants
-      auto ent_of = [&](int e, EntryRef* er) -> bool {  // chunk index row e
-        if (e >= EC || cb + e >= D.cnt) return false;
-        *er = entry_ref(static_cast<uint32_t>(entries[D.start + cb + e]), D.seq, kslots, q_begin, q_count);
-        return true;
-      };
-      stage_rows([&](int rho) -> const uint16_t* {
-        EntryRef er;
-        if (!ent_of(rho / G, &er)) return nullptr;
-        return q + ((static_cast<int64_t>(bat) * N + er.i) * H_q + r * G + rho % G) * kDh;
-      }, qr_lds, nullptr);
-      {
-        // index rows: thread t loads 16-byte chunk t % 16 (< DIDX / 8) of rows
-        // 4 (t / 16) .. + 3 (all 64 rows written, zeros past the chunk)
-        const int dg = tid & 15, rc = tid >> 4;
-        if (dg < DIDX / 8) {
-          u32x4 w[4];
+    // ---- teacher: mean over the G heads of the main probabilities
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            EntryRef er;
-            w[j] = u32x4{0u, 0u, 0u, 0u};
-            if (ent_of(4 * rc + j, &er))
-              w[j] = *reinterpret_cast<const u32x4*>(
-                  q_idx + ((static_cast<int64_t>(bat) * N + er.i) * H_sel + r) * DIDX + 8 * dg);
-            *reinterpret_cast<u32x4*>(qi_lds + (4 * rc + j) * kStr + 16 * dg) = w[j];
-          }
-          const int col = tpos(4 * rc);
+    for (int rt = 0; rt < 2; ++rt) {
+      f32x16 s = {};
 #pragma unroll
-          for (int dd = 0; dd < 8; ++dd) {
-            const u32x2 v = {bf16_of(w[0], dd) | (bf16_of(w[1], dd) << 16),
-                             bf16_of(w[2], dd) | (bf16_of(w[3], dd) << 16)};
-            *reinterpret_cast<u32x2*>(qit_lds + (8 * dg + dd) * kTStr + 2 * col) = v;
-          }
+      for (int ks = 0; ks < 8; ++ks)
+        s = mfma32x32x16(lds_frag(qr_lds + (32 * rt + n) * kStr + 32 * ks + 16 * h), as_bf16x8(kf[ks]), s);
+      constexpr int RUN = G < 4 ? G : 4;  // consecutive elements of one query
+#pragma unroll
+      for (int e0 = 0; e0 < 16; e0 += RUN) {
+        float acc = 0.f;
+#pragma unroll
+        for (int e = e0; e < e0 + RUN; ++e) {
+          const int rho = 32 * rt + acc_row(e, h);
+          acc += key_abs <= ri_i[rho]
+                     ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[e], scale_log2, -ri_lse2[rho]))
+                     : 0.f;
         }
+        const int row = (32 * rt + acc_row(e0, h)) / G;
+        atomicAdd(&tch[row * kBk + key_l], acc * kInvG);
       }
-      if (tid < kRows) {
-        EntryRef er;
-        const bool ok = ent_of(tid / G, &er);
-        ri_i[tid] = ok ? er.i : -1;
-        ri_lse2[tid] = ok ? lse[(static_cast<int64_t>(bat) * N + er.i) * H_q + r * G + tid % G] * kLog2e : 0.f;
-        const bool oke = ent_of(tid, &er);
-        ei_i[tid] = oke ? er.i : -1;
-        ei_l2[tid] = oke ? lsei2[er.slot / kslots] : 0.f;
-        ei_slot[tid] = oke ? er.slot : 0;
-      }
-      for (int x = tid; x < 64 * kBk; x += kBT) tch[x] = 0.f;
-      __syncthreads();
-
-      // ---- teacher: mean over the G heads of the main probabilities
-#pragma unroll
-      for (int rt = 0; rt < 2; ++rt) {
-        f32x16 s = {};
-#pragma unroll
-        for (int ks = 0; ks < 8; ++ks)
-          s = mfma32x32x16(lds_frag(qr_lds + (32 * rt + n) * kStr + 32 * ks + 16 * h), as_bf16x8(kf[ks]), s);
-        constexpr int RUN = G < 4 ? G : 4;  // consecutive elements of one query
-#pragma unroll
-        for (int e0 = 0; e0 < 16; e0 += RUN) {
-          float acc = 0.f;
-#pragma unroll
-          for (int e = e0; e < e0 + RUN; ++e) {
-            const int rho = 32 * rt + acc_row(e, h);
-            acc += key_abs <= ri_i[rho]
-                       ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[e], scale_log2, -ri_lse2[rho]))
-                       : 0.f;
-          }
-          const int row = (32 * rt + acc_row(e0, h)) / G;
-          atomicAdd(&tch[row * kBk + key_l], acc * kInvG);
-        }
-      }
-
-      // ---- proxy probabilities, KL terms and the gradient g on z
-      bf16x8 gb[2 * ZT];
-#pragma unroll
-      for (int zt = 0; zt < ZT; ++zt) {
-        f32x16 z = {};
-#pragma unroll
-        for (int ks = 0; ks < KSI; ++ks)
-          z = mfma32x32x16(lds_frag(qi_lds + (32 * zt + n) * kStr + 32 * ks + 16 * h), as_bf16x8(kif[ks]), z);
-        f32x16 g;
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int row = 32 * zt + acc_row(e, h);
-          float ge = 0.f;
-          if (row < EC) {
-            const bool vis = key_abs <= ei_i[row];
-            const float zl2 = __builtin_fmaf(z[e], idx_scale_log2, -ei_l2[row]);  // log2 p_px
-            const float ppx = vis ? __builtin_amdgcn_exp2f(zl2) : 0.f;
-            float* tp = &tch[row * kBk + key_l];
-            const float T = *tp;
-            *tp = (vis && T > 0.f) ? T * (__builtin_amdgcn_logf(T) - zl2) * kLn2 : 0.f;
-            ge = gscale * (ppx - T);
-            *reinterpret_cast<uint16_t*>(g_lds + row * kStr + 2 * key_l) = bf16_bits(ge);
-          }
-          g[e] = ge;
-        }
-        gb[2 * zt] = pack_step(g, 0);
-        gb[2 * zt + 1] = pack_step(g, 1);
-      }
-
-      // ---- dk_idx^T += q_idx^T g (reduction over the chunk's index rows)
-#pragma unroll
-      for (int tt = 0; tt < TT; ++tt)
-#pragma unroll
-        for (int st = 0; st < KE; ++st)
-          dkit[tt] = mfma32x32x16(lds_frag(qit_lds + (32 * tt + n) * kTStr + 32 * st + 16 * h), gb[st], dkit[tt]);
-      __syncthreads();
-
-      // ---- dq_idx^T = k_idx^T g^T over the block's keys, and the KL sums
-#pragma unroll
-      for (int x = wave; x < TT * ZT; x += kBW) {
-        const int tt = x % TT, zt = x / TT;
-        f32x16 a = {};
-#pragma unroll
-        for (int kk = 0; kk < 8; ++kk)
-          a = mfma32x32x16(lds_frag(kit_lds + (32 * tt + n) * kStr + 32 * kk + 16 * h),
-                           lds_frag(g_lds + (32 * zt + n) * kStr + 32 * kk + 16 * h), a);
-        const int row = 32 * zt + n;
-        if (row < EC && ei_i[row] >= 0) {
-          float* dst = dqi_part + ei_slot[row] * DIDX + 32 * tt + 4 * h;
-#pragma unroll
-          for (int e4 = 0; e4 < 4; ++e4)
-            *reinterpret_cast<f32x4*>(dst + 8 * e4) = f32x4{a[4 * e4], a[4 * e4 + 1], a[4 * e4 + 2], a[4 * e4 + 3]};
-        }
-      }
-      if (tid < EC && ei_i[tid] >= 0) {
-        float s = 0.f;
-        for (int j = 0; j < kBk; ++j) s += tch[tid * kBk + j];
-        kl_part[ei_slot[tid]] = s;
-      }
-      __syncthreads();
     }
+
+    // ---- the next chunk's rows go out while this chunk finishes
+    chunk_rows(src, en, eni, enc, enci);
+
+    // ---- proxy probabilities, KL terms and the gradient g on z
+    bf16x8 gb[2 * ZT];
+#pragma unroll
+    for (int zt = 0; zt < ZT; ++zt) {
+      f32x16 z = {};
+#pragma unroll
+      for (int ks = 0; ks < KSI; ++ks)
+        z = mfma32x32x16(lds_frag(qi_lds + (32 * zt + n) * kStr + 32 * ks + 16 * h), as_bf16x8(kif[ks]), z);
+      f32x16 g;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int row = 32 * zt + acc_row(e, h);
+        float ge = 0.f;
+        if (row < EC) {
+          const bool vis = key_abs <= ei_i[row];
+          const float zl2 = __builtin_fmaf(z[e], idx_scale_log2, -ei_l2[row]);  // log2 p_px
+          const float ppx = vis ? __builtin_amdgcn_exp2f(zl2) : 0.f;
+          float* tp = &tch[row * kBk + key_l];
+          const float T = *tp;
+          *tp = (vis && T > 0.f) ? T * (__builtin_amdgcn_logf(T) - zl2) * kLn2 : 0.f;
+          ge = gscale * (ppx - T);
+          *reinterpret_cast<uint16_t*>(g_lds + row * kStr + 2 * key_l) = bf16_bits(ge);
+        }
+        g[e] = ge;
+      }
+      gb[2 * zt] = pack_step(g, 0);
+      gb[2 * zt + 1] = pack_step(g, 1);
+    }
+
+    // ---- dk_idx^T += q_idx^T g (reduction over the chunk's index rows)
+#pragma unroll
+    for (int tt = 0; tt < TT; ++tt)
+#pragma unroll
+      for (int st = 0; st < KE; ++st)
+        dkit[tt] = mfma32x32x16(lds_frag(qit_lds + (32 * tt + n) * kTStr + 32 * st + 16 * h), gb[st], dkit[tt]);
+    __syncthreads();
+
+    // ---- dq_idx^T = k_idx^T g^T over the block's keys (padding rows write
+    // the spare row), and the per-row KL sums (a wave per row)
+#pragma unroll
+    for (int x = wave; x < TT * ZT; x += kBW) {
+      const int tt = x % TT, zt = x / TT;
+      f32x16 a = {};
+#pragma unroll
+      for (int kk = 0; kk < 8; ++kk)
+        a = mfma32x32x16(lds_frag(kit_lds + (32 * tt + n) * kStr + 32 * kk + 16 * h),
+                         lds_frag(g_lds + (32 * zt + n) * kStr + 32 * kk + 16 * h), a);
+      const int row = 32 * zt + n;
+      float* dst = dqi_part + (row < EC ? ei_slot[row] : dummy_slot) * DIDX + 32 * tt + 4 * h;
+#pragma unroll
+      for (int e4 = 0; e4 < 4; ++e4)
+        *reinterpret_cast<f32x4*>(dst + 8 * e4) = f32x4{a[4 * e4], a[4 * e4 + 1], a[4 * e4 + 2], a[4 * e4 + 3]};
+    }
+#pragma unroll
+    for (int row = wave; row < EC; row += kBW) {
+      float sum = tch[row * kBk + lane] + tch[row * kBk + 64 + lane];
+#pragma unroll
+      for (int m = 32; m >= 1; m >>= 1) sum += __shfl_xor(sum, m);
+      kl_part[ei_slot[row]] = sum;  // every lane: the same value to the same word
+    }
+    __syncthreads();
+    if (!nx.ok) break;
+    cur = nx;
+    nx = next_chunk<EC>(cur, it, passes);
   }
   flush();
 }
@@ -791,6 +934,8 @@ hipError_t launch_backward_chunk(const BwdArgs& a, hipStream_t stream) {
   const int64_t min_passes = (seqs * a.q_count * a.k + s.EPP - 1) / s.EPP;
   auto clamp_grid = [&](int64_t g) { return static_cast<unsigned>(g < min_passes ? (g < 1 ? 1 : g) : min_passes); };
   const float scale_log2 = a.scale * kLog2e;
+  // the spare partial row past this range's slots (rows that are padding write there)
+  const int64_t dummy_slot = seqs * a.q_count * a.k;
 
   // D = rowsum(dO * O) of the range's rows
   {
@@ -820,7 +965,8 @@ hipError_t launch_backward_chunk(const BwdArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL((bwd_idx_kernel<GG, DD>), dim3(grid), dim3(kBT), 0, stream, a.q, a.k_ptr, a.q_idx, a.k_idx, \
                      a.lse, a.lsei2, a.N, a.H_sel, a.kv_shift, a.k, scale_log2, isl2,                           \
                      a.kl_weight * a.idx_scale, a.entries, segp, passes, static_cast<int>(s.B_c), npairs,       \
-                     static_cast<int>(a.q_begin), static_cast<int>(a.q_count), a.dqi_part, a.kl_part, a.dki_acc)
+                     static_cast<int>(a.q_begin), static_cast<int>(a.q_count), dummy_slot, a.dqi_part, a.kl_part, \
+                     a.dki_acc)
 #define MSA_BWD_IDX_G(GG)          \
   case GG:                         \
     if (a.d_idx == 64)             \
@@ -850,7 +996,7 @@ hipError_t launch_backward_chunk(const BwdArgs& a, hipStream_t stream) {
     hipLaunchKernelGGL(bwd_main_kernel<GG>, dim3(grid), dim3(kBT), 0, stream, a.q, a.k_ptr, a.v, a.dout, a.lse,  \
                        a.dlt, a.N, a.H_sel, a.kv_shift, a.k, a.scale, scale_log2, a.entries, segp, passes,      \
                        static_cast<int>(s.B_c), npairs, static_cast<int>(a.q_begin), static_cast<int>(a.q_count), \
-                       a.dq_part, a.dk_acc, a.dv_acc);                                                          \
+                       dummy_slot, a.dq_part, a.dk_acc, a.dv_acc);                                              \
     break;
     switch (a.G) {
       MSA_BWD_MAIN(1)
