@@ -52,6 +52,7 @@ namespace msa {
 namespace {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
 using tile::bf16_of;
 using tile::halves_max;
 using tile::halves_sum;
@@ -242,8 +243,8 @@ __global__ __launch_bounds__(kBT, 1) void bwd_main_kernel(
   __shared__ __attribute__((aligned(16))) uint8_t dot_lds[kDh * kTStr];
   __shared__ __attribute__((aligned(16))) uint8_t kt_lds[kDh * kStr];
   __shared__ __attribute__((aligned(16))) uint8_t ds_lds[kRows * kStr];
-  __shared__ int ri_i[kRows];
-  __shared__ float ri_lse2[kRows], ri_dlt[kRows];
+  __shared__ __attribute__((aligned(16))) int ri_i[kRows];
+  __shared__ __attribute__((aligned(16))) float ri_lse2[kRows], ri_dlt[kRows];
   __shared__ int64_t ri_orow[kRows];
 
   PassIter it{segp, B_c, npairs};
@@ -282,8 +283,8 @@ __global__ __launch_bounds__(kBT, 1) void bwd_main_kernel(
   Chunk cur = first_chunk<EC>(it, passes);
   if (!cur.ok) return;
   u32x4 wq[4], wdo[4];   // this thread's staging chunks of the next rows
-  int p_i = -1;          // the row constants of row tid (< kRows)
-  float p_lse2 = 0.f, p_dlt = 0.f;
+  int p_i = -1;          // the row constants of row tid (< kRows); the loaded
+  float p_l = 0.f, p_dl = 0.f;  // lse and D stay raw until the next iteration
   int64_t p_orow = 0;
   const int rc = tid >> 4, crow = tid & (kRows - 1);
 
@@ -306,10 +307,9 @@ __global__ __launch_bounds__(kBT, 1) void bwd_main_kernel(
     const EntryRef x = entry_ref(enc, c.D.seq, kslots, q_begin, q_count);
     const int64_t o = (static_cast<int64_t>(cbat) * N + x.i) * H_q + cr * G + crow % G;
     const bool ok = c.cb + crow / G < c.D.cnt;
-    const float l = lse[o], dl = dlt[o];
+    p_l = lse[o];
+    p_dl = dlt[o];
     p_i = ok ? x.i : -1;
-    p_lse2 = ok ? l * kLog2e : 0.f;
-    p_dlt = ok ? dl : 0.f;
     p_orow = (ok ? x.slot : dummy_slot) * G + crow % G;
   };
   {
@@ -327,8 +327,8 @@ __global__ __launch_bounds__(kBT, 1) void bwd_main_kernel(
     put_rows(wdo, dor_lds, dot_lds);
     if (tid < kRows) {
       ri_i[tid] = p_i;
-      ri_lse2[tid] = p_lse2;
-      ri_dlt[tid] = p_dlt;
+      ri_lse2[tid] = p_i >= 0 ? p_l * kLog2e : 0.f;
+      ri_dlt[tid] = p_i >= 0 ? p_dl : 0.f;
       ri_orow[tid] = p_orow;
     }
     if (D.seq != cur_seq || D.blk != cur_blk) {
@@ -377,14 +377,23 @@ __global__ __launch_bounds__(kBT, 1) void bwd_main_kernel(
       }
       f32x16 p, ds;
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int rho = 32 * rt + acc_row(e, h);
-        const float pe = key_abs <= ri_i[rho]
-                             ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[e], scale_log2, -ri_lse2[rho]))
-                             : 0.f;
-        p[e] = pe;
-        ds[e] = pe * (dp[e] - ri_dlt[rho]);
-        *reinterpret_cast<uint16_t*>(ds_lds + rho * kStr + 2 * key_l) = bf16_bits(ds[e]);
+      for (int a4 = 0; a4 < 4; ++a4) {
+        // elements 4 a4 .. + 3 are rows rb .. rb + 3: one 16-byte read per constant
+        const int rb = 32 * rt + 8 * a4 + 4 * h;
+        const i32x4 ri = *reinterpret_cast<const i32x4*>(ri_i + rb);
+        const f32x4 rl = *reinterpret_cast<const f32x4*>(ri_lse2 + rb);
+        const f32x4 rd = *reinterpret_cast<const f32x4*>(ri_dlt + rb);
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          const int e = 4 * a4 + b;
+          // the exponential runs for every key and a bit mask hides the keys
+          // past the row (no branch per element)
+          const float ev = __builtin_amdgcn_exp2f(__builtin_fmaf(s[e], scale_log2, -rl[b]));
+          const float pe = __uint_as_float(__float_as_uint(ev) & (key_abs <= ri[b] ? 0xFFFFFFFFu : 0u));
+          p[e] = pe;
+          ds[e] = pe * (dp[e] - rd[b]);
+          *reinterpret_cast<uint16_t*>(ds_lds + (rb + b) * kStr + 2 * key_l) = bf16_bits(ds[e]);
+        }
       }
       pb[2 * rt] = pack_step(p, 0);
       pb[2 * rt + 1] = pack_step(p, 1);
@@ -435,6 +444,11 @@ __global__ __launch_bounds__(kBT, 1) void bwd_main_kernel(
     cur = nx;
     nx = next_chunk<EC>(cur, it, passes);
   }
+  // The prefetch registers stay live on the exit path: otherwise the compiler
+  // sinks their loads to the loop's back edge (where the exit path no longer
+  // runs them) and the next iteration waits for them at once.
+  asm volatile("" ::"v"(wq[0]), "v"(wq[1]), "v"(wq[2]), "v"(wq[3]), "v"(wdo[0]), "v"(wdo[1]), "v"(wdo[2]),
+               "v"(wdo[3]), "v"(p_l), "v"(p_dl));
   flush();
 }
 
@@ -459,8 +473,10 @@ __global__ __launch_bounds__(kBT, 1) void bwd_idx_kernel(
   __shared__ __attribute__((aligned(16))) uint8_t kit_lds[kDh * kStr];
   __shared__ __attribute__((aligned(16))) uint8_t g_lds[64 * kStr];
   __shared__ float tch[64 * kBk];  // teacher sums, then KL terms, [index row][key]
-  __shared__ int ri_i[kRows], ei_i[64];
-  __shared__ float ri_lse2[kRows], ei_l2[64];
+  __shared__ __attribute__((aligned(16))) int ri_i[kRows];
+  __shared__ int ei_i[64];
+  __shared__ __attribute__((aligned(16))) float ri_lse2[kRows];
+  __shared__ float ei_l2[64];
   __shared__ int64_t ei_slot[64];
 
   PassIter it{segp, B_c, npairs};
@@ -493,7 +509,7 @@ __global__ __launch_bounds__(kBT, 1) void bwd_idx_kernel(
   constexpr int NCI = DIDX / 8;  // 16-byte chunks per index row
   u32x4 wq[4], wqi[4];
   int p_i = -1, pe_i = -1;
-  float p_lse2 = 0.f, pe_l2 = 0.f;
+  float p_l = 0.f, pe_l = 0.f;  // loaded lse and proxy lse, raw until the next iteration
   int64_t pe_slot = 0;
 
   // entry words: staging rows 4 rc + j of the main rows (query (4 rc + j) / G)
@@ -523,15 +539,13 @@ __global__ __launch_bounds__(kBT, 1) void bwd_idx_kernel(
           q_idx + ((static_cast<int64_t>(cbat) * N + x.i) * H_sel + cr) * DIDX + 8 * min(dg, NCI - 1));
     }
     const EntryRef x = entry_ref(enc, c.D.seq, kslots, q_begin, q_count);
-    const float l = lse[(static_cast<int64_t>(cbat) * N + x.i) * H_q + cr * G + crow % G];
+    p_l = lse[(static_cast<int64_t>(cbat) * N + x.i) * H_q + cr * G + crow % G];
     const bool ok = c.cb + crow / G < c.D.cnt;
     p_i = ok ? x.i : -1;
-    p_lse2 = ok ? l * kLog2e : 0.f;
     const EntryRef y = entry_ref(enci, c.D.seq, kslots, q_begin, q_count);
-    const float l2 = lsei2[y.slot / kslots];
+    pe_l = lsei2[y.slot / kslots];
     const bool oke = crow < EC && c.cb + crow < c.D.cnt;
     pe_i = oke ? y.i : -1;
-    pe_l2 = oke ? l2 : 0.f;
     pe_slot = oke ? y.slot : dummy_slot;
   };
   {
@@ -564,9 +578,9 @@ __global__ __launch_bounds__(kBT, 1) void bwd_idx_kernel(
     }
     if (tid < kRows) {
       ri_i[tid] = p_i;
-      ri_lse2[tid] = p_lse2;
+      ri_lse2[tid] = p_i >= 0 ? p_l * kLog2e : 0.f;
       ei_i[tid] = pe_i;
-      ei_l2[tid] = pe_l2;
+      ei_l2[tid] = pe_i >= 0 ? pe_l : 0.f;
       ei_slot[tid] = pe_slot;
     }
     for (int x = tid; x < EC * kBk; x += kBT) tch[x] = 0.f;
@@ -611,12 +625,13 @@ __global__ __launch_bounds__(kBT, 1) void bwd_idx_kernel(
 #pragma unroll
       for (int e0 = 0; e0 < 16; e0 += RUN) {
         float acc = 0.f;
+        const int rb = 32 * rt + acc_row(e0 & ~3, h);  // rows of elements (e0 & ~3) .. + 3
+        const i32x4 ri = *reinterpret_cast<const i32x4*>(ri_i + rb);
+        const f32x4 rl = *reinterpret_cast<const f32x4*>(ri_lse2 + rb);
 #pragma unroll
         for (int e = e0; e < e0 + RUN; ++e) {
-          const int rho = 32 * rt + acc_row(e, h);
-          acc += key_abs <= ri_i[rho]
-                     ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[e], scale_log2, -ri_lse2[rho]))
-                     : 0.f;
+          const float ev = __builtin_amdgcn_exp2f(__builtin_fmaf(s[e], scale_log2, -rl[e & 3]));
+          acc += __uint_as_float(__float_as_uint(ev) & (key_abs <= ri[e & 3] ? 0xFFFFFFFFu : 0u));
         }
         const int row = (32 * rt + acc_row(e0, h)) / G;
         atomicAdd(&tch[row * kBk + key_l], acc * kInvG);
@@ -665,8 +680,13 @@ __global__ __launch_bounds__(kBT, 1) void bwd_idx_kernel(
 
     // ---- dq_idx^T = k_idx^T g^T over the block's keys (padding rows write
     // the spare row), and the per-row KL sums (a wave per row)
+    // (compile-time trip counts, so the compiler can count the stores its
+    // waits must leave in flight; EC is a multiple of the wave count)
+    constexpr int NXT = (TT * ZT + kBW - 1) / kBW;
 #pragma unroll
-    for (int x = wave; x < TT * ZT; x += kBW) {
+    for (int j = 0; j < NXT; ++j) {
+      const int x = wave + kBW * j;
+      if ((TT * ZT) % kBW != 0 && x >= TT * ZT) break;
       const int tt = x % TT, zt = x / TT;
       f32x16 a = {};
 #pragma unroll
@@ -679,8 +699,10 @@ __global__ __launch_bounds__(kBT, 1) void bwd_idx_kernel(
       for (int e4 = 0; e4 < 4; ++e4)
         *reinterpret_cast<f32x4*>(dst + 8 * e4) = f32x4{a[4 * e4], a[4 * e4 + 1], a[4 * e4 + 2], a[4 * e4 + 3]};
     }
+    static_assert(EC % kBW == 0, "index rows per chunk: a multiple of the wave count");
 #pragma unroll
-    for (int row = wave; row < EC; row += kBW) {
+    for (int rr = 0; rr < EC / kBW; ++rr) {
+      const int row = wave + kBW * rr;
       float sum = tch[row * kBk + lane] + tch[row * kBk + 64 + lane];
 #pragma unroll
       for (int m = 32; m >= 1; m >>= 1) sum += __shfl_xor(sum, m);
@@ -691,6 +713,8 @@ __global__ __launch_bounds__(kBT, 1) void bwd_idx_kernel(
     cur = nx;
     nx = next_chunk<EC>(cur, it, passes);
   }
+  asm volatile("" ::"v"(wq[0]), "v"(wq[1]), "v"(wq[2]), "v"(wq[3]), "v"(wqi[0]), "v"(wqi[1]), "v"(wqi[2]),
+               "v"(wqi[3]), "v"(p_l), "v"(pe_l));  // (see the main branch)
   flush();
 }
 
