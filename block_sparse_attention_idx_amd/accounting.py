@@ -100,13 +100,14 @@ def backward_flops(block_idx: np.ndarray, q_begin: int, N: int, B_k: int, G: int
                    d_idx: int, index: bool = True) -> tuple:
     """FLOPs of the backward pass as its kernels execute it, per visible
     (query, selection group, key): the main branch recomputes S and forms dP,
-    dV, dK and dQ, 10 d_h per head (2.5x the forward's 4 d_h); the index branch
-    recomputes the G heads' S for the teacher distribution (2 d_h G), the proxy
-    scores twice (once in the proxy log-sum-exp pass, once beside the gradient)
-    and forms dq_idx and dk_idx (8 d_idx in all).  Returns (main, index)."""
+    dV, dK and dQ, 10 d_h per head (2.5x the forward's 4 d_h), and hands the
+    teacher distribution (the mean of its heads' probabilities) to the index
+    branch; the index branch computes the proxy scores twice (once in the proxy
+    log-sum-exp pass, once beside the gradient) and forms dq_idx and dk_idx
+    (8 d_idx in all).  Returns (main, index)."""
     vis = float(visible_keys(block_idx, q_begin, N, B_k).sum())
     main = 10.0 * d_h * G * vis
-    idx = (2.0 * d_h * G + 8.0 * d_idx) * vis if index else 0.0
+    idx = 8.0 * d_idx * vis if index else 0.0
     return main, idx
 
 

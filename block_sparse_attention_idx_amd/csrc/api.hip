@@ -373,7 +373,7 @@ namespace {
 struct BackwardLayout {
   int64_t qc;  // rows per chunk
   size_t off_dk, off_dv, off_dki, off_dlt, off_bi, off_off, off_ent, off_sched, off_dqp, off_lsp, off_lsi,
-      off_dqip, off_klp, total;
+      off_dqip, off_klp, off_tch, total;
 };
 
 BackwardLayout backward_layout(const msa_dims* d, const msa_opts* o) {
@@ -409,6 +409,7 @@ BackwardLayout backward_layout(const msa_dims* d, const msa_opts* o) {
   L.off_lsi = take(static_cast<size_t>(seqs) * L.qc * 4);
   L.off_dqip = take((slots + 1) * d->d_idx * 4);
   L.off_klp = take((slots + 1) * 4);
+  L.off_tch = take((slots + 1) * static_cast<size_t>(d->B_k) * 4);
   L.total = off;
   return L;
 }
@@ -487,6 +488,7 @@ int msa_backward(const msa_dims* dims, const msa_opts* opts, float kl_weight, co
   a.lsei2 = reinterpret_cast<float*>(ws + L.off_lsi);
   a.dqi_part = reinterpret_cast<float*>(ws + L.off_dqip);
   a.kl_part = reinterpret_cast<float*>(ws + L.off_klp);
+  a.tch = reinterpret_cast<float*>(ws + L.off_tch);
   a.dk_acc = dk_acc;
   a.dv_acc = dv_acc;
   a.dki_acc = dki_acc;

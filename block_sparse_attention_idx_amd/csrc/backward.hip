@@ -228,15 +228,20 @@ __device__ __forceinline__ void store_keys_t(const u32x4 (&f)[KS], uint8_t* kt, 
 }
 
 // ---------------------------------------------------------------- main branch
-template <int G>
+// IDX: the index branch runs, so the teacher T of every entry (the mean over
+// the G heads of the probabilities of each key of the block) is written to
+// `tch_out` ([slot][key] fp32) for the index-branch kernel.
+template <int G, bool IDX>
 __global__ __launch_bounds__(kBT, 1) void bwd_main_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ dlt,
     int64_t N, int H_sel, int kv_shift, int kslots, float scale, float scale_log2,
     const int32_t* __restrict__ entries, const int32_t* __restrict__ segp,
     const PassDesc* __restrict__ passes, int B_c, int npairs, int q_begin, int q_count, int64_t dummy_slot,
-    uint16_t* __restrict__ dq_part, float* __restrict__ dk_acc, float* __restrict__ dv_acc) {
+    uint16_t* __restrict__ dq_part, float* __restrict__ dk_acc, float* __restrict__ dv_acc,
+    float* __restrict__ tch_out) {
   constexpr int EC = kRows / G;  // queries per chunk
+  constexpr float kInvG = 1.f / G;
   __shared__ __attribute__((aligned(16))) uint8_t qr_lds[kRows * kStr];
   __shared__ __attribute__((aligned(16))) uint8_t dor_lds[kRows * kStr];
   __shared__ __attribute__((aligned(16))) uint8_t qt_lds[kDh * kTStr];
@@ -246,6 +251,7 @@ __global__ __launch_bounds__(kBT, 1) void bwd_main_kernel(
   __shared__ __attribute__((aligned(16))) int ri_i[kRows];
   __shared__ __attribute__((aligned(16))) float ri_lse2[kRows], ri_dlt[kRows];
   __shared__ int64_t ri_orow[kRows];
+  __shared__ __attribute__((aligned(16))) float tch[IDX ? EC * kBk : 4];  // teacher sums [query][key]
 
   PassIter it{segp, B_c, npairs};
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, n = lane & 31, h = lane >> 5;
@@ -331,6 +337,10 @@ __global__ __launch_bounds__(kBT, 1) void bwd_main_kernel(
       ri_dlt[tid] = p_i >= 0 ? p_dl : 0.f;
       ri_orow[tid] = p_orow;
     }
+    if constexpr (IDX) {
+#pragma unroll
+      for (int j = 0; j < EC * kBk / kBT; ++j) tch[tid + kBT * j] = 0.f;
+    }
     if (D.seq != cur_seq || D.blk != cur_blk) {
       flush();
       cur_seq = D.seq;
@@ -399,6 +409,18 @@ __global__ __launch_bounds__(kBT, 1) void bwd_main_kernel(
       pb[2 * rt + 1] = pack_step(p, 1);
       db[2 * rt] = pack_step(ds, 0);
       db[2 * rt + 1] = pack_step(ds, 1);
+      if constexpr (IDX) {
+        // teacher: the lane's run of RUN consecutive elements is one query's
+        // heads; the G heads of a query meet in LDS
+        constexpr int RUN = G < 4 ? G : 4;
+#pragma unroll
+        for (int e0 = 0; e0 < 16; e0 += RUN) {
+          float acc = 0.f;
+#pragma unroll
+          for (int e = e0; e < e0 + RUN; ++e) acc += p[e];
+          atomicAdd(&tch[((32 * rt + acc_row(e0, h)) / G) * kBk + key_l], acc * kInvG);
+        }
+      }
     }
 
     // ---- the next chunk's rows go out while this chunk finishes
@@ -427,6 +449,19 @@ __global__ __launch_bounds__(kBT, 1) void bwd_main_kernel(
         for (int j = 0; j < 2; ++j)
           qa[j] = mfma32x32x16(lds_frag(kt_lds + (32 * (dt0 + j) + n) * kStr + 32 * kk + 16 * h), b, qa[j]);
       }
+      if constexpr (IDX) {
+        // the chunk's teacher rows, one per entry (padding rows: the spare
+        // row; threads past the rows repeat a store, so every thread stores)
+        constexpr int NF = EC * kBk / 4;
+#pragma unroll
+        for (int j = 0; j < (NF + kBT - 1) / kBT; ++j) {
+          const int f = (tid + kBT * j) % NF;
+          const int row = f / (kBk / 4), c4 = f % (kBk / 4);
+          const int64_t slot = ri_orow[row * G] / G;
+          *reinterpret_cast<f32x4*>(tch_out + slot * kBk + 4 * c4) =
+              *reinterpret_cast<const f32x4*>(tch + row * kBk + 4 * c4);
+        }
+      }
       const int rho = 32 * rt + n;
       uint16_t* dst = dq_part + ri_orow[rho] * kDh;
 #pragma unroll
@@ -453,39 +488,45 @@ __global__ __launch_bounds__(kBT, 1) void bwd_main_kernel(
 }
 
 // ---------------------------------------------------------------- index branch
+// The teacher T (for each entry (query, slot) and key of the block, the mean
+// over the group's heads of the main probabilities; zero for keys past the
+// query) comes from the main-branch kernel as one fp32 row per entry, so this
+// kernel reads only the proxy operands: z = q_idx . k_idx (scaled),
+// p_px = exp(z - LSE_px), the KL terms T ln(T / p_px) and g = w (p_px - T),
+// then dk_idx^T += q_idx^T g (per-block accumulators, as dK) and
+// dq_idx^T = k_idx^T g^T per entry.  Chunks are EI index rows (entries) of
+// one pass, prefetched one chunk ahead like the main branch.
 template <int G, int DIDX>
 __global__ __launch_bounds__(kBT, 1) void bwd_idx_kernel(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ q_idx,
-    const uint16_t* __restrict__ k_idx, const float* __restrict__ lse, const float* __restrict__ lsei2,
-    int64_t N, int H_sel, int kv_shift, int kslots, float scale_log2, float idx_scale_log2, float gscale,
+    const uint16_t* __restrict__ q_idx, const uint16_t* __restrict__ k_idx, const float* __restrict__ lsei2,
+    const float* __restrict__ tch_in, int64_t N, int H_sel, int kslots, float idx_scale_log2, float gscale,
     const int32_t* __restrict__ entries, const int32_t* __restrict__ segp,
     const PassDesc* __restrict__ passes, int B_c, int npairs, int q_begin, int q_count, int64_t dummy_slot,
     float* __restrict__ dqi_part, float* __restrict__ kl_part, float* __restrict__ dki_acc) {
-  constexpr int EC = kRows / G;        // queries (index rows) per chunk
-  constexpr int ZT = (EC + 31) / 32;   // 32-row tiles of index rows
-  constexpr int KE = (EC + 15) / 16;   // 16-row steps of index rows
-  constexpr int KSI = DIDX / 16;       // reduction steps of the index dot product
-  constexpr int TT = DIDX / 32;        // 32-dim tiles of dq_idx / dk_idx
-  constexpr float kInvG = 1.f / G;
-  __shared__ __attribute__((aligned(16))) uint8_t qr_lds[kRows * kStr];
+  constexpr int EPP = 256 / G;                 // entries per pass
+  constexpr int EI = EPP < 64 ? EPP : 64;      // index rows per chunk
+  constexpr int ZT = (EI + 31) / 32;           // 32-row tiles of index rows
+  constexpr int KE = (EI + 15) / 16;           // 16-row steps of index rows
+  constexpr int KSI = DIDX / 16;               // reduction steps of the index dot product
+  constexpr int TT = DIDX / 32;                // 32-dim tiles of dq_idx / dk_idx
+  constexpr int NCI = DIDX / 8;                // 16-byte chunks per index row
+  constexpr int NT4 = EI * (kBk / 4) / kBT;    // 16-byte pieces of T per thread
+  static_assert(EI % kBW == 0 && NT4 >= 1, "chunk shape");
   __shared__ __attribute__((aligned(16))) uint8_t qi_lds[64 * kStr];
   __shared__ __attribute__((aligned(16))) uint8_t qit_lds[kDh * kTStr];
   __shared__ __attribute__((aligned(16))) uint8_t kit_lds[kDh * kStr];
   __shared__ __attribute__((aligned(16))) uint8_t g_lds[64 * kStr];
-  __shared__ float tch[64 * kBk];  // teacher sums, then KL terms, [index row][key]
-  __shared__ __attribute__((aligned(16))) int ri_i[kRows];
+  __shared__ __attribute__((aligned(16))) float tt[EI * kBk];  // teacher, then KL terms, [index row][key]
   __shared__ int ei_i[64];
-  __shared__ __attribute__((aligned(16))) float ri_lse2[kRows];
   __shared__ float ei_l2[64];
   __shared__ int64_t ei_slot[64];
 
   PassIter it{segp, B_c, npairs};
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, n = lane & 31, h = lane >> 5;
-  const int H_q = H_sel * G, H_kv = H_sel >> kv_shift;
   const int key_l = 32 * wave + n;
 
   int cur_seq = -1, cur_blk = 0, cur_nvalid = 0;
-  u32x4 kf[8], kif[KSI];
+  u32x4 kif[KSI];
   f32x16 dkit[TT];
 
   auto flush = [&]() {
@@ -493,78 +534,65 @@ __global__ __launch_bounds__(kBT, 1) void bwd_idx_kernel(
     const int bat = cur_seq / H_sel;
     float* dst = dki_acc + (static_cast<int64_t>(bat) * N + static_cast<int64_t>(cur_blk) * kBk + key_l) * DIDX;
 #pragma unroll
-    for (int tt = 0; tt < TT; ++tt)
+    for (int tt2 = 0; tt2 < TT; ++tt2)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) unsafeAtomicAdd(dst + 32 * tt + acc_row(e, h), dkit[tt][e]);
+      for (int e = 0; e < 16; ++e) unsafeAtomicAdd(dst + 32 * tt2 + acc_row(e, h), dkit[tt2][e]);
   };
 
-  // Software pipeline over the workgroup's chunks, as in the main branch:
-  // chunk c + 1's entry words load before the teacher's S, its Q rows, index
-  // rows and row constants after it; every global load and store of the loop
-  // is unconditional (padding rows read the pass's last entry and store to a
-  // spare row).
-  Chunk cur = first_chunk<EC>(it, passes);
+  Chunk cur = first_chunk<EI>(it, passes);
   if (!cur.ok) return;
-  const int rc = tid >> 4, dg = tid & 15, crow = tid & (kRows - 1);
-  constexpr int NCI = DIDX / 8;  // 16-byte chunks per index row
-  u32x4 wq[4], wqi[4];
-  int p_i = -1, pe_i = -1;
-  float p_l = 0.f, pe_l = 0.f;  // loaded lse and proxy lse, raw until the next iteration
+  const int rc = tid >> 4, dg = tid & 15, crow = tid & 63;
+  u32x4 wqi[4];       // this thread's 16-byte pieces of index rows 4 rc .. + 3
+  f32x4 wt[NT4];      // and of T rows tid / 32 + 8 j (pieces tid % 32)
+  int pe_i = -1;      // row constants of index row crow; the loaded proxy LSE
+  float pe_l = 0.f;   // stays raw until the next iteration
   int64_t pe_slot = 0;
 
-  // entry words: staging rows 4 rc + j of the main rows (query (4 rc + j) / G)
-  // and of the index rows (query 4 rc + j), then the constant rows
-  auto chunk_entries = [&](const Chunk& c, uint32_t (&en)[4], uint32_t (&eni)[4], uint32_t& enc,
-                           uint32_t& enci) {
+  auto chunk_entries = [&](const Chunk& c, uint32_t (&eni)[4], uint32_t (&ent)[NT4], uint32_t& enci) {
     const int last = c.D.cnt - 1;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      en[j] = static_cast<uint32_t>(entries[c.D.start + min(c.cb + (4 * rc + j) / G, last)]);
-      eni[j] = static_cast<uint32_t>(entries[c.D.start + min(c.cb + min(4 * rc + j, EC - 1), last)]);
-    }
-    enc = static_cast<uint32_t>(entries[c.D.start + min(c.cb + crow / G, last)]);
-    enci = static_cast<uint32_t>(entries[c.D.start + min(c.cb + min(crow, EC - 1), last)]);
+    for (int j = 0; j < 4; ++j)
+      eni[j] = static_cast<uint32_t>(entries[c.D.start + min(c.cb + min(4 * rc + j, EI - 1), last)]);
+#pragma unroll
+    for (int j = 0; j < NT4; ++j)
+      ent[j] = static_cast<uint32_t>(entries[c.D.start + min(c.cb + (tid >> 5) + 8 * j, last)]);
+    enci = static_cast<uint32_t>(entries[c.D.start + min(c.cb + min(crow, EI - 1), last)]);
   };
-  auto chunk_rows = [&](const Chunk& c, const uint32_t (&en)[4], const uint32_t (&eni)[4], uint32_t enc,
-                        uint32_t enci) {
+  auto chunk_rows = [&](const Chunk& c, const uint32_t (&eni)[4], const uint32_t (&ent)[NT4], uint32_t enci) {
     const int cbat = c.D.seq / H_sel, cr = c.D.seq - cbat * H_sel;
-    load_rows([&](int rho) {
-      const EntryRef x = entry_ref(en[rho & 3], c.D.seq, kslots, q_begin, q_count);
-      return q + ((static_cast<int64_t>(cbat) * N + x.i) * H_q + cr * G + rho % G) * kDh;
-    }, wq);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const EntryRef x = entry_ref(eni[j], c.D.seq, kslots, q_begin, q_count);
       wqi[j] = *reinterpret_cast<const u32x4*>(
           q_idx + ((static_cast<int64_t>(cbat) * N + x.i) * H_sel + cr) * DIDX + 8 * min(dg, NCI - 1));
     }
-    const EntryRef x = entry_ref(enc, c.D.seq, kslots, q_begin, q_count);
-    p_l = lse[(static_cast<int64_t>(cbat) * N + x.i) * H_q + cr * G + crow % G];
-    const bool ok = c.cb + crow / G < c.D.cnt;
-    p_i = ok ? x.i : -1;
+#pragma unroll
+    for (int j = 0; j < NT4; ++j) {
+      const EntryRef x = entry_ref(ent[j], c.D.seq, kslots, q_begin, q_count);
+      wt[j] = *reinterpret_cast<const f32x4*>(tch_in + x.slot * kBk + 4 * (tid & 31));
+    }
     const EntryRef y = entry_ref(enci, c.D.seq, kslots, q_begin, q_count);
     pe_l = lsei2[y.slot / kslots];
-    const bool oke = crow < EC && c.cb + crow < c.D.cnt;
+    const bool oke = crow < EI && c.cb + crow < c.D.cnt;
     pe_i = oke ? y.i : -1;
     pe_slot = oke ? y.slot : dummy_slot;
   };
   {
-    uint32_t en[4], eni[4], enc, enci;
-    chunk_entries(cur, en, eni, enc, enci);
-    chunk_rows(cur, en, eni, enc, enci);
+    uint32_t eni[4], ent[NT4], enci;
+    chunk_entries(cur, eni, ent, enci);
+    chunk_rows(cur, eni, ent, enci);
   }
-  Chunk nx = next_chunk<EC>(cur, it, passes);
+  Chunk nx = next_chunk<EI>(cur, it, passes);
 
   while (true) {
     const PassDesc D = cur.D;
-    const int bat = D.seq / H_sel, r = D.seq - bat * H_sel;
-    // ---- this chunk's Q rows, index rows (row-major and transposed; rows
-    // past the chunk are zeros) and row constants into LDS
-    put_rows(wq, qr_lds, nullptr);
+    const int bat = D.seq / H_sel;
+    // ---- this chunk's index rows (row-major and transposed; rows past the
+    // chunk are zeros), T rows (zeros for padding rows) and row constants
     if (dg < NCI) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const u32x4 w = 4 * rc + j < EC ? wqi[j] : u32x4{0u, 0u, 0u, 0u};
+        const u32x4 w = 4 * rc + j < EI ? wqi[j] : u32x4{0u, 0u, 0u, 0u};
         wqi[j] = w;
         *reinterpret_cast<u32x4*>(qi_lds + (4 * rc + j) * kStr + 16 * dg) = w;
       }
@@ -576,14 +604,17 @@ __global__ __launch_bounds__(kBT, 1) void bwd_idx_kernel(
         *reinterpret_cast<u32x2*>(qit_lds + (8 * dg + dd) * kTStr + 2 * col) = v;
       }
     }
-    if (tid < kRows) {
-      ri_i[tid] = p_i;
-      ri_lse2[tid] = p_i >= 0 ? p_l * kLog2e : 0.f;
+#pragma unroll
+    for (int j = 0; j < NT4; ++j) {
+      const int row = (tid >> 5) + 8 * j;
+      *reinterpret_cast<f32x4*>(tt + row * kBk + 4 * (tid & 31)) =
+          cur.cb + row < D.cnt ? wt[j] : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    if (tid < 64) {
       ei_i[tid] = pe_i;
       ei_l2[tid] = pe_i >= 0 ? pe_l : 0.f;
       ei_slot[tid] = pe_slot;
     }
-    for (int x = tid; x < EC * kBk; x += kBT) tch[x] = 0.f;
     if (D.seq != cur_seq || D.blk != cur_blk) {
       flush();
       cur_seq = D.seq;
@@ -592,54 +623,21 @@ __global__ __launch_bounds__(kBT, 1) void bwd_idx_kernel(
       cur_nvalid = static_cast<int>(min<int64_t>(kBk, N - key0));
       const int kr = min(key_l, cur_nvalid - 1);
       const bool ok = key_l < cur_nvalid;
-      const uint16_t* kb = k + ((static_cast<int64_t>(bat) * N + key0 + kr) * H_kv + (r >> kv_shift)) * kDh;
       const uint16_t* kib = k_idx + (static_cast<int64_t>(bat) * N + key0 + kr) * DIDX;
-#pragma unroll
-      for (int ks = 0; ks < 8; ++ks) {
-        const u32x4 a = *reinterpret_cast<const u32x4*>(kb + 16 * ks + 8 * h);
-        kf[ks] = ok ? a : u32x4{0u, 0u, 0u, 0u};
-      }
 #pragma unroll
       for (int ks = 0; ks < KSI; ++ks) {
         const u32x4 a = *reinterpret_cast<const u32x4*>(kib + 16 * ks + 8 * h);
         kif[ks] = ok ? a : u32x4{0u, 0u, 0u, 0u};
       }
 #pragma unroll
-      for (int tt = 0; tt < TT; ++tt) dkit[tt] = f32x16{};
+      for (int t2 = 0; t2 < TT; ++t2) dkit[t2] = f32x16{};
       store_keys_t<KSI>(kif, kit_lds, wave, n, h);
     }
     const int key_abs = D.blk * kBk + key_l;
     const Chunk& src = nx.ok ? nx : cur;
-    uint32_t en[4], eni[4], enc, enci;
-    chunk_entries(src, en, eni, enc, enci);
+    uint32_t eni[4], ent[NT4], enci;
+    chunk_entries(src, eni, ent, enci);
     __syncthreads();
-
-    // ---- teacher: mean over the G heads of the main probabilities
-#pragma unroll
-    for (int rt = 0; rt < 2; ++rt) {
-      f32x16 s = {};
-#pragma unroll
-      for (int ks = 0; ks < 8; ++ks)
-        s = mfma32x32x16(lds_frag(qr_lds + (32 * rt + n) * kStr + 32 * ks + 16 * h), as_bf16x8(kf[ks]), s);
-      constexpr int RUN = G < 4 ? G : 4;  // consecutive elements of one query
-#pragma unroll
-      for (int e0 = 0; e0 < 16; e0 += RUN) {
-        float acc = 0.f;
-        const int rb = 32 * rt + acc_row(e0 & ~3, h);  // rows of elements (e0 & ~3) .. + 3
-        const i32x4 ri = *reinterpret_cast<const i32x4*>(ri_i + rb);
-        const f32x4 rl = *reinterpret_cast<const f32x4*>(ri_lse2 + rb);
-#pragma unroll
-        for (int e = e0; e < e0 + RUN; ++e) {
-          const float ev = __builtin_amdgcn_exp2f(__builtin_fmaf(s[e], scale_log2, -rl[e & 3]));
-          acc += __uint_as_float(__float_as_uint(ev) & (key_abs <= ri[e & 3] ? 0xFFFFFFFFu : 0u));
-        }
-        const int row = (32 * rt + acc_row(e0, h)) / G;
-        atomicAdd(&tch[row * kBk + key_l], acc * kInvG);
-      }
-    }
-
-    // ---- the next chunk's rows go out while this chunk finishes
-    chunk_rows(src, en, eni, enc, enci);
 
     // ---- proxy probabilities, KL terms and the gradient g on z
     bf16x8 gb[2 * ZT];
@@ -654,11 +652,11 @@ __global__ __launch_bounds__(kBT, 1) void bwd_idx_kernel(
       for (int e = 0; e < 16; ++e) {
         const int row = 32 * zt + acc_row(e, h);
         float ge = 0.f;
-        if (row < EC) {
+        if (row < EI) {
           const bool vis = key_abs <= ei_i[row];
           const float zl2 = __builtin_fmaf(z[e], idx_scale_log2, -ei_l2[row]);  // log2 p_px
           const float ppx = vis ? __builtin_amdgcn_exp2f(zl2) : 0.f;
-          float* tp = &tch[row * kBk + key_l];
+          float* tp = tt + row * kBk + key_l;
           const float T = *tp;
           *tp = (vis && T > 0.f) ? T * (__builtin_amdgcn_logf(T) - zl2) * kLn2 : 0.f;
           ge = gscale * (ppx - T);
@@ -670,40 +668,42 @@ __global__ __launch_bounds__(kBT, 1) void bwd_idx_kernel(
       gb[2 * zt + 1] = pack_step(g, 1);
     }
 
+    // ---- the next chunk's rows go out while this chunk finishes
+    chunk_rows(src, eni, ent, enci);
+
     // ---- dk_idx^T += q_idx^T g (reduction over the chunk's index rows)
 #pragma unroll
-    for (int tt = 0; tt < TT; ++tt)
+    for (int t2 = 0; t2 < TT; ++t2)
 #pragma unroll
       for (int st = 0; st < KE; ++st)
-        dkit[tt] = mfma32x32x16(lds_frag(qit_lds + (32 * tt + n) * kTStr + 32 * st + 16 * h), gb[st], dkit[tt]);
+        dkit[t2] = mfma32x32x16(lds_frag(qit_lds + (32 * t2 + n) * kTStr + 32 * st + 16 * h), gb[st], dkit[t2]);
     __syncthreads();
 
-    // ---- dq_idx^T = k_idx^T g^T over the block's keys (padding rows write
-    // the spare row), and the per-row KL sums (a wave per row)
-    // (compile-time trip counts, so the compiler can count the stores its
-    // waits must leave in flight; EC is a multiple of the wave count)
+    // ---- dq_idx^T = k_idx^T g^T over the block's keys (rows past the chunk
+    // write the spare row), and the per-row KL sums (a wave per row); the
+    // trip counts are compile-time, so the compiler can count the stores its
+    // waits leave in flight
     constexpr int NXT = (TT * ZT + kBW - 1) / kBW;
 #pragma unroll
     for (int j = 0; j < NXT; ++j) {
       const int x = wave + kBW * j;
       if ((TT * ZT) % kBW != 0 && x >= TT * ZT) break;
-      const int tt = x % TT, zt = x / TT;
+      const int t2 = x % TT, zt = x / TT;
       f32x16 a = {};
 #pragma unroll
       for (int kk = 0; kk < 8; ++kk)
-        a = mfma32x32x16(lds_frag(kit_lds + (32 * tt + n) * kStr + 32 * kk + 16 * h),
+        a = mfma32x32x16(lds_frag(kit_lds + (32 * t2 + n) * kStr + 32 * kk + 16 * h),
                          lds_frag(g_lds + (32 * zt + n) * kStr + 32 * kk + 16 * h), a);
       const int row = 32 * zt + n;
-      float* dst = dqi_part + (row < EC ? ei_slot[row] : dummy_slot) * DIDX + 32 * tt + 4 * h;
+      float* dst = dqi_part + (row < EI ? ei_slot[row] : dummy_slot) * DIDX + 32 * t2 + 4 * h;
 #pragma unroll
       for (int e4 = 0; e4 < 4; ++e4)
         *reinterpret_cast<f32x4*>(dst + 8 * e4) = f32x4{a[4 * e4], a[4 * e4 + 1], a[4 * e4 + 2], a[4 * e4 + 3]};
     }
-    static_assert(EC % kBW == 0, "index rows per chunk: a multiple of the wave count");
 #pragma unroll
-    for (int rr = 0; rr < EC / kBW; ++rr) {
+    for (int rr = 0; rr < EI / kBW; ++rr) {
       const int row = wave + kBW * rr;
-      float sum = tch[row * kBk + lane] + tch[row * kBk + 64 + lane];
+      float sum = tt[row * kBk + lane] + tt[row * kBk + 64 + lane];
 #pragma unroll
       for (int m = 32; m >= 1; m >>= 1) sum += __shfl_xor(sum, m);
       kl_part[ei_slot[row]] = sum;  // every lane: the same value to the same word
@@ -711,10 +711,12 @@ __global__ __launch_bounds__(kBT, 1) void bwd_idx_kernel(
     __syncthreads();
     if (!nx.ok) break;
     cur = nx;
-    nx = next_chunk<EC>(cur, it, passes);
+    nx = next_chunk<EI>(cur, it, passes);
   }
-  asm volatile("" ::"v"(wq[0]), "v"(wq[1]), "v"(wq[2]), "v"(wq[3]), "v"(wqi[0]), "v"(wqi[1]), "v"(wqi[2]),
-               "v"(wqi[3]), "v"(p_l), "v"(pe_l));  // (see the main branch)
+  // (the prefetch registers stay live on the exit path; see the main branch)
+  asm volatile("" ::"v"(wqi[0]), "v"(wqi[1]), "v"(wqi[2]), "v"(wqi[3]), "v"(pe_l));
+#pragma unroll
+  for (int j = 0; j < NT4; ++j) asm volatile("" ::"v"(wt[j]));
   flush();
 }
 
@@ -970,8 +972,8 @@ hipError_t launch_backward_chunk(const BwdArgs& a, hipStream_t stream) {
     if (e != hipSuccess) return e;
   }
 
+  const float isl2 = a.idx_scale * kLog2e;
   if (a.index) {
-    const float isl2 = a.idx_scale * kLog2e;
     const unsigned lgrid = clamp_grid(static_cast<int64_t>(cus_of_device()) * kLseWgPerCu);
     auto lk = a.d_idx == 64 ? proxy_lse_kernel<64> : proxy_lse_kernel<128>;
     hipLaunchKernelGGL(lk, dim3(lgrid), dim3(64), 0, stream, a.q_idx, a.k_idx, a.N, a.H_sel, a.k, isl2,
@@ -984,13 +986,44 @@ hipError_t launch_backward_chunk(const BwdArgs& a, hipStream_t stream) {
                        a.lsei_part, a.k, a.q_begin, a.q_count, rows, a.lsei2);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
+  }
+
+  {
+    const unsigned grid = clamp_grid(cus_of_device());
+#define MSA_BWD_MAIN(GG)                                                                                        \
+  case GG:                                                                                                      \
+    if (a.index)                                                                                                \
+      hipLaunchKernelGGL((bwd_main_kernel<GG, true>), dim3(grid), dim3(kBT), 0, stream, a.q, a.k_ptr, a.v,     \
+                         a.dout, a.lse, a.dlt, a.N, a.H_sel, a.kv_shift, a.k, a.scale, scale_log2, a.entries,   \
+                         segp, passes, static_cast<int>(s.B_c), npairs, static_cast<int>(a.q_begin),            \
+                         static_cast<int>(a.q_count), dummy_slot, a.dq_part, a.dk_acc, a.dv_acc, a.tch);        \
+    else                                                                                                        \
+      hipLaunchKernelGGL((bwd_main_kernel<GG, false>), dim3(grid), dim3(kBT), 0, stream, a.q, a.k_ptr, a.v,    \
+                         a.dout, a.lse, a.dlt, a.N, a.H_sel, a.kv_shift, a.k, a.scale, scale_log2, a.entries,   \
+                         segp, passes, static_cast<int>(s.B_c), npairs, static_cast<int>(a.q_begin),            \
+                         static_cast<int>(a.q_count), dummy_slot, a.dq_part, a.dk_acc, a.dv_acc, a.tch);        \
+    break;
+    switch (a.G) {
+      MSA_BWD_MAIN(1)
+      MSA_BWD_MAIN(2)
+      MSA_BWD_MAIN(4)
+      MSA_BWD_MAIN(8)
+      MSA_BWD_MAIN(16)
+      default:
+        return hipErrorInvalidValue;
+    }
+#undef MSA_BWD_MAIN
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+
+  if (a.index) {
     const unsigned grid = clamp_grid(cus_of_device());
 #define MSA_BWD_IDX(GG, DD)                                                                                    \
-  hipLaunchKernelGGL((bwd_idx_kernel<GG, DD>), dim3(grid), dim3(kBT), 0, stream, a.q, a.k_ptr, a.q_idx, a.k_idx, \
-                     a.lse, a.lsei2, a.N, a.H_sel, a.kv_shift, a.k, scale_log2, isl2,                           \
-                     a.kl_weight * a.idx_scale, a.entries, segp, passes, static_cast<int>(s.B_c), npairs,       \
-                     static_cast<int>(a.q_begin), static_cast<int>(a.q_count), dummy_slot, a.dqi_part, a.kl_part, \
-                     a.dki_acc)
+  hipLaunchKernelGGL((bwd_idx_kernel<GG, DD>), dim3(grid), dim3(kBT), 0, stream, a.q_idx, a.k_idx, a.lsei2,     \
+                     a.tch, a.N, a.H_sel, a.k, isl2, a.kl_weight * a.idx_scale, a.entries, segp, passes,        \
+                     static_cast<int>(s.B_c), npairs, static_cast<int>(a.q_begin), static_cast<int>(a.q_count), \
+                     dummy_slot, a.dqi_part, a.kl_part, a.dki_acc)
 #define MSA_BWD_IDX_G(GG)          \
   case GG:                         \
     if (a.d_idx == 64)             \
@@ -1009,30 +1042,7 @@ hipError_t launch_backward_chunk(const BwdArgs& a, hipStream_t stream) {
     }
 #undef MSA_BWD_IDX_G
 #undef MSA_BWD_IDX
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
-
-  {
-    const unsigned grid = clamp_grid(cus_of_device());
-#define MSA_BWD_MAIN(GG)                                                                                        \
-  case GG:                                                                                                      \
-    hipLaunchKernelGGL(bwd_main_kernel<GG>, dim3(grid), dim3(kBT), 0, stream, a.q, a.k_ptr, a.v, a.dout, a.lse,  \
-                       a.dlt, a.N, a.H_sel, a.kv_shift, a.k, a.scale, scale_log2, a.entries, segp, passes,      \
-                       static_cast<int>(s.B_c), npairs, static_cast<int>(a.q_begin), static_cast<int>(a.q_count), \
-                       dummy_slot, a.dq_part, a.dk_acc, a.dv_acc);                                              \
-    break;
-    switch (a.G) {
-      MSA_BWD_MAIN(1)
-      MSA_BWD_MAIN(2)
-      MSA_BWD_MAIN(4)
-      MSA_BWD_MAIN(8)
-      MSA_BWD_MAIN(16)
-      default:
-        return hipErrorInvalidValue;
-    }
-#undef MSA_BWD_MAIN
-    hipError_t e = hipGetLastError();
+    const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
 

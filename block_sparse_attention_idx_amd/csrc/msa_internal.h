@@ -203,6 +203,7 @@ struct BwdArgs {
   float scale, idx_scale, kl_weight;
   bool index;
   float *dlt, *lsei_part, *lsei2, *dqi_part, *kl_part, *dk_acc, *dv_acc, *dki_acc, *kl;
+  float* tch;  // teacher rows per entry [slot][key], written by the main branch for the index branch
   uint16_t *dq_part, *dq, *dq_idx;
 };
 hipError_t launch_backward_chunk(const BwdArgs& a, hipStream_t stream);

@@ -327,7 +327,8 @@ int msa_decode(const msa_dims *dims, const msa_opts *opts, const void *q, const 
  *              per-row KL(P || p_idx), not weighted
  *   workspace  device memory of msa_backward_workspace_size bytes, 256-byte
  *              aligned: fp32 gradient accumulators, the inversion, per-slot
- *              partials (dQ and dq_idx are sums over a row's slots)
+ *              partials (dQ and dq_idx are sums over a row's slots) and the
+ *              teacher rows the main branch hands to the index branch
  * bf16 only and B_k = 128 (MSA_ERR_UNSUPPORTED otherwise); opts->q_chunk
  * splits the query rows into chunks as in msa_forward (dK, dV and dk_idx
  * accumulate over all chunks).  Softmax scale: opts->softmax_scale (<= 0:
