@@ -164,16 +164,20 @@ def main():
     for _ in range(args.warmup):
         msa.msa_forward(*args_f, o=out, block_idx_out=bi, workspace=ws)
     torch.cuda.synchronize()
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # an event between consecutive steps gives the per-step times as well
+    evs_f = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     t0 = time.perf_counter()
-    ev0.record(stream)
-    for _ in range(args.steps):
+    evs_f[0].record(stream)
+    for j in range(args.steps):
         msa.msa_forward(*args_f, o=out, block_idx_out=bi, workspace=ws)
-    ev1.record(stream)
+        evs_f[j + 1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ms_step = ev0.elapsed_time(ev1) / args.steps
-    log(f"msa_forward: {ms_step:.3f} ms/step (host wall {1e3 * wall / args.steps:.3f} ms/step)")
+    ms_step = evs_f[0].elapsed_time(evs_f[-1]) / args.steps
+    step_ms = sorted(evs_f[j].elapsed_time(evs_f[j + 1]) for j in range(args.steps))
+    ms_median, ms_min = float(np.median(step_ms)), step_ms[0]
+    log(f"msa_forward: {ms_step:.3f} ms/step (median {ms_median:.3f}, min {ms_min:.3f}; "
+        f"host wall {1e3 * wall / args.steps:.3f} ms/step)")
 
     # ---- per-kernel timing: the same pass through the four entry points, with
     # HIP events between the calls on the launch stream (single-chunk workloads)
@@ -314,6 +318,22 @@ def main():
                   + bins * 2 * w.B_k * w.d_h * eb)             # K, V once per selected block
     bytes_comb = part + 4 * w.batch * w.H_kv * w.N * w.k + w.batch * w.N * w.H_q * w.d_h * 2
     bytes_inv = 4 * w.batch * w.H_kv * w.N * w.k + 4 * valid_slots
+    # block popularity: non-local selections per (sequence, group, block), the
+    # skew the pre-scheduled chunking absorbs
+    loc = (np.arange(w.N) // w.B_k)[None, :, None]
+    nonlocal_sel = (sel >= 0) & (sel != loc)
+    counts = np.zeros((sel.shape[0], w.B), np.int64)
+    for g in range(sel.shape[0]):
+        counts[g] = np.bincount(sel[g][nonlocal_sel[g]], minlength=w.B)[:w.B]
+    popularity = {"max": int(counts.max()), "mean": float(counts.mean()),
+                  "p99": float(np.percentile(counts, 99)),
+                  "max_over_mean": float(counts.max() / max(counts.mean(), 1e-9))}
+    if w.plant:
+        hot = np.zeros(w.B, bool)
+        hot[synth.hot_blocks(w)] = True
+        if hot.any() and (~hot).any():
+            popularity["hot_mean"] = float(counts[:, hot].mean())
+            popularity["other_mean"] = float(counts[:, ~hot].mean())
     tokens_s = w.batch * w.N / (ms_step * 1e-3)
     tflops = (f_idx + f_main) / (ms_step * 1e-3) / 1e12
 
@@ -394,8 +414,16 @@ def main():
         csec = time.perf_counter() - c0
         sample_flops = (float((rows // w.B_k).sum()) * 2 * w.d_idx * w.H_kv * w.B_k
                         + acc.main_flops(obi, 0, w.N, w.B_k, w.G, w.d_h) / 1.0)
+        model = None
+        try:
+            with open("/proc/cpuinfo") as f:
+                model = next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")), None)
+        except OSError:
+            pass
         cpu = {"value": len(rows) / csec, "unit": "tokens/s", "cores": oracle.num_threads(),
+               "cpu_model": model,
                "kind": "oracle", "seconds": csec, "gflops": sample_flops / csec / 1e9,
+               "extrapolated_full_seconds": csec * (f_idx + f_main) / sample_flops,
                "sample": f"{len(rows)} seeded random query rows of {w.name}, all {w.H_kv} groups "
                          f"and {w.H_q} heads: index branch (fp32) + sparse attention (fp64)"}
         log(f"cpu baseline: {csec:.1f} s -> {cpu['value']:.1f} tokens/s on {cpu['cores']} threads")
@@ -408,7 +436,9 @@ def main():
         "config": {"workload": w.name, "batch": w.batch, "N": w.N, "H_q": w.H_q, "H_kv": w.H_kv,
                    "d_h": w.d_h, "d_idx": w.d_idx, "B_k": w.B_k, "k": w.k,
                    "q_chunk": w.q_chunk, "hot_blocks": w.plant},
+        "ms_median": ms_median, "ms_min": ms_min,
         "sparse_tflops": tflops, "index_flops": f_idx, "main_flops": f_main,
+        "block_popularity": popularity,
         "roofline": roofline, "kernels": kernels, "dense_baseline": dense, "decode": decode,
         "backward": backward,
         "measured_peaks": peaks, "cpu_baseline": cpu,

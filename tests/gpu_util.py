@@ -91,9 +91,19 @@ def check_selection(gpu, orc, marg, M, k, what=""):
             "near_tie_differing": n_diff}
 
 
-def err_stats(got, ref):
-    d = np.abs(np.asarray(got, np.float64) - np.asarray(ref, np.float64))
-    return float(d.max()), float(d.mean())
+def err_stats(got, ref, label=None):
+    """max |diff| and mean |diff|; with a label, also log the cosine
+    similarity and the relative L2 error ||got - ref|| / ||ref||."""
+    g = np.asarray(got, np.float64)
+    r = np.asarray(ref, np.float64)
+    d = np.abs(g - r)
+    mx, mn = float(d.max()), float(d.mean())
+    if label is not None:
+        nr, ng = float(np.linalg.norm(r)), float(np.linalg.norm(g))
+        cos = float((g * r).sum() / max(nr * ng, 1e-300))
+        rel = float(np.linalg.norm(g - r) / max(nr, 1e-300))
+        log(f"  {label}: max |diff| {mx:.3g}  mean |diff| {mn:.3g}  cos-sim {cos:.8f}  rel L2 {rel:.3g}")
+    return mx, mn
 
 
 def compact_attention_rows(w: synth.Workload, rows: np.ndarray, sel: np.ndarray, bat: int = 0):

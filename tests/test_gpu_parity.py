@@ -231,7 +231,7 @@ def test_attention_and_combine_parity(w):
                                 synth.host_rows(w, "k", b * w.N + np.arange(w.N)),
                                 synth.host_rows(w, "v", b * w.N + np.arange(w.N)), sel[b],
                                 dtype=code, q_scale=sc, k_scale=sc, v_scale=sc)
-        mx, mn = err_stats(out[b], O)
+        mx, mn = err_stats(out[b], O, label="O")
         log(f"  batch {b}: output max abs {mx:.3g} mean abs {mn:.3g}")
         assert mx <= tol_max and mn <= 2e-3
         lmx, _ = err_stats(lse[b], L)
@@ -251,7 +251,7 @@ def test_combine_parity_random_partials():
     lpt = torch.from_numpy(lp[None]).to(DEV)
     out, lse = msa.msa_combine(d, bi, opt, lpt, want_lse=True)
     O, L = oracle.combine(sel, op, lp)
-    mx, mn = err_stats(out.float().cpu().numpy()[0], O)
+    mx, mn = err_stats(out.float().cpu().numpy()[0], O, label="O")
     assert mx <= 2e-2 and mn <= 2e-3
     lmx, _ = err_stats(lse.cpu().numpy()[0], L)
     assert lmx <= 1e-5
@@ -285,7 +285,7 @@ def test_forward_parity(w):
     O, L = oracle.attention(w.N, w.B_k, rows, synth.host_all(w, "q"), synth.host_all(w, "k"),
                             synth.host_all(w, "v"), gsel, dtype=code, q_scale=sc, k_scale=sc,
                             v_scale=sc)
-    mx, mn = err_stats(out.float().cpu().numpy()[0], O)
+    mx, mn = err_stats(out.float().cpu().numpy()[0], O, label="O")
     log(f"  output max abs {mx:.3g} mean abs {mn:.3g}")
     assert mx <= (6e-2 if w.dtype == "fp8" else 2e-2) and mn <= 2e-3
     lmx, _ = err_stats(lse.cpu().numpy()[0], L)
@@ -365,7 +365,7 @@ def test_window_selection_attention_parity(w):
         keys = b * w.N + np.arange(w.N)
         O, L = oracle.attention(w.N, w.B_k, rows, synth.host_rows(w, "q", b * w.N + rows),
                                 synth.host_rows(w, "k", keys), synth.host_rows(w, "v", keys), want)
-        mx, mn = err_stats(out[b], O)
+        mx, mn = err_stats(out[b], O, label="O")
         log(f"  batch {b}: output max abs {mx:.3g} mean abs {mn:.3g}")
         assert mx <= 2e-2 and mn <= 2e-3
         lmx, _ = err_stats(lse[b], L)
@@ -404,7 +404,7 @@ def test_dense_attention_parity(w):
     rows = np.arange(w.N)
     for b in range(w.batch):
         O, L = _dense_oracle(w, rows, b)
-        mx, mn = err_stats(out[b], O)
+        mx, mn = err_stats(out[b], O, label="O")
         log(f"  batch {b}: output max abs {mx:.3g} mean abs {mn:.3g}")
         assert mx <= 2e-2 and mn <= 2e-3
         lmx, _ = err_stats(lse[b], L)
@@ -428,7 +428,7 @@ def test_dense_attention_subrange_leaves_other_rows():
     assert (o[outside] == 7.0).all() and (lse[outside] == -5.0).all()
     rows = np.arange(qb, qb + qn)
     O, L = _dense_oracle(w, rows)
-    mx, mn = err_stats(o[rows], O)
+    mx, mn = err_stats(o[rows], O, label="O")
     assert mx <= 2e-2 and mn <= 2e-3
     lmx, _ = err_stats(lse[rows], L)
     assert lmx <= 1e-3
@@ -451,7 +451,7 @@ def test_dense_attention_full_size_sampled():
     log(f"dense full-size {w.name}: oracle on {len(rows)} rows")
     O, L = oracle.dense_attention(w.N, w.B_k, rows, synth.host_rows(w, "q", rows),
                                   synth.host_all(w, "k"), synth.host_all(w, "v"))
-    mx, mn = err_stats(gout, O)
+    mx, mn = err_stats(gout, O, label="O")
     log(f"  output max abs {mx:.3g} mean abs {mn:.3g}")
     assert mx <= 2e-2 and mn <= 2e-3
     lmx, _ = err_stats(glse, L)
@@ -488,7 +488,7 @@ def _check_decode(w, t, out, lse, bi, tol_max=2e-2):
         gsel = bi[b][:, None, :]                                   # [H_sel, 1, k]
         st = check_selection(gsel, ob, marg, M, w.k, what=f"decode b{b}")
         O, L = compact_attention_rows(w, last, gsel, bat=b)
-        mx, mn = err_stats(out[b], O[0])
+        mx, mn = err_stats(out[b], O[0], label="O")
         log(f"  batch {b}: {st}; output max abs {mx:.3g} mean abs {mn:.3g}")
         assert mx <= tol_max and mn <= 2e-3
         lmx, _ = err_stats(lse[b], L[0])
@@ -559,7 +559,7 @@ def test_decode_ragged_lengths(w, lens):
         check_selection(gsel, ob, marg, M, w.k, what=f"ragged b{b}")
         O, L = oracle.attention(n, w.B_k, row, synth.host_rows(w, "q", flat), synth.host_rows(w, "k", keys),
                                 synth.host_rows(w, "v", keys), gsel)
-        mx, mn = err_stats(out[b], O[0])
+        mx, mn = err_stats(out[b], O[0], label="O")
         log(f"  seq {b} (len {n}): output max abs {mx:.3g} mean abs {mn:.3g}")
         assert mx <= 2e-2 and mn <= 2e-3
         lmx, _ = err_stats(lse[b], L[0])
@@ -608,6 +608,6 @@ def test_full_size_sampled_parity(w, nrows):
     log(f"  selection: {st}")
     log(f"full-size {w.name}: oracle attention on {len(rows)} rows")
     O, _ = compact_attention_rows(w, rows, gsel)
-    mx, mn = err_stats(gout, O)
+    mx, mn = err_stats(gout, O, label="O")
     log(f"  output max abs {mx:.3g} mean abs {mn:.3g}")
     assert mx <= (6e-2 if w.dtype == "fp8" else 2e-2) and mn <= 2e-3
