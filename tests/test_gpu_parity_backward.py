@@ -107,12 +107,13 @@ def test_backward_without_index_branch_matches():
         _grad_check(name, _f(b[name]), _f(a[name]))
 
 
-def test_backward_16k_sampled_rows_and_sums():
-    """A 16K prefill with 64 query heads: dQ, dq_idx and KL on sampled rows
-    against the oracle; over all rows, the exact sums sum_j dK_j = 0,
+@pytest.mark.parametrize("w", [synth.P16K, synth.P128K_HOT], ids=lambda w: w.name)
+def test_backward_sampled_rows_and_sums(w):
+    """The 16K prefill and the 128K prefill with planted hot blocks (the
+    backward bench workload), 64 query heads: dQ, dq_idx and KL on sampled
+    rows against the oracle; over all rows, the exact sums sum_j dK_j = 0,
     sum_j dk_idx_j = 0 (softmax rows sum to one, dS and g rows to zero) and
     sum_j dV_j = sum over rows and heads of dO."""
-    w = synth.P16K
     log(f"backward {w.name}")
     t = device_inputs(w, DEV)
     d_o = synth.device_tensor(w, "d_o", DEV)
@@ -122,9 +123,10 @@ def test_backward_16k_sampled_rows_and_sums():
     ref = oracle.backward(w.N, w.B_k, rows, synth.host_rows(w, "q", rows), allk["k"], allk["v"],
                           synth.host_rows(w, "q_idx", rows), allk["k_idx"], sel[0][:, rows],
                           synth.host_rows(w, "d_o", rows), kl_weight=KL_W)
-    _grad_check("dq (sampled rows)", _f(g["dq"][0])[rows], ref["dq"])
-    _grad_check("dq_idx (sampled rows)", _f(g["dq_idx"][0])[rows], ref["dq_idx"])
-    kl = _f(g["kl"][0])[:, rows]
+    ri = torch.as_tensor(rows, device=DEV)
+    _grad_check("dq (sampled rows)", _f(g["dq"][0][ri]), ref["dq"])
+    _grad_check("dq_idx (sampled rows)", _f(g["dq_idx"][0][ri]), ref["dq_idx"])
+    kl = _f(g["kl"][0][:, ri])
     assert np.abs(kl - ref["kl"]).max() <= 1e-3 * max(1.0, float(ref["kl"].max()))
     dk = g["dk"][0].view(torch.bfloat16).double()
     dv = g["dv"][0].view(torch.bfloat16).double()
