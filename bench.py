@@ -118,6 +118,9 @@ def main():
                     help="skip the dense causal GQA baseline on the same Q, K, V")
     ap.add_argument("--no-decode", action="store_true",
                     help="skip the decode step (last token of 8 sequences of the workload's length)")
+    ap.add_argument("--no-variants", action="store_true",
+                    help="skip the selection-variant timings (block sizes, index heads, forced and "
+                         "sliding-window selections)")
     ap.add_argument("--no-backward", action="store_true",
                     help="skip the training backward pass (msa_backward) timing")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
@@ -242,6 +245,73 @@ def main():
                     "tokens_s": w.batch * w.N / (bms * 1e-3), "workspace_bytes": wsb.numel()}
         log(f"backward: {bms:.2f} ms, {backward['achieved']:.0f} TFLOP/s")
         del d_o, wsb
+        torch.cuda.empty_cache()
+
+    # ---- selection variants (the paper's ablations) on the same Q, K, V,
+    # Q^idx, K^idx: 64- and 32-token key blocks (k = 32), eight index heads
+    # over the four K/V heads, the forced first block with a 4-block local
+    # window, and the FLOP-matched sliding window; each is one whole pass
+    # (selection, inversion, attention, combine) timed like the forward
+    variants = None
+    if kern and not args.no_variants and w.dtype == "bf16":
+        variants = {}
+
+        def timed(fn, reps=3):
+            fn()
+            torch.cuda.synchronize()
+            a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a0.record(stream)
+            for _ in range(reps):
+                fn()
+            a1.record(stream)
+            torch.cuda.synchronize()
+            return a0.elapsed_time(a1) / reps
+
+        def record(name, dv, ms, biv):
+            selv = biv.cpu().numpy().reshape(-1, w.N, dv.k)
+            f_m = acc.main_flops(selv, 0, w.N, dv.B_k, w.H_q // dv.H_sel, w.d_h)
+            f_i = acc.index_flops(0, w.N, dv.H_sel, w.d_idx, dv.B_k, batch=w.batch)
+            variants[name] = {"ms": ms, "tokens_s": w.batch * w.N / (ms * 1e-3), "B_k": dv.B_k, "k": dv.k,
+                              "H_idx": dv.H_sel, "index_flops": f_i, "main_flops": f_m,
+                              "sparse_tflops": (f_i + f_m) / (ms * 1e-3) / 1e12}
+            log(f"variant {name}: {ms:.2f} ms, {variants[name]['sparse_tflops']:.0f} sparse TFLOP/s")
+
+        qi8 = synth.device_tensor(w.with_(H_idx=8), "q_idx", dev)
+        for name, B_k, k, H_idx, qiv in (("block64_k32", 64, 32, 0, t["q_idx"]),
+                                         ("block32_k32", 32, 32, 0, t["q_idx"]),
+                                         ("index_heads8", w.B_k, w.k, 8, qi8)):
+            dv = msa.make_dims(w.batch, w.N, w.H_q, w.H_kv, w.d_h, w.d_idx, B_k, k, H_idx=H_idx)
+            biv = torch.empty((w.batch, dv.H_sel, w.N, k), dtype=torch.int32, device=dev)
+            wsv = torch.empty((msa.msa_workspace_size(dv, o),), dtype=torch.uint8, device=dev)
+            ms = timed(lambda: msa.msa_forward(dv, o, t["q"], t["k"], t["v"], qiv, t["k_idx"], o=out,
+                                               block_idx_out=biv, workspace=wsv))
+            record(name, dv, ms, biv)
+            del biv, wsv
+            torch.cuda.empty_cache()
+        del qi8
+
+        # composed passes: the selection call, then the inversion, attention
+        # and combine entry points on preallocated buffers
+        sb_v = msa.msa_invert_workspace_size(d, 0, w.N)
+        sched_v = torch.empty(((sb_v + 3) // 4,), dtype=torch.int32, device=dev)
+        offs_v = torch.empty((w.batch, w.H_kv, w.B + 1), dtype=torch.int32, device=dev)
+        ents_v = torch.empty((w.batch * w.H_kv * w.N * w.k,), dtype=torch.int32, device=dev)
+        op_v = torch.empty((w.batch, w.H_kv, w.N, w.k, w.G, w.d_h), dtype=torch.bfloat16, device=dev)
+        lp_v = torch.empty((w.batch, w.H_kv, w.N, w.k, w.G), dtype=torch.float32, device=dev)
+        biv = torch.empty((w.batch, w.H_kv, w.N, w.k), dtype=torch.int32, device=dev)
+
+        def rest():
+            msa.msa_invert_blocks(d, biv, blk_offsets=offs_v, blk_entries=ents_v, sched=sched_v)
+            msa.msa_sparse_attn_fwd(d, o, t["q"], t["k"], t["v"], offs_v, ents_v, sched_v,
+                                    o_part=op_v, lse_part=lp_v)
+            msa.msa_combine(d, biv, op_v, lp_v, o=out)
+
+        ms = timed(lambda: (msa.msa_index_topk_forced(d, t["q_idx"], t["k_idx"], force_first=True,
+                                                       local_window=4, block_idx=biv), rest()))
+        record("forced_first_window4", d, ms, biv)
+        ms = timed(lambda: (msa.msa_window_select(d, block_idx=biv), rest()))
+        record("sliding_window", d, ms, biv)
+        del sched_v, offs_v, ents_v, op_v, lp_v, biv
         torch.cuda.empty_cache()
 
     # ---- the dense causal GQA baseline on the same Q, K, V (bf16 workloads up
@@ -440,7 +510,7 @@ def main():
         "sparse_tflops": tflops, "index_flops": f_idx, "main_flops": f_main,
         "block_popularity": popularity,
         "roofline": roofline, "kernels": kernels, "dense_baseline": dense, "decode": decode,
-        "backward": backward,
+        "backward": backward, "variants": variants,
         "measured_peaks": peaks, "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
