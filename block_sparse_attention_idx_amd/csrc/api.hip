@@ -92,7 +92,7 @@ size_t align256(size_t b) { return (b + 255) / 256 * 256; }
 
 struct ForwardLayout {
   int64_t qc;  // rows per chunk
-  size_t off_bi, off_off, off_ent, off_sched, off_opart, off_lpart, total;
+  size_t off_bi, off_off, off_ent, off_sched, off_opart, off_lpart, off_biall, total;
 };
 
 ForwardLayout forward_layout(const msa_dims* d, const msa_opts* o) {
@@ -122,6 +122,9 @@ ForwardLayout forward_layout(const msa_dims* d, const msa_opts* o) {
   off += align256(slots * GS(d) * d->d_h * 2);
   L.off_lpart = off;
   off += align256(slots * GS(d) * 4);
+  // chunked: the whole selection (one index launch over all rows)
+  L.off_biall = off;
+  if (L.qc < d->N) off += align256(static_cast<size_t>(seqs) * d->N * d->k * 4);
   L.total = off;
   return L;
 }
@@ -569,13 +572,34 @@ int msa_forward(const msa_dims* dims, const msa_opts* opts, const void* q, const
   const bool one_chunk = L.qc >= dims->N;
   const int64_t seqs = static_cast<int64_t>(dims->batch) * HS(dims);
 
+  // With several chunks the index branch runs once over all rows (its
+  // workgroups heaviest first across the whole sequence, instead of one
+  // launch per chunk that waits for its heaviest tile); each chunk's rows of
+  // every sequence are then copied out contiguous for the inversion and the
+  // combine.
+  int32_t* bi_all = nullptr;
+  if (!one_chunk) {
+    bi_all = block_idx_out ? block_idx_out : reinterpret_cast<int32_t*>(ws + L.off_biall);
+    const hipError_t e = msa::launch_index_topk(static_cast<const uint16_t*>(q_idx),
+                                                static_cast<const uint16_t*>(k_idx), dims->batch, dims->N,
+                                                HS(dims), dims->d_idx, dims->k, 0, dims->N, bi_all, s, 0, 1,
+                                                dims->B_k);
+    if (e != hipSuccess) return hip_fail(e);
+  }
+
   for (int64_t qb = 0; qb < dims->N; qb += L.qc) {
     const int64_t qn = (dims->N - qb) < L.qc ? (dims->N - qb) : L.qc;
     int32_t* bi = (one_chunk && block_idx_out) ? block_idx_out : bi_chunk;
-    hipError_t e = msa::launch_index_topk(static_cast<const uint16_t*>(q_idx),
-                                          static_cast<const uint16_t*>(k_idx), dims->batch, dims->N,
-                                          HS(dims), dims->d_idx, dims->k, qb, qn, bi, s, 0, 1,
-                                          dims->B_k);
+    hipError_t e;
+    if (one_chunk) {
+      e = msa::launch_index_topk(static_cast<const uint16_t*>(q_idx), static_cast<const uint16_t*>(k_idx),
+                                 dims->batch, dims->N, HS(dims), dims->d_idx, dims->k, qb, qn, bi, s, 0, 1,
+                                 dims->B_k);
+    } else {
+      const size_t w = static_cast<size_t>(qn) * dims->k * sizeof(int32_t);
+      e = hipMemcpy2DAsync(bi, w, bi_all + qb * dims->k, static_cast<size_t>(dims->N) * dims->k * 4, w,
+                           static_cast<size_t>(seqs), hipMemcpyDeviceToDevice, s);
+    }
     if (e != hipSuccess) return hip_fail(e);
     e = msa::launch_invert(bi, dims->batch, HS(dims), GS(dims), dims->k, qb, qn, offs, ents, sched, s,
                            dims->B_k);
@@ -587,12 +611,6 @@ int msa_forward(const msa_dims* dims, const msa_opts* opts, const void* q, const
     e = msa::launch_combine(bi, opart, lpart, dims->batch, dims->N, HS(dims), GS(dims), dims->k,
                             qb, qn, static_cast<uint16_t*>(o), lse, s);
     if (e != hipSuccess) return hip_fail(e);
-    if (block_idx_out && !one_chunk) {
-      const size_t w = static_cast<size_t>(qn) * dims->k * sizeof(int32_t);
-      e = hipMemcpy2DAsync(block_idx_out + qb * dims->k, static_cast<size_t>(dims->N) * dims->k * 4,
-                           bi, w, w, static_cast<size_t>(seqs), hipMemcpyDeviceToDevice, s);
-      if (e != hipSuccess) return hip_fail(e);
-    }
   }
   return MSA_OK;
 }

@@ -231,9 +231,10 @@ int msa_combine(const msa_dims *dims, const int32_t *block_idx, const void *o_pa
 /*
  * msa_workspace_size / msa_forward -- the whole forward pass: for each chunk of
  * opts->q_chunk query rows (all N at once when 0): index_topk, invert_blocks,
- * sparse_attn_fwd, combine.  The workspace (device memory, at least
- * msa_workspace_size bytes, 256-byte aligned) holds the per-chunk selection,
- * inverted index, work list and partial outputs.
+ * sparse_attn_fwd, combine (with several chunks, index_topk runs once over
+ * all rows first).  The workspace (device memory, at least msa_workspace_size
+ * bytes, 256-byte aligned) holds the per-chunk selection, inverted index,
+ * work list and partial outputs, and with several chunks the whole selection.
  *
  *   q, k, v        as for msa_sparse_attn_fwd
  *   q_idx, k_idx   as for msa_index_topk
