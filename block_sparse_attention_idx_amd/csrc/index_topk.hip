@@ -116,7 +116,12 @@ __global__ __launch_bounds__(kIdxThreads, 1) void index_topk_kernel(
   constexpr int STEPS = DIDX / 16;
   constexpr int KSTR = kidx_stride<DIDX>();
   constexpr int BK = 32 * KT;
-  constexpr int TILE = BK * KSTR;
+  // Ring buffer stride: a whole number of the 1 KB a wave's DMA instruction
+  // writes.  The last instruction of a block covers slots past the tile's end
+  // (their sources are clamped to the last slot, the LDS destination is not),
+  // so with 32-key blocks (4.5 or 8.5 KB of slots) the stride is padded and
+  // those lanes land in the buffer's own padding instead of the next buffer.
+  constexpr int TILE = (BK * KSTR + 1023) / 1024 * 1024;
   constexpr int NBUF = 4;  // LDS ring: two blocks scored, two in flight
   __shared__ __attribute__((aligned(16))) uint8_t lds[KM > 0 ? NBUF * TILE : 16];
 

@@ -63,6 +63,11 @@ INDEX_CASES = [
     TINY.with_(N=2000, k=4, H_q=16, H_kv=2, H_idx=8),       # more index heads than K/V heads
     TINY.with_(N=1500, k=6, B_k=64),                        # 64-token blocks
     TINY.with_(N=1000, k=8, B_k=32, d_idx=128),             # 32-token blocks
+    # 32-token blocks with one free slot: every score of the ring's blocks
+    # decides the selection (the ring's buffer stride must hold the last DMA
+    # instruction of a block, which reaches past a 4.5 / 8.5 KB tile)
+    TINY.with_(N=521, k=2, H_q=4, H_kv=2, B_k=32, d_idx=64, batch=2),
+    TINY.with_(N=777, k=2, B_k=32, d_idx=128),
     TINY.with_(batch=2, N=1300),
 ]
 
