@@ -8,7 +8,8 @@ Forward: the selection is checked on sampled rows (edge rows and seeded random
 rows) by the margin rule of the other parity tests, and the output and LSE of
 those rows against the oracle's attention over the GPU's own selection.
 Backward (B_k = 128, small N): every gradient and the KL over all rows, with
-the tolerances of the backward parity tests.
+the tolerances of the backward parity tests.  Decode: the last token of every
+sequence, selection and output, as in the decode parity tests.
 """
 from __future__ import annotations
 
@@ -21,6 +22,7 @@ import oracle
 import synth
 from gpu_util import (check_selection, device_inputs, dims_of, err_stats, log, opts_of, oracle_index_rows,
                       sample_rows)
+from test_gpu_parity import _check_decode, _decode_inputs
 from test_gpu_parity_backward import KL_W, _f, _grad_check, _run
 
 pytestmark = pytest.mark.gpu
@@ -56,6 +58,8 @@ def _draw(rng, backward: bool, seed: int) -> synth.Workload:
 _RNG = np.random.default_rng(20261202)
 FWD_SWEEP = [_draw(_RNG, False, 1000 + j) for j in range(14)]
 BWD_SWEEP = [_draw(_RNG, True, 2000 + j) for j in range(6)]
+DEC_SWEEP = [_draw(_RNG, False, 3000 + j).with_(dtype="bf16", q_chunk=0, N=int(_RNG.integers(1, 6000)))
+             for j in range(6)]
 
 
 def _wid(w):
@@ -108,3 +112,15 @@ def test_backward_sweep(w):
             _grad_check(f"{name}[{bat}]", _f(g[name][bat]), ref[name])
         kl = _f(g["kl"][bat])
         assert float(np.abs(kl - ref["kl"]).max()) <= 1e-3 * max(1.0, float(ref["kl"].max()))
+
+
+@pytest.mark.parametrize("w", DEC_SWEEP, ids=_wid)
+def test_decode_sweep(w):
+    log(f"sweep decode {_wid(w)}")
+    t = device_inputs(w, DEV)
+    q1, qi1 = _decode_inputs(w, t)
+    bi = torch.empty((w.batch, w.H_sel, w.k), dtype=torch.int32, device=DEV)
+    out, lse, _ = msa.msa_decode(dims_of(w), msa.make_opts(), q1, qi1, t["k"], t["v"], t["k_idx"],
+                                 block_idx_out=bi, want_lse=True)
+    torch.cuda.synchronize()
+    _check_decode(w, t, out.float().cpu().numpy(), lse.cpu().numpy(), bi.cpu().numpy())
