@@ -41,10 +41,15 @@
 // swapped, so that the 8 rows a lane contributes to one 16-row step are one
 // 16-byte chunk).
 //
-// The proxy softmax needs the proxy LSE over all of a query's selected tokens
-// first: a KV-outer pass over the same work list (one wave per workgroup)
-// writes one partial LSE per (query, slot), merged per query ("Flash-MSA",
-// Backward: a cheap sparse proxy pass recomputes the proxy LSE).
+// The main-branch kernel, which has every head's probabilities, also forms
+// the teacher distribution (the mean over the group's heads) and writes one
+// fp32 row of it per (query, slot); the index-branch kernel reads those rows
+// and only the proxy operands.  The proxy softmax needs the proxy LSE over all
+// of a query's selected tokens first: a KV-outer pass over the same work list
+// (one wave per workgroup) writes one partial LSE per (query, slot), merged per
+// query ("Flash-MSA", Backward: a cheap sparse proxy pass recomputes the proxy
+// LSE).  Order: D, proxy LSE, main branch (with the teacher rows), index
+// branch, then the per-slot sums.
 #include "attn_tile.h"
 #include "msa_internal.h"
 
@@ -183,7 +188,7 @@ __device__ __forceinline__ void put_rows(const u32x4 (&w)[4], uint8_t* rm, uint8
 }
 
 // The chunks of a workgroup's passes in order: pass descriptor and first
-// entry.  `after` advances the pass iterator, so it is called once per chunk,
+// entry.  `next_chunk` advances the pass iterator, so it is called once per chunk,
 // in sequence.
 struct Chunk {
   PassDesc D;
