@@ -78,3 +78,24 @@ def test_decode_bytes_dominated_by_index_scan():
     small = acc.decode_bytes(2, 100, 8, 2, 128, 64, 128, 4, 2 * 2)
     assert small == (2 * 2 * 64 * 2 + 2 * 4 * 2 * 2 * 1 + 4 * 2 * 128 * 128 * 2
                      + 2 * 4 * 4 * (256 + 4) + 2 * 4 * 2 * 2 * 4 + 2 * 2 * 8 * 128 * 2)
+
+
+def test_backward_flops_relations():
+    """The backward's main-branch count is 2.5x the forward's 4 d_h per visible
+    key (S recomputed, dP, dV, dK, dQ), the index branch's 8 d_idx per visible
+    (query, group, key), and nothing when the index branch is off; a full
+    budget (every causal block selected) counts every key j <= i."""
+    N, B_k, k, G, d_h, d_idx = 640, 64, 16, 4, 128, 64
+    i = np.arange(N)
+    L = i // B_k
+    sel = np.full((2, N, k), -1, np.int32)
+    for r in range(2):
+        for row in range(N):
+            sel[r, row, :L[row] + 1] = np.arange(L[row] + 1)   # k * B_k >= N: all causal blocks
+    fwd = acc.main_flops(sel, 0, N, B_k, G, d_h)
+    main, idx = acc.backward_flops(sel, 0, N, B_k, G, d_h, d_idx)
+    keys = float((i + 1).sum()) * 2                             # visible (query, group, key)
+    assert fwd == 4.0 * d_h * G * keys
+    assert main == 2.5 * fwd
+    assert idx == 8.0 * d_idx * keys
+    assert acc.backward_flops(sel, 0, N, B_k, G, d_h, d_idx, index=False)[1] == 0.0
