@@ -80,13 +80,14 @@ def brute_select(M, k):
     return out, marg
 
 
-@pytest.mark.parametrize("N,H,d,k,seed", [
-    (256, 1, 64, 1, 0), (256, 2, 64, 2, 1), (1000, 2, 128, 4, 2), (1000, 1, 64, 16, 3),
-    (2048, 2, 64, 4, 4), (2048, 1, 128, 8, 5), (640, 3, 32, 3, 6),
+@pytest.mark.parametrize("N,H,d,k,seed,B_k", [
+    (256, 1, 64, 1, 0, 128), (256, 2, 64, 2, 1, 128), (1000, 2, 128, 4, 2, 128), (1000, 1, 64, 16, 3, 128),
+    (2048, 2, 64, 4, 4, 128), (2048, 1, 128, 8, 5, 128), (640, 3, 32, 3, 6, 128),
+    (521, 2, 64, 2, 7, 32), (777, 1, 128, 2, 8, 32), (1000, 2, 64, 16, 9, 32),   # 32-token blocks
+    (1200, 2, 128, 6, 10, 64), (200, 1, 64, 3, 11, 64),                           # 64-token blocks
 ])
-def test_index_matches_brute_force(N, H, d, k, seed):
+def test_index_matches_brute_force(N, H, d, k, seed, B_k):
     rng = np.random.default_rng(seed)
-    B_k = 128
     q = _rand_bf16(rng, (N, H, d))
     kk = _rand_bf16(rng, (N, d))
     pos = np.arange(N)
@@ -102,16 +103,16 @@ def test_index_matches_brute_force(N, H, d, k, seed):
     assert np.array_equal(bi[sure], bb[sure])
 
 
-@pytest.mark.parametrize("N,H,d,k,first,window,seed", [
-    (2048, 2, 64, 6, True, 1, 20), (2048, 1, 64, 6, False, 3, 21), (1500, 2, 128, 8, True, 4, 22),
-    (1000, 1, 64, 4, True, 3, 23),                      # all k - 1 choices forced
+@pytest.mark.parametrize("N,H,d,k,first,window,seed,B_k", [
+    (2048, 2, 64, 6, True, 1, 20, 128), (2048, 1, 64, 6, False, 3, 21, 128), (1500, 2, 128, 8, True, 4, 22, 128),
+    (1000, 1, 64, 4, True, 3, 23, 128),                 # all k - 1 choices forced
+    (900, 2, 64, 6, True, 2, 24, 32), (1100, 1, 128, 5, True, 2, 25, 64),
 ])
-def test_forced_selection_matches_brute_force(N, H, d, k, first, window, seed):
+def test_forced_selection_matches_brute_force(N, H, d, k, first, window, seed, B_k):
     """Forced first block / local window: the forced blocks are always chosen,
     the remaining slots go to the best others (fp64 brute force with the
     forced blocks removed from the candidates)."""
     rng = np.random.default_rng(seed)
-    B_k = 128
     q = _rand_bf16(rng, (N, H, d))
     kk = _rand_bf16(rng, (N, d))
     pos = np.arange(N)
@@ -296,11 +297,12 @@ def test_dense_attention_is_library_causal_gqa(N, Hq, Hkv, rows):
     np.testing.assert_allclose(lse, ref_lse[pos], rtol=0, atol=1e-12)
 
 
-@pytest.mark.parametrize("N,Hq,Hkv,k,seed", [(900, 4, 2, 3, 11), (1024, 6, 3, 2, 12),
-                                            (513, 2, 1, 4, 13)])
-def test_attention_matches_masked_library_attention(N, Hq, Hkv, k, seed):
+@pytest.mark.parametrize("N,Hq,Hkv,k,seed,B_k", [(900, 4, 2, 3, 11, 128), (1024, 6, 3, 2, 12, 128),
+                                                (513, 2, 1, 4, 13, 128), (450, 4, 2, 3, 16, 32),
+                                                (700, 2, 1, 5, 17, 64)])
+def test_attention_matches_masked_library_attention(N, Hq, Hkv, k, seed, B_k):
     rng = np.random.default_rng(seed)
-    d, B_k = 32, 128
+    d = 32
     G = Hq // Hkv
     q, K, V = _make_attn_inputs(rng, N, Hq, Hkv, d)
     bi = _rand_selection(rng, N, Hkv, B_k, k)
