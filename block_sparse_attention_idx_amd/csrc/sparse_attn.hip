@@ -204,8 +204,8 @@ struct QFrag<true> {
 
 // BKS: log2 of the key block size.  Blocks of 32 or 64 tokens (the paper's
 // block-size ablation) stage their tokens into the 128-key tile with zeros
-// after them, and every pass hides the keys past the block: the same kernel
-// at 2x or 4x the MFMA work per visible key.
+// after them; the key tiles past the block are left out of the scores, the
+// softmax and P V at compile time.
 template <int G, bool FP8, int BKS>
 __global__ __launch_bounds__(kThreads, 8 / kWaves) void sparse_attn_kernel(
     const void* __restrict__ qp, const void* __restrict__ kp, const void* __restrict__ vp,
@@ -355,10 +355,13 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void sparse_attn_kernel(
   // of every row and swap partial results with one v_permlane32_swap.
   // P^T fragments (B operand of O^T = V^T P^T): step st = 2 mt + e2 covers
   // keys 32mt + 16e2 + 8(j/4) + 4h + (j%4), accumulator elements 8e2 .. +7.
+  // Key tiles past a smaller block hold no keys: their probabilities are zero
+  // and neither the softmax nor P V visits them.
+  constexpr int kMT = (1 << BKS) / 32;
   auto softmax = [&](const f32x16(&acc)[4], bf16x8(&pf)[8], float& inv, float& lse2) {
     float m0 = -__builtin_huge_valf(), m1 = -__builtin_huge_valf();
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
+    for (int mt = 0; mt < kMT; ++mt) {
 #pragma unroll
       for (int el = 0; el < 16; el += 4) {
         m0 = fmaxf(m0, fmaxf(acc[mt][el], acc[mt][el + 1]));
@@ -368,7 +371,7 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void sparse_attn_kernel(
     const float mb = halves_max(fmaxf(m0, m1)) * scale_log2;  // scale_log2 > 0
     float l0 = 0.f, l1 = 0.f;
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
+    for (int mt = 0; mt < kMT; ++mt) {
 #pragma unroll
       for (int e2 = 0; e2 < 2; ++e2) {
         uint32_t w[4];
@@ -395,7 +398,7 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void sparse_attn_kernel(
     for (int dt = 0; dt < 4; ++dt) {
       f32x16 oa = {};
 #pragma unroll
-      for (int st = 0; st < 8; ++st) {
+      for (int st = 0; st < 2 * kMT; ++st) {
         // row dsel + 16 dt (stored at dvt_row(dsel) + 32 dt); keys
         // 16 st + 8 h .. + 7, one 16-byte chunk in the permuted key order
         const u32x4 vf = *reinterpret_cast<const u32x4*>(v_base + 32 * dt * kVStride + 32 * st);
