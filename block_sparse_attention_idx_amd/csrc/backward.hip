@@ -130,39 +130,11 @@ __device__ __forceinline__ EntryRef entry_ref(uint32_t ent, int seq, int kslots,
   return r;
 }
 
-// Stage 64 rows of a [*, d_h = 128] bf16 tensor: row-major into `rm` (may be
-// null) and transposed into `tr` (may be null).  Thread t loads 16-byte chunk
-// t % 16 of rows 4 (t / 16) .. + 3; `row_ptr(rho)` gives the row (null =
-// zeros).
-template <typename RowPtr>
-__device__ __forceinline__ void stage_rows(RowPtr row_ptr, uint8_t* rm, uint8_t* tr) {
-  const int t = threadIdx.x;
-  const int dg = t & 15, rc = t >> 4;
-  u32x4 w[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const uint16_t* p = row_ptr(4 * rc + j);
-    w[j] = p ? *reinterpret_cast<const u32x4*>(p + 8 * dg) : u32x4{0u, 0u, 0u, 0u};
-  }
-  if (rm) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) *reinterpret_cast<u32x4*>(rm + (4 * rc + j) * kStr + 16 * dg) = w[j];
-  }
-  if (tr) {
-    const int col = tpos(4 * rc);
-#pragma unroll
-    for (int dd = 0; dd < 8; ++dd) {
-      const u32x2 v = {bf16_of(w[0], dd) | (bf16_of(w[1], dd) << 16),
-                       bf16_of(w[2], dd) | (bf16_of(w[3], dd) << 16)};
-      *reinterpret_cast<u32x2*>(tr + (8 * dg + dd) * kTStr + 2 * col) = v;
-    }
-  }
-}
-
-// The two halves of stage_rows, for software pipelining: load_rows issues
-// this thread's global loads (16-byte chunk t % 16 of rows 4 (t / 16) .. + 3;
-// `row_ptr(rho)` must give a readable row), put_rows writes them row-major
-// into `rm` and transposed into `tr` (either may be null).
+// Staging of 64 rows of a [*, d_h = 128] bf16 tensor in two halves, for
+// software pipelining: load_rows issues this thread's global loads (16-byte
+// chunk t % 16 of rows 4 (t / 16) .. + 3; `row_ptr(rho)` must give a readable
+// row), put_rows writes them row-major into `rm` and transposed into `tr`
+// (either may be null).
 template <typename RowPtr>
 __device__ __forceinline__ void load_rows(RowPtr row_ptr, u32x4 (&w)[4]) {
   const int dg = threadIdx.x & 15, rc = threadIdx.x >> 4;
