@@ -168,24 +168,43 @@ struct Chunk {
   bool ok;
 };
 
-template <int EC>
+//
+// MERGE: a chunk may also span several passes.  The passes of one (seq, key
+// block) segment hold consecutive runs of its entries, so when a pass holds
+// fewer than EC entries, the passes that follow it in the workgroup's share
+// and continue the same run join its chunk while the total fits in EC.
+template <int EC, bool MERGE>
+__device__ __forceinline__ PassDesc take_pass(int pi, PassIter& it, const PassDesc* __restrict__ passes) {
+  PassDesc D = passes[pi];
+  if constexpr (MERGE) {
+    while (D.cnt < EC && it.p + 1 < it.end) {
+      const PassDesc E = passes[it.p + 1];
+      if (E.seq != D.seq || E.blk != D.blk || E.start != D.start + D.cnt || D.cnt + E.cnt > EC) break;
+      ++it.p;
+      D.cnt += E.cnt;
+    }
+  }
+  return D;
+}
+
+template <int EC, bool MERGE = false>
 __device__ __forceinline__ Chunk first_chunk(PassIter& it, const PassDesc* __restrict__ passes) {
   Chunk c{};
   const int pi = it.next();
   c.ok = pi >= 0;
-  if (c.ok) c.D = passes[pi];
+  if (c.ok) c.D = take_pass<EC, MERGE>(pi, it, passes);
   c.cb = 0;
   return c;
 }
 
-template <int EC>
+template <int EC, bool MERGE = false>
 __device__ __forceinline__ Chunk next_chunk(const Chunk& c, PassIter& it, const PassDesc* __restrict__ passes) {
   Chunk n = c;
   n.cb += EC;
   if (n.cb >= c.D.cnt) {
     const int pi = it.next();
     n.ok = pi >= 0;
-    if (n.ok) n.D = passes[pi];
+    if (n.ok) n.D = take_pass<EC, MERGE>(pi, it, passes);
     n.cb = 0;
   }
   return n;
@@ -472,7 +491,8 @@ __global__ __launch_bounds__(kBT, 1) void bwd_main_kernel(
 // p_px = exp(z - LSE_px), the KL terms T ln(T / p_px) and g = w (p_px - T),
 // then dk_idx^T += q_idx^T g (per-block accumulators, as dK) and
 // dq_idx^T = k_idx^T g^T per entry.  Chunks are EI index rows (entries) of
-// one pass, prefetched one chunk ahead like the main branch.
+// one key block, from one pass or from consecutive passes of the block,
+// prefetched one chunk ahead like the main branch.
 template <int G, int DIDX>
 __global__ __launch_bounds__(kBT, 1) void bwd_idx_kernel(
     const uint16_t* __restrict__ q_idx, const uint16_t* __restrict__ k_idx, const float* __restrict__ lsei2,
@@ -480,8 +500,9 @@ __global__ __launch_bounds__(kBT, 1) void bwd_idx_kernel(
     const int32_t* __restrict__ entries, const int32_t* __restrict__ segp,
     const PassDesc* __restrict__ passes, int B_c, int npairs, int q_begin, int q_count, int64_t dummy_slot,
     float* __restrict__ dqi_part, float* __restrict__ kl_part, float* __restrict__ dki_acc) {
-  constexpr int EPP = 256 / G;                 // entries per pass
-  constexpr int EI = EPP < 64 ? EPP : 64;      // index rows per chunk
+  // Index rows per chunk: 64 entries of one key block, from one pass (a pass
+  // holds 256 / G entries) or from consecutive passes of the block (G >= 8).
+  constexpr int EI = 64;
   constexpr int ZT = (EI + 31) / 32;           // 32-row tiles of index rows
   constexpr int KE = (EI + 15) / 16;           // 16-row steps of index rows
   constexpr int KSI = DIDX / 16;               // reduction steps of the index dot product
@@ -516,7 +537,7 @@ __global__ __launch_bounds__(kBT, 1) void bwd_idx_kernel(
       for (int e = 0; e < 16; ++e) unsafeAtomicAdd(dst + 32 * tt2 + acc_row(e, h), dkit[tt2][e]);
   };
 
-  Chunk cur = first_chunk<EI>(it, passes);
+  Chunk cur = first_chunk<EI, true>(it, passes);
   if (!cur.ok) return;
   const int rc = tid >> 4, dg = tid & 15, crow = tid & 63;
   u32x4 wqi[4];       // this thread's 16-byte pieces of index rows 4 rc .. + 3
@@ -559,7 +580,7 @@ __global__ __launch_bounds__(kBT, 1) void bwd_idx_kernel(
     chunk_entries(cur, eni, ent, enci);
     chunk_rows(cur, eni, ent, enci);
   }
-  Chunk nx = next_chunk<EI>(cur, it, passes);
+  Chunk nx = next_chunk<EI, true>(cur, it, passes);
 
   while (true) {
     const PassDesc D = cur.D;
@@ -688,7 +709,7 @@ __global__ __launch_bounds__(kBT, 1) void bwd_idx_kernel(
     __syncthreads();
     if (!nx.ok) break;
     cur = nx;
-    nx = next_chunk<EI>(cur, it, passes);
+    nx = next_chunk<EI, true>(cur, it, passes);
   }
   // (the prefetch registers stay live on the exit path; see the main branch)
   asm volatile("" ::"v"(wqi[0]), "v"(wqi[1]), "v"(wqi[2]), "v"(wqi[3]), "v"(pe_l));
