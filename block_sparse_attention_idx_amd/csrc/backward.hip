@@ -720,8 +720,10 @@ __global__ __launch_bounds__(kBT, 1) void bwd_idx_kernel(
 
 // ---------------------------------------------------------------- proxy LSE
 // One wave per workgroup: for every entry (query, slot) of a pass, the
-// log2-sum-exp2 of its proxy scores over the block's visible keys.
-// z^T = K^idx Q^idx^T with the keys on the row index, as in the forward.
+// log2-sum-exp2 of its proxy scores over the block's visible keys, 32
+// entries at a time (a pass of fewer entries takes the block's next passes
+// along).  z^T = K^idx Q^idx^T with the keys on the row index, as in the
+// forward.
 constexpr int kLseWgPerCu = 4;
 
 template <int DIDX>
@@ -736,7 +738,7 @@ __global__ __launch_bounds__(64) void proxy_lse_kernel(
   const int lane = threadIdx.x, n = lane & 31, h = lane >> 5;
   int cur_seq = -1, cur_blk = 0;
   for (int pi = it.next(); pi >= 0; pi = it.next()) {
-    const PassDesc D = passes[pi];
+    const PassDesc D = take_pass<32, true>(pi, it, passes);
     const int bat = D.seq / H_sel, r = D.seq - bat * H_sel;
     if (D.seq / H_sel != cur_seq / H_sel || cur_seq < 0 || D.blk != cur_blk) {
       // K^idx is shared by the groups of a sequence
