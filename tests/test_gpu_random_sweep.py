@@ -7,8 +7,9 @@ Q/K/V, drawn from a fixed seed so that every run checks the same cases.
 Forward: the selection is checked on sampled rows (edge rows and seeded random
 rows) by the margin rule of the other parity tests, and the output and LSE of
 those rows against the oracle's attention over the GPU's own selection.
-Backward (B_k = 128, small N): every gradient and the KL over all rows, with
-the tolerances of the backward parity tests.  Decode: the last token of every
+Backward (B_k = 128; small N, and N of 2.5K-8K where workgroups take runs of
+consecutive passes): every gradient and the KL over all rows, with the
+tolerances of the backward parity tests.  Decode: the last token of every
 sequence, selection and output, as in the decode parity tests.
 """
 from __future__ import annotations
@@ -62,6 +63,22 @@ DEC_SWEEP = [_draw(_RNG, False, 3000 + j).with_(dtype="bf16", q_chunk=0, N=int(_
              for j in range(6)]
 
 
+def _draw_joined(rng, seed: int) -> synth.Workload:
+    """Backward shapes where a group's passes outnumber the 256 workgroups at
+    least twice (N k >= 2 * 256 * 256 / G), so workgroups get runs of
+    consecutive passes of one key block and the index-branch chunks join
+    them."""
+    G = int(rng.choice([8, 16]))
+    k = int(rng.integers(3, 6))
+    N = max(int(rng.integers(2500, 4600)), 2 * 256 * 256 // (G * k) + int(rng.integers(0, 128)))
+    return synth.TINY.with_(name=f"sweepj{seed}", seed=seed, N=N, H_q=2 * G, H_kv=2, H_idx=0, B_k=128, k=k,
+                            d_idx=int(rng.choice([64, 128])), batch=1, q_chunk=0, dtype="bf16")
+
+
+_RNG_J = np.random.default_rng(20261203)
+BWD_JOINED = [_draw_joined(_RNG_J, 4000 + j) for j in range(3)]
+
+
 def _wid(w):
     return (f"N{w.N}_G{w.G}_Hs{w.H_sel}_bk{w.B_k}_k{w.k}_d{w.d_idx}_b{w.batch}_c{w.q_chunk}_{w.dtype}")
 
@@ -96,7 +113,7 @@ def test_forward_sweep(w):
         assert lmx <= 1e-3
 
 
-@pytest.mark.parametrize("w", BWD_SWEEP, ids=_wid)
+@pytest.mark.parametrize("w", BWD_SWEEP + BWD_JOINED, ids=_wid)
 def test_backward_sweep(w):
     log(f"sweep backward {_wid(w)}")
     t = device_inputs(w, DEV)
