@@ -5,6 +5,7 @@ import ctypes
 import os
 import re
 import subprocess
+import sys
 
 import pytest
 
@@ -224,3 +225,19 @@ def test_backward_validation(L):
     assert call(wsp=ctypes.c_void_p(0x100010)) == 4
     assert call(nbytes=size - 1) == 5
     assert call(d=dims(B_k=32)) == 3
+
+
+@pytest.mark.parametrize("args,env", [(["--gpus", "2"], {}), (["--gpus", "8"], {}), ([], {"WORLD_SIZE": "2"})])
+def test_bench_refuses_more_than_one_gpu(args, env):
+    """The measurement is a one-GPU build: asked for several GPUs (flag or a
+    launcher's WORLD_SIZE), bench.py exits with status 2 and says so before
+    touching torch or the GPU."""
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    e = dict(os.environ)
+    e.pop("WORLD_SIZE", None)
+    e.update(env)
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), *args], capture_output=True, text=True,
+                       env=e, timeout=60)
+    assert r.returncode == 2
+    assert "one GPU only" in r.stderr
+    assert r.stdout == ""
