@@ -98,6 +98,14 @@ def test_index_matches_brute_force(N, H, d, k, seed, B_k):
     assert np.array_equal(np.sign(M[~fin]), np.sign(Mb[~fin]))
     np.testing.assert_allclose(M[fin], Mb[fin], rtol=2e-6, atol=2e-5)
     bb, mb = brute_select(Mb, k)
+    # The margin decides which rows the GPU must match exactly: it is the
+    # fp64 brute force's gap between the (k-1)-th and k-th best non-local
+    # scores, over the larger magnitude.  Sorted values are continuous in the
+    # scores, so fp32 and fp64 agree to the scores' rounding even at near ties.
+    assert np.array_equal(np.isinf(marg), np.isinf(mb))
+    fm = np.isfinite(mb)
+    assert fm.any() == (k >= 2 and N > k * B_k)
+    np.testing.assert_allclose(marg[fm], mb[fm], rtol=0, atol=1e-5)
     sure = (mb > 1e-5) & (marg > 1e-5)
     assert sure.mean() > 0.9
     assert np.array_equal(bi[sure], bb[sure])
@@ -129,15 +137,56 @@ def test_forced_selection_matches_brute_force(N, H, d, k, first, window, seed, B
             free = min(k - len(forced), len(rest))
             order = sorted(rest, key=lambda b: (-Mb[i, r, b], b))
             cand = [Mb[i, r, b] for b in order]
+            # margin: the gap between the last free choice and the best block
+            # left out; +inf when no free slot or no block is left out
             if free < len(cand) and free > 0:
                 a, b2 = cand[free - 1], cand[free]
-                if (a - b2) / max(abs(a), abs(b2), 1e-6) <= 1e-5:
+                want = (a - b2) / max(abs(a), abs(b2), 1e-6)
+                assert abs(marg[r, i] - want) <= 1e-5, (r, i, marg[r, i], want)
+                if want <= 1e-5:
                     continue                            # near tie: fp32 vs fp64 order may differ
+            else:
+                assert marg[r, i] == np.inf, (r, i, marg[r, i])
             assert set(got) == forced | set(order[:free]), (r, i)
             assert len(got) == min(k, L + 1)
             checked += 1
     assert checked > 0.9 * H * N
     assert np.isfinite(marg).sum() + np.isinf(marg).sum() == marg.size   # no NaN margins
+
+
+def test_margin_exact_values():
+    """Hand-built score rows whose margin is known exactly: the (k-1)-th and
+    k-th best non-local scores c_{k-1}, c_k give (c_{k-1} - c_k) /
+    max(|c_{k-1}|, |c_k|, 1e-6).  Rows cover positive and negative scores,
+    the 1e-6 floor, a tie (margin 0, smaller id kept), a forced block (+inf
+    score) taking a slot, and too few candidates (+inf)."""
+    inf = np.inf
+    B_k = 128
+    cases = [
+        # scores of blocks 0..L-1, k, expected margin, expected ids
+        ([3.0, -1.0, 2.0, 0.5, 2.5], 3, 0.5 / 2.5, [0, 4, 5]),
+        ([-1.0, -4.0, -2.0], 2, 1.0 / 2.0, [0, 3]),
+        ([-1.0, -4.0, -2.0], 3, 2.0 / 4.0, [0, 2, 3]),
+        ([1e-7, 0.0, -1e-7], 2, 1e-7 / 1e-6, [0, 3]),
+        ([0.25, 1.0, 0.25, -3.0], 3, 0.0, [0, 1, 4]),
+        ([inf, 3.0, 1.0, 2.0], 3, 1.0 / 3.0, [0, 1, 4]),
+        ([4.0, 8.0], 3, inf, [0, 1, 2]),
+        ([4.0, 8.0, 1.0], 1, inf, [3]),
+    ]
+    for scores, k, want, ids in cases:
+        L = len(scores)
+        M = np.full((1, 1, L + 2), -inf, np.float32)
+        M[0, 0, :L] = scores
+        M[0, 0, L] = inf
+        bi, marg = oracle.select(M, np.array([L * B_k + 5]), B_k, k)
+        got = float(marg[0, 0])
+        if np.isinf(want):
+            assert got == inf, (scores, k, got)
+        else:
+            # the scores are stored in fp32 (1e-7 is not exact there); the
+            # margin is fp64 arithmetic on them
+            assert abs(got - want) <= 1e-7 * max(1.0, abs(want)), (scores, k, got, want)
+        assert bi[0, 0].tolist() == ids + [-1] * (k - len(ids)), (scores, k, bi[0, 0])
 
 
 def test_window_selection_closed_form():
