@@ -270,7 +270,7 @@ int msa_combine(const msa_dims* dims, const int32_t* block_idx, const void* o_pa
   hipError_t e = msa::launch_combine(block_idx, static_cast<const uint16_t*>(o_part), lse_part,
                                      dims->batch, dims->N, HS(dims), GS(dims), dims->k, q_begin,
                                      q_count, static_cast<uint16_t*>(o), lse,
-                                     static_cast<hipStream_t>(stream));
+                                     static_cast<hipStream_t>(stream), dims->B_k);
   return e == hipSuccess ? MSA_OK : hip_fail(e);
 }
 
@@ -609,7 +609,7 @@ int msa_forward(const msa_dims* dims, const msa_opts* opts, const void* q, const
                                 sl2, osc, offs, ents, sched, qb, qn, opart, lpart, s, dims->B_k);
     if (e != hipSuccess) return hip_fail(e);
     e = msa::launch_combine(bi, opart, lpart, dims->batch, dims->N, HS(dims), GS(dims), dims->k,
-                            qb, qn, static_cast<uint16_t*>(o), lse, s);
+                            qb, qn, static_cast<uint16_t*>(o), lse, s, dims->B_k);
     if (e != hipSuccess) return hip_fail(e);
   }
   return MSA_OK;

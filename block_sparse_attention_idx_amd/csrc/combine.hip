@@ -4,6 +4,10 @@
 // log-sum-exp merge).  For query i and head h of group r, over the slots s
 // whose block id is valid:
 //     LSE = ln sum_s exp(lse_s),   O = sum_s exp(lse_s - LSE) * Obar_s.
+// A slot is valid when its id lies in [0, floor(i / B_k)], the same test the
+// inversion applies: the attention pass never writes the partials of any
+// other slot (-1 padding, or an out-of-range id the inversion skipped and
+// counted), so those partials are never read.
 //
 // A pure streaming kernel.  The partials of one (query, group) are one
 // contiguous k * G * d_h bf16 slab; a workgroup of 256 threads owns
@@ -25,7 +29,7 @@ template <int G, int KMAX>
 __global__ __launch_bounds__(kCombThreads) void combine_kernel(
     const int32_t* __restrict__ block_idx, const uint16_t* __restrict__ o_part,
     const float* __restrict__ lse_part, int64_t N, int H_kv, int k, int64_t q_begin,
-    int64_t q_count, int64_t rows_total, uint16_t* __restrict__ o, float* __restrict__ lse) {
+    int64_t q_count, int64_t rows_total, int bks, uint16_t* __restrict__ o, float* __restrict__ lse) {
   constexpr int TPQ = 16 * G;              // threads per (query, group)
   constexpr int QPW = kCombThreads / TPQ;  // (query, group) pairs per workgroup
   const int t = threadIdx.x;
@@ -44,12 +48,15 @@ __global__ __launch_bounds__(kCombThreads) void combine_kernel(
   const int r = static_cast<int>(seq % H_kv);
   const int32_t* sel = block_idx + f * k;
   const int64_t base = f * k;  // slot 0 of this (query, group)
+  // the row's local block: the largest id a slot may hold (bks < 0: rows of
+  // one decode step, whose ids the library itself wrote, are not checked)
+  const uint32_t lmax = bks < 0 ? 0x7FFFFFFFu : static_cast<uint32_t>((q_begin + row) >> bks);
 
   bool valid[KMAX];
   float l[KMAX];
   u32x4 v[KMAX];
 #pragma unroll
-  for (int s = 0; s < KMAX; ++s) valid[s] = s < k && sel[s] >= 0;
+  for (int s = 0; s < KMAX; ++s) valid[s] = s < k && static_cast<uint32_t>(sel[s]) <= lmax;
 #pragma unroll
   for (int s = 0; s < KMAX; ++s) {
     v[s] = u32x4{0u, 0u, 0u, 0u};
@@ -70,7 +77,9 @@ __global__ __launch_bounds__(kCombThreads) void combine_kernel(
     l[s] = valid[s] ? __builtin_amdgcn_exp2f((l[s] - mx) * kLog2e) : 0.f;
     sum += l[s];
   }
-  const float inv = 1.f / sum;
+  // a row left with no valid slot (a caller's selection may hold none) gets
+  // O = 0 and LSE = -inf
+  const float inv = sum > 0.f ? 1.f / sum : 0.f;
 
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -92,41 +101,47 @@ __global__ __launch_bounds__(kCombThreads) void combine_kernel(
 template <int G, int KMAX>
 hipError_t launch_gk(const int32_t* block_idx, const uint16_t* o_part, const float* lse_part,
                      int batch, int64_t N, int H_kv, int k, int64_t q_begin, int64_t q_count,
-                     uint16_t* o, float* lse, hipStream_t stream) {
+                     int bks, uint16_t* o, float* lse, hipStream_t stream) {
   constexpr int QPW = kCombThreads / (16 * G);
   const int64_t rows_total = static_cast<int64_t>(batch) * H_kv * q_count;
   const int64_t nx = (rows_total + QPW - 1) / QPW;
   const int64_t grid = (nx + kXcds - 1) / kXcds * kXcds;  // see the kernel
   hipLaunchKernelGGL((combine_kernel<G, KMAX>), dim3(static_cast<unsigned>(grid)),
                      dim3(kCombThreads), 0, stream, block_idx, o_part, lse_part, N, H_kv, k,
-                     q_begin, q_count, rows_total, o, lse);
+                     q_begin, q_count, rows_total, bks, o, lse);
   return hipGetLastError();
 }
 
 template <int G>
 hipError_t launch_g(const int32_t* block_idx, const uint16_t* o_part, const float* lse_part,
                     int batch, int64_t N, int H_kv, int k, int64_t q_begin, int64_t q_count,
-                    uint16_t* o, float* lse, hipStream_t stream) {
+                    int bks, uint16_t* o, float* lse, hipStream_t stream) {
   if (k <= 4)
-    return launch_gk<G, 4>(block_idx, o_part, lse_part, batch, N, H_kv, k, q_begin, q_count, o, lse, stream);
+    return launch_gk<G, 4>(block_idx, o_part, lse_part, batch, N, H_kv, k, q_begin, q_count, bks, o, lse, stream);
   if (k <= 8)
-    return launch_gk<G, 8>(block_idx, o_part, lse_part, batch, N, H_kv, k, q_begin, q_count, o, lse, stream);
+    return launch_gk<G, 8>(block_idx, o_part, lse_part, batch, N, H_kv, k, q_begin, q_count, bks, o, lse, stream);
   if (k <= 16)
-    return launch_gk<G, 16>(block_idx, o_part, lse_part, batch, N, H_kv, k, q_begin, q_count, o, lse, stream);
-  return launch_gk<G, 32>(block_idx, o_part, lse_part, batch, N, H_kv, k, q_begin, q_count, o, lse, stream);
+    return launch_gk<G, 16>(block_idx, o_part, lse_part, batch, N, H_kv, k, q_begin, q_count, bks, o, lse, stream);
+  return launch_gk<G, 32>(block_idx, o_part, lse_part, batch, N, H_kv, k, q_begin, q_count, bks, o, lse, stream);
 }
 
 }  // namespace
 
 hipError_t launch_combine(const int32_t* block_idx, const uint16_t* o_part, const float* lse_part,
                           int batch, int64_t N, int H_kv, int G, int k, int64_t q_begin,
-                          int64_t q_count, uint16_t* o, float* lse, hipStream_t stream) {
+                          int64_t q_count, uint16_t* o, float* lse, hipStream_t stream, int bk) {
+  int bks = -1;
+  if (bk > 0) {
+    bks = 0;
+    while ((1 << bks) < bk) ++bks;
+    if ((1 << bks) != bk) return hipErrorInvalidValue;
+  }
   switch (G) {
-    case 1: return launch_g<1>(block_idx, o_part, lse_part, batch, N, H_kv, k, q_begin, q_count, o, lse, stream);
-    case 2: return launch_g<2>(block_idx, o_part, lse_part, batch, N, H_kv, k, q_begin, q_count, o, lse, stream);
-    case 4: return launch_g<4>(block_idx, o_part, lse_part, batch, N, H_kv, k, q_begin, q_count, o, lse, stream);
-    case 8: return launch_g<8>(block_idx, o_part, lse_part, batch, N, H_kv, k, q_begin, q_count, o, lse, stream);
-    case 16: return launch_g<16>(block_idx, o_part, lse_part, batch, N, H_kv, k, q_begin, q_count, o, lse, stream);
+    case 1: return launch_g<1>(block_idx, o_part, lse_part, batch, N, H_kv, k, q_begin, q_count, bks, o, lse, stream);
+    case 2: return launch_g<2>(block_idx, o_part, lse_part, batch, N, H_kv, k, q_begin, q_count, bks, o, lse, stream);
+    case 4: return launch_g<4>(block_idx, o_part, lse_part, batch, N, H_kv, k, q_begin, q_count, bks, o, lse, stream);
+    case 8: return launch_g<8>(block_idx, o_part, lse_part, batch, N, H_kv, k, q_begin, q_count, bks, o, lse, stream);
+    case 16: return launch_g<16>(block_idx, o_part, lse_part, batch, N, H_kv, k, q_begin, q_count, bks, o, lse, stream);
     default: return hipErrorInvalidValue;
   }
 }

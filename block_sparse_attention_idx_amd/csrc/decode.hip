@@ -407,7 +407,7 @@ hipError_t launch_decode(const uint16_t* q, const uint16_t* q_idx, const uint16_
   }
   if (e != hipSuccess) return e;
   // One query row per sequence: the combine's output rows [batch][1][H_q].
-  return launch_combine(block_idx, o_part, lse_part, batch, 1, H_sel, G, kslots, 0, 1, o, lse, stream);
+  return launch_combine(block_idx, o_part, lse_part, batch, 1, H_sel, G, kslots, 0, 1, o, lse, stream, 0);
 }
 
 }  // namespace msa

@@ -158,9 +158,11 @@ hipError_t launch_sparse_attn(const void* q, const void* k, const void* v, bool 
                               int64_t q_count, uint16_t* o_part, float* lse_part,
                               hipStream_t stream, int bk = kBk);
 
+// Slots whose id is outside [0, floor(i / bk)] (i the query's position) are
+// left out, like the inversion leaves them out; bk = 0 checks only id >= 0.
 hipError_t launch_combine(const int32_t* block_idx, const uint16_t* o_part, const float* lse_part,
                           int batch, int64_t N, int H_kv, int G, int k, int64_t q_begin,
-                          int64_t q_count, uint16_t* o, float* lse, hipStream_t stream);
+                          int64_t q_count, uint16_t* o, float* lse, hipStream_t stream, int bk);
 
 // Dense causal GQA attention (bf16), query rows [q_begin, q_begin + q_count):
 // o [batch][N][H_q][d_h], lse [batch][N][H_q] (natural log; may be null).

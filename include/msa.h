@@ -217,7 +217,11 @@ int msa_sparse_attn_fwd(const msa_dims *dims, const msa_opts *opts, const void *
  * msa_combine -- split-K log-sum-exp merge of the partials of each query
  * ("MiniMax Sparse Attention (MSA)", Deep Dive > KV-Outer Sparse Attention,
  *  step 6): LSE = ln sum_s exp(lse_s), O = sum_s exp(lse_s - LSE) * Obar_s over
- *  the slots s whose block_idx entry is >= 0.
+ *  the valid slots s of each row: those whose block_idx entry b satisfies
+ *  0 <= b <= floor(i / B_k), the test msa_invert_blocks applies.  Other
+ *  slots (-1 padding, out-of-range ids) are never read, so their o_part and
+ *  lse_part contents do not matter.  A row with no valid slot gets O = 0 and
+ *  LSE = -inf.
  *
  *   block_idx  int32 [batch][H_sel][q_count][k]
  *   o_part, lse_part  as written by msa_sparse_attn_fwd

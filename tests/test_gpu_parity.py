@@ -262,6 +262,53 @@ def test_combine_parity_random_partials():
     assert lmx <= 1e-5
 
 
+def test_combine_never_reads_invalid_slots():
+    """Partial buffers prefilled with NaN: slots the attention pass does not
+    write (-1 padding, an id past the row's local block, a negative id, a row
+    with no valid slot) must never reach O.  O equals a run on zeroed buffers
+    bit for bit and the oracle on the selection with those slots dropped."""
+    w = TINY.with_(N=1500, k=6)
+    log(f"NaN-poisoned partials N={w.N} H_q={w.H_q} H_kv={w.H_kv} k={w.k}")
+    t = device_inputs(w, DEV)
+    d, o = dims_of(w), opts_of(w)
+    rows = np.arange(w.N)
+    sel, _, _ = oracle_index_rows(w, rows)
+    sel = sel.copy()
+    assert (sel == -1).any()                     # early rows are padded
+    sel[0, 700, 0] = 11                          # past the row's local block (5)
+    sel[1, 900, 2] = -7                          # negative, not the -1 padding
+    sel[0, 1000, :] = -1                         # no valid slot at all
+    bi = torch.from_numpy(sel[None]).to(DEV)
+    off, ent, sched = msa.msa_invert_blocks(d, bi)
+    assert msa.msa_invert_status(sched) == 2
+    shp = (1, w.H_sel, w.N, w.k, w.G_sel)
+    outs = []
+    for fill in (float("nan"), 0.0):
+        op = torch.full(shp + (w.d_h,), fill, dtype=torch.bfloat16, device=DEV)
+        lp = torch.full(shp, fill, dtype=torch.float32, device=DEV)
+        msa.msa_sparse_attn_fwd(d, o, t["q"], t["k"], t["v"], off, ent, sched, o_part=op, lse_part=lp)
+        out, lse = msa.msa_combine(d, bi, op, lp, want_lse=True)
+        torch.cuda.synchronize()
+        outs.append((out.view(torch.int16).cpu().numpy(), lse.cpu().numpy()))
+    (o_nan, l_nan), (o_zero, l_zero) = outs
+    assert np.array_equal(o_nan, o_zero)
+    assert np.array_equal(l_nan.view(np.int32), l_zero.view(np.int32))
+    of = synth.bf16_bits_to_f32(o_nan.view(np.uint16))[0]
+    assert np.isfinite(of).all()
+    G = w.G_sel
+    assert (of[1000, 0:G] == 0).all() and np.isneginf(l_nan[0, 1000, 0:G]).all()
+    clean = sel.copy()
+    clean[0, 700, 0] = -1
+    clean[1, 900, 2] = -1
+    keep = np.setdiff1d(rows, [1000])
+    O, L = oracle.attention(w.N, w.B_k, keep, synth.host_rows(w, "q", keep), synth.host_all(w, "k"),
+                            synth.host_all(w, "v"), np.ascontiguousarray(clean[:, keep]))
+    mx, mn = err_stats(of[keep], O, label="O")
+    assert mx <= 2e-2 and mn <= 2e-3
+    lmx, _ = err_stats(l_nan[0, keep], L)
+    assert lmx <= 1e-3
+
+
 # --------------------------------------------------------------------------- whole forward
 
 FWD_CASES = [TINY, TINY.with_(N=1000, k=5), TINY.with_(N=2304, k=4, q_chunk=512),
