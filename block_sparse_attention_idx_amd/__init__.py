@@ -28,8 +28,11 @@ EXPORTS = (
     "msa_invert_workspace_size", "msa_invert_blocks", "msa_invert_status",
     "msa_sparse_attn_fwd", "msa_combine", "msa_workspace_size", "msa_forward",
     "msa_dense_attn_fwd", "msa_decode_workspace_size", "msa_decode", "msa_index_topk_forced",
-    "msa_window_select", "msa_backward_workspace_size", "msa_backward",
+    "msa_window_select", "msa_backward_workspace_size", "msa_backward", "msa_decode_static",
 )
+
+# Size of the device scratch msa_decode_static works in (MSA_STATIC_SCRATCH_BYTES).
+STATIC_SCRATCH_BYTES = 64 * 1024 * 1024
 
 
 class MSAError(RuntimeError):
@@ -111,6 +114,7 @@ def lib():
             "msa_window_select": ([D, I64, I64, P, P], ctypes.c_int),
             "msa_backward_workspace_size": ([D, O, ctypes.POINTER(SZ)], ctypes.c_int),
             "msa_backward": ([D, O, ctypes.c_float] + [P] * 16 + [SZ, P], ctypes.c_int),
+            "msa_decode_static": ([D, O, P, P, P, P, P, P, P, P, P, P], ctypes.c_int),
         }
         for name, (args, res) in sig.items():
             f = getattr(L, name)
@@ -337,6 +341,24 @@ def msa_decode(dims: msa_dims, opts: msa_opts, q, q_idx, k, v, k_idx, o=None, ls
                                 _p(k_idx), _p(seq_lens), _p(o), _p(lse), _p(block_idx_out), _p(workspace),
                                 workspace.numel() * workspace.element_size(), _stream(q)),
                "msa_decode")
+    return o, lse, block_idx_out
+
+
+def msa_decode_static(dims: msa_dims, opts: msa_opts, q, q_idx, k, v, k_idx, o=None, lse=None,
+                      block_idx_out=None, want_lse: bool = False, seq_lens=None):
+    """msa_decode without a workspace: the library's static device scratch is
+    used instead (for callers that cannot allocate).  Arguments and result as
+    for msa_decode; steps needing more than STATIC_SCRATCH_BYTES raise."""
+    import torch
+    if o is None:
+        o = _empty((dims.batch, dims.H_q, dims.d_h), torch.bfloat16, q)
+    if lse is None and want_lse:
+        lse = _empty((dims.batch, dims.H_q), torch.float32, q)
+    with _dev(q):
+        _check(lib().msa_decode_static(ctypes.byref(dims), ctypes.byref(opts), _p(q), _p(q_idx), _p(k),
+                                       _p(v), _p(k_idx), _p(seq_lens), _p(o), _p(lse), _p(block_idx_out),
+                                       _stream(q)),
+               "msa_decode_static")
     return o, lse, block_idx_out
 
 

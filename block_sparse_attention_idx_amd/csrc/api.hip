@@ -5,12 +5,42 @@
 #include <math.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "msa.h"
 #include "msa_internal.h"
+
+// Device-resident scratch of msa_decode_static, for callers that cannot
+// allocate.  In host code `scratch` names a host-side stand-in, never the
+// device copy: only the address hipGetSymbolAddress returns is passed on.
+static __device__ __align__(256) uint8_t scratch[MSA_STATIC_SCRATCH_BYTES];
 
 namespace {
 
 thread_local int g_last_hip_error = 0;
+
+// Per-device address of `scratch`, looked up once per device (with that
+// device current) on the first msa_decode_static call there.
+constexpr int kMaxDevices = 64;
+void* g_scratch_ptr[kMaxDevices] = {};
+std::mutex g_scratch_mu;
+
+hipError_t scratch_address(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
 
 int hip_fail(hipError_t e) {
   g_last_hip_error = static_cast<int>(e);
@@ -144,6 +174,7 @@ const char* msa_status_string(int status) {
     case MSA_ERR_ALIGN: return "device pointer not 16-byte aligned";
     case MSA_ERR_WORKSPACE: return "workspace too small";
     case MSA_ERR_HIP: return "HIP runtime error";
+    case MSA_ERR_SCRATCH: return "problem needs more than the static scratch (MSA_STATIC_SCRATCH_BYTES)";
     default: return "unknown status";
   }
 }
@@ -369,6 +400,30 @@ int msa_decode(const msa_dims* dims, const msa_opts* opts, const void* q, const 
       reinterpret_cast<uint16_t*>(ws + L.off_opart), reinterpret_cast<float*>(ws + L.off_lpart),
       static_cast<uint16_t*>(o), lse, static_cast<hipStream_t>(stream), dims->B_k, seq_lens);
   return e == hipSuccess ? MSA_OK : hip_fail(e);
+}
+
+int msa_decode_static(const msa_dims* dims, const msa_opts* opts, const void* q, const void* q_idx,
+                      const void* k, const void* v, const void* k_idx, const int32_t* seq_lens,
+                      void* o, float* lse, int32_t* block_idx_out, void* stream) {
+  int st = check_decode(dims, opts);
+  if (st) return st;
+  if (decode_layout(dims).total > static_cast<size_t>(MSA_STATIC_SCRATCH_BYTES)) return MSA_ERR_SCRATCH;
+  // (msa_decode checks pointers and alignment before it enqueues anything;
+  // these are the same checks, made before the scratch lookup touches the
+  // device)
+  if (!q || !q_idx || !k || !v || !k_idx || !o) return MSA_ERR_NULL;
+  if (misaligned(q) || misaligned(q_idx) || misaligned(k) || misaligned(v) || misaligned(k_idx) ||
+      misaligned(o) || (lse && misaligned(lse)) || (block_idx_out && misaligned(block_idx_out)) ||
+      (seq_lens && (reinterpret_cast<uintptr_t>(seq_lens) & 3u)))
+    return MSA_ERR_ALIGN;
+  void* ws = nullptr;
+  const hipError_t e = scratch_address(&ws);
+  if (e != hipSuccess) return hip_fail(e);
+  // Every kernel of the step writes the scratch regions it later reads
+  // (scores of the blocks before each sequence's local block, the selection,
+  // the partials of the valid slots), so nothing needs clearing between calls.
+  return msa_decode(dims, opts, q, q_idx, k, v, k_idx, seq_lens, o, lse, block_idx_out, ws,
+                    static_cast<size_t>(MSA_STATIC_SCRATCH_BYTES), stream);
 }
 
 namespace {

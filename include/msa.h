@@ -68,7 +68,9 @@ enum msa_status_code {
     MSA_ERR_UNSUPPORTED = 3, /* valid but outside the supported shapes above */
     MSA_ERR_ALIGN = 4,       /* a device pointer is not 16-byte aligned */
     MSA_ERR_WORKSPACE = 5,   /* workspace smaller than the size query returned */
-    MSA_ERR_HIP = 6          /* a HIP runtime call failed (see msa_last_hip_error) */
+    MSA_ERR_HIP = 6,         /* a HIP runtime call failed (see msa_last_hip_error) */
+    MSA_ERR_SCRATCH = 7      /* msa_decode_static: the step needs more scratch than
+                                MSA_STATIC_SCRATCH_BYTES */
 };
 
 enum msa_dtype_code {
@@ -301,6 +303,28 @@ int msa_decode_workspace_size(const msa_dims *dims, const msa_opts *opts, size_t
 int msa_decode(const msa_dims *dims, const msa_opts *opts, const void *q, const void *q_idx,
                const void *k, const void *v, const void *k_idx, const int32_t *seq_lens, void *o,
                float *lse, int32_t *block_idx_out, void *workspace, size_t ws_bytes, void *stream);
+
+/*
+ * msa_decode_static -- msa_decode for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): the same step, the same kernels and results, with the
+ * workspace taken from a scratch array of MSA_STATIC_SCRATCH_BYTES that the
+ * library holds in device memory, one per GPU, for the life of the process.
+ * The call allocates nothing; the caller still passes every input and output.
+ *
+ *   arguments  as for msa_decode, without workspace and ws_bytes
+ * Returns MSA_ERR_SCRATCH, before anything is enqueued, when
+ * msa_decode_workspace_size exceeds MSA_STATIC_SCRATCH_BYTES (with H_sel 4,
+ * k 16, G_sel 16 a step fits up to batch 237 at N = 128K, 168 at N = 1M).
+ * The first call on a device looks the array's address up (with that device
+ * current).  All calls on one GPU share its array: calls that may overlap on
+ * one GPU (other streams, other host threads) race and must be serialised by
+ * the caller; calls on one stream are ordered and safe.
+ */
+#define MSA_STATIC_SCRATCH_BYTES (64 * 1024 * 1024)
+int msa_decode_static(const msa_dims *dims, const msa_opts *opts, const void *q, const void *q_idx,
+                      const void *k, const void *v, const void *k_idx, const int32_t *seq_lens,
+                      void *o, float *lse, int32_t *block_idx_out, void *stream);
 
 /*
  * msa_backward_workspace_size / msa_backward -- the training backward pass:

@@ -164,6 +164,27 @@ def test_decode_validation(L):
     assert L.msa_decode_workspace_size(ctypes.byref(d), ctypes.byref(o), None) == 1
 
 
+def test_decode_static_validation(L):
+    """msa_decode_static: the decode checks, then the static scratch limit, all
+    before the device is touched."""
+    o = msa.make_opts()
+    call = lambda d, o=o, q=FAKE, out=FAKE, lse=None: L.msa_decode_static(
+        ctypes.byref(d), ctypes.byref(o), q, FAKE, FAKE, FAKE, FAKE, None, out, lse, None, None)
+    big = dims(N=1 << 20, H_q=64, H_kv=4, d_idx=128, k=16, batch=600)
+    n = ctypes.c_size_t(0)
+    assert L.msa_decode_workspace_size(ctypes.byref(big), ctypes.byref(o), ctypes.byref(n)) == 0
+    assert n.value > msa.STATIC_SCRATCH_BYTES
+    assert call(big) == 7
+    assert L.msa_status_string(7).startswith(b"problem needs more than the static scratch")
+    assert call(dims(), msa.make_opts(dtype="fp8")) == 3
+    assert call(dims(k=0)) == 2
+    assert call(dims(), q=None) == 1
+    assert call(dims(), out=ODD) == 4
+    assert call(dims(), lse=ODD) == 4
+    assert L.msa_decode_static(None, ctypes.byref(o), FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, None,
+                               None, None) == 1
+
+
 @pytest.mark.parametrize("H_idx,status", [(-1, 2), (3, 2), (6, 2), (16, 0), (8, 0), (4, 0), (0, 0)])
 def test_index_head_validation(L, H_idx, status):
     """H_idx: a multiple of H_kv = 2 dividing H_q = 16 (G_sel a power of two
