@@ -13,8 +13,10 @@ fraction against the published peaks and against peaks measured on this GPU by
 a probe for the same access patterns, the dense causal GQA kernel on the same
 Q, K, V (the baseline MSA's speedup is quoted against), one decode step over 8
 caches of the workload's shape, the training backward (msa_backward) on the
-forward just timed, and the CPU oracle timed on a bounded sample of the same
-workload.
+forward just timed, the same measurements of the forward for the 128K workload
+with fp8 Q/K/V (`fp8`) and the 1M-token workload in 32K-row chunks
+(`long_context`), and the CPU oracle timed on a bounded sample of the same
+workload plus over every row of the tiny and 16K workloads.
 """
 from __future__ import annotations
 
@@ -103,6 +105,198 @@ MEASURED_PEAK_OF = {"index_topk": "mfma_bf16_TFLOPs", "invert_blocks": "hbm_copy
                     "sparse_attn_fwd": "hbm_rand4k_mixed_GBs", "combine": "hbm_seq_read_GBs"}
 
 
+def path_accounting(acc, synth, w, sel):
+    """Work of one forward from the selection it made (sel [batch * H_kv, N, k]):
+    index and main-branch FLOPs and each kernel's algorithmic bytes -- the
+    inversion reads and writes 4 B per slot, the attention writes the partials
+    and reads each entry, Q once and K, V once per selected (group, block), the
+    combine reads the partials and the selection and writes O."""
+    f_idx = acc.index_flops(0, w.N, w.H_kv, w.d_idx, w.B_k, batch=w.batch)
+    f_main = acc.main_flops(sel, 0, w.N, w.B_k, w.G, w.d_h)
+    valid_slots = int((sel >= 0).sum())
+    seq = np.arange(sel.shape[0], dtype=np.int64)[:, None, None]
+    bins = int(np.count_nonzero(np.bincount((seq * w.B + sel)[sel >= 0], minlength=sel.shape[0] * w.B)))
+    eb = 1 if w.dtype == "fp8" else 2
+    part = acc.partial_bytes(valid_slots, w.G, w.d_h)
+    return {
+        "f_idx": f_idx, "f_main": f_main, "valid_slots": valid_slots,
+        "attn": (part + 4 * valid_slots + w.batch * w.N * w.H_q * w.d_h * eb
+                 + bins * 2 * w.B_k * w.d_h * eb),
+        "comb": part + 4 * w.batch * w.H_kv * w.N * w.k + w.batch * w.N * w.H_q * w.d_h * 2,
+        "inv": 4 * w.batch * w.H_kv * w.N * w.k + 4 * valid_slots,
+    }
+
+
+def kernel_table(kern, a):
+    """Per-kernel time, algorithmic work and fraction of the published peak."""
+    kernels = {
+        "index_topk": {"ms": kern["index_topk"], "bound": "mfma", "flops": a["f_idx"],
+                       "achieved": a["f_idx"] / kern["index_topk"] / 1e9, "peak": PEAK_BF16_TFLOPS,
+                       "unit": "TFLOP/s"},
+        "invert_blocks": {"ms": kern["invert_blocks"], "bound": "hbm", "bytes": a["inv"],
+                          "achieved": a["inv"] / kern["invert_blocks"] / 1e6,
+                          "peak": PEAK_HBM_GBS, "unit": "GB/s"},
+        "sparse_attn_fwd": {"ms": kern["sparse_attn_fwd"], "bound": "hbm", "bytes": a["attn"],
+                            "achieved": a["attn"] / kern["sparse_attn_fwd"] / 1e6,
+                            "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                            "mfma_tflops": a["f_main"] / kern["sparse_attn_fwd"] / 1e9},
+        "combine": {"ms": kern["combine"], "bound": "hbm", "bytes": a["comb"],
+                    "achieved": a["comb"] / kern["combine"] / 1e6, "peak": PEAK_HBM_GBS,
+                    "unit": "GB/s"},
+    }
+    for v in kernels.values():
+        v["frac"] = v["achieved"] / v["peak"]
+    return kernels
+
+
+def time_forward(msa, torch, fwd, steps, warmup, stream):
+    """Mean, median and minimum ms of `steps` calls after `warmup` calls, from
+    events recorded between consecutive calls on the launch stream."""
+    for _ in range(warmup):
+        fwd()
+    torch.cuda.synchronize()
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    evs[0].record(stream)
+    for j in range(steps):
+        fwd()
+        evs[j + 1].record(stream)
+    torch.cuda.synchronize()
+    per = sorted(evs[j].elapsed_time(evs[j + 1]) for j in range(steps))
+    return evs[0].elapsed_time(evs[-1]) / steps, float(np.median(per)), per[0]
+
+
+def time_chunked_kernels(msa, torch, d, o, t, w, bi_all, out, stream, dev, reps=1):
+    """Per-kernel times of the chunked forward, summed over its chunks: the
+    index branch once over all rows, then per chunk of q_chunk rows the chunk's
+    selection rows copied out, the inversion, the attention and the combine,
+    each bracketed by events on the launch stream (the steps msa_forward runs,
+    through the entry points)."""
+    qc = w.q_chunk
+    seqs = w.batch * w.H_kv
+    bi_c = torch.empty((w.batch, w.H_kv, qc, w.k), dtype=torch.int32, device=dev)
+    sb = max(msa.msa_invert_workspace_size(d, qb, min(qc, w.N - qb)) for qb in range(0, w.N, qc))
+    sched = torch.empty(((sb + 3) // 4,), dtype=torch.int32, device=dev)
+    offs = torch.empty((seqs * (w.B + 1),), dtype=torch.int32, device=dev)
+    ents = torch.empty((seqs * qc * w.k,), dtype=torch.int32, device=dev)
+    opart = torch.empty((seqs * qc * w.k * w.G * w.d_h,), dtype=torch.bfloat16, device=dev)
+    lpart = torch.empty((seqs * qc * w.k * w.G,), dtype=torch.float32, device=dev)
+    tot = {"index_topk": 0.0, "invert_blocks": 0.0, "sparse_attn_fwd": 0.0, "combine": 0.0}
+    for it in range(reps + 1):                 # pass 0 is a warmup
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        msa.msa_index_topk(d, t["q_idx"], t["k_idx"], block_idx=bi_all)
+        e1.record(stream)
+        marks = []
+        for qb in range(0, w.N, qc):
+            qn = min(qc, w.N - qb)
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+            sel = bi_c[:, :, :qn]
+            sel.copy_(bi_all[:, :, qb:qb + qn])
+            ev[0].record(stream)
+            msa.msa_invert_blocks(d, sel, qb, qn, blk_offsets=offs, blk_entries=ents, sched=sched)
+            ev[1].record(stream)
+            msa.msa_sparse_attn_fwd(d, o, t["q"], t["k"], t["v"], offs, ents, sched, qb, qn,
+                                    o_part=opart, lse_part=lpart)
+            ev[2].record(stream)
+            msa.msa_combine(d, sel, opart, lpart, qb, qn, o=out)
+            ev[3].record(stream)
+            marks.append(ev)
+        torch.cuda.synchronize()
+        if it == 0:
+            continue
+        tot["index_topk"] += e0.elapsed_time(e1) / reps
+        for ev in marks:
+            tot["invert_blocks"] += ev[0].elapsed_time(ev[1]) / reps
+            tot["sparse_attn_fwd"] += ev[1].elapsed_time(ev[2]) / reps
+            tot["combine"] += ev[2].elapsed_time(ev[3]) / reps
+    return tot
+
+
+def measure_workload(msa, acc, synth, torch, w, steps, warmup, dev):
+    """One more workload of the path, measured like the headline one: the
+    whole msa_forward (inputs resident in HBM), each kernel's time (the four
+    entry points, or the chunk loop through them), the work from the selection
+    made, and the dominant kernel's roofline."""
+    log(f"{w.name}: generating inputs on the device")
+    stream = torch.cuda.current_stream(dev)
+    t = {x: synth.device_tensor(w, x, dev) for x in ("q", "k", "v", "q_idx", "k_idx")}
+    d = msa.make_dims(w.batch, w.N, w.H_q, w.H_kv, w.d_h, w.d_idx, w.B_k, w.k)
+    s = synth.fp8_scale() if w.dtype == "fp8" else 1.0
+    o = msa.make_opts(w.dtype, q_scale=s, k_scale=s, v_scale=s, q_chunk=w.q_chunk)
+    out = torch.empty((w.batch, w.N, w.H_q, w.d_h), dtype=torch.bfloat16, device=dev)
+    bi = torch.empty((w.batch, w.H_kv, w.N, w.k), dtype=torch.int32, device=dev)
+    ws = torch.empty((msa.msa_workspace_size(d, o),), dtype=torch.uint8, device=dev)
+    fwd = lambda: msa.msa_forward(d, o, t["q"], t["k"], t["v"], t["q_idx"], t["k_idx"], o=out,
+                                  block_idx_out=bi, workspace=ws)
+    ms, med, mn = time_forward(msa, torch, fwd, steps, warmup, stream)
+    log(f"{w.name}: msa_forward {ms:.3f} ms/step (median {med:.3f}, min {mn:.3f})")
+    del ws
+    torch.cuda.empty_cache()
+    if w.q_chunk and w.q_chunk < w.N:
+        kern = time_chunked_kernels(msa, torch, d, o, t, w, bi, out, stream, dev)
+    else:
+        sb = msa.msa_invert_workspace_size(d, 0, w.N)
+        sched = torch.empty(((sb + 3) // 4,), dtype=torch.int32, device=dev)
+        offs = torch.empty((w.batch, w.H_kv, w.B + 1), dtype=torch.int32, device=dev)
+        ents = torch.empty((w.batch * w.H_kv * w.N * w.k,), dtype=torch.int32, device=dev)
+        opart = torch.empty((w.batch, w.H_kv, w.N, w.k, w.G, w.d_h), dtype=torch.bfloat16, device=dev)
+        lpart = torch.empty((w.batch, w.H_kv, w.N, w.k, w.G), dtype=torch.float32, device=dev)
+        names = ("index_topk", "invert_blocks", "sparse_attn_fwd", "combine")
+        kern = dict.fromkeys(names, 0.0)
+        for it in range(steps + 1):           # pass 0 is a warmup
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
+            e[0].record(stream)
+            msa.msa_index_topk(d, t["q_idx"], t["k_idx"], block_idx=bi)
+            e[1].record(stream)
+            msa.msa_invert_blocks(d, bi, blk_offsets=offs, blk_entries=ents, sched=sched)
+            e[2].record(stream)
+            msa.msa_sparse_attn_fwd(d, o, t["q"], t["k"], t["v"], offs, ents, sched,
+                                    o_part=opart, lse_part=lpart)
+            e[3].record(stream)
+            msa.msa_combine(d, bi, opart, lpart, o=out)
+            e[4].record(stream)
+            torch.cuda.synchronize()
+            if it:
+                for j, name in enumerate(names):
+                    kern[name] += e[j].elapsed_time(e[j + 1]) / steps
+    log(f"{w.name}: per kernel ms: " + ", ".join(f"{k} {v:.3f}" for k, v in kern.items()))
+    sel = bi.cpu().numpy().reshape(w.batch * w.H_kv, w.N, w.k)
+    del t, out, bi
+    torch.cuda.empty_cache()
+    a = path_accounting(acc, synth, w, sel)
+    kernels = kernel_table(kern, a)
+    dom = max(kernels, key=lambda n: kernels[n]["ms"])
+    dk = kernels[dom]
+    return {
+        "workload": w.name, "dtype": w.dtype, "N": w.N, "q_chunk": w.q_chunk, "steps": steps,
+        "warmup": warmup, "ms_per_step": ms, "ms_median": med, "ms_min": mn,
+        "tokens_s": w.batch * w.N / (ms * 1e-3),
+        "sparse_tflops": (a["f_idx"] + a["f_main"]) / (ms * 1e-3) / 1e12,
+        "index_flops": a["f_idx"], "main_flops": a["f_main"],
+        "roofline": {"kernel": dom, "bound": dk["bound"], "achieved": dk["achieved"], "peak": dk["peak"],
+                     "unit": dk["unit"], "frac": dk["frac"], "traffic": None},
+        "kernels": kernels,
+    }
+
+
+def cpu_full_run(oracle, synth, acc, w):
+    """The oracle over every row of a workload (index branch, then the main
+    branch on its selection), timed on this host."""
+    rows = np.arange(w.N)
+    qi = synth.host_rows(w, "q_idx", rows)
+    ki = synth.host_all(w, "k_idx")
+    qr = synth.host_rows(w, "q", rows)
+    K = synth.host_all(w, "k")
+    V = synth.host_all(w, "v")
+    c0 = time.perf_counter()
+    obi, _, _ = oracle.index_topk(w.N, w.B_k, w.k, rows, qi, ki)
+    oracle.attention(w.N, w.B_k, rows, qr, K, V, obi)
+    csec = time.perf_counter() - c0
+    flops = acc.index_flops(0, w.N, w.H_kv, w.d_idx, w.B_k) + acc.main_flops(obi, 0, w.N, w.B_k, w.G, w.d_h)
+    return {"workload": w.name, "rows": int(w.N), "seconds": csec, "value": w.N / csec,
+            "unit": "tokens/s", "gflops": flops / csec / 1e9}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -123,6 +317,12 @@ def main():
                          "sliding-window selections)")
     ap.add_argument("--no-backward", action="store_true",
                     help="skip the training backward pass (msa_backward) timing")
+    ap.add_argument("--no-fp8", action="store_true",
+                    help="skip the 128K forward with fp8 Q/K/V")
+    ap.add_argument("--no-long-context", action="store_true",
+                    help="skip the 1M-token forward in 32K-row chunks")
+    ap.add_argument("--no-cpu-full", action="store_true",
+                    help="skip the oracle over every row of the tiny and 16K workloads")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="first run one plain device-to-device copy of this many MiB (a kernel "
                          "of known traffic, to calibrate hardware byte counters)")
@@ -377,17 +577,8 @@ def main():
 
     # ---- work accounting from the selection actually made
     sel = bi.cpu().numpy().reshape(w.batch * w.H_kv, w.N, w.k)
-    f_idx = acc.index_flops(0, w.N, w.H_kv, w.d_idx, w.B_k, batch=w.batch)
-    f_main = acc.main_flops(sel, 0, w.N, w.B_k, w.G, w.d_h)
-    valid_slots = int((sel >= 0).sum())
-    bins = len(np.unique((np.arange(sel.shape[0])[:, None, None] * (w.B + 1) + sel)[sel >= 0]))
-    eb = 1 if w.dtype == "fp8" else 2
-    part = acc.partial_bytes(valid_slots, w.G, w.d_h)
-    bytes_attn = (part + 4 * valid_slots                       # partials out, entries in
-                  + w.batch * w.N * w.H_q * w.d_h * eb         # Q once
-                  + bins * 2 * w.B_k * w.d_h * eb)             # K, V once per selected block
-    bytes_comb = part + 4 * w.batch * w.H_kv * w.N * w.k + w.batch * w.N * w.H_q * w.d_h * 2
-    bytes_inv = 4 * w.batch * w.H_kv * w.N * w.k + 4 * valid_slots
+    acct = path_accounting(acc, synth, w, sel)
+    f_idx, f_main = acct["f_idx"], acct["f_main"]
     # block popularity: non-local selections per (sequence, group, block), the
     # skew the pre-scheduled chunking absorbs
     loc = (np.arange(w.N) // w.B_k)[None, :, None]
@@ -409,23 +600,7 @@ def main():
 
     kernels = {}
     if kern:
-        kernels = {
-            "index_topk": {"ms": kern["index_topk"], "bound": "mfma", "flops": f_idx,
-                           "achieved": f_idx / kern["index_topk"] / 1e9, "peak": PEAK_BF16_TFLOPS,
-                           "unit": "TFLOP/s"},
-            "invert_blocks": {"ms": kern["invert_blocks"], "bound": "hbm", "bytes": bytes_inv,
-                              "achieved": bytes_inv / kern["invert_blocks"] / 1e6,
-                              "peak": PEAK_HBM_GBS, "unit": "GB/s"},
-            "sparse_attn_fwd": {"ms": kern["sparse_attn_fwd"], "bound": "hbm", "bytes": bytes_attn,
-                                "achieved": bytes_attn / kern["sparse_attn_fwd"] / 1e6,
-                                "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                                "mfma_tflops": f_main / kern["sparse_attn_fwd"] / 1e9},
-            "combine": {"ms": kern["combine"], "bound": "hbm", "bytes": bytes_comb,
-                        "achieved": bytes_comb / kern["combine"] / 1e6, "peak": PEAK_HBM_GBS,
-                        "unit": "GB/s"},
-        }
-        for v in kernels.values():
-            v["frac"] = v["achieved"] / v["peak"]
+        kernels = kernel_table(kern, acct)
         dom = max(kernels, key=lambda n: kernels[n]["ms"])
         dk = kernels[dom]
         traffic = recorded_traffic(w.name) if dom == "sparse_attn_fwd" else None
@@ -460,6 +635,18 @@ def main():
             mp = kernels[roofline["kernel"]].get("measured_peak")
             if mp:
                 roofline["traffic_frac_measured"] = roofline["traffic_achieved"] / mp
+
+    # ---- the other workloads of the path: the 128K forward with fp8 Q/K/V and
+    # the 1M-token forward in 32K-row chunks (the headline workload's device
+    # buffers are released first)
+    del t, out, bi
+    opart = lpart = sched = offs = ents = lse_out = None
+    torch.cuda.empty_cache()
+    fp8 = long_ctx = None
+    if not args.no_fp8 and w.name != synth.P128K_FP8.name:
+        fp8 = measure_workload(msa, acc, synth, torch, synth.P128K_FP8, args.steps, args.warmup, dev)
+    if not args.no_long_context and w.name != synth.P1M.name:
+        long_ctx = measure_workload(msa, acc, synth, torch, synth.P1M, 2, 1, dev)
 
     # ---- the CPU oracle on a bounded sample of the same workload
     cpu = None
@@ -497,6 +684,14 @@ def main():
                "sample": f"{len(rows)} seeded random query rows of {w.name}, all {w.H_kv} groups "
                          f"and {w.H_q} heads: index branch (fp32) + sparse attention (fp64)"}
         log(f"cpu baseline: {csec:.1f} s -> {cpu['value']:.1f} tokens/s on {cpu['cores']} threads")
+        if not args.no_cpu_full:
+            # the oracle over every row of the tiny and the 16K workloads
+            cpu["full_runs"] = {}
+            for wf in (synth.TINY, synth.P16K):
+                log(f"cpu baseline: the oracle over all {wf.N} rows of {wf.name}")
+                r = cpu_full_run(oracle, synth, acc, wf)
+                cpu["full_runs"][wf.name] = r
+                log(f"cpu baseline: {r['seconds']:.1f} s -> {r['value']:.1f} tokens/s")
 
     line = {
         "metric": "MSA fwd sparse TFLOP/s + tokens/s at N=128K (Hq64/Hkv4/d128/k16); % MFMA/HBM peak",
@@ -510,7 +705,7 @@ def main():
         "sparse_tflops": tflops, "index_flops": f_idx, "main_flops": f_main,
         "block_popularity": popularity,
         "roofline": roofline, "kernels": kernels, "dense_baseline": dense, "decode": decode,
-        "backward": backward, "variants": variants,
+        "backward": backward, "variants": variants, "fp8": fp8, "long_context": long_ctx,
         "measured_peaks": peaks, "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
