@@ -36,11 +36,13 @@
 //    contiguous per instruction (non-temporal), so L2 receives whole 128-byte
 //    lines rather than 16-byte pieces of 64 different rows.
 //  * Software pipeline over passes: while pass p computes, the Q rows of pass
-//    p+2 are gathered into registers and the entry of pass p+3 is read; the
-//    scores of pass p+1 follow pass p's P V.  The loop is unrolled twice so
-//    the score and Q registers alternate by name.  Every memory operation of
-//    the loop is issued unconditionally, so the compiler's in-order vmcnt
-//    waits never have to cover the stores or the loads just issued.
+//    p+1 are gathered into registers and the entry of pass p+2 is read; the
+//    scores of pass p+1 follow pass p's P V.  One register set each for Q and
+//    the scores (158 VGPRs in the bf16 kernel), which leaves the scheduler
+//    room to keep LDS fragment reads ahead of their MFMAs.  Every memory
+//    operation of the loop is issued unconditionally, so the compiler's
+//    in-order vmcnt waits never have to cover the stores or the loads just
+//    issued.
 //  * Softmax in base 2 (v_exp_f32) with the scale folded into one FMA; fp8
 //    (OCP e4m3) inputs are widened exactly to bf16 when used and the
 //    per-tensor scales are folded into the softmax scale and the output scale.
@@ -52,12 +54,6 @@ namespace {
 
 constexpr int kWaves = kAttnWaves;
 constexpr int kThreads = 64 * kWaves;
-// Scores of the next pass computed while the softmax of this one runs (needs
-// the registers of one wave per SIMD), or after this pass's P V.
-#ifndef MSA_ATTN_OVERLAP
-#define MSA_ATTN_OVERLAP (MSA_ATTN_WAVES == 4)
-#endif
-constexpr bool kOverlap = MSA_ATTN_OVERLAP;
 
 // LDS layouts.  Rows are padded rather than swizzled so that every fragment
 // read of a lane is one base address plus a compile-time offset (no per-read
@@ -311,11 +307,24 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void sparse_attn_kernel(
         for (int mt = 0; mt < 4; ++mt) acc[mt] = mfma32x32x16(kfrag(mt, ks), qk, acc[mt]);
       }
     } else {
+      // Rolling K fragments: the register that fed MFMA (mt, ks) is refilled
+      // with fragment (mt + 1, ks) right after it, so every read has a whole
+      // tile of MFMAs (8 x 32 cycles) to land; scheduling barriers keep each
+      // read beside its MFMA (left alone, the scheduler sinks every read next
+      // to its use and each MFMA waits out an LDS round trip).
+      bf16x8 kf[8];
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) kf[ks] = kfrag(0, ks);
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
         acc[mt] = f32x16{};
 #pragma unroll
-        for (int ks = 0; ks < 8; ++ks) acc[mt] = mfma32x32x16(kfrag(mt, ks), q.get(ks), acc[mt]);
+        for (int ks = 0; ks < 8; ++ks) {
+          acc[mt] = mfma32x32x16(kf[ks], q.get(ks), acc[mt]);
+          __builtin_amdgcn_sched_barrier(0);
+          if (mt + 1 < 4) kf[ks] = kfrag(mt + 1, ks);
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
     }
   };
@@ -417,78 +426,43 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void sparse_attn_kernel(
     }
   };
 
-  // ---- software pipeline over passes p, p+1, p+2, p+3: pass p runs its
-  // softmax and P V while the scores of pass p+1 go through the matrix cores
-  // (when p+1 uses the same K/V block), the Q rows of pass p+2 are in flight
-  // and the entry of pass p+3 is being read.  Past the end of the work the
-  // last pass stands in (its loads are valid and their results unused).
+  // ---- software pipeline over passes: at the start of pass p the entry of
+  // pass p+2 is read and the Q rows of pass p+1 are gathered (a whole pass of
+  // latency each), then pass p runs its softmax, P V and stores, and pass
+  // p+1's scores end the step.  One Q register set and one accumulator set
+  // serve every pass (an earlier two-pass-ahead form with alternating register
+  // sets sat at the 256-register limit, which cost its schedule the room to
+  // keep LDS reads ahead of the MFMAs and spilled the fp8 kernel).  Past the
+  // end of the work the last pass stands in (its loads are valid and their
+  // results unused).
   const int i1 = next_pass();
-  const bool have1_0 = i1 >= 0;
-  const int j1 = have1_0 ? i1 : i0;
-  const int i2 = have1_0 ? next_pass() : -1;
-  const bool have2_0 = i2 >= 0;
-  int j_last = have2_0 ? i2 : j1;  // furthest pass looked up (a valid index)
+  bool have1 = i1 >= 0;
+  int j_last = have1 ? i1 : i0;  // furthest pass looked up (a valid index)
   PassDesc D0 = passes[i0];
-  PassDesc D1 = passes[j1];
-  PassDesc D2 = passes[j_last];
-  bool have1 = have1_0, have2 = have2_0;
+  PassDesc D1 = passes[j_last];
   RowRef rr0 = row_dec(row_ent(D0), D0.seq);
   RowRef rr1 = row_dec(row_ent(D1), D1.seq);
-  RowRef rr2 = row_dec(row_ent(D2), D2.seq);
-  QFrag<FP8> qa, qb;
-  f32x16 acca[4], accb[4];
-  {
-    QFrag<FP8> q0;
-    q0.load(rr0.q, h);
-    qa.load(rr1.q, h);
-    // Settle the first gathers here, once: inside the loop every Q fragment is
-    // a prefetch issued one pass earlier.
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks) asm volatile("" ::"v"(q0.w[ks]), "v"(qa.w[ks]));
-    stage(D0);
-    __syncthreads();
-    scores(q0, acca);
-  }
+  QFrag<FP8> q;
+  f32x16 acc[4];
+  q.load(rr0.q, h);
+  stage(D0);
+  __syncthreads();
+  scores(q, acc);
 
-  // One pass.  acc holds its scores, qc the Q rows of pass p+1; the scores of
-  // pass p+1 go to accn and the Q rows of pass p+2 to qn.  The loop below
-  // alternates the two register sets, so nothing is copied between passes.
-  auto step = [&](f32x16(&acc)[4], f32x16(&accn)[4], const QFrag<FP8>& qc, QFrag<FP8>& qn) -> bool {
-    // ---- entry of pass p+3 and the Q rows of pass p+2 (unconditionally)
-    const int i3 = have2 ? next_pass() : -1;
-    const bool have3 = i3 >= 0;
-    if (have3) j_last = i3;
-    const PassDesc D3 = passes[j_last];
-    const uint32_t raw3 = row_ent(D3);
-    qn.load(rr2.q, h);
+  for (;;) {
+    // ---- entry of pass p+2 and the Q rows of pass p+1 (unconditionally)
+    const int i2 = have1 ? next_pass() : -1;
+    const bool have2 = i2 >= 0;
+    if (have2) j_last = i2;
+    const PassDesc D2 = passes[j_last];
+    const uint32_t raw2 = row_ent(D2);
+    q.load(rr1.q, h);
 
+    // ---- softmax of pass p
     mask_own(acc, rr0, D0.blk);
-
-    // ---- softmax of pass p; the scores of pass p+1 overlap it when that pass
-    // uses the staged block (the MFMAs run while the VALU does the softmax).
-    const bool same = have1 && D1.seq == D0.seq && D1.blk == D0.blk;
     bf16x8 pf[8];
     float inv, lse2;
-    if (kOverlap && same) {
-      scores(qc, accn);
-      softmax(acc, pf, inv, lse2);
-      // Interleave: each MFMA with about nine VALU operations, the K fragment
-      // reads two MFMAs ahead.
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-#pragma unroll
-      for (int i = 0; i < 30; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x402, 9, 0);
-      }
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x402, 9, 0);
-      }
-    } else {
-      softmax(acc, pf, inv, lse2);
-    }
+    softmax(acc, pf, inv, lse2);
 
     // ---- O^T = V^T P^T into the wave's tile, then out
     if (h == 0) orow_tile[n] = rr0.orow;
@@ -507,30 +481,22 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void sparse_attn_kernel(
       const int64_t orow = orow_tile[row];
       __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(o_part + orow * kDh + chunk * 8));
     }
-    if (!have1) return false;
+    if (!have1) break;
 
-    // ---- pass p+1 on another block: stage it, then its scores
-    if (!same) {
+    // ---- pass p+1: stage its block when it changes, then its scores
+    if (D1.seq != D0.seq || D1.blk != D0.blk) {
       __syncthreads();
       stage(D1);
       __syncthreads();
-      scores(qc, accn);
-    } else if (!kOverlap) {
-      scores(qc, accn);
     }
+    scores(q, acc);
 
     // ---- advance the pass descriptors and row references
     D0 = D1;
     D1 = D2;
-    D2 = D3;
     rr0 = rr1;
-    rr1 = rr2;
-    rr2 = row_dec(raw3, D3.seq);
+    rr1 = row_dec(raw2, D2.seq);
     have1 = have2;
-    have2 = have3;
-    return true;
-  };
-  while (step(acca, accb, qa, qb) && step(accb, acca, qb, qa)) {
   }
 }
 
