@@ -209,20 +209,25 @@ __global__ __launch_bounds__(kIdxThreads, 1) void index_topk_kernel(
     float pend_x = 0.f;
     int pend_b = 0;
     bool pend_need = false;
+    // The list is sorted descending, so c_j = (x > ts[j]) holds exactly for
+    // j >= the candidate's place p: entry j takes ts[j - 1] when c_{j-1}
+    // (shifted down), x when c_j alone (j = p), and keeps ts[j] otherwise.
+    // Walking j downwards keeps ts[j - 1] unmodified when entry j needs it,
+    // and each comparison serves two entries: one compare and four selects
+    // per entry.  A candidate that is not needed enters as -inf and moves
+    // nothing (the comparisons are strict).
     auto insert_pending = [&]() {
-      float x = pend_x;
-      int xi = pend_b;
-      bool moved = false;
+      const float x = pend_need ? pend_x : -__builtin_huge_valf();
+      const int xi = pend_b;
+      bool c = x > ts[KM - 1];
 #pragma unroll
-      for (int j = 0; j < KM; ++j) {
-        const bool sw = pend_need && (moved || x > ts[j]);
-        const float t = ts[j];
-        const int ti = ids[j];
-        ts[j] = sw ? x : t;
-        ids[j] = sw ? xi : ti;
-        x = sw ? t : x;
-        xi = sw ? ti : xi;
-        moved = moved || sw;
+      for (int j = KM - 1; j >= 0; --j) {
+        const bool cp = j > 0 && x > ts[j > 0 ? j - 1 : 0];
+        const float tp = ts[j > 0 ? j - 1 : 0];
+        const int ip = ids[j > 0 ? j - 1 : 0];
+        ts[j] = cp ? tp : (c ? x : ts[j]);
+        ids[j] = cp ? ip : (c ? xi : ids[j]);
+        c = cp;
       }
       pend_need = false;
     };
