@@ -22,14 +22,17 @@
 //    32-key tile, so the block max-pool is an in-lane max plus one exchange
 //    between the two half-waves.  No score ever leaves the VGPRs.
 //  * Q^idx fragments stay in VGPRs for the whole scan; K^idx blocks stream
-//    through double-buffered, row-padded LDS with one barrier per block, and
-//    the K^idx fragments of the next 32-key tile are read while the MFMAs of
-//    the current one run.
+//    through a 4-buffer, row-padded LDS ring filled by direct global->LDS
+//    loads, with one barrier per two blocks.  K^idx fragments roll: the
+//    register that fed a step is refilled with the next tile's fragment.
 //  * After the exchange, each lane owns exactly one row and keeps that row's
-//    top-(k-1) (score, block) list sorted in VGPRs.  A new block can only
-//    enter when it beats the row's current k-1-th score; the insertion runs
-//    only when some lane of the wave needs it (wave vote).  Blocks arrive in
-//    ascending id order, so "ties keep the earlier block" is a strict compare.
+//    top-(k-1) (score, block) list sorted in VGPRs.  A block's candidate is
+//    inserted, branch-free, while the next block's first key tile runs
+//    through the matrix cores; blocks arrive in ascending id order, so "ties
+//    keep the earlier block" is a strict compare.
+//  * A tile's MFMAs are interleaved with VALU work that does not depend on
+//    them (the previous tile's max-pool, or the pending insertion), so the
+//    vector ALU runs beside the matrix cores within each wave.
 //  * Workgroups are issued heaviest (latest queries, most blocks) first.
 #include <limits.h>
 
@@ -216,19 +219,35 @@ __global__ __launch_bounds__(kIdxThreads, 1) void index_topk_kernel(
     // and each comparison serves two entries: one compare and four selects
     // per entry.  A candidate that is not needed enters as -inf and moves
     // nothing (the comparisons are strict).
-    auto insert_pending = [&]() {
-      const float x = pend_need ? pend_x : -__builtin_huge_valf();
-      const int xi = pend_b;
-      bool c = x > ts[KM - 1];
+    // The walk can be split into ranges of entries (insert_entries), so that
+    // its VALU work can sit between MFMAs.
+    float ins_x = 0.f;
+    int ins_xi = 0;
+    bool ins_c = false;
+    auto insert_begin = [&]() {
+      ins_x = pend_need ? pend_x : -__builtin_huge_valf();
+      ins_xi = pend_b;
+      ins_c = ins_x > ts[KM - 1];
+    };
+    auto insert_entries = [&](int jhi, int jlo) {  // entries jhi down to jlo
 #pragma unroll
       for (int j = KM - 1; j >= 0; --j) {
-        const bool cp = j > 0 && x > ts[j > 0 ? j - 1 : 0];
-        const float tp = ts[j > 0 ? j - 1 : 0];
-        const int ip = ids[j > 0 ? j - 1 : 0];
-        ts[j] = cp ? tp : (c ? x : ts[j]);
-        ids[j] = cp ? ip : (c ? xi : ids[j]);
-        c = cp;
+        if (j > jhi || j < jlo) continue;
+        // (values, not lvalues, in the selects: a conditional over two
+        // lvalues selects an address and would put the list in scratch)
+        const float x = ins_x, tj = ts[j], tp = ts[j > 0 ? j - 1 : 0];
+        const int xi = ins_xi, ij = ids[j], ip = ids[j > 0 ? j - 1 : 0];
+        const bool c = ins_c, cp = j > 0 && x > tp;
+        const float nt = c ? x : tj;
+        const int ni = c ? xi : ij;
+        ts[j] = cp ? tp : nt;
+        ids[j] = cp ? ip : ni;
+        ins_c = cp;
       }
+    };
+    auto insert_pending = [&]() {
+      insert_begin();
+      insert_entries(KM - 1, 0);
       pend_need = false;
     };
 
@@ -239,31 +258,45 @@ __global__ __launch_bounds__(kIdxThreads, 1) void index_topk_kernel(
       // STEPS MFMAs of tile mt run.
       const uint8_t* tile = lds + (b % NBUF) * TILE + n * KSTR + h * 16;
       float mx0 = -__builtin_huge_valf(), mx1 = -__builtin_huge_valf();
-      bf16x8 kf[2][STEPS];
+      // Software-pipelined: tile mt's MFMAs are interleaved, two at a time,
+      // with VALU work that does not depend on them -- the max-pool of tile
+      // mt - 1, or in the first tile the previous block's deferred insertion
+      // -- so that the vector ALU runs while the matrix cores do.  K
+      // fragments roll: the register that fed step ks is refilled with tile
+      // mt + 1's fragment right after.
+      constexpr int EPK = 16 / STEPS;                      // max-pool elements per step
+      constexpr int IPK = (KM + STEPS - 1) / STEPS;        // insertion entries per step
+      bf16x8 kr[STEPS];
+      f32x16 A[2][2];
 #pragma unroll
-      for (int ks = 0; ks < STEPS; ++ks)
-        kf[0][ks] = as_bf16x8(*reinterpret_cast<const u32x4*>(tile + 32 * ks));
+      for (int ks = 0; ks < STEPS; ++ks) kr[ks] = as_bf16x8(*reinterpret_cast<const u32x4*>(tile + 32 * ks));
+      if (kDefer) insert_begin();
 #pragma unroll
       for (int mt = 0; mt < KT; ++mt) {
-        if (mt + 1 < KT) {
-#pragma unroll
-          for (int ks = 0; ks < STEPS; ++ks)
-            kf[(mt + 1) & 1][ks] = as_bf16x8(
-                *reinterpret_cast<const u32x4*>(tile + 32 * (mt + 1) * KSTR + 32 * ks));
-        }
-        // keep those reads ahead of this tile's MFMAs (the scheduler would
-        // otherwise sink each read next to its use and expose its latency)
-        __builtin_amdgcn_sched_barrier(0);
-        f32x16 a0 = {}, a1 = {};
+        const int st = mt & 1;
 #pragma unroll
         for (int ks = 0; ks < STEPS; ++ks) {
-          a0 = mfma32x32x16(kf[mt & 1][ks], qf[0][ks], a0);
-          a1 = mfma32x32x16(kf[mt & 1][ks], qf[1][ks], a1);
+          A[st][0] = mfma32x32x16(kr[ks], qf[0][ks], ks ? A[st][0] : f32x16{});
+          A[st][1] = mfma32x32x16(kr[ks], qf[1][ks], ks ? A[st][1] : f32x16{});
+          __builtin_amdgcn_sched_barrier(0);
+          if (mt + 1 < KT)
+            kr[ks] = as_bf16x8(*reinterpret_cast<const u32x4*>(tile + 32 * (mt + 1) * KSTR + 32 * ks));
+          if (mt > 0) {
+#pragma unroll
+            for (int e = EPK * ks; e < EPK * (ks + 1); e += 2) {
+              mx0 = fmaxf(mx0, fmaxf(A[st ^ 1][0][e], A[st ^ 1][0][e + 1]));
+              mx1 = fmaxf(mx1, fmaxf(A[st ^ 1][1][e], A[st ^ 1][1][e + 1]));
+            }
+          } else if (kDefer) {
+            const int jhi = KM - 1 - IPK * ks, jlo = jhi - IPK + 1;
+            if (jhi >= 0) insert_entries(jhi, jlo < 0 ? 0 : jlo);
+          }
+          __builtin_amdgcn_sched_barrier(0);
         }
-        if (kDefer && mt == 0) insert_pending();
-        mx0 = fmaxf(mx0, max16(a0));
-        mx1 = fmaxf(mx1, max16(a1));
       }
+      if (kDefer) pend_need = false;
+      mx0 = fmaxf(mx0, max16(A[(KT - 1) & 1][0]));
+      mx1 = fmaxf(mx1, max16(A[(KT - 1) & 1][1]));
       // Lane half 0 holds keys 4h.. of every 8 for column tile 0 and 1; swap so
       // that half 0 finishes column tile 0 and half 1 column tile 1.
       const float send = h ? mx0 : mx1;
