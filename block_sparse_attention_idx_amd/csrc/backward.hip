@@ -93,15 +93,15 @@ __device__ __forceinline__ bf16x8 lds_frag(const uint8_t* p) {
   return as_bf16x8(*reinterpret_cast<const u32x4*>(p));
 }
 
-// This workgroup's passes: the (seq, window) pairs in order and, in each, one
+// This workgroup's passes: the sequences in order and, in each, one
 // contiguous equal share of its passes (the forward's partition).
 struct PassIter {
   const int32_t* segp;
-  int B_c, npairs;
+  int B_c, nseqs;
   int pair = -1, p = 0, end = 0;
   __device__ int next() {
     if (++p < end) return p;
-    while (++pair < npairs) {
+    while (++pair < nseqs) {
       const int a = segp[pair * B_c];
       const int64_t np = segp[(pair + 1) * B_c] - a;
       const int s0 = a + static_cast<int>(np * blockIdx.x / gridDim.x);
@@ -233,7 +233,7 @@ __global__ __launch_bounds__(kBT, 1) void bwd_main_kernel(
     const uint16_t* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ dlt,
     int64_t N, int H_sel, int kv_shift, int kslots, float scale, float scale_log2,
     const int32_t* __restrict__ entries, const int32_t* __restrict__ segp,
-    const PassDesc* __restrict__ passes, int B_c, int npairs, int q_begin, int q_count, int64_t dummy_slot,
+    const PassDesc* __restrict__ passes, int B_c, int nseqs, int q_begin, int q_count, int64_t dummy_slot,
     uint16_t* __restrict__ dq_part, float* __restrict__ dk_acc, float* __restrict__ dv_acc,
     float* __restrict__ tch_out) {
   constexpr int EC = kRows / G;  // queries per chunk
@@ -249,7 +249,7 @@ __global__ __launch_bounds__(kBT, 1) void bwd_main_kernel(
   __shared__ int64_t ri_orow[kRows];
   __shared__ __attribute__((aligned(16))) float tch[IDX ? EC * kBk : 4];  // teacher sums [query][key]
 
-  PassIter it{segp, B_c, npairs};
+  PassIter it{segp, B_c, nseqs};
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, n = lane & 31, h = lane >> 5;
   const int H_q = H_sel * G, H_kv = H_sel >> kv_shift;
   const int key_l = 32 * wave + n;  // this lane's key within the block
@@ -498,7 +498,7 @@ __global__ __launch_bounds__(kBT, 1) void bwd_idx_kernel(
     const uint16_t* __restrict__ q_idx, const uint16_t* __restrict__ k_idx, const float* __restrict__ lsei2,
     const float* __restrict__ tch_in, int64_t N, int H_sel, int kslots, float idx_scale_log2, float gscale,
     const int32_t* __restrict__ entries, const int32_t* __restrict__ segp,
-    const PassDesc* __restrict__ passes, int B_c, int npairs, int q_begin, int q_count, int64_t dummy_slot,
+    const PassDesc* __restrict__ passes, int B_c, int nseqs, int q_begin, int q_count, int64_t dummy_slot,
     float* __restrict__ dqi_part, float* __restrict__ kl_part, float* __restrict__ dki_acc) {
   // Index rows per chunk: 64 entries of one key block, from one pass (a pass
   // holds 256 / G entries) or from consecutive passes of the block (G >= 8).
@@ -519,7 +519,7 @@ __global__ __launch_bounds__(kBT, 1) void bwd_idx_kernel(
   __shared__ float ei_l2[64];
   __shared__ int64_t ei_slot[64];
 
-  PassIter it{segp, B_c, npairs};
+  PassIter it{segp, B_c, nseqs};
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, n = lane & 31, h = lane >> 5;
   const int key_l = 32 * wave + n;
 
@@ -730,11 +730,11 @@ template <int DIDX>
 __global__ __launch_bounds__(64) void proxy_lse_kernel(
     const uint16_t* __restrict__ q_idx, const uint16_t* __restrict__ k_idx, int64_t N, int H_sel, int kslots,
     float idx_scale_log2, const int32_t* __restrict__ entries, const int32_t* __restrict__ segp,
-    const PassDesc* __restrict__ passes, int B_c, int npairs, int q_begin, int q_count,
+    const PassDesc* __restrict__ passes, int B_c, int nseqs, int q_begin, int q_count,
     float* __restrict__ lsei_part) {
   constexpr int KSI = DIDX / 16;
   __shared__ __attribute__((aligned(16))) uint8_t ki_lds[kBk * kStr];
-  PassIter it{segp, B_c, npairs};
+  PassIter it{segp, B_c, nseqs};
   const int lane = threadIdx.x, n = lane & 31, h = lane >> 5;
   int cur_seq = -1, cur_blk = 0;
   for (int pi = it.next(); pi >= 0; pi = it.next()) {
@@ -954,7 +954,7 @@ hipError_t launch_backward_chunk(const BwdArgs& a, hipStream_t stream) {
   const SchedLayout s = sched_layout(a.batch, a.H_sel, a.G, a.k, a.q_begin, a.q_count, kBk);
   const int64_t seqs = static_cast<int64_t>(a.batch) * a.H_sel;
   const int H_q = a.H_sel * a.G;
-  const int npairs = static_cast<int>(seqs * s.nW);
+  const int nseqs = static_cast<int>(seqs);
   const int32_t* segp = a.sched + s.off_segp;
   const PassDesc* passes = reinterpret_cast<const PassDesc*>(a.sched + s.off_pass);
   const int64_t min_passes = (seqs * a.q_count * a.k + s.EPP - 1) / s.EPP;
@@ -977,7 +977,7 @@ hipError_t launch_backward_chunk(const BwdArgs& a, hipStream_t stream) {
     const unsigned lgrid = clamp_grid(static_cast<int64_t>(cus_of_device()) * kLseWgPerCu);
     auto lk = a.d_idx == 64 ? proxy_lse_kernel<64> : proxy_lse_kernel<128>;
     hipLaunchKernelGGL(lk, dim3(lgrid), dim3(64), 0, stream, a.q_idx, a.k_idx, a.N, a.H_sel, a.k, isl2,
-                       a.entries, segp, passes, static_cast<int>(s.B_c), npairs, static_cast<int>(a.q_begin),
+                       a.entries, segp, passes, static_cast<int>(s.B_c), nseqs, static_cast<int>(a.q_begin),
                        static_cast<int>(a.q_count), a.lsei_part);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -995,12 +995,12 @@ hipError_t launch_backward_chunk(const BwdArgs& a, hipStream_t stream) {
     if (a.index)                                                                                                \
       hipLaunchKernelGGL((bwd_main_kernel<GG, true>), dim3(grid), dim3(kBT), 0, stream, a.q, a.k_ptr, a.v,     \
                          a.dout, a.lse, a.dlt, a.N, a.H_sel, a.kv_shift, a.k, a.scale, scale_log2, a.entries,   \
-                         segp, passes, static_cast<int>(s.B_c), npairs, static_cast<int>(a.q_begin),            \
+                         segp, passes, static_cast<int>(s.B_c), nseqs, static_cast<int>(a.q_begin),            \
                          static_cast<int>(a.q_count), dummy_slot, a.dq_part, a.dk_acc, a.dv_acc, a.tch);        \
     else                                                                                                        \
       hipLaunchKernelGGL((bwd_main_kernel<GG, false>), dim3(grid), dim3(kBT), 0, stream, a.q, a.k_ptr, a.v,    \
                          a.dout, a.lse, a.dlt, a.N, a.H_sel, a.kv_shift, a.k, a.scale, scale_log2, a.entries,   \
-                         segp, passes, static_cast<int>(s.B_c), npairs, static_cast<int>(a.q_begin),            \
+                         segp, passes, static_cast<int>(s.B_c), nseqs, static_cast<int>(a.q_begin),            \
                          static_cast<int>(a.q_count), dummy_slot, a.dq_part, a.dk_acc, a.dv_acc, a.tch);        \
     break;
     switch (a.G) {
@@ -1022,7 +1022,7 @@ hipError_t launch_backward_chunk(const BwdArgs& a, hipStream_t stream) {
 #define MSA_BWD_IDX(GG, DD)                                                                                    \
   hipLaunchKernelGGL((bwd_idx_kernel<GG, DD>), dim3(grid), dim3(kBT), 0, stream, a.q_idx, a.k_idx, a.lsei2,     \
                      a.tch, a.N, a.H_sel, a.k, isl2, a.kl_weight * a.idx_scale, a.entries, segp, passes,        \
-                     static_cast<int>(s.B_c), npairs, static_cast<int>(a.q_begin), static_cast<int>(a.q_count), \
+                     static_cast<int>(s.B_c), nseqs, static_cast<int>(a.q_begin), static_cast<int>(a.q_count), \
                      dummy_slot, a.dqi_part, a.kl_part, a.dki_acc)
 #define MSA_BWD_IDX_G(GG)          \
   case GG:                         \

@@ -15,21 +15,19 @@
 //               in place; column totals tot[seq][block].
 //  3. binscan:  one workgroup scans the totals over all (seq, block) bins into
 //               absolute CSR offsets, then the pass counts ceil(len / EPP),
-//               EPP = kPassRows / G, of the segments -- a bin restricted to
-//               one query window, in (seq, window, block) order -- into the
-//               first pass of every segment.
+//               EPP = kPassRows / G, of the bins into the first pass of every
+//               bin.
 //  4. scatter:  the count workgroup's masks are rebuilt and every entry lands at
 //               offset[bin] + colprefix[tile][bin] + popcount(mask below row).
 //  5. passes:   the work list: one descriptor per pass of EPP consecutive
-//               entries of a segment (the last one partial).
+//               entries of a bin (the last one partial).
 //
 // Pre-scheduled chunking ("MiniMax Sparse Attention (MSA)", KV-Outer Sparse
-// Attention, step 5): the attention kernel takes the (seq, window) pairs one
-// after another and splits each pair's passes into one contiguous, equal
-// share per workgroup, so a block that many queries picked is spread over as
-// many workgroups as its share of the work asks for, all workgroups gather
-// the Q rows of one window at a time (they stay in the memory-side cache while
-// every block they picked is processed), and every (query, slot) keeps its own
+// Attention, step 5): the attention kernel takes the sequences one after
+// another and splits each one's passes into one contiguous, equal share per
+// workgroup, so a block that many queries picked is spread over as many
+// workgroups as its share of the work asks for, a workgroup restages K/V only
+// when its passes move to the next bin, and every (query, slot) keeps its own
 // preassigned output slot.
 #include "msa_internal.h"
 
@@ -41,22 +39,17 @@ SchedLayout sched_layout(int batch, int H_kv, int G, int k, int64_t q_begin, int
   const int64_t nseq = static_cast<int64_t>(batch) * H_kv;
   s.B_c = (q_begin + q_count + bk - 1) / bk;
   s.T64 = (q_count + 63) / 64;
-  s.TW = kAttnWindowRows / 64;
-  s.nW = (s.T64 + s.TW - 1) / s.TW;
   s.nbins = nseq * s.B_c;
-  s.nseg = nseq * s.nW * s.B_c;
   s.EPP = kPassRows / (G > 0 ? G : 1);
-  // sum_g ceil(t_g / EPP) <= (sum_g t_g) / EPP + (non-empty segments), and a
-  // window of TW tiles holds at most min(B_c, blocks the window's rows see)
-  // non-empty segments per seq; nseg bounds that.
-  s.max_passes = (nseq * q_count * k + s.EPP - 1) / s.EPP + s.nseg;
+  // sum_g ceil(t_g / EPP) <= (sum_g t_g) / EPP + (non-empty bins)
+  s.max_passes = (nseq * q_count * k + s.EPP - 1) / s.EPP + s.nbins;
   int64_t w = kHdrWords;
   s.off_tot = w;
   w = al(w + s.nbins);
   s.off_bad = w;
   w = al(w + nseq * s.T64);
   s.off_segp = w;
-  w = al(w + s.nseg + 1);
+  w = al(w + s.nbins + 1);
   s.off_pass = w;
   w = al(w + s.max_passes * 4);
   s.off_cnt = w;
@@ -150,18 +143,6 @@ __global__ __launch_bounds__(kScanWaves * 64) void inv_colscan_kernel(
 // earlier kernels wrote.
 constexpr int kBinThreads = 1024;
 
-// Entries of segment g = ((seq * nW) + w) * B_c + blk: the rows of tiles
-// [w TW, (w + 1) TW) in the bin's column prefix.
-__device__ __forceinline__ int seg_len(const int32_t* __restrict__ tot, const int32_t* __restrict__ cnt,
-                                       int64_t g, int64_t B_c, int64_t T64, int64_t TW, int64_t nW) {
-  const int64_t blk = g % B_c, sw = g / B_c;
-  const int64_t seq = sw / nW, w = sw % nW;
-  const int64_t t0 = w * TW, t1 = t0 + TW;
-  const int lo = cnt[(seq * T64 + t0) * B_c + blk];
-  const int hi = t1 < T64 ? cnt[(seq * T64 + t1) * B_c + blk] : tot[seq * B_c + blk];
-  return hi - lo;
-}
-
 __device__ __forceinline__ void block_exclusive_scan(int* se, int& e) {
   const int t = threadIdx.x;
   se[t] = e;
@@ -177,8 +158,8 @@ __device__ __forceinline__ void block_exclusive_scan(int* se, int& e) {
 }
 
 __global__ __launch_bounds__(kBinThreads) void inv_binscan_kernel(
-    const int32_t* __restrict__ tot, const int32_t* __restrict__ cnt, int64_t nbins, int64_t B_c,
-    int64_t T64, int64_t TW, int64_t nW, int64_t nseg, int epp, const int32_t* __restrict__ bad,
+    const int32_t* __restrict__ tot, int64_t nbins, int64_t B_c,
+    int epp, const int32_t* __restrict__ bad,
     int64_t nbad_slots, int32_t* __restrict__ blk_offsets, int32_t* __restrict__ segp,
     int32_t* __restrict__ hdr) {
   __shared__ int se[kBinThreads];
@@ -206,19 +187,19 @@ __global__ __launch_bounds__(kBinThreads) void inv_binscan_kernel(
   }
   __syncthreads();
 
-  // ---- part 2: first pass of every segment
+  // ---- part 2: first pass of every bin
   {
-    const int64_t per = (nseg + kBinThreads - 1) / kBinThreads;
-    const int64_t s0 = min<int64_t>(nseg, t * per), s1 = min<int64_t>(nseg, s0 + per);
+    const int64_t per = (nbins + kBinThreads - 1) / kBinThreads;
+    const int64_t s0 = min<int64_t>(nbins, t * per), s1 = min<int64_t>(nbins, s0 + per);
     int np = 0;
-    for (int64_t g = s0; g < s1; ++g) np += (seg_len(tot, cnt, g, B_c, T64, TW, nW) + epp - 1) / epp;
+    for (int64_t g = s0; g < s1; ++g) np += (tot[g] + epp - 1) / epp;
     block_exclusive_scan(se, np);
     for (int64_t g = s0; g < s1; ++g) {
       segp[g] = np;
-      np += (seg_len(tot, cnt, g, B_c, T64, TW, nW) + epp - 1) / epp;
+      np += (tot[g] + epp - 1) / epp;
     }
     if (t == kBinThreads - 1) {
-      segp[nseg] = np;
+      segp[nbins] = np;
       hdr[kHdrPasses] = np;
     }
   }
@@ -228,16 +209,15 @@ __global__ __launch_bounds__(kBinThreads) void inv_binscan_kernel(
 // Pass descriptors: workgroups stride over the segments, threads over a
 // segment's passes.
 __global__ __launch_bounds__(kInvThreads) void inv_passes_kernel(
-    const int32_t* __restrict__ tot, const int32_t* __restrict__ cnt,
-    const int32_t* __restrict__ segp, const int32_t* __restrict__ blk_offsets, int64_t B_c,
-    int64_t T64, int64_t TW, int64_t nW, int64_t nseg, int epp, PassDesc* __restrict__ passes) {
-  for (int64_t g = blockIdx.x; g < nseg; g += gridDim.x) {
+    const int32_t* __restrict__ tot, const int32_t* __restrict__ segp,
+    const int32_t* __restrict__ blk_offsets, int64_t B_c, int64_t nbins, int epp,
+    PassDesc* __restrict__ passes) {
+  for (int64_t g = blockIdx.x; g < nbins; g += gridDim.x) {
     const int p0 = segp[g], np = segp[g + 1] - p0;
     if (np == 0) continue;
-    const int64_t blk = g % B_c, sw = g / B_c;
-    const int64_t seq = sw / nW, w = sw % nW;
-    const int len = seg_len(tot, cnt, g, B_c, T64, TW, nW);
-    const int off = blk_offsets[seq * (B_c + 1) + blk] + cnt[(seq * T64 + w * TW) * B_c + blk];
+    const int64_t blk = g % B_c, seq = g / B_c;
+    const int len = tot[g];
+    const int off = blk_offsets[seq * (B_c + 1) + blk];
     for (int j = threadIdx.x; j < np; j += blockDim.x) {
       PassDesc d;
       d.start = off + j * epp;
@@ -306,19 +286,18 @@ hipError_t launch_invert(const int32_t* block_idx, int batch, int H_kv, int G, i
                      dim3(kScanWaves * 64), 0, stream, cnt, s.B_c, s.T64, tot);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(inv_binscan_kernel, dim3(1), dim3(kBinThreads), 0, stream, tot, cnt, s.nbins,
-                     s.B_c, s.T64, s.TW, s.nW, s.nseg, epp, bad, nseq * s.T64, blk_offsets, segp,
-                     hdr);
+  hipLaunchKernelGGL(inv_binscan_kernel, dim3(1), dim3(kBinThreads), 0, stream, tot, s.nbins,
+                     s.B_c, epp, bad, nseq * s.T64, blk_offsets, segp, hdr);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(inv_scatter_kernel, tiles, dim3(kInvThreads), lds, stream, block_idx, k, q_begin,
                      q_count, s.B_c, s.T64, cnt, blk_offsets, blk_entries, bk);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int64_t pgrid = s.nseg < 8192 ? s.nseg : 8192;
+  const int64_t pgrid = s.nbins < 8192 ? s.nbins : 8192;
   hipLaunchKernelGGL(inv_passes_kernel, dim3(static_cast<unsigned>(pgrid > 0 ? pgrid : 1)),
-                     dim3(kInvThreads), 0, stream, tot, cnt, segp, blk_offsets, s.B_c, s.T64, s.TW,
-                     s.nW, s.nseg, epp, reinterpret_cast<PassDesc*>(sched + s.off_pass));
+                     dim3(kInvThreads), 0, stream, tot, segp, blk_offsets, s.B_c, s.nbins, epp,
+                     reinterpret_cast<PassDesc*>(sched + s.off_pass));
   return hipGetLastError();
 }
 

@@ -28,17 +28,6 @@ constexpr int kAttnWaves = MSA_ATTN_WAVES;
 static_assert(kAttnWaves == 4 || kAttnWaves == 8, "4 or 8 attention waves");
 constexpr int kPassRows = 32 * kAttnWaves;
 
-// Query rows per scheduling window of the attention pass: the passes of one
-// (seq, window) pair are shared out over all workgroups before the next pair
-// starts, so the Q rows one window gathers can be re-read while a cache still
-// holds them.  A multiple of 64; build-time tunable.  The default, 2^21 rows,
-// is one window for every supported N: with non-temporal partial-output
-// stores, windows of 4K-32K rows measured slower than none.
-#ifndef MSA_ATTN_WINDOW_ROWS
-#define MSA_ATTN_WINDOW_ROWS 2097152
-#endif
-constexpr int64_t kAttnWindowRows = MSA_ATTN_WINDOW_ROWS;
-static_assert(kAttnWindowRows % 64 == 0 && kAttnWindowRows > 0, "window must be whole 64-row tiles");
 
 // ---------------------------------------------------------------- device helpers
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
@@ -107,23 +96,19 @@ hipError_t launch_window_select(int batch, int H_kv, int k, int64_t q_begin, int
                                 int32_t* block_idx, hipStream_t stream, int bk = kBk);
 
 // Inversion scratch layout (all offsets in 4-byte words, 256-byte aligned).
-// A segment is a (seq, block) bin restricted to one query window; segments are
-// ordered (seq, window, block), and (seq, window) pairs own B_c consecutive
-// segments.  The attention work list is a flat array of passes in segment
-// order: each holds up to EPP = kPassRows / G consecutive entries of one
-// segment, so no pass spans two segments (or two bins).
+// Bins are (seq, block), ordered seq-major, so a seq owns B_c consecutive
+// bins.  The attention work list is a flat array of passes in bin order: each
+// holds up to EPP = kPassRows / G consecutive entries of one bin, so no pass
+// spans two bins.
 struct SchedLayout {
   int64_t nbins;       // batch * H_kv * B_c
   int64_t B_c;         // key blocks visible to the range
   int64_t T64;         // 64-row query tiles of the range
-  int64_t TW;          // 64-row tiles per scheduling window
-  int64_t nW;          // scheduling windows of the range
-  int64_t nseg;        // batch * H_kv * nW * B_c
   int64_t EPP;         // entries per pass
   int64_t max_passes;  // capacity of the pass list
   int64_t off_tot;     // per-bin totals [nbins]
   int64_t off_bad;     // per-tile out-of-range counts [batch * H_kv * T64]
-  int64_t off_segp;    // first pass of each segment [nseg + 1]
+  int64_t off_segp;    // first pass of each bin [nbins + 1]
   int64_t off_pass;    // pass descriptors [max_passes]
   int64_t off_cnt;     // per-(seq, tile, bin) counts, then column prefixes
   int64_t words;       // total size in words

@@ -15,11 +15,11 @@
 // gfx950 design:
 //  * Persistent grid, one workgroup of 8 waves per CU (two waves per SIMD).
 //    The work list is a flat array of pass descriptors (entry start, count,
-//    group, block) built by the inversion, ordered (sequence, query window,
-//    block); the workgroups take the (sequence, window) pairs in order and
-//    each takes an equal contiguous share of every pair's passes: every
-//    workgroup gets the same work whatever the block popularity, and a K/V
-//    block is staged only when consecutive passes change block.
+//    group, block) built by the inversion, ordered (sequence, block); the
+//    workgroups take the sequences in order and each takes an equal
+//    contiguous share of every sequence's passes: every workgroup gets the
+//    same work whatever the block popularity, and a K/V block is staged only
+//    when consecutive passes change block.
 //  * A pass is 256 (query, head) rows: 256 / G entries x G heads (a query's G
 //    heads are contiguous in Q, 256 B each); each wave owns one 32-row MFMA
 //    column tile.  K (row-major) and V (transposed) live in padded LDS
@@ -207,7 +207,7 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void sparse_attn_kernel(
     const void* __restrict__ qp, const void* __restrict__ kp, const void* __restrict__ vp,
     int64_t N, int H_sel, int kv_shift, int kslots, uint32_t kdiv_magic, int kdiv_shift, float scale_log2,
     float out_scale, const int32_t* __restrict__ entries, const int32_t* __restrict__ segp,
-    const PassDesc* __restrict__ passes, int B_c, int npairs, int q_begin, int q_count,
+    const PassDesc* __restrict__ passes, int B_c, int nseqs, int q_begin, int q_count,
     uint16_t* __restrict__ o_part, float* __restrict__ lse_part) {
   constexpr int EB = FP8 ? 1 : 2;  // bytes per Q/K/V element
   __shared__ __attribute__((aligned(16))) uint8_t k_lds[kBk * kKStride];
@@ -215,15 +215,16 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void sparse_attn_kernel(
   __shared__ __attribute__((aligned(16))) uint8_t o_lds[kWaves * 32 * kOStride];
   __shared__ __attribute__((aligned(8))) int64_t orow_lds[kWaves * 32];
 
-  // This workgroup's passes: the (seq, window) pairs in order, and in each
-  // pair one contiguous, equal share of its passes.  next_pass() returns the
-  // next pass index, or -1 when the shares are exhausted (and from then on).
-  int it_pair = -1, it_p = 0, it_end = 0;
+  // This workgroup's passes: the sequences (seq = batch * H_sel + group) in
+  // order, and in each one contiguous, equal share of its passes.
+  // next_pass() returns the next pass index, or -1 when the shares are
+  // exhausted (and from then on).
+  int it_seq = -1, it_p = 0, it_end = 0;
   auto next_pass = [&]() -> int {
     if (++it_p < it_end) return it_p;
-    while (++it_pair < npairs) {
-      const int a = segp[it_pair * B_c];
-      const int64_t np = segp[(it_pair + 1) * B_c] - a;
+    while (++it_seq < nseqs) {
+      const int a = segp[it_seq * B_c];
+      const int64_t np = segp[(it_seq + 1) * B_c] - a;
       const int s0 = a + static_cast<int>(np * blockIdx.x / gridDim.x);
       const int s1 = a + static_cast<int>(np * (blockIdx.x + 1) / gridDim.x);
       if (s0 < s1) {
@@ -557,7 +558,7 @@ hipError_t launch_g(const void* q, const void* k, const void* v, bool fp8, int b
   hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(grid)), dim3(kThreads), 0, stream, q, k, v,
                      N, H_sel, kv_shift, kslots, magic, shift, scale_log2, out_scale, blk_entries,
                      sched + s.off_segp, reinterpret_cast<const PassDesc*>(sched + s.off_pass),
-                     static_cast<int>(s.B_c), static_cast<int>(batch * H_sel * s.nW),
+                     static_cast<int>(s.B_c), static_cast<int>(batch * H_sel),
                      static_cast<int>(q_begin), static_cast<int>(q_count), o_part, lse_part);
   return hipGetLastError();
 }
