@@ -144,3 +144,46 @@ def test_backward_sampled_rows_and_sums(w):
         err = float(s.abs().max())
         log(f"  {name}: max {err:.3g} (root-sum-square {rss:.3g})")
         assert err <= 2e-2 * rss, name
+
+
+@pytest.mark.parametrize("w", [synth.P16K, synth.P128K_HOT], ids=lambda w: w.name)
+def test_backward_key_blocks_elementwise(w):
+    """Whole key blocks of dK, dV and dk_idx, element by element, at full size.
+    A key's gradient sums over every query that selected its block, so the
+    oracle runs on exactly those queries (found in the forward's selection):
+    for group 1, the last block (selected only as the local block), the one
+    before it, and the least-selected block of the middle half of the
+    sequence; for dk_idx (shared by all groups) the last block over all
+    groups.  A misplaced atomic (another key row, another head) fails here
+    even when the column sums agree."""
+    log(f"backward key blocks {w.name}")
+    t = device_inputs(w, DEV)
+    d_o = synth.device_tensor(w, "d_o", DEV)
+    g, sel = _run(w, t, d_o)
+    sel0 = sel[0]                                     # [H_sel, N, k]
+    B, r, G = w.B, 1, w.G_sel
+    allk = {x: synth.host_all(w, x) for x in ("k", "v", "k_idx")}
+    picked = lambda rr, b: np.nonzero((sel0[rr] == b).any(axis=1))[0]
+    mid = np.arange(B // 4, 3 * B // 4)
+    counts = np.array([len(picked(r, b)) for b in mid])
+    blocks = [B - 1, B - 2, int(mid[int(np.argmin(counts))])]
+    rows = np.unique(np.concatenate([picked(r, b) for b in blocks]))
+    log(f"  group {r}: blocks {blocks}, {len(rows)} selecting queries")
+    heads = slice(r * G, (r + 1) * G)
+    ref = oracle.backward(w.N, w.B_k, rows, synth.host_rows(w, "q", rows)[:, heads],
+                          allk["k"][:, r:r + 1], allk["v"][:, r:r + 1],
+                          synth.host_rows(w, "q_idx", rows)[:, r:r + 1], allk["k_idx"],
+                          np.ascontiguousarray(sel0[r:r + 1][:, rows]),
+                          synth.host_rows(w, "d_o", rows)[:, heads], kl_weight=KL_W)
+    dk, dv = _f(g["dk"][0]), _f(g["dv"][0])
+    for b in blocks:
+        keys = slice(b * w.B_k, min((b + 1) * w.B_k, w.N))
+        _grad_check(f"dK block {b}", dk[keys, r], ref["dk"][keys, 0])
+        _grad_check(f"dV block {b}", dv[keys, r], ref["dv"][keys, 0])
+    last = np.unique(np.concatenate([picked(rr, B - 1) for rr in range(w.H_sel)]))
+    ref2 = oracle.backward(w.N, w.B_k, last, synth.host_rows(w, "q", last), allk["k"], allk["v"],
+                           synth.host_rows(w, "q_idx", last), allk["k_idx"],
+                           np.ascontiguousarray(sel0[:, last]), synth.host_rows(w, "d_o", last),
+                           kl_weight=KL_W)
+    keys = slice((B - 1) * w.B_k, w.N)
+    _grad_check(f"dk_idx block {B - 1}", _f(g["dk_idx"][0])[keys], ref2["dk_idx"][keys])
