@@ -267,14 +267,18 @@ def measure_workload(msa, acc, synth, torch, w, steps, warmup, dev):
     kernels = kernel_table(kern, a)
     dom = max(kernels, key=lambda n: kernels[n]["ms"])
     dk = kernels[dom]
+    traffic = recorded_traffic(w.name) if dom == "sparse_attn_fwd" else None
+    roofline = {"kernel": dom, "bound": dk["bound"], "achieved": dk["achieved"], "peak": dk["peak"],
+                "unit": dk["unit"], "frac": dk["frac"], "traffic": traffic}
+    if traffic:
+        roofline["traffic_achieved"] = traffic / dk["ms"] / 1e6
     return {
         "workload": w.name, "dtype": w.dtype, "N": w.N, "q_chunk": w.q_chunk, "steps": steps,
         "warmup": warmup, "ms_per_step": ms, "ms_median": med, "ms_min": mn,
         "tokens_s": w.batch * w.N / (ms * 1e-3),
         "sparse_tflops": (a["f_idx"] + a["f_main"]) / (ms * 1e-3) / 1e12,
         "index_flops": a["f_idx"], "main_flops": a["f_main"],
-        "roofline": {"kernel": dom, "bound": dk["bound"], "achieved": dk["achieved"], "peak": dk["peak"],
-                     "unit": dk["unit"], "frac": dk["frac"], "traffic": None},
+        "roofline": roofline,
         "kernels": kernels,
     }
 
