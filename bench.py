@@ -98,10 +98,13 @@ def measured_peaks():
 
 
 # The measured peak each kernel is compared with: the indexer with sustained
-# MFMA throughput, the attention kernel with the random 4 KB read/write mix
-# (its Q gathers and partial-output stores), the combine with sequential reads
-# (its partial slabs), the inversion with a plain copy.
-MEASURED_PEAK_OF = {"index_topk": "mfma_bf16_TFLOPs", "invert_blocks": "hbm_copy_GBs",
+# MFMA throughput on random operands (real Q and K tiles change from one MFMA
+# to the next; the fixed-pattern figure, mfma_bf16_TFLOPs, runs at a higher
+# clock), the attention kernel with the random 4 KB read/write mix (its Q
+# gathers and partial-output stores), the combine with sequential reads (its
+# partial slabs), the inversion with a plain copy.
+MFMA_PEAK_KEY = "mfma_bf16_random_TFLOPs"
+MEASURED_PEAK_OF = {"index_topk": MFMA_PEAK_KEY, "invert_blocks": "hbm_copy_GBs",
                     "sparse_attn_fwd": "hbm_rand4k_mixed_GBs", "combine": "hbm_seq_read_GBs"}
 
 
@@ -631,10 +634,10 @@ def main():
             decode["measured_peak"] = peaks["hbm_seq_read_GBs"]
             decode["measured_peak_kind"] = "hbm_seq_read_GBs"
             decode["frac_measured"] = decode["achieved"] / peaks["hbm_seq_read_GBs"]
-        if dense and peaks.get("mfma_bf16_TFLOPs", 0) > 0:
-            dense["measured_peak"] = peaks["mfma_bf16_TFLOPs"]
-            dense["measured_peak_kind"] = "mfma_bf16_TFLOPs"
-            dense["frac_measured"] = dense["achieved"] / peaks["mfma_bf16_TFLOPs"]
+        if dense and peaks.get(MFMA_PEAK_KEY, 0) > 0:
+            dense["measured_peak"] = peaks[MFMA_PEAK_KEY]
+            dense["measured_peak_kind"] = MFMA_PEAK_KEY
+            dense["frac_measured"] = dense["achieved"] / peaks[MFMA_PEAK_KEY]
         if roofline and roofline.get("traffic_achieved") and roofline["kernel"] in kernels:
             mp = kernels[roofline["kernel"]].get("measured_peak")
             if mp:

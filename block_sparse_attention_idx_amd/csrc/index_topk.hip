@@ -26,15 +26,18 @@
 //    loads, with one barrier per two blocks.  K^idx fragments roll: the
 //    register that fed a step is refilled with the next tile's fragment.
 //  * After the exchange, each lane owns exactly one row and keeps that row's
-//    top-(k-1) (score, block) list sorted in VGPRs.  A block's candidate is
-//    inserted, branch-free, while the next block's first key tile runs
-//    through the matrix cores; blocks arrive in ascending id order, so "ties
-//    keep the earlier block" is a strict compare.
+//    top-(k-1) (score, block) list sorted in VGPRs; blocks arrive in
+//    ascending id order, so "ties keep the earlier block" is a strict
+//    compare.
 //  * A tile's MFMAs are interleaved with VALU work that does not depend on
-//    them (the previous tile's max-pool, or the pending insertion), so the
-//    vector ALU runs beside the matrix cores within each wave.
+//    them, so the vector ALU runs beside the matrix cores within each wave:
+//    the previous tile's max-pool, and a block's whole epilogue (its last
+//    tile's max-pool, the exchange, the threshold test and the branch-free
+//    insertion) under the next block's first two key tiles.
 //  * Workgroups are issued heaviest (latest queries, most blocks) first.
 #include <limits.h>
+
+#include <type_traits>
 
 #include "msa_internal.h"
 
@@ -61,9 +64,18 @@ __device__ __forceinline__ int kidx_lds_off(int key, int c) {
 }
 
 // 16 bytes per lane from global memory straight into LDS: the wave writes
-// 1 KB at lds_base (wave-uniform), lane i at lds_base + 16 i.
-__device__ __forceinline__ void lds_dma16(const void* g, void* lds_base) {
-  __builtin_amdgcn_global_load_lds(g, lds_base, 16, 0, 0);
+// 1 KB at lds_base (wave-uniform), lane i at lds_base + 16 i, reading
+// byte offset voff of the buffer r.  The buffer form (MUBUF) of the LDS load
+// is used rather than the global one: with a global load to LDS in flight,
+// the compiler cannot count LDS reads in order and makes every wait for an
+// LDS fragment wait for all of them; with the buffer form it waits for the
+// one fragment an MFMA needs.
+__device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t r, uint32_t voff, void* lds_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds_base, 16, voff, 0, 0, 0);
+}
+// Raw buffer resource over bytes [p, p + bytes) (gfx9 data-format word).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* p, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, bytes, 0x00020000);
 }
 
 __device__ __forceinline__ float max16(const f32x16& a) {
@@ -170,7 +182,7 @@ __global__ __launch_bounds__(kIdxThreads, 1) void index_topk_kernel(
     }
 
     // K^idx blocks go straight from global memory into a 4-buffer LDS ring
-    // (global_load_lds, no registers): while blocks b and b + 1 are scored,
+    // (buffer_load ... lds, no registers): while blocks b and b + 1 are scored,
     // blocks b + 2 and b + 3 are in flight into the other two buffers, and one
     // barrier per two blocks makes them visible.  The padded tile is
     // NSLOT = 128 x (NCH + 1) 16-byte slots; wave instruction j fills slots
@@ -191,23 +203,21 @@ __global__ __launch_bounds__(kIdxThreads, 1) void index_topk_kernel(
     }
     auto stage_block = [&](int blk, int buf) {
       blk = min(blk, Lmax - 1);
-      const uint16_t* src = kbase + static_cast<int64_t>(blk) * BK * DIDX;
+      const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(kbase + static_cast<int64_t>(blk) * BK * DIDX, BK * DIDX * 2);
 #pragma unroll
       for (int q = 0; q < JW; ++q) {
         const int j = wave + kIdxWaves * q;
         if (j < NJ)  // wave-uniform
-          lds_dma16(src + src_off[q], lds + buf * TILE + 1024 * j);
+          lds_dma16(rs, static_cast<uint32_t>(src_off[q]) * 2, lds + buf * TILE + 1024 * j);
       }
     };
 
     // Insertion of a candidate (score, block) into the row's sorted list: the
     // candidate moves down the list, swapping with every smaller entry.  For
-    // lists of up to 15 entries the candidate of block b is inserted,
-    // branch-free, in the same scheduling region as the MFMAs of block b + 1's
-    // first key tile, so its VALU work runs between those MFMAs instead of
-    // stalling the matrix cores; block b + 1's threshold test comes after it,
-    // so the order of insertions is unchanged.  (Longer lists would not fit
-    // the registers that way; they insert at once, when a lane needs it.)
+    // lists of up to 15 entries the insertion is branch-free and split over
+    // the steps of a key tile, so that its VALU work sits between MFMAs
+    // instead of stalling the matrix cores.  (Longer lists would not fit the
+    // registers that way; they insert at once, when a lane needs it.)
     constexpr bool kDefer = IX_DEFER && KP <= 16;
     float pend_x = 0.f;
     int pend_b = 0;
@@ -251,29 +261,69 @@ __global__ __launch_bounds__(kIdxThreads, 1) void index_topk_kernel(
       pend_need = false;
     };
 
-    // Score block b from LDS buffer b % NBUF and update the row's top list.
-    auto score_block = [&](int b) {
-      // Fragment (mt, ks) of this lane: key row 32 mt + n, 16-byte chunk
-      // 2 ks + h.  The fragments of key tile mt + 1 are read while the 2 x
-      // STEPS MFMAs of tile mt run.
-      const uint8_t* tile = lds + (b % NBUF) * TILE + n * KSTR + h * 16;
-      float mx0 = -__builtin_huge_valf(), mx1 = -__builtin_huge_valf();
-      // Software-pipelined: tile mt's MFMAs are interleaved, two at a time,
-      // with VALU work that does not depend on them -- the max-pool of tile
-      // mt - 1, or in the first tile the previous block's deferred insertion
-      // -- so that the vector ALU runs while the matrix cores do.  K
-      // fragments roll: the register that fed step ks is refilled with tile
-      // mt + 1's fragment right after.
-      constexpr int EPK = 16 / STEPS;                      // max-pool elements per step
-      constexpr int IPK = (KM + STEPS - 1) / STEPS;        // insertion entries per step
-      bf16x8 kr[STEPS];
-      f32x16 A[2][2];
+    // Key tile mt of block b uses accumulators A[(b * KT + mt) & 1], so
+    // consecutive tiles alternate also across blocks.  A block's epilogue --
+    // the max-pool of its last tile, the exchange between the half-waves, the
+    // threshold test and the insertion -- runs under the MFMAs of the next
+    // block's first two tiles: the matrix cores go from one block to the next
+    // without waiting for it.  (Lists longer than 15 entries leave no
+    // registers for that; their blocks finish at once, with A[mt & 1].)
+    // mx0 / mx1 collect the pooled maxima of the block whose tiles are being
+    // pooled (column tile 0 / 1).
+    constexpr bool kLate = kDefer;
+    f32x16 A[2][2];
 #pragma unroll
-      for (int ks = 0; ks < STEPS; ++ks) kr[ks] = as_bf16x8(*reinterpret_cast<const u32x4*>(tile + 32 * ks));
-      if (kDefer) insert_begin();
+    for (int st = 0; st < 2; ++st) A[st][0] = A[st][1] = f32x16{};
+    float mx0 = -__builtin_huge_valf(), mx1 = -__builtin_huge_valf();
+    bf16x8 kr[STEPS];
+    auto pool = [&](const f32x16& a0, const f32x16& a1, int e0, int e1) {  // elements [e0, e1)
+#pragma unroll
+      for (int e = e0; e < e1; e += 2) {
+        mx0 = fmaxf(mx0, fmaxf(a0[e], a0[e + 1]));
+        mx1 = fmaxf(mx1, fmaxf(a1[e], a1[e + 1]));
+      }
+    };
+    // Block pb's pooled maxima are complete: lane half 0 holds keys 4h.. of
+    // every 8 for both column tiles; v_permlane32_swap hands half 0 the other
+    // half's column-tile-0 maxima and half 1 the other half's column-tile-1
+    // maxima, so half 0 finishes column tile 0 and half 1 column tile 1.
+    auto finish = [&](int pb) {
+      const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx0), __float_as_uint(mx1), false, false);
+      float score = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+      if constexpr (FORCED) {
+        if ((force_first && pb == 0) || pb > L_mine - window) score = __builtin_huge_valf();
+      }
+      pend_x = score;
+      pend_b = pb;
+      pend_need = pb >= 0 && pb < L_mine && score > ts[KM - 1];
+      mx0 = mx1 = -__builtin_huge_valf();
+    };
+
+    // Score block b (parity PAR = b & 1) from LDS buffer b % NBUF.  Fragment
+    // (mt, ks) of this lane: key row 32 mt + n, 16-byte chunk 2 ks + h.  K
+    // fragments roll: the register that fed step ks of tile mt is refilled
+    // with tile mt + 1's fragment right after its MFMAs, and in the last tile
+    // of the first block of a pair with the next block's first fragment (that
+    // buffer is already visible), so the second block starts with its
+    // operands in registers.  Each pair of MFMAs is followed, inside
+    // scheduling fences, by VALU work that does not depend on it: in tile 0
+    // the max-pool of the previous block's last tile and then its finish, in
+    // tile 1 (KT >= 2) that block's insertion, and from tile 1 on the
+    // max-pool of the tile before.
+    constexpr int EPK = 16 / STEPS;                // max-pool elements per step
+    constexpr int IPK = (KM + STEPS - 1) / STEPS;  // insertion entries per step
+    auto score_block = [&](auto par, int b) {
+      constexpr int PAR = decltype(par)::value;
+      constexpr int SP = ((PAR ^ 1) * KT + KT - 1) & 1;  // the previous block's last tile
+      const uint8_t* tile = lds + (b % NBUF) * TILE + n * KSTR + h * 16;
+      const uint8_t* tnext = lds + ((b + 1) % NBUF) * TILE + n * KSTR + h * 16;
+      if (PAR == 0) {
+#pragma unroll
+        for (int ks = 0; ks < STEPS; ++ks) kr[ks] = as_bf16x8(*reinterpret_cast<const u32x4*>(tile + 32 * ks));
+      }
 #pragma unroll
       for (int mt = 0; mt < KT; ++mt) {
-        const int st = mt & 1;
+        const int st = kLate ? (PAR * KT + mt) & 1 : mt & 1;
 #pragma unroll
         for (int ks = 0; ks < STEPS; ++ks) {
           A[st][0] = mfma32x32x16(kr[ks], qf[0][ks], ks ? A[st][0] : f32x16{});
@@ -281,41 +331,39 @@ __global__ __launch_bounds__(kIdxThreads, 1) void index_topk_kernel(
           __builtin_amdgcn_sched_barrier(0);
           if (mt + 1 < KT)
             kr[ks] = as_bf16x8(*reinterpret_cast<const u32x4*>(tile + 32 * (mt + 1) * KSTR + 32 * ks));
-          if (mt > 0) {
-#pragma unroll
-            for (int e = EPK * ks; e < EPK * (ks + 1); e += 2) {
-              mx0 = fmaxf(mx0, fmaxf(A[st ^ 1][0][e], A[st ^ 1][0][e + 1]));
-              mx1 = fmaxf(mx1, fmaxf(A[st ^ 1][1][e], A[st ^ 1][1][e + 1]));
+          else if (PAR == 0)
+            kr[ks] = as_bf16x8(*reinterpret_cast<const u32x4*>(tnext + 32 * ks));
+          if (mt == 0) {
+            if constexpr (kLate) {
+              pool(A[SP][0], A[SP][1], EPK * ks, EPK * (ks + 1));
+              if (ks == STEPS - 1) {
+                finish(b - 1);
+                if (KT == 1) insert_pending();
+                else insert_begin();
+              }
             }
-          } else if (kDefer) {
-            const int jhi = KM - 1 - IPK * ks, jlo = jhi - IPK + 1;
-            if (jhi >= 0) insert_entries(jhi, jlo < 0 ? 0 : jlo);
+          } else {
+            pool(A[st ^ 1][0], A[st ^ 1][1], EPK * ks, EPK * (ks + 1));
+            if (kDefer && mt == 1) {
+              const int jhi = KM - 1 - IPK * ks, jlo = jhi - IPK + 1;
+              if (jhi >= 0) insert_entries(jhi, jlo < 0 ? 0 : jlo);
+            }
           }
           __builtin_amdgcn_sched_barrier(0);
         }
       }
-      if (kDefer) pend_need = false;
-      mx0 = fmaxf(mx0, max16(A[(KT - 1) & 1][0]));
-      mx1 = fmaxf(mx1, max16(A[(KT - 1) & 1][1]));
-      // Lane half 0 holds keys 4h.. of every 8 for column tile 0 and 1; swap so
-      // that half 0 finishes column tile 0 and half 1 column tile 1.
-      const float send = h ? mx0 : mx1;
-      const float recv = __shfl_xor(send, 32);
-      float score = fmaxf(h ? mx1 : mx0, recv);
-      if constexpr (FORCED) {
-        if ((force_first && b == 0) || b > L_mine - window) score = __builtin_huge_valf();
+      if constexpr (!kLate) {
+        pool(A[(KT - 1) & 1][0], A[(KT - 1) & 1][1], 0, 16);
+        finish(b);
+        if (__any(pend_need)) insert_pending();
       }
-      const bool need = (b < L_mine) && (score > ts[KM - 1]);
-      if constexpr (kDefer) {
-        pend_x = score;
-        pend_b = b;
-        pend_need = need;
-      } else if (__any(need)) {
-        pend_x = score;
-        pend_b = b;
-        pend_need = need;
-        insert_pending();
-      }
+    };
+    // The last block's epilogue, after the loop.
+    auto finish_last = [&](auto par) {
+      constexpr int SL = (decltype(par)::value * KT + KT - 1) & 1;
+      pool(A[SL][0], A[SL][1], 0, 16);
+      finish(Lmax - 1);
+      insert_pending();
     };
 
     if (Lmax > 0) {
@@ -329,14 +377,17 @@ __global__ __launch_bounds__(kIdxThreads, 1) void index_topk_kernel(
         stage_block(b + 2, (b + 2) % NBUF);
         stage_block(b + 3, (b + 3) % NBUF);
       }
-      score_block(b);
-      if (b + 1 < Lmax) score_block(b + 1);
+      score_block(std::integral_constant<int, 0>{}, b);
+      if (b + 1 < Lmax) score_block(std::integral_constant<int, 1>{}, b + 1);
       // this wave's ring loads have landed; the barrier makes every wave's
       // visible and frees the two buffers just scored
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
     }
-    if constexpr (kDefer) insert_pending();  // the last block's candidate
+    if (kLate && Lmax > 0) {
+      if (KT % 2 == 0 || ((Lmax - 1) & 1)) finish_last(std::integral_constant<int, 1>{});
+      else finish_last(std::integral_constant<int, 0>{});
+    }
   }
 
   if (!mine_ok) return;

@@ -8,7 +8,10 @@
 //    partial-output pieces at scattered places).
 //  * MFMA: back-to-back v_mfma_f32_32x32x16_bf16 on register operands, four
 //    independent accumulators per wave, every SIMD busy (the clock the chip
-//    sustains under that load sets the ceiling).
+//    sustains under that load sets the ceiling).  Two operand kinds: a few
+//    fixed low-entropy patterns, and random unit-scale bf16 fragments that
+//    change from one MFMA to the next, as real Q and K tiles do; the matrix
+//    cores draw more power on the latter and the clock drops accordingly.
 //
 // Every index is reduced modulo its buffer, so all accesses stay inside the
 // allocations.  Prints one JSON line.
@@ -91,6 +94,42 @@ __global__ __launch_bounds__(kThreads) void rand_kernel(u32x4* a, uint64_t nchun
   if (MODE == 0 && acc[0] == 0x12345678u && acc[1] == 0x9abcdefu) sink[threadIdx.x] = acc;
 }
 
+// Random operands: 8 A and 8 B fragments per lane, bf16 values of random
+// sign and magnitude in [0.25, 1), cycled so that consecutive MFMAs see
+// different data.
+__device__ __forceinline__ bf16x8 random_fragment(uint64_t seed) {
+  u32x4 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint64_t z = mix64(seed * 4 + i);
+    const uint32_t lo = 0x3E00u | (static_cast<uint32_t>(z) & 0x81FFu);
+    const uint32_t hi = 0x3E00u | (static_cast<uint32_t>(z >> 32) & 0x81FFu);
+    r[i] = lo | (hi << 16);
+  }
+  return __builtin_bit_cast(bf16x8, r);
+}
+
+__global__ __launch_bounds__(kThreads) void mfma_rand_kernel(int iters, float* sink) {
+  const uint64_t t = static_cast<uint64_t>(blockIdx.x) * kThreads + threadIdx.x;
+  bf16x8 a[8], b[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    a[j] = random_fragment(t * 16 + j);
+    b[j] = random_fragment(t * 16 + 8 + j);
+  }
+  f32x16 c[4] = {};
+  for (int i = 0; i < iters; i += 64) {  // iters: a multiple of 64
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        c[j & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[j], b[(3 * j + r) & 7], c[j & 3], 0, 0, 0);
+    }
+  }
+  const float s = c[0][0] + c[1][1] + c[2][2] + c[3][3];
+  if (s == 1.2345f) sink[t % kThreads] = s;
+}
+
 __global__ __launch_bounds__(kThreads) void mfma_kernel(int iters, float* sink) {
   const int t = threadIdx.x;
   u32x4 ra = {static_cast<uint32_t>(t) * 0x3F803F80u, 0x3F003F00u, 0x3E803E80u, 0x3F803F80u};
@@ -159,12 +198,13 @@ int main() {
   const unsigned mgrid = static_cast<unsigned>(cus) * 2;  // 8 waves per CU, two per SIMD
   const float t_mf = time_ms([&] { hipLaunchKernelGGL(mfma_kernel, dim3(mgrid), dim3(kThreads), 0, 0, iters, reinterpret_cast<float*>(sink)); }, 3);
   const double mflop = static_cast<double>(mgrid) * (kThreads / 64) * iters * 4 * (32.0 * 32 * 16 * 2);
+  const float t_mr = time_ms([&] { hipLaunchKernelGGL(mfma_rand_kernel, dim3(mgrid), dim3(kThreads), 0, 0, 4 * iters, reinterpret_cast<float*>(sink)); }, 3);
 
   printf("{\"hbm_seq_read_GBs\": %.1f, \"hbm_seq_write_GBs\": %.1f, \"hbm_copy_GBs\": %.1f, "
          "\"hbm_rand4k_read_GBs\": %.1f, \"hbm_rand4k_write_GBs\": %.1f, \"hbm_rand4k_mixed_GBs\": %.1f, "
-         "\"mfma_bf16_TFLOPs\": %.1f}\n",
+         "\"mfma_bf16_TFLOPs\": %.1f, \"mfma_bf16_random_TFLOPs\": %.1f}\n",
          sb / t_rd / 1e6, sb / t_wr / 1e6, 2 * sb / t_cp / 1e6, rb / t_rr / 1e6, rb / t_rw / 1e6,
-         2 * rb / t_rm / 1e6, mflop / t_mf / 1e9);
+         2 * rb / t_rm / 1e6, mflop / t_mf / 1e9, mflop / t_mr / 1e9);
   CHECK(hipFree(a));
   CHECK(hipFree(b));
   CHECK(hipFree(sink));
