@@ -247,7 +247,7 @@ __global__ __launch_bounds__(kBT, 1) void bwd_main_kernel(
   __shared__ __attribute__((aligned(16))) int ri_i[kRows];
   __shared__ __attribute__((aligned(16))) float ri_lse2[kRows], ri_dlt[kRows];
   __shared__ int64_t ri_orow[kRows];
-  __shared__ __attribute__((aligned(16))) float tch[IDX ? EC * kBk : 4];  // teacher sums [query][key]
+  __shared__ __attribute__((aligned(16))) float tch[IDX ? EC * kBk : 4];  // teacher [query][key]
 
   PassIter it{segp, B_c, nseqs};
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, n = lane & 31, h = lane >> 5;
@@ -333,10 +333,6 @@ __global__ __launch_bounds__(kBT, 1) void bwd_main_kernel(
       ri_dlt[tid] = p_i >= 0 ? p_dl : 0.f;
       ri_orow[tid] = p_orow;
     }
-    if constexpr (IDX) {
-#pragma unroll
-      for (int j = 0; j < EC * kBk / kBT; ++j) tch[tid + kBT * j] = 0.f;
-    }
     if (D.seq != cur_seq || D.blk != cur_blk) {
       flush();
       cur_seq = D.seq;
@@ -406,15 +402,39 @@ __global__ __launch_bounds__(kBT, 1) void bwd_main_kernel(
       db[2 * rt] = pack_step(ds, 0);
       db[2 * rt + 1] = pack_step(ds, 1);
       if constexpr (IDX) {
-        // teacher: the lane's run of RUN consecutive elements is one query's
-        // heads; the G heads of a query meet in LDS
-        constexpr int RUN = G < 4 ? G : 4;
+        // teacher: the mean over a query's G heads of this lane's key.  The
+        // lane holds rows acc_row(e, h): for G <= 4 each run of G elements is
+        // one query's heads; for G = 8 elements 4a .. 4a + 3 of the two lane
+        // halves are the two halves of one query's heads, for G = 16 elements
+        // 0-7 (8-15) of both halves.  The halves meet through
+        // v_permlane32_swap (half 0 receives the total of the first operand,
+        // half 1 of the second), so every (query, key) value is formed in
+        // registers and stored once, with no LDS atomics.
+        if constexpr (G <= 4) {
 #pragma unroll
-        for (int e0 = 0; e0 < 16; e0 += RUN) {
-          float acc = 0.f;
+          for (int e0 = 0; e0 < 16; e0 += G) {
+            float acc = 0.f;
 #pragma unroll
-          for (int e = e0; e < e0 + RUN; ++e) acc += p[e];
-          atomicAdd(&tch[((32 * rt + acc_row(e0, h)) / G) * kBk + key_l], acc * kInvG);
+            for (int e = e0; e < e0 + G; ++e) acc += p[e];
+            tch[((32 * rt + acc_row(e0, h)) / G) * kBk + key_l] = acc * kInvG;
+          }
+        } else {
+          constexpr int NS = 16 / (G / 2);  // per-half sums: 4 (G = 8) or 2 (G = 16)
+          float hs[NS];
+#pragma unroll
+          for (int j = 0; j < NS; ++j) {
+            hs[j] = 0.f;
+#pragma unroll
+            for (int e = j * (G / 2); e < (j + 1) * (G / 2); ++e) hs[j] += p[e];
+          }
+#pragma unroll
+          for (int j = 0; j < NS; j += 2) {
+            const auto x = __builtin_amdgcn_permlane32_swap(__float_as_uint(hs[j]), __float_as_uint(hs[j + 1]),
+                                                             false, false);
+            const float tot = __uint_as_float(x[0]) + __uint_as_float(x[1]);
+            // query (32 rt + 8 j (G = 8) or 16 j (G = 16)) / G, plus the half
+            tch[((32 * rt) / G + j + h) * kBk + key_l] = tot * kInvG;
+          }
         }
       }
     }
