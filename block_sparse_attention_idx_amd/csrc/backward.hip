@@ -75,6 +75,17 @@ constexpr float kLn2 = 0.69314718055994531f;
 // to 16-row step s are the 8 consecutive columns 16 s + 8 h .. + 7.
 __device__ __forceinline__ int tpos(int rho) { return (rho & ~12) | ((rho & 4) << 1) | ((rho & 8) >> 1); }
 
+// Byte offset of byte b (0 .. 127) of row d in a transposed tile.  The
+// row's eight 16-byte chunks are permuted, chunk c stored at position
+// c ^ ((d / 8) % 8): the 8-byte stores that fill the tile hit rows 8 apart
+// at one column, which at the 144-byte row stride fell on two sets of banks
+// (an 8-way conflict); swizzled they take the minimum two passes.  Eight
+// consecutive rows, which the fragment reads take together, share one
+// permutation, so those reads stay conflict-free.
+__device__ __forceinline__ int tr_off(int d, int b) {
+  return d * kTStr + ((((b >> 4) ^ (d >> 3)) & 7) << 4) + (b & 15);
+}
+
 // Accumulator element e of a 32x32 tile holds row 8 (e / 4) + 4 h + (e % 4).
 __device__ __forceinline__ int acc_row(int e, int h) { return 8 * (e >> 2) + 4 * h + (e & 3); }
 
@@ -154,7 +165,7 @@ __device__ __forceinline__ void put_rows(const u32x4 (&w)[4], uint8_t* rm, uint8
     for (int dd = 0; dd < 8; ++dd) {
       const u32x2 v = {bf16_of(w[0], dd) | (bf16_of(w[1], dd) << 16),
                        bf16_of(w[2], dd) | (bf16_of(w[3], dd) << 16)};
-      *reinterpret_cast<u32x2*>(tr + (8 * dg + dd) * kTStr + 2 * col) = v;
+      *reinterpret_cast<u32x2*>(tr + tr_off(8 * dg + dd, 2 * col)) = v;
     }
   }
 }
@@ -447,7 +458,7 @@ __global__ __launch_bounds__(kBT, 1) void bwd_main_kernel(
     for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
       for (int st = 0; st < 4; ++st) {
-        const int off = (32 * dt + n) * kTStr + 32 * st + 16 * h;
+        const int off = tr_off(32 * dt + n, 32 * st + 16 * h);
         dvt[dt] = mfma32x32x16(lds_frag(dot_lds + off), pb[st], dvt[dt]);
         dkt[dt] = mfma32x32x16(lds_frag(qt_lds + off), db[st], dkt[dt]);
       }
@@ -619,7 +630,7 @@ __global__ __launch_bounds__(kBT, 1) void bwd_idx_kernel(
       for (int dd = 0; dd < 8; ++dd) {
         const u32x2 v = {bf16_of(wqi[0], dd) | (bf16_of(wqi[1], dd) << 16),
                          bf16_of(wqi[2], dd) | (bf16_of(wqi[3], dd) << 16)};
-        *reinterpret_cast<u32x2*>(qit_lds + (8 * dg + dd) * kTStr + 2 * col) = v;
+        *reinterpret_cast<u32x2*>(qit_lds + tr_off(8 * dg + dd, 2 * col)) = v;
       }
     }
 #pragma unroll
@@ -694,7 +705,7 @@ __global__ __launch_bounds__(kBT, 1) void bwd_idx_kernel(
     for (int t2 = 0; t2 < TT; ++t2)
 #pragma unroll
       for (int st = 0; st < KE; ++st)
-        dkit[t2] = mfma32x32x16(lds_frag(qit_lds + (32 * t2 + n) * kTStr + 32 * st + 16 * h), gb[st], dkit[t2]);
+        dkit[t2] = mfma32x32x16(lds_frag(qit_lds + tr_off(32 * t2 + n, 32 * st + 16 * h)), gb[st], dkit[t2]);
     __syncthreads();
 
     // ---- dq_idx^T = k_idx^T g^T over the block's keys (rows past the chunk
