@@ -19,9 +19,10 @@
 // 256 / G consecutive entries (query, slot); persistent workgroups take equal
 // contiguous shares of the pass list, so every workgroup keeps one key block
 // for a run of passes.  Per workgroup of 4 waves, wave w owns keys
-// 32 w .. 32 w + 31 of the block, keeps their K, V (and K^idx) rows in
-// registers and accumulates their dK^T, dV^T (and dK^idx^T) in MFMA
-// accumulators across the run; when the block changes, the accumulators are
+// 32 w .. 32 w + 31 of the block (the block's K and V rows are staged in LDS
+// when the block changes; the index branch keeps its K^idx rows in registers)
+// and accumulates their dK^T, dV^T (and dK^idx^T) in MFMA accumulators across
+// the run; when the block changes, the accumulators are
 // added to fp32 gradient buffers with global atomics (a block's passes may be
 // shared by two workgroups, and with more index heads than K/V heads several
 // groups share a K/V head).  dQ (and dq_idx) need a sum over the block's keys,
@@ -30,16 +31,17 @@
 //
 // Rows of a pass are processed 64 at a time (64 / G queries x G heads).  All
 // products run on v_mfma_f32_32x32x16_bf16:
-//   S  = Q K^T       A = Q rows (LDS),       B = K rows (registers)
-//   dP = dO V^T      A = dO rows (LDS),      B = V rows (registers)
-//   dV^T += dO^T P   A = dO^T (LDS),         B = P straight from the accumulator
-//   dK^T += Q^T dS   A = Q^T (LDS),          B = dS straight from the accumulator
-//   dQ^T = K^T dS^T  A = K^T (LDS),          B = dS rows (LDS)
+//   S  = Q K^T       A = Q rows (LDS),       B = K rows (LDS)
+//   dP = dO V^T      A = dO rows (LDS),      B = V rows (LDS)
+//   dV^T += dO^T P   A = dO^T (LDS, read transposed), B = P straight from the accumulator
+//   dK^T += Q^T dS   A = Q^T (LDS, read transposed),  B = dS straight from the accumulator
+//   dQ^T = K^T dS^T  A = K^T (LDS, read transposed),  B = dS rows (LDS)
 // S, P and dS have the keys on the lane (column) index, so the row-reducing
-// products take them as B operands without a shuffle; the transposed A
-// operands store the rows in the order that makes this exact (row bits 2 and 3
-// swapped, so that the 8 rows a lane contributes to one 16-row step are one
-// 16-byte chunk).
+// products take them as B operands without a shuffle.  Q, dO, K and V sit in
+// LDS once, row-major; the transposed A operands come straight out of those
+// tiles through ds_read_b64_tr_b16, in the row order the accumulator gives
+// the B operand (the 8 rows a lane contributes to one 16-row step are rows
+// 4 h .. 4 h + 3 and 8 + 4 h .. 8 + 4 h + 3 of the step).
 //
 // The main-branch kernel, which has every head's probabilities, also forms
 // the teacher distribution (the mean over the group's heads) and writes one
@@ -67,6 +69,7 @@ constexpr int kBT = 64 * kBW;    // threads
 constexpr int kRows = 64;        // (query, head) rows per chunk
 constexpr int kStr = 272;        // row-major LDS row: 128 bf16 + 16 B of padding
 constexpr int kTStr = 144;       // transposed LDS row: 64 bf16 + 16 B of padding
+constexpr int kRS = 288;         // main-branch row-major tiles: 128 bf16 + 32 B of padding
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.69314718055994531f;
 
@@ -84,6 +87,29 @@ __device__ __forceinline__ int tpos(int rho) { return (rho & ~12) | ((rho & 4) <
 // permutation, so those reads stay conflict-free.
 __device__ __forceinline__ int tr_off(int d, int b) {
   return d * kTStr + ((((b >> 4) ^ (d >> 3)) & 7) << 4) + (b & 15);
+}
+
+// A operand of v_mfma_f32_32x32x16_bf16 read transposed out of a row-major
+// bf16 tile T (row stride kRS): lane (n, h) receives, as k-values j = 0 .. 7,
+// T[r_lo + j][c0 + n] for j < 4 and T[r_hi + j - 4][c0 + n] for j >= 4 (r_lo,
+// r_hi may depend on h).  ds_read_b64_tr_b16 works on groups of 16 lanes:
+// output lane i of a group receives, as its element m, element i % 4 of the
+// 8-byte piece addressed by lane i / 4 + 4 m of the group.  So lane s of group
+// g addresses row r + s / 4 and columns c0 + 16 (g % 2) + 4 (s % 4) .. + 3, and
+// two reads (rows from r_lo, then from r_hi) give the eight k-values.  At the
+// 288-byte stride the 16 pieces of a group (4 rows x 4 column quarters) fall
+// on 32 distinct banks.
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ bf16x8 lds_frag_tr(const uint8_t* tile, int r_lo, int r_hi, int c0) {
+  const int l = threadIdx.x & 63, s = l & 15;
+  const int off = (s >> 2) * kRS + 2 * (c0 + 16 * ((l >> 4) & 1) + 4 * (s & 3));
+  typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+  const i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(tile + r_lo * kRS + off));
+  const i16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(tile + r_hi * kRS + off));
+  return as_bf16x8(u32x4{__builtin_bit_cast(uint32_t, __builtin_shufflevector(a, a, 0, 1)),
+                         __builtin_bit_cast(uint32_t, __builtin_shufflevector(a, a, 2, 3)),
+                         __builtin_bit_cast(uint32_t, __builtin_shufflevector(b, b, 0, 1)),
+                         __builtin_bit_cast(uint32_t, __builtin_shufflevector(b, b, 2, 3))});
 }
 
 // Accumulator element e of a 32x32 tile holds row 8 (e / 4) + 4 h + (e % 4).
@@ -144,8 +170,7 @@ __device__ __forceinline__ EntryRef entry_ref(uint32_t ent, int seq, int kslots,
 // Staging of 64 rows of a [*, d_h = 128] bf16 tensor in two halves, for
 // software pipelining: load_rows issues this thread's global loads (16-byte
 // chunk t % 16 of rows 4 (t / 16) .. + 3; `row_ptr(rho)` must give a readable
-// row), put_rows writes them row-major into `rm` and transposed into `tr`
-// (either may be null).
+// row), put_rows writes them row-major into `rm` (row stride kRS).
 template <typename RowPtr>
 __device__ __forceinline__ void load_rows(RowPtr row_ptr, u32x4 (&w)[4]) {
   const int dg = threadIdx.x & 15, rc = threadIdx.x >> 4;
@@ -153,21 +178,10 @@ __device__ __forceinline__ void load_rows(RowPtr row_ptr, u32x4 (&w)[4]) {
   for (int j = 0; j < 4; ++j) w[j] = *reinterpret_cast<const u32x4*>(row_ptr(4 * rc + j) + 8 * dg);
 }
 
-__device__ __forceinline__ void put_rows(const u32x4 (&w)[4], uint8_t* rm, uint8_t* tr) {
+__device__ __forceinline__ void put_rows(const u32x4 (&w)[4], uint8_t* rm) {
   const int dg = threadIdx.x & 15, rc = threadIdx.x >> 4;
-  if (rm) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) *reinterpret_cast<u32x4*>(rm + (4 * rc + j) * kStr + 16 * dg) = w[j];
-  }
-  if (tr) {
-    const int col = tpos(4 * rc);
-#pragma unroll
-    for (int dd = 0; dd < 8; ++dd) {
-      const u32x2 v = {bf16_of(w[0], dd) | (bf16_of(w[1], dd) << 16),
-                       bf16_of(w[2], dd) | (bf16_of(w[3], dd) << 16)};
-      *reinterpret_cast<u32x2*>(tr + tr_off(8 * dg + dd, 2 * col)) = v;
-    }
-  }
+  for (int j = 0; j < 4; ++j) *reinterpret_cast<u32x4*>(rm + (4 * rc + j) * kRS + 16 * dg) = w[j];
 }
 
 // The chunks of a workgroup's passes in order: pass descriptor and first
@@ -249,11 +263,10 @@ __global__ __launch_bounds__(kBT, 1) void bwd_main_kernel(
     float* __restrict__ tch_out) {
   constexpr int EC = kRows / G;  // queries per chunk
   constexpr float kInvG = 1.f / G;
-  __shared__ __attribute__((aligned(16))) uint8_t qr_lds[kRows * kStr];
-  __shared__ __attribute__((aligned(16))) uint8_t dor_lds[kRows * kStr];
-  __shared__ __attribute__((aligned(16))) uint8_t qt_lds[kDh * kTStr];
-  __shared__ __attribute__((aligned(16))) uint8_t dot_lds[kDh * kTStr];
-  __shared__ __attribute__((aligned(16))) uint8_t kt_lds[kDh * kStr];
+  __shared__ __attribute__((aligned(16))) uint8_t qr_lds[kRows * kRS];
+  __shared__ __attribute__((aligned(16))) uint8_t dor_lds[kRows * kRS];
+  __shared__ __attribute__((aligned(16))) uint8_t k_lds[kBk * kRS];
+  __shared__ __attribute__((aligned(16))) uint8_t v_lds[kBk * kRS];
   __shared__ __attribute__((aligned(16))) uint8_t ds_lds[kRows * kStr];
   __shared__ __attribute__((aligned(16))) int ri_i[kRows];
   __shared__ __attribute__((aligned(16))) float ri_lse2[kRows], ri_dlt[kRows];
@@ -266,7 +279,6 @@ __global__ __launch_bounds__(kBT, 1) void bwd_main_kernel(
   const int key_l = 32 * wave + n;  // this lane's key within the block
 
   int cur_seq = -1, cur_blk = 0, cur_nvalid = 0;
-  u32x4 kf[8], vf[8];
   f32x16 dkt[4], dvt[4];
 
   auto flush = [&]() {
@@ -336,8 +348,8 @@ __global__ __launch_bounds__(kBT, 1) void bwd_main_kernel(
     const PassDesc D = cur.D;
     const int bat = D.seq / H_sel, r = D.seq - bat * H_sel;
     // ---- this chunk's rows and constants into LDS
-    put_rows(wq, qr_lds, qt_lds);
-    put_rows(wdo, dor_lds, dot_lds);
+    put_rows(wq, qr_lds);
+    put_rows(wdo, dor_lds);
     if (tid < kRows) {
       ri_i[tid] = p_i;
       ri_lse2[tid] = p_i >= 0 ? p_l * kLog2e : 0.f;
@@ -350,25 +362,37 @@ __global__ __launch_bounds__(kBT, 1) void bwd_main_kernel(
       cur_blk = D.blk;
       const int64_t key0 = static_cast<int64_t>(D.blk) * kBk;
       cur_nvalid = static_cast<int>(min<int64_t>(kBk, N - key0));
+      // the block's K and V rows into LDS, row-major (keys at or past the
+      // sequence end as zeros): thread t moves 16-byte chunk t % 16 of keys
+      // t / 16 + 16 p.  Every wave finished the previous chunk's reads of
+      // them (trailing barrier); the barrier below publishes them.
       const int64_t rstride = static_cast<int64_t>(H_kv) * kDh;
-      const int64_t base = ((static_cast<int64_t>(bat) * N + key0) * H_kv + (r >> kv_shift)) * kDh +
-                           min(key_l, cur_nvalid - 1) * rstride;
-      const bool kv_ok = key_l < cur_nvalid;
+      const uint16_t* kb = k + ((static_cast<int64_t>(bat) * N + key0) * H_kv + (r >> kv_shift)) * kDh;
+      const uint16_t* vb = v + ((static_cast<int64_t>(bat) * N + key0) * H_kv + (r >> kv_shift)) * kDh;
+      const int ch = tid & 15;
 #pragma unroll
-      for (int ks = 0; ks < 8; ++ks) {
-        const u32x4 a = *reinterpret_cast<const u32x4*>(k + base + 16 * ks + 8 * h);
-        const u32x4 b = *reinterpret_cast<const u32x4*>(v + base + 16 * ks + 8 * h);
-        kf[ks] = kv_ok ? a : u32x4{0u, 0u, 0u, 0u};
-        vf[ks] = kv_ok ? b : u32x4{0u, 0u, 0u, 0u};
+      for (int p2 = 0; p2 < kBk / 16; p2 += 4) {
+        u32x4 a[4], b[4];
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          const int key = (tid >> 4) + 16 * (p2 + p);
+          const int64_t o = min(key, cur_nvalid - 1) * rstride + 8 * ch;
+          a[p] = *reinterpret_cast<const u32x4*>(kb + o);
+          b[p] = *reinterpret_cast<const u32x4*>(vb + o);
+        }
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          const int key = (tid >> 4) + 16 * (p2 + p);
+          const bool ok = key < cur_nvalid;
+          *reinterpret_cast<u32x4*>(k_lds + key * kRS + 16 * ch) = ok ? a[p] : u32x4{0u, 0u, 0u, 0u};
+          *reinterpret_cast<u32x4*>(v_lds + key * kRS + 16 * ch) = ok ? b[p] : u32x4{0u, 0u, 0u, 0u};
+        }
       }
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt) {
         dkt[dt] = f32x16{};
         dvt[dt] = f32x16{};
       }
-      // every wave finished the previous chunk's dQ (trailing barrier), so
-      // K^T can be replaced; the barrier below publishes it
-      store_keys_t<8>(kf, kt_lds, wave, n, h);
     }
     const int key_abs = D.blk * kBk + key_l;
     // ---- the next chunk's entry words (the last chunk reloads its own)
@@ -384,9 +408,10 @@ __global__ __launch_bounds__(kBT, 1) void bwd_main_kernel(
       f32x16 s = {}, dp = {};
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks) {
-        const int off = (32 * rt + n) * kStr + 32 * ks + 16 * h;
-        s = mfma32x32x16(lds_frag(qr_lds + off), as_bf16x8(kf[ks]), s);
-        dp = mfma32x32x16(lds_frag(dor_lds + off), as_bf16x8(vf[ks]), dp);
+        const int off = (32 * rt + n) * kRS + 32 * ks + 16 * h;
+        const int koff = key_l * kRS + 32 * ks + 16 * h;
+        s = mfma32x32x16(lds_frag(qr_lds + off), lds_frag(k_lds + koff), s);
+        dp = mfma32x32x16(lds_frag(dor_lds + off), lds_frag(v_lds + koff), dp);
       }
       f32x16 p, ds;
 #pragma unroll
@@ -458,9 +483,11 @@ __global__ __launch_bounds__(kBT, 1) void bwd_main_kernel(
     for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
       for (int st = 0; st < 4; ++st) {
-        const int off = tr_off(32 * dt + n, 32 * st + 16 * h);
-        dvt[dt] = mfma32x32x16(lds_frag(dot_lds + off), pb[st], dvt[dt]);
-        dkt[dt] = mfma32x32x16(lds_frag(qt_lds + off), db[st], dkt[dt]);
+        // rows 16 st + 4 h + (0..3) and 16 st + 8 + 4 h + (0..3): the order in
+        // which pb[st] and db[st] hold them
+        const int r_lo = 16 * st + 4 * h, r_hi = r_lo + 8;
+        dvt[dt] = mfma32x32x16(lds_frag_tr(dor_lds, r_lo, r_hi, 32 * dt), pb[st], dvt[dt]);
+        dkt[dt] = mfma32x32x16(lds_frag_tr(qr_lds, r_lo, r_hi, 32 * dt), db[st], dkt[dt]);
       }
     __syncthreads();
 
@@ -474,7 +501,7 @@ __global__ __launch_bounds__(kBT, 1) void bwd_main_kernel(
         const bf16x8 b = lds_frag(ds_lds + (32 * rt + n) * kStr + 32 * kk + 16 * h);
 #pragma unroll
         for (int j = 0; j < 2; ++j)
-          qa[j] = mfma32x32x16(lds_frag(kt_lds + (32 * (dt0 + j) + n) * kStr + 32 * kk + 16 * h), b, qa[j]);
+          qa[j] = mfma32x32x16(lds_frag_tr(k_lds, 16 * kk + 8 * h, 16 * kk + 8 * h + 4, 32 * (dt0 + j)), b, qa[j]);
       }
       if constexpr (IDX) {
         // the chunk's teacher rows, one per entry (padding rows: the spare
