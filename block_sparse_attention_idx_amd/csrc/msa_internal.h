@@ -68,18 +68,6 @@ __device__ __forceinline__ u32x2 e4m3x4_to_bf16x4_int(uint32_t w) {
   return r;
 }
 
-// 4 OCP e4m3fn codes (one u32) -> 4 bf16 (two u32), each value times 2^-8,
-// exactly: v_cvt_scalef32_pk_bf16_fp8 converts two codes (bytes 0-1, or 2-3
-// with the word select) per instruction.  Every e4m3 value, subnormals
-// included, is a bf16 value, and so is its product with 2^-8; the NaN codes
-// (0x7F, 0xFF) do not occur in saturating quantised inputs.
-__device__ __forceinline__ u32x2 e4m3x4_to_bf16x4(uint32_t w) {
-  u32x2 r;
-  r[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 0x1p-8f, false));
-  r[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 0x1p-8f, true));
-  return r;
-}
-
 // ---------------------------------------------------------------- launchers
 // Each returns hipSuccess or the HIP error of the launch.
 

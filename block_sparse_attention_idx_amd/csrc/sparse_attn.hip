@@ -43,8 +43,10 @@
 //    operation of the loop is issued unconditionally, so the compiler's
 //    in-order vmcnt waits never have to cover the stores or the loads just
 //    issued.
-//  * Softmax in base 2 (v_exp_f32) with the scale folded into one FMA; fp8
-//    (OCP e4m3) inputs are widened exactly to bf16 when used and the
+//  * Softmax in base 2 (v_exp_f32) with the scale folded into one FMA.  fp8
+//    (OCP e4m3) inputs: the scores come from v_mfma_scale_f32_32x32x64_f8f6f4
+//    on the Q and K codes (exact products, K kept as codes in LDS), V is
+//    widened exactly to bf16 when staged (P V stays a bf16 product), and the
 //    per-tensor scales are folded into the softmax scale and the output scale.
 #include "attn_tile.h"
 #include "msa_internal.h"
@@ -70,6 +72,9 @@ constexpr int kThreads = 64 * kWaves;
 //  * Output tile, 272 B per row: 16-byte writes of rows n .. n + 15 and
 //    16-byte reads of the 16 chunks of one row are both conflict free.
 constexpr int kKStride = tile::kStr;
+// fp8: K stays as e4m3 codes, 144 B per key row (128 codes + 16 B): the
+// 16-byte reads of rows n .. n + 15 start at banks 36 n mod 64, all distinct.
+constexpr int kK8Stride = 144;
 constexpr int kVStride = tile::kStr;
 constexpr int kOStride = tile::kStr;
 
@@ -123,11 +128,7 @@ __device__ __forceinline__ void stage_kv(const uint8_t* __restrict__ kb, const u
 #pragma unroll
     for (int p = 0; p < R; ++p) {
       const int key = (tid >> 3) + (kThreads / 8) * p, cc = tid & 7;
-      const u32x4 w = key < nvalid ? wk[p] : u32x4{0u, 0u, 0u, 0u};
-      const u32x2 a = e4m3x4_to_bf16x4_int(w[0]), b = e4m3x4_to_bf16x4_int(w[1]);
-      const u32x2 c2 = e4m3x4_to_bf16x4_int(w[2]), d2 = e4m3x4_to_bf16x4_int(w[3]);
-      *reinterpret_cast<u32x4*>(k_lds + k_lds_off(key, 2 * cc)) = u32x4{a[0], a[1], b[0], b[1]};
-      *reinterpret_cast<u32x4*>(k_lds + k_lds_off(key, 2 * cc + 1)) = u32x4{c2[0], c2[1], d2[0], d2[1]};
+      *reinterpret_cast<u32x4*>(k_lds + key * kK8Stride + cc * 16) = key < nvalid ? wk[p] : u32x4{0u, 0u, 0u, 0u};
     }
   }
   // V: item (dg, kc) transposes the 8 dims 8 dg .. 8 dg + 7 of keys
@@ -169,11 +170,10 @@ __device__ __forceinline__ void stage_kv(const uint8_t* __restrict__ kb, const u
   }
 }
 
-// Q fragments (B operand of S^T) of one row, dims 16 ks + 8 h .. + 8, kept as
-// loaded (bf16: 8 x 16 B; fp8: 8 x 8 B of codes) and widened when used (two
-// v_cvt_scalef32_pk_bf16_fp8 per 4 codes), so a prefetch is never waited on
-// before its pass.  K and V are widened once per staging with integer
-// arithmetic (the conversion instruction there made the compiler spill).
+// Q fragments (B operand of S^T) of one row, kept as loaded, so a prefetch is
+// never waited on before its pass: bf16 dims 16 ks + 8 h .. + 7 (8 x 16 B),
+// fp8 codes as below.  V is widened once per staging with integer arithmetic
+// (the conversion instruction there made the compiler spill).
 template <bool FP8>
 struct QFrag;
 template <>
@@ -185,17 +185,24 @@ struct QFrag<false> {
   }
   __device__ __forceinline__ bf16x8 get(int ks) const { return as_bf16x8(w[ks]); }
 };
+// fp8: the codes of dims 64 s + 32 h .. + 31 (s = 0, 1), the B operand of
+// one v_mfma_scale_f32_32x32x64_f8f6f4 each.
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+__device__ __forceinline__ i32x8 as_i32x8(const u32x4& a, const u32x4& b) {
+  return i32x8{static_cast<int>(a[0]), static_cast<int>(a[1]), static_cast<int>(a[2]), static_cast<int>(a[3]),
+               static_cast<int>(b[0]), static_cast<int>(b[1]), static_cast<int>(b[2]), static_cast<int>(b[3])};
+}
 template <>
 struct QFrag<true> {
-  u32x2 w[8];
+  u32x4 w[4];
   __device__ __forceinline__ void load(const uint8_t* __restrict__ qr, int h) {
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) w[ks] = *reinterpret_cast<const u32x2*>(qr + 16 * ks + 8 * h);
+    for (int s = 0; s < 2; ++s) {
+      w[2 * s] = *reinterpret_cast<const u32x4*>(qr + 64 * s + 32 * h);
+      w[2 * s + 1] = *reinterpret_cast<const u32x4*>(qr + 64 * s + 32 * h + 16);
+    }
   }
-  __device__ __forceinline__ bf16x8 get(int ks) const {
-    const u32x2 a = e4m3x4_to_bf16x4(w[ks][0]), b = e4m3x4_to_bf16x4(w[ks][1]);
-    return as_bf16x8(u32x4{a[0], a[1], b[0], b[1]});
-  }
+  __device__ __forceinline__ i32x8 get8(int s) const { return as_i32x8(w[2 * s], w[2 * s + 1]); }
 };
 
 // BKS: log2 of the key block size.  Blocks of 32 or 64 tokens (the paper's
@@ -299,13 +306,26 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void sparse_attn_kernel(
       return as_bf16x8(*reinterpret_cast<const u32x4*>(k_base + 32 * mt * kKStride + 32 * ks));
     };
     if constexpr (FP8) {
+      // The e4m3 codes go straight into v_mfma_scale_f32_32x32x64_f8f6f4
+      // (exact products, fp32 sums): lane (n, h) supplies key 32 mt + n and
+      // row n with the same 32 dims 64 s + 32 h .. + 31, and both operands
+      // carry the block scale 2^-8 (E8M0 code 119), the factor the widening
+      // to bf16 applies to each value, so the scores are those of the bf16
+      // path up to the order of the fp32 sums.
+      const uint8_t* k8 = k_lds + n * kK8Stride + 32 * h;
+      auto kfrag8 = [&](int mt, int s2) {
+        const uint8_t* p = k8 + 32 * mt * kK8Stride + 64 * s2;
+        return as_i32x8(*reinterpret_cast<const u32x4*>(p), *reinterpret_cast<const u32x4*>(p + 16));
+      };
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) acc[mt] = f32x16{};
 #pragma unroll
-      for (int ks = 0; ks < 8; ++ks) {
-        const bf16x8 qk = q.get(ks);
+      for (int s2 = 0; s2 < 2; ++s2) {
+        const i32x8 qk = q.get8(s2);
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt) acc[mt] = mfma32x32x16(kfrag(mt, ks), qk, acc[mt]);
+        for (int mt = 0; mt < 4; ++mt)
+          acc[mt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kfrag8(mt, s2), qk, acc[mt], 0, 0, 0, 119,
+                                                                    0, 119);
       }
     } else {
       // Rolling K fragments: the register that fed MFMA (mt, ks) is refilled
