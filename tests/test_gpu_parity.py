@@ -243,6 +243,44 @@ def test_attention_and_combine_parity(w):
         assert lmx <= 1e-3
 
 
+def test_fp8_every_code_attention_parity():
+    """fp8 Q, K and V drawn uniformly from every finite e4m3 code (subnormals,
+    zeros of both signs and +-448 included), so the score MFMAs, which take
+    the codes as they are, meet every value; each row attends to all of its
+    visible blocks (N = 500: a partial last block), G = 16."""
+    N, H_q, H_kv, d_h, B_k, k = 500, 16, 1, 128, 128, 4
+    log(f"fp8 every-code attention N={N} G={H_q // H_kv}")
+    rng = np.random.default_rng(20261203)
+
+    def codes(shape):
+        c = rng.integers(0, 256, size=shape, dtype=np.uint8)
+        c[(c & 0x7F) == 0x7F] -= 1          # the two NaN codes become +-448
+        return c
+
+    q, kk, vv = codes((N, H_q, d_h)), codes((N, H_kv, d_h)), codes((N, H_kv, d_h))
+    s = 1.0 / 256                            # decoded values within +-1.75
+    rows = np.arange(N)
+    sel = np.full((1, N, k), -1, np.int32)   # every visible block, ascending
+    for i in rows:
+        L = i // B_k
+        sel[0, i, :L + 1] = np.arange(L + 1)
+    d = msa.make_dims(1, N, H_q, H_kv, d_h, 128, B_k, k)
+    o = msa.make_opts("fp8", q_scale=s, k_scale=s, v_scale=s)
+    tq, tk, tv = (torch.from_numpy(x[None]).to(DEV) for x in (q, kk, vv))
+    bi = torch.from_numpy(sel[None]).to(DEV)
+    off, ent, sched = msa.msa_invert_blocks(d, bi)
+    opart, lpart = msa.msa_sparse_attn_fwd(d, o, tq, tk, tv, off, ent, sched)
+    out, lse = msa.msa_combine(d, bi, opart, lpart, want_lse=True)
+    torch.cuda.synchronize()
+    O, L = oracle.attention(N, B_k, rows, q, kk, vv, sel, dtype=oracle.FP8, q_scale=s, k_scale=s,
+                            v_scale=s)
+    mx, mn = err_stats(out[0].float().cpu().numpy(), O, label="O")
+    log(f"  output max abs {mx:.3g} mean abs {mn:.3g}")
+    assert mx <= 6e-2 and mn <= 2e-3
+    lmx, _ = err_stats(lse[0].cpu().numpy(), L)
+    assert lmx <= 1e-3
+
+
 def test_combine_parity_random_partials():
     rng = np.random.default_rng(21)
     H, n, k, G = 2, 300, 6, 4
