@@ -139,7 +139,7 @@ __global__ __launch_bounds__(kScanWaves * 64) void inv_colscan_kernel(
 
 // Single workgroup.  Part 1: exclusive scan of the entry counts over all bins
 // (CSR offsets) and the sum of the bad-id counts.  Part 2: exclusive scan of
-// the pass counts of the segments (seq, window, block).  Both read only what
+// the pass counts of the bins (seq, block).  Both read only what
 // earlier kernels wrote.
 constexpr int kBinThreads = 1024;
 
@@ -206,8 +206,8 @@ __global__ __launch_bounds__(kBinThreads) void inv_binscan_kernel(
   if (t == 0) hdr[kHdrBad] = sbad;
 }
 
-// Pass descriptors: workgroups stride over the segments, threads over a
-// segment's passes.
+// Pass descriptors: workgroups stride over the bins, threads over a bin's
+// passes.
 __global__ __launch_bounds__(kInvThreads) void inv_passes_kernel(
     const int32_t* __restrict__ tot, const int32_t* __restrict__ segp,
     const int32_t* __restrict__ blk_offsets, int64_t B_c, int64_t nbins, int epp,
