@@ -44,9 +44,6 @@
 namespace msa {
 namespace {
 
-#ifndef IX_DEFER
-#define IX_DEFER 1
-#endif
 constexpr int kIdxThreads = 512;
 constexpr int kIdxWaves = kIdxThreads / 64;
 constexpr int kIdxRows = 512;  // rows per workgroup, 64 per wave
@@ -218,7 +215,7 @@ __global__ __launch_bounds__(kIdxThreads, 1) void index_topk_kernel(
     // the steps of a key tile, so that its VALU work sits between MFMAs
     // instead of stalling the matrix cores.  (Longer lists would not fit the
     // registers that way; they insert at once, when a lane needs it.)
-    constexpr bool kDefer = IX_DEFER && KP <= 16;
+    constexpr bool kDefer = KP <= 16;
     float pend_x = 0.f;
     int pend_b = 0;
     bool pend_need = false;

@@ -18,14 +18,11 @@ constexpr int kBk = 128;   // tokens per key block
 constexpr int kDh = 128;   // head dimension of Q, K, V
 constexpr int kXcds = 8;   // MI355X: workgroups are dealt round-robin to 8 XCDs
 
-// Attention workgroup: kAttnWaves waves, one 32-row MFMA tile each, so a pass
-// is kPassRows (query, head) rows = kPassRows / G entries.  Build-time
-// tunable: 8 waves (two per SIMD) or 4 waves (one per SIMD, all 512 registers).
-#ifndef MSA_ATTN_WAVES
-#define MSA_ATTN_WAVES 8
-#endif
-constexpr int kAttnWaves = MSA_ATTN_WAVES;
-static_assert(kAttnWaves == 4 || kAttnWaves == 8, "4 or 8 attention waves");
+// Attention workgroup: kAttnWaves = 8 waves, two per SIMD, one 32-row MFMA
+// tile each, so a pass is kPassRows (query, head) rows = kPassRows / G
+// entries.  (Four waves, one per SIMD with all 512 registers, measured
+// slower.)
+constexpr int kAttnWaves = 8;
 constexpr int kPassRows = 32 * kAttnWaves;
 
 

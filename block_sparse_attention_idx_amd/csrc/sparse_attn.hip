@@ -210,7 +210,7 @@ struct QFrag<true> {
 // after them; the key tiles past the block are left out of the scores, the
 // softmax and P V at compile time.
 template <int G, bool FP8, int BKS>
-__global__ __launch_bounds__(kThreads, 8 / kWaves) void sparse_attn_kernel(
+__global__ __launch_bounds__(kThreads, 1) void sparse_attn_kernel(
     const void* __restrict__ qp, const void* __restrict__ kp, const void* __restrict__ vp,
     int64_t N, int H_sel, int kv_shift, int kslots, uint32_t kdiv_magic, int kdiv_shift, float scale_log2,
     float out_scale, const int32_t* __restrict__ entries, const int32_t* __restrict__ segp,
