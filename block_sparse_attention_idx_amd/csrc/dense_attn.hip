@@ -71,9 +71,8 @@ __global__ __launch_bounds__(kDThreads, 1) void dense_attn_kernel(
   const int64_t t_row = min(t_raw, t_last);
   const int g = rho % G;
   const int64_t orow = (static_cast<int64_t>(bat) * N + t_row) * H_q + r * G + g;
-  // The wave's first and last tokens.
+  // The wave's first token.
   const int64_t tw_lo = min(t0 + (32 * wave) / G, t_last);
-  const int64_t tw_hi = min(t0 + (32 * wave + 31) / G, t_last);
 
   u32x4 qf[8];
 #pragma unroll

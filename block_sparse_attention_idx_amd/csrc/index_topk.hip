@@ -75,15 +75,6 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* p, int
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, bytes, 0x00020000);
 }
 
-__device__ __forceinline__ float max16(const f32x16& a) {
-  float m0 = fmaxf(fmaxf(a[0], a[1]), a[2]);
-  float m1 = fmaxf(fmaxf(a[3], a[4]), a[5]);
-  float m2 = fmaxf(fmaxf(a[6], a[7]), a[8]);
-  float m3 = fmaxf(fmaxf(a[9], a[10]), a[11]);
-  float m4 = fmaxf(fmaxf(a[12], a[13]), a[14]);
-  return fmaxf(fmaxf(fmaxf(m0, m1), fmaxf(m2, m3)), fmaxf(m4, a[15]));
-}
-
 // Ascending compare-exchange network (bitonic) over KP (power of two) ints.
 template <int KP>
 __device__ __forceinline__ void sort_ascending(int (&v)[KP]) {

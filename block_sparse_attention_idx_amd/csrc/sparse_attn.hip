@@ -587,7 +587,7 @@ hipError_t launch_g(const void* q, const void* k, const void* v, bool fp8, int b
 
 hipError_t launch_sparse_attn(const void* q, const void* k, const void* v, bool fp8, int batch,
                               int64_t N, int H_sel, int G, int kv_shift, int kslots, float scale_log2,
-                              float out_scale, const int32_t* blk_offsets,
+                              float out_scale, const int32_t* /*blk_offsets: the pass list carries them*/,
                               const int32_t* blk_entries, const int32_t* sched, int64_t q_begin,
                               int64_t q_count, uint16_t* o_part, float* lse_part,
                               hipStream_t stream, int bk) {
