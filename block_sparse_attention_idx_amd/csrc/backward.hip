@@ -64,12 +64,17 @@ using tile::bf16_of;
 using tile::halves_max;
 using tile::halves_sum;
 
-constexpr int kBW = 4;           // waves per backward workgroup
+constexpr int kBW = 4;           // waves per index-branch workgroup
 constexpr int kBT = 64 * kBW;    // threads
 constexpr int kRows = 64;        // (query, head) rows per chunk
 constexpr int kStr = 272;        // row-major LDS row: 128 bf16 + 16 B of padding
 constexpr int kTStr = 144;       // transposed LDS row: 64 bf16 + 16 B of padding
-constexpr int kRS = 288;         // main-branch row-major tiles: 128 bf16 + 32 B of padding
+// Main-branch row-major tiles: 128 bf16 + 48 B of padding.  At this stride
+// both of their read forms run without bank conflicts on gfx950: the 16-byte
+// fragment reads (32 rows, two 16-byte halves) and the transposed
+// ds_read_b64_tr_b16 reads (8 rows of 64 bytes).  At 288 B the fragment
+// reads conflict two ways, at 272 B the transposed ones.
+constexpr int kRS = 304;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.69314718055994531f;
 
@@ -167,21 +172,23 @@ __device__ __forceinline__ EntryRef entry_ref(uint32_t ent, int seq, int kslots,
   return r;
 }
 
-// Staging of 64 rows of a [*, d_h = 128] bf16 tensor in two halves, for
-// software pipelining: load_rows issues this thread's global loads (16-byte
-// chunk t % 16 of rows 4 (t / 16) .. + 3; `row_ptr(rho)` must give a readable
-// row), put_rows writes them row-major into `rm` (row stride kRS).
-template <typename RowPtr>
-__device__ __forceinline__ void load_rows(RowPtr row_ptr, u32x4 (&w)[4]) {
+// Staging of 64 rows of a [*, d_h = 128] bf16 tensor for software
+// pipelining, by 1024 / RPT threads: load_rows issues this thread's
+// global loads (16-byte chunk t % 16 of rows RPT (t / 16) .. + RPT - 1;
+// `row_ptr(rho)` must give a readable row), put_rows writes them row-major
+// into `rm` (row stride kRS).
+template <int RPT, typename RowPtr>
+__device__ __forceinline__ void load_rows(RowPtr row_ptr, u32x4 (&w)[RPT]) {
   const int dg = threadIdx.x & 15, rc = threadIdx.x >> 4;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) w[j] = *reinterpret_cast<const u32x4*>(row_ptr(4 * rc + j) + 8 * dg);
+  for (int j = 0; j < RPT; ++j) w[j] = *reinterpret_cast<const u32x4*>(row_ptr(RPT * rc + j) + 8 * dg);
 }
 
-__device__ __forceinline__ void put_rows(const u32x4 (&w)[4], uint8_t* rm) {
+template <int RPT>
+__device__ __forceinline__ void put_rows(const u32x4 (&w)[RPT], uint8_t* rm) {
   const int dg = threadIdx.x & 15, rc = threadIdx.x >> 4;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) *reinterpret_cast<u32x4*>(rm + (4 * rc + j) * kRS + 16 * dg) = w[j];
+  for (int j = 0; j < RPT; ++j) *reinterpret_cast<u32x4*>(rm + (RPT * rc + j) * kRS + 16 * dg) = w[j];
 }
 
 // The chunks of a workgroup's passes in order: pass descriptor and first
@@ -249,11 +256,23 @@ __device__ __forceinline__ void store_keys_t(const u32x4 (&f)[KS], uint8_t* kt, 
 }
 
 // ---------------------------------------------------------------- main branch
+// Workgroup of 8 waves, two per SIMD.  Wave w owns keys 32 (w % 4) .. + 31
+// of the block and rows 32 (w / 4) .. + 31 of each 64-row chunk: it forms S,
+// P, dP and dS of that 32 x 32 tile and adds its rows' share of dV^T and dK^T
+// of its keys to accumulators of its own (waves w and w + 4 both add theirs
+// into the fp32 buffers when the block changes).  No product is formed twice
+// and each wave keeps one 32-key x 128-dim dV^T, dK^T pair, so a wave fits
+// the 256 registers of two waves per SIMD.  Then all 8 waves share
+// dQ^T = K^T dS^T.
 // IDX: the index branch runs, so the teacher T of every entry (the mean over
 // the G heads of the probabilities of each key of the block) is written to
 // `tch_out` ([slot][key] fp32) for the index-branch kernel.
+constexpr int kMW = 8;           // waves per main-branch workgroup
+constexpr int kMT = 64 * kMW;    // threads
+constexpr int kMRows = 1024 / kMT;  // staged rows per thread (64 rows x 16 chunks)
+
 template <int G, bool IDX>
-__global__ __launch_bounds__(kBT, 1) void bwd_main_kernel(
+__global__ __launch_bounds__(kMT, 1) void bwd_main_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ dlt,
     int64_t N, int H_sel, int kv_shift, int kslots, float scale, float scale_log2,
@@ -263,6 +282,7 @@ __global__ __launch_bounds__(kBT, 1) void bwd_main_kernel(
     float* __restrict__ tch_out) {
   constexpr int EC = kRows / G;  // queries per chunk
   constexpr float kInvG = 1.f / G;
+  constexpr int RPT = kMRows;
   __shared__ __attribute__((aligned(16))) uint8_t qr_lds[kRows * kRS];
   __shared__ __attribute__((aligned(16))) uint8_t dor_lds[kRows * kRS];
   __shared__ __attribute__((aligned(16))) uint8_t k_lds[kBk * kRS];
@@ -271,15 +291,15 @@ __global__ __launch_bounds__(kBT, 1) void bwd_main_kernel(
   __shared__ __attribute__((aligned(16))) int ri_i[kRows];
   __shared__ __attribute__((aligned(16))) float ri_lse2[kRows], ri_dlt[kRows];
   __shared__ int64_t ri_orow[kRows];
-  __shared__ __attribute__((aligned(16))) float tch[IDX ? EC * kBk : 4];  // teacher [query][key]
 
   PassIter it{segp, B_c, nseqs};
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, n = lane & 31, h = lane >> 5;
+  const int kw = wave & 3, rt = wave >> 2;  // key tile, row tile
   const int H_q = H_sel * G, H_kv = H_sel >> kv_shift;
-  const int key_l = 32 * wave + n;  // this lane's key within the block
+  const int key_l = 32 * kw + n;  // this lane's key within the block
 
   int cur_seq = -1, cur_blk = 0, cur_nvalid = 0;
-  f32x16 dkt[4], dvt[4];
+  f32x16 dkt[4], dvt[4];  // this wave's rows' share of dK^T, dV^T of its keys
 
   auto flush = [&]() {
     if (cur_seq < 0 || key_l >= cur_nvalid) return;
@@ -307,28 +327,28 @@ __global__ __launch_bounds__(kBT, 1) void bwd_main_kernel(
   // the prefetch early.
   Chunk cur = first_chunk<EC>(it, passes);
   if (!cur.ok) return;
-  u32x4 wq[4], wdo[4];   // this thread's staging chunks of the next rows
-  int p_i = -1;          // the row constants of row tid (< kRows); the loaded
+  u32x4 wq[RPT], wdo[RPT];  // this thread's staging chunks of the next rows
+  int p_i = -1;             // the row constants of row tid (< kRows); the loaded
   float p_l = 0.f, p_dl = 0.f;  // lse and D stay raw until the next iteration
   int64_t p_orow = 0;
   const int rc = tid >> 4, crow = tid & (kRows - 1);
 
   // entry words of chunk c for this thread's staging rows and constant row
-  auto chunk_entries = [&](const Chunk& c, uint32_t (&en)[4], uint32_t& enc) {
+  auto chunk_entries = [&](const Chunk& c, uint32_t (&en)[RPT], uint32_t& enc) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      en[j] = static_cast<uint32_t>(entries[c.D.start + min(c.cb + (4 * rc + j) / G, c.D.cnt - 1)]);
+    for (int j = 0; j < RPT; ++j)
+      en[j] = static_cast<uint32_t>(entries[c.D.start + min(c.cb + (RPT * rc + j) / G, c.D.cnt - 1)]);
     enc = static_cast<uint32_t>(entries[c.D.start + min(c.cb + crow / G, c.D.cnt - 1)]);
   };
   // issue the row loads of chunk c from its entry words
-  auto chunk_rows = [&](const Chunk& c, const uint32_t (&en)[4], uint32_t enc) {
+  auto chunk_rows = [&](const Chunk& c, const uint32_t (&en)[RPT], uint32_t enc) {
     const int cbat = c.D.seq / H_sel, cr = c.D.seq - cbat * H_sel;
     auto rowoff = [&](uint32_t ent, int rho) -> int64_t {
       const EntryRef x = entry_ref(ent, c.D.seq, kslots, q_begin, q_count);
       return (static_cast<int64_t>(cbat) * N + x.i) * H_q + cr * G + rho % G;
     };
-    load_rows([&](int rho) { return q + rowoff(en[rho & 3], rho) * kDh; }, wq);
-    load_rows([&](int rho) { return dout + rowoff(en[rho & 3], rho) * kDh; }, wdo);
+    load_rows<RPT>([&](int rho) { return q + rowoff(en[rho % RPT], rho) * kDh; }, wq);
+    load_rows<RPT>([&](int rho) { return dout + rowoff(en[rho % RPT], rho) * kDh; }, wdo);
     const EntryRef x = entry_ref(enc, c.D.seq, kslots, q_begin, q_count);
     const int64_t o = (static_cast<int64_t>(cbat) * N + x.i) * H_q + cr * G + crow % G;
     const bool ok = c.cb + crow / G < c.D.cnt;
@@ -338,7 +358,7 @@ __global__ __launch_bounds__(kBT, 1) void bwd_main_kernel(
     p_orow = (ok ? x.slot : dummy_slot) * G + crow % G;
   };
   {
-    uint32_t en[4], enc;
+    uint32_t en[RPT], enc;
     chunk_entries(cur, en, enc);
     chunk_rows(cur, en, enc);
   }
@@ -348,8 +368,8 @@ __global__ __launch_bounds__(kBT, 1) void bwd_main_kernel(
     const PassDesc D = cur.D;
     const int bat = D.seq / H_sel, r = D.seq - bat * H_sel;
     // ---- this chunk's rows and constants into LDS
-    put_rows(wq, qr_lds);
-    put_rows(wdo, dor_lds);
+    put_rows<RPT>(wq, qr_lds);
+    put_rows<RPT>(wdo, dor_lds);
     if (tid < kRows) {
       ri_i[tid] = p_i;
       ri_lse2[tid] = p_i >= 0 ? p_l * kLog2e : 0.f;
@@ -364,29 +384,27 @@ __global__ __launch_bounds__(kBT, 1) void bwd_main_kernel(
       cur_nvalid = static_cast<int>(min<int64_t>(kBk, N - key0));
       // the block's K and V rows into LDS, row-major (keys at or past the
       // sequence end as zeros): thread t moves 16-byte chunk t % 16 of keys
-      // t / 16 + 16 p.  Every wave finished the previous chunk's reads of
+      // t / 16 + 32 p.  Every wave finished the previous chunk's reads of
       // them (trailing barrier); the barrier below publishes them.
       const int64_t rstride = static_cast<int64_t>(H_kv) * kDh;
       const uint16_t* kb = k + ((static_cast<int64_t>(bat) * N + key0) * H_kv + (r >> kv_shift)) * kDh;
       const uint16_t* vb = v + ((static_cast<int64_t>(bat) * N + key0) * H_kv + (r >> kv_shift)) * kDh;
       const int ch = tid & 15;
+      constexpr int KP = kBk * 16 / kMT;  // keys per thread
+      u32x4 a[KP], b[KP];
 #pragma unroll
-      for (int p2 = 0; p2 < kBk / 16; p2 += 4) {
-        u32x4 a[4], b[4];
+      for (int p = 0; p < KP; ++p) {
+        const int key = (tid >> 4) + (kMT / 16) * p;
+        const int64_t o = min(key, cur_nvalid - 1) * rstride + 8 * ch;
+        a[p] = *reinterpret_cast<const u32x4*>(kb + o);
+        b[p] = *reinterpret_cast<const u32x4*>(vb + o);
+      }
 #pragma unroll
-        for (int p = 0; p < 4; ++p) {
-          const int key = (tid >> 4) + 16 * (p2 + p);
-          const int64_t o = min(key, cur_nvalid - 1) * rstride + 8 * ch;
-          a[p] = *reinterpret_cast<const u32x4*>(kb + o);
-          b[p] = *reinterpret_cast<const u32x4*>(vb + o);
-        }
-#pragma unroll
-        for (int p = 0; p < 4; ++p) {
-          const int key = (tid >> 4) + 16 * (p2 + p);
-          const bool ok = key < cur_nvalid;
-          *reinterpret_cast<u32x4*>(k_lds + key * kRS + 16 * ch) = ok ? a[p] : u32x4{0u, 0u, 0u, 0u};
-          *reinterpret_cast<u32x4*>(v_lds + key * kRS + 16 * ch) = ok ? b[p] : u32x4{0u, 0u, 0u, 0u};
-        }
+      for (int p = 0; p < KP; ++p) {
+        const int key = (tid >> 4) + (kMT / 16) * p;
+        const bool ok = key < cur_nvalid;
+        *reinterpret_cast<u32x4*>(k_lds + key * kRS + 16 * ch) = ok ? a[p] : u32x4{0u, 0u, 0u, 0u};
+        *reinterpret_cast<u32x4*>(v_lds + key * kRS + 16 * ch) = ok ? b[p] : u32x4{0u, 0u, 0u, 0u};
       }
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt) {
@@ -397,14 +415,13 @@ __global__ __launch_bounds__(kBT, 1) void bwd_main_kernel(
     const int key_abs = D.blk * kBk + key_l;
     // ---- the next chunk's entry words (the last chunk reloads its own)
     const Chunk& src = nx.ok ? nx : cur;
-    uint32_t en[4], enc;
+    uint32_t en[RPT], enc;
     chunk_entries(src, en, enc);
     __syncthreads();
 
-    // ---- S, P, dP, dS for the wave's 32 keys (lane = key, elements = rows)
-    bf16x8 pb[4], db[4];
-#pragma unroll
-    for (int rt = 0; rt < 2; ++rt) {
+    // ---- S, P, dP, dS of the wave's tile (lane = key, elements = rows)
+    bf16x8 pb[2], db[2];  // P and dS as B operands of the tile's two 16-row steps
+    {
       f32x16 s = {}, dp = {};
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks) {
@@ -433,26 +450,27 @@ __global__ __launch_bounds__(kBT, 1) void bwd_main_kernel(
           *reinterpret_cast<uint16_t*>(ds_lds + (rb + b) * kStr + 2 * key_l) = bf16_bits(ds[e]);
         }
       }
-      pb[2 * rt] = pack_step(p, 0);
-      pb[2 * rt + 1] = pack_step(p, 1);
-      db[2 * rt] = pack_step(ds, 0);
-      db[2 * rt + 1] = pack_step(ds, 1);
+      pb[0] = pack_step(p, 0);
+      pb[1] = pack_step(p, 1);
+      db[0] = pack_step(ds, 0);
+      db[1] = pack_step(ds, 1);
       if constexpr (IDX) {
         // teacher: the mean over a query's G heads of this lane's key.  The
-        // lane holds rows acc_row(e, h): for G <= 4 each run of G elements is
-        // one query's heads; for G = 8 elements 4a .. 4a + 3 of the two lane
-        // halves are the two halves of one query's heads, for G = 16 elements
-        // 0-7 (8-15) of both halves.  The halves meet through
-        // v_permlane32_swap (half 0 receives the total of the first operand,
-        // half 1 of the second), so every (query, key) value is formed in
-        // registers and stored once, with no LDS atomics.
+        // lane holds rows acc_row(e, h): for G <= 4 each run of G elements
+        // is one query's heads; for G = 8 elements 4a .. 4a + 3 of the two
+        // lane halves are the two halves of one query's heads, for G = 16
+        // elements 0-7 (8-15) of both halves.  The halves meet through
+        // v_permlane32_swap (half 0 receives the total of the first
+        // operand, half 1 of the second), so every (query, key) value is
+        // formed in registers and stored once, straight into its entry's
+        // teacher row (32 lanes write 128 contiguous bytes).
         if constexpr (G <= 4) {
 #pragma unroll
           for (int e0 = 0; e0 < 16; e0 += G) {
-            float acc = 0.f;
+            float t = 0.f;
 #pragma unroll
-            for (int e = e0; e < e0 + G; ++e) acc += p[e];
-            tch[((32 * rt + acc_row(e0, h)) / G) * kBk + key_l] = acc * kInvG;
+            for (int e = e0; e < e0 + G; ++e) t += p[e];
+            tch_out[(ri_orow[32 * rt + acc_row(e0, h)] / G) * kBk + key_l] = t * kInvG;
           }
         } else {
           constexpr int NS = 16 / (G / 2);  // per-half sums: 4 (G = 8) or 2 (G = 16)
@@ -469,7 +487,7 @@ __global__ __launch_bounds__(kBT, 1) void bwd_main_kernel(
                                                              false, false);
             const float tot = __uint_as_float(x[0]) + __uint_as_float(x[1]);
             // query (32 rt + 8 j (G = 8) or 16 j (G = 16)) / G, plus the half
-            tch[((32 * rt) / G + j + h) * kBk + key_l] = tot * kInvG;
+            tch_out[(ri_orow[((32 * rt) / G + j + h) * G] / G) * kBk + key_l] = tot * kInvG;
           }
         }
       }
@@ -478,55 +496,37 @@ __global__ __launch_bounds__(kBT, 1) void bwd_main_kernel(
     // ---- the next chunk's rows go out while this chunk finishes
     chunk_rows(src, en, enc);
 
-    // ---- dV^T += dO^T P, dK^T += Q^T dS (reduction over the 64 rows)
+    // ---- dV^T += dO^T P, dK^T += Q^T dS over the tile's 32 rows
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-      for (int st = 0; st < 4; ++st) {
-        // rows 16 st + 4 h + (0..3) and 16 st + 8 + 4 h + (0..3): the order in
-        // which pb[st] and db[st] hold them
-        const int r_lo = 16 * st + 4 * h, r_hi = r_lo + 8;
-        dvt[dt] = mfma32x32x16(lds_frag_tr(dor_lds, r_lo, r_hi, 32 * dt), pb[st], dvt[dt]);
-        dkt[dt] = mfma32x32x16(lds_frag_tr(qr_lds, r_lo, r_hi, 32 * dt), db[st], dkt[dt]);
+      for (int j = 0; j < 2; ++j) {
+        // rows 16 st + 4 h + (0..3) and 16 st + 8 + 4 h + (0..3) (st = 2 rt + j):
+        // the order in which pb[j] and db[j] hold them
+        const int r_lo = 16 * (2 * rt + j) + 4 * h, r_hi = r_lo + 8;
+        dvt[dt] = mfma32x32x16(lds_frag_tr(dor_lds, r_lo, r_hi, 32 * dt), pb[j], dvt[dt]);
+        dkt[dt] = mfma32x32x16(lds_frag_tr(qr_lds, r_lo, r_hi, 32 * dt), db[j], dkt[dt]);
       }
     __syncthreads();
 
     // ---- dQ^T = K^T dS^T over the block's 128 keys: wave w takes rows
-    // 32 (w / 2) .. + 31 and dims 64 (w % 2) .. + 63
+    // 32 (w / 4) .. + 31 and dims 32 (w % 4) .. + 31
     {
-      const int rt = wave >> 1, dt0 = 2 * (wave & 1);
-      f32x16 qa[2] = {};
+      const int dt = wave & 3;
+      f32x16 qa = {};
 #pragma unroll
-      for (int kk = 0; kk < 8; ++kk) {
-        const bf16x8 b = lds_frag(ds_lds + (32 * rt + n) * kStr + 32 * kk + 16 * h);
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-          qa[j] = mfma32x32x16(lds_frag_tr(k_lds, 16 * kk + 8 * h, 16 * kk + 8 * h + 4, 32 * (dt0 + j)), b, qa[j]);
-      }
-      if constexpr (IDX) {
-        // the chunk's teacher rows, one per entry (padding rows: the spare
-        // row; threads past the rows repeat a store, so every thread stores)
-        constexpr int NF = EC * kBk / 4;
-#pragma unroll
-        for (int j = 0; j < (NF + kBT - 1) / kBT; ++j) {
-          const int f = (tid + kBT * j) % NF;
-          const int row = f / (kBk / 4), c4 = f % (kBk / 4);
-          const int64_t slot = ri_orow[row * G] / G;
-          *reinterpret_cast<f32x4*>(tch_out + slot * kBk + 4 * c4) =
-              *reinterpret_cast<const f32x4*>(tch + row * kBk + 4 * c4);
-        }
-      }
+      for (int kk = 0; kk < 8; ++kk)
+        qa = mfma32x32x16(lds_frag_tr(k_lds, 16 * kk + 8 * h, 16 * kk + 8 * h + 4, 32 * dt),
+                          lds_frag(ds_lds + (32 * rt + n) * kStr + 32 * kk + 16 * h), qa);
       const int rho = 32 * rt + n;
       uint16_t* dst = dq_part + ri_orow[rho] * kDh;
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int e4 = 0; e4 < 4; ++e4) {
-          const int d0 = 32 * (dt0 + j) + 8 * e4 + 4 * h;
-          *reinterpret_cast<u32x2*>(dst + d0) =
-              u32x2{pack_bf16x2(qa[j][4 * e4] * scale, qa[j][4 * e4 + 1] * scale),
-                    pack_bf16x2(qa[j][4 * e4 + 2] * scale, qa[j][4 * e4 + 3] * scale)};
-        }
+      for (int e4 = 0; e4 < 4; ++e4) {
+        const int d0 = 32 * dt + 8 * e4 + 4 * h;
+        *reinterpret_cast<u32x2*>(dst + d0) =
+            u32x2{pack_bf16x2(qa[4 * e4] * scale, qa[4 * e4 + 1] * scale),
+                  pack_bf16x2(qa[4 * e4 + 2] * scale, qa[4 * e4 + 3] * scale)};
+      }
     }
     __syncthreads();
     if (!nx.ok) break;
@@ -536,8 +536,9 @@ __global__ __launch_bounds__(kBT, 1) void bwd_main_kernel(
   // The prefetch registers stay live on the exit path: otherwise the compiler
   // sinks their loads to the loop's back edge (where the exit path no longer
   // runs them) and the next iteration waits for them at once.
-  asm volatile("" ::"v"(wq[0]), "v"(wq[1]), "v"(wq[2]), "v"(wq[3]), "v"(wdo[0]), "v"(wdo[1]), "v"(wdo[2]),
-               "v"(wdo[3]), "v"(p_l), "v"(p_dl));
+#pragma unroll
+  for (int j = 0; j < RPT; ++j) asm volatile("" ::"v"(wq[j]), "v"(wdo[j]));
+  asm volatile("" ::"v"(p_l), "v"(p_dl));
   flush();
 }
 
@@ -1051,12 +1052,12 @@ hipError_t launch_backward_chunk(const BwdArgs& a, hipStream_t stream) {
 #define MSA_BWD_MAIN(GG)                                                                                        \
   case GG:                                                                                                      \
     if (a.index)                                                                                                \
-      hipLaunchKernelGGL((bwd_main_kernel<GG, true>), dim3(grid), dim3(kBT), 0, stream, a.q, a.k_ptr, a.v,     \
+      hipLaunchKernelGGL((bwd_main_kernel<GG, true>), dim3(grid), dim3(kMT), 0, stream, a.q, a.k_ptr, a.v,     \
                          a.dout, a.lse, a.dlt, a.N, a.H_sel, a.kv_shift, a.k, a.scale, scale_log2, a.entries,   \
                          segp, passes, static_cast<int>(s.B_c), nseqs, static_cast<int>(a.q_begin),            \
                          static_cast<int>(a.q_count), dummy_slot, a.dq_part, a.dk_acc, a.dv_acc, a.tch);        \
     else                                                                                                        \
-      hipLaunchKernelGGL((bwd_main_kernel<GG, false>), dim3(grid), dim3(kBT), 0, stream, a.q, a.k_ptr, a.v,    \
+      hipLaunchKernelGGL((bwd_main_kernel<GG, false>), dim3(grid), dim3(kMT), 0, stream, a.q, a.k_ptr, a.v,    \
                          a.dout, a.lse, a.dlt, a.N, a.H_sel, a.kv_shift, a.k, a.scale, scale_log2, a.entries,   \
                          segp, passes, static_cast<int>(s.B_c), nseqs, static_cast<int>(a.q_begin),            \
                          static_cast<int>(a.q_count), dummy_slot, a.dq_part, a.dk_acc, a.dv_acc, a.tch);        \
