@@ -52,11 +52,12 @@ def sources_sha256() -> str:
     return hsh.hexdigest()
 
 
-def recorded_traffic(workload: str):
+def recorded_traffic(workload: str, rows_per_launch: int):
     """HBM bytes per attention launch from the committed rocprofv3 counter
     summary for this workload (FETCH_SIZE and WRITE_SIZE scaled by a plain
-    copy of known size), or None when there is none or the kernel sources
-    changed since the counters were taken."""
+    copy of known size), or None when there is none, the kernel sources
+    changed since the counters were taken, or they were taken with another
+    number of query rows per launch."""
     path = os.path.join(ROOT, "profiles", f"sparse_attn_fwd_{workload}_hbm_traffic.md")
     if not os.path.exists(path):
         return None
@@ -66,6 +67,8 @@ def recorded_traffic(workload: str):
             key, val = line[2:].split(":", 1)
             fields[key.strip()] = val.strip().strip("`")
     if fields.get("source_sha256") != sources_sha256():
+        return None
+    if fields.get("rows_per_launch") != str(rows_per_launch):
         return None
     try:
         return float(fields["traffic_bytes_per_launch"])
@@ -168,13 +171,26 @@ def time_forward(msa, torch, fwd, steps, warmup, stream):
     return evs[0].elapsed_time(evs[-1]) / steps, float(np.median(per)), per[0]
 
 
+def rows_per_pass(msa, w):
+    """The query rows msa_forward processes per pass for this workload: its
+    q_chunk, or the library's default when that is 0."""
+    qc = w.q_chunk if w.q_chunk else msa.DEFAULT_Q_CHUNK
+    return min(qc, w.N)
+
+
+def launches_per_step(kernel: str, w, qc: int) -> int:
+    """Launches of a kernel in one msa_forward: the index branch runs once
+    over all rows, the inversion, attention and combine once per pass."""
+    return 1 if kernel == "index_topk" else -(-w.N // qc)
+
+
 def time_chunked_kernels(msa, torch, d, o, t, w, bi_all, out, stream, dev, reps=1):
     """Per-kernel times of the chunked forward, summed over its chunks: the
     index branch once over all rows, then per chunk of q_chunk rows the chunk's
     selection rows copied out, the inversion, the attention and the combine,
     each bracketed by events on the launch stream (the steps msa_forward runs,
     through the entry points)."""
-    qc = w.q_chunk
+    qc = rows_per_pass(msa, w)
     seqs = w.batch * w.H_kv
     bi_c = torch.empty((w.batch, w.H_kv, qc, w.k), dtype=torch.int32, device=dev)
     sb = max(msa.msa_invert_workspace_size(d, qb, min(qc, w.N - qb)) for qb in range(0, w.N, qc))
@@ -235,7 +251,8 @@ def measure_workload(msa, acc, synth, torch, w, steps, warmup, dev):
     log(f"{w.name}: msa_forward {ms:.3f} ms/step (median {med:.3f}, min {mn:.3f})")
     del ws
     torch.cuda.empty_cache()
-    if w.q_chunk and w.q_chunk < w.N:
+    qc = rows_per_pass(msa, w)
+    if qc < w.N:
         kern = time_chunked_kernels(msa, torch, d, o, t, w, bi, out, stream, dev)
     else:
         sb = msa.msa_invert_workspace_size(d, 0, w.N)
@@ -270,13 +287,15 @@ def measure_workload(msa, acc, synth, torch, w, steps, warmup, dev):
     kernels = kernel_table(kern, a)
     dom = max(kernels, key=lambda n: kernels[n]["ms"])
     dk = kernels[dom]
-    traffic = recorded_traffic(w.name) if dom == "sparse_attn_fwd" else None
+    traffic = recorded_traffic(w.name, qc) if dom == "sparse_attn_fwd" else None
+    launches = launches_per_step(dom, w, qc)
     roofline = {"kernel": dom, "bound": dk["bound"], "achieved": dk["achieved"], "peak": dk["peak"],
-                "unit": dk["unit"], "frac": dk["frac"], "traffic": traffic}
+                "unit": dk["unit"], "frac": dk["frac"], "traffic": traffic,
+                "launches_per_step": launches, "ms_per_launch": dk["ms"] / launches}
     if traffic:
-        roofline["traffic_achieved"] = traffic / dk["ms"] / 1e6
+        roofline["traffic_achieved"] = traffic * launches / dk["ms"] / 1e6
     return {
-        "workload": w.name, "dtype": w.dtype, "N": w.N, "q_chunk": w.q_chunk, "steps": steps,
+        "workload": w.name, "dtype": w.dtype, "N": w.N, "q_chunk": qc, "steps": steps,
         "warmup": warmup, "ms_per_step": ms, "ms_median": med, "ms_min": mn,
         "tokens_s": w.batch * w.N / (ms * 1e-3),
         "sparse_tflops": (a["f_idx"] + a["f_main"]) / (ms * 1e-3) / 1e12,
@@ -390,9 +409,21 @@ def main():
         f"host wall {1e3 * wall / args.steps:.3f} ms/step)")
 
     # ---- per-kernel timing: the same pass through the four entry points, with
-    # HIP events between the calls on the launch stream (single-chunk workloads)
+    # HIP events between the calls on the launch stream (chunked: the chunk
+    # loop msa_forward runs, summed over the chunks)
     kern = {}
-    if w.q_chunk == 0 or w.q_chunk >= w.N:
+    qc = rows_per_pass(msa, w)
+    lse_out = torch.empty((w.batch, w.N, w.H_q), dtype=torch.float32, device=dev)
+    opart = lpart = None
+    if qc < w.N:
+        kern = time_chunked_kernels(msa, torch, d, o, t, w, bi, out, stream, dev, reps=args.steps)
+        log("per call ms (summed over the chunks): " + ", ".join(f"{k} {v:.3f}" for k, v in kern.items()))
+        # the output and LSE the backward starts from
+        msa.msa_forward(*args_f, o=out, lse=lse_out, block_idx_out=bi, workspace=ws)
+        torch.cuda.synchronize()
+        del ws
+        torch.cuda.empty_cache()
+    else:
         sb = msa.msa_invert_workspace_size(d, 0, w.N)
         sched = torch.empty(((sb + 3) // 4,), dtype=torch.int32, device=dev)
         offs = torch.empty((w.batch, w.H_kv, w.B + 1), dtype=torch.int32, device=dev)
@@ -401,7 +432,6 @@ def main():
         lpart = torch.empty((w.batch, w.H_kv, w.N, w.k, w.G), dtype=torch.float32, device=dev)
         del ws
         torch.cuda.empty_cache()
-        lse_out = torch.empty((w.batch, w.N, w.H_q), dtype=torch.float32, device=dev)
         names = ("index_topk", "invert_blocks", "sparse_attn_fwd", "combine")
         evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps + 1)]
         for it in range(args.steps + 1):       # iteration 0 is a warmup
@@ -427,7 +457,7 @@ def main():
     # for single-chunk bf16 workloads; dO is seeded N(0, 1)
     backward = None
     if kern and not args.no_backward and w.dtype == "bf16":
-        del opart, lpart
+        opart = lpart = None
         torch.cuda.empty_cache()
         d_o = synth.device_tensor(w, "d_o", dev)
         wsb = torch.empty((msa.msa_backward_workspace_size(d, o),), dtype=torch.uint8, device=dev)
@@ -610,13 +640,18 @@ def main():
         kernels = kernel_table(kern, acct)
         dom = max(kernels, key=lambda n: kernels[n]["ms"])
         dk = kernels[dom]
-        traffic = recorded_traffic(w.name) if dom == "sparse_attn_fwd" else None
+        traffic = recorded_traffic(w.name, qc) if dom == "sparse_attn_fwd" else None
+        launches = launches_per_step(dom, w, qc)
+        # a step launches the attention once per pass (the index branch once):
+        # achieved is the step's algorithmic bytes (or FLOPs) over their summed
+        # launch time, the same as per launch on average; traffic is per launch
         roofline = {"kernel": dom, "bound": dk["bound"], "achieved": dk["achieved"],
                     "peak": dk["peak"], "unit": dk["unit"], "frac": dk["frac"],
-                    "traffic": traffic}
+                    "traffic": traffic, "launches_per_step": launches,
+                    "ms_per_launch": dk["ms"] / launches}
         if traffic:
             # the counted HBM bytes over the same launch time (GB/s)
-            roofline["traffic_achieved"] = traffic / dk["ms"] / 1e6
+            roofline["traffic_achieved"] = traffic * launches / dk["ms"] / 1e6
     else:
         roofline = None
 
@@ -707,7 +742,7 @@ def main():
         "scaling": "weak", "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
         "config": {"workload": w.name, "batch": w.batch, "N": w.N, "H_q": w.H_q, "H_kv": w.H_kv,
                    "d_h": w.d_h, "d_idx": w.d_idx, "B_k": w.B_k, "k": w.k,
-                   "q_chunk": w.q_chunk, "hot_blocks": w.plant},
+                   "q_chunk": qc, "hot_blocks": w.plant},
         "ms_median": ms_median, "ms_min": ms_min,
         "sparse_tflops": tflops, "index_flops": f_idx, "main_flops": f_main,
         "block_popularity": popularity,

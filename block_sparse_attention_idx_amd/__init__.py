@@ -64,6 +64,10 @@ class msa_dims(ctypes.Structure):
         return self.H_q // self.H_sel
 
 
+# MSA_DEFAULT_Q_CHUNK: msa_forward's query rows per pass when opts.q_chunk is 0
+DEFAULT_Q_CHUNK = 16384
+
+
 class msa_opts(ctypes.Structure):
     _fields_ = [("qkv_dtype", ctypes.c_int32), ("softmax_scale", ctypes.c_float),
                 ("q_scale", ctypes.c_float), ("k_scale", ctypes.c_float),

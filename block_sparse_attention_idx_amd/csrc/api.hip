@@ -127,7 +127,8 @@ struct ForwardLayout {
 
 ForwardLayout forward_layout(const msa_dims* d, const msa_opts* o) {
   ForwardLayout L{};
-  L.qc = o->q_chunk > 0 ? (o->q_chunk < d->N ? o->q_chunk : d->N) : d->N;
+  const int64_t want = o->q_chunk > 0 ? o->q_chunk : MSA_DEFAULT_Q_CHUNK;
+  L.qc = want < d->N ? want : d->N;
   const int64_t seqs = static_cast<int64_t>(d->batch) * HS(d);
   const int64_t B = (d->N + d->B_k - 1) / d->B_k;
   const size_t slots = static_cast<size_t>(seqs) * L.qc * d->k;

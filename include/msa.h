@@ -59,7 +59,7 @@
 extern "C" {
 #endif
 
-#define MSA_ABI_VERSION 3
+#define MSA_ABI_VERSION 4
 
 enum msa_status_code {
     MSA_OK = 0,
@@ -104,9 +104,19 @@ typedef struct msa_opts {
     float k_scale;
     float v_scale;
     int32_t reserved;    /* must be 0 */
-    int64_t q_chunk;     /* msa_forward only: 0 = all N rows at once; else a
-                            positive multiple of B_k, rows processed per pass */
+    int64_t q_chunk;     /* query rows per pass of msa_forward and msa_backward:
+                            a positive multiple of B_k, or 0 for the default
+                            (msa_forward: MSA_DEFAULT_Q_CHUNK rows, all N when
+                            N is at most that; msa_backward: all N rows) */
 } msa_opts;
+
+/* The forward's default rows per pass.  At H_q = 64 and d_h = 128 the Q rows
+ * of 16,384 queries take 256 MiB, the size of MI355X's last-level (Infinity)
+ * cache, so the attention's repeated Q gathers within a pass mostly hit it;
+ * the per-pass selection, inversion and partial outputs also shrink to a
+ * pass's rows (at N = 131,072, H_q = 64, k = 16: 4.1 GiB of workspace
+ * instead of 32.6 GiB). */
+#define MSA_DEFAULT_Q_CHUNK 16384
 
 /* Library identity and diagnostics. */
 int msa_abi_version(void);
@@ -236,7 +246,7 @@ int msa_combine(const msa_dims *dims, const int32_t *block_idx, const void *o_pa
 
 /*
  * msa_workspace_size / msa_forward -- the whole forward pass: for each chunk of
- * opts->q_chunk query rows (all N at once when 0): index_topk, invert_blocks,
+ * opts->q_chunk query rows (MSA_DEFAULT_Q_CHUNK when 0): index_topk, invert_blocks,
  * sparse_attn_fwd, combine (with several chunks, index_topk runs once over
  * all rows first).  The workspace (device memory, at least msa_workspace_size
  * bytes, 256-byte aligned) holds the per-chunk selection, inverted index,

@@ -43,7 +43,7 @@ def test_exports_every_declared_symbol(L):
 
 
 def test_identity(L):
-    assert L.msa_abi_version() == 3
+    assert L.msa_abi_version() == 4
     assert L.msa_status_string(0) == b"ok"
     assert L.msa_status_string(5) == b"workspace too small"
 
@@ -120,6 +120,18 @@ def test_workspace_and_opts(L):
     c = msa.make_opts(q_chunk=512)
     assert L.msa_workspace_size(ctypes.byref(d), ctypes.byref(c), ctypes.byref(n)) == 0
     assert n.value < ws
+    # q_chunk 0 takes msa_forward's default rows per pass (all rows when N is
+    # at most that): the same workspace as asking for them explicitly
+    big = dims(N=4 * msa.DEFAULT_Q_CHUNK)
+    sizes = {}
+    for qc in (0, msa.DEFAULT_Q_CHUNK, 4 * msa.DEFAULT_Q_CHUNK):
+        assert L.msa_workspace_size(ctypes.byref(big), ctypes.byref(msa.make_opts(q_chunk=qc)),
+                                    ctypes.byref(n)) == 0
+        sizes[qc] = n.value
+    assert sizes[0] == sizes[msa.DEFAULT_Q_CHUNK] < sizes[4 * msa.DEFAULT_Q_CHUNK]
+    assert L.msa_workspace_size(ctypes.byref(d), ctypes.byref(msa.make_opts(q_chunk=d.N)),
+                                ctypes.byref(n)) == 0
+    assert n.value == ws  # N = 2048 is below the default: one pass either way
 
 
 def test_dense_attn_validation(L):

@@ -394,6 +394,21 @@ def test_forward_chunked_equals_whole_and_deterministic():
     assert torch.equal(a.view(torch.int16), c.view(torch.int16))
 
 
+def test_forward_default_chunks_equal_single_pass():
+    """q_chunk 0 runs msa.DEFAULT_Q_CHUNK rows per pass (here two passes, the
+    second ragged): output and LSE bit for bit those of one pass over all rows."""
+    w = TINY.with_(N=msa.DEFAULT_Q_CHUNK + 2560, k=6)
+    log(f"forward default chunks N={w.N}")
+    t = device_inputs(w, DEV)
+    d = dims_of(w)
+    args = (t["q"], t["k"], t["v"], t["q_idx"], t["k_idx"])
+    a, la, _ = msa.msa_forward(d, msa.make_opts(), *args, want_lse=True)
+    b, lb, _ = msa.msa_forward(d, msa.make_opts(q_chunk=w.N), *args, want_lse=True)
+    assert msa.msa_workspace_size(d, msa.make_opts()) < msa.msa_workspace_size(d, msa.make_opts(q_chunk=w.N))
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    assert torch.equal(la, lb)
+
+
 # --------------------------------------------------------------------------- selection variants
 
 FORCED_CASES = [
