@@ -2,7 +2,8 @@
 """Benchmark of the MSA forward pass on one MI355X.
 
 One step = one msa_forward over the whole workload (index branch, inversion,
-KV-outer sparse attention, combine) with every input already resident in HBM.
+KV-outer sparse attention, combine; by default the last three once per pass of
+16,384 query rows) with every input already resident in HBM.
 Default workload: the 128K prefill with 64 planted hot blocks (N = 131,072,
 H_q = 64, H_kv = 4, d_h = d_idx = 128, B_k = 128, k = 16, bf16), synthetic
 seeded inputs.
