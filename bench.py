@@ -232,11 +232,25 @@ def time_chunked_kernels(msa, torch, d, o, t, w, bi_all, out, stream, dev, reps=
     return tot
 
 
-def measure_workload(msa, acc, synth, torch, w, steps, warmup, dev):
+def time_dense_in_ranges(msa, torch, d, o, t, w, out, stream, rows=16384):
+    """The dense causal GQA kernel over every query row of the workload, one
+    launch per range of `rows` queries (each launch well under a second), timed
+    as one pass with events on the launch stream."""
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for qb in range(0, w.N, rows):
+        msa.msa_dense_attn_fwd(d, o, t["q"], t["k"], t["v"], q_begin=qb, q_count=min(rows, w.N - qb), o=out)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1)
+
+
+def measure_workload(msa, acc, synth, torch, w, steps, warmup, dev, dense=False):
     """One more workload of the path, measured like the headline one: the
     whole msa_forward (inputs resident in HBM), each kernel's time (the four
     entry points, or the chunk loop through them), the work from the selection
-    made, and the dominant kernel's roofline."""
+    made, and the dominant kernel's roofline; with `dense`, also the dense
+    causal GQA baseline over every row of the workload."""
     log(f"{w.name}: generating inputs on the device")
     stream = torch.cuda.current_stream(dev)
     t = {x: synth.device_tensor(w, x, dev) for x in ("q", "k", "v", "q_idx", "k_idx")}
@@ -281,6 +295,21 @@ def measure_workload(msa, acc, synth, torch, w, steps, warmup, dev):
                 for j, name in enumerate(names):
                     kern[name] += e[j].elapsed_time(e[j + 1]) / steps
     log(f"{w.name}: per kernel ms: " + ", ".join(f"{k} {v:.3f}" for k, v in kern.items()))
+    dense_res = None
+    if dense:
+        # a short warm launch first (the last 256 rows), then every row once
+        msa.msa_dense_attn_fwd(d, o, t["q"], t["k"], t["v"], q_begin=w.N - 256, q_count=256, o=out)
+        torch.cuda.synchronize()
+        log(f"{w.name}: dense baseline over all {w.N} rows in 16,384-row launches")
+        dms = time_dense_in_ranges(msa, torch, d, o, t, w, out, stream)
+        f_dense = acc.dense_flops(0, w.N, w.H_q, w.d_h, batch=w.batch)
+        dense_res = {"kernel": "dense_attn_fwd", "ms": dms, "bound": "mfma", "flops": f_dense,
+                     "achieved": f_dense / dms / 1e9, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": f_dense / dms / 1e9 / PEAK_BF16_TFLOPS,
+                     "tokens_s": w.batch * w.N / (dms * 1e-3), "msa_speedup": dms / ms,
+                     "launches": -(-w.N // 16384)}
+        log(f"{w.name}: dense baseline {dms:.1f} ms, {dense_res['achieved']:.0f} TFLOP/s; "
+            f"msa_forward is {dense_res['msa_speedup']:.2f}x faster")
     sel = bi.cpu().numpy().reshape(w.batch * w.H_kv, w.N, w.k)
     del t, out, bi
     torch.cuda.empty_cache()
@@ -303,6 +332,7 @@ def measure_workload(msa, acc, synth, torch, w, steps, warmup, dev):
         "index_flops": a["f_idx"], "main_flops": a["f_main"],
         "roofline": roofline,
         "kernels": kernels,
+        "dense_baseline": dense_res,
     }
 
 
@@ -689,7 +719,7 @@ def main():
     if not args.no_fp8 and w.name != synth.P128K_FP8.name:
         fp8 = measure_workload(msa, acc, synth, torch, synth.P128K_FP8, args.steps, args.warmup, dev)
     if not args.no_long_context and w.name != synth.P1M.name:
-        long_ctx = measure_workload(msa, acc, synth, torch, synth.P1M, 2, 1, dev)
+        long_ctx = measure_workload(msa, acc, synth, torch, synth.P1M, 2, 1, dev, dense=not args.no_dense)
 
     # ---- the CPU oracle on a bounded sample of the same workload
     cpu = None

@@ -563,6 +563,32 @@ def test_dense_attention_full_size_sampled():
     assert lmx <= 1e-3
 
 
+def test_dense_attention_1m_last_rows():
+    """1M tokens: the heaviest rows (the last 512, each over about a million
+    keys), computed by one range launch, sampled against the oracle."""
+    w = synth.P1M
+    log(f"dense 1M last rows {w.name}")
+    t = device_inputs(w, DEV)
+    qb = w.N - 512
+    out, lse = msa.msa_dense_attn_fwd(dims_of(w), msa.make_opts(), t["q"], t["k"], t["v"], q_begin=qb,
+                                      q_count=512, want_lse=True)
+    torch.cuda.synchronize()
+    rows = np.array([qb, qb + 1, qb + 255, w.N - 2, w.N - 1])
+    ridx = torch.from_numpy(rows).to(DEV)
+    gout = out[0][ridx].float().cpu().numpy()
+    glse = lse[0][ridx].cpu().numpy()
+    del t, out, lse
+    torch.cuda.empty_cache()
+    log(f"dense 1M: oracle on {len(rows)} rows")
+    O, L = oracle.dense_attention(w.N, w.B_k, rows, synth.host_rows(w, "q", rows),
+                                  synth.host_all(w, "k"), synth.host_all(w, "v"))
+    mx, mn = err_stats(gout, O, label="O")
+    log(f"  output max abs {mx:.3g} mean abs {mn:.3g}")
+    assert mx <= 2e-2 and mn <= 2e-3
+    lmx, _ = err_stats(glse, L)
+    assert lmx <= 1e-3
+
+
 # --------------------------------------------------------------------------- decode
 
 DECODE_CASES = [
