@@ -900,33 +900,51 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const uint16_t* __restric
 }
 
 // Sum of the per-slot partials of one (group, query): dQ of its G heads,
-// dq_idx and the KL value, over the slots with a valid block.
+// dq_idx and the KL value, over the slots with a valid block.  A pure
+// streaming kernel like the forward's combine: the slot loop is unrolled at
+// compile time (KMAX >= k), so a thread's loads of all valid slots are in
+// flight together, and the sums still run over the slots in order.  Each XCD
+// streams one contiguous share of the partial buffer.
 constexpr int kRedThreads = 320;
 
-template <int G>
+template <int G, int KMAX>
 __global__ __launch_bounds__(kRedThreads) void bwd_reduce_kernel(
     const int32_t* __restrict__ block_idx, const uint16_t* __restrict__ dq_part,
     const float* __restrict__ dqi_part, const float* __restrict__ kl_part, int64_t N, int H_sel, int k,
-    int d_idx, int64_t q_begin, int64_t q_count, uint16_t* __restrict__ dq, uint16_t* __restrict__ dq_idx,
-    float* __restrict__ kl) {
-  const int64_t f = blockIdx.x;  // seq * q_count + query row
+    int d_idx, int64_t q_begin, int64_t q_count, int64_t rows_total, uint16_t* __restrict__ dq,
+    uint16_t* __restrict__ dq_idx, float* __restrict__ kl) {
+  // Workgroups are dealt round-robin to the kXcds XCDs; the grid is a
+  // multiple of kXcds and XCD x takes the x-th contiguous share of the rows.
+  const int64_t per = gridDim.x / kXcds;
+  const int64_t f = (blockIdx.x % kXcds) * per + blockIdx.x / kXcds;  // seq * q_count + query row
+  if (f >= rows_total) return;
   const int64_t seq = f / q_count, qrow = f % q_count, i = q_begin + qrow;
   const int64_t bat = seq / H_sel;
   const int r = static_cast<int>(seq % H_sel);
   const int64_t L = i / kBk;
   const int t = threadIdx.x;
   const int32_t* sel = block_idx + f * k;
+  bool ok[KMAX];
+#pragma unroll
+  for (int s = 0; s < KMAX; ++s) {
+    const int b = s < k ? sel[s] : -1;
+    ok[s] = b >= 0 && b <= L;
+  }
   if (t < 16 * G) {
     const int g = t >> 4, c = t & 15;
+    u32x4 w[KMAX];
+#pragma unroll
+    for (int s = 0; s < KMAX; ++s)
+      w[s] = ok[s] ? *reinterpret_cast<const u32x4*>(dq_part + ((f * k + s) * G + g) * kDh + 8 * c)
+                   : u32x4{0u, 0u, 0u, 0u};
     float acc[8] = {};
-    for (int s = 0; s < k; ++s) {
-      const int b = sel[s];
-      if (b < 0 || b > L) continue;
-      const u32x4 w = *reinterpret_cast<const u32x4*>(dq_part + ((f * k + s) * G + g) * kDh + 8 * c);
+#pragma unroll
+    for (int s = 0; s < KMAX; ++s) {
+      if (!ok[s]) continue;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        acc[2 * j] += __uint_as_float(w[j] << 16);
-        acc[2 * j + 1] += __uint_as_float(w[j] & 0xFFFF0000u);
+        acc[2 * j] += __uint_as_float(w[s][j] << 16);
+        acc[2 * j + 1] += __uint_as_float(w[s][j] & 0xFFFF0000u);
       }
     }
     *reinterpret_cast<u32x4*>(dq + ((bat * N + i) * (H_sel * G) + r * G + g) * kDh + 8 * c) =
@@ -934,22 +952,24 @@ __global__ __launch_bounds__(kRedThreads) void bwd_reduce_kernel(
               pack_bf16x2(acc[6], acc[7])};
   } else if (dq_idx && t < 16 * G + d_idx / 4) {
     const int c = t - 16 * G;
-    float acc[4] = {};
-    for (int s = 0; s < k; ++s) {
-      const int b = sel[s];
-      if (b < 0 || b > L) continue;
-      const f32x4 w = *reinterpret_cast<const f32x4*>(dqi_part + (f * k + s) * d_idx + 4 * c);
+    f32x4 w[KMAX];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc[j] += w[j];
+    for (int s = 0; s < KMAX; ++s)
+      w[s] = ok[s] ? *reinterpret_cast<const f32x4*>(dqi_part + (f * k + s) * d_idx + 4 * c) : f32x4{};
+    float acc[4] = {};
+#pragma unroll
+    for (int s = 0; s < KMAX; ++s) {
+      if (!ok[s]) continue;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[j] += w[s][j];
     }
     *reinterpret_cast<u32x2*>(dq_idx + ((bat * N + i) * H_sel + r) * d_idx + 4 * c) =
         u32x2{pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])};
   } else if (kl && t == 16 * G + d_idx / 4) {
     float s = 0.f;
-    for (int j = 0; j < k; ++j) {
-      const int b = sel[j];
-      if (b >= 0 && b <= L) s += kl_part[f * k + j];
-    }
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j)
+      if (ok[j]) s += kl_part[f * k + j];
     kl[seq * N + i] = s;
   }
 }
@@ -1107,19 +1127,28 @@ hipError_t launch_backward_chunk(const BwdArgs& a, hipStream_t stream) {
 
   {
     const int64_t rows = seqs * a.q_count;
+    const int64_t grid = (rows + kXcds - 1) / kXcds * kXcds;  // see the kernel
     auto launch = [&](auto kern) {
-      hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(rows)), dim3(kRedThreads), 0, stream, a.block_idx,
+      hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(grid)), dim3(kRedThreads), 0, stream, a.block_idx,
                          a.dq_part, a.dqi_part, a.kl_part, a.N, a.H_sel, a.k, a.d_idx, a.q_begin, a.q_count,
-                         a.dq, a.index ? a.dq_idx : nullptr, a.index ? a.kl : nullptr);
+                         rows, a.dq, a.index ? a.dq_idx : nullptr, a.index ? a.kl : nullptr);
     };
+#define MSA_BWD_RED(GG)                                            \
+  case GG:                                                         \
+    if (a.k <= 4) launch(bwd_reduce_kernel<GG, 4>);                \
+    else if (a.k <= 8) launch(bwd_reduce_kernel<GG, 8>);           \
+    else if (a.k <= 16) launch(bwd_reduce_kernel<GG, 16>);         \
+    else launch(bwd_reduce_kernel<GG, 32>);                        \
+    break;
     switch (a.G) {
-      case 1: launch(bwd_reduce_kernel<1>); break;
-      case 2: launch(bwd_reduce_kernel<2>); break;
-      case 4: launch(bwd_reduce_kernel<4>); break;
-      case 8: launch(bwd_reduce_kernel<8>); break;
-      case 16: launch(bwd_reduce_kernel<16>); break;
+      MSA_BWD_RED(1)
+      MSA_BWD_RED(2)
+      MSA_BWD_RED(4)
+      MSA_BWD_RED(8)
+      MSA_BWD_RED(16)
       default: return hipErrorInvalidValue;
     }
+#undef MSA_BWD_RED
     return hipGetLastError();
   }
 }
