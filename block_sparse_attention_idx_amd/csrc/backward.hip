@@ -757,13 +757,21 @@ __global__ __launch_bounds__(kBT, 1) void bwd_idx_kernel(
       for (int e4 = 0; e4 < 4; ++e4)
         *reinterpret_cast<f32x4*>(dst + 8 * e4) = f32x4{a[4 * e4], a[4 * e4 + 1], a[4 * e4 + 2], a[4 * e4 + 3]};
     }
+    {
+      // row tid / 4, keys 32 (tid % 4) .. + 31: eight 16-byte reads, then the
+      // four threads of the row add their sums (two shuffles in a quad)
+      static_assert(EI * 4 == kBT, "one thread per quarter row");
+      const int row = tid >> 2, q4 = tid & 3;
+      const f32x4* src = reinterpret_cast<const f32x4*>(tt + row * kBk + 32 * q4);
+      float sum = 0.f;
 #pragma unroll
-    for (int rr = 0; rr < EI / kBW; ++rr) {
-      const int row = wave + kBW * rr;
-      float sum = tt[row * kBk + lane] + tt[row * kBk + 64 + lane];
-#pragma unroll
-      for (int m = 32; m >= 1; m >>= 1) sum += __shfl_xor(sum, m);
-      kl_part[ei_slot[row]] = sum;  // every lane: the same value to the same word
+      for (int j = 0; j < 8; ++j) {
+        const f32x4 x = src[j];
+        sum += (x[0] + x[1]) + (x[2] + x[3]);
+      }
+      sum += __shfl_xor(sum, 1);
+      sum += __shfl_xor(sum, 2);
+      kl_part[ei_slot[row]] = sum;  // the quad's four lanes: the same value to the same word
     }
     __syncthreads();
     if (!nx.ok) break;
