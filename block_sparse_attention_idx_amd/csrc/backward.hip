@@ -18,11 +18,13 @@
 // Each pass is one (sequence, group, key block) bin restricted to up to
 // 256 / G consecutive entries (query, slot); persistent workgroups take equal
 // contiguous shares of the pass list, so every workgroup keeps one key block
-// for a run of passes.  Per workgroup of 4 waves, wave w owns keys
-// 32 w .. 32 w + 31 of the block (the block's K and V rows are staged in LDS
-// when the block changes; the index branch keeps its K^idx rows in registers)
-// and accumulates their dK^T, dV^T (and dK^idx^T) in MFMA accumulators across
-// the run; when the block changes, the accumulators are
+// for a run of passes.  In the main branch (8 waves) wave w owns keys
+// 32 (w % 4) .. + 31 of the block and rows 32 (w / 4) .. + 31 of each chunk;
+// in the index branch (4 waves) wave w owns keys 32 w .. + 31.  The block's
+// K and V rows are staged in LDS when the block changes (the index branch
+// keeps its K^idx rows in registers), and each wave accumulates its keys'
+// dK^T, dV^T (or dK^idx^T) in MFMA accumulators across the run; when the
+// block changes, the accumulators are
 // added to fp32 gradient buffers with global atomics (a block's passes may be
 // shared by two workgroups, and with more index heads than K/V heads several
 // groups share a K/V head).  dQ (and dq_idx) need a sum over the block's keys,
