@@ -152,7 +152,8 @@ class Workload:
     dtype: str = "bf16"          # "bf16" or "fp8" for Q, K, V
     plant: int = 0               # number of planted hot blocks (0 = none)
     plant_gain: float = 2.0
-    q_chunk: int = 0             # 0 = whole sequence in one pass
+    q_chunk: int = 0             # 0 = the library default (msa_forward: passes of
+                                 # 16,384 rows; msa_backward: one pass)
     H_idx: int = 0               # index (proxy) heads; 0 = H_kv
 
     @property

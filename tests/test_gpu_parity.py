@@ -394,17 +394,34 @@ def test_forward_chunked_equals_whole_and_deterministic():
     assert torch.equal(a.view(torch.int16), c.view(torch.int16))
 
 
-def test_forward_default_chunks_equal_single_pass():
-    """q_chunk 0 runs msa.DEFAULT_Q_CHUNK rows per pass (here two passes, the
-    second ragged): output and LSE bit for bit those of one pass over all rows."""
-    w = TINY.with_(N=msa.DEFAULT_Q_CHUNK + 2560, k=6)
-    log(f"forward default chunks N={w.N}")
+DEFAULT_PASS_CASES = [
+    TINY.with_(N=msa.DEFAULT_Q_CHUNK + 2560, k=6),
+    TINY.with_(N=msa.DEFAULT_Q_CHUNK + 1000, H_q=32, H_kv=2, k=8, d_idx=128, dtype="fp8"),
+    TINY.with_(N=2 * msa.DEFAULT_Q_CHUNK + 700, k=10, B_k=64),
+    TINY.with_(N=msa.DEFAULT_Q_CHUNK + 300, H_q=32, H_kv=2, H_idx=8, k=5),
+]
+
+
+@pytest.mark.parametrize("w", DEFAULT_PASS_CASES, ids=lambda w: f"N{w.N}_k{w.k}_bk{w.B_k}_{w.dtype}_hidx{w.H_idx}")
+def test_forward_default_chunks_equal_single_pass(w):
+    """q_chunk 0 runs msa.DEFAULT_Q_CHUNK rows per pass (here two or three
+    passes, the last ragged): output, LSE and selection bit for bit those of
+    one pass over all rows."""
+    log(f"forward default chunks N={w.N} k={w.k} B_k={w.B_k} {w.dtype} H_idx={w.H_idx}")
     t = device_inputs(w, DEV)
     d = dims_of(w)
     args = (t["q"], t["k"], t["v"], t["q_idx"], t["k_idx"])
-    a, la, _ = msa.msa_forward(d, msa.make_opts(), *args, want_lse=True)
-    b, lb, _ = msa.msa_forward(d, msa.make_opts(q_chunk=w.N), *args, want_lse=True)
-    assert msa.msa_workspace_size(d, msa.make_opts()) < msa.msa_workspace_size(d, msa.make_opts(q_chunk=w.N))
+    runs = []
+    one_pass = -(-w.N // w.B_k) * w.B_k        # a multiple of B_k covering all rows
+    for qc in (0, one_pass):
+        o = opts_of(w)
+        o.q_chunk = qc
+        bi = torch.empty((w.batch, w.H_sel, w.N, w.k), dtype=torch.int32, device=DEV)
+        out, lse, _ = msa.msa_forward(d, o, *args, block_idx_out=bi, want_lse=True)
+        runs.append((out, lse, bi, msa.msa_workspace_size(d, o)))
+    (a, la, ba, wa), (b, lb, bb, wb) = runs
+    assert wa < wb
+    assert torch.equal(ba, bb)
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
     assert torch.equal(la, lb)
 
