@@ -914,7 +914,9 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const uint16_t* __restric
 // streaming kernel like the forward's combine: the slot loop is unrolled at
 // compile time (KMAX >= k), so a thread's loads of all valid slots are in
 // flight together, and the sums still run over the slots in order.  Each XCD
-// streams one contiguous share of the partial buffer.
+// streams one contiguous share of the partial buffer.  Partials are read once
+// and the outputs written once, in whole lines: loads and stores are
+// non-temporal.
 constexpr int kRedThreads = 320;
 
 template <int G, int KMAX>
@@ -945,7 +947,7 @@ __global__ __launch_bounds__(kRedThreads) void bwd_reduce_kernel(
     u32x4 w[KMAX];
 #pragma unroll
     for (int s = 0; s < KMAX; ++s)
-      w[s] = ok[s] ? *reinterpret_cast<const u32x4*>(dq_part + ((f * k + s) * G + g) * kDh + 8 * c)
+      w[s] = ok[s] ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(dq_part + ((f * k + s) * G + g) * kDh + 8 * c))
                    : u32x4{0u, 0u, 0u, 0u};
     float acc[8] = {};
 #pragma unroll
@@ -957,15 +959,16 @@ __global__ __launch_bounds__(kRedThreads) void bwd_reduce_kernel(
         acc[2 * j + 1] += __uint_as_float(w[s][j] & 0xFFFF0000u);
       }
     }
-    *reinterpret_cast<u32x4*>(dq + ((bat * N + i) * (H_sel * G) + r * G + g) * kDh + 8 * c) =
+    __builtin_nontemporal_store(
         u32x4{pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]), pack_bf16x2(acc[4], acc[5]),
-              pack_bf16x2(acc[6], acc[7])};
+              pack_bf16x2(acc[6], acc[7])},
+        reinterpret_cast<u32x4*>(dq + ((bat * N + i) * (H_sel * G) + r * G + g) * kDh + 8 * c));
   } else if (dq_idx && t < 16 * G + d_idx / 4) {
     const int c = t - 16 * G;
     f32x4 w[KMAX];
 #pragma unroll
     for (int s = 0; s < KMAX; ++s)
-      w[s] = ok[s] ? *reinterpret_cast<const f32x4*>(dqi_part + (f * k + s) * d_idx + 4 * c) : f32x4{};
+      w[s] = ok[s] ? __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(dqi_part + (f * k + s) * d_idx + 4 * c)) : f32x4{};
     float acc[4] = {};
 #pragma unroll
     for (int s = 0; s < KMAX; ++s) {
@@ -973,8 +976,8 @@ __global__ __launch_bounds__(kRedThreads) void bwd_reduce_kernel(
 #pragma unroll
       for (int j = 0; j < 4; ++j) acc[j] += w[s][j];
     }
-    *reinterpret_cast<u32x2*>(dq_idx + ((bat * N + i) * H_sel + r) * d_idx + 4 * c) =
-        u32x2{pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])};
+    __builtin_nontemporal_store(u32x2{pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])},
+        reinterpret_cast<u32x2*>(dq_idx + ((bat * N + i) * H_sel + r) * d_idx + 4 * c));
   } else if (kl && t == 16 * G + d_idx / 4) {
     float s = 0.f;
 #pragma unroll
