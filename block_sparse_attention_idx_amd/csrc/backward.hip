@@ -861,7 +861,10 @@ __global__ __launch_bounds__(64) void proxy_lse_kernel(
 }
 
 // Merge of the partial proxy LSEs of one (group, query) over its valid slots
-// (log2 units).
+// (log2 units).  The slot loop is unrolled at compile time (KMAX >= k): every
+// id and value is requested before the max and the sum, which then run over
+// the slots in order.
+template <int KMAX>
 __global__ __launch_bounds__(256) void proxy_lse_merge_kernel(const int32_t* __restrict__ block_idx,
                                                               const float* __restrict__ lsei_part, int k,
                                                               int64_t q_begin, int64_t q_count, int64_t rows,
@@ -869,44 +872,57 @@ __global__ __launch_bounds__(256) void proxy_lse_merge_kernel(const int32_t* __r
   const int64_t f = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   if (f >= rows) return;
   const int64_t L = (q_begin + f % q_count) / kBk;
+  int b[KMAX];
+  float v[KMAX];
+#pragma unroll
+  for (int s = 0; s < KMAX; ++s) b[s] = s < k ? block_idx[f * k + s] : -1;
+#pragma unroll
+  for (int s = 0; s < KMAX; ++s) v[s] = s < k ? lsei_part[f * k + s] : 0.f;
   float m = -__builtin_huge_valf();
-  for (int s = 0; s < k; ++s) {
-    const int b = block_idx[f * k + s];
-    if (b >= 0 && b <= L) m = fmaxf(m, lsei_part[f * k + s]);
-  }
+#pragma unroll
+  for (int s = 0; s < KMAX; ++s)
+    if (b[s] >= 0 && b[s] <= L) m = fmaxf(m, v[s]);
   float l = 0.f;
-  for (int s = 0; s < k; ++s) {
-    const int b = block_idx[f * k + s];
-    if (b >= 0 && b <= L) l += __builtin_amdgcn_exp2f(lsei_part[f * k + s] - m);
-  }
+#pragma unroll
+  for (int s = 0; s < KMAX; ++s)
+    if (b[s] >= 0 && b[s] <= L) l += __builtin_amdgcn_exp2f(v[s] - m);
   lsei2[f] = m + __builtin_amdgcn_logf(l);
 }
 
-// D = rowsum(dO * O) per (query, head), fp32: 16 threads per row.
+// D = rowsum(dO * O) per (query, head), fp32: 16 threads per row.  blockIdx.y
+// is the batch element, whose rows of the range (q_count queries x H_q heads)
+// are contiguous; each 16-lane group takes kPrepRows rows a grid width apart,
+// with all of its loads in flight before the sums.
+constexpr int kPrepRows = 4;
+
 __global__ __launch_bounds__(256) void bwd_prep_kernel(const uint16_t* __restrict__ dout,
                                                        const uint16_t* __restrict__ o, int64_t N, int H_q,
-                                                       int64_t q_begin, int64_t q_count, int64_t rows,
-                                                       float* __restrict__ dlt) {
-  const int64_t x = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  const int64_t row = x >> 4;  // (batch, query in range, head)
-  const int c = static_cast<int>(x & 15);
-  float s = 0.f;
-  int64_t off = 0;
-  if (row < rows) {
-    const int64_t hq = row % H_q, qb = row / H_q;
-    const int64_t bat = qb / q_count, qi = q_begin + qb % q_count;
-    off = (bat * N + qi) * H_q + hq;
-    const u32x4 a = *reinterpret_cast<const u32x4*>(dout + off * kDh + 8 * c);
-    const u32x4 b = *reinterpret_cast<const u32x4*>(o + off * kDh + 8 * c);
+                                                       int64_t q_begin, int64_t rows, float* __restrict__ dlt) {
+  const int64_t base = (static_cast<int64_t>(blockIdx.y) * N + q_begin) * H_q;
+  const int64_t grp = (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) >> 4;
+  const int64_t ngrp = static_cast<int64_t>(gridDim.x) * (blockDim.x >> 4);
+  const int c = static_cast<int>(threadIdx.x & 15);
+  u32x4 a[kPrepRows], b[kPrepRows];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      s += __uint_as_float(a[j] << 16) * __uint_as_float(b[j] << 16);
-      s += __uint_as_float(a[j] & 0xFFFF0000u) * __uint_as_float(b[j] & 0xFFFF0000u);
-    }
+  for (int j = 0; j < kPrepRows; ++j) {
+    const int64_t row = grp + j * ngrp;
+    const int64_t off = (base + (row < rows ? row : rows - 1)) * kDh + 8 * c;
+    a[j] = *reinterpret_cast<const u32x4*>(dout + off);
+    b[j] = *reinterpret_cast<const u32x4*>(o + off);
   }
 #pragma unroll
-  for (int w = 8; w >= 1; w >>= 1) s += __shfl_xor(s, w, 16);
-  if (row < rows && c == 0) dlt[off] = s;
+  for (int j = 0; j < kPrepRows; ++j) {
+    float s = 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      s += __uint_as_float(a[j][e] << 16) * __uint_as_float(b[j][e] << 16);
+      s += __uint_as_float(a[j][e] & 0xFFFF0000u) * __uint_as_float(b[j][e] & 0xFFFF0000u);
+    }
+#pragma unroll
+    for (int w = 8; w >= 1; w >>= 1) s += __shfl_xor(s, w, 16);
+    const int64_t row = grp + j * ngrp;
+    if (row < rows && c == 0) dlt[base + row] = s;
+  }
 }
 
 // Sum of the per-slot partials of one (group, query): dQ of its G heads,
@@ -1057,9 +1073,9 @@ hipError_t launch_backward_chunk(const BwdArgs& a, hipStream_t stream) {
 
   // D = rowsum(dO * O) of the range's rows
   {
-    const int64_t rows = static_cast<int64_t>(a.batch) * a.q_count * H_q;
-    hipLaunchKernelGGL(bwd_prep_kernel, dim3(grid_exact(rows * 16)), dim3(256), 0, stream, a.dout, a.o, a.N, H_q,
-                       a.q_begin, a.q_count, rows, a.dlt);
+    const int64_t rows = a.q_count * H_q;  // per batch element
+    hipLaunchKernelGGL(bwd_prep_kernel, dim3(grid_exact(rows * 16, 256 * kPrepRows), a.batch), dim3(256), 0, stream,
+                       a.dout, a.o, a.N, H_q, a.q_begin, rows, a.dlt);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -1074,8 +1090,11 @@ hipError_t launch_backward_chunk(const BwdArgs& a, hipStream_t stream) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int64_t rows = seqs * a.q_count;
-    hipLaunchKernelGGL(proxy_lse_merge_kernel, dim3(grid_exact(rows)), dim3(256), 0, stream, a.block_idx,
-                       a.lsei_part, a.k, a.q_begin, a.q_count, rows, a.lsei2);
+    auto mk = a.k <= 4 ? proxy_lse_merge_kernel<4>
+              : a.k <= 8 ? proxy_lse_merge_kernel<8>
+              : a.k <= 16 ? proxy_lse_merge_kernel<16> : proxy_lse_merge_kernel<32>;
+    hipLaunchKernelGGL(mk, dim3(grid_exact(rows)), dim3(256), 0, stream, a.block_idx, a.lsei_part, a.k,
+                       a.q_begin, a.q_count, rows, a.lsei2);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
