@@ -792,7 +792,10 @@ __global__ __launch_bounds__(kBT, 1) void bwd_idx_kernel(
 // log2-sum-exp2 of its proxy scores over the block's visible keys, 32
 // entries at a time (a pass of fewer entries takes the block's next passes
 // along).  z^T = K^idx Q^idx^T with the keys on the row index, as in the
-// forward.
+// forward.  Software pipeline over chunks of 32 entries: while chunk c is
+// scored, the Q^idx rows of chunk c+1 are in flight and the entry words of
+// chunk c+2 are read (past the end of the work the last chunk stands in, so
+// every load of the loop is unconditional).
 constexpr int kLseWgPerCu = 4;
 
 template <int DIDX>
@@ -802,61 +805,99 @@ __global__ __launch_bounds__(64) void proxy_lse_kernel(
     const PassDesc* __restrict__ passes, int B_c, int nseqs, int q_begin, int q_count,
     float* __restrict__ lsei_part) {
   constexpr int KSI = DIDX / 16;
+  constexpr int KC = DIDX / 8;  // 16-byte chunks per K^idx row
   __shared__ __attribute__((aligned(16))) uint8_t ki_lds[kBk * kStr];
   PassIter it{segp, B_c, nseqs};
   const int lane = threadIdx.x, n = lane & 31, h = lane >> 5;
-  int cur_seq = -1, cur_blk = 0;
-  for (int pi = it.next(); pi >= 0; pi = it.next()) {
-    const PassDesc D = take_pass<32, true>(pi, it, passes);
-    const int bat = D.seq / H_sel, r = D.seq - bat * H_sel;
-    if (D.seq / H_sel != cur_seq / H_sel || cur_seq < 0 || D.blk != cur_blk) {
-      // K^idx is shared by the groups of a sequence
-      cur_seq = D.seq;
-      cur_blk = D.blk;
-      const int64_t key0 = static_cast<int64_t>(D.blk) * kBk;
+
+  auto entry_of = [&](const Chunk& c) {
+    const int e = c.cb + n;
+    return static_cast<uint32_t>(entries[c.D.start + (e < c.D.cnt ? e : c.cb)]);
+  };
+  auto q_of = [&](const Chunk& c, uint32_t ent, bf16x8(&qf)[KSI]) {
+    const int bat = c.D.seq / H_sel, r = c.D.seq - bat * H_sel;
+    const EntryRef er = entry_ref(ent, c.D.seq, kslots, q_begin, q_count);
+    const uint16_t* qr = q_idx + ((static_cast<int64_t>(bat) * N + er.i) * H_sel + r) * DIDX;
+#pragma unroll
+    for (int ks = 0; ks < KSI; ++ks) qf[ks] = as_bf16x8(*reinterpret_cast<const u32x4*>(qr + 16 * ks + 8 * h));
+  };
+
+  Chunk cur = first_chunk<32, true>(it, passes);
+  if (!cur.ok) return;  // uniform
+  uint32_t ent_cur = entry_of(cur);
+  bf16x8 q_cur[KSI];
+  q_of(cur, ent_cur, q_cur);
+  Chunk nx = next_chunk<32, true>(cur, it, passes);
+  uint32_t ent_nx = entry_of(nx.ok ? nx : cur);
+  int stg_bat = -1, stg_blk = 0;
+
+  for (;;) {
+    // K^idx of the chunk's block (shared by the groups of a sequence), all
+    // loads in flight before the LDS stores; the wave is alone in its
+    // workgroup and its LDS operations complete in order.
+    const int bat = cur.D.seq / H_sel;
+    if (bat != stg_bat || cur.D.blk != stg_blk) {
+      stg_bat = bat;
+      stg_blk = cur.D.blk;
+      const int64_t key0 = static_cast<int64_t>(cur.D.blk) * kBk;
       const int nvalid = static_cast<int>(min<int64_t>(kBk, N - key0));
       const uint16_t* kb = k_idx + (static_cast<int64_t>(bat) * N + key0) * DIDX;
-      for (int x = lane; x < kBk * (DIDX / 8); x += 64) {
-        const int key = x / (DIDX / 8), c = x % (DIDX / 8);
-        const u32x4 w = *reinterpret_cast<const u32x4*>(kb + min(key, nvalid - 1) * DIDX + 8 * c);
-        *reinterpret_cast<u32x4*>(ki_lds + key * kStr + 16 * c) = key < nvalid ? w : u32x4{0u, 0u, 0u, 0u};
+      u32x4 w[kBk * KC / 64];
+#pragma unroll
+      for (int j = 0; j < kBk * KC / 64; ++j) {
+        const int x = lane + 64 * j, key = x / KC, c = x % KC;
+        w[j] = *reinterpret_cast<const u32x4*>(kb + min(key, nvalid - 1) * DIDX + 8 * c);
+      }
+#pragma unroll
+      for (int j = 0; j < kBk * KC / 64; ++j) {
+        const int x = lane + 64 * j, key = x / KC, c = x % KC;
+        *reinterpret_cast<u32x4*>(ki_lds + key * kStr + 16 * c) = key < nvalid ? w[j] : u32x4{0u, 0u, 0u, 0u};
       }
     }
-    cur_seq = D.seq;
-    for (int cb = 0; cb < D.cnt; cb += 32) {
-      const int e = cb + n;
-      const EntryRef er =
-          entry_ref(static_cast<uint32_t>(entries[D.start + (e < D.cnt ? e : 0)]), D.seq, kslots, q_begin, q_count);
-      const uint16_t* qr = q_idx + ((static_cast<int64_t>(bat) * N + er.i) * H_sel + r) * DIDX;
-      bf16x8 qf[KSI];
+
+    // ---- the next chunk's Q^idx rows, the entry words of the one after
+    const Chunk nxv = nx.ok ? nx : cur;
+    bf16x8 q_nx[KSI];
+    q_of(nxv, ent_nx, q_nx);
+    const Chunk nx2 = nx.ok ? next_chunk<32, true>(nx, it, passes) : nx;
+    const uint32_t ent_nx2 = entry_of(nx2.ok ? nx2 : nxv);
+
+    // ---- this chunk
+    const int e = cur.cb + n;
+    const EntryRef er = entry_ref(ent_cur, cur.D.seq, kslots, q_begin, q_count);
+    f32x16 z[4];
 #pragma unroll
-      for (int ks = 0; ks < KSI; ++ks) qf[ks] = as_bf16x8(*reinterpret_cast<const u32x4*>(qr + 16 * ks + 8 * h));
-      f32x16 z[4];
+    for (int mt = 0; mt < 4; ++mt) {
+      z[mt] = f32x16{};
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
-        z[mt] = f32x16{};
-#pragma unroll
-        for (int ks = 0; ks < KSI; ++ks)
-          z[mt] = mfma32x32x16(lds_frag(ki_lds + (32 * mt + n) * kStr + 32 * ks + 16 * h), qf[ks], z[mt]);
-      }
-      // keys 32 mt + acc_row(e, h) of the block; hide those past the query
-      const int lim = er.i - D.blk * kBk;
-      float m = -__builtin_huge_valf();
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-        for (int el = 0; el < 16; ++el)
-          if (32 * mt + acc_row(el, h) <= lim) m = fmaxf(m, z[mt][el]);
-      m = halves_max(m);
-      float l = 0.f;
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-        for (int el = 0; el < 16; ++el)
-          if (32 * mt + acc_row(el, h) <= lim) l += __builtin_amdgcn_exp2f((z[mt][el] - m) * idx_scale_log2);
-      l = halves_sum(l);
-      if (h == 0 && e < D.cnt) lsei_part[er.slot] = m * idx_scale_log2 + __builtin_amdgcn_logf(l);
+      for (int ks = 0; ks < KSI; ++ks)
+        z[mt] = mfma32x32x16(lds_frag(ki_lds + (32 * mt + n) * kStr + 32 * ks + 16 * h), q_cur[ks], z[mt]);
     }
+    // keys 32 mt + acc_row(e, h) of the block; hide those past the query
+    const int lim = er.i - cur.D.blk * kBk;
+    float m = -__builtin_huge_valf();
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int el = 0; el < 16; ++el)
+        if (32 * mt + acc_row(el, h) <= lim) m = fmaxf(m, z[mt][el]);
+    m = halves_max(m);
+    float l = 0.f;
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int el = 0; el < 16; ++el)
+        if (32 * mt + acc_row(el, h) <= lim) l += __builtin_amdgcn_exp2f((z[mt][el] - m) * idx_scale_log2);
+    l = halves_sum(l);
+    if (h == 0 && e < cur.D.cnt) lsei_part[er.slot] = m * idx_scale_log2 + __builtin_amdgcn_logf(l);
+
+    if (!nx.ok) break;
+    cur = nx;
+    nx = nx2;
+    ent_cur = ent_nx;
+    ent_nx = ent_nx2;
+#pragma unroll
+    for (int ks = 0; ks < KSI; ++ks) q_cur[ks] = q_nx[ks];
   }
 }
 
