@@ -140,8 +140,8 @@ __global__ __launch_bounds__(kDThreads, 1) void dense_attn_kernel(
     for (int mt2 = 0; mt2 < 2; ++mt2) {
 #pragma unroll
       for (int el = 0; el < 16; el += 4) {
-        m0 = fmaxf(m0, fmaxf(s[mt2][el], s[mt2][el + 1]));
-        m1 = fmaxf(m1, fmaxf(s[mt2][el + 2], s[mt2][el + 3]));
+        m0 = max3f(m0, s[mt2][el], s[mt2][el + 1]);
+        m1 = max3f(m1, s[mt2][el + 2], s[mt2][el + 3]);
       }
     }
     const float m_blk = halves_max(fmaxf(m0, m1)) * scale_log2;

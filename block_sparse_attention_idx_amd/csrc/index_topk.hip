@@ -267,8 +267,8 @@ __global__ __launch_bounds__(kIdxThreads, 1) void index_topk_kernel(
     auto pool = [&](const f32x16& a0, const f32x16& a1, int e0, int e1) {  // elements [e0, e1)
 #pragma unroll
       for (int e = e0; e < e1; e += 2) {
-        mx0 = fmaxf(mx0, fmaxf(a0[e], a0[e + 1]));
-        mx1 = fmaxf(mx1, fmaxf(a1[e], a1[e + 1]));
+        mx0 = max3f(mx0, a0[e], a0[e + 1]);
+        mx1 = max3f(mx1, a1[e], a1[e + 1]);
       }
     };
     // Block pb's pooled maxima are complete: lane half 0 holds keys 4h.. of

@@ -37,6 +37,17 @@ __device__ __forceinline__ f32x16 mfma32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+// max(a, b, c) as one v_max3_f32.  With NaNs excluded (-fno-honor-nans) the
+// compiler treats fmaxf as associative and rebalances a running maximum over
+// pairs into pairwise maxima plus v_max3 (three instructions per four values
+// instead of two); a chain of these keeps the running form.  Exact, so the
+// result is the same whatever the order.
+__device__ __forceinline__ float max3f(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
 // Pack two fp32 into two bf16 (round to nearest even) in one u32.
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));

@@ -394,8 +394,8 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_kernel(
     for (int mt = 0; mt < kMT; ++mt) {
 #pragma unroll
       for (int el = 0; el < 16; el += 4) {
-        m0 = fmaxf(m0, fmaxf(acc[mt][el], acc[mt][el + 1]));
-        m1 = fmaxf(m1, fmaxf(acc[mt][el + 2], acc[mt][el + 3]));
+        m0 = max3f(m0, acc[mt][el], acc[mt][el + 1]);
+        m1 = max3f(m1, acc[mt][el + 2], acc[mt][el + 3]);
       }
     }
     const float mb = halves_max(fmaxf(m0, m1)) * scale_log2;  // scale_log2 > 0
