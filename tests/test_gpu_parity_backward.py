@@ -70,6 +70,7 @@ BWD_CASES = [
     TINY.with_(N=900, H_q=16, H_kv=2, H_idx=8, k=4),            # 8 index heads over 2 K/V heads
     TINY.with_(N=1300, H_q=16, H_kv=2, k=6, d_idx=128),         # G 8
     TINY.with_(N=700, batch=2, k=3),                            # batch 2
+    TINY.with_(N=1100, batch=2, k=4, q_chunk=384),              # batch 2, three query chunks (ragged)
     # G 16 and 8 at N = 4096: a group's 512-1024 passes leave every workgroup
     # several consecutive passes of one key block, so the index branch's
     # chunks join passes (a pass holds 256 / G entries, a chunk 64)
