@@ -214,8 +214,8 @@ __global__ __launch_bounds__(kIdxThreads, 1) void index_topk_kernel(
     // j >= the candidate's place p: entry j takes ts[j - 1] when c_{j-1}
     // (shifted down), x when c_j alone (j = p), and keeps ts[j] otherwise.
     // Walking j downwards keeps ts[j - 1] unmodified when entry j needs it,
-    // and each comparison serves two entries: one compare and four selects
-    // per entry.  A candidate that is not needed enters as -inf and moves
+    // and each comparison serves two entries: per entry one compare, two
+    // selects for the id and one median-of-three for the score.  A candidate that is not needed enters as -inf and moves
     // nothing (the comparisons are strict).
     // The walk can be split into ranges of entries (insert_entries), so that
     // its VALU work can sit between MFMAs.
@@ -233,12 +233,14 @@ __global__ __launch_bounds__(kIdxThreads, 1) void index_topk_kernel(
         if (j > jhi || j < jlo) continue;
         // (values, not lvalues, in the selects: a conditional over two
         // lvalues selects an address and would put the list in scratch)
+        // The new score is clamp(x, ts[j], ts[j - 1]) (ts[j - 1] >= ts[j]),
+        // one v_med3_f32: ts[j - 1] when c_{j-1}, x when c_j alone, ts[j]
+        // otherwise, bit for bit the selects below make for the ids.
         const float x = ins_x, tj = ts[j], tp = ts[j > 0 ? j - 1 : 0];
         const int xi = ins_xi, ij = ids[j], ip = ids[j > 0 ? j - 1 : 0];
         const bool c = ins_c, cp = j > 0 && x > tp;
-        const float nt = c ? x : tj;
         const int ni = c ? xi : ij;
-        ts[j] = cp ? tp : nt;
+        ts[j] = j > 0 ? __builtin_amdgcn_fmed3f(x, tp, tj) : fmaxf(x, tj);
         ids[j] = cp ? ip : ni;
         ins_c = cp;
       }
