@@ -38,12 +38,13 @@
 //  * Software pipeline over passes: while pass p computes, the Q rows of pass
 //    p+1 are gathered into registers and the entry of pass p+2 is read; the
 //    scores of pass p+1 follow pass p's P V.  One register set each for Q and
-//    the scores (158 VGPRs in the bf16 kernel), which leaves the scheduler
+//    the scores (214 VGPRs in the bf16 kernel), which leaves the scheduler
 //    room to keep LDS fragment reads ahead of their MFMAs.  Every memory
 //    operation of the loop is issued unconditionally, so the compiler's
 //    in-order vmcnt waits never have to cover the stores or the loads just
 //    issued.
-//  * Softmax in base 2 (v_exp_f32) with the scale folded into one FMA.  fp8
+//  * Softmax in base 2 (v_exp_f32) with the scale folded into one FMA, its
+//    exponentials interleaved with the P V MFMAs of the previous key step.  fp8
 //    (OCP e4m3) inputs: the scores come from v_mfma_scale_f32_32x32x64_f8f6f4
 //    on the Q and K codes (exact products, K kept as codes in LDS), V is
 //    widened exactly to bf16 when staged (P V stays a bf16 product), and the
@@ -379,16 +380,22 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_kernel(
     }
   };
 
-  // Row maximum on the raw scores, then the scale folded into one FMA before
-  // exp2; the row sum adds the fp32 probabilities, so lse is the exact
+  // Softmax and O^T = V^T P^T in one walk over the keys.  Row maximum on the
+  // raw scores, then the scale folded into one FMA before exp2; the row sum
+  // adds the fp32 probabilities in key order, so lse is the exact
   // log-sum-exp up to fp32 rounding.  The two half-waves hold the two halves
   // of every row and swap partial results with one v_permlane32_swap.
   // P^T fragments (B operand of O^T = V^T P^T): step st = 2 mt + e2 covers
   // keys 32mt + 16e2 + 8(j/4) + 4h + (j%4), accumulator elements 8e2 .. +7.
   // Key tiles past a smaller block hold no keys: their probabilities are zero
   // and neither the softmax nor P V visits them.
+  // After the maximum, fenced slot (st, dt) issues the P V MFMA of dims tile
+  // dt on P step st and turns probability pair dt of step st + 1, so the
+  // exponentials run beside the matrix cores; each V fragment is read two
+  // slots ahead.  Lane (n, h) receives dims 64h + 16dt + el of its row and
+  // writes them, scaled by 1/l, to the wave's tile.
   constexpr int kMT = (1 << BKS) / 32;
-  auto softmax = [&](const f32x16(&acc)[4], bf16x8(&pf)[8], float& inv, float& lse2) {
+  auto softmax_pv = [&](const f32x16(&acc)[4], float& lse2) {
     float m0 = -__builtin_huge_valf(), m1 = -__builtin_huge_valf();
 #pragma unroll
     for (int mt = 0; mt < kMT; ++mt) {
@@ -398,51 +405,60 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_kernel(
         m1 = max3f(m1, acc[mt][el + 2], acc[mt][el + 3]);
       }
     }
-    const float mb = halves_max(fmaxf(m0, m1)) * scale_log2;  // scale_log2 > 0
+    // Rounded once and opaque: otherwise the compiler may contract the
+    // product into the lse sum below (one fma instead of a multiply and an
+    // add), which moves lse by an ulp depending on the schedule around it.
+    float mb = halves_max(fmaxf(m0, m1)) * scale_log2;  // scale_log2 > 0
+    asm volatile("" : "+v"(mb));
+    constexpr int NS = 2 * kMT;  // P steps of 16 keys
     float l0 = 0.f, l1 = 0.f;
+    // probability pair j of step st: keys of accumulator elements 8 e2 + 2j, + 1
+    auto pair = [&](int st, int j) {
+      const int mt = st >> 1, e2 = st & 1;
+      const float pa = __builtin_amdgcn_exp2f(__builtin_fmaf(acc[mt][8 * e2 + 2 * j], scale_log2, -mb));
+      const float pb = __builtin_amdgcn_exp2f(__builtin_fmaf(acc[mt][8 * e2 + 2 * j + 1], scale_log2, -mb));
+      l0 += pa;
+      l1 += pb;
+      return pack_bf16x2(pa, pb);
+    };
+    // V^T fragment i = 4 st + dt: row dsel + 16 dt (stored at dvt_row(dsel) +
+    // 32 dt); keys 16 st + 8 h .. + 7, one 16-byte chunk in the permuted order
+    auto vread = [&](int i) {
+      return *reinterpret_cast<const u32x4*>(v_base + 32 * (i & 3) * kVStride + 32 * (i >> 2));
+    };
+    uint32_t w[2][4];
 #pragma unroll
-    for (int mt = 0; mt < kMT; ++mt) {
+    for (int j = 0; j < 4; ++j) w[0][j] = pair(0, j);
+    u32x4 vr[3];
+    vr[0] = vread(0);
+    vr[1] = vread(1);
+    f32x16 oa[4] = {};
 #pragma unroll
-      for (int e2 = 0; e2 < 2; ++e2) {
-        uint32_t w[4];
+    for (int st = 0; st < NS; ++st) {
+      const bf16x8 pfs = as_bf16x8(u32x4{w[st & 1][0], w[st & 1][1], w[st & 1][2], w[st & 1][3]});
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const float pa = __builtin_amdgcn_exp2f(__builtin_fmaf(acc[mt][8 * e2 + 2 * j], scale_log2, -mb));
-          const float pb = __builtin_amdgcn_exp2f(__builtin_fmaf(acc[mt][8 * e2 + 2 * j + 1], scale_log2, -mb));
-          w[j] = pack_bf16x2(pa, pb);
-          l0 += pa;
-          l1 += pb;
-        }
-        pf[2 * mt + e2] = as_bf16x8(u32x4{w[0], w[1], w[2], w[3]});
+      for (int dt = 0; dt < 4; ++dt) {
+        const int i = 4 * st + dt;
+        if (i + 2 < 4 * NS) vr[(i + 2) % 3] = vread(i + 2);
+        oa[dt] = mfma32x32x16(as_bf16x8(vr[i % 3]), pfs, oa[dt]);
+        if (st + 1 < NS) w[(st + 1) & 1][dt] = pair(st + 1, dt);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
     const float l = halves_sum(l0 + l1);
-    inv = out_scale * __builtin_amdgcn_rcpf(l);
+    const float inv = out_scale * __builtin_amdgcn_rcpf(l);
     lse2 = mb + __builtin_amdgcn_logf(l);
-  };
-
-  // O^T = V^T P^T, one 32-dim tile at a time; lane (n, h) receives dims
-  // 64h + 16dt + el of its row and writes them, scaled, to the wave's tile.
-  auto pv_out = [&](const bf16x8(&pf)[8], float inv) {
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) {
-      f32x16 oa = {};
-#pragma unroll
-      for (int st = 0; st < 2 * kMT; ++st) {
-        // row dsel + 16 dt (stored at dvt_row(dsel) + 32 dt); keys
-        // 16 st + 8 h .. + 7, one 16-byte chunk in the permuted key order
-        const u32x4 vf = *reinterpret_cast<const u32x4*>(v_base + 32 * dt * kVStride + 32 * st);
-        oa = mfma32x32x16(as_bf16x8(vf), pf[st], oa);
-      }
       uint8_t* dst = o_tile + n * kOStride + 128 * h + 32 * dt;
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf) {
         const int b8 = 8 * hf;
         *reinterpret_cast<u32x4*>(dst + 16 * hf) =
-            u32x4{pack_bf16x2(oa[b8 + 0] * inv, oa[b8 + 1] * inv),
-                  pack_bf16x2(oa[b8 + 2] * inv, oa[b8 + 3] * inv),
-                  pack_bf16x2(oa[b8 + 4] * inv, oa[b8 + 5] * inv),
-                  pack_bf16x2(oa[b8 + 6] * inv, oa[b8 + 7] * inv)};
+            u32x4{pack_bf16x2(oa[dt][b8 + 0] * inv, oa[dt][b8 + 1] * inv),
+                  pack_bf16x2(oa[dt][b8 + 2] * inv, oa[dt][b8 + 3] * inv),
+                  pack_bf16x2(oa[dt][b8 + 4] * inv, oa[dt][b8 + 5] * inv),
+                  pack_bf16x2(oa[dt][b8 + 6] * inv, oa[dt][b8 + 7] * inv)};
       }
     }
   };
@@ -479,15 +495,12 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_kernel(
     const uint32_t raw2 = row_ent(D2);
     q.load(rr1.q, h);
 
-    // ---- softmax of pass p
+    // ---- pass p: causal mask, softmax and O^T = V^T P^T into the wave's
+    // tile, then out
     mask_own(acc, rr0, D0.blk);
-    bf16x8 pf[8];
-    float inv, lse2;
-    softmax(acc, pf, inv, lse2);
-
-    // ---- O^T = V^T P^T into the wave's tile, then out
+    float lse2;
     if (h == 0) orow_tile[n] = rr0.orow;
-    pv_out(pf, inv);
+    softmax_pv(acc, lse2);
     // (both half-waves hold the same m and l; their stores coincide)
     lse_part[rr0.orow] = lse2 * 0.69314718055994531f;
     // The wave's 32 rows leave row-contiguous: instruction j stores rows
