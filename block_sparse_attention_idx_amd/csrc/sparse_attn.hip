@@ -38,7 +38,7 @@
 //  * Software pipeline over passes: while pass p computes, the Q rows of pass
 //    p+1 are gathered into registers and the entry of pass p+2 is read; the
 //    scores of pass p+1 follow pass p's P V.  One register set each for Q and
-//    the scores (214 VGPRs in the bf16 kernel), which leaves the scheduler
+//    the scores (194 VGPRs in the bf16 kernel), which leaves the scheduler
 //    room to keep LDS fragment reads ahead of their MFMAs.  Every memory
 //    operation of the loop is issued unconditionally, so the compiler's
 //    in-order vmcnt waits never have to cover the stores or the loads just
@@ -393,7 +393,8 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_kernel(
   // dt on P step st and turns probability pair dt of step st + 1, so the
   // exponentials run beside the matrix cores; each V fragment is read two
   // slots ahead.  Lane (n, h) receives dims 64h + 16dt + el of its row and
-  // writes them, scaled by 1/l, to the wave's tile.
+  // writes them, scaled by 1/l, to the wave's tile: in the last key step each
+  // dims tile goes out beside the next tile's MFMA (l is complete by then).
   constexpr int kMT = (1 << BKS) / 32;
   auto softmax_pv = [&](const f32x16(&acc)[4], float& lse2) {
     float m0 = -__builtin_huge_valf(), m1 = -__builtin_huge_valf();
@@ -433,23 +434,8 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_kernel(
     vr[0] = vread(0);
     vr[1] = vread(1);
     f32x16 oa[4] = {};
-#pragma unroll
-    for (int st = 0; st < NS; ++st) {
-      const bf16x8 pfs = as_bf16x8(u32x4{w[st & 1][0], w[st & 1][1], w[st & 1][2], w[st & 1][3]});
-#pragma unroll
-      for (int dt = 0; dt < 4; ++dt) {
-        const int i = 4 * st + dt;
-        if (i + 2 < 4 * NS) vr[(i + 2) % 3] = vread(i + 2);
-        oa[dt] = mfma32x32x16(as_bf16x8(vr[i % 3]), pfs, oa[dt]);
-        if (st + 1 < NS) w[(st + 1) & 1][dt] = pair(st + 1, dt);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    }
-    const float l = halves_sum(l0 + l1);
-    const float inv = out_scale * __builtin_amdgcn_rcpf(l);
-    lse2 = mb + __builtin_amdgcn_logf(l);
-#pragma unroll
-    for (int dt = 0; dt < 4; ++dt) {
+    float inv = 0.f;
+    auto out_tile = [&](int dt) {
       uint8_t* dst = o_tile + n * kOStride + 128 * h + 32 * dt;
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf) {
@@ -460,7 +446,27 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_kernel(
                   pack_bf16x2(oa[dt][b8 + 4] * inv, oa[dt][b8 + 5] * inv),
                   pack_bf16x2(oa[dt][b8 + 6] * inv, oa[dt][b8 + 7] * inv)};
       }
+    };
+#pragma unroll
+    for (int st = 0; st < NS; ++st) {
+      if (st == NS - 1) {
+        // every probability has been added: the row's l, 1/l and lse
+        const float l = halves_sum(l0 + l1);
+        inv = out_scale * __builtin_amdgcn_rcpf(l);
+        lse2 = mb + __builtin_amdgcn_logf(l);
+      }
+      const bf16x8 pfs = as_bf16x8(u32x4{w[st & 1][0], w[st & 1][1], w[st & 1][2], w[st & 1][3]});
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) {
+        const int i = 4 * st + dt;
+        if (i + 2 < 4 * NS) vr[(i + 2) % 3] = vread(i + 2);
+        oa[dt] = mfma32x32x16(as_bf16x8(vr[i % 3]), pfs, oa[dt]);
+        if (st + 1 < NS) w[(st + 1) & 1][dt] = pair(st + 1, dt);
+        else if (dt > 0) out_tile(dt - 1);  // its last MFMA was the slot before
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
+    out_tile(3);
   };
 
   // ---- software pipeline over passes: at the start of pass p the entry of
